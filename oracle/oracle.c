@@ -1,0 +1,306 @@
+/*
+ * oracle.c -- plain CPU reference for paged-attention decode, in fp64.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h).  Every routine is the plain
+ * definition: gather the context through the block table into contiguous rows,
+ * then evaluate softmax(scale * q.K^T) V with the max subtracted, in double
+ * precision.  No blocking, fusion or reordering beyond that.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <omp.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- codecs */
+
+/* IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Exponent 0 holds zero and subnormals (fraction * 2^-24); 31 holds inf/NaN. */
+double orc_f16_value(uint16_t bits) {
+  int sign = bits >> 15;
+  int e = (bits >> 10) & 0x1F;
+  int f = bits & 0x3FF;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)f, -24);
+  } else if (e == 31) {
+    v = f ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + f), e - 25);
+  }
+  return sign ? -v : v;
+}
+
+/* OCP e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+ * Exponent 0 holds zero and subnormals (m * 2^-9).  There are no infinities;
+ * exponent 15 with mantissa 7 is NaN, so the largest finite value is
+ * 1.75 * 2^8 = 448. */
+double orc_e4m3fn_value(uint8_t byte) {
+  int sign = byte >> 7;
+  int e = (byte >> 3) & 0xF;
+  int m = byte & 0x7;
+  double v;
+  if (e == 15 && m == 7) {
+    v = NAN;
+  } else if (e == 0) {
+    v = ldexp((double)m, -9);
+  } else {
+    v = ldexp((double)(8 + m), e - 10); /* 2^(e-7) * (1 + m/8) */
+  }
+  return sign ? -v : v;
+}
+
+/* Round a non-negative double to the nearest integer, ties to the even one. */
+static double round_half_even(double n) {
+  double fl = floor(n);
+  double frac = n - fl;
+  if (frac > 0.5) return fl + 1.0;
+  if (frac < 0.5) return fl;
+  return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/* fp32 -> e4m3fn.  Steps: NaN stays NaN (sign kept, S.1111.111); magnitudes at
+ * or beyond the largest finite value saturate to 448 (values in (448, 464)
+ * would round to 448 anyway, and 464 is a tie that rounds to the even
+ * mantissa 448); otherwise find the binade, count quanta of that binade and
+ * round the count to nearest even.  Below 2^-6 the quantum is the subnormal
+ * step 2^-9. */
+uint8_t orc_e4m3fn_encode(float x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return (uint8_t)(sign | 0x7F);
+  double a = fabs((double)x);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+  if (a == 0.0) return sign;
+  int ex;
+  (void)frexp(a, &ex);           /* a = fr * 2^ex, fr in [0.5, 1) */
+  int E = ex - 1;                /* a = 2^E * (1.f)                 */
+  if (E < -6) {
+    double n = round_half_even(a * 512.0);   /* quanta of 2^-9: 0..8 */
+    return (uint8_t)(sign | (uint8_t)n);     /* 8 is the smallest normal, 0x08 */
+  }
+  double quantum = ldexp(1.0, E - 3);
+  double n = round_half_even(a / quantum);   /* 8..16 */
+  if (n == 16.0) {
+    E += 1;
+    n = 8.0;
+  }
+  int code = ((E + 7) << 3) | ((int)n - 8);
+  if (code > 0x7E) code = 0x7E;
+  return (uint8_t)(sign | code);
+}
+
+void orc_f16_values(const uint16_t* bits, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_value(bits[i]);
+}
+
+void orc_e4m3fn_values(const uint8_t* bytes, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3fn_value(bytes[i]);
+}
+
+void orc_e4m3fn_encode_n(const float* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3fn_encode(x[i]);
+}
+
+/* ------------------------------------------------------------ pool access */
+
+static int64_t block_stride_of(const orc_pool* p) {
+  if (p->block_stride) return p->block_stride;
+  return (int64_t)p->block_size * p->num_kv_heads * p->head_dim * p->elem_bytes;
+}
+
+/* Byte offset of element (block, offset-in-block, kv head, dim). */
+static int64_t elem_offset(const orc_pool* p, int64_t blk, int32_t off, int32_t kh, int32_t d) {
+  int64_t in_block = (((int64_t)off * p->num_kv_heads + kh) * p->head_dim + d) * p->elem_bytes;
+  return blk * block_stride_of(p) + in_block;
+}
+
+static double read_elem(const orc_pool* p, const void* base, int64_t byte_off, double scale) {
+  const uint8_t* b = (const uint8_t*)base + byte_off;
+  if (p->elem_bytes == 2) {
+    uint16_t bits;
+    memcpy(&bits, b, 2);
+    return orc_f16_value(bits);
+  }
+  return orc_e4m3fn_value(*b) * scale;
+}
+
+static int nthreads_or_default(int n) { return n > 0 ? n : omp_get_max_threads(); }
+
+/* ---------------------------------------------------------------- writes */
+
+void orc_scatter(const orc_pool* p, const uint16_t* k_new, const uint16_t* v_new,
+                 const int64_t* slots, int64_t T, int nthreads) {
+  const int32_t Hkv = p->num_kv_heads, D = p->head_dim;
+  const float ks = (float)p->k_scale, vs = (float)p->v_scale;
+#pragma omp parallel for schedule(static) num_threads(nthreads_or_default(nthreads))
+  for (int64_t i = 0; i < T; ++i) {
+    int64_t slot = slots[i];
+    if (slot < 0) continue;
+    int64_t blk = slot / p->block_size;
+    int32_t off = (int32_t)(slot % p->block_size);
+    for (int32_t kh = 0; kh < Hkv; ++kh) {
+      for (int32_t d = 0; d < D; ++d) {
+        int64_t src = ((int64_t)i * Hkv + kh) * D + d;
+        int64_t dst = elem_offset(p, blk, off, kh, d);
+        if (p->elem_bytes == 2) {
+          memcpy((uint8_t*)p->k + dst, &k_new[src], 2);
+          memcpy((uint8_t*)p->v + dst, &v_new[src], 2);
+        } else {
+          float kx = (float)orc_f16_value(k_new[src]);
+          float vx = (float)orc_f16_value(v_new[src]);
+          ((uint8_t*)p->k)[dst] = orc_e4m3fn_encode(kx / ks);
+          ((uint8_t*)p->v)[dst] = orc_e4m3fn_encode(vx / vs);
+        }
+      }
+    }
+  }
+}
+
+void orc_copy_blocks(const orc_pool* p, const int64_t* pairs, int64_t n) {
+  const int64_t stride = block_stride_of(p);
+  const int64_t bytes = (int64_t)p->block_size * p->num_kv_heads * p->head_dim * p->elem_bytes;
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    memmove((uint8_t*)p->k + dst * stride, (const uint8_t*)p->k + src * stride, (size_t)bytes);
+    memmove((uint8_t*)p->v + dst * stride, (const uint8_t*)p->v + src * stride, (size_t)bytes);
+  }
+}
+
+/* ------------------------------------------------------------------ reads */
+
+void orc_gather_head(const orc_pool* p, const int32_t* bt_row, int32_t len, int32_t kh,
+                     double* Kc, double* Vc) {
+  const int32_t D = p->head_dim;
+  for (int32_t t = 0; t < len; ++t) {
+    int64_t blk = bt_row[t / p->block_size];
+    int32_t off = t % p->block_size;
+    for (int32_t d = 0; d < D; ++d) {
+      int64_t o = elem_offset(p, blk, off, kh, d);
+      Kc[(int64_t)t * D + d] = read_elem(p, p->k, o, p->k_scale);
+      Vc[(int64_t)t * D + d] = read_elem(p, p->v, o, p->v_scale);
+    }
+  }
+}
+
+void orc_attend(const double* q, const double* Kc, const double* Vc, int32_t len,
+                int32_t D, double scale, double* out) {
+  for (int32_t d = 0; d < D; ++d) out[d] = 0.0;
+  if (len <= 0) return;
+  double* x = (double*)malloc(sizeof(double) * (size_t)len);
+  double m = -INFINITY;
+  for (int32_t t = 0; t < len; ++t) {
+    double dot = 0.0;
+    for (int32_t d = 0; d < D; ++d) dot += q[d] * Kc[(int64_t)t * D + d];
+    x[t] = scale * dot;
+    if (x[t] > m) m = x[t];
+  }
+  double denom = 0.0;
+  for (int32_t t = 0; t < len; ++t) {
+    double w = exp(x[t] - m);
+    denom += w;
+    for (int32_t d = 0; d < D; ++d) out[d] += w * Vc[(int64_t)t * D + d];
+  }
+  for (int32_t d = 0; d < D; ++d) out[d] /= denom;
+  free(x);
+}
+
+/* One (sequence, KV head) unit of work, evaluated for each of its query heads. */
+typedef void (*head_fn)(const double* q, const double* Kc, const double* Vc, int32_t len,
+                        int32_t D, double scale, int32_t psz, double* out);
+
+static void attend_adapter(const double* q, const double* Kc, const double* Vc, int32_t len,
+                           int32_t D, double scale, int32_t psz, double* out) {
+  (void)psz;
+  orc_attend(q, Kc, Vc, len, D, scale, out);
+}
+
+/* Partitioned evaluation: per partition, m_p = max score, l_p = sum exp(x - m_p),
+ * o_p = sum exp(x - m_p) v / l_p; then M = max m_p and
+ * out = sum_p exp(m_p - M) l_p o_p / sum_p exp(m_p - M) l_p. */
+static void attend_split(const double* q, const double* Kc, const double* Vc, int32_t len,
+                         int32_t D, double scale, int32_t psz, double* out) {
+  for (int32_t d = 0; d < D; ++d) out[d] = 0.0;
+  if (len <= 0) return;
+  int32_t np = (len + psz - 1) / psz;
+  double* m = (double*)malloc(sizeof(double) * (size_t)np);
+  double* l = (double*)malloc(sizeof(double) * (size_t)np);
+  double* o = (double*)calloc((size_t)np * (size_t)D, sizeof(double));
+  for (int32_t pi = 0; pi < np; ++pi) {
+    int32_t t0 = pi * psz, t1 = t0 + psz < len ? t0 + psz : len;
+    double mp = -INFINITY;
+    for (int32_t t = t0; t < t1; ++t) {
+      double dot = 0.0;
+      for (int32_t d = 0; d < D; ++d) dot += q[d] * Kc[(int64_t)t * D + d];
+      double xt = scale * dot;
+      if (xt > mp) mp = xt;
+    }
+    double lp = 0.0;
+    for (int32_t t = t0; t < t1; ++t) {
+      double dot = 0.0;
+      for (int32_t d = 0; d < D; ++d) dot += q[d] * Kc[(int64_t)t * D + d];
+      double w = exp(scale * dot - mp);
+      lp += w;
+      for (int32_t d = 0; d < D; ++d) o[(int64_t)pi * D + d] += w * Vc[(int64_t)t * D + d];
+    }
+    for (int32_t d = 0; d < D; ++d) o[(int64_t)pi * D + d] /= lp;
+    m[pi] = mp;
+    l[pi] = lp;
+  }
+  double M = -INFINITY;
+  for (int32_t pi = 0; pi < np; ++pi)
+    if (m[pi] > M) M = m[pi];
+  double W = 0.0;
+  for (int32_t pi = 0; pi < np; ++pi) {
+    double w = exp(m[pi] - M) * l[pi];
+    W += w;
+    for (int32_t d = 0; d < D; ++d) out[d] += w * o[(int64_t)pi * D + d];
+  }
+  for (int32_t d = 0; d < D; ++d) out[d] /= W;
+  free(m);
+  free(l);
+  free(o);
+}
+
+static void decode_units(const orc_pool* p, const uint16_t* qbits, int32_t S, int32_t Hq,
+                         const int32_t* bt, int32_t max_blocks, const int32_t* lens,
+                         float scale, int32_t psz, const int32_t* units, int64_t n_units,
+                         double* out, int nthreads, head_fn fn) {
+  const int32_t Hkv = p->num_kv_heads, D = p->head_dim, g = Hq / Hkv;
+  const int64_t total = units ? n_units : (int64_t)S * Hkv;
+  const double sc = (double)scale;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads_or_default(nthreads))
+  for (int64_t u = 0; u < total; ++u) {
+    int32_t s = units ? units[2 * u] : (int32_t)(u / Hkv);
+    int32_t kh = units ? units[2 * u + 1] : (int32_t)(u % Hkv);
+    int32_t len = lens[s];
+    size_t rows = (size_t)(len > 0 ? len : 1) * (size_t)D;
+    double* Kc = (double*)malloc(sizeof(double) * rows);
+    double* Vc = (double*)malloc(sizeof(double) * rows);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+    orc_gather_head(p, bt + (int64_t)s * max_blocks, len, kh, Kc, Vc);
+    for (int32_t h = kh * g; h < (kh + 1) * g; ++h) {
+      const uint16_t* qh = qbits + ((int64_t)s * Hq + h) * D;
+      for (int32_t d = 0; d < D; ++d) qd[d] = orc_f16_value(qh[d]);
+      fn(qd, Kc, Vc, len, D, sc, psz, out + ((int64_t)s * Hq + h) * D);
+    }
+    free(Kc);
+    free(Vc);
+    free(qd);
+  }
+}
+
+void orc_decode(const orc_pool* p, const uint16_t* q, int32_t S, int32_t Hq,
+                const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                float scale, const int32_t* units, int64_t n_units, double* out, int nthreads) {
+  decode_units(p, q, S, Hq, block_tables, max_blocks, seq_lens, scale, 0, units, n_units, out,
+               nthreads, attend_adapter);
+}
+
+void orc_decode_split(const orc_pool* p, const uint16_t* q, int32_t S, int32_t Hq,
+                      const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                      float scale, int32_t partition_size, const int32_t* units,
+                      int64_t n_units, double* out, int nthreads) {
+  decode_units(p, q, S, Hq, block_tables, max_blocks, seq_lens, scale, partition_size, units,
+               n_units, out, nthreads, attend_split);
+}

@@ -1,0 +1,391 @@
+"""Seeded synthetic decode workloads (input construction only).
+
+This module draws everything a paged-attention decode step consumes and nothing
+it computes: per-sequence context lengths, physical block ids handed out from a
+seeded shuffled free list, the pool slot of every token, and fp16 q/K/V values.
+It holds no attention, softmax or fp8-coding arithmetic, so the GPU path and the
+CPU oracle can both take their inputs from here without sharing any of the
+method.
+
+Shapes follow the pages' workloads:
+  * the block pool of one layer is ``[num_blocks, block_size, num_kv_heads,
+    head_dim]`` ("KV Cache memory core", section 2.2 code sketch);
+  * a sequence's ``block_table`` maps logical block j to a physical id, stacked
+    into a 2-D ``[num_seqs, max_num_blocks]`` tensor, and ``slot_mapping`` gives
+    each new token's absolute slot ``block_id * block_size + offset``
+    ("vLLM intro part 2", section 3.2);
+  * the number of blocks a sequence holds is ``cdiv(num_tokens, block_size)``
+    ("Paging saves no KV bytes", section 3).
+
+Random streams: ``SeedSequence(seed).spawn(6)`` gives, in this order, the
+children for lengths, free-list permutation, q, K, V and needles.  Large K/V
+draws are split into fixed 16K-token chunks, each with its own grandchild seed,
+so the bytes do not depend on how many threads fill them.
+"""
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import dataclasses
+import os
+from typing import Optional
+
+import numpy as np
+
+F16_NAN_BITS = np.uint16(0x7E00)   # quiet NaN in IEEE binary16
+E4M3_NAN_BYTE = np.uint8(0x7F)     # S.1111.111 is NaN in OCP e4m3fn
+E4M3_MAX = np.float32(448.0)       # largest finite OCP e4m3fn magnitude
+
+_CHUNK_TOKENS = 16384
+
+
+def cdiv(a: int, b: int) -> int:
+    """Ceiling division: blocks needed for ``a`` tokens at ``b`` tokens/block."""
+    return -(-int(a) // int(b))
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    seed: int
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    kv_dtype: str                    # "f16" or "fp8_e4m3fn"
+    scale: float                     # softmax scale (fp32 value)
+    k_scale: float                   # per-tensor fp8 scale (1.0 for f16)
+    v_scale: float
+    seq_lens: np.ndarray             # int32 [S]
+    block_tables: np.ndarray         # int32 [S, max_blocks]; padding -> pad_block
+    pad_block: int                   # physical id table padding points at
+    used_blocks: np.ndarray          # int32 ids holding at least one token
+    tok_k: np.ndarray                # float16 [T, Hkv, D] every context token's K
+    tok_v: np.ndarray                # float16 [T, Hkv, D]
+    tok_slot: np.ndarray             # int64 [T] absolute pool slot of each token
+    new_idx: np.ndarray              # int64 indices into tok_* written this step
+    q: np.ndarray                    # float16 [S, Hq, D]
+    partition_size: int = 0          # partition the workload names (0: none)
+    cow_pairs: Optional[np.ndarray] = None      # int64 [N, 2] (src, dst)
+    block_tables_before_cow: Optional[np.ndarray] = None
+    group_size: int = 1              # sequences forked from one prompt
+    prefix_tokens: int = 0
+    variant: str = "plain"
+    # where each sequence's tokens sit in tok_*: positions t < own_from[s] are a
+    # shared prompt starting at shared_start[s]; the rest start at own_start[s]
+    own_from: Optional[np.ndarray] = None
+    own_start: Optional[np.ndarray] = None
+    shared_start: Optional[np.ndarray] = None
+
+    def token_index(self, s: int, t: int) -> int:
+        if t < int(self.own_from[s]):
+            return int(self.shared_start[s]) + t
+        return int(self.own_start[s]) + t - int(self.own_from[s])
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.seq_lens.size else 0
+
+    @property
+    def gqa(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return 1 if self.kv_dtype == "fp8_e4m3fn" else 2
+
+    @property
+    def new_slots(self) -> np.ndarray:
+        return self.tok_slot[self.new_idx]
+
+
+# --------------------------------------------------------------------------
+# drawing helpers
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _normal_f16(seed_seq: np.random.SeedSequence, shape, parallel_axis_len: int) -> np.ndarray:
+    """N(0,1) drawn in fp32 and rounded to fp16, filled in fixed token chunks."""
+    out = np.empty(shape, dtype=np.float16)
+    n = parallel_axis_len
+    nchunks = max(1, cdiv(n, _CHUNK_TOKENS))
+    kids = seed_seq.spawn(nchunks)
+    row = int(np.prod(shape[1:])) if len(shape) > 1 else 1
+    flat = out.reshape(n, row)
+
+    def fill(i: int) -> None:
+        lo, hi = i * _CHUNK_TOKENS, min(n, (i + 1) * _CHUNK_TOKENS)
+        g = np.random.default_rng(kids[i])
+        flat[lo:hi] = g.standard_normal((hi - lo, row), dtype=np.float32).astype(np.float16)
+
+    if nchunks == 1:
+        fill(0)
+    else:
+        with _cf.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out
+
+
+def _amax_f32(a: np.ndarray) -> np.float32:
+    """max |a| over an fp16 array, as fp32 (exact: fp16 values are fp32 values)."""
+    n = a.shape[0]
+    nchunks = max(1, cdiv(n, _CHUNK_TOKENS))
+
+    def part(i: int) -> float:
+        lo, hi = i * _CHUNK_TOKENS, min(n, (i + 1) * _CHUNK_TOKENS)
+        return float(np.abs(a[lo:hi]).max())
+
+    with _cf.ThreadPoolExecutor(_threads()) as ex:
+        return np.float32(max(ex.map(part, range(nchunks))))
+
+
+class _FreeList:
+    """Physical ids popped in the order of a seeded permutation."""
+
+    def __init__(self, num_blocks: int, rng: np.random.Generator):
+        self.order = rng.permutation(num_blocks).astype(np.int64)
+        self.pos = 0
+
+    def take(self, n: int) -> np.ndarray:
+        if self.pos + n > self.order.size:
+            raise ValueError(f"pool exhausted: need {n}, have {self.order.size - self.pos}")
+        ids = self.order[self.pos:self.pos + n]
+        self.pos += n
+        return ids.copy()
+
+
+def _slots_for(table_row: np.ndarray, ntok: int, bs: int, start: int = 0) -> np.ndarray:
+    t = np.arange(start, start + ntok, dtype=np.int64)
+    return table_row[t // bs].astype(np.int64) * bs + (t % bs)
+
+
+def _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, lens, tables, pad_block,
+            tok_slot, new_idx, ss, partition_size=0, **extra) -> Workload:
+    T = int(tok_slot.size)
+    q = _normal_f16(ss[2], (S, Hq, D), S)
+    tok_k = _normal_f16(ss[3], (T, Hkv, D), T)
+    tok_v = _normal_f16(ss[4], (T, Hkv, D), T)
+    k_scale = v_scale = 1.0
+    if kv_dtype == "fp8_e4m3fn":
+        k_scale = float(_amax_f32(tok_k) / E4M3_MAX)
+        v_scale = float(_amax_f32(tok_v) / E4M3_MAX)
+    used = np.unique(tok_slot // bs).astype(np.int32)
+    return Workload(name=name, seed=seed, num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv,
+                    head_dim=D, block_size=bs, num_blocks=num_blocks, kv_dtype=kv_dtype,
+                    scale=float(np.float32(1.0) / np.sqrt(np.float32(D))),
+                    k_scale=k_scale, v_scale=v_scale, seq_lens=lens.astype(np.int32),
+                    block_tables=tables.astype(np.int32), pad_block=int(pad_block),
+                    used_blocks=used, tok_k=tok_k, tok_v=tok_v,
+                    tok_slot=tok_slot.astype(np.int64), new_idx=new_idx.astype(np.int64), q=q,
+                    partition_size=partition_size, **extra)
+
+
+def _independent(name, seed, lens, Hq, Hkv, D, bs, num_blocks, kv_dtype="f16",
+                 partition_size=0) -> Workload:
+    """Sequences with private blocks; the last token of each is this step's write."""
+    ss = np.random.SeedSequence(seed).spawn(6)
+    S = len(lens)
+    free = _FreeList(num_blocks, np.random.default_rng(ss[1]))
+    nb = [cdiv(n, bs) for n in lens]
+    max_blocks = max(1, max(nb))
+    blocks = [free.take(n) for n in nb]
+    pad_block = int(free.take(1)[0])          # table padding target (never a real block)
+    tables = np.full((S, max_blocks), pad_block, dtype=np.int64)
+    slots, new_idx, pos = [], [], 0
+    own_start = np.zeros(S, np.int64)
+    for s in range(S):
+        tables[s, :nb[s]] = blocks[s]
+        slots.append(_slots_for(tables[s], int(lens[s]), bs))
+        own_start[s] = pos
+        pos += int(lens[s])
+        if lens[s] > 0:
+            new_idx.append(pos - 1)
+    tok_slot = np.concatenate(slots) if slots else np.zeros(0, np.int64)
+    return _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, np.asarray(lens),
+                   tables, pad_block, tok_slot, np.asarray(new_idx, np.int64), ss,
+                   partition_size=partition_size, own_from=np.zeros(S, np.int64),
+                   own_start=own_start, shared_start=np.full(S, -1, np.int64))
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+
+
+def tiny(seed: int = 7201) -> Workload:
+    """4 sequences of lengths {1,17,33,100}; 8 query / 2 KV heads, head_dim 64,
+    block_size 16, a 64-block fp16 pool whose ids are a seeded permutation."""
+    return _independent("tiny", seed, [1, 17, 33, 100], 8, 2, 64, 16, 64)
+
+
+def llama3_8b_b64(seed: int = 7202) -> Workload:
+    """Llama-3-8B-shaped single-layer decode: 64 sequences, lengths uniform in
+    [512, 4096]; 32 query / 8 KV heads, head_dim 128, block_size 16; a
+    20,000-block fp16 pool from a shuffled free list; 64 new tokens written."""
+    ss = np.random.SeedSequence(seed).spawn(6)
+    lens = np.random.default_rng(ss[0]).integers(512, 4096, size=64, endpoint=True)
+    return _independent("llama3_8b_b64", seed, lens.tolist(), 32, 8, 128, 16, 20000)
+
+
+def qwen25_7b_8k(seed: int = 7203) -> Workload:
+    """Qwen2.5-7B-shaped decode at full context: 13 sequences x 8192 tokens
+    (512 blocks each); 28 query / 4 KV heads (GQA 7), head_dim 128, block_size
+    16, fp16; non-contiguous physical blocks; one slot write per sequence."""
+    return _independent("qwen25_7b_8k", seed, [8192] * 13, 28, 4, 128, 16, 8192)
+
+
+def long_fp8(seed: int = 7206) -> Workload:
+    """Long-context split-KV: 8 sequences x 131,072 tokens; 32 query / 8 KV
+    heads, head_dim 128, block_size 32; KV stored as OCP fp8 e4m3fn with a
+    per-tensor fp32 scale (K/V ~ N(0,1) before quantisation); 512-token
+    partitions followed by a log-sum-exp reduce; fp16 output."""
+    return _independent("long_fp8", seed, [131072] * 8, 32, 8, 128, 32, 36864,
+                        kv_dtype="fp8_e4m3fn", partition_size=512)
+
+
+def prefix_share(block_size: int = 16, seed: Optional[int] = None) -> Workload:
+    """Short requests with parallel-sampling prefix sharing: 1,024 sequences in
+    groups of 4 that share a 256-token prompt; tails of 1-40 tokens (717 of
+    them, 70%) or 100-300 tokens (307, 30%), assigned by a seeded shuffle;
+    32 query / 8 KV heads, head_dim 128, fp16.  On fork, child 0 of every group
+    takes a copy-on-write copy of the group's last prompt block (one
+    copy_blocks call with 256 pairs) and its table is retargeted to the copy."""
+    if seed is None:
+        seed = 7204 if block_size == 16 else 7205
+    ss = np.random.SeedSequence(seed).spawn(6)
+    rl = np.random.default_rng(ss[0])
+    n_groups, gsz, prefix = 256, 4, 256
+    S = n_groups * gsz
+    n_short = 717
+    tails = np.concatenate([rl.integers(1, 40, size=n_short, endpoint=True),
+                            rl.integers(100, 300, size=S - n_short, endpoint=True)])
+    tails = tails[rl.permutation(S)]
+    lens = prefix + tails
+    num_blocks = 12288 if block_size == 16 else 24576
+    free = _FreeList(num_blocks, np.random.default_rng(ss[1]))
+    npb = cdiv(prefix, block_size)
+    max_blocks = int(max(cdiv(int(n), block_size) for n in lens))
+    tables = np.zeros((S, max_blocks), dtype=np.int64)
+    slots, new_idx, pos = [], [], 0
+    prefix_blocks = []
+    own_start = np.zeros(S, np.int64)
+    shared_start = np.zeros(S, np.int64)
+    for gi in range(n_groups):
+        pb = free.take(npb)
+        prefix_blocks.append(pb)
+        slots.append(_slots_for(pb, prefix, block_size))
+        shared_start[gi * gsz:(gi + 1) * gsz] = pos
+        pos += prefix
+        for c in range(gsz):
+            s = gi * gsz + c
+            tail = int(tails[s])
+            own_start[s] = pos
+            first_tail_blk = prefix // block_size      # prompt is block aligned
+            ntail_blk = cdiv(int(lens[s]), block_size) - first_tail_blk
+            tables[s, :npb] = pb
+            tables[s, first_tail_blk:first_tail_blk + ntail_blk] = free.take(ntail_blk)
+            slots.append(_slots_for(tables[s], tail, block_size, start=prefix))
+            pos += tail
+            new_idx.append(pos - 1)
+    cow_dst = free.take(n_groups)
+    pad_block = int(free.take(1)[0])
+    for s in range(S):
+        nb = cdiv(int(lens[s]), block_size)
+        tables[s, nb:] = pad_block
+    before = tables.copy()
+    cow = np.zeros((n_groups, 2), dtype=np.int64)
+    for gi in range(n_groups):
+        src = int(prefix_blocks[gi][-1])
+        cow[gi] = (src, int(cow_dst[gi]))
+        tables[gi * gsz, npb - 1] = cow_dst[gi]
+    tok_slot = np.concatenate(slots)
+    return _finish(f"prefix_share_bs{block_size}", seed, S, 32, 8, 128, block_size, num_blocks,
+                   "f16", lens, tables, pad_block, tok_slot, np.asarray(new_idx, np.int64), ss,
+                   cow_pairs=cow, block_tables_before_cow=before.astype(np.int32),
+                   group_size=gsz, prefix_tokens=prefix,
+                   own_from=np.full(S, prefix, np.int64), own_start=own_start,
+                   shared_start=shared_start)
+
+
+CONFIGS = {
+    "tiny": tiny,
+    "llama3_8b_b64": llama3_8b_b64,
+    "qwen25_7b_8k": qwen25_7b_8k,
+    "prefix_share_bs16": lambda: prefix_share(16),
+    "prefix_share_bs8": lambda: prefix_share(8),
+    "long_fp8": long_fp8,
+}
+
+
+def custom(name: str, seed: int, lens, Hq: int, Hkv: int, D: int, bs: int,
+           num_blocks: Optional[int] = None, kv_dtype: str = "f16") -> Workload:
+    """Independent sequences of the given lengths (for edge cases and sweeps)."""
+    need = sum(cdiv(int(n), bs) for n in lens) + 1
+    if num_blocks is None:
+        num_blocks = max(need + 7, 2 * need)
+    return _independent(name, seed, list(lens), Hq, Hkv, D, bs, int(num_blocks),
+                        kv_dtype=kv_dtype)
+
+
+# --------------------------------------------------------------------------
+# structured variants (input construction; the method is untouched)
+
+
+def with_v_offset(w: Workload, c: float = 1.0) -> Workload:
+    """V += c on every token: the output must then sit near c."""
+    v = (w.tok_v.astype(np.float32) + np.float32(c)).astype(np.float16)
+    out = dataclasses.replace(w, tok_v=v, variant=f"v_offset{c:g}")
+    if w.kv_dtype == "fp8_e4m3fn":
+        out.v_scale = float(_amax_f32(v) / E4M3_MAX)
+    return out
+
+
+def needle_positions(w: Workload, s: int, partition: int = 512) -> list:
+    """Token positions that get a boosted key: the first and last slot of the
+    first block, both sides of a block and a partition boundary, and the last
+    valid slot."""
+    n = int(w.seq_lens[s])
+    bs = w.block_size
+    cand = {0, bs - 1, bs, partition - 1, partition, n - 1, (n // 2) // bs * bs}
+    return sorted(p for p in cand if 0 <= p < n)
+
+
+def with_needles(w: Workload, alpha: float = 64.0, seed_offset: int = 0) -> Workload:
+    """Plant keys aligned with one query head of the group (k = alpha * q_hat)
+    at one seeded position per (sequence, KV head), drawn from
+    needle_positions(); those heads then attend almost only to that token."""
+    ss = np.random.SeedSequence(w.seed + seed_offset).spawn(6)
+    rng = np.random.default_rng(ss[5])
+    k = w.tok_k.copy()
+    g = w.gqa
+    for s in range(w.num_seqs):
+        if w.seq_lens[s] == 0:
+            continue
+        pos = needle_positions(w, s, w.partition_size or 512)
+        for kh in range(w.num_kv_heads):
+            t = int(pos[rng.integers(len(pos))])
+            idx = w.token_index(s, t)
+            h = kh * g + int(rng.integers(g))
+            qv = w.q[s, h].astype(np.float32)
+            qn = qv / np.float32(np.linalg.norm(qv) + 1e-6)
+            k[idx, kh] = (np.float32(alpha) * qn).astype(np.float16)
+    out = dataclasses.replace(w, tok_k=k, variant="needles")
+    if w.kv_dtype == "fp8_e4m3fn":
+        out.k_scale = float(_amax_f32(k) / E4M3_MAX)
+    return out
+
+
+def poison_pool_bits(w: Workload) -> int:
+    """Bit pattern every unwritten pool element is filled with in poison runs."""
+    return int(E4M3_NAN_BYTE) if w.kv_dtype == "fp8_e4m3fn" else int(F16_NAN_BITS)
