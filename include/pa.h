@@ -1,0 +1,156 @@
+/*
+ * pa.h -- paged-attention decode for AMD MI355X (gfx950): the C ABI of libpa.so.
+ *
+ * The operation, as the pages state it:
+ *   - One layer's KV cache is a K pool and a V pool, each
+ *     [num_blocks, block_size, num_kv_heads, head_dim]; block_size tokens share
+ *     a block ("KV Cache memory core", section 2.2 layout sketch; "vLLM intro
+ *     part 2", section 3.1: one pool per layer, separate K and V blocks).
+ *   - A sequence's logical block j lives in physical block block_table[j]; the
+ *     tables of a batch are stacked into a 2-D [num_seqs, max_num_blocks]
+ *     array and handed to the kernel together with slot_mapping, the absolute
+ *     pool slot (block * block_size + offset) of every new token ("vLLM intro
+ *     part 2", section 3.2).
+ *   - Decode reads the blocks of block_table[seq] in order and scores the query
+ *     against each block's keys, softmax over all scores, then weights the
+ *     values ("KV Cache memory core", section 3, read path); scores are
+ *     scale * dot(q, k) and the softmax subtracts the running max ("vLLM intro
+ *     part 2", section 4.2); partial results of different blocks are merged
+ *     with the online-softmax rule ("PagedAttention & vLLM", PagedAttention
+ *     kernel steps).
+ *   - Query head h reads KV head h / (num_q_heads / num_kv_heads): consecutive
+ *     query heads share one KV head ("KV Cache memory core", section 4.2).
+ *   - Copy-on-write duplicates a whole block before a shared block is written
+ *     ("GPU memory & KV cache", copy-on-write steps and incident code).
+ *   - fp8 KV is quantised on write and dequantised inside the attention kernel
+ *     on read ("KV Cache memory core", section 4.4); the format is OCP e4m3fn
+ *     ("Paging saves no KV bytes", section 4) with one fp32 scale per pool.
+ *
+ * Conventions for every entry point:
+ *   - All pointers named as device pointers point to device memory the caller
+ *     owns.  The library allocates nothing, keeps no per-call state and never
+ *     synchronises: work is enqueued on the caller's stream and the call returns.
+ *   - Host-checkable arguments are validated before anything is launched; a
+ *     failed check returns a negative pa_status and launches nothing.  The
+ *     message is available from pa_last_error() on the same thread.
+ *   - Device contents are not validated.  Indices that would leave a buffer are
+ *     made harmless instead (see each function), so a bad table cannot fault
+ *     the GPU, but the affected outputs are then unspecified.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef HIP_INCLUDE_HIP_HIP_RUNTIME_API_H
+typedef struct ihipStream_t* hipStream_t; /* same type as HIP's own declaration */
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, bad size or shape                    */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim, block_size, dtype or GQA ratio not built  */
+  PA_ERR_ALIGNMENT = -3,   /* a pointer or stride is not 16-byte aligned          */
+  PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required          */
+  PA_ERR_HIP = -5          /* the HIP runtime rejected a launch                   */
+} pa_status;
+
+typedef enum {
+  PA_KV_F16 = 0,        /* IEEE binary16 elements                                */
+  PA_KV_FP8_E4M3FN = 1  /* OCP e4m3fn bytes; value = e4m3(byte) * pool scale      */
+} pa_kv_dtype;
+
+/* One layer's KV pool.
+ * Element (block b, slot o, KV head h, dim d) of the K pool is at byte
+ *   k_base + b * block_stride + ((o * num_kv_heads + h) * head_dim + d) * elem_bytes
+ * and likewise in the V pool.  block_stride_bytes = 0 means dense blocks,
+ * block_size * num_kv_heads * head_dim * elem_bytes; a larger stride (a
+ * multiple of 16) lets K and V blocks interleave in one allocation.
+ * Supported: head_dim 64 or 128; block_size 8, 16 or 32; k_base, v_base 16-byte
+ * aligned.  k_scale / v_scale are the per-pool fp8 scales (ignored for f16). */
+typedef struct {
+  void* k_base;                /* device */
+  void* v_base;                /* device */
+  int64_t num_blocks;
+  int64_t block_stride_bytes;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;               /* pa_kv_dtype */
+  float k_scale;
+  float v_scale;
+} pa_kv_pool;
+
+/* Write num_tokens new tokens into their slots (the write side of slot_mapping,
+ * "vLLM intro part 2", section 3.2).
+ *   k_new, v_new  device, [num_tokens, num_kv_heads, head_dim] binary16, contiguous,
+ *                 16-byte aligned.
+ *   slot_mapping  device, [num_tokens] int64; token i goes to block
+ *                 slot / block_size, offset slot % block_size.  A negative slot,
+ *                 or one at or beyond num_blocks * block_size, skips the token.
+ *                 Slots must be distinct within one call.
+ * f16 pools receive the bits unchanged.  fp8 pools receive
+ * e4m3fn(float(x) / scale), rounded to nearest even and saturated to +-448
+ * (NaN stays NaN).  num_tokens == 0 is a no-op. */
+int pa_reshape_and_cache(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping, int64_t num_tokens, hipStream_t stream);
+
+/* Copy whole blocks, K and V, for copy-on-write ("GPU memory & KV cache",
+ * copy_blocks(blk, new) in the incident fix).
+ *   block_mapping device, [num_pairs, 2] int64 of (src, dst).  Destinations must
+ *                 be distinct and must not also be sources in the same call.
+ *                 Pairs with an id outside [0, num_blocks) are skipped. */
+int pa_copy_blocks(const pa_kv_pool* pool, const int64_t* block_mapping, int64_t num_pairs,
+                   hipStream_t stream);
+
+/* The partition size pa_decode will use for these arguments: 0 for the single
+ * pass (one workgroup per sequence and KV head), otherwise the number of tokens
+ * per partition of the split pass.  partition_size follows pa_decode: -1 forces
+ * the single pass, 0 lets the library choose, > 0 (a multiple of 16) forces the
+ * split pass with that size.  Returns a negative pa_status on bad arguments. */
+int32_t pa_decode_plan(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_seq_len, int32_t partition_size);
+
+/* Bytes of workspace pa_decode needs for these arguments (0 for the single
+ * pass).  Returns 0 as well when the arguments are invalid; pa_decode then
+ * reports the error. */
+size_t pa_decode_workspace_size(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_seq_len, int32_t partition_size);
+
+/* Decode attention for one new query token per sequence.
+ *   out           device, [num_seqs, num_q_heads, head_dim] binary16 (written).
+ *   q             device, [num_seqs, num_q_heads, head_dim] binary16.
+ *   block_tables  device, [num_seqs, max_blocks_per_seq] int32 physical ids; only
+ *                 the first cdiv(seq_lens[s], block_size) entries of a row are
+ *                 read.  Ids are clamped into [0, num_blocks).
+ *   seq_lens      device, [num_seqs] int32 context lengths, including the token
+ *                 this step wrote; each must be <= max_seq_len and
+ *                 <= max_blocks_per_seq * block_size (larger values are clamped).
+ *                 A length of 0 gives an all-zero output row.
+ *   max_seq_len   host upper bound of seq_lens; sizes the grid and workspace.
+ *   scale         softmax scale applied to q.k (e.g. 1/sqrt(head_dim)).
+ *   partition_size  -1 single pass, 0 library choice, > 0 split pass with that
+ *                 many tokens per partition (multiple of 16) followed by a
+ *                 log-sum-exp reduce of the partitions.
+ *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes,
+ *                 16-byte aligned; may be NULL when that size is 0.
+ * num_q_heads must be a multiple of num_kv_heads with a ratio of at most 16.
+ * Outputs are bitwise reproducible for the same inputs and do not depend on
+ * which physical ids hold the blocks. */
+int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs,
+              int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_size,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

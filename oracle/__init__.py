@@ -33,8 +33,8 @@ class OrcPool(C.Structure):
 
 
 def build(verbose: bool = False) -> str:
-    from . import build as _b
-    return _b.build(verbose=verbose)
+    from . import build_lib
+    return build_lib.build(verbose=verbose)
 
 
 def lib():

@@ -1,0 +1,224 @@
+// pa_api.hip -- the extern "C" entry points of libpa.so (declared in include/pa.h).
+//
+// Host side only: validate what the host can see, resolve the pool geometry,
+// choose single pass or split pass, and enqueue the kernels on the caller's
+// stream.  Nothing here allocates device memory or synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
+  if (!p) return fail(PA_ERR_INVALID_ARG, "pool descriptor is NULL");
+  if (!p->k_base || !p->v_base) return fail(PA_ERR_INVALID_ARG, "pool k_base/v_base is NULL");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", p->head_dim);
+  if (p->block_size != 8 && p->block_size != 16 && p->block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (8, 16, 32)", p->block_size);
+  if (p->dtype != PA_KV_F16 && p->dtype != PA_KV_FP8_E4M3FN)
+    return fail(PA_ERR_UNSUPPORTED, "kv dtype %d not supported", p->dtype);
+  if (p->num_kv_heads < 1 || p->num_kv_heads > 4096)
+    return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d out of range", p->num_kv_heads);
+  if (p->num_blocks < 1 || p->num_blocks > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks %lld out of range", (long long)p->num_blocks);
+  if (!aligned16(p->k_base) || !aligned16(p->v_base))
+    return fail(PA_ERR_ALIGNMENT, "pool bases must be 16-byte aligned");
+  const int32_t e = p->dtype == PA_KV_F16 ? 2 : 1;
+  const int64_t row = (int64_t)p->num_kv_heads * p->head_dim * e;
+  const int64_t dense = row * p->block_size;
+  const int64_t stride = p->block_stride_bytes ? p->block_stride_bytes : dense;
+  if (stride < dense)
+    return fail(PA_ERR_INVALID_ARG, "block_stride_bytes %lld smaller than a block (%lld)",
+                (long long)stride, (long long)dense);
+  if (stride % 16) return fail(PA_ERR_ALIGNMENT, "block_stride_bytes must be a multiple of 16");
+  if (row > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "token row too large");
+  if (p->dtype == PA_KV_FP8_E4M3FN &&
+      (!(p->k_scale > 0.f) || !(p->v_scale > 0.f) || !std::isfinite(p->k_scale) ||
+       !std::isfinite(p->v_scale)))
+    return fail(PA_ERR_INVALID_ARG, "fp8 pools need finite positive k_scale and v_scale");
+  g->k = (char*)p->k_base;
+  g->v = (char*)p->v_base;
+  g->num_blocks = p->num_blocks;
+  g->block_stride = stride;
+  g->row_stride = (int32_t)row;
+  g->block_size = p->block_size;
+  g->num_kv_heads = p->num_kv_heads;
+  g->head_dim = p->head_dim;
+  g->elem_bytes = e;
+  g->k_scale = p->dtype == PA_KV_F16 ? 1.f : p->k_scale;
+  g->v_scale = p->dtype == PA_KV_F16 ? 1.f : p->v_scale;
+  return PA_OK;
+}
+
+// Single pass when there are enough (sequence, KV head) units to occupy the
+// GPU and contexts are short; otherwise split contexts into partitions so that
+// the grid holds a few thousand workgroups and long and short sequences cost
+// the same per workgroup.
+int32_t choose_partition(int64_t units, int32_t max_seq_len) {
+  if (max_seq_len <= 256) return 0;
+  if (units >= 2048 && max_seq_len <= 2048) return 0;
+  int32_t P = 512;
+  while (P > 256 && units * cdiv64(max_seq_len, P) < 2048) P /= 2;
+  return P;
+}
+
+int plan(const pa_kv_pool* pool, int32_t S, int32_t Hq, int32_t max_seq_len, int32_t req,
+         pa::PoolGeom* g, int32_t* part) {
+  int st = check_pool(pool, g);
+  if (st) return st;
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", S);
+  if (Hq < 1 || Hq % g->num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", Hq,
+                g->num_kv_heads);
+  if (Hq / g->num_kv_heads > 16)
+    return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d > 16", Hq / g->num_kv_heads);
+  if (max_seq_len < 0) return fail(PA_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
+  if (req < -1) return fail(PA_ERR_INVALID_ARG, "partition_size %d invalid", req);
+  if (req > 0 && req % 16)
+    return fail(PA_ERR_INVALID_ARG, "partition_size %d is not a multiple of 16", req);
+  const int64_t units = (int64_t)S * g->num_kv_heads;
+  int32_t P = req == -1 ? 0 : (req > 0 ? req : choose_partition(units, max_seq_len));
+  if (P > 0 && max_seq_len <= 0) P = 0;
+  const int64_t grid = units * (P > 0 ? cdiv64(max_seq_len, P) : 1);
+  if (grid > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "grid of %lld workgroups too large",
+                                    (long long)grid);
+  *part = P;
+  return PA_OK;
+}
+
+size_t workspace_bytes_for(int64_t S, int64_t Hq, int64_t D, int64_t num_parts) {
+  const int64_t rows = S * Hq * num_parts;
+  const int64_t ml = ((rows * 8) + 255) / 256 * 256;
+  return (size_t)(ml + rows * D * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_reshape_and_cache(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping, int64_t num_tokens, hipStream_t stream) {
+  pa::PoolGeom g;
+  int st = check_pool(pool, &g);
+  if (st) return st;
+  if (num_tokens < 0 || num_tokens > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_tokens %lld out of range", (long long)num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "k_new, v_new and slot_mapping must be non-NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_ALIGNMENT, "k_new and v_new must be 16-byte aligned");
+  if (hipError_t e = pa::launch_reshape_and_cache(g, (const _Float16*)k_new,
+                                                  (const _Float16*)v_new, slot_mapping,
+                                                  num_tokens, stream))
+    return fail(PA_ERR_HIP, "reshape_and_cache launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_copy_blocks(const pa_kv_pool* pool, const int64_t* block_mapping, int64_t num_pairs,
+                   hipStream_t stream) {
+  pa::PoolGeom g;
+  int st = check_pool(pool, &g);
+  if (st) return st;
+  if (num_pairs < 0 || num_pairs > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_pairs %lld out of range", (long long)num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!block_mapping) return fail(PA_ERR_INVALID_ARG, "block_mapping is NULL");
+  if (hipError_t e = pa::launch_copy_blocks(g, block_mapping, num_pairs, stream))
+    return fail(PA_ERR_HIP, "copy_blocks launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int32_t pa_decode_plan(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_seq_len, int32_t partition_size) {
+  pa::PoolGeom g;
+  int32_t P = 0;
+  int st = plan(pool, num_seqs, num_q_heads, max_seq_len, partition_size, &g, &P);
+  return st ? st : P;
+}
+
+size_t pa_decode_workspace_size(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_seq_len, int32_t partition_size) {
+  pa::PoolGeom g;
+  int32_t P = 0;
+  if (plan(pool, num_seqs, num_q_heads, max_seq_len, partition_size, &g, &P) || P == 0) return 0;
+  return workspace_bytes_for(num_seqs, num_q_heads, g.head_dim, cdiv64(max_seq_len, P));
+}
+
+int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs,
+              int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_size,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  pa::PoolGeom g;
+  int32_t P = 0;
+  int st = plan(pool, num_seqs, num_q_heads, max_seq_len, partition_size, &g, &P);
+  if (st) return st;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !block_tables || !seq_lens)
+    return fail(PA_ERR_INVALID_ARG, "out, q, block_tables and seq_lens must be non-NULL");
+  if (!aligned16(out) || !aligned16(q))
+    return fail(PA_ERR_ALIGNMENT, "q and out must be 16-byte aligned");
+  if (max_blocks_per_seq < 1)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+
+  pa::DecodeArgs a{};
+  a.k = g.k;
+  a.v = g.v;
+  a.block_stride = g.block_stride;
+  a.row_stride = g.row_stride;
+  a.num_kv_heads = g.num_kv_heads;
+  a.num_blocks_m1 = (int32_t)(g.num_blocks - 1);
+  a.num_q_heads = num_q_heads;
+  a.gqa = num_q_heads / g.num_kv_heads;
+  a.q = (const _Float16*)q;
+  a.out = (_Float16*)out;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  const int64_t table_cap = (int64_t)max_blocks_per_seq * g.block_size;
+  a.len_cap = (int32_t)(table_cap < max_seq_len ? table_cap : max_seq_len);
+  a.seq_lens = seq_lens;
+  a.score_scale = (float)((double)scale * 1.4426950408889634 * (double)g.k_scale);
+  a.v_scale = g.v_scale;
+  if (P > 0) {
+    a.part_tokens = P;
+    a.num_parts = (int32_t)cdiv64(max_seq_len, P);
+    const size_t need = workspace_bytes_for(num_seqs, num_q_heads, g.head_dim, a.num_parts);
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "split pass needs %zu workspace bytes, got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(PA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    const int64_t rows = (int64_t)num_seqs * num_q_heads * a.num_parts;
+    a.ws_ml = (float2*)workspace;
+    a.ws_o = (float*)((char*)workspace + ((rows * 8) + 255) / 256 * 256);
+  }
+  if (hipError_t e = pa::launch_decode(a, num_seqs, g.head_dim, g.block_size,
+                                       g.elem_bytes == 1, P > 0, stream))
+    return fail(PA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// pa_cache.hip -- the write side of the paged KV cache on gfx950.
+//
+//   rc_scatter   : slot_mapping write of new tokens ("vLLM intro part 2",
+//                  section 3.2: every new token has an absolute pool slot
+//                  block * block_size + offset; decode appends one per step).
+//   copy_blocks  : whole-block copy for copy-on-write ("GPU memory & KV cache",
+//                  copy_blocks(blk, new) before the table is retargeted).
+//
+// Both are pure data movement: a token row (num_kv_heads * head_dim elements)
+// is contiguous in k_new and in its pool slot, and a block is contiguous in the
+// pool, so every lane moves 16 bytes per access and a wavefront covers 1 KiB.
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+// fp32 -> OCP e4m3fn by field arithmetic on the fp32 bits: round to nearest
+// even, saturate to +-448 (infinities included), keep NaN as S.1111.111.
+__device__ __forceinline__ uint32_t e4m3fn_from_f32(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;        // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;       // |y| >= 448: largest finite
+  if (a < 0x3C800000u) {                           // |y| < 2^-6: steps of 2^-9
+    const float n = rintf(__uint_as_float(a) * 512.0f);   // exact scaling, RNE
+    return sign | (uint32_t)n;                     // 8 lands on the smallest normal
+  }
+  uint32_t code = (a >> 20) - (120u << 3);         // rebias exponent, keep 3 mantissa bits
+  const uint32_t rest = a & 0xFFFFFu;
+  code += (rest > 0x80000u) || (rest == 0x80000u && (code & 1u));
+  return sign | code;
+}
+
+// One workgroup per token.  Threads [0, n16) move K, [n16, 2*n16) move V, where
+// n16 = row bytes / 16 of the binary16 source.
+__global__ __launch_bounds__(256) void rc_scatter_f16(PoolGeom g, const uint4* __restrict__ k_new,
+                                                      const uint4* __restrict__ v_new,
+                                                      const int64_t* __restrict__ slots,
+                                                      int32_t n16) {
+  const int64_t i = blockIdx.x;
+  const int64_t slot = slots[i];
+  const int64_t cap = g.num_blocks * g.block_size;
+  if (slot < 0 || slot >= cap) return;
+  const int64_t blk = slot / g.block_size;
+  const int32_t off = (int32_t)(slot - blk * g.block_size);
+  const int64_t dst_off = blk * g.block_stride + (int64_t)off * g.row_stride;
+  for (int t = threadIdx.x; t < 2 * n16; t += blockDim.x) {
+    const bool is_v = t >= n16;
+    const int c = is_v ? t - n16 : t;
+    const uint4* src = (is_v ? v_new : k_new) + i * n16 + c;
+    uint4* dst = (uint4*)((is_v ? g.v : g.k) + dst_off) + c;
+    *dst = *src;
+  }
+}
+
+// fp8 pools: each thread reads 8 binary16 values (16 B) and writes 8 bytes.
+__global__ __launch_bounds__(256) void rc_scatter_fp8(PoolGeom g, const uint4* __restrict__ k_new,
+                                                      const uint4* __restrict__ v_new,
+                                                      const int64_t* __restrict__ slots,
+                                                      int32_t n16) {
+  const int64_t i = blockIdx.x;
+  const int64_t slot = slots[i];
+  const int64_t cap = g.num_blocks * g.block_size;
+  if (slot < 0 || slot >= cap) return;
+  const int64_t blk = slot / g.block_size;
+  const int32_t off = (int32_t)(slot - blk * g.block_size);
+  const int64_t dst_off = blk * g.block_stride + (int64_t)off * g.row_stride;
+  for (int t = threadIdx.x; t < 2 * n16; t += blockDim.x) {
+    const bool is_v = t >= n16;
+    const int c = is_v ? t - n16 : t;
+    const float scale = is_v ? g.v_scale : g.k_scale;
+    const uint4 x = ((is_v ? v_new : k_new) + i * n16)[c];
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint16_t hb = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+      const float xf = (float)__builtin_bit_cast(_Float16, hb);
+      packed[j >> 2] |= e4m3fn_from_f32(xf / scale) << (8 * (j & 3));
+    }
+    uint2* dst = (uint2*)((is_v ? g.v : g.k) + dst_off) + c;
+    *dst = make_uint2(packed[0], packed[1]);
+  }
+}
+
+// Grid: (pairs, 2 pools, chunks of 4 KiB); 256 threads x 16 B per chunk.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(PoolGeom g,
+                                                          const int64_t* __restrict__ pairs,
+                                                          int64_t block_bytes) {
+  const int64_t p = blockIdx.x;
+  const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+  if (src < 0 || dst < 0 || src >= g.num_blocks || dst >= g.num_blocks) return;
+  char* base = blockIdx.y ? g.v : g.k;
+  const uint4* s = (const uint4*)(base + src * g.block_stride);
+  uint4* d = (uint4*)(base + dst * g.block_stride);
+  const int64_t n16 = block_bytes / 16;
+  for (int64_t c = (int64_t)blockIdx.z * blockDim.x + threadIdx.x; c < n16;
+       c += (int64_t)gridDim.z * blockDim.x)
+    d[c] = s[c];
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const PoolGeom& g, const _Float16* k_new,
+                                    const _Float16* v_new, const int64_t* slots, int64_t T,
+                                    hipStream_t stream) {
+  const int32_t n16 = g.num_kv_heads * g.head_dim * 2 / 16;   // 16-B chunks per source row
+  const int threads = 2 * n16 < 256 ? ((2 * n16 + 63) / 64) * 64 : 256;
+  if (g.elem_bytes == 2)
+    hipLaunchKernelGGL(rc_scatter_f16, dim3((uint32_t)T), dim3(threads), 0, stream, g,
+                       (const uint4*)k_new, (const uint4*)v_new, slots, n16);
+  else
+    hipLaunchKernelGGL(rc_scatter_fp8, dim3((uint32_t)T), dim3(threads), 0, stream, g,
+                       (const uint4*)k_new, (const uint4*)v_new, slots, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const PoolGeom& g, const int64_t* pairs, int64_t n,
+                              hipStream_t stream) {
+  const int64_t block_bytes =
+      (int64_t)g.block_size * g.num_kv_heads * g.head_dim * g.elem_bytes;
+  const int64_t chunks = (block_bytes + 4095) / 4096;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((uint32_t)n, 2, (uint32_t)chunks), dim3(256), 0,
+                     stream, g, pairs, block_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,56 @@
+// pa_internal.h -- argument blocks and launchers shared by the HIP sources of
+// libpa.so.  Not installed; the public interface is include/pa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Resolved geometry of one pool, computed on the host from pa_kv_pool.
+struct PoolGeom {
+  char* k;
+  char* v;
+  int64_t num_blocks;
+  int64_t block_stride;  // bytes between consecutive blocks
+  int32_t row_stride;    // bytes between consecutive slots of a block (Hkv*D*e)
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t elem_bytes;    // 2: binary16, 1: e4m3fn
+  float k_scale;
+  float v_scale;
+};
+
+struct DecodeArgs {
+  const char* k;
+  const char* v;
+  int64_t block_stride;
+  int32_t row_stride;
+  int32_t num_kv_heads;
+  int32_t num_blocks_m1;      // largest valid physical id
+  int32_t num_q_heads;
+  int32_t gqa;                // query heads per KV head
+  const _Float16* q;
+  _Float16* out;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  int32_t len_cap;            // min(max_seq_len, max_blocks * block_size)
+  const int32_t* seq_lens;
+  float score_scale;          // scale * log2(e) * k_scale: scores in log2 units
+  float v_scale;
+  int32_t part_tokens;        // split pass: tokens per partition
+  int32_t num_parts;          // split pass: partitions per (sequence, KV head)
+  float* ws_o;                // split pass: [S][Hq][num_parts][D] normalised partials
+  float2* ws_ml;              // split pass: [S][Hq][num_parts] (max in log2 units, sum)
+};
+
+hipError_t launch_reshape_and_cache(const PoolGeom& g, const _Float16* k_new,
+                                    const _Float16* v_new, const int64_t* slots, int64_t T,
+                                    hipStream_t stream);
+hipError_t launch_copy_blocks(const PoolGeom& g, const int64_t* pairs, int64_t n,
+                              hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int32_t num_seqs, int32_t head_dim,
+                         int32_t block_size, bool fp8, bool split, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,190 @@
+"""ctypes binding of libpa.so: same entry-point names as include/pa.h.
+
+Argument marshalling only -- every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory and the stream.  Loading fails
+loudly if libpa.so has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_ALIGNMENT, PA_ERR_WORKSPACE, PA_ERR_HIP = \
+    0, -1, -2, -3, -4, -5
+PA_KV_F16, PA_KV_FP8_E4M3FN = 0, 1
+_DTYPES = {"f16": PA_KV_F16, "fp8_e4m3fn": PA_KV_FP8_E4M3FN}
+
+EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
+           "pa_decode_workspace_size", "pa_decode", "pa_last_error")
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libpa status {status}: {msg}")
+        self.status = status
+
+
+class pa_kv_pool(C.Structure):
+    _fields_ = [
+        ("k_base", C.c_void_p), ("v_base", C.c_void_p),
+        ("num_blocks", C.c_int64), ("block_stride_bytes", C.c_int64),
+        ("block_size", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+        ("dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
+    ]
+
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Load libpa.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        P, I32, I64, PP = C.c_void_p, C.c_int32, C.c_int64, C.POINTER(pa_kv_pool)
+        L.pa_reshape_and_cache.restype = C.c_int
+        L.pa_reshape_and_cache.argtypes = [PP, P, P, P, I64, P]
+        L.pa_copy_blocks.restype = C.c_int
+        L.pa_copy_blocks.argtypes = [PP, P, I64, P]
+        L.pa_decode_plan.restype = I32
+        L.pa_decode_plan.argtypes = [PP, I32, I32, I32, I32]
+        L.pa_decode_workspace_size.restype = C.c_size_t
+        L.pa_decode_workspace_size.argtypes = [PP, I32, I32, I32, I32]
+        L.pa_decode.restype = C.c_int
+        L.pa_decode.argtypes = [PP, P, P, I32, I32, P, I32, P, I32, C.c_float, I32, P, C.c_size_t,
+                                P]
+        L.pa_last_error.restype = C.c_char_p
+        L.pa_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def pa_last_error() -> str:
+    return load().pa_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        raise PaError(status, pa_last_error())
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+class KVPool:
+    """One layer's K and V pools, [num_blocks, block_size, num_kv_heads,
+    head_dim] each, in device memory owned by torch."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, block_size: int, num_kv_heads: int,
+                 head_dim: int, kv_dtype: str = "f16", k_scale: float = 1.0,
+                 v_scale: float = 1.0, num_blocks: Optional[int] = None,
+                 block_stride_bytes: int = 0):
+        self.k, self.v = k, v
+        self.block_size, self.num_kv_heads, self.head_dim = block_size, num_kv_heads, head_dim
+        self.kv_dtype = kv_dtype
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        self.num_blocks = int(num_blocks if num_blocks is not None else k.shape[0])
+        self.block_stride_bytes = int(block_stride_bytes)
+        self.desc = pa_kv_pool(k.data_ptr(), v.data_ptr(), self.num_blocks,
+                               self.block_stride_bytes, block_size, num_kv_heads, head_dim,
+                               _DTYPES[kv_dtype], self.k_scale, self.v_scale)
+
+    @classmethod
+    def allocate(cls, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+                 kv_dtype: str = "f16", k_scale: float = 1.0, v_scale: float = 1.0,
+                 device="cuda", fill_bits: Optional[int] = None) -> "KVPool":
+        tdt = torch.uint8 if kv_dtype == "fp8_e4m3fn" else torch.int16
+        shape = (num_blocks, block_size, num_kv_heads, head_dim)
+        k = torch.empty(shape, dtype=tdt, device=device)
+        v = torch.empty(shape, dtype=tdt, device=device)
+        if fill_bits is not None:
+            fb = fill_bits if kv_dtype == "fp8_e4m3fn" else (fill_bits - 65536 if fill_bits >= 32768
+                                                            else fill_bits)
+            k.fill_(fb)
+            v.fill_(fb)
+        return cls(k, v, block_size, num_kv_heads, head_dim, kv_dtype, k_scale, v_scale)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 1 if self.kv_dtype == "fp8_e4m3fn" else 2
+
+
+def pa_reshape_and_cache(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
+                         slot_mapping: torch.Tensor, stream=None) -> None:
+    T = int(slot_mapping.numel())
+    if k_new.shape != (T, pool.num_kv_heads, pool.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [num_tokens, num_kv_heads, head_dim]")
+    _check(load().pa_reshape_and_cache(
+        C.byref(pool.desc), _dev(k_new, torch.float16, "k_new"),
+        _dev(v_new, torch.float16, "v_new"), _dev(slot_mapping, torch.int64, "slot_mapping"),
+        T, _stream(stream)))
+
+
+def pa_copy_blocks(pool: KVPool, block_mapping: torch.Tensor, stream=None) -> None:
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [num_pairs, 2]")
+    _check(load().pa_copy_blocks(C.byref(pool.desc),
+                                 _dev(block_mapping, torch.int64, "block_mapping"),
+                                 int(block_mapping.shape[0]), _stream(stream)))
+
+
+def pa_decode_plan(pool: KVPool, num_seqs: int, num_q_heads: int, max_seq_len: int,
+                   partition_size: int = 0) -> int:
+    r = load().pa_decode_plan(C.byref(pool.desc), num_seqs, num_q_heads, max_seq_len,
+                              partition_size)
+    if r < 0:
+        raise PaError(r, pa_last_error())
+    return int(r)
+
+
+def pa_decode_workspace_size(pool: KVPool, num_seqs: int, num_q_heads: int, max_seq_len: int,
+                             partition_size: int = 0) -> int:
+    return int(load().pa_decode_workspace_size(C.byref(pool.desc), num_seqs, num_q_heads,
+                                               max_seq_len, partition_size))
+
+
+def alloc_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_seq_len: int,
+                    partition_size: int = 0, device="cuda") -> Optional[torch.Tensor]:
+    n = pa_decode_workspace_size(pool, num_seqs, num_q_heads, max_seq_len, partition_size)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def pa_decode(pool: KVPool, out: torch.Tensor, q: torch.Tensor, block_tables: torch.Tensor,
+              seq_lens: torch.Tensor, max_seq_len: int, scale: float, partition_size: int = 0,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    S, Hq, D = q.shape
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape [num_seqs, num_q_heads, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], seq_lens [num_seqs]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, workspace.dtype, "workspace"), workspace.numel() * \
+            workspace.element_size()
+    _check(load().pa_decode(
+        C.byref(pool.desc), _dev(out, torch.float16, "out"), _dev(q, torch.float16, "q"), S, Hq,
+        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+        _dev(seq_lens, torch.int32, "seq_lens"), int(max_seq_len), C.c_float(scale),
+        int(partition_size), ws_ptr, ws_bytes, _stream(stream)))

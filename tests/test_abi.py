@@ -1,0 +1,139 @@
+"""The C ABI of libpa.so on the CPU: every symbol include/pa.h declares is
+exported, and host-side validation rejects bad arguments before any launch.
+No compute call is made here (no GPU in this suite); the fake device pointers
+below are never dereferenced because validation fails or nothing is launched.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_72_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def so():
+    if not os.path.exists(L.LIB_PATH):
+        from paged_kv_cache_72_amd import build
+        build.build()
+    return L.load()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_bound_entry_points():
+    assert set(_declared_functions()) == set(L.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(so):
+    for name in _declared_functions():
+        assert hasattr(so, name), f"{name} not exported by libpa.so"
+
+
+def _pool(**kw):
+    d = dict(k_base=FAKE, v_base=FAKE + (1 << 20), num_blocks=1024, block_stride_bytes=0,
+             block_size=16, num_kv_heads=8, head_dim=128, dtype=L.PA_KV_F16, k_scale=1.0,
+             v_scale=1.0)
+    d.update(kw)
+    return L.pa_kv_pool(**d)
+
+
+def _decode(so, pool, S=4, Hq=32, max_len=100, part=0, ws=None, ws_bytes=0, **kw):
+    args = dict(out=FAKE, q=FAKE, bt=FAKE, maxb=64, lens=FAKE, scale=0.088)
+    args.update(kw)
+    return so.pa_decode(C.byref(pool) if pool is not None else None, args["out"], args["q"], S,
+                        Hq, args["bt"], args["maxb"], args["lens"], max_len,
+                        C.c_float(args["scale"]), part, ws, ws_bytes, None)
+
+
+def test_null_pool_rejected(so):
+    assert _decode(so, None) == L.PA_ERR_INVALID_ARG
+    assert "NULL" in L.pa_last_error()
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, L.PA_ERR_UNSUPPORTED),
+    ("block_size", 64, L.PA_ERR_UNSUPPORTED),
+    ("dtype", 7, L.PA_ERR_UNSUPPORTED),
+    ("k_base", FAKE + 8, L.PA_ERR_ALIGNMENT),
+    ("block_stride_bytes", 1000, L.PA_ERR_INVALID_ARG),
+    ("block_stride_bytes", 32768 + 8, L.PA_ERR_ALIGNMENT),
+    ("num_kv_heads", 0, L.PA_ERR_INVALID_ARG),
+    ("num_blocks", 0, L.PA_ERR_INVALID_ARG),
+])
+def test_bad_pool_fields(so, field, value, code):
+    assert _decode(so, _pool(**{field: value})) == code
+
+
+def test_fp8_pool_needs_positive_scales(so):
+    assert _decode(so, _pool(dtype=L.PA_KV_FP8_E4M3FN, k_scale=0.0)) == L.PA_ERR_INVALID_ARG
+
+
+def test_head_ratio_checks(so):
+    assert _decode(so, _pool(), Hq=30) == L.PA_ERR_INVALID_ARG        # 30 % 8 != 0
+    assert _decode(so, _pool(num_kv_heads=1), Hq=32) == L.PA_ERR_UNSUPPORTED   # ratio 32 > 16
+
+
+def test_partition_size_checks(so):
+    assert _decode(so, _pool(), part=100) == L.PA_ERR_INVALID_ARG     # not a multiple of 16
+    assert _decode(so, _pool(), part=-2) == L.PA_ERR_INVALID_ARG
+
+
+def test_split_pass_needs_workspace(so):
+    assert _decode(so, _pool(), part=256, max_len=4096) == L.PA_ERR_WORKSPACE
+    need = so.pa_decode_workspace_size(C.byref(_pool()), 4, 32, 4096, 256)
+    assert need > 0
+    assert _decode(so, _pool(), part=256, max_len=4096, ws=FAKE, ws_bytes=need - 1) == \
+        L.PA_ERR_WORKSPACE
+
+
+def test_misaligned_q_rejected(so):
+    assert _decode(so, _pool(), q=FAKE + 2) == L.PA_ERR_ALIGNMENT
+
+
+def test_nothing_to_do_is_ok_without_launch(so):
+    p = _pool()
+    assert _decode(so, p, S=0) == L.PA_OK
+    assert so.pa_reshape_and_cache(C.byref(p), FAKE, FAKE, FAKE, 0, None) == L.PA_OK
+    assert so.pa_copy_blocks(C.byref(p), FAKE, 0, None) == L.PA_OK
+
+
+def test_reshape_and_cache_arg_checks(so):
+    p = _pool()
+    assert so.pa_reshape_and_cache(C.byref(p), None, FAKE, FAKE, 4, None) == L.PA_ERR_INVALID_ARG
+    assert so.pa_reshape_and_cache(C.byref(p), FAKE + 4, FAKE, FAKE, 4, None) == \
+        L.PA_ERR_ALIGNMENT
+    assert so.pa_reshape_and_cache(C.byref(p), FAKE, FAKE, FAKE, -1, None) == \
+        L.PA_ERR_INVALID_ARG
+    assert so.pa_copy_blocks(C.byref(p), None, 3, None) == L.PA_ERR_INVALID_ARG
+
+
+def test_workspace_size_formula(so):
+    p = _pool()
+    S, Hq, D, P, T = 64, 32, 128, 512, 4096
+    rows = S * Hq * (T // P)
+    ml = (rows * 8 + 255) // 256 * 256
+    assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, P) == ml + rows * D * 4
+    assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, -1) == 0
+
+
+@pytest.mark.parametrize("S,Hkv,Hq,bs,maxlen,expect", [
+    (4, 2, 8, 16, 100, 0),          # tiny: single pass
+    (64, 8, 32, 16, 4096, 512),     # Llama-3-8B-shaped batch 64
+    (13, 4, 28, 16, 8192, 256),     # Qwen2.5-7B-shaped, 13 x 8k
+    (1024, 8, 32, 16, 556, 0),      # short requests with shared prefixes
+    (8, 8, 32, 32, 131072, 512),    # long context
+])
+def test_plan_choices(so, S, Hkv, Hq, bs, maxlen, expect):
+    p = _pool(num_kv_heads=Hkv, block_size=bs)
+    assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 0) == expect
+    assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, -1) == 0
+    assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 64) == 64
