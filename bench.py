@@ -1,0 +1,217 @@
+"""Benchmark: one paged-attention decode step on one MI355X.
+
+A step is the whole hot path over one batch: pa_reshape_and_cache writes this
+step's new token of every sequence through slot_mapping, then pa_decode
+attends each sequence's query over its paged context (single pass or split
+pass + log-sum-exp reduce, as the library plans it).
+
+Workload (default): Llama-3-8B-shaped single-layer decode -- 64 sequences with
+lengths uniform in [512, 4096], 32 query / 8 KV heads, head_dim 128,
+block_size 16, fp16 KV in a 20,000-block pool filled from a seeded shuffled
+free list; 64 new tokens written per step.  Inputs are seeded synthetic data.
+
+Consecutive steps use different layers' pools (--layers copies, 1.3 GB each),
+as a model's consecutive attention calls do, so no step finds its KV in the
+256 MB Infinity Cache left behind by the previous one.
+
+Prints ONE JSON line.  `value` is achieved algorithmic GB/s of the whole step
+(K/V context, q, out, tables, lengths, and the new tokens' write), from wall
+time over exactly --steps steps.  `roofline` covers the dominant kernel
+(pa_decode), timed with HIP events on its stream inside the timed region.
+`cpu_baseline` times the fp64 CPU oracle on the host cores over the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode achieved HBM GB/s (% of MI355X peak) + KV tokens/s"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "paged_kv_cache_72_amd", "csrc"))):
+        with open(os.path.join(ROOT, "paged_kv_cache_72_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def alg_bytes(w) -> dict:
+    """Bytes the method itself must move (no partials, no masked slots)."""
+    e = w.kv_elem_bytes
+    lens = w.seq_lens.astype(np.int64)
+    kv = int(lens.sum()) * w.num_kv_heads * w.head_dim * e * 2
+    qo = w.num_seqs * w.num_q_heads * w.head_dim * 2 * 2
+    tables = int(((lens + w.block_size - 1) // w.block_size).sum()) * 4 + w.num_seqs * 4
+    T = int(w.new_idx.size)
+    write = T * w.num_kv_heads * w.head_dim * (2 * 2 + 2 * e) + T * 8
+    return {"kv": kv, "decode": kv + qo + tables, "write": write}
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    import oracle as O
+    nthreads = min(16, len(os.sched_getaffinity(0)))
+    pool = O.pool_for_workload(w, nthreads=nthreads)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.decode(pool, w.q, w.block_tables, w.seq_lens, w.scale, nthreads=nthreads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per = el / reps
+    b = alg_bytes(w)
+    return {"value": round(b["decode"] / per / 1e9, 4), "unit": "GB/s", "cores": nthreads,
+            "kind": "oracle", "ms_per_step": round(per * 1e3, 2),
+            "kv_tokens_per_s": round(float(w.seq_lens.sum()) / per, 1),
+            "sample": f"full decode of the {w.name} step (all {w.num_seqs} sequences, "
+                      f"{w.num_q_heads} query heads), repeated {reps}x over {el:.1f} s; "
+                      "fp64 C oracle, OpenMP"}
+
+
+def traffic_entry(config: str):
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = d.get(config)
+    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="llama3_8b_b64")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-gib", type=float, default=0.0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path shards by sequence or KV head "
+              "with no exchange, so a single-GPU figure is the per-GPU figure. Run with "
+              "--gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    from paged_kv_cache_72_amd import lib as L
+    from paged_kv_cache_72_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    L.load()
+    w = W.CONFIGS[args.config]()
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs resident in HBM: per-layer pools holding the context
+    q = torch.from_numpy(w.q).to(dev)
+    bt = torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    out = torch.empty_like(q)
+    k_all = torch.from_numpy(w.tok_k).to(dev)
+    v_all = torch.from_numpy(w.tok_v).to(dev)
+    slots = torch.from_numpy(w.tok_slot).to(dev)
+    base = L.KVPool.allocate(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                             w.kv_dtype, w.k_scale, w.v_scale, dev, fill_bits=0)
+    L.pa_reshape_and_cache(base, k_all, v_all, slots)
+    if w.cow_pairs is not None:
+        L.pa_copy_blocks(base, torch.from_numpy(w.cow_pairs).to(dev))
+    idx = torch.from_numpy(w.new_idx).to(dev)
+    k_new = k_all.index_select(0, idx).contiguous()
+    v_new = v_all.index_select(0, idx).contiguous()
+    slot_new = slots.index_select(0, idx).contiguous()
+    del k_all, v_all, slots
+    pools = [base]
+    for _ in range(args.layers - 1):
+        pools.append(L.KVPool(base.k.clone(), base.v.clone(), w.block_size, w.num_kv_heads,
+                              w.head_dim, w.kv_dtype, w.k_scale, w.v_scale))
+    part = L.pa_decode_plan(base, w.num_seqs, w.num_q_heads, w.max_seq_len, args.partition)
+    ws = L.alloc_workspace(base, w.num_seqs, w.num_q_heads, w.max_seq_len, args.partition)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        p = pools[i % len(pools)]
+        L.pa_reshape_and_cache(p, k_new, v_new, slot_new, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        L.pa_decode(p, out, q, bt, lens, w.max_seq_len, w.scale, args.partition, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in events]
+    dec_avg = float(np.mean(dec_ms))
+
+    if args.calib_copy_gib > 0:
+        n = int(args.calib_copy_gib * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    b = alg_bytes(w)
+    step_bytes = b["decode"] + b["write"]
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = b["decode"] / (dec_avg * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and free-list block ids)",
+        "config": {"workload": f"{w.name}: {w.num_seqs} seqs, seq_lens "
+                               f"{int(w.seq_lens.min())}-{int(w.seq_lens.max())} "
+                               f"(sum {int(w.seq_lens.sum())}), {w.num_q_heads} q / "
+                               f"{w.num_kv_heads} kv heads, head_dim {w.head_dim}, block_size "
+                               f"{w.block_size}, {w.kv_dtype} KV, {w.num_blocks}-block pool; "
+                               f"step = reshape_and_cache of {w.new_idx.size} tokens + decode",
+                   "global_batch": w.num_seqs, "seq_len": w.max_seq_len, "parallelism": "none",
+                   "layers_rotated": args.layers, "partition_tokens": part},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kv_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_step * 1e-3), 1),
+        "decode_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "alg_bytes_per_step": step_bytes,
+        "roofline": {"bound": "hbm", "kernel": "pa_decode", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_entry(w.name), "avg_launch_ms": round(dec_avg, 5),
+                     "alg_bytes_per_launch": b["decode"],
+                     "kernel_source_hash": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

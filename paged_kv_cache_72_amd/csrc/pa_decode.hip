@@ -91,7 +91,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   typedef typename Vec<VB>::T VT;
 
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int r = lane >> 4;                // MFMA k-group / output row group
   const int c = lane & 15;                // MFMA column: token (K load) or head
 
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     t_end = min(len, t_begin + a.part_tokens);
   }
   const int j_begin = t_begin >> 4;           // 16-token tiles (partition sizes are x16)
-  const int j_end = (t_end + 15) >> 4;
+  const int j_end = (t_end + 15) >> 4;        // only the last tile can be partial
   const int nblk = (len + BS - 1) / BS;       // valid table entries of this sequence
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
 
@@ -131,7 +131,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- lane-constant byte offsets inside a tile
+  // ---- addressing.  A tile's byte base inside a pool is uniform (block id from
+  // the table, read with scalar loads one tile ahead); lanes add constant 32-bit
+  // offsets: key token c at dims cl*4*KCH + r*KCH, value rows 4r+k at dims c*DCH.
   const int64_t head_off = (int64_t)kh * D * E;
   const int rs = a.row_stride;
   const int nb_m1 = a.num_blocks_m1;
@@ -139,38 +141,53 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     lb = lb < nblk - 1 ? lb : nblk - 1;     // never read past the valid table entries
     int id = bt[lb];
     id = id < 0 ? 0 : (id > nb_m1 ? nb_m1 : id);
-    return (int64_t)id;
+    return (int64_t)id * a.block_stride + head_off;
+  };
+  struct Ids { int64_t lo, hi; };           // bases of the tile's two halves (same if BS >= 16)
+  auto tile_ids = [&](int jj) -> Ids {
+    if constexpr (BS >= 16) {
+      const int t = jj * 16;
+      const int64_t b = phys(t / BS) + (int64_t)(t % BS) * rs;
+      return {b, b};
+    } else {
+      return {phys(2 * jj), phys(2 * jj + 1)};
+    }
+  };
+  // Lane offsets are constant across tiles; a tile's base is a scalar buffer
+  // descriptor covering its 16 token rows, so loads carry no 64-bit per-lane
+  // address math and an offset outside the rows would read zeros.
+  const uint32_t koff = (uint32_t)((BS >= 16 ? c : (c & 7)) * rs + r * 16);
+  const uint32_t voff = (uint32_t)((BS >= 16 ? 4 * r : ((4 * r) & 7)) * rs + c * VB);
+  const int rows_bytes = 16 * rs;
+  auto rsrc = [&](const char* p) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, rows_bytes, 0x00020000);
+  };
+  auto ld_k = [&](__amdgpu_buffer_rsrc_t R, int cl) -> uint4 {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, koff + cl * 64, 0, 0));
+  };
+  auto ld_v = [&](__amdgpu_buffer_rsrc_t R, int k) -> VT {
+    if constexpr (VB == 16)
+      return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, voff, k * rs, 0));
+    else if constexpr (VB == 8)
+      return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R, voff, k * rs, 0));
+    else
+      return __builtin_amdgcn_raw_buffer_load_b32(R, voff, k * rs, 0);
   };
 
-  uint4 kc[NKL], kn[NKL];
-  VT vc[4], vn[4];
-
-  // Issue the loads of tile j: key token c (16 B at dims cl*4*KCH + r*KCH) and
-  // value rows 4r+k (VB bytes at dims c*DCH).  For block_size >= 16 the tile
-  // lies in one block, whose id is wave-uniform; for block_size 8 the tile's
-  // first and second halves come from two blocks.
-  auto issue = [&](int j, uint4* kr, VT* vr) {
-    const char* kb;
-    const char* vb[4];
+  auto issue = [&](const Ids& ids, uint4* kr, VT* vr) {
+    const __amdgpu_buffer_rsrc_t klo = rsrc(a.k + ids.lo), vlo = rsrc(a.v + ids.lo);
     if constexpr (BS >= 16) {
-      const int t = j * 16;
-      const int64_t blk = phys(t / BS);
-      const int64_t base = blk * a.block_stride + (int64_t)(t % BS) * rs + head_off;
-      kb = a.k + base + (int64_t)c * rs + r * 16;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) vb[k] = a.v + base + (int64_t)(4 * r + k) * rs + c * VB;
-    } else {
-      const int64_t b0 = phys(2 * j) * a.block_stride + head_off;
-      const int64_t b1 = phys(2 * j + 1) * a.block_stride + head_off;
-      kb = a.k + (c < 8 ? b0 : b1) + (int64_t)(c & 7) * rs + r * 16;
+      for (int cl = 0; cl < NKL; ++cl) kr[cl] = ld_k(klo, cl);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        vb[k] = a.v + (r < 2 ? b0 : b1) + (int64_t)((4 * r + k) & 7) * rs + c * VB;
+      for (int k = 0; k < 4; ++k) vr[k] = ld_v(vlo, k);
+    } else {   // tokens 0-7 of the tile in block 2j, tokens 8-15 in block 2j+1
+      const __amdgpu_buffer_rsrc_t khi = rsrc(a.k + ids.hi), vhi = rsrc(a.v + ids.hi);
+#pragma unroll
+      for (int cl = 0; cl < NKL; ++cl) kr[cl] = c < 8 ? ld_k(klo, cl) : ld_k(khi, cl);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vr[k] = r < 2 ? ld_v(vlo, k) : ld_v(vhi, k);
     }
-#pragma unroll
-    for (int cl = 0; cl < NKL; ++cl) kr[cl] = *(const uint4*)(kb + cl * 64);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) vr[k] = *(const VT*)vb[k];
   };
 
   float m_run = kNegBig;     // per lane: head c (identical across the 4 rows)
@@ -182,18 +199,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const bool head_ok = c < g;
   const float sc = a.score_scale;
 
-  int j = j_begin + wid;
-  if (j < j_end) issue(j, kc, vc);
-  while (j < j_end) {
-    const int jn = j + NW;
-    if (jn < j_end) issue(jn, kn, vn);
-
+  auto compute = [&](int j, const uint4* kr, const VT* vr_in) {
     // ---- scores S[token 4r+i][head c]
     float4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cl = 0; cl < NKL; ++cl) {
       uint32_t w[4];
-      vec_words<16>(kc[cl], w);
+      vec_words<16>(kr[cl], w);
 #pragma unroll
       for (int grp = 0; grp < GPL; ++grp) {
         half4_t kop;
@@ -202,21 +214,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kop, qop[cl * GPL + grp], sacc, 0, 0, 0);
       }
     }
-
+    const bool partial = j * 16 + 16 > t_end;   // wave-uniform
     const int t0 = j * 16 + 4 * r;
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + i;
-      x[i] = (t >= t_begin && t < t_end) ? sacc[i] * sc : -INFINITY;
-    }
+    for (int i = 0; i < 4; ++i) x[i] = (t0 + i < t_end) ? sacc[i] * sc : -INFINITY;
     float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     tmax = xor_max(tmax, 16);
     tmax = xor_max(tmax, 32);
     const bool grow = head_ok && (tmax > m_run + kLazy);
     if (__any(grow)) {
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -228,21 +237,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = exp2f(x[i] - m_run);
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_run);
     l_run += (p[0] + p[1]) + (p[2] + p[3]);
     const float4_t pf = {p[0], p[1], p[2], p[3]};
     const half4_t pop = __builtin_convertvector(pf, half4_t);
 
-    // ---- values: zero masked rows, transpose in-lane, P.V on the matrix core
-    VT vv[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = j * 16 + 4 * r + k;
-      vv[k] = (t >= t_begin && t < t_end) ? vc[k] : vec_zero<VB>();
-    }
+    // ---- values: zero masked rows (last tile only), transpose in-lane, P.V
     uint32_t vw[4][VB / 4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) vec_words<VB>(vv[k], vw[k]);
+    for (int k = 0; k < 4; ++k) vec_words<VB>(vr_in[k], vw[k]);
+    if (partial) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bool ok = t0 + k < t_end;
+#pragma unroll
+        for (int wi = 0; wi < VB / 4; ++wi) vw[k][wi] = ok ? vw[k][wi] : 0u;
+      }
+    }
     if constexpr (!FP8) {
 #pragma unroll
       for (int e = 0; e < DCH; ++e) {
@@ -273,12 +284,32 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(pop, bop, acc[e], 0, 0, 0);
       }
     }
+  };
 
-#pragma unroll
-    for (int cl = 0; cl < NKL; ++cl) kc[cl] = kn[cl];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) vc[k] = vn[k];
-    j = jn;
+  // ---- software pipeline: the loads of tile j+NW and the block ids of tile
+  // j+2NW are in flight while tile j is computed; two register sets alternate.
+  // The next tile's loads are issued unconditionally -- past the end of the
+  // range they repeat the range's last tile, which is cache-resident -- so the
+  // wave always waits for exactly one tile of outstanding loads.
+  uint4 kA[NKL], kB[NKL];
+  VT vA[4], vB[4];
+  int j = j_begin + wid;
+  if (j < j_end) {
+    const int j_last = j_end - 1;
+    issue(tile_ids(j), kA, vA);
+    Ids ids_b = tile_ids(min(j + NW, j_last));
+    for (;;) {
+      issue(ids_b, kB, vB);
+      const Ids ids_a = tile_ids(min(j + 2 * NW, j_last));
+      compute(j, kA, vA);
+      j += NW;
+      if (j >= j_end) break;
+      issue(ids_a, kA, vA);
+      ids_b = tile_ids(min(j + 2 * NW, j_last));
+      compute(j, kB, vB);
+      j += NW;
+      if (j >= j_end) break;
+    }
   }
 
   // ---- per-wave totals: l summed over the 4 row groups
