@@ -108,11 +108,16 @@ int pa_reshape_and_cache(const pa_kv_pool* pool, const void* k_new, const void* 
 int pa_copy_blocks(const pa_kv_pool* pool, const int64_t* block_mapping, int64_t num_pairs,
                    hipStream_t stream);
 
-/* The partition size pa_decode will use for these arguments: 0 for the single
- * pass (one workgroup per sequence and KV head), otherwise the number of tokens
- * per partition of the split pass.  partition_size follows pa_decode: -1 forces
- * the single pass, 0 lets the library choose, > 0 (a multiple of 16) forces the
- * split pass with that size.  Returns a negative pa_status on bad arguments. */
+/* The schedule pa_decode will use for these arguments:
+ *   0   single pass: one workgroup per (sequence, KV head);
+ *   1   flat schedule: the (sequence, 16-token) units of the whole batch are
+ *       cut into equal ranges, each walked by one wavefront per KV head, so
+ *       long and short contexts cost the same; contexts cut by range
+ *       boundaries are merged by a log-sum-exp kernel;
+ *   >=16 split pass with that many tokens per partition, followed by a
+ *       log-sum-exp reduce kernel.
+ * partition_size follows pa_decode.  Returns a negative pa_status on bad
+ * arguments. */
 int32_t pa_decode_plan(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                        int32_t max_seq_len, int32_t partition_size);
 
@@ -134,11 +139,13 @@ size_t pa_decode_workspace_size(const pa_kv_pool* pool, int32_t num_seqs, int32_
  *                 A length of 0 gives an all-zero output row.
  *   max_seq_len   host upper bound of seq_lens; sizes the grid and workspace.
  *   scale         softmax scale applied to q.k (e.g. 1/sqrt(head_dim)).
- *   partition_size  -1 single pass, 0 library choice, > 0 split pass with that
- *                 many tokens per partition (multiple of 16) followed by a
- *                 log-sum-exp reduce of the partitions.
+ *   partition_size  -1 single pass, 0 library choice (the flat schedule for up
+ *                 to 8000 sequences), 1 flat schedule, >= 16 split pass with
+ *                 that many tokens per partition (a multiple of 16) followed by
+ *                 a log-sum-exp reduce of the partitions.
  *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes,
- *                 16-byte aligned; may be NULL when that size is 0.
+ *                 16-byte aligned; may be NULL when that size is 0.  Calls
+ *                 that run concurrently need separate workspaces.
  * num_q_heads must be a multiple of num_kv_heads with a ratio of at most 16.
  * Outputs are bitwise reproducible for the same inputs and do not depend on
  * which physical ids hold the blocks. */

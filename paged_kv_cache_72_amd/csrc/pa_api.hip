@@ -71,10 +71,19 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
   return PA_OK;
 }
 
-// Single pass when there are enough (sequence, KV head) units to occupy the
-// GPU and contexts are short; otherwise split contexts into partitions so that
-// the grid holds a few thousand workgroups and long and short sequences cost
-// the same per workgroup.
+// Planning.  The flat schedule balances any mix of context lengths, so it is
+// the default; it keeps per-sequence prefix and lengths in LDS (2 S + 1 ints).
+constexpr int32_t kFlatMaxSeqs = 8000;
+#ifndef PA_FLAT_MAX_WAVES
+#define PA_FLAT_MAX_WAVES 3072                // 256 CUs x 4 SIMDs x 3 waves
+#endif
+constexpr int64_t kFlatMaxWaves = PA_FLAT_MAX_WAVES;
+constexpr int64_t kFlatMinTiles = 8;         // keep at least this many tiles per range
+constexpr int32_t kPlanFlat = 1;             // pa_decode_plan's code for the flat schedule
+
+// Beyond the flat schedule's limit: the single pass when there are enough
+// (sequence, KV head) units to occupy the GPU and contexts are short, else a
+// split pass with a few thousand workgroups of at least 256 tokens each.
 int32_t choose_partition(int64_t units, int32_t max_seq_len) {
   if (max_seq_len <= 256) return 0;
   if (units >= 2048 && max_seq_len <= 2048) return 0;
@@ -83,8 +92,15 @@ int32_t choose_partition(int64_t units, int32_t max_seq_len) {
   return P;
 }
 
+struct Plan {
+  int mode;             // pa::kMode*
+  int32_t part;         // split pass: tokens per partition
+  int32_t num_parts;
+  int64_t waves;        // flat: number of ranges (one wave per KV head each)
+};
+
 int plan(const pa_kv_pool* pool, int32_t S, int32_t Hq, int32_t max_seq_len, int32_t req,
-         pa::PoolGeom* g, int32_t* part) {
+         pa::PoolGeom* g, Plan* pl) {
   int st = check_pool(pool, g);
   if (st) return st;
   if (S < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", S);
@@ -94,23 +110,57 @@ int plan(const pa_kv_pool* pool, int32_t S, int32_t Hq, int32_t max_seq_len, int
   if (Hq / g->num_kv_heads > 16)
     return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d > 16", Hq / g->num_kv_heads);
   if (max_seq_len < 0) return fail(PA_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
-  if (req < -1) return fail(PA_ERR_INVALID_ARG, "partition_size %d invalid", req);
-  if (req > 0 && req % 16)
-    return fail(PA_ERR_INVALID_ARG, "partition_size %d is not a multiple of 16", req);
+  if (req < -1 || (req > kPlanFlat && req % 16))
+    return fail(PA_ERR_INVALID_ARG,
+                "partition_size %d invalid (-1, 0, 1 or a multiple of 16)", req);
   const int64_t units = (int64_t)S * g->num_kv_heads;
+  const int64_t tiles_ub = units * cdiv64(max_seq_len, 16);
+  if (tiles_ub > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "too many 16-token tiles");
+  pl->mode = pa::kModeSingle;
+  pl->part = 0;
+  pl->num_parts = 0;
+  pl->waves = 0;
+  if (req == kPlanFlat || (req == 0 && S <= kFlatMaxSeqs)) {
+    if (S > kFlatMaxSeqs)
+      return fail(PA_ERR_UNSUPPORTED, "flat schedule supports at most %d sequences", kFlatMaxSeqs);
+    // ranges: about kFlatMaxWaves waves in all, at least kFlatMinTiles units each
+    const int64_t per_head_ub = (int64_t)S * cdiv64(max_seq_len, 16);
+    int64_t ranges = kFlatMaxWaves / g->num_kv_heads;
+    if (ranges > per_head_ub / kFlatMinTiles) ranges = per_head_ub / kFlatMinTiles;
+    if (ranges < 1) ranges = 1;
+    pl->mode = pa::kModeFlat;
+    pl->waves = ranges;           // number of ranges
+    return PA_OK;
+  }
   int32_t P = req == -1 ? 0 : (req > 0 ? req : choose_partition(units, max_seq_len));
-  if (P > 0 && max_seq_len <= 0) P = 0;
-  const int64_t grid = units * (P > 0 ? cdiv64(max_seq_len, P) : 1);
-  if (grid > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "grid of %lld workgroups too large",
-                                    (long long)grid);
-  *part = P;
+  if (P > 0 && max_seq_len > 0) {
+    pl->mode = pa::kModeSplit;
+    pl->part = P;
+    pl->num_parts = (int32_t)cdiv64(max_seq_len, P);
+    if (units * pl->num_parts > INT32_MAX)
+      return fail(PA_ERR_INVALID_ARG, "grid of %lld workgroups too large",
+                  (long long)(units * pl->num_parts));
+  }
   return PA_OK;
 }
 
-size_t workspace_bytes_for(int64_t S, int64_t Hq, int64_t D, int64_t num_parts) {
-  const int64_t rows = S * Hq * num_parts;
-  const int64_t ml = ((rows * 8) + 255) / 256 * 256;
-  return (size_t)(ml + rows * D * 4);
+int32_t plan_code(const Plan& pl) {
+  return pl.mode == pa::kModeFlat ? kPlanFlat : (pl.mode == pa::kModeSplit ? pl.part : 0);
+}
+
+// Workspace layouts.  Split: (m, l) pairs [S][Hq][parts] then o [S][Hq][parts][D].
+// Flat: prefix [S + 1] int32 then partial records [ranges * Hkv][2][gqa][D + 2].
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+size_t workspace_bytes_for(const Plan& pl, int64_t S, int64_t Hq, int64_t Hkv, int64_t D) {
+  if (pl.mode == pa::kModeSplit) {
+    const int64_t rows = S * Hq * pl.num_parts;
+    return align256((size_t)rows * 8) + (size_t)(rows * D * 4);
+  }
+  if (pl.mode == pa::kModeFlat)
+    return align256((size_t)((S + 1) * 4)) +
+           (size_t)(pl.waves * Hkv * 2 * (Hq / Hkv) * (D + 2) * 4);
+  return 0;
 }
 
 }  // namespace
@@ -155,17 +205,17 @@ int pa_copy_blocks(const pa_kv_pool* pool, const int64_t* block_mapping, int64_t
 int32_t pa_decode_plan(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                        int32_t max_seq_len, int32_t partition_size) {
   pa::PoolGeom g;
-  int32_t P = 0;
-  int st = plan(pool, num_seqs, num_q_heads, max_seq_len, partition_size, &g, &P);
-  return st ? st : P;
+  Plan pl;
+  int st = plan(pool, num_seqs, num_q_heads, max_seq_len, partition_size, &g, &pl);
+  return st ? st : plan_code(pl);
 }
 
 size_t pa_decode_workspace_size(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                 int32_t max_seq_len, int32_t partition_size) {
   pa::PoolGeom g;
-  int32_t P = 0;
-  if (plan(pool, num_seqs, num_q_heads, max_seq_len, partition_size, &g, &P) || P == 0) return 0;
-  return workspace_bytes_for(num_seqs, num_q_heads, g.head_dim, cdiv64(max_seq_len, P));
+  Plan pl;
+  if (plan(pool, num_seqs, num_q_heads, max_seq_len, partition_size, &g, &pl)) return 0;
+  return workspace_bytes_for(pl, num_seqs, num_q_heads, g.num_kv_heads, g.head_dim);
 }
 
 int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs,
@@ -173,8 +223,8 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
               const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_size,
               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   pa::PoolGeom g;
-  int32_t P = 0;
-  int st = plan(pool, num_seqs, num_q_heads, max_seq_len, partition_size, &g, &P);
+  Plan pl;
+  int st = plan(pool, num_seqs, num_q_heads, max_seq_len, partition_size, &g, &pl);
   if (st) return st;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !block_tables || !seq_lens)
@@ -184,6 +234,13 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
   if (max_blocks_per_seq < 1)
     return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  const size_t need = workspace_bytes_for(pl, num_seqs, num_q_heads, g.num_kv_heads, g.head_dim);
+  if (need) {
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "this schedule needs %zu workspace bytes, got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(PA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  }
 
   pa::DecodeArgs a{};
   a.k = g.k;
@@ -203,20 +260,21 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
   a.seq_lens = seq_lens;
   a.score_scale = (float)((double)scale * 1.4426950408889634 * (double)g.k_scale);
   a.v_scale = g.v_scale;
-  if (P > 0) {
-    a.part_tokens = P;
-    a.num_parts = (int32_t)cdiv64(max_seq_len, P);
-    const size_t need = workspace_bytes_for(num_seqs, num_q_heads, g.head_dim, a.num_parts);
-    if (!workspace || workspace_bytes < need)
-      return fail(PA_ERR_WORKSPACE, "split pass needs %zu workspace bytes, got %zu", need,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned16(workspace)) return fail(PA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
-    const int64_t rows = (int64_t)num_seqs * num_q_heads * a.num_parts;
+  pa::FlatArgs f{};
+  if (pl.mode == pa::kModeSplit) {
+    a.part_tokens = pl.part;
+    a.num_parts = pl.num_parts;
+    const int64_t rows = (int64_t)num_seqs * num_q_heads * pl.num_parts;
     a.ws_ml = (float2*)workspace;
-    a.ws_o = (float*)((char*)workspace + ((rows * 8) + 255) / 256 * 256);
+    a.ws_o = (float*)((char*)workspace + align256((size_t)rows * 8));
+  } else if (pl.mode == pa::kModeFlat) {
+    f.num_seqs = num_seqs;
+    f.num_ranges = (int32_t)pl.waves;
+    f.prefix = (int32_t*)workspace;
+    f.slots = (float*)((char*)workspace + align256((size_t)(num_seqs + 1) * 4));
   }
-  if (hipError_t e = pa::launch_decode(a, num_seqs, g.head_dim, g.block_size,
-                                       g.elem_bytes == 1, P > 0, stream))
+  if (hipError_t e = pa::launch_decode(a, &f, num_seqs, g.head_dim, g.block_size,
+                                       g.elem_bytes == 1, pl.mode, stream))
     return fail(PA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return PA_OK;
 }

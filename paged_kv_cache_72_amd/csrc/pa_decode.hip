@@ -6,37 +6,60 @@
 // sum_t e^{x_t - max} v_t / sum_t e^{x_t - max} ("KV Cache memory core",
 // section 3 read path; "vLLM intro part 2", section 4.2 formulas).  Blocks are
 // merged one after another with the online-softmax rule ("PagedAttention &
-// vLLM", PagedAttention kernel: merge across blocks as FlashAttention does).
+// vLLM", PagedAttention kernel: merge across blocks as FlashAttention does),
+// and separately computed pieces of one context are merged by the same rule
+// in log-sum-exp form.
 //
-// How it maps to CDNA4:
-//   * One workgroup serves one (sequence, KV head[, partition]) and ALL of the
-//     gqa query heads that share that KV head, so every K/V byte is read from
-//     HBM once.  Its waves take 16-token tiles round-robin.
-//   * A tile's scores S[16 tokens x 16 heads] come from one 16x16x16 f16 MFMA
-//     per 16 head dims: lane (row r, column c) loads 16 contiguous bytes of
-//     token c's key (the A operand) and holds the same 16 bytes of query head
-//     c (the B operand), so K feeds the matrix core straight from its 128-bit
-//     load with no LDS staging.  Heads beyond gqa are zero columns.
+// The tile engine (one copy of the math, used by every schedule):
+//   * Work unit: 16 consecutive tokens of one (sequence, KV head) pair, for
+//     ALL gqa query heads of that KV head, so every K/V byte leaves HBM once.
+//   * Scores S[16 tokens x 16 heads]: one 16x16x16 f16 MFMA per 16 head dims.
+//     Lane (row r, column c) loads 16 contiguous bytes of token c's key (the A
+//     operand) and holds the same dims of query head c (the B operand), so K
+//     feeds the matrix core straight from its 128-bit load.  Heads beyond gqa
+//     are zero columns.
 //   * The MFMA result leaves lane (r, c) with the scores of tokens 4r..4r+3 for
-//     head c -- exactly the A-operand layout P[head][token] of the next MFMA,
-//     P.V.  V is loaded as 4 rows of D/16 contiguous elements per lane (token
-//     4r+k, dims c*D/16..), then transposed inside the lane into B operands
-//     V[4r..4r+3][dim] with byte permutes; D/16 MFMAs give the whole P.V.
-//     P goes to the matrix core in binary16, V in binary16 (fp8 pools are
-//     widened exactly first); accumulation is fp32.
-//   * Softmax state per head: running max m (log2 units), per-lane partial
-//     sums l, and the P.V accumulators.  The max is only moved (and l, acc
-//     rescaled) when a tile's max exceeds it by more than 2^8, so P <= 256 always
-//     fits binary16 and most tiles skip the rescale.
-//   * Masked tokens (past the sequence or the partition) get score -inf by a
-//     select and their V rows are zeroed by a select, so NaN in unused slots
-//     never reaches a valid output.
-//   * Split pass: each partition writes (m, l, o = acc / l) per head to the
-//     workspace; lse_reduce merges them with weights l_p * 2^(m_p - M).
+//     head c -- exactly the A-operand layout P[head][token] of the P.V MFMA.
+//     V arrives as 4 rows of D/16 contiguous elements per lane (tokens 4r+k,
+//     dims c*D/16..) and is transposed inside the lane into B operands
+//     V[4r..4r+3][dim]; D/16 MFMAs give P.V.  P and V enter the matrix core as
+//     binary16 (fp8 pools are widened exactly first), accumulation is fp32.
+//   * Softmax state per head: running max m (log2 units), per-lane partial sum
+//     l and the P.V accumulators.  The max moves (and l, acc are rescaled) only
+//     when a tile's max exceeds it by more than 2^8, so P <= 256 fits binary16.
+//   * Masked tokens get score -inf by a select and their V rows are zeroed by a
+//     select, so NaN in unused slots never reaches a valid output.
+//   * Loads: a tile's base is a scalar buffer descriptor over its 16 token rows;
+//     lanes add constant 32-bit offsets.  Block ids are read with scalar loads
+//     one tile ahead; the next tile's loads are always in flight while the
+//     current one is computed.
+//
+// Schedules:
+//   * single pass   -- one workgroup per (sequence, KV head); its waves take
+//                      tiles round-robin and merge in LDS.
+//   * split pass    -- one workgroup per (sequence, KV head, partition) writing
+//                      (m, l, o) partials, then lse_reduce_kernel.
+//   * flat (default)-- the list of all (sequence, 16-token tile) units is cut
+//                      into equal ranges; each range is walked by one wave per
+//                      KV head, side by side, so long and short contexts cost
+//                      the same per wave and the heads of a block are read
+//                      together.  Sequences inside one range are written
+//                      directly; a sequence cut by range boundaries leaves one
+//                      partial per range, merged by flat_merge_kernel in range
+//                      order (deterministic).
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
+
+// Tuning knobs (compile time): waves per decode workgroup, and the occupancy
+// the register allocator is asked to reach (waves per SIMD).
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_WAVES_PER_EU
+#define PA_WAVES_PER_EU 3
+#endif
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -57,13 +80,6 @@ __device__ __forceinline__ void vec_words(const typename Vec<BYTES>::T& v, uint3
   else { w[0] = v; }
 }
 
-template <int BYTES>
-__device__ __forceinline__ typename Vec<BYTES>::T vec_zero() {
-  if constexpr (BYTES == 16) return make_uint4(0, 0, 0, 0);
-  else if constexpr (BYTES == 8) return make_uint2(0, 0);
-  else return 0u;
-}
-
 __device__ __forceinline__ half4_t halves_of(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(half4_t, make_uint2(lo, hi));
 }
@@ -78,129 +94,134 @@ __device__ __forceinline__ half4_t fp8x4_to_half4(uint32_t w) {
 
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int D, int BS, bool FP8, int NW, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
-  constexpr int E = FP8 ? 1 : 2;          // bytes per KV element
-  constexpr int KCH = 16 / E;             // elements in a lane's 16-B key load
-  constexpr int NKL = D * E / 64;         // 16-B key loads per lane per tile
-  constexpr int GPL = KCH / 4;            // MFMA operand groups per key load
-  constexpr int NQ = D / 16;              // QK MFMAs per tile (= q operands per lane)
-  constexpr int DCH = D / 16;             // value dims per lane
-  constexpr int VB = DCH * E;             // bytes per lane per value row
+__device__ __forceinline__ int clamp_len(int len, int cap) {
+  return len < 0 ? 0 : (len > cap ? cap : len);
+}
+
+// Byte bases, inside the pools, of a tile's two halves (equal when block_size >= 16).
+struct Ids {
+  int64_t lo, hi;
+};
+
+// One (sequence, KV head) pair as the loads see it.
+struct PairRef {
+  const int32_t* bt;   // block table row
+  int nblk;            // valid table entries
+  int len;             // context length
+  int64_t head_off;    // byte offset of the KV head inside a token row
+};
+
+template <int D, int BS, bool FP8>
+struct Engine {
+  static constexpr int E = FP8 ? 1 : 2;        // bytes per KV element
+  static constexpr int KCH = 16 / E;           // elements in a lane's 16-B key load
+  static constexpr int NKL = D * E / 64;       // 16-B key loads per lane per tile
+  static constexpr int GPL = KCH / 4;          // MFMA operand groups per key load
+  static constexpr int NQ = D / 16;            // QK MFMAs per tile (q operands per lane)
+  static constexpr int DCH = D / 16;           // value dims per lane
+  static constexpr int VB = DCH * E;           // bytes per lane per value row
   typedef typename Vec<VB>::T VT;
 
-  const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const int r = lane >> 4;                // MFMA k-group / output row group
-  const int c = lane & 15;                // MFMA column: token (K load) or head
+  int r, c, g, rs, nb_m1;
+  uint32_t koff, voff;
+  int64_t block_stride;
+  const char* kp;
+  const char* vp;
+  float sc;
 
-  int bid = blockIdx.x;
-  int part = 0;
-  if constexpr (SPLIT) { part = bid % a.num_parts; bid /= a.num_parts; }
-  const int kh = bid % a.num_kv_heads;
-  const int s = bid / a.num_kv_heads;
-  const int g = a.gqa;
-
-  int len = a.seq_lens[s];
-  len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
-  int t_begin = 0, t_end = len;
-  if constexpr (SPLIT) {
-    t_begin = part * a.part_tokens;
-    if (t_begin >= len) return;               // partition past the end: nothing to do
-    t_end = min(len, t_begin + a.part_tokens);
-  }
-  const int j_begin = t_begin >> 4;           // 16-token tiles (partition sizes are x16)
-  const int j_end = (t_end + 15) >> 4;        // only the last tile can be partial
-  const int nblk = (len + BS - 1) / BS;       // valid table entries of this sequence
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
-
-  // ---- query operands: lane (r, c) holds head c, dims (cl*4*KCH + r*KCH + 4*grp ..+3)
   half4_t qop[NQ];
-  {
-    const _Float16* qrow = a.q + ((int64_t)s * a.num_q_heads + (int64_t)kh * g + c) * D;
+  float m_run, l_run;
+  float4_t acc[DCH];
+
+  __device__ __forceinline__ void init(const DecodeArgs& a, int lane) {
+    r = lane >> 4;
+    c = lane & 15;
+    g = a.gqa;
+    rs = a.row_stride;
+    nb_m1 = a.num_blocks_m1;
+    block_stride = a.block_stride;
+    kp = a.k;
+    vp = a.v;
+    sc = a.score_scale;
+    koff = (uint32_t)((BS >= 16 ? c : (c & 7)) * rs + r * 16);
+    voff = (uint32_t)((BS >= 16 ? 4 * r : ((4 * r) & 7)) * rs + c * VB);
+  }
+
+  __device__ __forceinline__ void reset() {
+    m_run = kNegBig;
+    l_run = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DCH; ++e) acc[e] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  }
+
+  // q rows of the pair's gqa heads, starting at head 0 of the group.
+  // Lane (r, c) holds head c at dims cl*4*KCH + r*KCH + 4*grp .. +3.
+  __device__ __forceinline__ void load_q(const _Float16* qrow0) {
+    const _Float16* qrow = qrow0 + (int64_t)c * D;
 #pragma unroll
     for (int cl = 0; cl < NKL; ++cl) {
 #pragma unroll
       for (int grp = 0; grp < GPL; ++grp) {
-        const int d0 = cl * 4 * KCH + r * KCH + 4 * grp;
         half4_t v = {0, 0, 0, 0};
-        if (c < g) v = *(const half4_t*)(qrow + d0);
+        if (c < g) v = *(const half4_t*)(qrow + cl * 4 * KCH + r * KCH + 4 * grp);
         qop[cl * GPL + grp] = v;
       }
     }
   }
 
-  // ---- addressing.  A tile's byte base inside a pool is uniform (block id from
-  // the table, read with scalar loads one tile ahead); lanes add constant 32-bit
-  // offsets: key token c at dims cl*4*KCH + r*KCH, value rows 4r+k at dims c*DCH.
-  const int64_t head_off = (int64_t)kh * D * E;
-  const int rs = a.row_stride;
-  const int nb_m1 = a.num_blocks_m1;
-  auto phys = [&](int lb) -> int64_t {
-    lb = lb < nblk - 1 ? lb : nblk - 1;     // never read past the valid table entries
-    int id = bt[lb];
+  __device__ __forceinline__ int64_t phys(const PairRef& p, int lb) const {
+    lb = lb < p.nblk - 1 ? lb : p.nblk - 1;      // never past the valid table entries
+    int id = p.bt[lb];
     id = id < 0 ? 0 : (id > nb_m1 ? nb_m1 : id);
-    return (int64_t)id * a.block_stride + head_off;
-  };
-  struct Ids { int64_t lo, hi; };           // bases of the tile's two halves (same if BS >= 16)
-  auto tile_ids = [&](int jj) -> Ids {
+    return (int64_t)id * block_stride + p.head_off;
+  }
+
+  __device__ __forceinline__ Ids tile_ids(const PairRef& p, int j) const {
     if constexpr (BS >= 16) {
-      const int t = jj * 16;
-      const int64_t b = phys(t / BS) + (int64_t)(t % BS) * rs;
+      const int t = j * 16;
+      const int64_t b = phys(p, t / BS) + (int64_t)(t % BS) * rs;
       return {b, b};
     } else {
-      return {phys(2 * jj), phys(2 * jj + 1)};
+      return {phys(p, 2 * j), phys(p, 2 * j + 1)};
     }
-  };
-  // Lane offsets are constant across tiles; a tile's base is a scalar buffer
-  // descriptor covering its 16 token rows, so loads carry no 64-bit per-lane
-  // address math and an offset outside the rows would read zeros.
-  const uint32_t koff = (uint32_t)((BS >= 16 ? c : (c & 7)) * rs + r * 16);
-  const uint32_t voff = (uint32_t)((BS >= 16 ? 4 * r : ((4 * r) & 7)) * rs + c * VB);
-  const int rows_bytes = 16 * rs;
-  auto rsrc = [&](const char* p) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, rows_bytes, 0x00020000);
-  };
-  auto ld_k = [&](__amdgpu_buffer_rsrc_t R, int cl) -> uint4 {
+  }
+
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const char* p) const {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 16 * rs, 0x00020000);
+  }
+  __device__ __forceinline__ uint4 ld_k(__amdgpu_buffer_rsrc_t R, int cl) const {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, koff + cl * 64, 0, 0));
-  };
-  auto ld_v = [&](__amdgpu_buffer_rsrc_t R, int k) -> VT {
+  }
+  __device__ __forceinline__ VT ld_v(__amdgpu_buffer_rsrc_t R, int k) const {
     if constexpr (VB == 16)
       return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, voff, k * rs, 0));
     else if constexpr (VB == 8)
       return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R, voff, k * rs, 0));
     else
       return __builtin_amdgcn_raw_buffer_load_b32(R, voff, k * rs, 0);
-  };
+  }
 
-  auto issue = [&](const Ids& ids, uint4* kr, VT* vr) {
-    const __amdgpu_buffer_rsrc_t klo = rsrc(a.k + ids.lo), vlo = rsrc(a.v + ids.lo);
+  __device__ __forceinline__ void issue(const Ids& ids, uint4* kr, VT* vr) const {
+    const __amdgpu_buffer_rsrc_t klo = rsrc(kp + ids.lo), vlo = rsrc(vp + ids.lo);
     if constexpr (BS >= 16) {
 #pragma unroll
       for (int cl = 0; cl < NKL; ++cl) kr[cl] = ld_k(klo, cl);
 #pragma unroll
       for (int k = 0; k < 4; ++k) vr[k] = ld_v(vlo, k);
     } else {   // tokens 0-7 of the tile in block 2j, tokens 8-15 in block 2j+1
-      const __amdgpu_buffer_rsrc_t khi = rsrc(a.k + ids.hi), vhi = rsrc(a.v + ids.hi);
+      const __amdgpu_buffer_rsrc_t khi = rsrc(kp + ids.hi), vhi = rsrc(vp + ids.hi);
 #pragma unroll
       for (int cl = 0; cl < NKL; ++cl) kr[cl] = c < 8 ? ld_k(klo, cl) : ld_k(khi, cl);
 #pragma unroll
       for (int k = 0; k < 4; ++k) vr[k] = r < 2 ? ld_v(vlo, k) : ld_v(vhi, k);
     }
-  };
+  }
 
-  float m_run = kNegBig;     // per lane: head c (identical across the 4 rows)
-  float l_run = 0.0f;        // per lane partial sum over the tokens it scored
-  float4_t acc[DCH];
-#pragma unroll
-  for (int e = 0; e < DCH; ++e) acc[e] = (float4_t){0.f, 0.f, 0.f, 0.f};
-
-  const bool head_ok = c < g;
-  const float sc = a.score_scale;
-
-  auto compute = [&](int j, const uint4* kr, const VT* vr_in) {
-    // ---- scores S[token 4r+i][head c]
+  // Fold tile j (tokens 16j..16j+15) into the running state; tokens >= t_end
+  // are masked.
+  __device__ __forceinline__ void compute(int j, int t_end, const uint4* kr, const VT* vr_in) {
     float4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cl = 0; cl < NKL; ++cl) {
@@ -222,7 +243,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     tmax = xor_max(tmax, 16);
     tmax = xor_max(tmax, 32);
-    const bool grow = head_ok && (tmax > m_run + kLazy);
+    const bool grow = (c < g) && (tmax > m_run + kLazy);
     if (__any(grow)) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -242,7 +263,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const float4_t pf = {p[0], p[1], p[2], p[3]};
     const half4_t pop = __builtin_convertvector(pf, half4_t);
 
-    // ---- values: zero masked rows (last tile only), transpose in-lane, P.V
     uint32_t vw[4][VB / 4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) vec_words<VB>(vr_in[k], vw[k]);
@@ -284,44 +304,119 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(pop, bop, acc[e], 0, 0, 0);
       }
     }
-  };
+  }
 
-  // ---- software pipeline: the loads of tile j+NW and the block ids of tile
-  // j+2NW are in flight while tile j is computed; two register sets alternate.
-  // The next tile's loads are issued unconditionally -- past the end of the
-  // range they repeat the range's last tile, which is cache-resident -- so the
-  // wave always waits for exactly one tile of outstanding loads.
-  uint4 kA[NKL], kB[NKL];
+  // Sum of l over the 4 row groups: lane (any r, c) then holds head c's total.
+  __device__ __forceinline__ float l_total() const {
+    return xor_sum(xor_sum(l_run, 16), 32);
+  }
+
+  // Write acc / l (times v_scale) for the gqa heads of a pair.  dst points at
+  // head 0 of the group; rows are D elements apart.
+  __device__ __forceinline__ void store_out(_Float16* dst, float lt, float v_scale) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * r + i;
+      const float lh = __shfl(lt, h);
+      if (h < g) {
+        const float inv = lh > 0.f ? v_scale / lh : 0.f;
+        _Float16 o[DCH];
+#pragma unroll
+        for (int e = 0; e < DCH; ++e) o[e] = (_Float16)(acc[e][i] * inv);
+        if constexpr (DCH == 8)
+          *(uint4*)(dst + (int64_t)h * D + c * DCH) = __builtin_bit_cast(uint4, o);
+        else
+          *(uint2*)(dst + (int64_t)h * D + c * DCH) = __builtin_bit_cast(uint2, o);
+      }
+    }
+  }
+
+  // Write a partial: o[h][d] = acc / l * v_scale (fp32) then (m, l) per head.
+  __device__ __forceinline__ void store_partial(float* rec, float lt, float v_scale) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * r + i;
+      const float lh = __shfl(lt, h);
+      if (h < g) {
+        const float inv = lh > 0.f ? v_scale / lh : 0.f;
+        float4* d4 = (float4*)(rec + (int64_t)h * D + c * DCH);
+#pragma unroll
+        for (int q = 0; q < DCH / 4; ++q)
+          d4[q] = make_float4(acc[4 * q][i] * inv, acc[4 * q + 1][i] * inv,
+                              acc[4 * q + 2][i] * inv, acc[4 * q + 3][i] * inv);
+      }
+    }
+    if (r == 0 && c < g) ((float2*)(rec + g * D))[c] = make_float2(m_run, lt);
+  }
+};
+
+// ---------------------------------------------------------------- single / split
+
+template <int D, int BS, bool FP8, int NW, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU, 8)))
+void decode_kernel(DecodeArgs a) {
+  typedef Engine<D, BS, FP8> En;
+  typedef typename En::VT VT;
+  const int lane = threadIdx.x & 63;
+  const int wid = uni(threadIdx.x >> 6);
+
+  int bid = blockIdx.x;
+  int part = 0;
+  if constexpr (SPLIT) { part = bid % a.num_parts; bid /= a.num_parts; }
+  const int kh = bid % a.num_kv_heads;
+  const int s = bid / a.num_kv_heads;
+  const int g = a.gqa;
+
+  const int len = clamp_len(a.seq_lens[s], a.len_cap);
+  int t_begin = 0, t_end = len;
+  if constexpr (SPLIT) {
+    t_begin = part * a.part_tokens;
+    if (t_begin >= len) return;               // partition past the end: nothing to do
+    t_end = min(len, t_begin + a.part_tokens);
+  }
+  const int j_begin = t_begin >> 4;           // partition sizes are multiples of 16
+  const int j_end = (t_end + 15) >> 4;
+
+  En en;
+  en.init(a, lane);
+  en.load_q(a.q + ((int64_t)s * a.num_q_heads + (int64_t)kh * g) * D);
+  en.reset();
+  const PairRef pr{a.block_tables + (int64_t)s * a.max_blocks, (len + BS - 1) / BS, len,
+                   (int64_t)kh * D * En::E};
+
+  // The loads of tile j+NW and the block ids of tile j+2NW are in flight while
+  // tile j is computed; two register sets alternate.  Past the end of the
+  // range the next-tile loads repeat the range's last tile (cache-resident), so
+  // the wave always waits on exactly one tile of outstanding loads.
+  uint4 kA[En::NKL], kB[En::NKL];
   VT vA[4], vB[4];
   int j = j_begin + wid;
   if (j < j_end) {
     const int j_last = j_end - 1;
-    issue(tile_ids(j), kA, vA);
-    Ids ids_b = tile_ids(min(j + NW, j_last));
+    en.issue(en.tile_ids(pr, j), kA, vA);
+    Ids ids_b = en.tile_ids(pr, min(j + NW, j_last));
     for (;;) {
-      issue(ids_b, kB, vB);
-      const Ids ids_a = tile_ids(min(j + 2 * NW, j_last));
-      compute(j, kA, vA);
+      en.issue(ids_b, kB, vB);
+      const Ids ids_a = en.tile_ids(pr, min(j + 2 * NW, j_last));
+      en.compute(j, t_end, kA, vA);
       j += NW;
       if (j >= j_end) break;
-      issue(ids_a, kA, vA);
-      ids_b = tile_ids(min(j + 2 * NW, j_last));
-      compute(j, kB, vB);
+      en.issue(ids_a, kA, vA);
+      ids_b = en.tile_ids(pr, min(j + 2 * NW, j_last));
+      en.compute(j, t_end, kB, vB);
       j += NW;
       if (j >= j_end) break;
     }
   }
-
-  // ---- per-wave totals: l summed over the 4 row groups
-  float l_tot = xor_sum(l_run, 16);
-  l_tot = xor_sum(l_tot, 32);
+  const float l_tot = en.l_total();
 
   // ---- merge the waves of the workgroup in LDS, then write
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
   __shared__ float sm_o[NW][16][D];
+  const int r = lane >> 4, c = lane & 15;
   if (r == 0) {
-    sm_m[wid][c] = m_run;
+    sm_m[wid][c] = en.m_run;
     sm_l[wid][c] = l_tot;
   }
 #pragma unroll
@@ -329,7 +424,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const int h = 4 * r + i;
     if (h < g) {
 #pragma unroll
-      for (int e = 0; e < DCH; ++e) sm_o[wid][h][c * DCH + e] = acc[e][i];
+      for (int e = 0; e < En::DCH; ++e) sm_o[wid][h][c * En::DCH + e] = en.acc[e][i];
     }
   }
   __syncthreads();
@@ -367,8 +462,7 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeArgs a) {
   constexpr int NG = NT / D;                  // thread groups sharing the partitions
   const int row_id = blockIdx.x;
   const int s = row_id / a.num_q_heads;
-  int len = a.seq_lens[s];
-  len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
+  const int len = clamp_len(a.seq_lens[s], a.len_cap);
   const int np = (len + a.part_tokens - 1) / a.part_tokens;
   const int64_t base = (int64_t)row_id * a.num_parts;
   const float2* ml = a.ws_ml + base;
@@ -376,7 +470,6 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeArgs a) {
   __shared__ float red[NT / 64];
   __shared__ float sm_part[NG][D];
 
-  // M: max over partitions
   float mx = kNegBig;
   for (int p = threadIdx.x; p < np; p += NT) mx = fmaxf(mx, ml[p].x);
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -387,7 +480,6 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeArgs a) {
   for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, red[w]);
   __syncthreads();
 
-  // W: total weight
   float wsum = 0.f;
   for (int p = threadIdx.x; p < np; p += NT) {
     const float2 v = ml[p];
@@ -400,7 +492,6 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeArgs a) {
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) W += red[w];
 
-  // weighted sum of the partial outputs, groups of D threads over strided partitions
   const int d = threadIdx.x % D, grp = threadIdx.x / D;
   const float* o = a.ws_o + base * D + d;
   float acc = 0.f;
@@ -428,12 +519,210 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeArgs a) {
   }
 }
 
-constexpr int kWaves = 4;
+// ---------------------------------------------------------------- flat schedule
+
+// Range that owns unit t when T units are cut into NR ranges
+// [floor(r*T/NR), floor((r+1)*T/NR)).
+__device__ __forceinline__ int range_of(int64_t t, int64_t T, int64_t NR) {
+  return (int)(((t + 1) * NR - 1) / T);
+}
+
+// Units are (sequence, 16-token tile) pairs in sequence order.  Range r is
+// walked by the Hkv consecutive waves r*Hkv + kh, one per KV head, so the heads
+// of a block are read together.  A sequence that lies inside one range is
+// written directly; one cut by range boundaries leaves a partial record per
+// range (slot 0: the range's first sequence, slot 1: its last), merged by
+// flat_merge_kernel.
+template <int D, int BS, bool FP8, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU, 8)))
+void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ tables,
+                        const int32_t* __restrict__ lens, const _Float16* __restrict__ qs,
+                        _Float16* __restrict__ outs, float* __restrict__ slots,
+                        int32_t* __restrict__ prefix) {
+  // The read-only arrays arrive as separate restrict arguments: stores to the
+  // outputs inside the loop then provably leave the block table alone, so its
+  // entries can be read with scalar loads.
+  typedef Engine<D, BS, FP8> En;
+  typedef typename En::VT VT;
+  extern __shared__ int sm[];                 // [S + 1] tiles before sequence s, then [S] lengths
+  const int S = f.num_seqs, Hkv = a.num_kv_heads, g = a.gqa;
+  int* sm_pre = sm;
+  int* sm_len = sm + S + 1;
+  const int lane = threadIdx.x & 63;
+  const int wid = uni(threadIdx.x >> 6);
+
+  // ---- exclusive prefix of per-sequence tile counts (wave 0; workgroup 0 also
+  // stores it for the merge), lengths in LDS, and zero rows of empty sequences
+  if (wid == 0) {
+    int carry = 0;
+    for (int base = 0; base < S; base += 64) {
+      const int i = base + lane;
+      const int len = i < S ? clamp_len(lens[i], a.len_cap) : 0;
+      const int v = (len + 15) >> 4;
+      int x = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      if (i < S) {
+        sm_pre[i] = carry + x - v;
+        sm_len[i] = len;
+        if (blockIdx.x == 0) prefix[i] = carry + x - v;
+      }
+      carry += __shfl(x, 63);
+    }
+    if (lane == 0) {
+      sm_pre[S] = carry;
+      if (blockIdx.x == 0) prefix[S] = carry;
+    }
+  }
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+    if (clamp_len(lens[s], a.len_cap) == 0) {
+      _Float16* o = outs + (int64_t)s * a.num_q_heads * D;
+      for (int i = threadIdx.x; i < a.num_q_heads * D; i += NW * 64) o[i] = (_Float16)0.f;
+    }
+  }
+  __syncthreads();
+
+  const int64_t T = sm_pre[S];
+  const int64_t NR = f.num_ranges;
+  const int gw = blockIdx.x * NW + wid;
+  const int rg = gw / Hkv, kh = gw - (gw / Hkv) * Hkv;
+  if (rg >= NR) return;                        // no barrier follows
+  const int g0 = (int)((int64_t)rg * T / NR), g1 = (int)((int64_t)(rg + 1) * T / NR);
+  if (g0 >= g1) return;
+
+  // ---- cursors over (sequence, tile) units; all wave-uniform
+  auto ntiles = [&](int ss) { return uni(sm_pre[ss + 1] - sm_pre[ss]); };
+  auto advance = [&](int& cs, int& cj) {       // to the next unit (callers know one exists)
+    if (cj + 1 < ntiles(cs)) { ++cj; return; }
+    do { ++cs; } while (ntiles(cs) == 0);
+    cs = uni(cs);
+    cj = 0;
+  };
+  int lo = 0, hi = S;                          // sequence with pre[s] <= g0 < pre[s+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (sm_pre[mid] <= g0) lo = mid; else hi = mid;
+  }
+  int s0 = uni(lo), j0 = uni(g0 - sm_pre[lo]);     // unit being computed
+  int s1 = s0, j1 = j0, s2, j2;                    // units one and two ahead
+  if (g0 + 1 < g1) advance(s1, j1);
+  s2 = s1; j2 = j1;
+  if (g0 + 2 < g1) advance(s2, j2);
+
+  En en;
+  en.init(a, lane);
+  const int64_t head_off = (int64_t)kh * D * En::E;
+  auto ids_of = [&](int cs, int cj) -> Ids {
+    const int len = uni(sm_len[cs]);
+    const PairRef p{tables + (int64_t)cs * a.max_blocks, (len + BS - 1) / BS, len, head_off};
+    return en.tile_ids(p, cj);
+  };
+  auto q_of = [&](int cs) { return qs + ((int64_t)cs * a.num_q_heads + (int64_t)kh * g) * D; };
+  float* rec_base = slots + (int64_t)gw * 2 * g * (D + 2);
+
+  en.load_q(q_of(s0));
+  en.reset();
+  bool seg_from_start = j0 == 0;               // the current segment began at tile 0
+  int seg_start = g0;                          // unit index where the current segment began
+  int gt = g0;
+
+  // Fold unit (s0, j0) and, when it ends its sequence or the range, write the
+  // segment and move to the next sequence.
+  auto finish = [&]() {
+    const bool seq_end = j0 + 1 == ntiles(s0);
+    if (!(seq_end || gt + 1 == g1)) return;
+    const float lt = en.l_total();
+    if (seg_from_start && seq_end) {
+      en.store_out(outs + ((int64_t)s0 * a.num_q_heads + (int64_t)kh * g) * D, lt, a.v_scale);
+    } else {                                   // slot 0: the range's first segment
+      en.store_partial(rec_base + (seg_start == g0 ? 0 : 1) * g * (D + 2), lt, a.v_scale);
+    }
+    if (gt + 1 < g1) {                         // next sequence: new query rows, fresh state
+      en.load_q(q_of(s1));
+      en.reset();
+      seg_from_start = true;
+      seg_start = gt + 1;
+    }
+  };
+
+  uint4 kA[En::NKL], kB[En::NKL];
+  VT vA[4], vB[4];
+  en.issue(ids_of(s0, j0), kA, vA);
+  Ids ids_b = ids_of(s1, j1);
+  for (;;) {
+    en.issue(ids_b, kB, vB);                   // unit gt+1 (a repeat of the last one at the end)
+    const Ids ids_a = ids_of(s2, j2);
+    en.compute(j0, uni(sm_len[s0]), kA, vA);
+    finish();
+    if (++gt == g1) break;
+    s0 = s1; j0 = j1; s1 = s2; j1 = j2;
+    if (gt + 2 < g1) advance(s2, j2);
+    en.issue(ids_a, kA, vA);
+    ids_b = ids_of(s2, j2);
+    en.compute(j0, uni(sm_len[s0]), kB, vB);
+    finish();
+    if (++gt == g1) break;
+    s0 = s1; j0 = j1; s1 = s2; j1 = j2;
+    if (gt + 2 < g1) advance(s2, j2);
+  }
+}
+
+// One workgroup of head_dim threads per (sequence, query head): if the
+// sequence was cut by range boundaries, merge its per-range records by
+// log-sum-exp in range order; otherwise the decode kernel already wrote it.
+template <int D>
+__global__ __launch_bounds__(D) void flat_merge_kernel(DecodeArgs a, FlatArgs f) {
+  const int row = blockIdx.x;
+  const int s = row / a.num_q_heads, h = row - s * a.num_q_heads;
+  const int g = a.gqa, kh = h / g, hl = h - kh * g;
+  const int64_t T = f.prefix[f.num_seqs];
+  const int pre = f.prefix[s], end = f.prefix[s + 1];
+  if (end == pre) return;
+  const int64_t NR = f.num_ranges;
+  const int r_first = range_of(pre, T, NR), r_last = range_of(end - 1, T, NR);
+  if (r_first == r_last) return;
+  const bool first_is_last_slot = (int64_t)r_first * T / NR < pre;
+  const int rec = g * (D + 2);
+  const int d = threadIdx.x;
+  float M = kNegBig, L = 0.f, O = 0.f;
+#pragma unroll 4
+  for (int r = r_first; r <= r_last; ++r) {
+    const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
+    const float* p = f.slots + ((int64_t)(r * a.num_kv_heads + kh) * 2 + slot) * rec;
+    const float2 ml = ((const float2*)(p + g * D))[hl];
+    const float ov = p[hl * D + d];
+    const float mn = fmaxf(M, ml.x);
+    const float sa = __builtin_amdgcn_exp2f(M - mn), sb = __builtin_amdgcn_exp2f(ml.x - mn);
+    L = L * sa + ml.y * sb;
+    O = O * sa + ml.y * sb * ov;
+    M = mn;
+  }
+  a.out[(int64_t)row * D + d] = (_Float16)(L > 0.f ? O / L : 0.f);
+}
+
+// ---------------------------------------------------------------- launchers
+
+constexpr int kWaves = PA_DECODE_WAVES;
 
 template <int D, int BS, bool FP8>
-hipError_t launch_typed(const DecodeArgs& a, int32_t num_seqs, bool split, hipStream_t stream) {
+hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int mode,
+                        hipStream_t stream) {
   const uint32_t units = (uint32_t)num_seqs * (uint32_t)a.num_kv_heads;
-  if (split) {
+  if (mode == kModeFlat) {
+    const size_t lds = sizeof(int) * (2 * (size_t)num_seqs + 1);
+    const int64_t waves = (int64_t)f->num_ranges * a.num_kv_heads;
+    hipLaunchKernelGGL((decode_flat_kernel<D, BS, FP8, kWaves>),
+                       dim3((uint32_t)((waves + kWaves - 1) / kWaves)), dim3(kWaves * 64), lds,
+                       stream, a, *f, a.block_tables, a.seq_lens, a.q, a.out, f->slots,
+                       f->prefix);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((flat_merge_kernel<D>), dim3((uint32_t)num_seqs * (uint32_t)a.num_q_heads),
+                       dim3(D), 0, stream, a, *f);
+  } else if (mode == kModeSplit) {
     hipLaunchKernelGGL((decode_kernel<D, BS, FP8, kWaves, true>),
                        dim3(units * (uint32_t)a.num_parts), dim3(kWaves * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
@@ -448,29 +737,32 @@ hipError_t launch_typed(const DecodeArgs& a, int32_t num_seqs, bool split, hipSt
 }
 
 template <int D, int BS>
-hipError_t launch_bs(const DecodeArgs& a, int32_t num_seqs, bool fp8, bool split,
+hipError_t launch_bs(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, bool fp8, int mode,
                      hipStream_t stream) {
-  return fp8 ? launch_typed<D, BS, true>(a, num_seqs, split, stream)
-             : launch_typed<D, BS, false>(a, num_seqs, split, stream);
+  return fp8 ? launch_typed<D, BS, true>(a, f, num_seqs, mode, stream)
+             : launch_typed<D, BS, false>(a, f, num_seqs, mode, stream);
 }
 
 template <int D>
-hipError_t launch_d(const DecodeArgs& a, int32_t num_seqs, int32_t bs, bool fp8, bool split,
-                    hipStream_t stream) {
+hipError_t launch_d(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int32_t bs, bool fp8,
+                    int mode, hipStream_t stream) {
   switch (bs) {
-    case 8: return launch_bs<D, 8>(a, num_seqs, fp8, split, stream);
-    case 16: return launch_bs<D, 16>(a, num_seqs, fp8, split, stream);
-    case 32: return launch_bs<D, 32>(a, num_seqs, fp8, split, stream);
+    case 8: return launch_bs<D, 8>(a, f, num_seqs, fp8, mode, stream);
+    case 16: return launch_bs<D, 16>(a, f, num_seqs, fp8, mode, stream);
+    case 32: return launch_bs<D, 32>(a, f, num_seqs, fp8, mode, stream);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int32_t num_seqs, int32_t head_dim,
-                         int32_t block_size, bool fp8, bool split, hipStream_t stream) {
-  if (head_dim == 128) return launch_d<128>(a, num_seqs, block_size, fp8, split, stream);
-  if (head_dim == 64) return launch_d<64>(a, num_seqs, block_size, fp8, split, stream);
+int decode_waves_per_workgroup() { return kWaves; }
+
+hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
+                         int32_t head_dim, int32_t block_size, bool fp8, int mode,
+                         hipStream_t stream) {
+  if (head_dim == 128) return launch_d<128>(a, f, num_seqs, block_size, fp8, mode, stream);
+  if (head_dim == 64) return launch_d<64>(a, f, num_seqs, block_size, fp8, mode, stream);
   return hipErrorInvalidValue;
 }
 

@@ -45,12 +45,25 @@ struct DecodeArgs {
   float2* ws_ml;              // split pass: [S][Hq][num_parts] (max in log2 units, sum)
 };
 
+// Flat schedule: the list of all (sequence, 16-token tile) units is cut into
+// num_ranges equal ranges; range r is walked by waves r*Hkv .. r*Hkv+Hkv-1.
+struct FlatArgs {
+  int32_t num_seqs;
+  int32_t num_ranges;
+  int32_t* prefix;            // [S + 1] tiles before each sequence (written by the kernel)
+  float* slots;               // [num_ranges * Hkv][2][gqa][head_dim + 2] partial records
+};
+
+enum { kModeSingle = 0, kModeSplit = 1, kModeFlat = 2 };
+
 hipError_t launch_reshape_and_cache(const PoolGeom& g, const _Float16* k_new,
                                     const _Float16* v_new, const int64_t* slots, int64_t T,
                                     hipStream_t stream);
 hipError_t launch_copy_blocks(const PoolGeom& g, const int64_t* pairs, int64_t n,
                               hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int32_t num_seqs, int32_t head_dim,
-                         int32_t block_size, bool fp8, bool split, hipStream_t stream);
+int decode_waves_per_workgroup();
+hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
+                         int32_t head_dim, int32_t block_size, bool fp8, int mode,
+                         hipStream_t stream);
 
 }  // namespace pa

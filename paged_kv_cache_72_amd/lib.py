@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_ALIGNMENT, PA_ERR_WORKSPACE, PA_ERR_HIP = \
     0, -1, -2, -3, -4, -5
 PA_KV_F16, PA_KV_FP8_E4M3FN = 0, 1
+PLAN_SINGLE, PLAN_FLAT = 0, 1          # pa_decode_plan codes; >= 16 is a split partition size
 _DTYPES = {"f16": PA_KV_F16, "fp8_e4m3fn": PA_KV_FP8_E4M3FN}
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
@@ -168,7 +169,7 @@ def pa_decode_workspace_size(pool: KVPool, num_seqs: int, num_q_heads: int, max_
 def alloc_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_seq_len: int,
                     partition_size: int = 0, device="cuda") -> Optional[torch.Tensor]:
     n = pa_decode_workspace_size(pool, num_seqs, num_q_heads, max_seq_len, partition_size)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
 def pa_decode(pool: KVPool, out: torch.Tensor, q: torch.Tensor, block_tables: torch.Tensor,

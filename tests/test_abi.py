@@ -85,13 +85,15 @@ def test_head_ratio_checks(so):
 def test_partition_size_checks(so):
     assert _decode(so, _pool(), part=100) == L.PA_ERR_INVALID_ARG     # not a multiple of 16
     assert _decode(so, _pool(), part=-2) == L.PA_ERR_INVALID_ARG
+    assert _decode(so, _pool(), part=2) == L.PA_ERR_INVALID_ARG
 
 
-def test_split_pass_needs_workspace(so):
-    assert _decode(so, _pool(), part=256, max_len=4096) == L.PA_ERR_WORKSPACE
-    need = so.pa_decode_workspace_size(C.byref(_pool()), 4, 32, 4096, 256)
+@pytest.mark.parametrize("part", [256, 1, 0])
+def test_split_and_flat_need_workspace(so, part):
+    assert _decode(so, _pool(), part=part, max_len=4096) == L.PA_ERR_WORKSPACE
+    need = so.pa_decode_workspace_size(C.byref(_pool()), 4, 32, 4096, part)
     assert need > 0
-    assert _decode(so, _pool(), part=256, max_len=4096, ws=FAKE, ws_bytes=need - 1) == \
+    assert _decode(so, _pool(), part=part, max_len=4096, ws=FAKE, ws_bytes=need - 1) == \
         L.PA_ERR_WORKSPACE
 
 
@@ -123,17 +125,30 @@ def test_workspace_size_formula(so):
     ml = (rows * 8 + 255) // 256 * 256
     assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, P) == ml + rows * D * 4
     assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, -1) == 0
+    # flat: prefix [S+1] int32, then 2 records of gqa*(D+2) floats per wave
+    ranges = min(3072 // 8, S * (T // 16) // 8)
+    pre = ((S + 1) * 4 + 255) // 256 * 256
+    assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, 1) == \
+        pre + ranges * 8 * 2 * 4 * 130 * 4
 
 
-@pytest.mark.parametrize("S,Hkv,Hq,bs,maxlen,expect", [
-    (4, 2, 8, 16, 100, 0),          # tiny: single pass
-    (64, 8, 32, 16, 4096, 512),     # Llama-3-8B-shaped batch 64
-    (13, 4, 28, 16, 8192, 256),     # Qwen2.5-7B-shaped, 13 x 8k
-    (1024, 8, 32, 16, 556, 0),      # short requests with shared prefixes
-    (8, 8, 32, 32, 131072, 512),    # long context
+@pytest.mark.parametrize("S,Hkv,Hq,bs,maxlen", [
+    (4, 2, 8, 16, 100),             # tiny
+    (64, 8, 32, 16, 4096),          # Llama-3-8B-shaped batch 64
+    (13, 4, 28, 16, 8192),          # Qwen2.5-7B-shaped, 13 x 8k
+    (1024, 8, 32, 16, 556),         # short requests with shared prefixes
+    (8, 8, 32, 32, 131072),         # long context
 ])
-def test_plan_choices(so, S, Hkv, Hq, bs, maxlen, expect):
+def test_plan_choices(so, S, Hkv, Hq, bs, maxlen):
     p = _pool(num_kv_heads=Hkv, block_size=bs)
-    assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 0) == expect
-    assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, -1) == 0
+    assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 0) == L.PLAN_FLAT
+    assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 1) == L.PLAN_FLAT
+    assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, -1) == L.PLAN_SINGLE
     assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 64) == 64
+
+
+def test_plan_falls_back_past_flat_limit(so):
+    p = _pool()
+    assert so.pa_decode_plan(C.byref(p), 9000, 32, 300, 0) == L.PLAN_SINGLE
+    assert so.pa_decode_plan(C.byref(p), 9000, 32, 8192, 0) == 512
+    assert so.pa_decode_plan(C.byref(p), 9000, 32, 300, 1) == L.PA_ERR_UNSUPPORTED

@@ -20,9 +20,9 @@ CONFIGS = [
     ("tiny", W.tiny, 8, [0, -1, 16]),
     ("llama3_8b_b64", W.llama3_8b_b64, 24, [0, -1, 256]),
     ("qwen25_7b_8k", W.qwen25_7b_8k, 12, [0, -1, 512]),
-    ("prefix_share_bs16", lambda: W.prefix_share(16), 48, [0, 256]),
-    ("prefix_share_bs8", lambda: W.prefix_share(8), 48, [0, 256]),
-    ("long_fp8", W.long_fp8, 6, [512]),
+    ("prefix_share_bs16", lambda: W.prefix_share(16), 48, [0, -1, 256]),
+    ("prefix_share_bs8", lambda: W.prefix_share(8), 48, [0, -1, 256]),
+    ("long_fp8", W.long_fp8, 6, [0, 512]),
 ]
 
 

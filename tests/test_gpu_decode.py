@@ -47,7 +47,7 @@ def _ref(w, pool):
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
-@pytest.mark.parametrize("part", [-1, 0, 16, 64, 512])
+@pytest.mark.parametrize("part", [-1, 0, 1, 16, 64, 512])
 def test_decode_matches_oracle(name, part):
     w, hp = _case(name)
     say(f"decode {name} partition={part}")
@@ -61,7 +61,7 @@ def test_decode_matches_oracle(name, part):
 
 @pytest.mark.parametrize("name", ["tiny", "d128_bs8_g7", "fp8_d128_bs32", "d64_bs32_g16"])
 @pytest.mark.parametrize("variant", ["v_offset", "needles"])
-@pytest.mark.parametrize("part", [-1, 64])
+@pytest.mark.parametrize("part", [-1, 1, 64])
 def test_structured_variants(name, variant, part):
     w0, _ = _case(name)
     w = W.with_v_offset(w0, 1.0) if variant == "v_offset" else W.with_needles(w0, 64.0)
@@ -85,7 +85,7 @@ def _relabel(w, seed):
 
 
 @pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "fp8_d128_bs32"])
-@pytest.mark.parametrize("part", [-1, 64])
+@pytest.mark.parametrize("part", [-1, 1, 64])
 def test_physical_relabelling_is_bitwise_invariant(name, part):
     w, _ = _case(name)
     say(f"relabel {name} partition={part}")
@@ -94,7 +94,7 @@ def test_physical_relabelling_is_bitwise_invariant(name, part):
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
-@pytest.mark.parametrize("part", [-1, 0, 32])
+@pytest.mark.parametrize("part", [-1, 1, 32])
 def test_run_to_run_bitwise_determinism(part):
     w, _ = _case("d128_bs16_g4")
     dc = DeviceCase(w, poison=True)
@@ -108,7 +108,7 @@ def test_split_and_single_pass_agree():
     w, hp = _case("d128_bs16_g4")
     dc = DeviceCase(w, poison=True)
     ys = dc.decode(-1).cpu().numpy().astype(np.float64)
-    for p in (16, 48, 256, 1024):
+    for p in (1, 16, 48, 256, 1024):
         yp = dc.decode(p).cpu().numpy().astype(np.float64)
         assert np.max(np.abs(yp - ys)) < 2e-3
 
