@@ -47,5 +47,24 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+PROBE_LIB = os.path.join(HERE, "libpa_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The HBM read-ceiling probe used by bench.py (measurement only)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    src = os.path.join(HERE, "probe", "stream_read.hip")
+    cmd = [hipcc, *HIPCC_FLAGS, src, "-o", PROBE_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libpa_probe.so")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))

@@ -60,6 +60,9 @@ namespace {
 #ifndef PA_WAVES_PER_EU
 #define PA_WAVES_PER_EU 3
 #endif
+#ifndef PA_FLAT_STAGES
+#define PA_FLAT_STAGES 2      // flat schedule: tiles in flight per wave, plus one
+#endif
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -593,80 +596,84 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   const int g0 = (int)((int64_t)rg * T / NR), g1 = (int)((int64_t)(rg + 1) * T / NR);
   if (g0 >= g1) return;
 
-  // ---- cursors over (sequence, tile) units; all wave-uniform
+  // ---- cursors over (sequence, tile) units; all wave-uniform.  cur[0] is the
+  // unit being computed, cur[k] the k-th after it (clamped to the range's last
+  // unit, whose loads then repeat cache-resident data).
   auto ntiles = [&](int ss) { return uni(sm_pre[ss + 1] - sm_pre[ss]); };
-  auto advance = [&](int& cs, int& cj) {       // to the next unit (callers know one exists)
-    if (cj + 1 < ntiles(cs)) { ++cj; return; }
-    do { ++cs; } while (ntiles(cs) == 0);
-    cs = uni(cs);
-    cj = 0;
+  struct Cur { int s, j; };
+  auto advance = [&](Cur c) -> Cur {           // the next unit (callers know one exists)
+    if (c.j + 1 < ntiles(c.s)) return {c.s, c.j + 1};
+    int ns = c.s;
+    do { ++ns; } while (ntiles(ns) == 0);
+    return {uni(ns), 0};
   };
   int lo = 0, hi = S;                          // sequence with pre[s] <= g0 < pre[s+1]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (sm_pre[mid] <= g0) lo = mid; else hi = mid;
   }
-  int s0 = uni(lo), j0 = uni(g0 - sm_pre[lo]);     // unit being computed
-  int s1 = s0, j1 = j0, s2, j2;                    // units one and two ahead
-  if (g0 + 1 < g1) advance(s1, j1);
-  s2 = s1; j2 = j1;
-  if (g0 + 2 < g1) advance(s2, j2);
+  constexpr int ST = PA_FLAT_STAGES;           // tiles in flight per wave, plus one
+  Cur cur[ST + 1];
+  cur[0] = {uni(lo), uni(g0 - sm_pre[lo])};
+#pragma unroll
+  for (int k = 1; k <= ST; ++k) cur[k] = g0 + k < g1 ? advance(cur[k - 1]) : cur[k - 1];
 
   En en;
   en.init(a, lane);
   const int64_t head_off = (int64_t)kh * D * En::E;
-  auto ids_of = [&](int cs, int cj) -> Ids {
-    const int len = uni(sm_len[cs]);
-    const PairRef p{tables + (int64_t)cs * a.max_blocks, (len + BS - 1) / BS, len, head_off};
-    return en.tile_ids(p, cj);
+  auto ids_of = [&](Cur c) -> Ids {
+    const int len = uni(sm_len[c.s]);
+    const PairRef p{tables + (int64_t)c.s * a.max_blocks, (len + BS - 1) / BS, len, head_off};
+    return en.tile_ids(p, c.j);
   };
   auto q_of = [&](int cs) { return qs + ((int64_t)cs * a.num_q_heads + (int64_t)kh * g) * D; };
   float* rec_base = slots + (int64_t)gw * 2 * g * (D + 2);
 
-  en.load_q(q_of(s0));
+  en.load_q(q_of(cur[0].s));
   en.reset();
-  bool seg_from_start = j0 == 0;               // the current segment began at tile 0
+  bool seg_from_start = cur[0].j == 0;         // the current segment began at tile 0
   int seg_start = g0;                          // unit index where the current segment began
   int gt = g0;
 
-  // Fold unit (s0, j0) and, when it ends its sequence or the range, write the
-  // segment and move to the next sequence.
+  // After folding unit cur[0]: when it ends its sequence or the range, write
+  // the segment and, if the range goes on, switch to the next sequence.
   auto finish = [&]() {
-    const bool seq_end = j0 + 1 == ntiles(s0);
+    const bool seq_end = cur[0].j + 1 == ntiles(cur[0].s);
     if (!(seq_end || gt + 1 == g1)) return;
     const float lt = en.l_total();
     if (seg_from_start && seq_end) {
-      en.store_out(outs + ((int64_t)s0 * a.num_q_heads + (int64_t)kh * g) * D, lt, a.v_scale);
+      en.store_out(outs + ((int64_t)cur[0].s * a.num_q_heads + (int64_t)kh * g) * D, lt,
+                   a.v_scale);
     } else {                                   // slot 0: the range's first segment
       en.store_partial(rec_base + (seg_start == g0 ? 0 : 1) * g * (D + 2), lt, a.v_scale);
     }
     if (gt + 1 < g1) {                         // next sequence: new query rows, fresh state
-      en.load_q(q_of(s1));
+      en.load_q(q_of(cur[1].s));
       en.reset();
       seg_from_start = true;
       seg_start = gt + 1;
     }
   };
 
-  uint4 kA[En::NKL], kB[En::NKL];
-  VT vA[4], vB[4];
-  en.issue(ids_of(s0, j0), kA, vA);
-  Ids ids_b = ids_of(s1, j1);
+  // ST register sets rotate: while unit gt is computed, units gt+1 .. gt+ST-1
+  // are in flight; the loads of a unit past the range repeat its last unit.
+  uint4 kb[ST][En::NKL];
+  VT vb[ST][4];
+#pragma unroll
+  for (int k = 0; k < ST - 1; ++k) en.issue(ids_of(cur[k]), kb[k], vb[k]);
+  Ids ids_next = ids_of(cur[ST - 1]);
   for (;;) {
-    en.issue(ids_b, kB, vB);                   // unit gt+1 (a repeat of the last one at the end)
-    const Ids ids_a = ids_of(s2, j2);
-    en.compute(j0, uni(sm_len[s0]), kA, vA);
-    finish();
-    if (++gt == g1) break;
-    s0 = s1; j0 = j1; s1 = s2; j1 = j2;
-    if (gt + 2 < g1) advance(s2, j2);
-    en.issue(ids_a, kA, vA);
-    ids_b = ids_of(s2, j2);
-    en.compute(j0, uni(sm_len[s0]), kB, vB);
-    finish();
-    if (++gt == g1) break;
-    s0 = s1; j0 = j1; s1 = s2; j1 = j2;
-    if (gt + 2 < g1) advance(s2, j2);
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST]);
+      ids_next = ids_of(cur[ST]);
+      en.compute(cur[0].j, uni(sm_len[cur[0].s]), kb[st], vb[st]);
+      finish();
+      if (++gt == g1) return;
+#pragma unroll
+      for (int k = 0; k < ST; ++k) cur[k] = cur[k + 1];
+      if (gt + ST < g1) cur[ST] = advance(cur[ST]);
+    }
   }
 }
 
