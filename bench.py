@@ -130,8 +130,10 @@ def main() -> int:
     k_all = torch.from_numpy(w.tok_k).to(dev)
     v_all = torch.from_numpy(w.tok_v).to(dev)
     slots = torch.from_numpy(w.tok_slot).to(dev)
+    shared = w.has_shared_blocks      # cacheable K/V reads when blocks have several readers
     base = L.KVPool.allocate(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
-                             w.kv_dtype, w.k_scale, w.v_scale, dev, fill_bits=0)
+                             w.kv_dtype, w.k_scale, w.v_scale, dev, fill_bits=0,
+                             shared_blocks=shared)
     L.pa_reshape_and_cache(base, k_all, v_all, slots)
     if w.cow_pairs is not None:
         L.pa_copy_blocks(base, torch.from_numpy(w.cow_pairs).to(dev))
@@ -143,7 +145,8 @@ def main() -> int:
     pools = [base]
     for _ in range(args.layers - 1):
         pools.append(L.KVPool(base.k.clone(), base.v.clone(), w.block_size, w.num_kv_heads,
-                              w.head_dim, w.kv_dtype, w.k_scale, w.v_scale))
+                              w.head_dim, w.kv_dtype, w.k_scale, w.v_scale,
+                              shared_blocks=shared))
     part = L.pa_decode_plan(base, w.num_seqs, w.num_q_heads, w.max_seq_len, args.partition)
     ws = L.alloc_workspace(base, w.num_seqs, w.num_q_heads, w.max_seq_len, args.partition)
     torch.cuda.synchronize()
@@ -195,7 +198,8 @@ def main() -> int:
                                f"{w.block_size}, {w.kv_dtype} KV, {w.num_blocks}-block pool; "
                                f"step = reshape_and_cache of {w.new_idx.size} tokens + decode",
                    "global_batch": w.num_seqs, "seq_len": w.max_seq_len, "parallelism": "none",
-                   "layers_rotated": args.layers, "partition_tokens": part},
+                   "layers_rotated": args.layers, "partition_tokens": part,
+                   "shared_blocks": shared},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kv_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_step * 1e-3), 1),
         "decode_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),

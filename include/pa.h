@@ -72,7 +72,15 @@ typedef enum {
  * block_size * num_kv_heads * head_dim * elem_bytes; a larger stride (a
  * multiple of 16) lets K and V blocks interleave in one allocation.
  * Supported: head_dim 64 or 128; block_size 8, 16 or 32; k_base, v_base 16-byte
- * aligned.  k_scale / v_scale are the per-pool fp8 scales (ignored for f16). */
+ * aligned.  k_scale / v_scale are the per-pool fp8 scales (ignored for f16).
+ * flags: PA_POOL_SHARED_BLOCKS when some blocks are read by several sequences
+ * of one pa_decode batch (shared prefixes, forked sequences: "PagedAttention
+ * & vLLM", memory sharing); decode then keeps K/V reads cacheable so that the
+ * other readers of a block find it in cache.  Without it, K/V tiles are read
+ * with the streaming (non-temporal) cache policy, the faster choice when every
+ * block has one reader.  The flag changes speed only, never results.
+ * reserved must be 0. */
+#define PA_POOL_SHARED_BLOCKS 1u
 typedef struct {
   void* k_base;                /* device */
   void* v_base;                /* device */
@@ -84,6 +92,8 @@ typedef struct {
   int32_t dtype;               /* pa_kv_dtype */
   float k_scale;
   float v_scale;
+  uint32_t flags;              /* PA_POOL_* bits */
+  uint32_t reserved;
 } pa_kv_pool;
 
 /* Write num_tokens new tokens into their slots (the write side of slot_mapping,

@@ -57,6 +57,9 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
       (!(p->k_scale > 0.f) || !(p->v_scale > 0.f) || !std::isfinite(p->k_scale) ||
        !std::isfinite(p->v_scale)))
     return fail(PA_ERR_INVALID_ARG, "fp8 pools need finite positive k_scale and v_scale");
+  if (p->flags & ~PA_POOL_SHARED_BLOCKS)
+    return fail(PA_ERR_INVALID_ARG, "unknown pool flags 0x%x", (unsigned)p->flags);
+  if (p->reserved) return fail(PA_ERR_INVALID_ARG, "pool reserved field must be 0");
   g->k = (char*)p->k_base;
   g->v = (char*)p->v_base;
   g->num_blocks = p->num_blocks;
@@ -68,6 +71,7 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
   g->elem_bytes = e;
   g->k_scale = p->dtype == PA_KV_F16 ? 1.f : p->k_scale;
   g->v_scale = p->dtype == PA_KV_F16 ? 1.f : p->v_scale;
+  g->flags = p->flags;
   return PA_OK;
 }
 
@@ -75,7 +79,7 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
 // the default; it keeps per-sequence prefix and lengths in LDS (2 S + 1 ints).
 constexpr int32_t kFlatMaxSeqs = 8000;
 #ifndef PA_FLAT_MAX_WAVES
-#define PA_FLAT_MAX_WAVES 3072                // 256 CUs x 4 SIMDs x 3 waves
+#define PA_FLAT_MAX_WAVES 2048                // 256 CUs x 4 SIMDs x 2 waves
 #endif
 constexpr int64_t kFlatMaxWaves = PA_FLAT_MAX_WAVES;
 constexpr int64_t kFlatMinTiles = 8;         // keep at least this many tiles per range
@@ -273,8 +277,9 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
     f.prefix = (int32_t*)workspace;
     f.slots = (float*)((char*)workspace + align256((size_t)(num_seqs + 1) * 4));
   }
+  const bool stream_kv = !(g.flags & PA_POOL_SHARED_BLOCKS);
   if (hipError_t e = pa::launch_decode(a, &f, num_seqs, g.head_dim, g.block_size,
-                                       g.elem_bytes == 1, pl.mode, stream))
+                                       g.elem_bytes == 1, stream_kv, pl.mode, stream))
     return fail(PA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return PA_OK;
 }

@@ -60,11 +60,25 @@ namespace {
 #ifndef PA_WAVES_PER_EU
 #define PA_WAVES_PER_EU 3
 #endif
+#ifndef PA_FLAT_WAVES
+#define PA_FLAT_WAVES PA_DECODE_WAVES
+#endif
+#ifndef PA_FLAT_WAVES_PER_EU
+#define PA_FLAT_WAVES_PER_EU 2
+#endif
+#ifndef PA_FLAT_XCD_REMAP
+#define PA_FLAT_XCD_REMAP 0
+#endif
 #ifndef PA_FLAT_STAGES
 #define PA_FLAT_STAGES 2      // flat schedule: tiles in flight per wave, plus one
 #endif
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+// LDS-qualified pointers: stores through them provably leave global memory
+// alone, so uniform loads of read-only tables can stay scalar loads.
+typedef __attribute__((address_space(3))) char lds_char;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
@@ -116,29 +130,42 @@ struct PairRef {
   int64_t head_off;    // byte offset of the KV head inside a token row
 };
 
-template <int D, int BS, bool FP8>
+// NT: K/V tiles are read with the streaming (non-temporal) cache policy, for
+// pools whose blocks each belong to one sequence; blocks shared by several
+// sequences of the batch are read with the default policy so that they stay
+// cached for the other readers.
+template <int D, int BS, bool FP8, bool NT>
 struct Engine {
+  static constexpr int CPOL = NT ? 2 : 0;      // cache-policy operand of the tile loads
   static constexpr int E = FP8 ? 1 : 2;        // bytes per KV element
-  static constexpr int KCH = 16 / E;           // elements in a lane's 16-B key load
+  static constexpr int KCH = 16 / E;           // elements in a 16-B key chunk
   static constexpr int NKL = D * E / 64;       // 16-B key loads per lane per tile
-  static constexpr int GPL = KCH / 4;          // MFMA operand groups per key load
+  static constexpr int GPL = KCH / 4;          // MFMA operand groups per key chunk
   static constexpr int NQ = D / 16;            // QK MFMAs per tile (q operands per lane)
   static constexpr int DCH = D / 16;           // value dims per lane
   static constexpr int VB = DCH * E;           // bytes per lane per value row
+  static constexpr int RB = D * E;             // bytes of one KV head's row of one token
+  static constexpr int CPR = RB / 16;          // 16-B chunks per row
+  static constexpr int RPI = 64 / CPR;         // whole rows covered by one 64-lane key load
+  static constexpr int PER = RB >= 256 ? 1 : 256 / RB;   // rows per 256-B LDS bank period
+  static constexpr int KST = 16 * RB;          // bytes of one key tile staged in LDS
   typedef typename Vec<VB>::T VT;
 
   int r, c, g, rs, nb_m1;
+  int t0, ch;                                  // this lane's row and chunk in a key load
   uint32_t koff, voff;
   int64_t block_stride;
   const char* kp;
   const char* vp;
+  lds_char* kst;                               // this wave's key tile in LDS
   float sc;
 
   half4_t qop[NQ];
   float m_run, l_run;
   float4_t acc[DCH];
 
-  __device__ __forceinline__ void init(const DecodeArgs& a, int lane) {
+  // kstage: KST bytes of LDS owned by this wave alone.
+  __device__ __forceinline__ void init(const DecodeArgs& a, int lane, lds_char* kstage) {
     r = lane >> 4;
     c = lane & 15;
     g = a.gqa;
@@ -147,9 +174,18 @@ struct Engine {
     block_stride = a.block_stride;
     kp = a.k;
     vp = a.v;
+    kst = kstage;
     sc = a.score_scale;
-    koff = (uint32_t)((BS >= 16 ? c : (c & 7)) * rs + r * 16);
-    voff = (uint32_t)((BS >= 16 ? 4 * r : ((4 * r) & 7)) * rs + c * VB);
+    t0 = lane / CPR;
+    ch = lane % CPR;
+    koff = (uint32_t)((BS >= 16 || RPI <= 8 ? t0 : (t0 & 7)) * rs + ch * 16);
+    voff = (uint32_t)(r * rs + c * VB);
+  }
+
+  // LDS chunk slot of chunk `k` of token row t: XOR-swizzled so that both the
+  // row-wise writes and the column-wise operand reads hit distinct banks.
+  __device__ __forceinline__ static int kslot(int t, int k) {
+    return t * RB + ((k ^ ((t / PER) % CPR)) << 4);
   }
 
   __device__ __forceinline__ void reset() {
@@ -160,18 +196,25 @@ struct Engine {
   }
 
   // q rows of the pair's gqa heads, starting at head 0 of the group.
-  // Lane (r, c) holds head c at dims cl*4*KCH + r*KCH + 4*grp .. +3.
-  __device__ __forceinline__ void load_q(const _Float16* qrow0) {
-    const _Float16* qrow = qrow0 + (int64_t)c * D;
+  // Lane (r, c) holds head c at dims cl*4*KCH + r*KCH + 4*grp .. +3.  The
+  // rows are read through a buffer descriptor sized to the group, so lanes of
+  // heads c >= gqa read zeros and the address stays in scalar registers.
+  __device__ __forceinline__ void load_q_into(half4_t* dst, const _Float16* qrow0) const {
+    const __amdgpu_buffer_rsrc_t R =
+        __builtin_amdgcn_make_buffer_rsrc((void*)qrow0, (short)0, g * D * 2, 0x00020000);
+    const uint32_t qoff = (uint32_t)((c * D + r * KCH) * 2);
 #pragma unroll
     for (int cl = 0; cl < NKL; ++cl) {
 #pragma unroll
-      for (int grp = 0; grp < GPL; ++grp) {
-        half4_t v = {0, 0, 0, 0};
-        if (c < g) v = *(const half4_t*)(qrow + cl * 4 * KCH + r * KCH + 4 * grp);
-        qop[cl * GPL + grp] = v;
-      }
+      for (int grp = 0; grp < GPL; ++grp)
+        dst[cl * GPL + grp] = __builtin_bit_cast(
+            half4_t, __builtin_amdgcn_raw_buffer_load_b64(R, qoff, (cl * 4 * KCH + 4 * grp) * 2, 0));
     }
+  }
+  __device__ __forceinline__ void load_q(const _Float16* qrow0) { load_q_into(qop, qrow0); }
+  __device__ __forceinline__ void take_q(const half4_t* src) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) qop[i] = src[i];
   }
 
   __device__ __forceinline__ int64_t phys(const PairRef& p, int lb) const {
@@ -194,42 +237,64 @@ struct Engine {
   __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const char* p) const {
     return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 16 * rs, 0x00020000);
   }
-  __device__ __forceinline__ uint4 ld_k(__amdgpu_buffer_rsrc_t R, int cl) const {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, koff + cl * 64, 0, 0));
+  __device__ __forceinline__ uint4 ld_k(__amdgpu_buffer_rsrc_t R, int soff) const {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, koff, soff, CPOL));
   }
   __device__ __forceinline__ VT ld_v(__amdgpu_buffer_rsrc_t R, int k) const {
+    // value load k: rows 4k .. 4k+3 of the tile (lane: row 4k + r, chunk c)
+    const int so = (BS >= 16 ? 4 * k : ((4 * k) & 7)) * rs;
     if constexpr (VB == 16)
-      return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, voff, k * rs, 0));
+      return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, voff, so, CPOL));
     else if constexpr (VB == 8)
-      return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R, voff, k * rs, 0));
+      return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R, voff, so, CPOL));
     else
-      return __builtin_amdgcn_raw_buffer_load_b32(R, voff, k * rs, 0);
+      return __builtin_amdgcn_raw_buffer_load_b32(R, voff, so, CPOL);
   }
 
   __device__ __forceinline__ void issue(const Ids& ids, uint4* kr, VT* vr) const {
     const __amdgpu_buffer_rsrc_t klo = rsrc(kp + ids.lo), vlo = rsrc(vp + ids.lo);
+    // Key load u reads whole rows u*RPI .. u*RPI+RPI-1 of the tile (lane: row
+    // t0, chunk ch), so each load instruction covers contiguous 256-B runs.
     if constexpr (BS >= 16) {
 #pragma unroll
-      for (int cl = 0; cl < NKL; ++cl) kr[cl] = ld_k(klo, cl);
+      for (int u = 0; u < NKL; ++u) kr[u] = ld_k(klo, u * RPI * rs);
 #pragma unroll
       for (int k = 0; k < 4; ++k) vr[k] = ld_v(vlo, k);
     } else {   // tokens 0-7 of the tile in block 2j, tokens 8-15 in block 2j+1
       const __amdgpu_buffer_rsrc_t khi = rsrc(kp + ids.hi), vhi = rsrc(vp + ids.hi);
 #pragma unroll
-      for (int cl = 0; cl < NKL; ++cl) kr[cl] = c < 8 ? ld_k(klo, cl) : ld_k(khi, cl);
+      for (int u = 0; u < NKL; ++u) {
+        if constexpr (RPI <= 8) kr[u] = ld_k(u * RPI >= 8 ? khi : klo, ((u * RPI) & 7) * rs);
+        else kr[u] = t0 < 8 ? ld_k(klo, 0) : ld_k(khi, 0);
+      }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) vr[k] = r < 2 ? ld_v(vlo, k) : ld_v(vhi, k);
+      for (int k = 0; k < 4; ++k) vr[k] = ld_v(k < 2 ? vlo : vhi, k);
     }
   }
 
   // Fold tile j (tokens 16j..16j+15) into the running state; tokens >= t_end
   // are masked.
   __device__ __forceinline__ void compute(int j, int t_end, const uint4* kr, const VT* vr_in) {
+    // Loads issued before this point stay before it: otherwise the scheduler
+    // hoists the waits for this tile above the next tile's loads.
+    __builtin_amdgcn_sched_barrier(0);
+    // Keys arrive row-wise; the QK MFMA wants one token per lane.  Regroup
+    // through this wave's LDS tile: lane (r, c) reads chunks cl*4 + r of row
+    // (c >> 2) + 4 (c & 3), so that score lane (r, c) ends up holding tokens
+    // r, r+4, r+8, r+12 -- the rows value load k = 0..3 gives that lane.
+#pragma unroll
+    for (int u = 0; u < NKL; ++u)
+      *(lds_u32x4*)(kst + kslot(u * RPI + t0, ch)) = __builtin_bit_cast(u32x4_t, kr[u]);
+    uint4 kc[NKL];
+    const int krow = (c >> 2) + 4 * (c & 3);
+#pragma unroll
+    for (int cl = 0; cl < NKL; ++cl)
+      kc[cl] = __builtin_bit_cast(uint4, *(const lds_u32x4*)(kst + kslot(krow, cl * 4 + r)));
     float4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cl = 0; cl < NKL; ++cl) {
       uint32_t w[4];
-      vec_words<16>(kr[cl], w);
+      vec_words<16>(kc[cl], w);
 #pragma unroll
       for (int grp = 0; grp < GPL; ++grp) {
         half4_t kop;
@@ -239,10 +304,10 @@ struct Engine {
       }
     }
     const bool partial = j * 16 + 16 > t_end;   // wave-uniform
-    const int t0 = j * 16 + 4 * r;
+    const int tb = j * 16 + r;                  // token of score i: tb + 4 i
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (t0 + i < t_end) ? sacc[i] * sc : -INFINITY;
+    for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * i < t_end) ? sacc[i] * sc : -INFINITY;
     float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     tmax = xor_max(tmax, 16);
     tmax = xor_max(tmax, 32);
@@ -272,7 +337,7 @@ struct Engine {
     if (partial) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const bool ok = t0 + k < t_end;
+        const bool ok = tb + 4 * k < t_end;
 #pragma unroll
         for (int wi = 0; wi < VB / 4; ++wi) vw[k][wi] = ok ? vw[k][wi] : 0u;
       }
@@ -355,10 +420,13 @@ struct Engine {
 
 // ---------------------------------------------------------------- single / split
 
-template <int D, int BS, bool FP8, int NW, bool SPLIT>
+template <int D, int BS, bool FP8, int NW, bool SPLIT, bool NT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU, 8)))
-void decode_kernel(DecodeArgs a) {
-  typedef Engine<D, BS, FP8> En;
+void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
+                   const int32_t* __restrict__ lens) {
+  // The tables arrive as restrict arguments so that their uniform reads stay
+  // scalar loads (as in decode_flat_kernel).
+  typedef Engine<D, BS, FP8, NT> En;
   typedef typename En::VT VT;
   const int lane = threadIdx.x & 63;
   const int wid = uni(threadIdx.x >> 6);
@@ -370,7 +438,7 @@ void decode_kernel(DecodeArgs a) {
   const int s = bid / a.num_kv_heads;
   const int g = a.gqa;
 
-  const int len = clamp_len(a.seq_lens[s], a.len_cap);
+  const int len = clamp_len(lens[s], a.len_cap);
   int t_begin = 0, t_end = len;
   if constexpr (SPLIT) {
     t_begin = part * a.part_tokens;
@@ -380,11 +448,12 @@ void decode_kernel(DecodeArgs a) {
   const int j_begin = t_begin >> 4;           // partition sizes are multiples of 16
   const int j_end = (t_end + 15) >> 4;
 
+  __shared__ __attribute__((aligned(16))) char kstage[NW][En::KST];
   En en;
-  en.init(a, lane);
+  en.init(a, lane, (lds_char*)kstage[wid]);
   en.load_q(a.q + ((int64_t)s * a.num_q_heads + (int64_t)kh * g) * D);
   en.reset();
-  const PairRef pr{a.block_tables + (int64_t)s * a.max_blocks, (len + BS - 1) / BS, len,
+  const PairRef pr{tables + (int64_t)s * a.max_blocks, (len + BS - 1) / BS, len,
                    (int64_t)kh * D * En::E};
 
   // The loads of tile j+NW and the block ids of tile j+2NW are in flight while
@@ -536,8 +605,8 @@ __device__ __forceinline__ int range_of(int64_t t, int64_t T, int64_t NR) {
 // written directly; one cut by range boundaries leaves a partial record per
 // range (slot 0: the range's first sequence, slot 1: its last), merged by
 // flat_merge_kernel.
-template <int D, int BS, bool FP8, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU, 8)))
+template <int D, int BS, bool FP8, int NW, bool NT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_FLAT_WAVES_PER_EU, 8)))
 void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ tables,
                         const int32_t* __restrict__ lens, const _Float16* __restrict__ qs,
                         _Float16* __restrict__ outs, float* __restrict__ slots,
@@ -545,7 +614,7 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   // The read-only arrays arrive as separate restrict arguments: stores to the
   // outputs inside the loop then provably leave the block table alone, so its
   // entries can be read with scalar loads.
-  typedef Engine<D, BS, FP8> En;
+  typedef Engine<D, BS, FP8, NT> En;
   typedef typename En::VT VT;
   extern __shared__ int sm[];                 // [S + 1] tiles before sequence s, then [S] lengths
   const int S = f.num_seqs, Hkv = a.num_kv_heads, g = a.gqa;
@@ -554,43 +623,61 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   const int lane = threadIdx.x & 63;
   const int wid = uni(threadIdx.x >> 6);
 
-  // ---- exclusive prefix of per-sequence tile counts (wave 0; workgroup 0 also
-  // stores it for the merge), lengths in LDS, and zero rows of empty sequences
-  if (wid == 0) {
-    int carry = 0;
-    for (int base = 0; base < S; base += 64) {
-      const int i = base + lane;
-      const int len = i < S ? clamp_len(lens[i], a.len_cap) : 0;
-      const int v = (len + 15) >> 4;
-      int x = v;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-      }
-      if (i < S) {
-        sm_pre[i] = carry + x - v;
-        sm_len[i] = len;
-        if (blockIdx.x == 0) prefix[i] = carry + x - v;
-      }
-      carry += __shfl(x, 63);
-    }
-    if (lane == 0) {
-      sm_pre[S] = carry;
-      if (blockIdx.x == 0) prefix[S] = carry;
-    }
-  }
-  for (int s = blockIdx.x; s < S; s += gridDim.x) {
-    if (clamp_len(lens[s], a.len_cap) == 0) {
-      _Float16* o = outs + (int64_t)s * a.num_q_heads * D;
-      for (int i = threadIdx.x; i < a.num_q_heads * D; i += NW * 64) o[i] = (_Float16)0.f;
-    }
+  // ---- lengths and exclusive prefix of per-sequence tile counts in LDS
+  // (workgroup 0 also stores the prefix for the merge), and zero rows of
+  // empty sequences.  Every thread loads lengths; the scan is workgroup-wide:
+  // thread t sums its run of `per` counts, the run sums are scanned across
+  // waves, then each thread writes its run's prefixes.
+  constexpr int NTH = NW * 64;
+  __shared__ int sm_wsum[NW];
+  for (int i = threadIdx.x; i < S; i += NTH) {
+    const int len = clamp_len(lens[i], a.len_cap);
+    sm_len[i] = len;
+    sm_pre[i + 1] = (len + 15) >> 4;
   }
   __syncthreads();
+  {
+    const int per = (S + NTH - 1) / NTH;
+    const int b0 = min(S, (int)threadIdx.x * per), b1 = min(S, b0 + per);
+    int sum = 0;
+    for (int i = b0; i < b1; ++i) sum += sm_pre[i + 1];
+    int x = sum;                               // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) sm_wsum[wid] = x;
+    __syncthreads();
+    int run = x - sum;
+    for (int w = 0; w < wid; ++w) run += sm_wsum[w];
+    for (int i = b0; i < b1; ++i) {
+      run += sm_pre[i + 1];
+      sm_pre[i + 1] = run;
+    }
+    if (threadIdx.x == 0) sm_pre[0] = 0;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= S; i += NTH) prefix[i] = sm_pre[i];
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+    if (sm_len[s] == 0) {
+      _Float16* o = outs + (int64_t)s * a.num_q_heads * D;
+      for (int i = threadIdx.x; i < a.num_q_heads * D; i += NTH) o[i] = (_Float16)0.f;
+    }
+  }
 
   const int64_t T = sm_pre[S];
   const int64_t NR = f.num_ranges;
+#if PA_FLAT_XCD_REMAP
+  // workgroups are dealt to the 8 XCDs round robin: renumber them so that
+  // consecutive logical workgroups (the KV heads of one range) share an XCD
+  const int nb = gridDim.x, xcd = blockIdx.x & 7, q8 = nb >> 3, r8 = nb & 7;
+  const int lb = xcd * q8 + min(xcd, r8) + (blockIdx.x >> 3);
+  const int gw = lb * NW + wid;
+#else
   const int gw = blockIdx.x * NW + wid;
+#endif
   const int rg = gw / Hkv, kh = gw - (gw / Hkv) * Hkv;
   if (rg >= NR) return;                        // no barrier follows
   const int g0 = (int)((int64_t)rg * T / NR), g1 = (int)((int64_t)(rg + 1) * T / NR);
@@ -613,13 +700,15 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
     if (sm_pre[mid] <= g0) lo = mid; else hi = mid;
   }
   constexpr int ST = PA_FLAT_STAGES;           // tiles in flight per wave, plus one
+  static_assert(ST >= 2, "at least one tile in flight");
   Cur cur[ST + 1];
   cur[0] = {uni(lo), uni(g0 - sm_pre[lo])};
 #pragma unroll
   for (int k = 1; k <= ST; ++k) cur[k] = g0 + k < g1 ? advance(cur[k - 1]) : cur[k - 1];
 
+  __shared__ __attribute__((aligned(16))) char kstage[NW][En::KST];
   En en;
-  en.init(a, lane);
+  en.init(a, lane, (lds_char*)kstage[wid]);
   const int64_t head_off = (int64_t)kh * D * En::E;
   auto ids_of = [&](Cur c) -> Ids {
     const int len = uni(sm_len[c.s]);
@@ -631,6 +720,12 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
 
   en.load_q(q_of(cur[0].s));
   en.reset();
+  // The query rows of a sequence are loaded into qpre when its first tile is
+  // issued, so switching sequences waits on nothing that a tile load does not
+  // already wait on.  One set is held (tagged with its sequence); a sequence
+  // that starts while another's rows are pending loads its rows on switching.
+  half4_t qpre[En::NQ];
+  int q_seq = -1;
   bool seg_from_start = cur[0].j == 0;         // the current segment began at tile 0
   int seg_start = g0;                          // unit index where the current segment began
   int gt = g0;
@@ -648,7 +743,8 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
       en.store_partial(rec_base + (seg_start == g0 ? 0 : 1) * g * (D + 2), lt, a.v_scale);
     }
     if (gt + 1 < g1) {                         // next sequence: new query rows, fresh state
-      en.load_q(q_of(cur[1].s));
+      if (q_seq == cur[1].s) en.take_q(qpre); else en.load_q(q_of(cur[1].s));
+      q_seq = -1;
       en.reset();
       seg_from_start = true;
       seg_start = gt + 1;
@@ -660,11 +756,21 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   uint4 kb[ST][En::NKL];
   VT vb[ST][4];
 #pragma unroll
-  for (int k = 0; k < ST - 1; ++k) en.issue(ids_of(cur[k]), kb[k], vb[k]);
+  for (int k = 0; k < ST - 1; ++k) {
+    if (k > 0 && cur[k].j == 0 && g0 + k < g1 && q_seq < 0) {   // a sequence starts early
+      en.load_q_into(qpre, q_of(cur[k].s));
+      q_seq = cur[k].s;
+    }
+    en.issue(ids_of(cur[k]), kb[k], vb[k]);
+  }
   Ids ids_next = ids_of(cur[ST - 1]);
   for (;;) {
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
+      if (cur[ST - 1].j == 0 && gt + ST - 1 < g1 && q_seq < 0) {
+        en.load_q_into(qpre, q_of(cur[ST - 1].s));
+        q_seq = cur[ST - 1].s;
+      }
       en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST]);
       ids_next = ids_of(cur[ST]);
       en.compute(cur[0].j, uni(sm_len[cur[0].s]), kb[st], vb[st]);
@@ -714,15 +820,16 @@ __global__ __launch_bounds__(D) void flat_merge_kernel(DecodeArgs a, FlatArgs f)
 
 constexpr int kWaves = PA_DECODE_WAVES;
 
-template <int D, int BS, bool FP8>
+template <int D, int BS, bool FP8, bool NT>
 hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int mode,
                         hipStream_t stream) {
   const uint32_t units = (uint32_t)num_seqs * (uint32_t)a.num_kv_heads;
   if (mode == kModeFlat) {
     const size_t lds = sizeof(int) * (2 * (size_t)num_seqs + 1);
     const int64_t waves = (int64_t)f->num_ranges * a.num_kv_heads;
-    hipLaunchKernelGGL((decode_flat_kernel<D, BS, FP8, kWaves>),
-                       dim3((uint32_t)((waves + kWaves - 1) / kWaves)), dim3(kWaves * 64), lds,
+    constexpr int FW = PA_FLAT_WAVES;
+    hipLaunchKernelGGL((decode_flat_kernel<D, BS, FP8, FW, NT>),
+                       dim3((uint32_t)((waves + FW - 1) / FW)), dim3(FW * 64), lds,
                        stream, a, *f, a.block_tables, a.seq_lens, a.q, a.out, f->slots,
                        f->prefix);
     hipError_t e = hipGetLastError();
@@ -730,33 +837,37 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs
     hipLaunchKernelGGL((flat_merge_kernel<D>), dim3((uint32_t)num_seqs * (uint32_t)a.num_q_heads),
                        dim3(D), 0, stream, a, *f);
   } else if (mode == kModeSplit) {
-    hipLaunchKernelGGL((decode_kernel<D, BS, FP8, kWaves, true>),
-                       dim3(units * (uint32_t)a.num_parts), dim3(kWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, BS, FP8, kWaves, true, NT>),
+                       dim3(units * (uint32_t)a.num_parts), dim3(kWaves * 64), 0, stream, a,
+                       a.block_tables, a.seq_lens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((lse_reduce_kernel<D>), dim3((uint32_t)num_seqs * (uint32_t)a.num_q_heads),
                        dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<D, BS, FP8, kWaves, false>), dim3(units), dim3(kWaves * 64),
-                       0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, BS, FP8, kWaves, false, NT>), dim3(units),
+                       dim3(kWaves * 64), 0, stream, a, a.block_tables, a.seq_lens);
   }
   return hipGetLastError();
 }
 
 template <int D, int BS>
-hipError_t launch_bs(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, bool fp8, int mode,
-                     hipStream_t stream) {
-  return fp8 ? launch_typed<D, BS, true>(a, f, num_seqs, mode, stream)
-             : launch_typed<D, BS, false>(a, f, num_seqs, mode, stream);
+hipError_t launch_bs(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, bool fp8,
+                     bool stream_kv, int mode, hipStream_t stream) {
+  if (fp8)
+    return stream_kv ? launch_typed<D, BS, true, true>(a, f, num_seqs, mode, stream)
+                     : launch_typed<D, BS, true, false>(a, f, num_seqs, mode, stream);
+  return stream_kv ? launch_typed<D, BS, false, true>(a, f, num_seqs, mode, stream)
+                   : launch_typed<D, BS, false, false>(a, f, num_seqs, mode, stream);
 }
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int32_t bs, bool fp8,
-                    int mode, hipStream_t stream) {
+                    bool stream_kv, int mode, hipStream_t stream) {
   switch (bs) {
-    case 8: return launch_bs<D, 8>(a, f, num_seqs, fp8, mode, stream);
-    case 16: return launch_bs<D, 16>(a, f, num_seqs, fp8, mode, stream);
-    case 32: return launch_bs<D, 32>(a, f, num_seqs, fp8, mode, stream);
+    case 8: return launch_bs<D, 8>(a, f, num_seqs, fp8, stream_kv, mode, stream);
+    case 16: return launch_bs<D, 16>(a, f, num_seqs, fp8, stream_kv, mode, stream);
+    case 32: return launch_bs<D, 32>(a, f, num_seqs, fp8, stream_kv, mode, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -766,10 +877,12 @@ hipError_t launch_d(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, in
 int decode_waves_per_workgroup() { return kWaves; }
 
 hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
-                         int32_t head_dim, int32_t block_size, bool fp8, int mode,
+                         int32_t head_dim, int32_t block_size, bool fp8, bool stream_kv, int mode,
                          hipStream_t stream) {
-  if (head_dim == 128) return launch_d<128>(a, f, num_seqs, block_size, fp8, mode, stream);
-  if (head_dim == 64) return launch_d<64>(a, f, num_seqs, block_size, fp8, mode, stream);
+  if (head_dim == 128)
+    return launch_d<128>(a, f, num_seqs, block_size, fp8, stream_kv, mode, stream);
+  if (head_dim == 64)
+    return launch_d<64>(a, f, num_seqs, block_size, fp8, stream_kv, mode, stream);
   return hipErrorInvalidValue;
 }
 

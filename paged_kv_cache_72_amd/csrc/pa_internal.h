@@ -20,6 +20,7 @@ struct PoolGeom {
   int32_t elem_bytes;    // 2: binary16, 1: e4m3fn
   float k_scale;
   float v_scale;
+  uint32_t flags;        // pa_kv_pool.flags
 };
 
 struct DecodeArgs {
@@ -62,8 +63,10 @@ hipError_t launch_reshape_and_cache(const PoolGeom& g, const _Float16* k_new,
 hipError_t launch_copy_blocks(const PoolGeom& g, const int64_t* pairs, int64_t n,
                               hipStream_t stream);
 int decode_waves_per_workgroup();
+// stream_kv: read K/V tiles with the streaming cache policy (pools without
+// blocks shared between sequences of the batch).
 hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
-                         int32_t head_dim, int32_t block_size, bool fp8, int mode,
+                         int32_t head_dim, int32_t block_size, bool fp8, bool stream_kv, int mode,
                          hipStream_t stream);
 
 }  // namespace pa

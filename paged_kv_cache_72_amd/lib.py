@@ -19,6 +19,7 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_ALIGNMENT, PA_ERR_WORKSPAC
     0, -1, -2, -3, -4, -5
 PA_KV_F16, PA_KV_FP8_E4M3FN = 0, 1
 PLAN_SINGLE, PLAN_FLAT = 0, 1          # pa_decode_plan codes; >= 16 is a split partition size
+PA_POOL_SHARED_BLOCKS = 1
 _DTYPES = {"f16": PA_KV_F16, "fp8_e4m3fn": PA_KV_FP8_E4M3FN}
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
@@ -37,6 +38,7 @@ class pa_kv_pool(C.Structure):
         ("num_blocks", C.c_int64), ("block_stride_bytes", C.c_int64),
         ("block_size", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
         ("dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
+        ("flags", C.c_uint32), ("reserved", C.c_uint32),
     ]
 
 
@@ -101,7 +103,7 @@ class KVPool:
     def __init__(self, k: torch.Tensor, v: torch.Tensor, block_size: int, num_kv_heads: int,
                  head_dim: int, kv_dtype: str = "f16", k_scale: float = 1.0,
                  v_scale: float = 1.0, num_blocks: Optional[int] = None,
-                 block_stride_bytes: int = 0):
+                 block_stride_bytes: int = 0, shared_blocks: bool = False):
         self.k, self.v = k, v
         self.block_size, self.num_kv_heads, self.head_dim = block_size, num_kv_heads, head_dim
         self.kv_dtype = kv_dtype
@@ -110,12 +112,23 @@ class KVPool:
         self.block_stride_bytes = int(block_stride_bytes)
         self.desc = pa_kv_pool(k.data_ptr(), v.data_ptr(), self.num_blocks,
                                self.block_stride_bytes, block_size, num_kv_heads, head_dim,
-                               _DTYPES[kv_dtype], self.k_scale, self.v_scale)
+                               _DTYPES[kv_dtype], self.k_scale, self.v_scale,
+                               PA_POOL_SHARED_BLOCKS if shared_blocks else 0, 0)
+
+    @property
+    def shared_blocks(self) -> bool:
+        """Blocks may be read by several sequences of a batch (cacheable K/V reads)."""
+        return bool(self.desc.flags & PA_POOL_SHARED_BLOCKS)
+
+    @shared_blocks.setter
+    def shared_blocks(self, on: bool) -> None:
+        self.desc.flags = PA_POOL_SHARED_BLOCKS if on else 0
 
     @classmethod
     def allocate(cls, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
                  kv_dtype: str = "f16", k_scale: float = 1.0, v_scale: float = 1.0,
-                 device="cuda", fill_bits: Optional[int] = None) -> "KVPool":
+                 device="cuda", fill_bits: Optional[int] = None,
+                 shared_blocks: bool = False) -> "KVPool":
         tdt = torch.uint8 if kv_dtype == "fp8_e4m3fn" else torch.int16
         shape = (num_blocks, block_size, num_kv_heads, head_dim)
         k = torch.empty(shape, dtype=tdt, device=device)
@@ -125,7 +138,8 @@ class KVPool:
                                                             else fill_bits)
             k.fill_(fb)
             v.fill_(fb)
-        return cls(k, v, block_size, num_kv_heads, head_dim, kv_dtype, k_scale, v_scale)
+        return cls(k, v, block_size, num_kv_heads, head_dim, kv_dtype, k_scale, v_scale,
+                   shared_blocks=shared_blocks)
 
     @property
     def elem_bytes(self) -> int:

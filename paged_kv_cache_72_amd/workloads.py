@@ -103,6 +103,13 @@ class Workload:
     def new_slots(self) -> np.ndarray:
         return self.tok_slot[self.new_idx]
 
+    @property
+    def has_shared_blocks(self) -> bool:
+        """True when some physical block is listed by more than one sequence."""
+        nb = (self.seq_lens.astype(np.int64) + self.block_size - 1) // self.block_size
+        ids = np.concatenate([self.block_tables[s, :nb[s]] for s in range(self.num_seqs)])
+        return bool(np.unique(ids).size < ids.size)
+
 
 # --------------------------------------------------------------------------
 # drawing helpers

@@ -29,7 +29,8 @@ class DeviceCase:
         self.w = w
         fill = W.poison_pool_bits(w) if poison else 0
         self.pool = L.KVPool.allocate(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
-                                      w.kv_dtype, w.k_scale, w.v_scale, device, fill_bits=fill)
+                                      w.kv_dtype, w.k_scale, w.v_scale, device, fill_bits=fill,
+                                      shared_blocks=w.has_shared_blocks)
         self.fill = fill
         self.q = torch.from_numpy(w.q).to(device)
         self.bt = torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(device)

@@ -126,7 +126,7 @@ def test_workspace_size_formula(so):
     assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, P) == ml + rows * D * 4
     assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, -1) == 0
     # flat: prefix [S+1] int32, then 2 records of gqa*(D+2) floats per wave
-    ranges = min(3072 // 8, S * (T // 16) // 8)
+    ranges = min(2048 // 8, S * (T // 16) // 8)
     pre = ((S + 1) * 4 + 255) // 256 * 256
     assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, 1) == \
         pre + ranges * 8 * 2 * 4 * 130 * 4
@@ -145,6 +145,14 @@ def test_plan_choices(so, S, Hkv, Hq, bs, maxlen):
     assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 1) == L.PLAN_FLAT
     assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, -1) == L.PLAN_SINGLE
     assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 64) == 64
+
+
+def test_pool_flags_validated(so):
+    assert so.pa_decode_plan(C.byref(_pool(flags=L.PA_POOL_SHARED_BLOCKS)), 4, 32, 100, 0) == \
+        L.PLAN_FLAT
+    assert so.pa_decode_plan(C.byref(_pool(flags=2)), 4, 32, 100, 0) == L.PA_ERR_INVALID_ARG
+    assert "flags" in L.pa_last_error()
+    assert so.pa_decode_plan(C.byref(_pool(reserved=1)), 4, 32, 100, 0) == L.PA_ERR_INVALID_ARG
 
 
 def test_plan_falls_back_past_flat_limit(so):

@@ -136,3 +136,17 @@ def test_large_scores_stay_finite():
     for part in (-1, 32):
         y = DeviceCase(w, poison=True).decode(part).cpu().numpy()
         check_close(w, y, _ref(w, oracle_pool(w)), f"big/p{part}")
+
+
+@pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "fp8_d128_bs32", "d64_bs32_g16"])
+@pytest.mark.parametrize("part", [-1, 1, 64])
+def test_cache_policy_flag_changes_no_bits(name, part):
+    """Streaming and cacheable K/V reads must give identical outputs."""
+    w, _ = _case(name)
+    dc = DeviceCase(w, poison=True)
+    dc.pool.shared_blocks = False
+    a = dc.decode(part).clone()
+    dc.pool.shared_blocks = True
+    b = dc.decode(part, out=torch.empty_like(a))
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
