@@ -92,6 +92,55 @@ def traffic_entry(config: str):
     return e.get("bytes_per_launch")
 
 
+DECODE_KERNELS = ("decode_flat_kernel", "flat_merge_kernel", "decode_kernel", "lse_reduce_kernel")
+
+
+def ingest_counters(fetch_csv: str, write_csv: str, calib_gib: float, config: str,
+                    commands: list) -> dict:
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE, both with --calib-copy-gib) into HBM bytes per pa_decode call.
+    Each counter is scaled by what it reads for the plain device copies of
+    calib_gib GiB that the script runs last (torch's copy kernel)."""
+    import csv
+
+    def load(path):
+        rows = list(csv.DictReader(open(path)))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return rows
+
+    out = {}
+    for key, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = load(path)
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]][-3:]
+        kib_copy = sum(float(r["Counter_Value"]) for r in copies) / len(copies)
+        factor = calib_gib * (1 << 30) / (kib_copy * 1024)
+        dec = [r for r in rows if any(k in r["Kernel_Name"] for k in DECODE_KERNELS)]
+        calls = sum(1 for r in dec if ("decode_flat_kernel" in r["Kernel_Name"] or
+                                       "decode_kernel" in r["Kernel_Name"]))
+        per_kernel = {}
+        for r in dec:
+            name = next(k for k in DECODE_KERNELS if k in r["Kernel_Name"])
+            per_kernel.setdefault(name, []).append(float(r["Counter_Value"]))
+        kib_per_call = sum(sum(v) for v in per_kernel.values()) / calls
+        out[key] = {"counter": rows[0]["Counter_Name"], "kib_per_call_raw": round(kib_per_call, 2),
+                    "copy_kib_raw": round(kib_copy, 2), "factor": round(factor, 5),
+                    "bytes_per_call": int(kib_per_call * 1024 * factor),
+                    "kib_raw_by_kernel": {k: round(sum(v) / len(v), 2)
+                                          for k, v in per_kernel.items()}}
+    entry = {"kernel_source_hash": kernel_source_hash(),
+             "bytes_per_launch": out["fetch"]["bytes_per_call"] + out["write"]["bytes_per_call"],
+             "fetch": out["fetch"], "write": out["write"], "commands": commands}
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        d = {}
+    d[config] = entry
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(d, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return entry
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,7 +153,18 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: write the HBM traffic of --config's pa_decode call into "
+                         "profiles/pa_decode_traffic.json from two rocprofv3 --pmc runs")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --ingest-counters: the profiler commands, recorded verbatim")
     args = ap.parse_args()
+
+    if args.ingest_counters:
+        e = ingest_counters(*args.ingest_counters, args.calib_copy_gib or 1.0, args.config,
+                            args.command)
+        print(json.dumps(e, indent=1))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path shards by sequence or KV head "

@@ -76,7 +76,8 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
 }
 
 // Planning.  The flat schedule balances any mix of context lengths, so it is
-// the default; it keeps per-sequence prefix and lengths in LDS (2 S + 1 ints).
+// the default unless the batch is many short contexts; it keeps per-sequence
+// prefix and lengths in LDS (2 S + 1 ints).
 constexpr int32_t kFlatMaxSeqs = 8000;
 #ifndef PA_FLAT_MAX_WAVES
 #define PA_FLAT_MAX_WAVES 2048                // 256 CUs x 4 SIMDs x 2 waves
@@ -124,7 +125,11 @@ int plan(const pa_kv_pool* pool, int32_t S, int32_t Hq, int32_t max_seq_len, int
   pl->part = 0;
   pl->num_parts = 0;
   pl->waves = 0;
-  if (req == kPlanFlat || (req == 0 && S <= kFlatMaxSeqs)) {
+  // Many short contexts: one workgroup per (sequence, KV head) already fills
+  // the GPU several times over and no context is long enough to unbalance it,
+  // and the single pass has no range bookkeeping.
+  const bool many_short = units >= 4096 && max_seq_len <= 1024;
+  if (req == kPlanFlat || (req == 0 && !many_short && S <= kFlatMaxSeqs)) {
     if (S > kFlatMaxSeqs)
       return fail(PA_ERR_UNSUPPORTED, "flat schedule supports at most %d sequences", kFlatMaxSeqs);
     // ranges: about kFlatMaxWaves waves in all, at least kFlatMinTiles units each

@@ -141,7 +141,9 @@ def test_workspace_size_formula(so):
 ])
 def test_plan_choices(so, S, Hkv, Hq, bs, maxlen):
     p = _pool(num_kv_heads=Hkv, block_size=bs)
-    assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 0) == L.PLAN_FLAT
+    many_short = S * Hkv >= 4096 and maxlen <= 1024
+    assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 0) == \
+        (L.PLAN_SINGLE if many_short else L.PLAN_FLAT)
     assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 1) == L.PLAN_FLAT
     assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, -1) == L.PLAN_SINGLE
     assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 64) == 64
