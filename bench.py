@@ -48,16 +48,35 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def unique_kv_tokens(w) -> int:
+    """Token rows the batch reads when every physical block is counted once:
+    a block listed by several sequences contributes the most slots any of them
+    uses."""
+    bs = w.block_size
+    used = {}
+    for s in range(w.num_seqs):
+        n = int(w.seq_lens[s])
+        for j in range((n + bs - 1) // bs):
+            b = int(w.block_tables[s, j])
+            used[b] = max(used.get(b, 0), min(bs, n - j * bs))
+    return sum(used.values())
+
+
 def alg_bytes(w) -> dict:
-    """Bytes the method itself must move (no partials, no masked slots)."""
+    """Bytes the method itself must move (no partials, no masked slots).  With
+    blocks shared between sequences the K/V term counts each block once (the
+    logical figure, every sequence reading its whole context, is kept too)."""
     e = w.kv_elem_bytes
     lens = w.seq_lens.astype(np.int64)
-    kv = int(lens.sum()) * w.num_kv_heads * w.head_dim * e * 2
+    row = w.num_kv_heads * w.head_dim * e * 2
+    kv_logical = int(lens.sum()) * row
+    kv = unique_kv_tokens(w) * row if w.has_shared_blocks else kv_logical
     qo = w.num_seqs * w.num_q_heads * w.head_dim * 2 * 2
     tables = int(((lens + w.block_size - 1) // w.block_size).sum()) * 4 + w.num_seqs * 4
     T = int(w.new_idx.size)
     write = T * w.num_kv_heads * w.head_dim * (2 * 2 + 2 * e) + T * 8
-    return {"kv": kv, "decode": kv + qo + tables, "write": write}
+    return {"kv": kv, "kv_logical": kv_logical, "decode": kv + qo + tables,
+            "decode_logical": kv_logical + qo + tables, "write": write}
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
@@ -264,6 +283,7 @@ def main() -> int:
         "kv_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_step * 1e-3), 1),
         "decode_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "alg_bytes_per_step": step_bytes,
+        "logical_decode_bytes": b["decode_logical"],
         "roofline": {"bound": "hbm", "kernel": "pa_decode", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
