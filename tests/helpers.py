@@ -98,6 +98,7 @@ def check_close(w: W.Workload, y: np.ndarray, r: np.ndarray, what: str = "") -> 
     stats = {"max_abs": float(err.max()) if err.size else 0.0,
              "max_rel": float((err / np.maximum(np.abs(r), 0.05)).max()) if err.size else 0.0,
              "rms_ref": float(np.sqrt((r ** 2).mean())) if r.size else 0.0}
+    stats["max_abs_over_rms_ref"] = stats["max_abs"] / stats["rms_ref"] if stats["rms_ref"] else 0.0
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
                            f"worst {stats}")
     return stats

@@ -3,7 +3,11 @@ the benchmark uses (the library's own partition choice) and in the forced
 single and split passes.  The oracle evaluates a seeded sample of
 (sequence, KV head) units -- all their query heads -- plus the shortest and
 longest sequences; the pool written by the library is compared bit for bit
-with the oracle's scatter over the sampled sequences' blocks."""
+with the oracle's scatter over the sampled sequences' blocks.  Every workload
+also runs two structured variants under the same gate (values offset by +1,
+so the output sits near 1 and an all-zero output fails; keys planted along
+one query head at block, partition and end positions), with NaN in every
+unused slot and padding block throughout."""
 import zlib
 
 import numpy as np
@@ -60,3 +64,31 @@ def test_full_size_parity(name, make, nunits, parts):
         st = check_close(w, y[idx], r[idx], f"{name}/p{part}")
         say(f"  {st}")
         assert np.all(np.isfinite(y))
+
+
+VARIANTS = [(name, make, nunits, parts[:1] + ([512] if name == "long_fp8" else []))
+            for name, make, nunits, parts in CONFIGS if name != "tiny"]
+
+
+@pytest.mark.parametrize("variant", ["v_offset", "needles"])
+@pytest.mark.parametrize("name,make,nunits,parts", VARIANTS, ids=[c[0] for c in VARIANTS])
+def test_full_size_structured_variants(name, make, nunits, parts, variant):
+    say(f"config {name} {variant}: generating")
+    w0 = make()
+    w = W.with_v_offset(w0, 1.0) if variant == "v_offset" else W.with_needles(w0, 64.0)
+    del w0
+    units = sample_units(w, max(4, nunits // 2), seed=zlib.crc32((name + variant).encode()))
+    seqs = sorted({s for s, _ in units})
+    dc = DeviceCase(w, poison=True)
+    tok = seq_token_indices(w, seqs) if w.tok_slot.size > 500_000 else None
+    hp = oracle_pool(w, poison=True, token_idx=tok)
+    say(f"config {name} {variant}: oracle on {len(units)} units")
+    r = O.decode(hp, w.q, w.block_tables, w.seq_lens, w.scale, units=units)
+    idx = tuple(np.array(unit_rows(w, units)).T)
+    for part in parts:
+        say(f"config {name} {variant}: decode partition={part}")
+        y = dc.decode(part).cpu().numpy()
+        say(f"  {check_close(w, y[idx], r[idx], f'{name}/{variant}/p{part}')}")
+    if variant == "v_offset":
+        with pytest.raises(AssertionError):
+            check_close(w, np.zeros_like(y[idx]), r[idx])
