@@ -783,11 +783,14 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   }
 }
 
-// One workgroup of head_dim threads per (sequence, query head): if the
-// sequence was cut by range boundaries, merge its per-range records by
-// log-sum-exp in range order; otherwise the decode kernel already wrote it.
-template <int D>
-__global__ __launch_bounds__(D) void flat_merge_kernel(DecodeArgs a, FlatArgs f) {
+// One workgroup per (sequence, query head): if the sequence was cut by range
+// boundaries, merge its per-range records by log-sum-exp.  The NG thread
+// groups of the workgroup (head_dim threads each) take every NG-th record and
+// fold them online, loads of four records in flight; the groups' (M, L, O)
+// are then combined in LDS in group order, so the result is deterministic.
+// NG grows with the expected number of records per sequence.
+template <int D, int NG>
+__global__ __launch_bounds__(NG * D) void flat_merge_kernel(DecodeArgs a, FlatArgs f) {
   const int row = blockIdx.x;
   const int s = row / a.num_q_heads, h = row - s * a.num_q_heads;
   const int g = a.gqa, kh = h / g, hl = h - kh * g;
@@ -796,24 +799,41 @@ __global__ __launch_bounds__(D) void flat_merge_kernel(DecodeArgs a, FlatArgs f)
   if (end == pre) return;
   const int64_t NR = f.num_ranges;
   const int r_first = range_of(pre, T, NR), r_last = range_of(end - 1, T, NR);
-  if (r_first == r_last) return;
+  if (r_first == r_last) return;               // written by the decode kernel
   const bool first_is_last_slot = (int64_t)r_first * T / NR < pre;
   const int rec = g * (D + 2);
-  const int d = threadIdx.x;
+  const int d = threadIdx.x % D, grp = threadIdx.x / D;
   float M = kNegBig, L = 0.f, O = 0.f;
 #pragma unroll 4
-  for (int r = r_first; r <= r_last; ++r) {
+  for (int r = r_first + grp; r <= r_last; r += NG) {
     const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
     const float* p = f.slots + ((int64_t)(r * a.num_kv_heads + kh) * 2 + slot) * rec;
     const float2 ml = ((const float2*)(p + g * D))[hl];
     const float ov = p[hl * D + d];
     const float mn = fmaxf(M, ml.x);
-    const float sa = __builtin_amdgcn_exp2f(M - mn), sb = __builtin_amdgcn_exp2f(ml.x - mn);
-    L = L * sa + ml.y * sb;
-    O = O * sa + ml.y * sb * ov;
+    const float sa = __builtin_amdgcn_exp2f(M - mn), sb = ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
+    L = L * sa + sb;
+    O = O * sa + sb * ov;
     M = mn;
   }
-  a.out[(int64_t)row * D + d] = (_Float16)(L > 0.f ? O / L : 0.f);
+  __shared__ float sm_o[NG][D];
+  __shared__ float2 sm_ml[NG];
+  sm_o[grp][d] = O;
+  if (d == 0) sm_ml[grp] = make_float2(M, L);
+  __syncthreads();
+  if (grp == 0) {
+    float Mt = sm_ml[0].x;
+#pragma unroll
+    for (int q = 1; q < NG; ++q) Mt = fmaxf(Mt, sm_ml[q].x);
+    float Lt = 0.f, Ot = 0.f;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const float w = __builtin_amdgcn_exp2f(sm_ml[q].x - Mt);
+      Lt += sm_ml[q].y * w;
+      Ot += sm_o[q][d] * w;
+    }
+    a.out[(int64_t)row * D + d] = (_Float16)(Lt > 0.f ? Ot / Lt : 0.f);
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -834,8 +854,17 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs
                        f->prefix);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((flat_merge_kernel<D>), dim3((uint32_t)num_seqs * (uint32_t)a.num_q_heads),
-                       dim3(D), 0, stream, a, *f);
+    // records per sequence ~ ranges / sequences: about 8 per thread group
+    const int64_t per_seq = num_seqs > 0 ? f->num_ranges / num_seqs : 0;
+    const dim3 mgrid((uint32_t)num_seqs * (uint32_t)a.num_q_heads);
+    if (per_seq < 16)
+      hipLaunchKernelGGL((flat_merge_kernel<D, 1>), mgrid, dim3(D), 0, stream, a, *f);
+    else if (per_seq < 32)
+      hipLaunchKernelGGL((flat_merge_kernel<D, 2>), mgrid, dim3(2 * D), 0, stream, a, *f);
+    else if (per_seq < 64)
+      hipLaunchKernelGGL((flat_merge_kernel<D, 4>), mgrid, dim3(4 * D), 0, stream, a, *f);
+    else
+      hipLaunchKernelGGL((flat_merge_kernel<D, 8>), mgrid, dim3(8 * D), 0, stream, a, *f);
   } else if (mode == kModeSplit) {
     hipLaunchKernelGGL((decode_kernel<D, BS, FP8, kWaves, true, NT>),
                        dim3(units * (uint32_t)a.num_parts), dim3(kWaves * 64), 0, stream, a,
