@@ -438,6 +438,12 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
   const int s = bid / a.num_kv_heads;
   const int g = a.gqa;
 
+  // The first two tiles' block ids are read together with the length (their
+  // logical blocks clamped to the table row, which the host bounds, rather
+  // than to the length), so the first K/V loads wait on one round trip.
+  const int j0 = (SPLIT ? part * a.part_tokens : 0) / 16 + wid;
+  const int64_t head_off = (int64_t)kh * D * Engine<D, BS, FP8, NT>::E;
+  const PairRef row{tables + (int64_t)s * a.max_blocks, a.max_blocks, 0, head_off};
   const int len = clamp_len(lens[s], a.len_cap);
   int t_begin = 0, t_end = len;
   if constexpr (SPLIT) {
@@ -453,8 +459,8 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
   en.init(a, lane, (lds_char*)kstage[wid]);
   en.load_q(a.q + ((int64_t)s * a.num_q_heads + (int64_t)kh * g) * D);
   en.reset();
-  const PairRef pr{tables + (int64_t)s * a.max_blocks, (len + BS - 1) / BS, len,
-                   (int64_t)kh * D * En::E};
+  const PairRef pr{tables + (int64_t)s * a.max_blocks, (len + BS - 1) / BS, len, head_off};
+  const Ids ids0 = en.tile_ids(row, j0), ids1 = en.tile_ids(row, j0 + NW);
 
   // The loads of tile j+NW and the block ids of tile j+2NW are in flight while
   // tile j is computed; two register sets alternate.  Past the end of the
@@ -465,8 +471,8 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
   int j = j_begin + wid;
   if (j < j_end) {
     const int j_last = j_end - 1;
-    en.issue(en.tile_ids(pr, j), kA, vA);
-    Ids ids_b = en.tile_ids(pr, min(j + NW, j_last));
+    en.issue(ids0, kA, vA);
+    Ids ids_b = j + NW <= j_last ? ids1 : ids0;  // past the end: repeat a loaded tile
     for (;;) {
       en.issue(ids_b, kB, vB);
       const Ids ids_a = en.tile_ids(pr, min(j + 2 * NW, j_last));
