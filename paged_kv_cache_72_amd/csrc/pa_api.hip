@@ -79,10 +79,21 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
 // the default unless the batch is many short contexts; it keeps per-sequence
 // prefix and lengths in LDS (2 S + 1 ints).
 constexpr int32_t kFlatMaxSeqs = 8000;
-#ifndef PA_FLAT_MAX_WAVES
-#define PA_FLAT_MAX_WAVES 2048                // 256 CUs x 4 SIMDs x 2 waves
+// Waves of the flat schedule: enough that about 8 MiB of K/V tiles are in
+// flight (each wave keeps about one 16-token tile of K and V in flight), at
+// least one wave per SIMD and at most the two per SIMD the kernel's registers
+// allow.  Measured: for fp16 head_dim 128 (8 KiB tiles) 1024 waves beat 2048;
+// for 4 KiB tiles (fp8, or head_dim 64) 2048 waves are needed.
+int64_t flat_waves(const pa::PoolGeom& g) {
+#ifdef PA_FLAT_MAX_WAVES
+  (void)g;
+  return PA_FLAT_MAX_WAVES;
+#else
+  const int64_t tile_bytes = 16 * (int64_t)g.head_dim * g.elem_bytes * 2;
+  int64_t w = (8 << 20) / tile_bytes;
+  return w < 1024 ? 1024 : (w > 2048 ? 2048 : w);
 #endif
-constexpr int64_t kFlatMaxWaves = PA_FLAT_MAX_WAVES;
+}
 constexpr int64_t kFlatMinTiles = 8;         // keep at least this many tiles per range
 constexpr int32_t kPlanFlat = 1;             // pa_decode_plan's code for the flat schedule
 
@@ -132,9 +143,9 @@ int plan(const pa_kv_pool* pool, int32_t S, int32_t Hq, int32_t max_seq_len, int
   if (req == kPlanFlat || (req == 0 && !many_short && S <= kFlatMaxSeqs)) {
     if (S > kFlatMaxSeqs)
       return fail(PA_ERR_UNSUPPORTED, "flat schedule supports at most %d sequences", kFlatMaxSeqs);
-    // ranges: about kFlatMaxWaves waves in all, at least kFlatMinTiles units each
+    // ranges: about flat_waves() waves in all, at least kFlatMinTiles units each
     const int64_t per_head_ub = (int64_t)S * cdiv64(max_seq_len, 16);
-    int64_t ranges = kFlatMaxWaves / g->num_kv_heads;
+    int64_t ranges = flat_waves(*g) / g->num_kv_heads;
     if (ranges > per_head_ub / kFlatMinTiles) ranges = per_head_ub / kFlatMinTiles;
     if (ranges < 1) ranges = 1;
     pl->mode = pa::kModeFlat;

@@ -126,7 +126,7 @@ def test_workspace_size_formula(so):
     assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, P) == ml + rows * D * 4
     assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, -1) == 0
     # flat: prefix [S+1] int32, then 2 records of gqa*(D+2) floats per wave
-    ranges = min(2048 // 8, S * (T // 16) // 8)
+    ranges = min(1024 // 8, S * (T // 16) // 8)    # 1024 waves for 8 KiB fp16 tiles
     pre = ((S + 1) * 4 + 255) // 256 * 256
     assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, 1) == \
         pre + ranges * 8 * 2 * 4 * 130 * 4
@@ -147,6 +147,20 @@ def test_plan_choices(so, S, Hkv, Hq, bs, maxlen):
     assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 1) == L.PLAN_FLAT
     assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, -1) == L.PLAN_SINGLE
     assert so.pa_decode_plan(C.byref(p), S, Hq, maxlen, 64) == 64
+
+
+def test_flat_wave_count_follows_tile_bytes(so):
+    """About 8 MiB of 16-token K/V tiles in flight, 1024..2048 waves: the flat
+    workspace holds two records per wave, so its size shows the wave count."""
+    S, Hq, T = 64, 32, 4096
+    for D, dt, waves in ((128, L.PA_KV_F16, 1024), (128, L.PA_KV_FP8_E4M3FN, 2048),
+                         (64, L.PA_KV_F16, 2048), (64, L.PA_KV_FP8_E4M3FN, 2048)):
+        p = _pool(head_dim=D, dtype=dt, k_scale=0.5, v_scale=0.5)
+        ranges = min(waves // 8, S * (T // 16) // 8)
+        pre = (S + 1) * 4
+        pre = (pre + 255) // 256 * 256
+        assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, 1) == \
+            pre + ranges * 8 * 2 * 4 * (D + 2) * 4
 
 
 def test_pool_flags_validated(so):
