@@ -253,6 +253,35 @@ def main() -> int:
     dec_ms = [a.elapsed_time(b) for a, b in events]
     dec_avg = float(np.mean(dec_ms))
 
+    # ---- the two write paths, timed on their own (after the decode timing)
+    def event_avg_ms(fn, reps=50):
+        for i in range(5):
+            fn(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i in range(reps):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(c) for a, c in ev]))
+
+    rc_ms = event_avg_ms(lambda i: L.pa_reshape_and_cache(pools[i % len(pools)], k_new, v_new,
+                                                           slot_new, stream))
+    pairs = w.cow_pairs
+    if pairs is None:   # copy 256 context blocks into blocks no table lists
+        nb_used = (w.seq_lens.astype(np.int64) + w.block_size - 1) // w.block_size
+        used = np.unique(np.concatenate([w.block_tables[s_, :nb_used[s_]]
+                                         for s_ in range(w.num_seqs)]))
+        free = np.setdiff1d(np.arange(w.num_blocks), used)
+        n_p = int(min(256, used.size, free.size))
+        pairs = np.stack([used[:n_p], free[:n_p]], axis=1).astype(np.int64)
+    pairs_d = torch.from_numpy(np.ascontiguousarray(pairs)).to(dev)
+    cb_ms = event_avg_ms(lambda i: L.pa_copy_blocks(pools[i % len(pools)], pairs_d, stream))
+    blk_bytes = w.block_size * w.num_kv_heads * w.head_dim * w.kv_elem_bytes
+    cb_bytes = int(pairs.shape[0]) * 2 * blk_bytes * 2
+
     if args.calib_copy_gib > 0:
         n = int(args.calib_copy_gib * (1 << 30))
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -283,6 +312,12 @@ def main() -> int:
         "kv_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_step * 1e-3), 1),
         "decode_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "alg_bytes_per_step": step_bytes,
+        "reshape_and_cache": {"tokens": int(w.new_idx.size), "avg_ms": round(rc_ms, 5),
+                              "alg_bytes": b["write"],
+                              "GB_per_s": round(b["write"] / (rc_ms * 1e-3) / 1e9, 1)},
+        "copy_blocks": {"pairs": int(pairs.shape[0]), "avg_ms": round(cb_ms, 5),
+                        "alg_bytes": cb_bytes,
+                        "GB_per_s": round(cb_bytes / (cb_ms * 1e-3) / 1e9, 1)},
         "logical_decode_bytes": b["decode_logical"],
         "roofline": {"bound": "hbm", "kernel": "pa_decode", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",

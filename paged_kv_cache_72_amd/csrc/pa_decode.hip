@@ -66,9 +66,6 @@ namespace {
 #ifndef PA_FLAT_WAVES_PER_EU
 #define PA_FLAT_WAVES_PER_EU 2
 #endif
-#ifndef PA_FLAT_XCD_REMAP
-#define PA_FLAT_XCD_REMAP 0
-#endif
 #ifndef PA_FLAT_STAGES
 #define PA_FLAT_STAGES 2      // flat schedule: tiles in flight per wave, plus one
 #endif
@@ -675,15 +672,7 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
 
   const int64_t T = sm_pre[S];
   const int64_t NR = f.num_ranges;
-#if PA_FLAT_XCD_REMAP
-  // workgroups are dealt to the 8 XCDs round robin: renumber them so that
-  // consecutive logical workgroups (the KV heads of one range) share an XCD
-  const int nb = gridDim.x, xcd = blockIdx.x & 7, q8 = nb >> 3, r8 = nb & 7;
-  const int lb = xcd * q8 + min(xcd, r8) + (blockIdx.x >> 3);
-  const int gw = lb * NW + wid;
-#else
   const int gw = blockIdx.x * NW + wid;
-#endif
   const int rg = gw / Hkv, kh = gw - (gw / Hkv) * Hkv;
   if (rg >= NR) return;                        // no barrier follows
   const int g0 = (int)((int64_t)rg * T / NR), g1 = (int)((int64_t)(rg + 1) * T / NR);
