@@ -13,26 +13,27 @@
 // The tile engine (one copy of the math, used by every schedule):
 //   * Work unit: 16 consecutive tokens of one (sequence, KV head) pair, for
 //     ALL gqa query heads of that KV head, so every K/V byte leaves HBM once.
-//   * Scores S[16 tokens x 16 heads]: one 16x16x16 f16 MFMA per 16 head dims.
-//     Lane (row r, column c) loads 16 contiguous bytes of token c's key (the A
-//     operand) and holds the same dims of query head c (the B operand), so K
-//     feeds the matrix core straight from its 128-bit load.  Heads beyond gqa
-//     are zero columns.
-//   * The MFMA result leaves lane (r, c) with the scores of tokens 4r..4r+3 for
-//     head c -- exactly the A-operand layout P[head][token] of the P.V MFMA.
-//     V arrives as 4 rows of D/16 contiguous elements per lane (tokens 4r+k,
-//     dims c*D/16..) and is transposed inside the lane into B operands
-//     V[4r..4r+3][dim]; D/16 MFMAs give P.V.  P and V enter the matrix core as
+//   * Loads: every K and V load instruction covers whole token rows of the
+//     head (64 lanes x 16 B = four 256-byte rows for fp16 head_dim 128), which
+//     the memory system serves far better than pieces of many rows.  A tile's
+//     base is a scalar buffer descriptor over its 16 rows; lanes add constant
+//     offsets.  Block ids are read with scalar loads one tile ahead, and the
+//     next tile's loads are always in flight while the current one is computed.
+//     Single-reader pools are read with the streaming cache policy.
+//   * Scores S[16 tokens x 16 heads]: one 16x16x16 f16 MFMA per 16 head dims
+//     with K as the A operand (one token per lane) and the query heads as B
+//     (heads beyond gqa are zero columns).  The row-wise K tile goes through a
+//     per-wave, XOR-swizzled LDS buffer to reach that layout; the token order
+//     is permuted so that score lane (r, c) holds tokens r, r+4, r+8, r+12 of
+//     head c -- the A-operand layout of the P.V MFMA and the rows that value
+//     load k = 0..3 gave the same lane.  V is transposed inside the lane into
+//     B operands; D/16 MFMAs give P.V.  P and V enter the matrix core as
 //     binary16 (fp8 pools are widened exactly first), accumulation is fp32.
 //   * Softmax state per head: running max m (log2 units), per-lane partial sum
 //     l and the P.V accumulators.  The max moves (and l, acc are rescaled) only
 //     when a tile's max exceeds it by more than 2^8, so P <= 256 fits binary16.
 //   * Masked tokens get score -inf by a select and their V rows are zeroed by a
 //     select, so NaN in unused slots never reaches a valid output.
-//   * Loads: a tile's base is a scalar buffer descriptor over its 16 token rows;
-//     lanes add constant 32-bit offsets.  Block ids are read with scalar loads
-//     one tile ahead; the next tile's loads are always in flight while the
-//     current one is computed.
 //
 // Schedules:
 //   * single pass   -- one workgroup per (sequence, KV head); its waves take
