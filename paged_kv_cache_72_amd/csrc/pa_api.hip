@@ -34,8 +34,10 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
   if (!p->k_base || !p->v_base) return fail(PA_ERR_INVALID_ARG, "pool k_base/v_base is NULL");
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", p->head_dim);
-  if (p->block_size != 8 && p->block_size != 16 && p->block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (8, 16, 32)", p->block_size);
+  if (p->block_size != 8 && p->block_size != 16 && p->block_size != 32 && p->block_size != 64 &&
+      p->block_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (8, 16, 32, 64, 128)",
+                p->block_size);
   if (p->dtype != PA_KV_F16 && p->dtype != PA_KV_FP8_E4M3FN)
     return fail(PA_ERR_UNSUPPORTED, "kv dtype %d not supported", p->dtype);
   if (p->num_kv_heads < 1 || p->num_kv_heads > 4096)

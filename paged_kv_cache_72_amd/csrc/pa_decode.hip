@@ -893,6 +893,8 @@ hipError_t launch_d(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, in
     case 8: return launch_bs<D, 8>(a, f, num_seqs, fp8, stream_kv, mode, stream);
     case 16: return launch_bs<D, 16>(a, f, num_seqs, fp8, stream_kv, mode, stream);
     case 32: return launch_bs<D, 32>(a, f, num_seqs, fp8, stream_kv, mode, stream);
+    case 64: return launch_bs<D, 64>(a, f, num_seqs, fp8, stream_kv, mode, stream);
+    case 128: return launch_bs<D, 128>(a, f, num_seqs, fp8, stream_kv, mode, stream);
   }
   return hipErrorInvalidValue;
 }

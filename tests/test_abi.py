@@ -61,7 +61,8 @@ def test_null_pool_rejected(so):
 
 @pytest.mark.parametrize("field,value,code", [
     ("head_dim", 96, L.PA_ERR_UNSUPPORTED),
-    ("block_size", 64, L.PA_ERR_UNSUPPORTED),
+    ("block_size", 48, L.PA_ERR_UNSUPPORTED),
+    ("block_size", 256, L.PA_ERR_UNSUPPORTED),
     ("dtype", 7, L.PA_ERR_UNSUPPORTED),
     ("k_base", FAKE + 8, L.PA_ERR_ALIGNMENT),
     ("block_stride_bytes", 1000, L.PA_ERR_INVALID_ARG),
@@ -161,6 +162,11 @@ def test_flat_wave_count_follows_tile_bytes(so):
         pre = (pre + 255) // 256 * 256
         assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, 1) == \
             pre + ranges * 8 * 2 * 4 * (D + 2) * 4
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32, 64, 128])
+def test_every_listed_block_size_is_accepted(so, bs):
+    assert so.pa_decode_plan(C.byref(_pool(block_size=bs)), 4, 32, 100, 0) >= 0
 
 
 def test_pool_flags_validated(so):

@@ -30,6 +30,10 @@ SHAPES = {
     "fp8_d128_bs16_g7": lambda: W.custom("s", 58, EDGE_LENS, 28, 4, 128, 16,
                                          kv_dtype="fp8_e4m3fn"),
     "fp8_d64_bs8": lambda: W.custom("s", 59, EDGE_LENS, 8, 2, 64, 8, kv_dtype="fp8_e4m3fn"),
+    "d128_bs64_g4": lambda: W.custom("s", 62, EDGE_LENS, 32, 8, 128, 64),
+    "d64_bs128_g2": lambda: W.custom("s", 63, EDGE_LENS, 8, 4, 64, 128),
+    "fp8_d128_bs128_g4": lambda: W.custom("s", 64, EDGE_LENS, 16, 4, 128, 128,
+                                          kv_dtype="fp8_e4m3fn"),
 }
 
 _cache = {}
