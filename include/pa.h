@@ -24,7 +24,8 @@
  *     ("GPU memory & KV cache", copy-on-write steps and incident code).
  *   - fp8 KV is quantised on write and dequantised inside the attention kernel
  *     on read ("KV Cache memory core", section 4.4); the format is OCP e4m3fn
- *     ("Paging saves no KV bytes", section 4) with one fp32 scale per pool.
+ *     ("Paging saves no KV bytes", section 4) or OCP e5m2 ("vLLM intro part 2",
+ *     section 7), with one fp32 scale per pool.
  *
  * Conventions for every entry point:
  *   - All pointers named as device pointers point to device memory the caller
@@ -62,7 +63,10 @@ typedef enum {
 
 typedef enum {
   PA_KV_F16 = 0,        /* IEEE binary16 elements                                */
-  PA_KV_FP8_E4M3FN = 1  /* OCP e4m3fn bytes; value = e4m3(byte) * pool scale      */
+  PA_KV_FP8_E4M3FN = 1, /* OCP e4m3fn bytes; value = e4m3(byte) * pool scale      */
+  PA_KV_FP8_E5M2 = 2    /* OCP e5m2 bytes; value = e5m2(byte) * pool scale (the
+                           pages' second fp8 KV format: wider range, one fewer
+                           mantissa bit; "vLLM intro part 2", section 7)        */
 } pa_kv_dtype;
 
 /* One layer's KV pool.
@@ -107,8 +111,9 @@ typedef struct {
  *                 or one at or beyond num_blocks * block_size, skips the token.
  *                 Slots must be distinct within one call.
  * f16 pools receive the bits unchanged.  fp8 pools receive
- * e4m3fn(float(x) / scale), rounded to nearest even and saturated to +-448
- * (NaN stays NaN).  num_tokens == 0 is a no-op. */
+ * enc(float(x) / scale), rounded to nearest even and saturated to the
+ * format's largest finite value (448 for e4m3fn, 57344 for e5m2; infinities
+ * saturate too), NaN stays NaN.  num_tokens == 0 is a no-op. */
 int pa_reshape_and_cache(const pa_kv_pool* pool, const void* k_new, const void* v_new,
                          const int64_t* slot_mapping, int64_t num_tokens, hipStream_t stream);
 

@@ -27,7 +27,7 @@ class OrcPool(C.Structure):
         ("k", C.c_void_p), ("v", C.c_void_p),
         ("num_blocks", C.c_int64), ("block_stride", C.c_int64),
         ("block_size", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
-        ("elem_bytes", C.c_int32),
+        ("elem_bytes", C.c_int32), ("fp8_format", C.c_int32),
         ("k_scale", C.c_double), ("v_scale", C.c_double),
     ]
 
@@ -50,7 +50,12 @@ def lib():
         L.orc_e4m3fn_value.argtypes = [C.c_uint8]
         L.orc_e4m3fn_encode.restype = C.c_uint8
         L.orc_e4m3fn_encode.argtypes = [C.c_float]
-        for n in ("orc_f16_values", "orc_e4m3fn_values", "orc_e4m3fn_encode_n"):
+        L.orc_e5m2_value.restype = D
+        L.orc_e5m2_value.argtypes = [C.c_uint8]
+        L.orc_e5m2_encode.restype = C.c_uint8
+        L.orc_e5m2_encode.argtypes = [C.c_float]
+        for n in ("orc_f16_values", "orc_e4m3fn_values", "orc_e4m3fn_encode_n",
+                  "orc_e5m2_values", "orc_e5m2_encode_n"):
             getattr(L, n).restype = None
             getattr(L, n).argtypes = [P, I64, P]
         L.orc_scatter.restype = None
@@ -94,6 +99,20 @@ def e4m3fn_values(b: np.ndarray) -> np.ndarray:
     return out
 
 
+def e5m2_values(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    out = np.empty(b.shape, np.float64)
+    lib().orc_e5m2_values(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def e5m2_encode(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().orc_e5m2_encode_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
 def e4m3fn_encode(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     out = np.empty(x.shape, np.uint8)
@@ -110,7 +129,8 @@ class HostPool:
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
                  kv_dtype: str = "f16", k_scale: float = 1.0, v_scale: float = 1.0,
                  fill_bits: int = 0):
-        self.elem_bytes = 1 if kv_dtype == "fp8_e4m3fn" else 2
+        self.elem_bytes = 1 if kv_dtype in ("fp8_e4m3fn", "fp8_e5m2") else 2
+        fp8_format = 1 if kv_dtype == "fp8_e5m2" else 0
         dt = np.uint8 if self.elem_bytes == 1 else np.uint16
         shape = (num_blocks, block_size, num_kv_heads, head_dim)
         if fill_bits:
@@ -121,8 +141,8 @@ class HostPool:
             self.v = np.zeros(shape, dtype=dt)
         self.kv_dtype = kv_dtype
         self.desc = OrcPool(self.k.ctypes.data, self.v.ctypes.data, num_blocks, 0, block_size,
-                            num_kv_heads, head_dim, self.elem_bytes, float(k_scale),
-                            float(v_scale))
+                            num_kv_heads, head_dim, self.elem_bytes, fp8_format,
+                            float(k_scale), float(v_scale))
 
     @classmethod
     def for_workload(cls, w, fill_bits: int = 0) -> "HostPool":

@@ -90,6 +90,62 @@ uint8_t orc_e4m3fn_encode(float x) {
   return (uint8_t)(sign | code);
 }
 
+/* OCP e5m2: 1 sign bit, 5 exponent bits (bias 15), 2 mantissa bits.
+ * Exponent 0 holds zero and subnormals (m * 2^-16); exponent 31 holds the
+ * infinities (m = 0) and NaN (m != 0), so the largest finite value is
+ * 1.75 * 2^15 = 57344. */
+double orc_e5m2_value(uint8_t byte) {
+  int sign = byte >> 7;
+  int e = (byte >> 2) & 0x1F;
+  int m = byte & 0x3;
+  double v;
+  if (e == 31) {
+    v = m ? NAN : INFINITY;
+  } else if (e == 0) {
+    v = ldexp((double)m, -16);
+  } else {
+    v = ldexp((double)(4 + m), e - 17); /* 2^(e-15) * (1 + m/4) */
+  }
+  return sign ? -v : v;
+}
+
+/* fp32 -> e5m2, the same steps as for e4m3fn with this format's constants:
+ * NaN stays NaN (sign kept, S.11111.11); magnitudes at or beyond the largest
+ * finite value, infinities included, saturate to 57344 (S.11110.11); otherwise
+ * count quanta of the binade (2^(E-2)) and round the count to nearest even.
+ * Below 2^-14 the quantum is the subnormal step 2^-16. */
+uint8_t orc_e5m2_encode(float x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return (uint8_t)(sign | 0x7F);
+  double a = fabs((double)x);
+  if (a >= 57344.0) return (uint8_t)(sign | 0x7B);
+  if (a == 0.0) return sign;
+  int ex;
+  (void)frexp(a, &ex);           /* a = fr * 2^ex, fr in [0.5, 1) */
+  int E = ex - 1;                /* a = 2^E * (1.f)                 */
+  if (E < -14) {
+    double n = round_half_even(a * 65536.0);  /* quanta of 2^-16: 0..4 */
+    return (uint8_t)(sign | (uint8_t)n);      /* 4 is the smallest normal, 0x04 */
+  }
+  double quantum = ldexp(1.0, E - 2);
+  double n = round_half_even(a / quantum);    /* 4..8 */
+  if (n == 8.0) {
+    E += 1;
+    n = 4.0;
+  }
+  int code = ((E + 15) << 2) | ((int)n - 4);
+  if (code > 0x7B) code = 0x7B;
+  return (uint8_t)(sign | code);
+}
+
+void orc_e5m2_values(const uint8_t* bytes, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_value(bytes[i]);
+}
+
+void orc_e5m2_encode_n(const float* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_encode(x[i]);
+}
+
 void orc_f16_values(const uint16_t* bits, int64_t n, double* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_value(bits[i]);
 }
@@ -122,7 +178,7 @@ static double read_elem(const orc_pool* p, const void* base, int64_t byte_off, d
     memcpy(&bits, b, 2);
     return orc_f16_value(bits);
   }
-  return orc_e4m3fn_value(*b) * scale;
+  return (p->fp8_format == ORC_FP8_E5M2 ? orc_e5m2_value(*b) : orc_e4m3fn_value(*b)) * scale;
 }
 
 static int nthreads_or_default(int n) { return n > 0 ? n : omp_get_max_threads(); }
@@ -149,8 +205,13 @@ void orc_scatter(const orc_pool* p, const uint16_t* k_new, const uint16_t* v_new
         } else {
           float kx = (float)orc_f16_value(k_new[src]);
           float vx = (float)orc_f16_value(v_new[src]);
-          ((uint8_t*)p->k)[dst] = orc_e4m3fn_encode(kx / ks);
-          ((uint8_t*)p->v)[dst] = orc_e4m3fn_encode(vx / vs);
+          if (p->fp8_format == ORC_FP8_E5M2) {
+            ((uint8_t*)p->k)[dst] = orc_e5m2_encode(kx / ks);
+            ((uint8_t*)p->v)[dst] = orc_e5m2_encode(vx / vs);
+          } else {
+            ((uint8_t*)p->k)[dst] = orc_e4m3fn_encode(kx / ks);
+            ((uint8_t*)p->v)[dst] = orc_e4m3fn_encode(vx / vs);
+          }
         }
       }
     }

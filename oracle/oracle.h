@@ -21,7 +21,8 @@
  *     KV head ("KV Cache memory core", section 4.2 GQA diagram).
  *   - Writing a token stores its K/V at its absolute slot, block*bs + offset
  *     ("vLLM intro part 2", section 3.2 slot_mapping); fp8 pools store
- *     e4m3fn(x / scale) (quantise on write, "KV Cache memory core", section 4.4).
+ *     e4m3fn(x / scale) or e5m2(x / scale) (quantise on write, "KV Cache memory
+ *     core", section 4.4; the two fp8 formats of "vLLM intro part 2", section 7).
  *   - copy_blocks copies a whole block for copy-on-write ("GPU memory & KV
  *     cache", COW incident code; "vLLM intro part 2", section 5).
  */
@@ -43,10 +44,14 @@ typedef struct {
   int32_t block_size;
   int32_t num_kv_heads;
   int32_t head_dim;
-  int32_t elem_bytes;     /* 2: IEEE binary16 elements, 1: OCP e4m3fn bytes   */
+  int32_t elem_bytes;     /* 2: IEEE binary16 elements, 1: fp8 bytes          */
+  int32_t fp8_format;     /* for 1-byte elements: ORC_FP8_E4M3FN or _E5M2     */
   double  k_scale;        /* fp8 dequantisation scales (1.0 for binary16)     */
   double  v_scale;
 } orc_pool;
+
+#define ORC_FP8_E4M3FN 0
+#define ORC_FP8_E5M2 1
 
 /* Value of an IEEE-754 binary16 bit pattern. */
 double orc_f16_value(uint16_t bits);
@@ -54,13 +59,20 @@ double orc_f16_value(uint16_t bits);
 double orc_e4m3fn_value(uint8_t byte);
 /* fp32 -> e4m3fn, round to nearest even, saturating to +-448, NaN -> NaN. */
 uint8_t orc_e4m3fn_encode(float x);
-/* Batch forms of the three codec functions (n elements). */
+/* Value of an OCP e5m2 byte (bias 15, infinities and NaN in exponent 31). */
+double orc_e5m2_value(uint8_t byte);
+/* fp32 -> e5m2, round to nearest even, saturating to +-57344, NaN -> NaN. */
+uint8_t orc_e5m2_encode(float x);
+/* Batch forms of the codec functions (n elements). */
 void orc_f16_values(const uint16_t* bits, int64_t n, double* out);
 void orc_e4m3fn_values(const uint8_t* bytes, int64_t n, double* out);
 void orc_e4m3fn_encode_n(const float* x, int64_t n, uint8_t* out);
+void orc_e5m2_values(const uint8_t* bytes, int64_t n, double* out);
+void orc_e5m2_encode_n(const float* x, int64_t n, uint8_t* out);
 
 /* Write T tokens: k_new/v_new are [T, Hkv, D] binary16 bit patterns; slot < 0
- * skips the token.  fp8 pools receive e4m3fn(float(x) / float(scale)). */
+ * skips the token.  fp8 pools receive enc(float(x) / float(scale)) with the
+ * pool's fp8 encoder. */
 void orc_scatter(const orc_pool* p, const uint16_t* k_new, const uint16_t* v_new,
                  const int64_t* slots, int64_t T, int nthreads);
 

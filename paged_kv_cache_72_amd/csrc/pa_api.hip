@@ -38,7 +38,7 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
       p->block_size != 128)
     return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (8, 16, 32, 64, 128)",
                 p->block_size);
-  if (p->dtype != PA_KV_F16 && p->dtype != PA_KV_FP8_E4M3FN)
+  if (p->dtype != PA_KV_F16 && p->dtype != PA_KV_FP8_E4M3FN && p->dtype != PA_KV_FP8_E5M2)
     return fail(PA_ERR_UNSUPPORTED, "kv dtype %d not supported", p->dtype);
   if (p->num_kv_heads < 1 || p->num_kv_heads > 4096)
     return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d out of range", p->num_kv_heads);
@@ -55,7 +55,7 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
                 (long long)stride, (long long)dense);
   if (stride % 16) return fail(PA_ERR_ALIGNMENT, "block_stride_bytes must be a multiple of 16");
   if (row > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "token row too large");
-  if (p->dtype == PA_KV_FP8_E4M3FN &&
+  if (p->dtype != PA_KV_F16 &&
       (!(p->k_scale > 0.f) || !(p->v_scale > 0.f) || !std::isfinite(p->k_scale) ||
        !std::isfinite(p->v_scale)))
     return fail(PA_ERR_INVALID_ARG, "fp8 pools need finite positive k_scale and v_scale");
@@ -71,6 +71,7 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
   g->num_kv_heads = p->num_kv_heads;
   g->head_dim = p->head_dim;
   g->elem_bytes = e;
+  g->fp8_e5m2 = p->dtype == PA_KV_FP8_E5M2;
   g->k_scale = p->dtype == PA_KV_F16 ? 1.f : p->k_scale;
   g->v_scale = p->dtype == PA_KV_F16 ? 1.f : p->v_scale;
   g->flags = p->flags;
@@ -297,7 +298,8 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
   }
   const bool stream_kv = !(g.flags & PA_POOL_SHARED_BLOCKS);
   if (hipError_t e = pa::launch_decode(a, &f, num_seqs, g.head_dim, g.block_size,
-                                       g.elem_bytes == 1, stream_kv, pl.mode, stream))
+                                       g.elem_bytes == 2 ? 0 : (g.fp8_e5m2 ? 2 : 1),
+                                       stream_kv, pl.mode, stream))
     return fail(PA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return PA_OK;
 }

@@ -32,6 +32,24 @@ __device__ __forceinline__ uint32_t e4m3fn_from_f32(float y) {
   return sign | code;
 }
 
+// fp32 -> OCP e5m2 the same way: round to nearest even, saturate to +-57344
+// (infinities included), keep NaN as S.11111.11.
+__device__ __forceinline__ uint32_t e5m2_from_f32(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;        // NaN
+  if (a >= 0x47600000u) return sign | 0x7Bu;       // |y| >= 57344: largest finite
+  if (a < 0x38800000u) {                           // |y| < 2^-14: steps of 2^-16
+    const float n = rintf(__uint_as_float(a) * 65536.0f);  // exact scaling, RNE
+    return sign | (uint32_t)n;                     // 4 lands on the smallest normal
+  }
+  uint32_t code = (a >> 21) - (112u << 2);         // rebias exponent, keep 2 mantissa bits
+  const uint32_t rest = a & 0x1FFFFFu;
+  code += (rest > 0x100000u) || (rest == 0x100000u && (code & 1u));
+  return sign | code;
+}
+
 // One workgroup per token.  Threads [0, n16) move K, [n16, 2*n16) move V, where
 // n16 = row bytes / 16 of the binary16 source.
 __global__ __launch_bounds__(256) void rc_scatter_f16(PoolGeom g, const uint4* __restrict__ k_new,
@@ -55,6 +73,7 @@ __global__ __launch_bounds__(256) void rc_scatter_f16(PoolGeom g, const uint4* _
 }
 
 // fp8 pools: each thread reads 8 binary16 values (16 B) and writes 8 bytes.
+template <bool E5M2>
 __global__ __launch_bounds__(256) void rc_scatter_fp8(PoolGeom g, const uint4* __restrict__ k_new,
                                                       const uint4* __restrict__ v_new,
                                                       const int64_t* __restrict__ slots,
@@ -77,7 +96,8 @@ __global__ __launch_bounds__(256) void rc_scatter_fp8(PoolGeom g, const uint4* _
     for (int j = 0; j < 8; ++j) {
       const uint16_t hb = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
       const float xf = (float)__builtin_bit_cast(_Float16, hb);
-      packed[j >> 2] |= e4m3fn_from_f32(xf / scale) << (8 * (j & 3));
+      const uint32_t code = E5M2 ? e5m2_from_f32(xf / scale) : e4m3fn_from_f32(xf / scale);
+      packed[j >> 2] |= code << (8 * (j & 3));
     }
     uint2* dst = (uint2*)((is_v ? g.v : g.k) + dst_off) + c;
     *dst = make_uint2(packed[0], packed[1]);
@@ -110,8 +130,11 @@ hipError_t launch_reshape_and_cache(const PoolGeom& g, const _Float16* k_new,
   if (g.elem_bytes == 2)
     hipLaunchKernelGGL(rc_scatter_f16, dim3((uint32_t)T), dim3(threads), 0, stream, g,
                        (const uint4*)k_new, (const uint4*)v_new, slots, n16);
+  else if (g.fp8_e5m2)
+    hipLaunchKernelGGL(rc_scatter_fp8<true>, dim3((uint32_t)T), dim3(threads), 0, stream, g,
+                       (const uint4*)k_new, (const uint4*)v_new, slots, n16);
   else
-    hipLaunchKernelGGL(rc_scatter_fp8, dim3((uint32_t)T), dim3(threads), 0, stream, g,
+    hipLaunchKernelGGL(rc_scatter_fp8<false>, dim3((uint32_t)T), dim3(threads), 0, stream, g,
                        (const uint4*)k_new, (const uint4*)v_new, slots, n16);
   return hipGetLastError();
 }

@@ -28,7 +28,9 @@
 //     head c -- the A-operand layout of the P.V MFMA and the rows that value
 //     load k = 0..3 gave the same lane.  V is transposed inside the lane into
 //     B operands; D/16 MFMAs give P.V.  P and V enter the matrix core as
-//     binary16 (fp8 pools are widened exactly first), accumulation is fp32.
+//     binary16 (fp8 pools are widened exactly first: e4m3fn through the fp32
+//     converter, e5m2 by placing the byte above 8 zero bits), accumulation is
+//     fp32.
 //   * Softmax state per head: running max m (log2 units), per-lane partial sum
 //     l and the P.V accumulators.  The max moves (and l, acc are rescaled) only
 //     when a tile's max exceeds it by more than 2^8, so P <= 256 fits binary16.
@@ -100,11 +102,25 @@ __device__ __forceinline__ half4_t halves_of(uint32_t lo, uint32_t hi) {
 }
 
 // 4 e4m3fn bytes -> 4 binary16 values (exact: every e4m3fn value is a binary16 value).
-__device__ __forceinline__ half4_t fp8x4_to_half4(uint32_t w) {
+__device__ __forceinline__ half4_t e4m3x4_to_half4(uint32_t w) {
   const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
   const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
   const float4_t f = {a.x, a.y, b.x, b.y};
   return __builtin_convertvector(f, half4_t);
+}
+
+// 4 e5m2 bytes -> 4 binary16 values: e5m2 is binary16 with the low 8 mantissa
+// bits dropped, so byte b widens to the bits b << 8 (NaN and infinity included).
+__device__ __forceinline__ half4_t e5m2x4_to_half4(uint32_t w) {
+  const uint32_t lo = ((w << 8) & 0x0000FF00u) | ((w << 16) & 0xFF000000u);
+  const uint32_t hi = ((w >> 8) & 0x0000FF00u) | (w & 0xFF000000u);
+  return halves_of(lo, hi);
+}
+
+// Byte b of words w0, w1 as two binary16 values (e5m2 widening of one value
+// dim for two tokens): low half from w0, high half from w1.
+__device__ __forceinline__ uint32_t e5m2_pair(uint32_t w0, uint32_t w1, int b) {
+  return (((w0 >> (8 * b)) & 0xFFu) << 8) | (((w1 >> (8 * b)) & 0xFFu) << 24);
 }
 
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
@@ -131,11 +147,12 @@ struct PairRef {
 // NT: K/V tiles are read with the streaming (non-temporal) cache policy, for
 // pools whose blocks each belong to one sequence; blocks shared by several
 // sequences of the batch are read with the default policy so that they stay
-// cached for the other readers.
-template <int D, int BS, bool FP8, bool NT>
+// cached for the other readers.  KV: element format of the pools, 0 binary16,
+// 1 e4m3fn, 2 e5m2.
+template <int D, int BS, int KV, bool NT>
 struct Engine {
   static constexpr int CPOL = NT ? 2 : 0;      // cache-policy operand of the tile loads
-  static constexpr int E = FP8 ? 1 : 2;        // bytes per KV element
+  static constexpr int E = KV ? 1 : 2;         // bytes per KV element
   static constexpr int KCH = 16 / E;           // elements in a 16-B key chunk
   static constexpr int NKL = D * E / 64;       // 16-B key loads per lane per tile
   static constexpr int GPL = KCH / 4;          // MFMA operand groups per key chunk
@@ -296,7 +313,8 @@ struct Engine {
 #pragma unroll
       for (int grp = 0; grp < GPL; ++grp) {
         half4_t kop;
-        if constexpr (FP8) kop = fp8x4_to_half4(w[grp]);
+        if constexpr (KV == 1) kop = e4m3x4_to_half4(w[grp]);
+        else if constexpr (KV == 2) kop = e5m2x4_to_half4(w[grp]);
         else kop = halves_of(w[2 * grp], w[2 * grp + 1]);
         sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kop, qop[cl * GPL + grp], sacc, 0, 0, 0);
       }
@@ -340,13 +358,21 @@ struct Engine {
         for (int wi = 0; wi < VB / 4; ++wi) vw[k][wi] = ok ? vw[k][wi] : 0u;
       }
     }
-    if constexpr (!FP8) {
+    if constexpr (KV == 0) {
 #pragma unroll
       for (int e = 0; e < DCH; ++e) {
         const int wi = e >> 1, sh = (e & 1) * 16;
         const uint32_t h0 = (vw[0][wi] >> sh) & 0xFFFFu, h1 = (vw[1][wi] >> sh) & 0xFFFFu;
         const uint32_t h2 = (vw[2][wi] >> sh) & 0xFFFFu, h3 = (vw[3][wi] >> sh) & 0xFFFFu;
         const half4_t bop = halves_of(h0 | (h1 << 16), h2 | (h3 << 16));
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(pop, bop, acc[e], 0, 0, 0);
+      }
+    } else if constexpr (KV == 2) {
+#pragma unroll
+      for (int e = 0; e < DCH; ++e) {
+        const int wi = e >> 2, b = e & 3;
+        const half4_t bop = halves_of(e5m2_pair(vw[0][wi], vw[1][wi], b),
+                                      e5m2_pair(vw[2][wi], vw[3][wi], b));
         acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(pop, bop, acc[e], 0, 0, 0);
       }
     } else {
@@ -418,13 +444,13 @@ struct Engine {
 
 // ---------------------------------------------------------------- single / split
 
-template <int D, int BS, bool FP8, int NW, bool SPLIT, bool NT>
+template <int D, int BS, int KV, int NW, bool SPLIT, bool NT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU, 8)))
 void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
                    const int32_t* __restrict__ lens) {
   // The tables arrive as restrict arguments so that their uniform reads stay
   // scalar loads (as in decode_flat_kernel).
-  typedef Engine<D, BS, FP8, NT> En;
+  typedef Engine<D, BS, KV, NT> En;
   typedef typename En::VT VT;
   const int lane = threadIdx.x & 63;
   const int wid = uni(threadIdx.x >> 6);
@@ -440,7 +466,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
   // logical blocks clamped to the table row, which the host bounds, rather
   // than to the length), so the first K/V loads wait on one round trip.
   const int j0 = (SPLIT ? part * a.part_tokens : 0) / 16 + wid;
-  const int64_t head_off = (int64_t)kh * D * Engine<D, BS, FP8, NT>::E;
+  const int64_t head_off = (int64_t)kh * D * Engine<D, BS, KV, NT>::E;
   const PairRef row{tables + (int64_t)s * a.max_blocks, a.max_blocks, 0, head_off};
   const int len = clamp_len(lens[s], a.len_cap);
   int t_begin = 0, t_end = len;
@@ -609,7 +635,7 @@ __device__ __forceinline__ int range_of(int64_t t, int64_t T, int64_t NR) {
 // written directly; one cut by range boundaries leaves a partial record per
 // range (slot 0: the range's first sequence, slot 1: its last), merged by
 // flat_merge_kernel.
-template <int D, int BS, bool FP8, int NW, bool NT>
+template <int D, int BS, int KV, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_FLAT_WAVES_PER_EU, 8)))
 void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ tables,
                         const int32_t* __restrict__ lens, const _Float16* __restrict__ qs,
@@ -618,7 +644,7 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   // The read-only arrays arrive as separate restrict arguments: stores to the
   // outputs inside the loop then provably leave the block table alone, so its
   // entries can be read with scalar loads.
-  typedef Engine<D, BS, FP8, NT> En;
+  typedef Engine<D, BS, KV, NT> En;
   typedef typename En::VT VT;
   extern __shared__ int sm[];                 // [S + 1] tiles before sequence s, then [S] lengths
   const int S = f.num_seqs, Hkv = a.num_kv_heads, g = a.gqa;
@@ -836,7 +862,7 @@ __global__ __launch_bounds__(NG * D) void flat_merge_kernel(DecodeArgs a, FlatAr
 
 constexpr int kWaves = PA_DECODE_WAVES;
 
-template <int D, int BS, bool FP8, bool NT>
+template <int D, int BS, int KV, bool NT>
 hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int mode,
                         hipStream_t stream) {
   const uint32_t units = (uint32_t)num_seqs * (uint32_t)a.num_kv_heads;
@@ -844,7 +870,7 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs
     const size_t lds = sizeof(int) * (2 * (size_t)num_seqs + 1);
     const int64_t waves = (int64_t)f->num_ranges * a.num_kv_heads;
     constexpr int FW = PA_FLAT_WAVES;
-    hipLaunchKernelGGL((decode_flat_kernel<D, BS, FP8, FW, NT>),
+    hipLaunchKernelGGL((decode_flat_kernel<D, BS, KV, FW, NT>),
                        dim3((uint32_t)((waves + FW - 1) / FW)), dim3(FW * 64), lds,
                        stream, a, *f, a.block_tables, a.seq_lens, a.q, a.out, f->slots,
                        f->prefix);
@@ -862,7 +888,7 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs
     else
       hipLaunchKernelGGL((flat_merge_kernel<D, 8>), mgrid, dim3(8 * D), 0, stream, a, *f);
   } else if (mode == kModeSplit) {
-    hipLaunchKernelGGL((decode_kernel<D, BS, FP8, kWaves, true, NT>),
+    hipLaunchKernelGGL((decode_kernel<D, BS, KV, kWaves, true, NT>),
                        dim3(units * (uint32_t)a.num_parts), dim3(kWaves * 64), 0, stream, a,
                        a.block_tables, a.seq_lens);
     hipError_t e = hipGetLastError();
@@ -870,31 +896,39 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs
     hipLaunchKernelGGL((lse_reduce_kernel<D>), dim3((uint32_t)num_seqs * (uint32_t)a.num_q_heads),
                        dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<D, BS, FP8, kWaves, false, NT>), dim3(units),
+    hipLaunchKernelGGL((decode_kernel<D, BS, KV, kWaves, false, NT>), dim3(units),
                        dim3(kWaves * 64), 0, stream, a, a.block_tables, a.seq_lens);
   }
   return hipGetLastError();
 }
 
+template <int D, int BS, int KV>
+hipError_t launch_nt(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, bool stream_kv,
+                     int mode, hipStream_t stream) {
+  return stream_kv ? launch_typed<D, BS, KV, true>(a, f, num_seqs, mode, stream)
+                   : launch_typed<D, BS, KV, false>(a, f, num_seqs, mode, stream);
+}
+
 template <int D, int BS>
-hipError_t launch_bs(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, bool fp8,
+hipError_t launch_bs(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int kv,
                      bool stream_kv, int mode, hipStream_t stream) {
-  if (fp8)
-    return stream_kv ? launch_typed<D, BS, true, true>(a, f, num_seqs, mode, stream)
-                     : launch_typed<D, BS, true, false>(a, f, num_seqs, mode, stream);
-  return stream_kv ? launch_typed<D, BS, false, true>(a, f, num_seqs, mode, stream)
-                   : launch_typed<D, BS, false, false>(a, f, num_seqs, mode, stream);
+  switch (kv) {
+    case 0: return launch_nt<D, BS, 0>(a, f, num_seqs, stream_kv, mode, stream);
+    case 1: return launch_nt<D, BS, 1>(a, f, num_seqs, stream_kv, mode, stream);
+    case 2: return launch_nt<D, BS, 2>(a, f, num_seqs, stream_kv, mode, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_d(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int32_t bs, bool fp8,
+hipError_t launch_d(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int32_t bs, int kv,
                     bool stream_kv, int mode, hipStream_t stream) {
   switch (bs) {
-    case 8: return launch_bs<D, 8>(a, f, num_seqs, fp8, stream_kv, mode, stream);
-    case 16: return launch_bs<D, 16>(a, f, num_seqs, fp8, stream_kv, mode, stream);
-    case 32: return launch_bs<D, 32>(a, f, num_seqs, fp8, stream_kv, mode, stream);
-    case 64: return launch_bs<D, 64>(a, f, num_seqs, fp8, stream_kv, mode, stream);
-    case 128: return launch_bs<D, 128>(a, f, num_seqs, fp8, stream_kv, mode, stream);
+    case 8: return launch_bs<D, 8>(a, f, num_seqs, kv, stream_kv, mode, stream);
+    case 16: return launch_bs<D, 16>(a, f, num_seqs, kv, stream_kv, mode, stream);
+    case 32: return launch_bs<D, 32>(a, f, num_seqs, kv, stream_kv, mode, stream);
+    case 64: return launch_bs<D, 64>(a, f, num_seqs, kv, stream_kv, mode, stream);
+    case 128: return launch_bs<D, 128>(a, f, num_seqs, kv, stream_kv, mode, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -904,12 +938,12 @@ hipError_t launch_d(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, in
 int decode_waves_per_workgroup() { return kWaves; }
 
 hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
-                         int32_t head_dim, int32_t block_size, bool fp8, bool stream_kv, int mode,
+                         int32_t head_dim, int32_t block_size, int kv, bool stream_kv, int mode,
                          hipStream_t stream) {
   if (head_dim == 128)
-    return launch_d<128>(a, f, num_seqs, block_size, fp8, stream_kv, mode, stream);
+    return launch_d<128>(a, f, num_seqs, block_size, kv, stream_kv, mode, stream);
   if (head_dim == 64)
-    return launch_d<64>(a, f, num_seqs, block_size, fp8, stream_kv, mode, stream);
+    return launch_d<64>(a, f, num_seqs, block_size, kv, stream_kv, mode, stream);
   return hipErrorInvalidValue;
 }
 

@@ -17,7 +17,8 @@ struct PoolGeom {
   int32_t block_size;
   int32_t num_kv_heads;
   int32_t head_dim;
-  int32_t elem_bytes;    // 2: binary16, 1: e4m3fn
+  int32_t elem_bytes;    // 2: binary16, 1: fp8
+  int32_t fp8_e5m2;      // 1-byte elements: 0 e4m3fn, 1 e5m2
   float k_scale;
   float v_scale;
   uint32_t flags;        // pa_kv_pool.flags
@@ -65,8 +66,9 @@ hipError_t launch_copy_blocks(const PoolGeom& g, const int64_t* pairs, int64_t n
 int decode_waves_per_workgroup();
 // stream_kv: read K/V tiles with the streaming cache policy (pools without
 // blocks shared between sequences of the batch).
+// kv: 0 binary16, 1 e4m3fn, 2 e5m2.
 hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
-                         int32_t head_dim, int32_t block_size, bool fp8, bool stream_kv, int mode,
+                         int32_t head_dim, int32_t block_size, int kv, bool stream_kv, int mode,
                          hipStream_t stream);
 
 }  // namespace pa

@@ -17,10 +17,10 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_ALIGNMENT, PA_ERR_WORKSPACE, PA_ERR_HIP = \
     0, -1, -2, -3, -4, -5
-PA_KV_F16, PA_KV_FP8_E4M3FN = 0, 1
+PA_KV_F16, PA_KV_FP8_E4M3FN, PA_KV_FP8_E5M2 = 0, 1, 2
 PLAN_SINGLE, PLAN_FLAT = 0, 1          # pa_decode_plan codes; >= 16 is a split partition size
 PA_POOL_SHARED_BLOCKS = 1
-_DTYPES = {"f16": PA_KV_F16, "fp8_e4m3fn": PA_KV_FP8_E4M3FN}
+_DTYPES = {"f16": PA_KV_F16, "fp8_e4m3fn": PA_KV_FP8_E4M3FN, "fp8_e5m2": PA_KV_FP8_E5M2}
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
            "pa_decode_workspace_size", "pa_decode", "pa_last_error")
@@ -129,12 +129,12 @@ class KVPool:
                  kv_dtype: str = "f16", k_scale: float = 1.0, v_scale: float = 1.0,
                  device="cuda", fill_bits: Optional[int] = None,
                  shared_blocks: bool = False) -> "KVPool":
-        tdt = torch.uint8 if kv_dtype == "fp8_e4m3fn" else torch.int16
+        tdt = torch.int16 if kv_dtype == "f16" else torch.uint8
         shape = (num_blocks, block_size, num_kv_heads, head_dim)
         k = torch.empty(shape, dtype=tdt, device=device)
         v = torch.empty(shape, dtype=tdt, device=device)
         if fill_bits is not None:
-            fb = fill_bits if kv_dtype == "fp8_e4m3fn" else (fill_bits - 65536 if fill_bits >= 32768
+            fb = fill_bits if kv_dtype != "f16" else (fill_bits - 65536 if fill_bits >= 32768
                                                             else fill_bits)
             k.fill_(fb)
             v.fill_(fb)
@@ -143,7 +143,7 @@ class KVPool:
 
     @property
     def elem_bytes(self) -> int:
-        return 1 if self.kv_dtype == "fp8_e4m3fn" else 2
+        return 2 if self.kv_dtype == "f16" else 1
 
 
 def pa_reshape_and_cache(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,

@@ -34,6 +34,14 @@ import numpy as np
 F16_NAN_BITS = np.uint16(0x7E00)   # quiet NaN in IEEE binary16
 E4M3_NAN_BYTE = np.uint8(0x7F)     # S.1111.111 is NaN in OCP e4m3fn
 E4M3_MAX = np.float32(448.0)       # largest finite OCP e4m3fn magnitude
+E5M2_MAX = np.float32(57344.0)     # largest finite OCP e5m2 magnitude
+E5M2_NAN_BYTE = np.uint8(0x7F)     # S.11111.11 is a NaN in OCP e5m2
+FP8_DTYPES = ("fp8_e4m3fn", "fp8_e5m2")
+
+
+def fp8_max(kv_dtype: str) -> np.float32:
+    """Largest finite magnitude of a pool's fp8 format (sets the per-pool scale)."""
+    return E5M2_MAX if kv_dtype == "fp8_e5m2" else E4M3_MAX
 
 _CHUNK_TOKENS = 16384
 
@@ -53,7 +61,7 @@ class Workload:
     head_dim: int
     block_size: int
     num_blocks: int
-    kv_dtype: str                    # "f16" or "fp8_e4m3fn"
+    kv_dtype: str                    # "f16", "fp8_e4m3fn" or "fp8_e5m2"
     scale: float                     # softmax scale (fp32 value)
     k_scale: float                   # per-tensor fp8 scale (1.0 for f16)
     v_scale: float
@@ -97,7 +105,7 @@ class Workload:
 
     @property
     def kv_elem_bytes(self) -> int:
-        return 1 if self.kv_dtype == "fp8_e4m3fn" else 2
+        return 1 if self.kv_dtype in FP8_DTYPES else 2
 
     @property
     def new_slots(self) -> np.ndarray:
@@ -185,9 +193,9 @@ def _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, lens, tables, p
     tok_k = _normal_f16(ss[3], (T, Hkv, D), T)
     tok_v = _normal_f16(ss[4], (T, Hkv, D), T)
     k_scale = v_scale = 1.0
-    if kv_dtype == "fp8_e4m3fn":
-        k_scale = float(_amax_f32(tok_k) / E4M3_MAX)
-        v_scale = float(_amax_f32(tok_v) / E4M3_MAX)
+    if kv_dtype in FP8_DTYPES:
+        k_scale = float(_amax_f32(tok_k) / fp8_max(kv_dtype))
+        v_scale = float(_amax_f32(tok_v) / fp8_max(kv_dtype))
     used = np.unique(tok_slot // bs).astype(np.int32)
     return Workload(name=name, seed=seed, num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv,
                     head_dim=D, block_size=bs, num_blocks=num_blocks, kv_dtype=kv_dtype,
@@ -261,6 +269,14 @@ def long_fp8(seed: int = 7206) -> Workload:
                         kv_dtype="fp8_e4m3fn", partition_size=512)
 
 
+def long_e5m2(seed: int = 7207) -> Workload:
+    """The long-context split-KV shape of long_fp8 (8 x 131,072 tokens, 32 / 8
+    heads, head_dim 128, block_size 32, 512-token partitions) with the KV
+    stored as OCP fp8 e5m2 (per-tensor fp32 scale = amax / 57344)."""
+    return _independent("long_e5m2", seed, [131072] * 8, 32, 8, 128, 32, 36864,
+                        kv_dtype="fp8_e5m2", partition_size=512)
+
+
 def prefix_share(block_size: int = 16, seed: Optional[int] = None) -> Workload:
     """Short requests with parallel-sampling prefix sharing: 1,024 sequences in
     groups of 4 that share a 256-token prompt; tails of 1-40 tokens (717 of
@@ -332,6 +348,7 @@ CONFIGS = {
     "prefix_share_bs16": lambda: prefix_share(16),
     "prefix_share_bs8": lambda: prefix_share(8),
     "long_fp8": long_fp8,
+    "long_e5m2": long_e5m2,
 }
 
 
@@ -353,8 +370,8 @@ def with_v_offset(w: Workload, c: float = 1.0) -> Workload:
     """V += c on every token: the output must then sit near c."""
     v = (w.tok_v.astype(np.float32) + np.float32(c)).astype(np.float16)
     out = dataclasses.replace(w, tok_v=v, variant=f"v_offset{c:g}")
-    if w.kv_dtype == "fp8_e4m3fn":
-        out.v_scale = float(_amax_f32(v) / E4M3_MAX)
+    if w.kv_dtype in FP8_DTYPES:
+        out.v_scale = float(_amax_f32(v) / fp8_max(w.kv_dtype))
     return out
 
 
@@ -388,11 +405,13 @@ def with_needles(w: Workload, alpha: float = 64.0, seed_offset: int = 0) -> Work
             qn = qv / np.float32(np.linalg.norm(qv) + 1e-6)
             k[idx, kh] = (np.float32(alpha) * qn).astype(np.float16)
     out = dataclasses.replace(w, tok_k=k, variant="needles")
-    if w.kv_dtype == "fp8_e4m3fn":
-        out.k_scale = float(_amax_f32(k) / E4M3_MAX)
+    if w.kv_dtype in FP8_DTYPES:
+        out.k_scale = float(_amax_f32(k) / fp8_max(w.kv_dtype))
     return out
 
 
 def poison_pool_bits(w: Workload) -> int:
     """Bit pattern every unwritten pool element is filled with in poison runs."""
+    if w.kv_dtype == "fp8_e5m2":
+        return int(E5M2_NAN_BYTE)
     return int(E4M3_NAN_BYTE) if w.kv_dtype == "fp8_e4m3fn" else int(F16_NAN_BITS)

@@ -74,8 +74,11 @@ def test_bad_pool_fields(so, field, value, code):
     assert _decode(so, _pool(**{field: value})) == code
 
 
-def test_fp8_pool_needs_positive_scales(so):
-    assert _decode(so, _pool(dtype=L.PA_KV_FP8_E4M3FN, k_scale=0.0)) == L.PA_ERR_INVALID_ARG
+@pytest.mark.parametrize("dt", [L.PA_KV_FP8_E4M3FN, L.PA_KV_FP8_E5M2])
+def test_fp8_pool_needs_positive_scales(so, dt):
+    assert _decode(so, _pool(dtype=dt, k_scale=0.0)) == L.PA_ERR_INVALID_ARG
+    assert _decode(so, _pool(dtype=dt, v_scale=float("inf"))) == L.PA_ERR_INVALID_ARG
+    assert _decode(so, _pool(dtype=dt, v_scale=float("nan"))) == L.PA_ERR_INVALID_ARG
 
 
 def test_head_ratio_checks(so):

@@ -17,6 +17,8 @@ pytestmark = pytest.mark.gpu
     ("bs8_g4", lambda: W.custom("c", 41, [1, 9, 100, 333], 8, 2, 128, 8)),
     ("bs32_fp8", lambda: W.custom("c", 42, [5, 64, 700], 8, 2, 128, 32, kv_dtype="fp8_e4m3fn")),
     ("d64_fp8", lambda: W.custom("c", 43, [17, 40], 8, 2, 64, 16, kv_dtype="fp8_e4m3fn")),
+    ("bs16_e5m2", lambda: W.custom("c", 45, [5, 64, 700], 8, 2, 128, 16, kv_dtype="fp8_e5m2")),
+    ("d64_bs8_e5m2", lambda: W.custom("c", 46, [17, 40], 8, 2, 64, 8, kv_dtype="fp8_e5m2")),
 ])
 @pytest.mark.parametrize("poison", [False, True])
 def test_scatter_bit_exact(name, make, poison):
@@ -28,21 +30,22 @@ def test_scatter_bit_exact(name, make, poison):
     assert np.array_equal(k, ref.k) and np.array_equal(v, ref.v)
 
 
+@pytest.mark.parametrize("dtype", ["fp8_e4m3fn", "fp8_e5m2"])
 @pytest.mark.parametrize("scale", [1.0, 0.37109375, 3.25, 1e-3])
-def test_fp8_encoder_exhaustive_over_binary16(scale):
+def test_fp8_encoder_exhaustive_over_binary16(scale, dtype):
     """Every binary16 bit pattern (NaN, inf, subnormals included) through the
     device encoder equals the oracle's round-to-nearest-even satfinite encode."""
-    say(f"fp8 exhaustive scale={scale}")
+    say(f"fp8 exhaustive {dtype} scale={scale}")
     Hkv, D = 4, 128
     T = 65536 // (Hkv * D)
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(T, Hkv, D)
     src = bits.view(np.float16)
     slots = np.random.default_rng(3).permutation(T * 2)[:T].astype(np.int64)
     nb = 2 * T // 16 + 1
-    pool = L.KVPool.allocate(nb, 16, Hkv, D, "fp8_e4m3fn", scale, scale * 2, fill_bits=0)
+    pool = L.KVPool.allocate(nb, 16, Hkv, D, dtype, scale, scale * 2, fill_bits=0)
     kd = torch.from_numpy(src).cuda()
     L.pa_reshape_and_cache(pool, kd, kd, torch.from_numpy(slots).cuda())
-    ref = O.HostPool(nb, 16, Hkv, D, "fp8_e4m3fn", scale, scale * 2)
+    ref = O.HostPool(nb, 16, Hkv, D, dtype, scale, scale * 2)
     O.scatter(ref, src, src, slots)
     assert np.array_equal(pool.k.cpu().numpy(), ref.k)
     assert np.array_equal(pool.v.cpu().numpy(), ref.v)

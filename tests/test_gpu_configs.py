@@ -27,6 +27,7 @@ CONFIGS = [
     ("prefix_share_bs16", lambda: W.prefix_share(16), 48, [0, -1, 256]),
     ("prefix_share_bs8", lambda: W.prefix_share(8), 48, [0, -1, 256]),
     ("long_fp8", W.long_fp8, 6, [0, 512]),
+    ("long_e5m2", W.long_e5m2, 6, [0, 512]),
 ]
 
 
@@ -66,7 +67,7 @@ def test_full_size_parity(name, make, nunits, parts):
         assert np.all(np.isfinite(y))
 
 
-VARIANTS = [(name, make, nunits, parts[:1] + ([512] if name == "long_fp8" else []))
+VARIANTS = [(name, make, nunits, parts[:1] + ([512] if name.startswith("long_") else []))
             for name, make, nunits, parts in CONFIGS if name != "tiny"]
 
 

@@ -1,7 +1,7 @@
 """GPU parity of pa_decode against the fp64 oracle on seeded inputs small
 enough for the oracle to evaluate every output, spanning several tiles,
 partitions and ragged tails.  Gate: |y - r| <= 2e-3 + 1e-2 |r| for fp16 KV,
-|y - r| <= 3e-2 for fp8 KV, all outputs finite.  Unused pool slots and table
+|y - r| <= 3e-2 for fp8 KV (e4m3fn or e5m2), all outputs finite.  Unused pool slots and table
 padding hold NaN in every run."""
 import dataclasses
 
@@ -34,6 +34,11 @@ SHAPES = {
     "d64_bs128_g2": lambda: W.custom("s", 63, EDGE_LENS, 8, 4, 64, 128),
     "fp8_d128_bs128_g4": lambda: W.custom("s", 64, EDGE_LENS, 16, 4, 128, 128,
                                           kv_dtype="fp8_e4m3fn"),
+    "e5m2_d128_bs16_g4": lambda: W.custom("s", 65, EDGE_LENS, 32, 8, 128, 16,
+                                          kv_dtype="fp8_e5m2"),
+    "e5m2_d64_bs8_g4": lambda: W.custom("s", 66, EDGE_LENS, 8, 2, 64, 8, kv_dtype="fp8_e5m2"),
+    "e5m2_d128_bs64_g7": lambda: W.custom("s", 67, EDGE_LENS, 28, 4, 128, 64,
+                                          kv_dtype="fp8_e5m2"),
 }
 
 _cache = {}
@@ -63,7 +68,8 @@ def test_decode_matches_oracle(name, part):
         assert np.all(y[s] == 0)
 
 
-@pytest.mark.parametrize("name", ["tiny", "d128_bs8_g7", "fp8_d128_bs32", "d64_bs32_g16"])
+@pytest.mark.parametrize("name", ["tiny", "d128_bs8_g7", "fp8_d128_bs32", "d64_bs32_g16",
+                                  "e5m2_d128_bs16_g4"])
 @pytest.mark.parametrize("variant", ["v_offset", "needles"])
 @pytest.mark.parametrize("part", [-1, 1, 64])
 def test_structured_variants(name, variant, part):
@@ -88,7 +94,8 @@ def _relabel(w, seed):
                                tok_slot=slot.astype(np.int64), pad_block=int(perm[w.pad_block]))
 
 
-@pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "fp8_d128_bs32"])
+@pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "fp8_d128_bs32",
+                                  "e5m2_d64_bs8_g4"])
 @pytest.mark.parametrize("part", [-1, 1, 64])
 def test_physical_relabelling_is_bitwise_invariant(name, part):
     w, _ = _case(name)
@@ -142,7 +149,8 @@ def test_large_scores_stay_finite():
         check_close(w, y, _ref(w, oracle_pool(w)), f"big/p{part}")
 
 
-@pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "fp8_d128_bs32", "d64_bs32_g16"])
+@pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "fp8_d128_bs32", "d64_bs32_g16",
+                                  "e5m2_d128_bs64_g7"])
 @pytest.mark.parametrize("part", [-1, 1, 64])
 def test_cache_policy_flag_changes_no_bits(name, part):
     """Streaming and cacheable K/V reads must give identical outputs."""

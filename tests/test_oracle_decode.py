@@ -198,12 +198,14 @@ def test_scatter_and_copy_are_bit_copies():
     assert np.array_equal(pool.k[dst], pool.k[src]) and np.array_equal(pool.v[dst], pool.v[src])
 
 
-def test_fp8_scatter_quantises_x_over_scale():
-    w = W.custom("q8", 33, [3, 20], 8, 2, 128, 32, kv_dtype="fp8_e4m3fn")
+@pytest.mark.parametrize("dt,tdt,top", [("fp8_e4m3fn", torch.float8_e4m3fn, 448.0),
+                                         ("fp8_e5m2", torch.float8_e5m2, 57344.0)])
+def test_fp8_scatter_quantises_x_over_scale(dt, tdt, top):
+    w = W.custom("q8", 33, [3, 20], 8, 2, 128, 32, kv_dtype=dt)
     pool = O.pool_for_workload(w)
     i = 7
     b, o = divmod(int(w.tok_slot[i]), w.block_size)
     x = w.tok_k[i].astype(np.float32) / np.float32(w.k_scale)
-    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    assert np.abs(x).max() < 448
+    ref = torch.from_numpy(x).to(tdt).view(torch.uint8).numpy()
+    assert np.abs(x).max() <= top
     assert np.array_equal(pool.k[b, o], ref)
