@@ -72,6 +72,9 @@ def lib():
         L.orc_decode_split.restype = None
         L.orc_decode_split.argtypes = [C.POINTER(OrcPool), P, I32, I32, P, I32, P, C.c_float,
                                        I32, P, I64, P, C.c_int]
+        L.orc_prefill.restype = None
+        L.orc_prefill.argtypes = [C.POINTER(OrcPool), P, P, I32, I32, P, I32, P, C.c_float, P,
+                                  I64, P, C.c_int]
         _lib = L
     return _lib
 
@@ -211,6 +214,27 @@ def decode(pool: HostPool, q: np.ndarray, block_tables: np.ndarray, seq_lens: np
     else:
         lib().orc_decode(C.byref(pool.desc), _ptr(qb), S, Hq, _ptr(bt), bt.shape[1], _ptr(lens),
                          C.c_float(scale), _ptr(u), nu, _ptr(out), nthreads)
+    return out
+
+
+def prefill(pool: HostPool, q: np.ndarray, q_start: np.ndarray, block_tables: np.ndarray,
+            seq_lens: np.ndarray, scale: float, rows: Optional[Sequence] = None,
+            nthreads: int = 0) -> np.ndarray:
+    """fp64 prefill output [total_q, Hq, D]: q row i of sequence s (rows
+    q_start[s] + i) attends causally to context positions 0..seq_len - q_len + i.
+    ``rows`` lists (s, kh, i) triples to evaluate (None = all); the rest is NaN."""
+    qb = np.ascontiguousarray(q, dtype=np.float16).view(np.uint16)
+    T, Hq, D = qb.shape
+    qs = np.ascontiguousarray(q_start, dtype=np.int32)
+    S = qs.size - 1
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    assert qs[-1] == T and np.all(np.diff(qs) >= 0) and np.all(np.diff(qs) <= lens)
+    r = None if rows is None else np.ascontiguousarray(np.asarray(rows, np.int32).reshape(-1, 3))
+    out = np.full((T, Hq, D), np.nan, np.float64)
+    lib().orc_prefill(C.byref(pool.desc), _ptr(qb), _ptr(qs), S, Hq, _ptr(bt), bt.shape[1],
+                      _ptr(lens), C.c_float(scale), _ptr(r), 0 if r is None else r.shape[0],
+                      _ptr(out), nthreads)
     return out
 
 

@@ -365,3 +365,51 @@ void orc_decode_split(const orc_pool* p, const uint16_t* q, int32_t S, int32_t H
   decode_units(p, q, S, Hq, block_tables, max_blocks, seq_lens, scale, partition_size, units,
                n_units, out, nthreads, attend_split);
 }
+
+/* ---------------------------------------------------------------- prefill */
+
+void orc_prefill(const orc_pool* p, const uint16_t* qbits, const int32_t* q_start, int32_t S,
+                 int32_t Hq, const int32_t* bt, int32_t max_blocks, const int32_t* lens,
+                 float scale, const int32_t* rows, int64_t n_rows, double* out, int nthreads) {
+  const int32_t Hkv = p->num_kv_heads, D = p->head_dim, g = Hq / Hkv;
+  const double sc = (double)scale;
+  /* with rows == NULL, enumerate (s, kh, i) in order */
+  int64_t total = n_rows;
+  int32_t* all = NULL;
+  if (!rows) {
+    total = 0;
+    for (int32_t s = 0; s < S; ++s) total += (int64_t)(q_start[s + 1] - q_start[s]) * Hkv;
+    all = (int32_t*)malloc(sizeof(int32_t) * 3 * (size_t)(total > 0 ? total : 1));
+    int64_t u = 0;
+    for (int32_t s = 0; s < S; ++s)
+      for (int32_t kh = 0; kh < Hkv; ++kh)
+        for (int32_t i = 0; i < q_start[s + 1] - q_start[s]; ++i) {
+          all[3 * u] = s;
+          all[3 * u + 1] = kh;
+          all[3 * u + 2] = i;
+          ++u;
+        }
+    rows = all;
+  }
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads_or_default(nthreads))
+  for (int64_t u = 0; u < total; ++u) {
+    const int32_t s = rows[3 * u], kh = rows[3 * u + 1], i = rows[3 * u + 2];
+    const int32_t q_len = q_start[s + 1] - q_start[s];
+    const int32_t pos = lens[s] - q_len + i;      /* this query's position */
+    const int32_t n = pos + 1;                    /* keys it sees: 0..pos */
+    double* Kc = (double*)malloc(sizeof(double) * (size_t)n * (size_t)D);
+    double* Vc = (double*)malloc(sizeof(double) * (size_t)n * (size_t)D);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+    orc_gather_head(p, bt + (int64_t)s * max_blocks, n, kh, Kc, Vc);
+    const int64_t row = (int64_t)q_start[s] + i;
+    for (int32_t h = kh * g; h < (kh + 1) * g; ++h) {
+      const uint16_t* qh = qbits + (row * Hq + h) * D;
+      for (int32_t d = 0; d < D; ++d) qd[d] = orc_f16_value(qh[d]);
+      orc_attend(qd, Kc, Vc, n, D, sc, out + (row * Hq + h) * D);
+    }
+    free(Kc);
+    free(Vc);
+    free(qd);
+  }
+  free(all);
+}

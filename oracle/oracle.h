@@ -25,6 +25,12 @@
  *     core", section 4.4; the two fp8 formats of "vLLM intro part 2", section 7).
  *   - copy_blocks copies a whole block for copy-on-write ("GPU memory & KV
  *     cache", COW incident code; "vLLM intro part 2", section 5).
+ *   - Prefill writes a prompt's K/V in bulk and then attends over the paged
+ *     context ("vLLM intro part 2", section 3, KV lifecycle: prefill writes
+ *     blocks in bulk, decode appends one slot); with a prefix-cache hit only the
+ *     uncached tail is computed (same page, section 6 worked example).  Each new
+ *     token attends to itself and every earlier position: the oracle runs the
+ *     decode formula once per query position over that position's prefix.
  */
 #ifndef PKV_ORACLE_H
 #define PKV_ORACLE_H
@@ -101,6 +107,19 @@ void orc_decode_split(const orc_pool* p, const uint16_t* q, int32_t S, int32_t H
                       const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
                       float scale, int32_t partition_size, const int32_t* units,
                       int64_t n_units, double* out, int nthreads);
+
+/* Prefill (a prompt, or the uncached chunk of one): q is [total_q, Hq, D]
+ * binary16 bits; sequence s owns q rows [q_start[s], q_start[s+1]).  Its
+ * q_len = q_start[s+1] - q_start[s] new tokens are the last q_len of its
+ * seq_lens[s] context positions (their K/V already written), so q row i of s
+ * sits at position c = seq_lens[s] - q_len + i and attends to positions 0..c
+ * (causal).  rows lists (s, kh, i) triples to evaluate, each for the gqa query
+ * heads of KV head kh (NULL = every row of every sequence); out is
+ * [total_q, Hq, D] fp64 and only the selected rows are written. */
+void orc_prefill(const orc_pool* p, const uint16_t* q, const int32_t* q_start, int32_t S,
+                 int32_t Hq, const int32_t* block_tables, int32_t max_blocks,
+                 const int32_t* seq_lens, float scale, const int32_t* rows, int64_t n_rows,
+                 double* out, int nthreads);
 
 #ifdef __cplusplus
 }

@@ -85,6 +85,24 @@ class Workload:
     own_from: Optional[np.ndarray] = None
     own_start: Optional[np.ndarray] = None
     shared_start: Optional[np.ndarray] = None
+    # prefill: sequence s brings q_lens[s] new tokens (the last q_lens[s] of its
+    # seq_lens[s] positions); q is then [sum(q_lens), Hq, D], sequence after
+    # sequence.  None for decode (one query token per sequence).
+    q_lens: Optional[np.ndarray] = None
+
+    @property
+    def is_prefill(self) -> bool:
+        return self.q_lens is not None
+
+    @property
+    def q_start(self) -> np.ndarray:
+        """int32 [S + 1]: sequence s owns q rows [q_start[s], q_start[s + 1])."""
+        ql = self.q_lens if self.q_lens is not None else np.ones(self.num_seqs, np.int32)
+        return np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+
+    @property
+    def max_q_len(self) -> int:
+        return int(self.q_lens.max()) if self.q_lens is not None and self.q_lens.size else 1
 
     def token_index(self, s: int, t: int) -> int:
         if t < int(self.own_from[s]):
@@ -187,9 +205,10 @@ def _slots_for(table_row: np.ndarray, ntok: int, bs: int, start: int = 0) -> np.
 
 
 def _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, lens, tables, pad_block,
-            tok_slot, new_idx, ss, partition_size=0, **extra) -> Workload:
+            tok_slot, new_idx, ss, partition_size=0, q_rows=None, **extra) -> Workload:
     T = int(tok_slot.size)
-    q = _normal_f16(ss[2], (S, Hq, D), S)
+    nq = S if q_rows is None else int(q_rows)
+    q = _normal_f16(ss[2], (nq, Hq, D), nq)
     tok_k = _normal_f16(ss[3], (T, Hkv, D), T)
     tok_v = _normal_f16(ss[4], (T, Hkv, D), T)
     k_scale = v_scale = 1.0
@@ -231,6 +250,36 @@ def _independent(name, seed, lens, Hq, Hkv, D, bs, num_blocks, kv_dtype="f16",
     return _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, np.asarray(lens),
                    tables, pad_block, tok_slot, np.asarray(new_idx, np.int64), ss,
                    partition_size=partition_size, own_from=np.zeros(S, np.int64),
+                   own_start=own_start, shared_start=np.full(S, -1, np.int64))
+
+
+def _prefill_independent(name, seed, ctx_lens, q_lens, Hq, Hkv, D, bs, num_blocks,
+                         kv_dtype="f16") -> Workload:
+    """Sequences with private blocks: ctx_lens[s] cached tokens followed by
+    q_lens[s] new ones, which are this step's writes and queries."""
+    ss = np.random.SeedSequence(seed).spawn(6)
+    ctx = np.asarray(ctx_lens, np.int64)
+    ql = np.asarray(q_lens, np.int64)
+    lens = ctx + ql
+    S = len(lens)
+    free = _FreeList(num_blocks, np.random.default_rng(ss[1]))
+    nb = [cdiv(int(n), bs) for n in lens]
+    max_blocks = max(1, max(nb))
+    blocks = [free.take(n) for n in nb]
+    pad_block = int(free.take(1)[0])
+    tables = np.full((S, max_blocks), pad_block, dtype=np.int64)
+    slots, new_idx, pos = [], [], 0
+    own_start = np.zeros(S, np.int64)
+    for s in range(S):
+        tables[s, :nb[s]] = blocks[s]
+        slots.append(_slots_for(tables[s], int(lens[s]), bs))
+        own_start[s] = pos
+        new_idx.append(np.arange(pos + ctx[s], pos + lens[s], dtype=np.int64))
+        pos += int(lens[s])
+    tok_slot = np.concatenate(slots) if slots else np.zeros(0, np.int64)
+    return _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, lens, tables, pad_block,
+                   tok_slot, np.concatenate(new_idx), ss, q_rows=int(ql.sum()),
+                   q_lens=ql.astype(np.int32), own_from=np.zeros(S, np.int64),
                    own_start=own_start, shared_start=np.full(S, -1, np.int64))
 
 
@@ -339,6 +388,86 @@ def prefix_share(block_size: int = 16, seed: Optional[int] = None) -> Workload:
                    group_size=gsz, prefix_tokens=prefix,
                    own_from=np.full(S, prefix, np.int64), own_start=own_start,
                    shared_start=shared_start)
+
+
+# --------------------------------------------------------------------------
+# prefill workloads (new tokens are written by reshape_and_cache, then attend
+# causally over the paged context)
+
+
+def prefill_tiny(seed: int = 7211) -> Workload:
+    """5 sequences, cached lengths {0,3,16,100,0} plus {1,5,17,40,33} new
+    tokens; 8 query / 2 KV heads, head_dim 64, block_size 16, fp16."""
+    return _prefill_independent("prefill_tiny", seed, [0, 3, 16, 100, 0], [1, 5, 17, 40, 33],
+                                8, 2, 64, 16, 64)
+
+
+def prefill_cold_2000(seed: int = 7212) -> Workload:
+    """Cold prefill of 2,000-token prompts (the pages' prefix-cache example
+    before any hit): 8 requests, nothing cached, 16,000 query rows; Llama-3-8B
+    shape (32 query / 8 KV heads, head_dim 128, block_size 16, fp16)."""
+    return _prefill_independent("prefill_cold_2000", seed, [0] * 8, [2000] * 8, 32, 8, 128,
+                                16, 2048)
+
+
+def prefill_chunked_8k(seed: int = 7213) -> Workload:
+    """Chunked prefill under an 8,192-token budget: 16 sequences each bring a
+    512-token chunk on top of 0..3,584 cached tokens (multiples of 512, seeded);
+    Llama-3-8B shape, block_size 16, fp16."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(7)[6])
+    ctx = (rng.integers(0, 8, size=16) * 512).tolist()
+    return _prefill_independent("prefill_chunked_8k", seed, ctx, [512] * 16, 32, 8, 128, 16,
+                                8192)
+
+
+def prefill_prefix_hit(seed: int = 7214) -> Workload:
+    """The pages' prefix-cache hit: a 2,000-token system prompt (125 full
+    blocks of 16) is cached once and shared by 32 requests; each prefills its
+    own 50 new tokens (4 private blocks).  Llama-3-8B shape, fp16."""
+    ss = np.random.SeedSequence(seed).spawn(6)
+    S, prefix, tail, bs = 32, 2000, 50, 16
+    num_blocks = 1024
+    free = _FreeList(num_blocks, np.random.default_rng(ss[1]))
+    npb = prefix // bs
+    pb = free.take(npb)
+    ntail = cdiv(prefix + tail, bs) - npb
+    max_blocks = npb + ntail
+    tables = np.zeros((S, max_blocks), np.int64)
+    slots = [_slots_for(pb, prefix, bs)]
+    new_idx, own_start = [], np.zeros(S, np.int64)
+    pos = prefix
+    for s in range(S):
+        tables[s, :npb] = pb
+        tables[s, npb:] = free.take(ntail)
+        slots.append(_slots_for(tables[s], tail, bs, start=prefix))
+        own_start[s] = pos
+        new_idx.append(np.arange(pos, pos + tail, dtype=np.int64))
+        pos += tail
+    pad_block = int(free.take(1)[0])
+    lens = np.full(S, prefix + tail, np.int64)
+    return _finish("prefill_prefix_hit", seed, S, 32, 8, 128, bs, num_blocks, "f16", lens,
+                   tables, pad_block, np.concatenate(slots), np.concatenate(new_idx), ss,
+                   q_rows=S * tail, q_lens=np.full(S, tail, np.int32), group_size=S,
+                   prefix_tokens=prefix, own_from=np.full(S, prefix, np.int64),
+                   own_start=own_start, shared_start=np.zeros(S, np.int64))
+
+
+PREFILL_CONFIGS = {
+    "prefill_tiny": prefill_tiny,
+    "prefill_cold_2000": prefill_cold_2000,
+    "prefill_chunked_8k": prefill_chunked_8k,
+    "prefill_prefix_hit": prefill_prefix_hit,
+}
+
+
+def custom_prefill(name: str, seed: int, ctx_lens, q_lens, Hq: int, Hkv: int, D: int, bs: int,
+                   num_blocks: Optional[int] = None, kv_dtype: str = "f16") -> Workload:
+    """Independent prefill sequences (cached lengths + new-token counts)."""
+    need = sum(cdiv(int(c) + int(n), bs) for c, n in zip(ctx_lens, q_lens)) + 1
+    if num_blocks is None:
+        num_blocks = max(need + 7, 2 * need)
+    return _prefill_independent(name, seed, list(ctx_lens), list(q_lens), Hq, Hkv, D, bs,
+                                int(num_blocks), kv_dtype=kv_dtype)
 
 
 CONFIGS = {
