@@ -171,6 +171,35 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
               const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_size,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Prefill and chunked-prefill attention over the paged cache.  A prompt's new
+ * tokens are written first (pa_reshape_and_cache, on the same stream) and then
+ * each attends to itself and every earlier position of its sequence ("vLLM
+ * intro part 2", section 3: bulk write on prefill, reads through the block
+ * table); with a prefix-cache hit only the uncached tail is new (same page,
+ * section 6 example).
+ *   out           device, [total_q, num_q_heads, head_dim] binary16 (written).
+ *   q             device, [total_q, num_q_heads, head_dim] binary16: the new
+ *                 tokens of every sequence, sequence after sequence.
+ *   q_start       device, [num_seqs + 1] int32: sequence s owns q rows
+ *                 [q_start[s], q_start[s + 1]).  q_len = q_start[s + 1] -
+ *                 q_start[s] is clamped to [0, max_q_len] and to seq_lens[s];
+ *                 rows outside [0, total_q) are neither read nor written.
+ *   block_tables  device, [num_seqs, max_blocks_per_seq] int32, as in pa_decode.
+ *   seq_lens      device, [num_seqs] int32 context lengths including the new
+ *                 tokens: q row i of sequence s sits at position
+ *                 seq_lens[s] - q_len + i and attends to positions 0 .. that
+ *                 (causal).  Clamped to max_blocks_per_seq * block_size.
+ *   max_q_len     host upper bound of q_len; sizes the grid.
+ *   scale         softmax scale applied to q.k.
+ * num_q_heads must be a multiple of num_kv_heads with a ratio of at most 16.
+ * No workspace is needed.  total_q, num_seqs or max_q_len of 0 is a no-op.
+ * Outputs are bitwise reproducible and do not depend on which physical ids
+ * hold the blocks. */
+int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q,
+               const int32_t* q_start, int32_t num_seqs, int32_t num_q_heads,
+               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+               int32_t max_q_len, float scale, hipStream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* pa_last_error(void);
 

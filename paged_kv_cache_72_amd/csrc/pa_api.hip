@@ -304,4 +304,63 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
   return PA_OK;
 }
 
+int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q,
+               const int32_t* q_start, int32_t num_seqs, int32_t num_q_heads,
+               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+               int32_t max_q_len, float scale, hipStream_t stream) {
+  pa::PoolGeom g;
+  int st = check_pool(pool, &g);
+  if (st) return st;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+  if (total_q < 0) return fail(PA_ERR_INVALID_ARG, "total_q %d < 0", total_q);
+  if (max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "max_q_len %d < 0", max_q_len);
+  if (num_q_heads < 1 || num_q_heads % g.num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, g.num_kv_heads);
+  const int32_t gqa = num_q_heads / g.num_kv_heads;
+  if (gqa > 16) return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d > 16", gqa);
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
+  if (!out || !q || !q_start || !block_tables || !seq_lens)
+    return fail(PA_ERR_INVALID_ARG,
+                "out, q, q_start, block_tables and seq_lens must be non-NULL");
+  if (!aligned16(out) || !aligned16(q))
+    return fail(PA_ERR_ALIGNMENT, "q and out must be 16-byte aligned");
+  if (max_blocks_per_seq < 1)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  const int32_t tile = pa::prefill_rows_per_workgroup() / gqa;
+  const int64_t num_qt = cdiv64(max_q_len, tile);
+  if ((int64_t)num_seqs * num_qt > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs * cdiv(max_q_len, %d) too large", tile);
+  if (g.num_kv_heads > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads %d > 65535 for prefill", g.num_kv_heads);
+
+  pa::PrefillArgs a{};
+  a.k = g.k;
+  a.v = g.v;
+  a.block_stride = g.block_stride;
+  a.row_stride = g.row_stride;
+  a.num_blocks_m1 = (int32_t)(g.num_blocks - 1);
+  a.num_kv_heads = g.num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.gqa = gqa;
+  a.q = (const _Float16*)q;
+  a.out = (_Float16*)out;
+  a.q_start = q_start;
+  a.seq_lens = seq_lens;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.tile_tokens = tile;
+  a.num_qt = (int32_t)num_qt;
+  a.score_scale = (float)((double)scale * 1.4426950408889634 * (double)g.k_scale);
+  a.v_scale = g.v_scale;
+  if (hipError_t e = pa::launch_prefill(a, g.head_dim, g.block_size,
+                                        g.elem_bytes == 2 ? 0 : (g.fp8_e5m2 ? 2 : 1), stream))
+    return fail(PA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 }  // extern "C"

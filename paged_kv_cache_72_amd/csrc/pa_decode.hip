@@ -50,6 +50,7 @@
 //                      directly; a sequence cut by range boundaries leaves one
 //                      partial per range, merged by flat_merge_kernel in range
 //                      order (deterministic).
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -73,18 +74,6 @@ namespace {
 #define PA_FLAT_STAGES 2      // flat schedule: tiles in flight per wave, plus one
 #endif
 
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-// LDS-qualified pointers: stores through them provably leave global memory
-// alone, so uniform loads of read-only tables can stay scalar loads.
-typedef __attribute__((address_space(3))) char lds_char;
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
-typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-
-constexpr float kNegBig = -1.0e30f;   // finite "minus infinity" for the running max
-constexpr float kLazy = 8.0f;         // rescale only when the max grows by > 2^8
-
 template <int BYTES> struct Vec;
 template <> struct Vec<16> { typedef uint4 T; };
 template <> struct Vec<8> { typedef uint2 T; };
@@ -97,38 +86,10 @@ __device__ __forceinline__ void vec_words(const typename Vec<BYTES>::T& v, uint3
   else { w[0] = v; }
 }
 
-__device__ __forceinline__ half4_t halves_of(uint32_t lo, uint32_t hi) {
-  return __builtin_bit_cast(half4_t, make_uint2(lo, hi));
-}
-
-// 4 e4m3fn bytes -> 4 binary16 values (exact: every e4m3fn value is a binary16 value).
-__device__ __forceinline__ half4_t e4m3x4_to_half4(uint32_t w) {
-  const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  const float4_t f = {a.x, a.y, b.x, b.y};
-  return __builtin_convertvector(f, half4_t);
-}
-
-// 4 e5m2 bytes -> 4 binary16 values: e5m2 is binary16 with the low 8 mantissa
-// bits dropped, so byte b widens to the bits b << 8 (NaN and infinity included).
-__device__ __forceinline__ half4_t e5m2x4_to_half4(uint32_t w) {
-  const uint32_t lo = ((w << 8) & 0x0000FF00u) | ((w << 16) & 0xFF000000u);
-  const uint32_t hi = ((w >> 8) & 0x0000FF00u) | (w & 0xFF000000u);
-  return halves_of(lo, hi);
-}
-
 // Byte b of words w0, w1 as two binary16 values (e5m2 widening of one value
 // dim for two tokens): low half from w0, high half from w1.
 __device__ __forceinline__ uint32_t e5m2_pair(uint32_t w0, uint32_t w1, int b) {
   return (((w0 >> (8 * b)) & 0xFFu) << 8) | (((w1 >> (8 * b)) & 0xFFu) << 24);
-}
-
-__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
-__device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ __forceinline__ int clamp_len(int len, int cap) {
-  return len < 0 ? 0 : (len > cap ? cap : len);
 }
 
 // Byte bases, inside the pools, of a tile's two halves (equal when block_size >= 16).

@@ -71,4 +71,37 @@ hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seq
                          int32_t head_dim, int32_t block_size, int kv, bool stream_kv, int mode,
                          hipStream_t stream);
 
+// Prefill over the paged cache: sequence s owns q rows [q_start[s], q_start[s+1]);
+// its new tokens are the last q_len of its seq_lens[s] positions.
+struct PrefillArgs {
+  const char* k;
+  const char* v;
+  int64_t block_stride;
+  int32_t row_stride;
+  int32_t num_blocks_m1;      // largest valid physical id
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t gqa;
+  const _Float16* q;          // [total_q, Hq, D]
+  _Float16* out;              // [total_q, Hq, D]
+  const int32_t* q_start;     // [num_seqs + 1]
+  const int32_t* seq_lens;    // [num_seqs]
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t total_q;
+  int32_t max_q_len;
+  int32_t tile_tokens;        // new tokens per workgroup: rows per workgroup / gqa
+  int32_t num_qt;             // workgroups per (sequence, KV head): cdiv(max_q_len, tile)
+  float score_scale;          // scale * log2(e) * k_scale
+  float v_scale;
+};
+
+// Query rows (token, head pairs) one prefill workgroup covers.
+int prefill_rows_per_workgroup();
+
+// kv: 0 binary16, 1 e4m3fn, 2 e5m2.
+hipError_t launch_prefill(const PrefillArgs& a, int32_t head_dim, int32_t block_size, int kv,
+                          hipStream_t stream);
+
 }  // namespace pa

@@ -23,7 +23,7 @@ PA_POOL_SHARED_BLOCKS = 1
 _DTYPES = {"f16": PA_KV_F16, "fp8_e4m3fn": PA_KV_FP8_E4M3FN, "fp8_e5m2": PA_KV_FP8_E5M2}
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
-           "pa_decode_workspace_size", "pa_decode", "pa_last_error")
+           "pa_decode_workspace_size", "pa_decode", "pa_prefill", "pa_last_error")
 
 
 class PaError(RuntimeError):
@@ -65,6 +65,8 @@ def load() -> C.CDLL:
         L.pa_decode.restype = C.c_int
         L.pa_decode.argtypes = [PP, P, P, I32, I32, P, I32, P, I32, C.c_float, I32, P, C.c_size_t,
                                 P]
+        L.pa_prefill.restype = C.c_int
+        L.pa_prefill.argtypes = [PP, P, P, I32, P, I32, I32, P, I32, P, I32, C.c_float, P]
         L.pa_last_error.restype = C.c_char_p
         L.pa_last_error.argtypes = []
         _lib = L
@@ -204,3 +206,23 @@ def pa_decode(pool: KVPool, out: torch.Tensor, q: torch.Tensor, block_tables: to
         _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
         _dev(seq_lens, torch.int32, "seq_lens"), int(max_seq_len), C.c_float(scale),
         int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_prefill(pool: KVPool, out: torch.Tensor, q: torch.Tensor, q_start: torch.Tensor,
+               block_tables: torch.Tensor, seq_lens: torch.Tensor, max_q_len: int, scale: float,
+               stream=None) -> None:
+    """Causal attention of each sequence's new tokens (q rows q_start[s] ..
+    q_start[s+1] - 1, the last positions of its seq_lens[s]) over its paged
+    context; their K/V must already be in the pool."""
+    T, Hq, D = q.shape
+    S = int(seq_lens.shape[0])
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape [total_q, num_q_heads, head_dim]")
+    if q_start.shape != (S + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("q_start must be [num_seqs + 1], block_tables [num_seqs, max_blocks]")
+    _check(load().pa_prefill(
+        C.byref(pool.desc), _dev(out, torch.float16, "out"), _dev(q, torch.float16, "q"), T,
+        _dev(q_start, torch.int32, "q_start"), S, Hq,
+        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+        _dev(seq_lens, torch.int32, "seq_lens"), int(max_q_len), C.c_float(scale),
+        _stream(stream)))

@@ -65,6 +65,14 @@ class DeviceCase:
                     partition_size, ws)
         return out
 
+    def prefill(self, out=None) -> torch.Tensor:
+        """pa_prefill of this step's new tokens (their K/V were written above)."""
+        w = self.w
+        out = self.out if out is None else out
+        qs = torch.from_numpy(w.q_start).to(self.q.device)
+        L.pa_prefill(self.pool, out, self.q, qs, self.bt, self.lens, w.max_q_len, w.scale)
+        return out
+
     def pool_bits(self, blocks=None):
         k, v = self.pool.k, self.pool.v
         if blocks is not None:
@@ -102,6 +110,29 @@ def check_close(w: W.Workload, y: np.ndarray, r: np.ndarray, what: str = "") -> 
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
                            f"worst {stats}")
     return stats
+
+
+def sample_prefill_rows(w: W.Workload, n: int, seed: int = 0):
+    """(s, kh, i) query rows to check at full size: seeded, plus the first and
+    last new token of the longest and shortest contexts."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for s in (int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens))):
+        ql = int(w.q_lens[s])
+        rows.update({(s, 0, 0), (s, w.num_kv_heads - 1, ql - 1)})
+    while len(rows) < n:
+        s = int(rng.integers(w.num_seqs))
+        if w.q_lens[s] == 0:
+            continue
+        rows.add((s, int(rng.integers(w.num_kv_heads)), int(rng.integers(int(w.q_lens[s])))))
+    return sorted(rows)
+
+
+def prefill_row_index(w: W.Workload, rows):
+    """numpy index (q row, head) of every query head of the given (s, kh, i)."""
+    g, qs = w.gqa, w.q_start
+    return tuple(np.array([(qs[s] + i, h) for s, kh, i in rows
+                           for h in range(kh * g, (kh + 1) * g)]).T)
 
 
 def sample_units(w: W.Workload, n: int, seed: int = 0):
