@@ -160,6 +160,147 @@ def ingest_counters(fetch_csv: str, write_csv: str, calib_gib: float, config: st
     return entry
 
 
+PREFILL_METRIC = "paged-attn prefill achieved TFLOP/s (% of MI355X fp16 MFMA peak)"
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(w, rows=None) -> int:
+    """Algorithmic flops of causal prefill: every (query row, head) scores and
+    weights pos + 1 positions, 2 flops per multiply-add in q.k and in p.v."""
+    ql = w.q_lens.astype(np.int64)
+    ctx = w.seq_lens.astype(np.int64) - ql
+    if rows is None:
+        keys = int((ql * ctx + ql * (ql + 1) // 2).sum())
+        return 4 * w.head_dim * w.num_q_heads * keys
+    keys = sum(int(ctx[s]) + i + 1 for s, _, i in rows)
+    return 4 * w.head_dim * w.gqa * keys
+
+
+def prefill_bytes(w) -> int:
+    """K/V read once (shared blocks once), q read and out written once."""
+    e = w.kv_elem_bytes
+    row = w.num_kv_heads * w.head_dim * e * 2
+    kv = unique_kv_tokens(w) * row
+    return kv + int(w.q.shape[0]) * w.num_q_heads * w.head_dim * 2 * 2
+
+
+def cpu_baseline_prefill(w, budget_s: float) -> dict:
+    """The oracle's prefill on seeded query rows for about budget_s seconds."""
+    import oracle as O
+    nthreads = min(16, len(os.sched_getaffinity(0)))
+    pool = O.pool_for_workload(w, nthreads=nthreads)
+    rng = np.random.default_rng(0)
+    qs = w.q_start
+    done_rows, done_flops, el = 0, 0, 0.0
+    t0 = time.perf_counter()
+    while el < budget_s:
+        rows = []
+        for _ in range(4 * nthreads):
+            s = int(rng.integers(w.num_seqs))
+            if w.q_lens[s]:
+                rows.append((s, int(rng.integers(w.num_kv_heads)),
+                             int(rng.integers(int(w.q_lens[s])))))
+        O.prefill(pool, w.q, qs, w.block_tables, w.seq_lens, w.scale, rows=rows,
+                  nthreads=nthreads)
+        done_rows += len(rows)
+        done_flops += prefill_flops(w, rows)
+        el = time.perf_counter() - t0
+    rate = done_flops / el
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads,
+            "kind": "oracle", "ms_per_step": round(prefill_flops(w) / rate * 1e3, 1),
+            "sample": f"{done_rows} seeded (sequence, KV head, new token) rows of the "
+                      f"{w.name} step, each for its {w.gqa} query heads, over {el:.1f} s; "
+                      "fp64 C oracle, OpenMP; ms_per_step extrapolates to the whole step"}
+
+
+def run_prefill(args, w) -> int:
+    import torch
+    from paged_kv_cache_72_amd import lib as L
+
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    q = torch.from_numpy(w.q).to(dev)
+    bt = torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    qs = torch.from_numpy(w.q_start).to(dev)
+    out = torch.empty_like(q)
+    k_all = torch.from_numpy(w.tok_k).to(dev)
+    v_all = torch.from_numpy(w.tok_v).to(dev)
+    slots = torch.from_numpy(w.tok_slot).to(dev)
+    shared = w.has_shared_blocks
+    base = L.KVPool.allocate(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                             w.kv_dtype, w.k_scale, w.v_scale, dev, fill_bits=0,
+                             shared_blocks=shared)
+    L.pa_reshape_and_cache(base, k_all, v_all, slots)
+    idx = torch.from_numpy(w.new_idx).to(dev)
+    k_new = k_all.index_select(0, idx).contiguous()
+    v_new = v_all.index_select(0, idx).contiguous()
+    slot_new = slots.index_select(0, idx).contiguous()
+    del k_all, v_all, slots
+    pools = [base]
+    for _ in range(args.layers - 1):
+        pools.append(L.KVPool(base.k.clone(), base.v.clone(), w.block_size, w.num_kv_heads,
+                              w.head_dim, w.kv_dtype, w.k_scale, w.v_scale,
+                              shared_blocks=shared))
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        p = pools[i % len(pools)]
+        L.pa_reshape_and_cache(p, k_new, v_new, slot_new, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        L.pa_prefill(p, out, q, qs, bt, lens, w.max_q_len, w.scale, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    pf_avg = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    flops = prefill_flops(w)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (pf_avg * 1e-3) / 1e12
+    nbytes = prefill_bytes(w)
+    res = {
+        "metric": PREFILL_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and free-list block ids)",
+        "config": {"workload": f"{w.name}: {w.num_seqs} seqs, new tokens "
+                               f"{int(w.q_lens.min())}-{int(w.q_lens.max())} "
+                               f"(sum {int(w.q_lens.sum())}), context "
+                               f"{int(w.seq_lens.min())}-{int(w.seq_lens.max())}, "
+                               f"{w.num_q_heads} q / {w.num_kv_heads} kv heads, head_dim "
+                               f"{w.head_dim}, block_size {w.block_size}, {w.kv_dtype} KV; "
+                               f"step = reshape_and_cache of {w.new_idx.size} tokens + prefill",
+                   "global_batch": w.num_seqs, "seq_len": w.max_seq_len, "parallelism": "none",
+                   "layers_rotated": args.layers, "shared_blocks": shared},
+        "pct_of_peak": round(100 * value / MFMA_F16_PEAK_TFLOPS, 2),
+        "prefill_tokens_per_s": round(float(w.q_lens.sum()) / (ms_step * 1e-3), 1),
+        "alg_flops_per_launch": flops,
+        "alg_bytes_per_launch": nbytes,
+        "hbm_GB_per_s": round(nbytes / (pf_avg * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill", "achieved": round(achieved, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_entry(w.name), "avg_launch_ms": round(pf_avg, 5),
+                     "alg_flops_per_launch": flops,
+                     "kernel_source_hash": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +338,8 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     L.load()
+    if args.config in W.PREFILL_CONFIGS:
+        return run_prefill(args, W.PREFILL_CONFIGS[args.config]())
     w = W.CONFIGS[args.config]()
     dev = "cuda"
     stream = torch.cuda.current_stream()

@@ -190,7 +190,7 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
  *                 seq_lens[s] - q_len + i and attends to positions 0 .. that
  *                 (causal).  Clamped to max_blocks_per_seq * block_size.
  *   max_q_len     host upper bound of q_len; sizes the grid.
- *   scale         softmax scale applied to q.k.
+ *   scale         softmax scale applied to q.k; finite and > 0.
  * num_q_heads must be a multiple of num_kv_heads with a ratio of at most 16.
  * No workspace is needed.  total_q, num_seqs or max_q_len of 0 is a no-op.
  * Outputs are bitwise reproducible and do not depend on which physical ids

@@ -327,13 +327,13 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
     return fail(PA_ERR_ALIGNMENT, "q and out must be 16-byte aligned");
   if (max_blocks_per_seq < 1)
     return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PA_ERR_INVALID_ARG, "scale must be finite and positive");
   const int32_t tile = pa::prefill_rows_per_workgroup() / gqa;
   const int64_t num_qt = cdiv64(max_q_len, tile);
-  if ((int64_t)num_seqs * num_qt > INT32_MAX)
-    return fail(PA_ERR_INVALID_ARG, "num_seqs * cdiv(max_q_len, %d) too large", tile);
-  if (g.num_kv_heads > 65535)
-    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads %d > 65535 for prefill", g.num_kv_heads);
+  if ((int64_t)num_seqs * g.num_kv_heads * num_qt > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs * num_kv_heads * cdiv(max_q_len, %d) too large",
+                tile);
 
   pa::PrefillArgs a{};
   a.k = g.k;

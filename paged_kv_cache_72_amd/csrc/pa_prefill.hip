@@ -13,14 +13,16 @@
 //
 // Work decomposition and data flow:
 //   * A workgroup owns one (sequence, KV head, tile of QT = floor(128 / gqa)
-//     new tokens).  Its 128 query rows are (token, head) pairs, head fastest,
+//     new tokens); the query tiles of one (sequence, KV head) are placed on
+//     one XCD so that they share its L2.  Its 128 query rows are (token, head) pairs, head fastest,
 //     so the gqa query heads of the KV head share every K/V tile it stages.
 //     4 waves x 2 groups x 16 rows.
 //   * K/V tiles of 32 positions are gathered through the block table into LDS
 //     by whole 16-byte row chunks (fp8 pools are widened exactly to binary16 on
 //     the way).  Rows are XOR-swizzled by chunk so that the column-wise reads
 //     below hit distinct banks.  The next tile's global loads are issued before
-//     the current tile is computed.
+//     the current tile is computed and land in the other of two LDS buffers, so
+//     each tile costs one workgroup barrier.
 //   * Scores are computed transposed, S^T = K Q^T, with the 16x16x32 f16 MFMA:
 //     K rows are the A operand (from LDS), the group's 16 query rows the B
 //     operand (held in registers for the whole loop).  Lane (h, n) then holds
@@ -31,9 +33,11 @@
 //     nb covers dims {8n + nb} (head_dim 128) so a lane's output dims are
 //     contiguous and each row is written with one 16-byte store.
 //   * Online softmax per query row in log2 units; the running max moves only
-//     when a tile exceeds it by more than 2^8 (P <= 256 fits binary16).  The
-//     causal mask is a select on position <= query position; positions past
-//     the context are never loaded (zeros in LDS) and are masked as well.
+//     when a tile exceeds it by more than 2^8 (P <= 256 fits binary16), which
+//     a wave vote detects, so the cross-lane row max is formed only then.  The
+//     causal mask is a select on position <= query position, applied only on
+//     tiles that reach past the workgroup's first query position; positions
+//     past the context are never loaded (zeros in LDS) and are masked as well.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -50,17 +54,34 @@ template <int D, int BS, int KV>
 struct PfTile {
   static constexpr int E = KV ? 1 : 2;        // bytes per stored element
   static constexpr int CPR = D / 8;           // 8-element chunks per row
-  static constexpr int RB = D * 2;            // LDS bytes per row (binary16)
-  static constexpr int NL = kPfKeys * CPR / (kPfWaves * 64);  // chunks per thread
+  static constexpr int KRB = D * 2;           // LDS bytes per K row (binary16)
+  static constexpr int NL = kPfKeys * CPR / (kPfWaves * 64);  // K chunks per thread
+  static constexpr int VK = NL;               // V positions per thread (same count)
   static constexpr int NST = D / 32;          // 32-dim MFMA steps of q . k
   static constexpr int NB = D / 16;           // P V column blocks
-  static constexpr int VB = NB * 2;           // V bytes per lane per key row
-  static constexpr int TILE = kPfKeys * RB;   // LDS bytes per K (or V) tile
-  static_assert(NL >= 1, "tile smaller than the workgroup");
+  static constexpr int TILE_K = kPfKeys * KRB;
+  static constexpr int TILE_V = D * kPfKeys * 2;   // V^T: one 64-byte row per dim
+  static constexpr int BUF = TILE_K + TILE_V;
+  static_assert(NL >= 1 && NL <= 2, "tile and workgroup sizes");
 
-  // byte offset of chunk c of row r inside a tile
-  __device__ static __forceinline__ int slot(int r, int c) {
-    return r * RB + ((c ^ (r % CPR)) << 4);
+  // K tile: row per position, 16-byte chunks XOR-swizzled by sw(key); sw maps
+  // the 16 positions each score MFMA reads (see kpos) to 16 distinct values.
+  __device__ static __forceinline__ int sw(int key) { return ((key >> 3) << 2) | (key & 3); }
+  __device__ static __forceinline__ int kslot(int key, int c) {
+    return key * KRB + ((c ^ (sw(key) & (CPR - 1))) << 4);
+  }
+  // V^T tile: for each chunk of 8 positions kc, a 16-byte slot per dim holding
+  // those 8 positions in order.  The dim's slot is XOR-swizzled by dim / 8 so
+  // that a write of one dim from 8 chunk-lanes and a read of 16 consecutive
+  // dims both spread over all banks.
+  __device__ static __forceinline__ int vslot(int dim, int kc) {
+    return (kc * D + (dim ^ ((dim >> 3) & 7))) << 4;
+  }
+  // Row r of score block kb holds position kpos(kb, r); then the scores a
+  // lane receives are positions 8h + 4kb + i, i.e. positions 8h .. 8h + 7 of
+  // the P operand's k slots in order.
+  __device__ static __forceinline__ int kpos(int kb, int r) {
+    return 8 * (r >> 2) + 4 * kb + (r & 3);
   }
 };
 
@@ -72,6 +93,10 @@ __device__ __forceinline__ uint4 widen8(uint2 w, int kv) {
   return make_uint4(ua.x, ua.y, ub.x, ub.y);
 }
 
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
 // lo/hi 16-bit halves of two words as one word: half `sel` of x low, of y high
 __device__ __forceinline__ uint32_t pick_halves(uint32_t x, uint32_t y, int sel) {
   return sel ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
@@ -80,17 +105,23 @@ __device__ __forceinline__ uint32_t pick_halves(uint32_t x, uint32_t y, int sel)
 template <int D, int BS, int KV>
 __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a) {
   typedef PfTile<D, BS, KV> T;
-  constexpr int E = T::E, CPR = T::CPR, NL = T::NL, NST = T::NST, NB = T::NB;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::TILE];
-  lds_char* ks = (lds_char*)smem;
-  lds_char* vs = ks + T::TILE;
+  constexpr int E = T::E, CPR = T::CPR, NL = T::NL, VK = T::VK, NST = T::NST, NB = T::NB;
+  // two buffers, each a K tile then a V^T tile
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::BUF];
+  lds_char* const lds0 = (lds_char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int h = lane >> 4, n = lane & 15;
-  const int S = a.num_seqs;
-  const int s = blockIdx.x % S;
-  const int qt = a.num_qt - 1 - (int)(blockIdx.x / S);   // longest tiles first
-  const int kh = blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that each
+  // XCD gets a contiguous run of (sequence, KV head, query tile) items and the
+  // query tiles of one (sequence, KV head) share that XCD's L2.
+  const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
+  const int xcd = wg & 7, per = nwg >> 3, rem = nwg & 7;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + (wg >> 3);
+  const int pair = item / a.num_qt;
+  const int qt = a.num_qt - 1 - (item - pair * a.num_qt);   // longest tiles first
+  const int s = pair / a.num_kv_heads;
+  const int kh = pair - s * a.num_kv_heads;
   const int g = a.gqa, QT = a.tile_tokens;
 
   const int qs0 = a.q_start[s];
@@ -123,51 +154,73 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
     }
   }
 
-  // ---- tile loader: thread chunk i covers row (tid + 256 i) / CPR, chunk % CPR.
-  // Raw pool bytes are held in registers while the previous tile is computed;
-  // fp8 is widened only when the tile is written to LDS.
+  // ---- tile loader.  K: chunk i of a thread is row (tid + 256 i) / CPR,
+  // chunk (tid + 256 i) % CPR.  V: positions VK * (tid / CPR) + u, chunk
+  // tid % CPR, written transposed.  A wave's positions (4 or 8 consecutive,
+  // aligned) lie in one block for every supported block size, so block ids are
+  // scalar loads.  Raw bytes wait in registers while the previous tile is
+  // computed; fp8 is widened when written to LDS.
   typedef typename std::conditional<E == 2, uint4, uint2>::type Raw;
-  Raw kr[NL], vr[NL];
+  Raw kr[NL], vr[VK];
+  const int64_t head_off = (int64_t)kh * D * E;
+  // V loader lanes: wave w covers positions 8w .. 8w + 7 of the tile; lane
+  // bits 0-1 (and bit 2 when VK == 1) pick the position, the rest the chunk.
+  const int vkey = VK == 2 ? 8 * wid + 2 * (tid & 3) : 8 * wid + (tid & 7);
+  const int vch = VK == 2 ? (lane >> 2) : (lane >> 3);
+  auto row_addr = [&](int pos, int pos0, int ch, bool& ok) -> int64_t {
+    ok = false;
+    if (pos0 >= kv_end) return 0;
+    int blk = bt[pos0 / BS];
+    blk = blk < 0 ? 0 : (blk > a.num_blocks_m1 ? a.num_blocks_m1 : blk);
+    ok = pos < kv_end;
+    return (int64_t)blk * a.block_stride + (int64_t)(pos % BS) * a.row_stride + head_off +
+           ch * 8 * E;
+  };
   auto load_tile = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int idx = tid + kPfWaves * 64 * i;
-      const int key = idx / CPR, ch = idx % CPR;
-      const int pos = kt + key;
-      // A wave's 64 chunks are 64 / CPR consecutive positions starting at a
-      // multiple of 64 / CPR (4 or 8), so they share one block for every
-      // supported block size: the block id is a scalar load.
+      const int pos = kt + idx / CPR;
       const int pos0 = uni(kt + (kPfWaves * 64 * i + 64 * wid) / CPR);
-      kr[i] = Raw{};
-      vr[i] = Raw{};
-      if (pos0 < kv_end) {
-        int blk = bt[pos0 / BS];
-        blk = blk < 0 ? 0 : (blk > a.num_blocks_m1 ? a.num_blocks_m1 : blk);
-        if (pos < kv_end) {
-          const int64_t off = (int64_t)blk * a.block_stride +
-                              (int64_t)(pos % BS) * a.row_stride + (int64_t)kh * D * E +
-                              ch * 8 * E;
-          kr[i] = *(const Raw*)(a.k + off);
-          vr[i] = *(const Raw*)(a.v + off);
-        }
-      }
+      bool ok;
+      const int64_t off = row_addr(pos, pos0, idx % CPR, ok);
+      kr[i] = ok ? *(const Raw*)(a.k + off) : Raw{};
+    }
+    const int vbase = kt + vkey;
+    const int vpos0 = uni(kt + 8 * wid);
+#pragma unroll
+    for (int u = 0; u < VK; ++u) {
+      bool ok;
+      const int64_t off = row_addr(vbase + u, vpos0, vch, ok);
+      vr[u] = ok ? *(const Raw*)(a.v + off) : Raw{};
     }
   };
-  auto store_tile = [&]() {
+  auto widen = [&](const Raw& r) -> uint4 {
+    if constexpr (E == 2) return r;
+    else return widen8(r, KV);
+  };
+  auto store_tile = [&](lds_char* ks) {
+    lds_char* vs = ks + T::TILE_K;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int idx = tid + kPfWaves * 64 * i;
-      const int key = idx / CPR, ch = idx % CPR;
-      uint4 kw, vw;
-      if constexpr (E == 2) {
-        kw = kr[i];
-        vw = vr[i];
+      *(lds_u32x4*)(ks + T::kslot(idx / CPR, idx % CPR)) = __builtin_bit_cast(u32x4_t, widen(kr[i]));
+    }
+    const int ch = vch;
+    uint4 vw[VK];
+#pragma unroll
+    for (int u = 0; u < VK; ++u) vw[u] = widen(vr[u]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int off = T::vslot(8 * ch + e, vkey >> 3) + (vkey & 7) * 2;
+      if constexpr (VK == 2) {
+        *(__attribute__((address_space(3))) uint32_t*)(vs + off) =
+            pick_halves(word_of(vw[0], e >> 1), word_of(vw[1], e >> 1), e & 1);
       } else {
-        kw = widen8(kr[i], KV);
-        vw = widen8(vr[i], KV);
+        const uint32_t wv = word_of(vw[0], e >> 1);
+        *(__attribute__((address_space(3))) uint16_t*)(vs + off) =
+            (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xFFFFu));
       }
-      *(lds_u32x4*)(ks + T::slot(key, ch)) = __builtin_bit_cast(u32x4_t, kw);
-      *(lds_u32x4*)(vs + T::slot(key, ch)) = __builtin_bit_cast(u32x4_t, vw);
     }
   };
 
@@ -179,14 +232,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
   float m_run[2] = {kNegBig, kNegBig}, l_run[2] = {0.f, 0.f};
   const float sc = a.score_scale;
 
-  load_tile(0);
-  for (int kt = 0; kt < kv_end; kt += kPfKeys) {
-    __syncthreads();                 // the previous tile's LDS reads are done
-    store_tile();
-    __syncthreads();
-    if (kt + kPfKeys < kv_end) load_tile(kt + kPfKeys);
-
-    // scores S^T for both row groups; K operand: key 16 kb + n, dims 32 st + 8 h .. + 7
+  // One tile of math on LDS buffer (ks, vs) for positions kt .. kt + 31.
+  auto compute = [&](const lds_char* ks, const lds_char* vs, int kt, bool diag) {
+    // scores S^T for both row groups; block kb row r is position kpos(kb, r)
     float4_t sa[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -194,7 +242,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
 #pragma unroll
       for (int st = 0; st < NST; ++st)
         kop[st] = __builtin_bit_cast(
-            half8_t, *(const lds_u32x4*)(ks + T::slot(16 * kb + n, 4 * st + h)));
+            half8_t, *(const lds_u32x4*)(ks + T::kslot(T::kpos(kb, n), 4 * st + h)));
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         sa[c][kb] = {0.f, 0.f, 0.f, 0.f};
@@ -203,49 +251,33 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
           sa[c][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[st], qop[c][st], sa[c][kb], 0, 0, 0);
       }
     }
-    // V operands: positions key(kk) = kk < 4 ? 4h + kk : 16 + 4h + kk - 4, the
-    // lane's NB dims starting at NB * n, transposed so that operand nb holds
-    // dim NB * n + nb of the 8 positions
-    uint32_t vw[8][NB / 2];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int key = kk < 4 ? 4 * h + kk : 12 + 4 * h + kk;
-      const int byte = n * T::VB;
-      const int off = key * T::RB + (((byte >> 4) ^ (key % CPR)) << 4) + (byte & 15);
-      if constexpr (NB == 8) {
-        const u32x4_t w = *(const lds_u32x4*)(vs + off);
-        vw[kk][0] = w.x; vw[kk][1] = w.y; vw[kk][2] = w.z; vw[kk][3] = w.w;
-      } else {
-        const u32x2_t w = *(const lds_u32x2*)(vs + off);
-        vw[kk][0] = w.x; vw[kk][1] = w.y;
-      }
-    }
+    // V^T operands: block nb column n is dim 16 nb + n, k slots are positions 8h .. 8h + 7
     half8_t vop[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      uint4 w;
-      w.x = pick_halves(vw[0][nb >> 1], vw[1][nb >> 1], nb & 1);
-      w.y = pick_halves(vw[2][nb >> 1], vw[3][nb >> 1], nb & 1);
-      w.z = pick_halves(vw[4][nb >> 1], vw[5][nb >> 1], nb & 1);
-      w.w = pick_halves(vw[6][nb >> 1], vw[7][nb >> 1], nb & 1);
-      vop[nb] = __builtin_bit_cast(half8_t, w);
-    }
+    for (int nb = 0; nb < NB; ++nb)
+      vop[nb] = __builtin_bit_cast(half8_t, *(const lds_u32x4*)(vs + T::vslot(16 * nb + n, h)));
 
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+      // raw scores of positions kt + 8h + k; the scale (> 0) is applied in the exponent's fma
       float x[8];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          x[4 * kb + i] = (kt + 16 * kb + 4 * h + i <= qpos[c]) ? sa[c][kb][i] * sc : -INFINITY;
-      float tmax = x[0];
+        for (int i = 0; i < 4; ++i) x[4 * kb + i] = sa[c][kb][i];
+      if (diag) {            // uniform branch: only diagonal tiles pay for the mask
+        const int lim = qpos[c] - kt - 8 * h;
 #pragma unroll
-      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
-      tmax = xor_max(tmax, 16);
-      tmax = xor_max(tmax, 32);
-      const bool grow = tmax > m_run[c] + kLazy;
-      if (__any(grow)) {
+        for (int k = 0; k < 8; ++k) x[k] = k <= lim ? x[k] : -INFINITY;
+      }
+      // The running max only has to move when some score exceeds it by more
+      // than 2^8, so each lane tests its own 8 scores and the wave votes; the
+      // row max across the 4 lanes of a row is formed only when it moves.
+      float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))) * sc;
+      if (__any(tmax > m_run[c] + kLazy)) {
+        tmax = xor_max(tmax, 16);
+        tmax = xor_max(tmax, 32);
         const float m_new = fmaxf(m_run[c], tmax);
         const float alpha = __builtin_amdgcn_exp2f(m_run[c] - m_new);
         l_run[c] *= alpha;
@@ -259,7 +291,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
       }
       float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_run[c]);
+      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sc, -m_run[c]));
       l_run[c] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       const float4_t p0 = {p[0], p[1], p[2], p[3]}, p1 = {p[4], p[5], p[6], p[7]};
       const half4_t h0 = __builtin_convertvector(p0, half4_t);
@@ -269,9 +301,27 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
       for (int nb = 0; nb < NB; ++nb)
         acc[c][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, vop[nb], acc[c][nb], 0, 0, 0);
     }
+  };
+
+  load_tile(0);
+  store_tile(lds0);
+  __syncthreads();
+  int buf = 0;
+  for (int kt = 0; kt < kv_end; kt += kPfKeys) {
+    // One barrier per tile: the next tile goes to the other buffer, whose last
+    // readers finished before the barrier that ended the previous iteration.
+    const bool more = kt + kPfKeys < kv_end;
+    if (more) load_tile(kt + kPfKeys);
+    const lds_char* ks = lds0 + buf * T::BUF;
+    // positions kt .. kt + 31 precede every query row of the workgroup except
+    // on the diagonal tiles: only those need the causal mask
+    compute(ks, ks + T::TILE_K, kt, kt + kPfKeys - 1 > ctx + q0);
+    if (more) store_tile(lds0 + (buf ^ 1) * T::BUF);
+    __syncthreads();
+    buf ^= 1;
   }
 
-  // ---- epilogue: lane (h, n) holds rows 4h + i, dims NB * n .. NB * n + NB - 1
+  // ---- epilogue: lane (h, n) holds rows 4h + i, dims 16 nb + n
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     float lt = xor_sum(l_run[c], 16);
@@ -284,22 +334,16 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
       const int row = qs0 + q0 + t;
       if (!(t < QT && q0 + t < q_len && row >= 0 && row < a.total_q)) continue;
       const float f = a.v_scale / li;
-      _Float16 o[NB];
+      _Float16* op = a.out + ((int64_t)row * a.num_q_heads + kh * g + j) * D + n;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) o[nb] = (_Float16)(acc[c][nb][i] * f);
-      _Float16* op = a.out + ((int64_t)row * a.num_q_heads + kh * g + j) * D + NB * n;
-      if constexpr (NB == 8) {
-        *(uint4*)op = __builtin_bit_cast(uint4, o);
-      } else {
-        *(uint2*)op = __builtin_bit_cast(uint2, o);
-      }
+      for (int nb = 0; nb < NB; ++nb) op[16 * nb] = (_Float16)(acc[c][nb][i] * f);
     }
   }
 }
 
 template <int D, int BS>
 hipError_t launch_pf_bs(const PrefillArgs& a, int kv, hipStream_t stream) {
-  const dim3 grid((uint32_t)a.num_seqs * (uint32_t)a.num_qt, (uint32_t)a.num_kv_heads);
+  const dim3 grid((uint32_t)a.num_seqs * (uint32_t)a.num_kv_heads * (uint32_t)a.num_qt);
   const dim3 block(kPfWaves * 64);
   switch (kv) {
     case 0: hipLaunchKernelGGL((prefill_kernel<D, BS, 0>), grid, block, 0, stream, a); break;
