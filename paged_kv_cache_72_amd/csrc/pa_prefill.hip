@@ -341,12 +341,305 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp16 pools: K/V tiles go from HBM straight into LDS (the 16-byte
+// global-to-LDS load, lane i filling bytes 16 i .. 16 i + 15 of a wave's 1 KB),
+// three LDS buffers deep, so two tiles are in flight while one is computed and
+// no registers hold staged data.  V stays row-major in LDS and the P V operand
+// is read with the LDS transpose read (within each 16-lane group, result lane
+// l, element k is halfword l % 4 of what source lane 4k + l / 4 points at), so
+// nothing is transposed by hand.  LDS reads are issued as inline asm: the
+// compiler would otherwise drain every outstanding global-to-LDS load before
+// each LDS read; here the waits are explicit, and only for the tile in use.
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct PfDma {
+  static constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  static constexpr int RB = 2 * D;                        // bytes per row
+  static constexpr int RPI = 1024 / RB;                   // rows per wave load
+  static constexpr int NI = kPfKeys / RPI / kPfWaves;     // loads per wave per tile, each of K and V
+  static constexpr int TILE = kPfKeys * RB;
+  static constexpr int BUF = 2 * TILE;                    // K tile then V tile
+  static constexpr int DPT = 2 * NI;                      // loads per thread per tile
+  static constexpr int NST = D / 32;
+  static constexpr int NB = D / 16;
+  static_assert(NI >= 1 && 3 * BUF <= 65536, "tile shape");
+  // K rows: chunk swizzle that gives the 16 rows one score MFMA reads
+  // (positions 8 (n / 4) + 4 kb + n % 4, n = 0..15) distinct chunks.
+  __device__ static __forceinline__ int ksw(int key) {
+    return (((key >> 3) << 2) | (key & 3)) & (CPR - 1);
+  }
+  // V rows: the 4 rows one transpose read spans (positions differing in
+  // bits 0-1) start their 32-byte dim windows on different banks.
+  __device__ static __forceinline__ int vsw(int key) { return (2 * (key & 3)) & (CPR - 1); }
+};
+
+template <int OFF>
+__device__ __forceinline__ half8_t lds_b128(uint32_t addr) {
+  u32x4_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+  return __builtin_bit_cast(half8_t, v);
+}
+
+template <int OFF>
+__device__ __forceinline__ half4_t lds_tr16(uint32_t addr) {
+  u32x2_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+  return __builtin_bit_cast(half4_t, v);
+}
+
+// Wait until at most N LDS / scalar-memory operations are outstanding, and
+// make the values read so far depend on that wait.
+template <int N, typename V>
+__device__ __forceinline__ void lgkm_wait(V& v) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "i"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_all_regs() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" : : "i"(N) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  // vmcnt(N), expcnt and lgkmcnt unchanged (gfx9 encoding: vmcnt low bits
+  // 3:0 and high bits 15:14, expcnt 6:4, lgkmcnt 11:8)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_f16_kernel(
+    PrefillArgs a, const int32_t* __restrict__ tables) {
+  typedef PfDma<D> T;
+  constexpr int CPR = T::CPR, RB = T::RB, NST = T::NST, NB = T::NB;
+  __shared__ __attribute__((aligned(1024))) char smem[3 * T::BUF];
+  lds_char* const lds0 = (lds_char*)smem;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds0;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int h = lane >> 4, n = lane & 15;
+  const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
+  const int xcd = wg & 7, per = nwg >> 3, rem = nwg & 7;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + (wg >> 3);
+  const int pair = item / a.num_qt;
+  const int qt = a.num_qt - 1 - (item - pair * a.num_qt);
+  const int s = pair / a.num_kv_heads;
+  const int kh = pair - s * a.num_kv_heads;
+  const int g = a.gqa, QT = a.tile_tokens;
+
+  const int qs0 = a.q_start[s];
+  const int cap = a.max_blocks * BS;
+  const int len = clamp_len(a.seq_lens[s], cap);
+  int q_len = clamp_len(a.q_start[s + 1] - qs0, a.max_q_len);
+  q_len = q_len < len ? q_len : len;
+  const int q0 = qt * QT;
+  if (q0 >= q_len) return;
+  const int ctx = len - q_len;
+  const int t_hi = q_len < q0 + QT ? q_len : q0 + QT;
+  const int kv_end = ctx + t_hi;
+  const int ntiles = (kv_end + kPfKeys - 1) / kPfKeys;
+  const int32_t* bt = tables + (int64_t)s * a.max_blocks;
+
+  half8_t qop[2][NST];
+  int qpos[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int r = 32 * wid + 16 * c + n;
+    const int t = r / g, j = r - t * g;
+    const int row = qs0 + q0 + t;
+    const bool ok = t < QT && q0 + t < q_len && row >= 0 && row < a.total_q;
+    qpos[c] = ok ? ctx + q0 + t : -1;
+    const _Float16* qp = a.q + ((int64_t)(ok ? row : 0) * a.num_q_heads + kh * g + j) * D;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      uint4 w = ok ? *(const uint4*)(qp + 32 * st + 8 * h) : make_uint4(0, 0, 0, 0);
+      qop[c][st] = __builtin_bit_cast(half8_t, w);
+    }
+  }
+
+  // ---- loads of tile t into buffer t % 3: wave w fills rows (w NI + i) RPI ..
+  // of K and of V; lane -> row r0 + lane / CPR, LDS chunk lane % CPR, which
+  // holds the row's chunk (lane % CPR) ^ swizzle.  Positions at or past kv_end
+  // repeat position kv_end - 1 (finite data; masked out of every score).
+  const char* const kbase = a.k + (int64_t)kh * D * 2;
+  const char* const vbase = a.v + (int64_t)kh * D * 2;
+  auto issue = [&](int t, int b) {
+    const int kt = t * kPfKeys;
+#pragma unroll
+    for (int i = 0; i < T::NI; ++i) {
+      const int r0 = (wid * T::NI + i) * T::RPI;
+      const int r = r0 + lane / CPR, pch = lane % CPR;
+      const int pu = uni((kt + r0 < kv_end ? kt + r0 : kv_end - 1));
+      int blk = bt[pu / BS];
+      blk = blk < 0 ? 0 : (blk > a.num_blocks_m1 ? a.num_blocks_m1 : blk);
+      const int pos = kt + r < kv_end ? kt + r : kv_end - 1;
+      const int64_t row_off = (int64_t)blk * a.block_stride + (int64_t)(pos % BS) * a.row_stride;
+      lds_char* kdst = lds0 + b * T::BUF + r0 * RB;
+      lds_char* vdst = kdst + T::TILE;
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + row_off + ((pch ^ T::ksw(r)) << 4)),
+                                       (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + row_off + ((pch ^ T::vsw(r)) << 4)),
+                                       (__attribute__((address_space(3))) void*)vdst, 16, 0, 0);
+    }
+  };
+
+  // ---- per-lane LDS read addresses (buffer 0; buffers differ by an immediate)
+  // K: position kpos(0, n) = 8 (n / 4) + (n % 4), chunk (4 st + h) ^ ksw = (4 st + h) ^ n
+  uint32_t kaddr[NST];
+  {
+    const int key = 8 * (n >> 2) + (n & 3);
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+      kaddr[st] = lds_base + key * RB + (((4 * st + h) ^ T::ksw(key)) << 4);
+  }
+  // V (transpose read): source lane n = 4k + m reads position 8h + k (+4 for the
+  // second half), dims 16 nb + 4m .. +3
+  uint32_t vaddr[NB];
+  {
+    const int k = n >> 2, m = n & 3;
+    const int key = 8 * h + k;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      vaddr[nb] = lds_base + T::TILE + key * RB + (((2 * nb + (m >> 1)) ^ T::vsw(key)) << 4) +
+                  8 * (m & 1);
+  }
+
+  float4_t acc[2][NB];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[c][nb] = {0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {kNegBig, kNegBig}, l_run[2] = {0.f, 0.f};
+  const float sc = a.score_scale;
+
+  auto compute = [&](uint32_t bo, int kt, bool diag) {
+    half8_t kop[2][NST];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      kop[0][st] = lds_b128<0>(kaddr[st] + bo);
+      kop[1][st] = lds_b128<4 * RB>(kaddr[st] + bo);
+    }
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      lgkm_wait<0>(kop[0][st]);
+      lgkm_wait<0>(kop[1][st]);
+    }
+    float4_t sa[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        sa[c][kb] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+          sa[c][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][st], qop[c][st], sa[c][kb], 0, 0, 0);
+      }
+    // V reads go out after the score MFMAs (the K operands are dead by then)
+    // and land while the first group's softmax runs
+    half4_t vh[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      vh[nb][0] = lds_tr16<0>(vaddr[nb] + bo);
+      vh[nb][1] = lds_tr16<4 * RB>(vaddr[nb] + bo);
+    }
+    half8_t vop[NB];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float x[8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * kb + i] = sa[c][kb][i];
+      if (diag) {
+        const int lim = qpos[c] - kt - 8 * h;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = k <= lim ? x[k] : -INFINITY;
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))) * sc;
+      if (__any(tmax > m_run[c] + kLazy)) {
+        tmax = xor_max(tmax, 16);
+        tmax = xor_max(tmax, 32);
+        const float m_new = fmaxf(m_run[c], tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[c] - m_new);
+        l_run[c] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ai = __shfl(alpha, 4 * h + i);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[c][nb][i] *= ai;
+        }
+        m_run[c] = m_new;
+      }
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sc, -m_run[c]));
+      l_run[c] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      const float4_t p0 = {p[0], p[1], p[2], p[3]}, p1 = {p[4], p[5], p[6], p[7]};
+      const half4_t h0 = __builtin_convertvector(p0, half4_t);
+      const half4_t h1 = __builtin_convertvector(p1, half4_t);
+      const half8_t pop = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      if (c == 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          lgkm_wait<0>(vh[nb][0]);
+          lgkm_wait<0>(vh[nb][1]);
+          vop[nb] = {vh[nb][0][0], vh[nb][0][1], vh[nb][0][2], vh[nb][0][3],
+                     vh[nb][1][0], vh[nb][1][1], vh[nb][1][2], vh[nb][1][3]};
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[c][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, vop[nb], acc[c][nb], 0, 0, 0);
+    }
+  };
+
+  // tile t (buffer b = t % 3): wait for its loads (tile t + 1 may still be in
+  // flight), barrier (every wave's loads of tile t have landed and every wave
+  // is done with tile t - 1, whose buffer tile t + 2 reuses), issue tile t + 2,
+  // compute tile t.
+  issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
+  int b = 0;
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) vm_wait<T::DPT>();
+    else vm_wait<0>();
+    lgkm_wait_all_regs<0>();
+    __builtin_amdgcn_s_barrier();
+    if (t + 2 < ntiles) issue(t + 2, b == 0 ? 2 : b - 1);
+    const int kt = t * kPfKeys;
+    compute((uint32_t)(b * T::BUF), kt, kt + kPfKeys - 1 > ctx + q0);
+    b = b == 2 ? 0 : b + 1;
+  }
+
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    float lt = xor_sum(l_run[c], 16);
+    lt = xor_sum(lt, 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float li = __shfl(lt, 4 * h + i);
+      const int r = 32 * wid + 16 * c + 4 * h + i;
+      const int t = r / g, j = r - t * g;
+      const int row = qs0 + q0 + t;
+      if (!(t < QT && q0 + t < q_len && row >= 0 && row < a.total_q)) continue;
+      const float f = a.v_scale / li;
+      _Float16* op = a.out + ((int64_t)row * a.num_q_heads + kh * g + j) * D + n;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) op[16 * nb] = (_Float16)(acc[c][nb][i] * f);
+    }
+  }
+}
+
 template <int D, int BS>
 hipError_t launch_pf_bs(const PrefillArgs& a, int kv, hipStream_t stream) {
   const dim3 grid((uint32_t)a.num_seqs * (uint32_t)a.num_kv_heads * (uint32_t)a.num_qt);
   const dim3 block(kPfWaves * 64);
   switch (kv) {
-    case 0: hipLaunchKernelGGL((prefill_kernel<D, BS, 0>), grid, block, 0, stream, a); break;
+    case 0:
+      hipLaunchKernelGGL((prefill_f16_kernel<D, BS>), grid, block, 0, stream, a, a.block_tables);
+      break;
     case 1: hipLaunchKernelGGL((prefill_kernel<D, BS, 1>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((prefill_kernel<D, BS, 2>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
