@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged-attn decode achieved HBM GB/s (% of MI355X peak) + KV tokens/s"
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def kernel_source_hash() -> str:
@@ -112,15 +112,21 @@ def traffic_entry(config: str):
 
 
 DECODE_KERNELS = ("decode_flat_kernel", "flat_merge_kernel", "decode_kernel", "lse_reduce_kernel")
+PREFILL_KERNELS = ("prefill_f16_kernel", "prefill_kernel")
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, calib_gib: float, config: str,
                     commands: list) -> dict:
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
-    WRITE_SIZE, both with --calib-copy-gib) into HBM bytes per pa_decode call.
-    Each counter is scaled by what it reads for the plain device copies of
-    calib_gib GiB that the script runs last (torch's copy kernel)."""
+    WRITE_SIZE, both with --calib-copy-gib) into HBM bytes per pa_decode (or,
+    for a prefill workload, pa_prefill) call.  Each counter is scaled by what it
+    reads for the plain device copies of calib_gib GiB that the script runs
+    last (torch's copy kernel)."""
     import csv
+    from paged_kv_cache_72_amd import workloads as W
+    kernels = PREFILL_KERNELS if config in W.PREFILL_CONFIGS else DECODE_KERNELS
+    # the kernels that run once per call (the rest, merges and reduces, run after them)
+    primary = ("prefill_f16_kernel", "prefill_kernel", "decode_flat_kernel", "decode_kernel")
 
     def load(path):
         rows = list(csv.DictReader(open(path)))
@@ -133,12 +139,11 @@ def ingest_counters(fetch_csv: str, write_csv: str, calib_gib: float, config: st
         copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]][-3:]
         kib_copy = sum(float(r["Counter_Value"]) for r in copies) / len(copies)
         factor = calib_gib * (1 << 30) / (kib_copy * 1024)
-        dec = [r for r in rows if any(k in r["Kernel_Name"] for k in DECODE_KERNELS)]
-        calls = sum(1 for r in dec if ("decode_flat_kernel" in r["Kernel_Name"] or
-                                       "decode_kernel" in r["Kernel_Name"]))
+        dec = [r for r in rows if any(k in r["Kernel_Name"] for k in kernels)]
+        calls = sum(1 for r in dec if any(p in r["Kernel_Name"] for p in primary))
         per_kernel = {}
         for r in dec:
-            name = next(k for k in DECODE_KERNELS if k in r["Kernel_Name"])
+            name = next(k for k in kernels if k in r["Kernel_Name"])
             per_kernel.setdefault(name, []).append(float(r["Counter_Value"]))
         kib_per_call = sum(sum(v) for v in per_kernel.values()) / calls
         out[key] = {"counter": rows[0]["Counter_Name"], "kib_per_call_raw": round(kib_per_call, 2),
@@ -265,6 +270,13 @@ def run_prefill(args, w) -> int:
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     pf_avg = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    if args.calib_copy_gib > 0:
+        n = int(args.calib_copy_gib * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     flops = prefill_flops(w)
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (pf_avg * 1e-3) / 1e12
@@ -315,7 +327,7 @@ def main() -> int:
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: write the HBM traffic of --config's pa_decode call into "
-                         "profiles/pa_decode_traffic.json from two rocprofv3 --pmc runs")
+                         "profiles/hbm_traffic.json from two rocprofv3 --pmc runs")
     ap.add_argument("--command", action="append", default=[],
                     help="with --ingest-counters: the profiler commands, recorded verbatim")
     args = ap.parse_args()

@@ -46,6 +46,13 @@
 namespace pa {
 namespace {
 
+#ifndef PA_PF_OCC
+#define PA_PF_OCC 2           // fp16 prefill: workgroups per CU the registers are sized for
+#endif
+#ifndef PA_PF_NBUF
+#define PA_PF_NBUF 3          // fp16 prefill: LDS tile buffers (tiles in flight + 1)
+#endif
+
 constexpr int kPfWaves = 4;
 constexpr int kPfRows = 128;       // query rows per workgroup
 constexpr int kPfKeys = 32;        // key positions per tile
@@ -363,9 +370,10 @@ struct PfDma {
   static constexpr int TILE = kPfKeys * RB;
   static constexpr int BUF = 2 * TILE;                    // K tile then V tile
   static constexpr int DPT = 2 * NI;                      // loads per thread per tile
+  static constexpr int NBUF = PA_PF_NBUF;
   static constexpr int NST = D / 32;
   static constexpr int NB = D / 16;
-  static_assert(NI >= 1 && 3 * BUF <= 65536, "tile shape");
+  static_assert(NI >= 1 && NBUF >= 2 && NBUF <= 4 && NBUF * BUF <= 65536, "tile shape");
   // K rows: chunk swizzle that gives the 16 rows one score MFMA reads
   // (positions 8 (n / 4) + 4 kb + n % 4, n = 0..15) distinct chunks.
   __device__ static __forceinline__ int ksw(int key) {
@@ -409,11 +417,11 @@ __device__ __forceinline__ void vm_wait() {
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_f16_kernel(
+__global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
     PrefillArgs a, const int32_t* __restrict__ tables) {
   typedef PfDma<D> T;
   constexpr int CPR = T::CPR, RB = T::RB, NST = T::NST, NB = T::NB;
-  __shared__ __attribute__((aligned(1024))) char smem[3 * T::BUF];
+  __shared__ __attribute__((aligned(1024))) char smem[T::NBUF * T::BUF];
   lds_char* const lds0 = (lds_char*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds0;
 
@@ -599,18 +607,23 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_f16_kernel(
   // flight), barrier (every wave's loads of tile t have landed and every wave
   // is done with tile t - 1, whose buffer tile t + 2 reuses), issue tile t + 2,
   // compute tile t.
-  issue(0, 0);
-  if (ntiles > 1) issue(1, 1);
+  constexpr int NB_ = T::NBUF;
+#pragma unroll
+  for (int t = 0; t < NB_ - 1; ++t)
+    if (t < ntiles) issue(t, t);
   int b = 0;
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) vm_wait<T::DPT>();
+    // tiles t + 1 .. t + NBUF - 2 may stay in flight
+    const int later = ntiles - 1 - t;
+    if (NB_ >= 4 && later >= 2) vm_wait<(NB_ >= 4 ? 2 : 1) * T::DPT>();
+    else if (NB_ >= 3 && later >= 1) vm_wait<T::DPT>();
     else vm_wait<0>();
     lgkm_wait_all_regs<0>();
     __builtin_amdgcn_s_barrier();
-    if (t + 2 < ntiles) issue(t + 2, b == 0 ? 2 : b - 1);
+    if (t + NB_ - 1 < ntiles) issue(t + NB_ - 1, b == 0 ? NB_ - 1 : b - 1);
     const int kt = t * kPfKeys;
     compute((uint32_t)(b * T::BUF), kt, kt + kPfKeys - 1 > ctx + q0);
-    b = b == 2 ? 0 : b + 1;
+    b = b == NB_ - 1 ? 0 : b + 1;
   }
 
 #pragma unroll

@@ -185,3 +185,38 @@ def test_plan_falls_back_past_flat_limit(so):
     assert so.pa_decode_plan(C.byref(p), 9000, 32, 300, 0) == L.PLAN_SINGLE
     assert so.pa_decode_plan(C.byref(p), 9000, 32, 8192, 0) == 512
     assert so.pa_decode_plan(C.byref(p), 9000, 32, 300, 1) == L.PA_ERR_UNSUPPORTED
+
+
+def _prefill(so, pool, T=10, S=2, Hq=32, maxq=8, **kw):
+    args = dict(out=FAKE, q=FAKE, qs=FAKE, bt=FAKE, maxb=64, lens=FAKE, scale=0.088)
+    args.update(kw)
+    return so.pa_prefill(C.byref(pool) if pool is not None else None, args["out"], args["q"], T,
+                         args["qs"], S, Hq, args["bt"], args["maxb"], args["lens"], maxq,
+                         C.c_float(args["scale"]), None)
+
+
+def test_prefill_validation(so):
+    assert _prefill(so, None) == L.PA_ERR_INVALID_ARG
+    assert _prefill(so, _pool(head_dim=96)) == L.PA_ERR_UNSUPPORTED
+    assert _prefill(so, _pool(), Hq=30) == L.PA_ERR_INVALID_ARG          # 30 % 8 != 0
+    assert _prefill(so, _pool(num_kv_heads=1), Hq=32) == L.PA_ERR_UNSUPPORTED
+    assert _prefill(so, _pool(), S=-1) == L.PA_ERR_INVALID_ARG
+    assert _prefill(so, _pool(), T=-1) == L.PA_ERR_INVALID_ARG
+    assert _prefill(so, _pool(), maxq=-1) == L.PA_ERR_INVALID_ARG
+    for bad in (0.0, -0.1, float("inf"), float("nan")):
+        assert _prefill(so, _pool(), scale=bad) == L.PA_ERR_INVALID_ARG
+    assert "positive" in L.pa_last_error() or "finite" in L.pa_last_error()
+    assert _prefill(so, _pool(), q=None) == L.PA_ERR_INVALID_ARG
+    assert _prefill(so, _pool(), qs=None) == L.PA_ERR_INVALID_ARG
+    assert _prefill(so, _pool(), out=FAKE + 8) == L.PA_ERR_ALIGNMENT
+    assert _prefill(so, _pool(), maxb=0) == L.PA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(S=0), dict(T=0), dict(maxq=0)])
+def test_prefill_empty_is_a_noop_even_with_null_buffers(so, kw):
+    assert _prefill(so, _pool(), out=None, q=None, qs=None, bt=None, lens=None, **kw) == L.PA_OK
+
+
+def test_prefill_grid_size_is_checked(so):
+    # 2^20 sequences x 8 KV heads x cdiv(2^20, 32) query tiles overflows the grid
+    assert _prefill(so, _pool(), S=1 << 20, maxq=1 << 20) == L.PA_ERR_INVALID_ARG
