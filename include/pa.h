@@ -58,7 +58,8 @@ typedef enum {
   PA_ERR_UNSUPPORTED = -2, /* head_dim, block_size, dtype or GQA ratio not built  */
   PA_ERR_ALIGNMENT = -3,   /* a pointer or stride is not 16-byte aligned          */
   PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required          */
-  PA_ERR_HIP = -5          /* the HIP runtime rejected a launch                   */
+  PA_ERR_HIP = -5,         /* the HIP runtime rejected a launch                   */
+  PA_ERR_NO_BLOCKS = -6    /* host block pool (pa_blocks.h): not enough free blocks */
 } pa_status;
 
 typedef enum {

@@ -25,7 +25,9 @@ HIPCC_FLAGS = [
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    """Every HIP source plus the host-only C++ of the library (the block pool)."""
+    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")) +
+                  glob.glob(os.path.join(HERE, "csrc", "*.cpp")))
 
 
 def build(verbose: bool = False, extra=()) -> str:

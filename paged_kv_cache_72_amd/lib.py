@@ -17,13 +17,21 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_ALIGNMENT, PA_ERR_WORKSPACE, PA_ERR_HIP = \
     0, -1, -2, -3, -4, -5
+PA_ERR_NO_BLOCKS = -6
 PA_KV_F16, PA_KV_FP8_E4M3FN, PA_KV_FP8_E5M2 = 0, 1, 2
 PLAN_SINGLE, PLAN_FLAT = 0, 1          # pa_decode_plan codes; >= 16 is a split partition size
 PA_POOL_SHARED_BLOCKS = 1
 _DTYPES = {"f16": PA_KV_F16, "fp8_e4m3fn": PA_KV_FP8_E4M3FN, "fp8_e5m2": PA_KV_FP8_E5M2}
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
-           "pa_decode_workspace_size", "pa_decode", "pa_prefill", "pa_last_error")
+           "pa_decode_workspace_size", "pa_decode", "pa_prefill", "pa_last_error",
+           # host block pool (include/pa_blocks.h)
+           "pa_bp_create", "pa_bp_destroy", "pa_bp_last_error", "pa_bp_num_free",
+           "pa_bp_ref_count", "pa_bp_block_hash", "pa_bp_free_queue", "pa_bp_get_new_blocks",
+           "pa_bp_free_blocks", "pa_bp_touch", "pa_bp_cache_block", "pa_bp_lookup",
+           "pa_hash_block_tokens", "pa_bp_allocate_request", "pa_bp_cache_request",
+           "pa_bp_append_slots", "pa_bp_free_request", "pa_bp_request_blocks",
+           "pa_bp_fork_request", "pa_bp_prepare_write")
 
 
 class PaError(RuntimeError):
@@ -69,6 +77,7 @@ def load() -> C.CDLL:
         L.pa_prefill.argtypes = [PP, P, P, I32, P, I32, I32, P, I32, P, I32, C.c_float, P]
         L.pa_last_error.restype = C.c_char_p
         L.pa_last_error.argtypes = []
+        _bind_block_pool(L)
         _lib = L
     return _lib
 
@@ -226,3 +235,163 @@ def pa_prefill(pool: KVPool, out: torch.Tensor, q: torch.Tensor, q_start: torch.
         _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
         _dev(seq_lens, torch.int32, "seq_lens"), int(max_q_len), C.c_float(scale),
         _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# host block pool with prefix caching (include/pa_blocks.h)
+
+
+class pa_block_hash(C.Structure):
+    _fields_ = [("bytes", C.c_uint8 * 32)]
+
+
+def _bind_block_pool(L) -> None:
+    P, I32, I64 = C.c_void_p, C.c_int32, C.c_int64
+    H = C.POINTER(pa_block_hash)
+    IP, LP = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
+    sig = {
+        "pa_bp_create": (P, [I32, I32]),
+        "pa_bp_destroy": (None, [P]),
+        "pa_bp_last_error": (C.c_char_p, []),
+        "pa_bp_num_free": (I32, [P]),
+        "pa_bp_ref_count": (I32, [P, I32]),
+        "pa_bp_block_hash": (C.c_int, [P, I32, H]),
+        "pa_bp_free_queue": (I32, [P, IP, I32]),
+        "pa_bp_get_new_blocks": (C.c_int, [P, I32, IP]),
+        "pa_bp_free_blocks": (C.c_int, [P, IP, I32]),
+        "pa_bp_touch": (C.c_int, [P, IP, I32]),
+        "pa_bp_cache_block": (C.c_int, [P, I32, H]),
+        "pa_bp_lookup": (I32, [P, H, I32, IP]),
+        "pa_hash_block_tokens": (None, [H, IP, I32, P, I32, H]),
+        "pa_bp_allocate_request": (C.c_int, [P, I64, IP, I32, P, I32, IP]),
+        "pa_bp_cache_request": (C.c_int, [P, I64, IP, I32, P, I32]),
+        "pa_bp_append_slots": (C.c_int, [P, I64, I32]),
+        "pa_bp_free_request": (C.c_int, [P, I64]),
+        "pa_bp_request_blocks": (I32, [P, I64, IP, I32]),
+        "pa_bp_fork_request": (C.c_int, [P, I64, I64]),
+        "pa_bp_prepare_write": (C.c_int, [P, I64, I32, LP]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+
+
+def _ints(xs) -> C.Array:
+    xs = [int(x) for x in xs]
+    return (C.c_int32 * max(1, len(xs)))(*xs)
+
+
+def _hash_arr(hs) -> C.Array:
+    arr = (pa_block_hash * max(1, len(hs)))()
+    for i, h in enumerate(hs):
+        C.memmove(arr[i].bytes, bytes(h), 32)
+    return arr
+
+
+def hash_block_tokens(parent: Optional[bytes], tokens, extra: bytes = b"") -> bytes:
+    """SHA-256(parent or 32 zero bytes | token ids as int32 LE | extra)."""
+    L = load()
+    out = pa_block_hash()
+    par = None
+    if parent is not None:
+        par = pa_block_hash()
+        C.memmove(par.bytes, bytes(parent), 32)
+    toks = _ints(tokens)
+    ex = C.create_string_buffer(bytes(extra), max(1, len(extra)))
+    L.pa_hash_block_tokens(C.byref(par) if par is not None else None, toks, len(tokens),
+                           ex if extra else None, len(extra), C.byref(out))
+    return bytes(out.bytes)
+
+
+class BlockPool:
+    """The native host block pool (reference counts, LRU free queue shared
+    with the prefix cache, chained block hashes, fork and copy-on-write)."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._L = load()
+        self._p = self._L.pa_bp_create(int(num_blocks), int(block_size))
+        if not self._p:
+            raise PaError(PA_ERR_INVALID_ARG, self._L.pa_bp_last_error().decode())
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def __del__(self):
+        if getattr(self, "_p", None):
+            self._L.pa_bp_destroy(self._p)
+            self._p = None
+
+    def _ok(self, st: int) -> int:
+        if st < 0:
+            raise PaError(st, self._L.pa_bp_last_error().decode())
+        return st
+
+    def num_free(self) -> int:
+        return self._L.pa_bp_num_free(self._p)
+
+    def ref_count(self, b: int) -> int:
+        return self._ok(self._L.pa_bp_ref_count(self._p, int(b)))
+
+    def block_hash(self, b: int) -> Optional[bytes]:
+        h = pa_block_hash()
+        return bytes(h.bytes) if self._ok(self._L.pa_bp_block_hash(self._p, int(b), C.byref(h))) else None
+
+    def free_queue(self) -> list:
+        n = self._ok(self._L.pa_bp_free_queue(self._p, None, 0))
+        out = (C.c_int32 * max(1, n))()
+        self._ok(self._L.pa_bp_free_queue(self._p, out, n))
+        return list(out[:n])
+
+    def get_new_blocks(self, n: int) -> list:
+        out = (C.c_int32 * max(1, n))()
+        self._ok(self._L.pa_bp_get_new_blocks(self._p, int(n), out))
+        return list(out[:n])
+
+    def free_blocks(self, ids) -> None:
+        self._ok(self._L.pa_bp_free_blocks(self._p, _ints(ids), len(ids)))
+
+    def touch(self, ids) -> None:
+        self._ok(self._L.pa_bp_touch(self._p, _ints(ids), len(ids)))
+
+    def cache_block(self, b: int, h: bytes) -> None:
+        hh = pa_block_hash()
+        C.memmove(hh.bytes, bytes(h), 32)
+        self._ok(self._L.pa_bp_cache_block(self._p, int(b), C.byref(hh)))
+
+    def lookup(self, hashes) -> list:
+        out = (C.c_int32 * max(1, len(hashes)))()
+        n = self._ok(self._L.pa_bp_lookup(self._p, _hash_arr(hashes), len(hashes), out))
+        return list(out[:n])
+
+    def allocate_request(self, rid: int, tokens, extra: bytes = b"") -> int:
+        cached = C.c_int32(0)
+        ex = C.create_string_buffer(bytes(extra), max(1, len(extra)))
+        self._ok(self._L.pa_bp_allocate_request(self._p, int(rid), _ints(tokens), len(tokens),
+                                                ex if extra else None, len(extra),
+                                                C.byref(cached)))
+        return cached.value
+
+    def cache_request(self, rid: int, tokens, extra: bytes = b"") -> None:
+        ex = C.create_string_buffer(bytes(extra), max(1, len(extra)))
+        self._ok(self._L.pa_bp_cache_request(self._p, int(rid), _ints(tokens), len(tokens),
+                                             ex if extra else None, len(extra)))
+
+    def append_slots(self, rid: int, num_tokens_after: int) -> None:
+        self._ok(self._L.pa_bp_append_slots(self._p, int(rid), int(num_tokens_after)))
+
+    def free_request(self, rid: int) -> None:
+        self._ok(self._L.pa_bp_free_request(self._p, int(rid)))
+
+    def request_blocks(self, rid: int) -> list:
+        n = self._ok(self._L.pa_bp_request_blocks(self._p, int(rid), None, 0))
+        out = (C.c_int32 * max(1, n))()
+        self._L.pa_bp_request_blocks(self._p, int(rid), out, n)
+        return list(out[:n])
+
+    def fork_request(self, parent: int, child: int) -> None:
+        self._ok(self._L.pa_bp_fork_request(self._p, int(parent), int(child)))
+
+    def prepare_write(self, rid: int, position: int) -> Optional[tuple]:
+        """(src, dst) for pa_copy_blocks when the block is shared, else None."""
+        pair = (C.c_int64 * 2)()
+        r = self._ok(self._L.pa_bp_prepare_write(self._p, int(rid), int(position), pair))
+        return (pair[0], pair[1]) if r == 1 else None

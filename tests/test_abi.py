@@ -24,7 +24,8 @@ def so():
 
 
 def _declared_functions():
-    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = "".join(open(os.path.join(ROOT, "include", f)).read()
+                   for f in sorted(os.listdir(os.path.join(ROOT, "include"))) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
 
