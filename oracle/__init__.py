@@ -29,6 +29,7 @@ class OrcPool(C.Structure):
         ("block_size", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
         ("elem_bytes", C.c_int32), ("fp8_format", C.c_int32),
         ("k_scale", C.c_double), ("v_scale", C.c_double),
+        ("k_head_scales", C.c_void_p), ("v_head_scales", C.c_void_p),
     ]
 
 
@@ -131,7 +132,7 @@ class HostPool:
 
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
                  kv_dtype: str = "f16", k_scale: float = 1.0, v_scale: float = 1.0,
-                 fill_bits: int = 0):
+                 fill_bits: int = 0, k_head_scales=None, v_head_scales=None):
         self.elem_bytes = 1 if kv_dtype in ("fp8_e4m3fn", "fp8_e5m2") else 2
         fp8_format = 1 if kv_dtype == "fp8_e5m2" else 0
         dt = np.uint8 if self.elem_bytes == 1 else np.uint16
@@ -143,14 +144,22 @@ class HostPool:
             self.k = np.zeros(shape, dtype=dt)
             self.v = np.zeros(shape, dtype=dt)
         self.kv_dtype = kv_dtype
+        # per-KV-head scales (fp8 only): the float32 values the device uses, in fp64
+        self.k_head = self.v_head = None
+        if k_head_scales is not None:
+            self.k_head = np.ascontiguousarray(np.asarray(k_head_scales, np.float32), np.float64)
+            self.v_head = np.ascontiguousarray(np.asarray(v_head_scales, np.float32), np.float64)
+            assert self.k_head.shape == (num_kv_heads,) == self.v_head.shape
         self.desc = OrcPool(self.k.ctypes.data, self.v.ctypes.data, num_blocks, 0, block_size,
                             num_kv_heads, head_dim, self.elem_bytes, fp8_format,
-                            float(k_scale), float(v_scale))
+                            float(k_scale), float(v_scale),
+                            None if self.k_head is None else self.k_head.ctypes.data,
+                            None if self.v_head is None else self.v_head.ctypes.data)
 
     @classmethod
     def for_workload(cls, w, fill_bits: int = 0) -> "HostPool":
         return cls(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype,
-                   w.k_scale, w.v_scale, fill_bits)
+                   w.k_scale, w.v_scale, fill_bits, w.k_head_scales, w.v_head_scales)
 
 
 def scatter(pool: HostPool, k_new: np.ndarray, v_new: np.ndarray, slots: np.ndarray,

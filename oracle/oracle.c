@@ -183,12 +183,19 @@ static double read_elem(const orc_pool* p, const void* base, int64_t byte_off, d
 
 static int nthreads_or_default(int n) { return n > 0 ? n : omp_get_max_threads(); }
 
+/* The dequantisation scale of KV head kh: per head when given, else per tensor. */
+static double k_scale_of(const orc_pool* p, int32_t kh) {
+  return p->k_head_scales ? p->k_head_scales[kh] : p->k_scale;
+}
+static double v_scale_of(const orc_pool* p, int32_t kh) {
+  return p->v_head_scales ? p->v_head_scales[kh] : p->v_scale;
+}
+
 /* ---------------------------------------------------------------- writes */
 
 void orc_scatter(const orc_pool* p, const uint16_t* k_new, const uint16_t* v_new,
                  const int64_t* slots, int64_t T, int nthreads) {
   const int32_t Hkv = p->num_kv_heads, D = p->head_dim;
-  const float ks = (float)p->k_scale, vs = (float)p->v_scale;
 #pragma omp parallel for schedule(static) num_threads(nthreads_or_default(nthreads))
   for (int64_t i = 0; i < T; ++i) {
     int64_t slot = slots[i];
@@ -196,6 +203,7 @@ void orc_scatter(const orc_pool* p, const uint16_t* k_new, const uint16_t* v_new
     int64_t blk = slot / p->block_size;
     int32_t off = (int32_t)(slot % p->block_size);
     for (int32_t kh = 0; kh < Hkv; ++kh) {
+      const float ks = (float)k_scale_of(p, kh), vs = (float)v_scale_of(p, kh);
       for (int32_t d = 0; d < D; ++d) {
         int64_t src = ((int64_t)i * Hkv + kh) * D + d;
         int64_t dst = elem_offset(p, blk, off, kh, d);
@@ -238,8 +246,8 @@ void orc_gather_head(const orc_pool* p, const int32_t* bt_row, int32_t len, int3
     int32_t off = t % p->block_size;
     for (int32_t d = 0; d < D; ++d) {
       int64_t o = elem_offset(p, blk, off, kh, d);
-      Kc[(int64_t)t * D + d] = read_elem(p, p->k, o, p->k_scale);
-      Vc[(int64_t)t * D + d] = read_elem(p, p->v, o, p->v_scale);
+      Kc[(int64_t)t * D + d] = read_elem(p, p->k, o, k_scale_of(p, kh));
+      Vc[(int64_t)t * D + d] = read_elem(p, p->v, o, v_scale_of(p, kh));
     }
   }
 }

@@ -23,6 +23,8 @@
  *     ("vLLM intro part 2", section 3.2 slot_mapping); fp8 pools store
  *     e4m3fn(x / scale) or e5m2(x / scale) (quantise on write, "KV Cache memory
  *     core", section 4.4; the two fp8 formats of "vLLM intro part 2", section 7).
+ *     The scale is one per tensor, or one per KV head (the finer granularity
+ *     the quantisation passage of "KV Cache memory core", section 4.4, names).
  *   - copy_blocks copies a whole block for copy-on-write ("GPU memory & KV
  *     cache", COW incident code; "vLLM intro part 2", section 5).
  *   - Prefill writes a prompt's K/V in bulk and then attends over the paged
@@ -54,6 +56,10 @@ typedef struct {
   int32_t fp8_format;     /* for 1-byte elements: ORC_FP8_E4M3FN or _E5M2     */
   double  k_scale;        /* fp8 dequantisation scales (1.0 for binary16)     */
   double  v_scale;
+  /* Optional finer grain: one scale per KV head ([num_kv_heads] each); when
+   * non-NULL they replace k_scale / v_scale for fp8 pools.                    */
+  const double* k_head_scales;
+  const double* v_head_scales;
 } orc_pool;
 
 #define ORC_FP8_E4M3FN 0

@@ -89,6 +89,9 @@ class Workload:
     # seq_lens[s] positions); q is then [sum(q_lens), Hq, D], sequence after
     # sequence.  None for decode (one query token per sequence).
     q_lens: Optional[np.ndarray] = None
+    # fp8 pools with one scale per KV head (float32 [Hkv]); None: per-tensor scales
+    k_head_scales: Optional[np.ndarray] = None
+    v_head_scales: Optional[np.ndarray] = None
 
     @property
     def is_prefill(self) -> bool:
@@ -171,6 +174,29 @@ def _normal_f16(seed_seq: np.random.SeedSequence, shape, parallel_axis_len: int)
     return out
 
 
+def _amax_per_head_f32(a: np.ndarray) -> np.ndarray:
+    """max |a| over tokens and dims for each KV head of [T, Hkv, D], as fp32."""
+    n = a.shape[0]
+    out = np.zeros(a.shape[1], np.float32)
+    for lo in range(0, n, _CHUNK_TOKENS):
+        part = np.abs(a[lo:lo + _CHUNK_TOKENS]).max(axis=(0, 2)).astype(np.float32)
+        out = np.maximum(out, part)
+    return out
+
+
+def fp8_scales(kv_dtype: str, tok_k: np.ndarray, tok_v: np.ndarray, grain: str = "tensor"):
+    """(k_scale, v_scale, k_head_scales, v_head_scales): amax / fp8 max, per
+    tensor, or per KV head when grain == "head" (then the tensor scales are 1)."""
+    if kv_dtype not in FP8_DTYPES:
+        return 1.0, 1.0, None, None
+    mx = fp8_max(kv_dtype)
+    if grain == "head":
+        kh = (_amax_per_head_f32(tok_k) / mx).astype(np.float32)
+        vh = (_amax_per_head_f32(tok_v) / mx).astype(np.float32)
+        return 1.0, 1.0, kh, vh
+    return (float(_amax_f32(tok_k) / mx), float(_amax_f32(tok_v) / mx), None, None)
+
+
 def _amax_f32(a: np.ndarray) -> np.float32:
     """max |a| over an fp16 array, as fp32 (exact: fp16 values are fp32 values)."""
     n = a.shape[0]
@@ -205,16 +231,21 @@ def _slots_for(table_row: np.ndarray, ntok: int, bs: int, start: int = 0) -> np.
 
 
 def _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, lens, tables, pad_block,
-            tok_slot, new_idx, ss, partition_size=0, q_rows=None, **extra) -> Workload:
+            tok_slot, new_idx, ss, partition_size=0, q_rows=None, scale_grain="tensor",
+            **extra) -> Workload:
     T = int(tok_slot.size)
     nq = S if q_rows is None else int(q_rows)
     q = _normal_f16(ss[2], (nq, Hq, D), nq)
     tok_k = _normal_f16(ss[3], (T, Hkv, D), T)
     tok_v = _normal_f16(ss[4], (T, Hkv, D), T)
-    k_scale = v_scale = 1.0
-    if kv_dtype in FP8_DTYPES:
-        k_scale = float(_amax_f32(tok_k) / fp8_max(kv_dtype))
-        v_scale = float(_amax_f32(tok_v) / fp8_max(kv_dtype))
+    if scale_grain == "head":
+        # heads of different magnitude, so that one scale per tensor would not fit all
+        mult = (2.0 ** np.arange(Hkv) % 7 + 0.25).astype(np.float32)[None, :, None]
+        tok_k = (tok_k.astype(np.float32) * mult).astype(np.float16)
+        tok_v = (tok_v.astype(np.float32) * mult[:, ::-1]).astype(np.float16)
+    k_scale, v_scale, k_head, v_head = fp8_scales(kv_dtype, tok_k, tok_v, scale_grain)
+    extra.setdefault("k_head_scales", k_head)
+    extra.setdefault("v_head_scales", v_head)
     used = np.unique(tok_slot // bs).astype(np.int32)
     return Workload(name=name, seed=seed, num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv,
                     head_dim=D, block_size=bs, num_blocks=num_blocks, kv_dtype=kv_dtype,
@@ -227,7 +258,7 @@ def _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, lens, tables, p
 
 
 def _independent(name, seed, lens, Hq, Hkv, D, bs, num_blocks, kv_dtype="f16",
-                 partition_size=0) -> Workload:
+                 partition_size=0, scale_grain="tensor") -> Workload:
     """Sequences with private blocks; the last token of each is this step's write."""
     ss = np.random.SeedSequence(seed).spawn(6)
     S = len(lens)
@@ -249,12 +280,13 @@ def _independent(name, seed, lens, Hq, Hkv, D, bs, num_blocks, kv_dtype="f16",
     tok_slot = np.concatenate(slots) if slots else np.zeros(0, np.int64)
     return _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, np.asarray(lens),
                    tables, pad_block, tok_slot, np.asarray(new_idx, np.int64), ss,
-                   partition_size=partition_size, own_from=np.zeros(S, np.int64),
+                   partition_size=partition_size, scale_grain=scale_grain,
+                   own_from=np.zeros(S, np.int64),
                    own_start=own_start, shared_start=np.full(S, -1, np.int64))
 
 
 def _prefill_independent(name, seed, ctx_lens, q_lens, Hq, Hkv, D, bs, num_blocks,
-                         kv_dtype="f16") -> Workload:
+                         kv_dtype="f16", scale_grain="tensor") -> Workload:
     """Sequences with private blocks: ctx_lens[s] cached tokens followed by
     q_lens[s] new ones, which are this step's writes and queries."""
     ss = np.random.SeedSequence(seed).spawn(6)
@@ -279,7 +311,8 @@ def _prefill_independent(name, seed, ctx_lens, q_lens, Hq, Hkv, D, bs, num_block
     tok_slot = np.concatenate(slots) if slots else np.zeros(0, np.int64)
     return _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, lens, tables, pad_block,
                    tok_slot, np.concatenate(new_idx), ss, q_rows=int(ql.sum()),
-                   q_lens=ql.astype(np.int32), own_from=np.zeros(S, np.int64),
+                   q_lens=ql.astype(np.int32), scale_grain=scale_grain,
+                   own_from=np.zeros(S, np.int64),
                    own_start=own_start, shared_start=np.full(S, -1, np.int64))
 
 
@@ -461,13 +494,14 @@ PREFILL_CONFIGS = {
 
 
 def custom_prefill(name: str, seed: int, ctx_lens, q_lens, Hq: int, Hkv: int, D: int, bs: int,
-                   num_blocks: Optional[int] = None, kv_dtype: str = "f16") -> Workload:
+                   num_blocks: Optional[int] = None, kv_dtype: str = "f16",
+                   scale_grain: str = "tensor") -> Workload:
     """Independent prefill sequences (cached lengths + new-token counts)."""
     need = sum(cdiv(int(c) + int(n), bs) for c, n in zip(ctx_lens, q_lens)) + 1
     if num_blocks is None:
         num_blocks = max(need + 7, 2 * need)
     return _prefill_independent(name, seed, list(ctx_lens), list(q_lens), Hq, Hkv, D, bs,
-                                int(num_blocks), kv_dtype=kv_dtype)
+                                int(num_blocks), kv_dtype=kv_dtype, scale_grain=scale_grain)
 
 
 CONFIGS = {
@@ -482,13 +516,14 @@ CONFIGS = {
 
 
 def custom(name: str, seed: int, lens, Hq: int, Hkv: int, D: int, bs: int,
-           num_blocks: Optional[int] = None, kv_dtype: str = "f16") -> Workload:
+           num_blocks: Optional[int] = None, kv_dtype: str = "f16",
+           scale_grain: str = "tensor") -> Workload:
     """Independent sequences of the given lengths (for edge cases and sweeps)."""
     need = sum(cdiv(int(n), bs) for n in lens) + 1
     if num_blocks is None:
         num_blocks = max(need + 7, 2 * need)
     return _independent(name, seed, list(lens), Hq, Hkv, D, bs, int(num_blocks),
-                        kv_dtype=kv_dtype)
+                        kv_dtype=kv_dtype, scale_grain=scale_grain)
 
 
 # --------------------------------------------------------------------------
@@ -500,7 +535,10 @@ def with_v_offset(w: Workload, c: float = 1.0) -> Workload:
     v = (w.tok_v.astype(np.float32) + np.float32(c)).astype(np.float16)
     out = dataclasses.replace(w, tok_v=v, variant=f"v_offset{c:g}")
     if w.kv_dtype in FP8_DTYPES:
-        out.v_scale = float(_amax_f32(v) / fp8_max(w.kv_dtype))
+        grain = "head" if w.k_head_scales is not None else "tensor"
+        _, out.v_scale, _, out.v_head_scales = fp8_scales(w.kv_dtype, w.tok_k[:1], v, grain)
+        if grain == "tensor":
+            out.v_scale = float(_amax_f32(v) / fp8_max(w.kv_dtype))
     return out
 
 
@@ -535,7 +573,10 @@ def with_needles(w: Workload, alpha: float = 64.0, seed_offset: int = 0) -> Work
             k[idx, kh] = (np.float32(alpha) * qn).astype(np.float16)
     out = dataclasses.replace(w, tok_k=k, variant="needles")
     if w.kv_dtype in FP8_DTYPES:
-        out.k_scale = float(_amax_f32(k) / fp8_max(w.kv_dtype))
+        if w.k_head_scales is not None:
+            out.k_head_scales = (_amax_per_head_f32(k) / fp8_max(w.kv_dtype)).astype(np.float32)
+        else:
+            out.k_scale = float(_amax_f32(k) / fp8_max(w.kv_dtype))
     return out
 
 
