@@ -79,7 +79,8 @@ typedef enum {
  * Supported: head_dim 64 or 128; block_size 8, 16, 32, 64 or 128 (the range
  * the pages give the block size, 16 being the default: "vLLM intro part 2",
  * section 3.3); k_base, v_base 16-byte
- * aligned.  k_scale / v_scale are the per-pool fp8 scales (ignored for f16).
+ * aligned.  k_scale / v_scale are the per-pool fp8 scales (ignored for f16);
+ * k_head_scales / v_head_scales optionally give one scale per KV head.
  * flags: PA_POOL_SHARED_BLOCKS when some blocks are read by several sequences
  * of one pa_decode batch (shared prefixes, forked sequences: "PagedAttention
  * & vLLM", memory sharing); decode then keeps K/V reads cacheable so that the
@@ -101,6 +102,13 @@ typedef struct {
   float v_scale;
   uint32_t flags;              /* PA_POOL_* bits */
   uint32_t reserved;
+  /* Optional finer fp8 scale grain: device arrays of num_kv_heads float32
+   * scales, one per KV head, for K and for V ("KV Cache memory core",
+   * section 4.4 names scale granularity finer than per tensor).  Both NULL
+   * (per-tensor k_scale / v_scale) or both set, fp8 pools only, 4-byte
+   * aligned; when set, k_scale and v_scale are ignored. */
+  const float* k_head_scales;
+  const float* v_head_scales;
 } pa_kv_pool;
 
 /* Write num_tokens new tokens into their slots (the write side of slot_mapping,

@@ -62,6 +62,14 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
   if (p->flags & ~PA_POOL_SHARED_BLOCKS)
     return fail(PA_ERR_INVALID_ARG, "unknown pool flags 0x%x", (unsigned)p->flags);
   if (p->reserved) return fail(PA_ERR_INVALID_ARG, "pool reserved field must be 0");
+  if ((p->k_head_scales == nullptr) != (p->v_head_scales == nullptr))
+    return fail(PA_ERR_INVALID_ARG, "k_head_scales and v_head_scales must be both set or both NULL");
+  if (p->k_head_scales) {
+    if (p->dtype == PA_KV_F16)
+      return fail(PA_ERR_INVALID_ARG, "per-head scales are for fp8 pools only");
+    if (((uintptr_t)p->k_head_scales & 3u) || ((uintptr_t)p->v_head_scales & 3u))
+      return fail(PA_ERR_ALIGNMENT, "per-head scale arrays must be 4-byte aligned");
+  }
   g->k = (char*)p->k_base;
   g->v = (char*)p->v_base;
   g->num_blocks = p->num_blocks;
@@ -75,6 +83,9 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
   g->k_scale = p->dtype == PA_KV_F16 ? 1.f : p->k_scale;
   g->v_scale = p->dtype == PA_KV_F16 ? 1.f : p->v_scale;
   g->flags = p->flags;
+  g->k_hs = p->k_head_scales;
+  g->v_hs = p->v_head_scales;
+  if (g->k_hs) g->k_scale = g->v_scale = 1.f;
   return PA_OK;
 }
 
@@ -283,6 +294,8 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
   a.seq_lens = seq_lens;
   a.score_scale = (float)((double)scale * 1.4426950408889634 * (double)g.k_scale);
   a.v_scale = g.v_scale;
+  a.k_hs = g.k_hs;
+  a.v_hs = g.v_hs;
   pa::FlatArgs f{};
   if (pl.mode == pa::kModeSplit) {
     a.part_tokens = pl.part;
@@ -357,6 +370,8 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
   a.num_qt = (int32_t)num_qt;
   a.score_scale = (float)((double)scale * 1.4426950408889634 * (double)g.k_scale);
   a.v_scale = g.v_scale;
+  a.k_hs = g.k_hs;
+  a.v_hs = g.v_hs;
   if (hipError_t e = pa::launch_prefill(a, g.head_dim, g.block_size,
                                         g.elem_bytes == 2 ? 0 : (g.fp8_e5m2 ? 2 : 1), stream))
     return fail(PA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

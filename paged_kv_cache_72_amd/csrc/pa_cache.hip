@@ -88,7 +88,9 @@ __global__ __launch_bounds__(256) void rc_scatter_fp8(PoolGeom g, const uint4* _
   for (int t = threadIdx.x; t < 2 * n16; t += blockDim.x) {
     const bool is_v = t >= n16;
     const int c = is_v ? t - n16 : t;
-    const float scale = is_v ? g.v_scale : g.k_scale;
+    const int head = c / (g.head_dim / 8);        // chunk c holds elements 8c .. 8c + 7
+    const float scale = is_v ? (g.v_hs ? g.v_hs[head] : g.v_scale)
+                             : (g.k_hs ? g.k_hs[head] : g.k_scale);
     const uint4 x = ((is_v ? v_new : k_new) + i * n16)[c];
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
     uint32_t packed[2] = {0u, 0u};

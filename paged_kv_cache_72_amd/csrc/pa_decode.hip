@@ -442,6 +442,8 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
   __shared__ __attribute__((aligned(16))) char kstage[NW][En::KST];
   En en;
   en.init(a, lane, (lds_char*)kstage[wid]);
+  if (a.k_hs) en.sc *= a.k_hs[kh];
+  const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
   en.load_q(a.q + ((int64_t)s * a.num_q_heads + (int64_t)kh * g) * D);
   en.reset();
   const PairRef pr{tables + (int64_t)s * a.max_blocks, (len + BS - 1) / BS, len, head_off};
@@ -505,7 +507,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
       L += f * sm_l[w][h];
       O += f * sm_o[w][h][d];
     }
-    const float o = L > 0.f ? (O / L) * a.v_scale : 0.f;
+    const float o = L > 0.f ? (O / L) * v_scale : 0.f;
     const int64_t row = (int64_t)s * a.num_q_heads + hq0 + h;
     if constexpr (SPLIT) {
       const int64_t prow = row * a.num_parts + part;
@@ -692,6 +694,8 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   __shared__ __attribute__((aligned(16))) char kstage[NW][En::KST];
   En en;
   en.init(a, lane, (lds_char*)kstage[wid]);
+  if (a.k_hs) en.sc *= a.k_hs[kh];
+  const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
   const int64_t head_off = (int64_t)kh * D * En::E;
   auto ids_of = [&](Cur c) -> Ids {
     const int len = uni(sm_len[c.s]);
@@ -721,9 +725,9 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
     const float lt = en.l_total();
     if (seg_from_start && seq_end) {
       en.store_out(outs + ((int64_t)cur[0].s * a.num_q_heads + (int64_t)kh * g) * D, lt,
-                   a.v_scale);
+                   v_scale);
     } else {                                   // slot 0: the range's first segment
-      en.store_partial(rec_base + (seg_start == g0 ? 0 : 1) * g * (D + 2), lt, a.v_scale);
+      en.store_partial(rec_base + (seg_start == g0 ? 0 : 1) * g * (D + 2), lt, v_scale);
     }
     if (gt + 1 < g1) {                         // next sequence: new query rows, fresh state
       if (q_seq == cur[1].s) en.take_q(qpre); else en.load_q(q_of(cur[1].s));

@@ -22,6 +22,8 @@ struct PoolGeom {
   float k_scale;
   float v_scale;
   uint32_t flags;        // pa_kv_pool.flags
+  const float* k_hs;     // per-KV-head fp8 scales (device) or null
+  const float* v_hs;
 };
 
 struct DecodeArgs {
@@ -41,6 +43,8 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   float score_scale;          // scale * log2(e) * k_scale: scores in log2 units
   float v_scale;
+  const float* k_hs;          // per-KV-head scales (device) or null: score_scale
+  const float* v_hs;          //   and v_scale then take the head's factor
   int32_t part_tokens;        // split pass: tokens per partition
   int32_t num_parts;          // split pass: partitions per (sequence, KV head)
   float* ws_o;                // split pass: [S][Hq][num_parts][D] normalised partials
@@ -95,6 +99,8 @@ struct PrefillArgs {
   int32_t num_qt;             // workgroups per (sequence, KV head): cdiv(max_q_len, tile)
   float score_scale;          // scale * log2(e) * k_scale
   float v_scale;
+  const float* k_hs;          // per-KV-head scales (device) or null
+  const float* v_hs;
 };
 
 // Query rows (token, head pairs) one prefill workgroup covers.

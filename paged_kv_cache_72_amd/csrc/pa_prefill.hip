@@ -237,7 +237,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[c][nb] = {0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {kNegBig, kNegBig}, l_run[2] = {0.f, 0.f};
-  const float sc = a.score_scale;
+  const float sc = a.k_hs ? a.score_scale * a.k_hs[kh] : a.score_scale;
+  const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
 
   // One tile of math on LDS buffer (ks, vs) for positions kt .. kt + 31.
   auto compute = [&](const lds_char* ks, const lds_char* vs, int kt, bool diag) {
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
       const int t = r / g, j = r - t * g;
       const int row = qs0 + q0 + t;
       if (!(t < QT && q0 + t < q_len && row >= 0 && row < a.total_q)) continue;
-      const float f = a.v_scale / li;
+      const float f = v_scale / li;
       _Float16* op = a.out + ((int64_t)row * a.num_q_heads + kh * g + j) * D + n;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) op[16 * nb] = (_Float16)(acc[c][nb][i] * f);
@@ -519,7 +520,8 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[c][nb] = {0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {kNegBig, kNegBig}, l_run[2] = {0.f, 0.f};
-  const float sc = a.score_scale;
+  const float sc = a.k_hs ? a.score_scale * a.k_hs[kh] : a.score_scale;
+  const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
 
   auto compute = [&](uint32_t bo, int kt, bool diag) {
     half8_t kop[2][NST];
@@ -637,7 +639,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
       const int t = r / g, j = r - t * g;
       const int row = qs0 + q0 + t;
       if (!(t < QT && q0 + t < q_len && row >= 0 && row < a.total_q)) continue;
-      const float f = a.v_scale / li;
+      const float f = v_scale / li;
       _Float16* op = a.out + ((int64_t)row * a.num_q_heads + kh * g + j) * D + n;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) op[16 * nb] = (_Float16)(acc[c][nb][i] * f);

@@ -47,6 +47,7 @@ class pa_kv_pool(C.Structure):
         ("block_size", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
         ("dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
         ("flags", C.c_uint32), ("reserved", C.c_uint32),
+        ("k_head_scales", C.c_void_p), ("v_head_scales", C.c_void_p),
     ]
 
 
@@ -114,8 +115,17 @@ class KVPool:
     def __init__(self, k: torch.Tensor, v: torch.Tensor, block_size: int, num_kv_heads: int,
                  head_dim: int, kv_dtype: str = "f16", k_scale: float = 1.0,
                  v_scale: float = 1.0, num_blocks: Optional[int] = None,
-                 block_stride_bytes: int = 0, shared_blocks: bool = False):
+                 block_stride_bytes: int = 0, shared_blocks: bool = False,
+                 k_head_scales: Optional[torch.Tensor] = None,
+                 v_head_scales: Optional[torch.Tensor] = None):
+        """k_head_scales / v_head_scales: optional device float32 [num_kv_heads]
+        fp8 scales, one per KV head (replacing k_scale / v_scale)."""
         self.k, self.v = k, v
+        self.k_head_scales, self.v_head_scales = k_head_scales, v_head_scales
+        khp = _dev(k_head_scales, torch.float32, "k_head_scales") if k_head_scales is not None \
+            else None
+        vhp = _dev(v_head_scales, torch.float32, "v_head_scales") if v_head_scales is not None \
+            else None
         self.block_size, self.num_kv_heads, self.head_dim = block_size, num_kv_heads, head_dim
         self.kv_dtype = kv_dtype
         self.k_scale, self.v_scale = float(k_scale), float(v_scale)
@@ -124,7 +134,7 @@ class KVPool:
         self.desc = pa_kv_pool(k.data_ptr(), v.data_ptr(), self.num_blocks,
                                self.block_stride_bytes, block_size, num_kv_heads, head_dim,
                                _DTYPES[kv_dtype], self.k_scale, self.v_scale,
-                               PA_POOL_SHARED_BLOCKS if shared_blocks else 0, 0)
+                               PA_POOL_SHARED_BLOCKS if shared_blocks else 0, 0, khp, vhp)
 
     @property
     def shared_blocks(self) -> bool:
@@ -139,7 +149,8 @@ class KVPool:
     def allocate(cls, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
                  kv_dtype: str = "f16", k_scale: float = 1.0, v_scale: float = 1.0,
                  device="cuda", fill_bits: Optional[int] = None,
-                 shared_blocks: bool = False) -> "KVPool":
+                 shared_blocks: bool = False, k_head_scales=None,
+                 v_head_scales=None) -> "KVPool":
         tdt = torch.int16 if kv_dtype == "f16" else torch.uint8
         shape = (num_blocks, block_size, num_kv_heads, head_dim)
         k = torch.empty(shape, dtype=tdt, device=device)
@@ -149,8 +160,12 @@ class KVPool:
                                                             else fill_bits)
             k.fill_(fb)
             v.fill_(fb)
+        khs = vhs = None
+        if k_head_scales is not None:
+            khs = torch.as_tensor(k_head_scales, dtype=torch.float32).to(device).contiguous()
+            vhs = torch.as_tensor(v_head_scales, dtype=torch.float32).to(device).contiguous()
         return cls(k, v, block_size, num_kv_heads, head_dim, kv_dtype, k_scale, v_scale,
-                   shared_blocks=shared_blocks)
+                   shared_blocks=shared_blocks, k_head_scales=khs, v_head_scales=vhs)
 
     @property
     def elem_bytes(self) -> int:

@@ -30,7 +30,9 @@ class DeviceCase:
         fill = W.poison_pool_bits(w) if poison else 0
         self.pool = L.KVPool.allocate(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
                                       w.kv_dtype, w.k_scale, w.v_scale, device, fill_bits=fill,
-                                      shared_blocks=w.has_shared_blocks)
+                                      shared_blocks=w.has_shared_blocks,
+                                      k_head_scales=w.k_head_scales,
+                                      v_head_scales=w.v_head_scales)
         self.fill = fill
         self.q = torch.from_numpy(w.q).to(device)
         self.bt = torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(device)

@@ -221,3 +221,14 @@ def test_prefill_empty_is_a_noop_even_with_null_buffers(so, kw):
 def test_prefill_grid_size_is_checked(so):
     # 2^20 sequences x 8 KV heads x cdiv(2^20, 32) query tiles overflows the grid
     assert _prefill(so, _pool(), S=1 << 20, maxq=1 << 20) == L.PA_ERR_INVALID_ARG
+
+
+def test_per_head_scale_fields_validated(so):
+    fp8 = dict(dtype=L.PA_KV_FP8_E4M3FN, k_scale=0.5, v_scale=0.5)
+    assert _decode(so, _pool(**fp8, k_head_scales=FAKE)) == L.PA_ERR_INVALID_ARG      # one of two
+    assert _decode(so, _pool(**fp8, k_head_scales=FAKE + 2, v_head_scales=FAKE)) == \
+        L.PA_ERR_ALIGNMENT
+    assert _decode(so, _pool(k_head_scales=FAKE, v_head_scales=FAKE)) == L.PA_ERR_INVALID_ARG  # f16
+    # accepted for fp8 pools: the call then fails only on the missing workspace
+    assert _decode(so, _pool(**fp8, k_head_scales=FAKE, v_head_scales=FAKE + 64), part=1,
+                   max_len=4096) == L.PA_ERR_WORKSPACE

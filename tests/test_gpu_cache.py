@@ -19,6 +19,10 @@ pytestmark = pytest.mark.gpu
     ("d64_fp8", lambda: W.custom("c", 43, [17, 40], 8, 2, 64, 16, kv_dtype="fp8_e4m3fn")),
     ("bs16_e5m2", lambda: W.custom("c", 45, [5, 64, 700], 8, 2, 128, 16, kv_dtype="fp8_e5m2")),
     ("d64_bs8_e5m2", lambda: W.custom("c", 46, [17, 40], 8, 2, 64, 8, kv_dtype="fp8_e5m2")),
+    ("bs16_e4m3_head", lambda: W.custom("c", 47, [5, 64, 700], 8, 8, 128, 16,
+                                        kv_dtype="fp8_e4m3fn", scale_grain="head")),
+    ("d64_e5m2_head", lambda: W.custom("c", 48, [17, 40], 8, 4, 64, 16, kv_dtype="fp8_e5m2",
+                                       scale_grain="head")),
 ])
 @pytest.mark.parametrize("poison", [False, True])
 def test_scatter_bit_exact(name, make, poison):

@@ -39,6 +39,11 @@ SHAPES = {
     "e5m2_d64_bs8_g4": lambda: W.custom("s", 66, EDGE_LENS, 8, 2, 64, 8, kv_dtype="fp8_e5m2"),
     "e5m2_d128_bs64_g7": lambda: W.custom("s", 67, EDGE_LENS, 28, 4, 128, 64,
                                           kv_dtype="fp8_e5m2"),
+    # one fp8 scale per KV head (heads of different magnitude)
+    "fp8h_d128_bs16_g4": lambda: W.custom("s", 68, EDGE_LENS, 32, 8, 128, 16,
+                                          kv_dtype="fp8_e4m3fn", scale_grain="head"),
+    "e5m2h_d64_bs32_g2": lambda: W.custom("s", 69, EDGE_LENS, 8, 4, 64, 32, kv_dtype="fp8_e5m2",
+                                          scale_grain="head"),
 }
 
 _cache = {}
@@ -69,7 +74,7 @@ def test_decode_matches_oracle(name, part):
 
 
 @pytest.mark.parametrize("name", ["tiny", "d128_bs8_g7", "fp8_d128_bs32", "d64_bs32_g16",
-                                  "e5m2_d128_bs16_g4"])
+                                  "e5m2_d128_bs16_g4", "fp8h_d128_bs16_g4"])
 @pytest.mark.parametrize("variant", ["v_offset", "needles"])
 @pytest.mark.parametrize("part", [-1, 1, 64])
 def test_structured_variants(name, variant, part):

@@ -39,6 +39,9 @@ SHAPES = {
     "decode_like": lambda: W.custom_prefill("pf", 89, [0, 1, 15, 16, 500], [1, 1, 1, 1, 1],
                                             32, 8, 128, 16),
     "empty_seq": lambda: W.custom_prefill("pf", 90, [10, 20, 5], [12, 0, 7], 8, 2, 128, 16),
+    "d128_bs16_g4_e4m3_head": lambda: W.custom_prefill("pf", 91, [0, 40], [64, 25], 32, 8, 128,
+                                                       16, kv_dtype="fp8_e4m3fn",
+                                                       scale_grain="head"),
 }
 
 
