@@ -30,6 +30,7 @@ class OrcPool(C.Structure):
         ("elem_bytes", C.c_int32), ("fp8_format", C.c_int32),
         ("k_scale", C.c_double), ("v_scale", C.c_double),
         ("k_head_scales", C.c_void_p), ("v_head_scales", C.c_void_p),
+        ("sliding_window", C.c_int32),
     ]
 
 
@@ -132,7 +133,8 @@ class HostPool:
 
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
                  kv_dtype: str = "f16", k_scale: float = 1.0, v_scale: float = 1.0,
-                 fill_bits: int = 0, k_head_scales=None, v_head_scales=None):
+                 fill_bits: int = 0, k_head_scales=None, v_head_scales=None,
+                 sliding_window: int = 0):
         self.elem_bytes = 1 if kv_dtype in ("fp8_e4m3fn", "fp8_e5m2") else 2
         fp8_format = 1 if kv_dtype == "fp8_e5m2" else 0
         dt = np.uint8 if self.elem_bytes == 1 else np.uint16
@@ -154,12 +156,14 @@ class HostPool:
                             num_kv_heads, head_dim, self.elem_bytes, fp8_format,
                             float(k_scale), float(v_scale),
                             None if self.k_head is None else self.k_head.ctypes.data,
-                            None if self.v_head is None else self.v_head.ctypes.data)
+                            None if self.v_head is None else self.v_head.ctypes.data,
+                            int(sliding_window))
 
     @classmethod
     def for_workload(cls, w, fill_bits: int = 0) -> "HostPool":
         return cls(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype,
-                   w.k_scale, w.v_scale, fill_bits, w.k_head_scales, w.v_head_scales)
+                   w.k_scale, w.v_scale, fill_bits, w.k_head_scales, w.v_head_scales,
+                   w.window)
 
 
 def scatter(pool: HostPool, k_new: np.ndarray, v_new: np.ndarray, slots: np.ndarray,

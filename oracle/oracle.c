@@ -274,6 +274,11 @@ void orc_attend(const double* q, const double* Kc, const double* Vc, int32_t len
   free(x);
 }
 
+/* First position a query sees when n positions (0 .. n - 1) precede and include it. */
+static int32_t window_start(const orc_pool* p, int32_t n) {
+  return (p->sliding_window > 0 && n > p->sliding_window) ? n - p->sliding_window : 0;
+}
+
 /* One (sequence, KV head) unit of work, evaluated for each of its query heads. */
 typedef void (*head_fn)(const double* q, const double* Kc, const double* Vc, int32_t len,
                         int32_t D, double scale, int32_t psz, double* out);
@@ -348,10 +353,13 @@ static void decode_units(const orc_pool* p, const uint16_t* qbits, int32_t S, in
     double* Vc = (double*)malloc(sizeof(double) * rows);
     double* qd = (double*)malloc(sizeof(double) * (size_t)D);
     orc_gather_head(p, bt + (int64_t)s * max_blocks, len, kh, Kc, Vc);
+    /* the query (position len - 1) sees the last sliding_window positions */
+    const int32_t w0 = window_start(p, len);
     for (int32_t h = kh * g; h < (kh + 1) * g; ++h) {
       const uint16_t* qh = qbits + ((int64_t)s * Hq + h) * D;
       for (int32_t d = 0; d < D; ++d) qd[d] = orc_f16_value(qh[d]);
-      fn(qd, Kc, Vc, len, D, sc, psz, out + ((int64_t)s * Hq + h) * D);
+      fn(qd, Kc + (int64_t)w0 * D, Vc + (int64_t)w0 * D, len - w0, D, sc, psz,
+         out + ((int64_t)s * Hq + h) * D);
     }
     free(Kc);
     free(Vc);
@@ -410,10 +418,12 @@ void orc_prefill(const orc_pool* p, const uint16_t* qbits, const int32_t* q_star
     double* qd = (double*)malloc(sizeof(double) * (size_t)D);
     orc_gather_head(p, bt + (int64_t)s * max_blocks, n, kh, Kc, Vc);
     const int64_t row = (int64_t)q_start[s] + i;
+    const int32_t w0 = window_start(p, n);
     for (int32_t h = kh * g; h < (kh + 1) * g; ++h) {
       const uint16_t* qh = qbits + (row * Hq + h) * D;
       for (int32_t d = 0; d < D; ++d) qd[d] = orc_f16_value(qh[d]);
-      orc_attend(qd, Kc, Vc, n, D, sc, out + (row * Hq + h) * D);
+      orc_attend(qd, Kc + (int64_t)w0 * D, Vc + (int64_t)w0 * D, n - w0, D, sc,
+                 out + (row * Hq + h) * D);
     }
     free(Kc);
     free(Vc);

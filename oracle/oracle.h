@@ -27,6 +27,9 @@
  *     the quantisation passage of "KV Cache memory core", section 4.4, names).
  *   - copy_blocks copies a whole block for copy-on-write ("GPU memory & KV
  *     cache", COW incident code; "vLLM intro part 2", section 5).
+ *   - A sliding-window layer lets a query see only the last sliding_window
+ *     positions; blocks wholly outside the window are released ("Paging saves
+ *     no KV bytes", section 5, sliding-window block release).
  *   - Prefill writes a prompt's K/V in bulk and then attends over the paged
  *     context ("vLLM intro part 2", section 3, KV lifecycle: prefill writes
  *     blocks in bulk, decode appends one slot); with a prefix-cache hit only the
@@ -60,6 +63,9 @@ typedef struct {
    * non-NULL they replace k_scale / v_scale for fp8 pools.                    */
   const double* k_head_scales;
   const double* v_head_scales;
+  /* Sliding-window attention: > 0 limits a query at position p to positions
+   * p - sliding_window + 1 .. p (0: every earlier position).                  */
+  int32_t sliding_window;
 } orc_pool;
 
 #define ORC_FP8_E4M3FN 0

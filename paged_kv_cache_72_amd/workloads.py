@@ -92,6 +92,8 @@ class Workload:
     # fp8 pools with one scale per KV head (float32 [Hkv]); None: per-tensor scales
     k_head_scales: Optional[np.ndarray] = None
     v_head_scales: Optional[np.ndarray] = None
+    # sliding-window layer: a query at position p sees positions p - window + 1 .. p
+    window: int = 0
 
     @property
     def is_prefill(self) -> bool:
