@@ -56,9 +56,11 @@ def unique_kv_tokens(w) -> int:
     used = {}
     for s in range(w.num_seqs):
         n = int(w.seq_lens[s])
-        for j in range((n + bs - 1) // bs):
+        w0 = max(0, n - w.window) if w.window else 0       # sliding window: read from w0
+        for j in range(w0 // bs, (n + bs - 1) // bs):
             b = int(w.block_tables[s, j])
-            used[b] = max(used.get(b, 0), min(bs, n - j * bs))
+            lo, hi = max(j * bs, w0), min((j + 1) * bs, n)
+            used[b] = max(used.get(b, 0), hi - lo)
     return sum(used.values())
 
 
@@ -69,7 +71,8 @@ def alg_bytes(w) -> dict:
     e = w.kv_elem_bytes
     lens = w.seq_lens.astype(np.int64)
     row = w.num_kv_heads * w.head_dim * e * 2
-    kv_logical = int(lens.sum()) * row
+    seen = np.minimum(lens, w.window) if w.window else lens      # positions each query reads
+    kv_logical = int(seen.sum()) * row
     kv = unique_kv_tokens(w) * row if w.has_shared_blocks else kv_logical
     qo = w.num_seqs * w.num_q_heads * w.head_dim * 2 * 2
     tables = int(((lens + w.block_size - 1) // w.block_size).sum()) * 4 + w.num_seqs * 4
@@ -423,7 +426,8 @@ def main() -> int:
     shared = w.has_shared_blocks      # cacheable K/V reads when blocks have several readers
     base = L.KVPool.allocate(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
                              w.kv_dtype, w.k_scale, w.v_scale, dev, fill_bits=0,
-                             shared_blocks=shared)
+                             shared_blocks=shared, k_head_scales=w.k_head_scales,
+                             v_head_scales=w.v_head_scales, sliding_window=w.window)
     L.pa_reshape_and_cache(base, k_all, v_all, slots)
     if w.cow_pairs is not None:
         L.pa_copy_blocks(base, torch.from_numpy(w.cow_pairs).to(dev))
@@ -436,7 +440,8 @@ def main() -> int:
     for _ in range(args.layers - 1):
         pools.append(L.KVPool(base.k.clone(), base.v.clone(), w.block_size, w.num_kv_heads,
                               w.head_dim, w.kv_dtype, w.k_scale, w.v_scale,
-                              shared_blocks=shared))
+                              shared_blocks=shared, k_head_scales=base.k_head_scales,
+                              v_head_scales=base.v_head_scales, sliding_window=w.window))
     part = L.pa_decode_plan(base, w.num_seqs, w.num_q_heads, w.max_seq_len, args.partition)
     ws = L.alloc_workspace(base, w.num_seqs, w.num_q_heads, w.max_seq_len, args.partition)
     torch.cuda.synchronize()
@@ -520,7 +525,8 @@ def main() -> int:
                    "layers_rotated": args.layers, "partition_tokens": part,
                    "shared_blocks": shared},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "kv_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_step * 1e-3), 1),
+        "kv_tokens_per_s": round(float((np.minimum(w.seq_lens, w.window) if w.window
+                                        else w.seq_lens).sum()) / (ms_step * 1e-3), 1),
         "decode_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "alg_bytes_per_step": step_bytes,
         "reshape_and_cache": {"tokens": int(w.new_idx.size), "avg_ms": round(rc_ms, 5),

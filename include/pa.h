@@ -87,7 +87,10 @@ typedef enum {
  * other readers of a block find it in cache.  Without it, K/V tiles are read
  * with the streaming (non-temporal) cache policy, the faster choice when every
  * block has one reader.  The flag changes speed only, never results.
- * reserved must be 0. */
+ * sliding_window > 0 makes the layer a sliding-window layer: a query at
+ * position p attends to positions p - sliding_window + 1 .. p only (0: every
+ * earlier position); blocks wholly before a sequence's window are never read,
+ * so the host may release them ("Paging saves no KV bytes", section 5). */
 #define PA_POOL_SHARED_BLOCKS 1u
 typedef struct {
   void* k_base;                /* device */
@@ -101,7 +104,7 @@ typedef struct {
   float k_scale;
   float v_scale;
   uint32_t flags;              /* PA_POOL_* bits */
-  uint32_t reserved;
+  int32_t sliding_window;      /* 0: full attention */
   /* Optional finer fp8 scale grain: device arrays of num_kv_heads float32
    * scales, one per KV head, for K and for V ("KV Cache memory core",
    * section 4.4 names scale granularity finer than per tensor).  Both NULL

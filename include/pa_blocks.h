@@ -88,6 +88,15 @@ int pa_bp_free_request(pa_block_pool* pool, int64_t request);
 int32_t pa_bp_request_blocks(const pa_block_pool* pool, int64_t request, int32_t* out,
                              int32_t cap);
 
+/* Sliding-window layers: once a request holds num_tokens tokens, its next
+ * query (position num_tokens) sees positions num_tokens - window + 1 onward;
+ * release every block lying wholly before that position ("Paging saves no KV
+ * bytes", section 5: out-of-window blocks are released directly).  Released
+ * entries of the block table read back as -1 and are skipped when the request
+ * is freed.  Returns the number of blocks released. */
+int32_t pa_bp_remove_skipped_blocks(pa_block_pool* pool, int64_t request, int32_t num_tokens,
+                                    int32_t window);
+
 /* Fork: child shares every block of parent (each count + 1). */
 int pa_bp_fork_request(pa_block_pool* pool, int64_t parent, int64_t child);
 /* Before writing the token at this position: if its block is shared (count

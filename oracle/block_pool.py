@@ -157,7 +157,23 @@ class BlockPoolModel:
             self.requests[rid] += self.get_new_blocks(need)
 
     def free_request(self, rid: int) -> None:
-        self.free_blocks(list(reversed(self.requests.pop(rid))))
+        self.free_blocks([b for b in reversed(self.requests.pop(rid)) if b >= 0])
+
+    def remove_skipped_blocks(self, rid: int, num_tokens: int, window: int) -> int:
+        """Sliding window: the next query (position num_tokens) sees positions
+        from num_tokens - window + 1; blocks wholly before that are released,
+        last to first, and their table entries become -1 ("Paging saves no KV
+        bytes", section 5)."""
+        first = num_tokens - window + 1
+        if first <= 0:
+            return 0
+        blocks = self.requests[rid]
+        n = min(first // self.block_size, len(blocks))
+        out = [b for b in reversed(blocks[:n]) if b >= 0]
+        self.free_blocks(out)
+        for j in range(n):
+            blocks[j] = -1
+        return len(out)
 
     # ---------------------------------------------------------------- state
     def state(self) -> dict:

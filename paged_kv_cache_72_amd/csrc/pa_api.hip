@@ -61,7 +61,8 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
     return fail(PA_ERR_INVALID_ARG, "fp8 pools need finite positive k_scale and v_scale");
   if (p->flags & ~PA_POOL_SHARED_BLOCKS)
     return fail(PA_ERR_INVALID_ARG, "unknown pool flags 0x%x", (unsigned)p->flags);
-  if (p->reserved) return fail(PA_ERR_INVALID_ARG, "pool reserved field must be 0");
+  if (p->sliding_window < 0)
+    return fail(PA_ERR_INVALID_ARG, "sliding_window %d < 0", p->sliding_window);
   if ((p->k_head_scales == nullptr) != (p->v_head_scales == nullptr))
     return fail(PA_ERR_INVALID_ARG, "k_head_scales and v_head_scales must be both set or both NULL");
   if (p->k_head_scales) {
@@ -83,6 +84,7 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
   g->k_scale = p->dtype == PA_KV_F16 ? 1.f : p->k_scale;
   g->v_scale = p->dtype == PA_KV_F16 ? 1.f : p->v_scale;
   g->flags = p->flags;
+  g->window = p->sliding_window;
   g->k_hs = p->k_head_scales;
   g->v_hs = p->v_head_scales;
   if (g->k_hs) g->k_scale = g->v_scale = 1.f;
@@ -296,6 +298,7 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
   a.v_scale = g.v_scale;
   a.k_hs = g.k_hs;
   a.v_hs = g.v_hs;
+  a.window = g.window;
   pa::FlatArgs f{};
   if (pl.mode == pa::kModeSplit) {
     a.part_tokens = pl.part;
@@ -372,6 +375,7 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
   a.v_scale = g.v_scale;
   a.k_hs = g.k_hs;
   a.v_hs = g.v_hs;
+  a.window = g.window;
   if (hipError_t e = pa::launch_prefill(a, g.head_dim, g.block_size,
                                         g.elem_bytes == 2 ? 0 : (g.fp8_e5m2 ? 2 : 1), stream))
     return fail(PA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

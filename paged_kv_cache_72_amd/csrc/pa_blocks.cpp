@@ -443,7 +443,8 @@ int pa_bp_free_request(pa_block_pool* p, int64_t rid) {
   auto it = p->requests.find(rid);
   if (it == p->requests.end()) return fail(PA_ERR_INVALID_ARG, "no request %lld", (long long)rid);
   const std::vector<int32_t>& v = it->second;
-  for (size_t i = v.size(); i-- > 0;) p->release(v[i]);
+  for (size_t i = v.size(); i-- > 0;)
+    if (v[i] >= 0) p->release(v[i]);           // -1: released by the sliding window
   p->requests.erase(it);
   return PA_OK;
 }
@@ -457,6 +458,27 @@ int32_t pa_bp_request_blocks(const pa_block_pool* p, int64_t rid, int32_t* out, 
   return n;
 }
 
+int32_t pa_bp_remove_skipped_blocks(pa_block_pool* p, int64_t rid, int32_t num_tokens,
+                                    int32_t window) {
+  if (!p) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  auto it = p->requests.find(rid);
+  if (it == p->requests.end()) return fail(PA_ERR_INVALID_ARG, "no request %lld", (long long)rid);
+  if (num_tokens < 0 || window < 1) return fail(PA_ERR_INVALID_ARG, "bad token count or window");
+  const int64_t first = (int64_t)num_tokens - window + 1;   // first position still seen
+  if (first <= 0) return 0;
+  int64_t nfull = first / p->block_size;                     // blocks wholly before it
+  if (nfull > (int64_t)it->second.size()) nfull = (int64_t)it->second.size();
+  int32_t released = 0;
+  for (int64_t j = nfull; j-- > 0;) {                        // last to first, as free does
+    int32_t& b = it->second[(size_t)j];
+    if (b < 0) continue;
+    p->release(b);
+    b = -1;
+    ++released;
+  }
+  return released;
+}
+
 int pa_bp_fork_request(pa_block_pool* p, int64_t parent, int64_t child) {
   if (!p) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
   auto it = p->requests.find(parent);
@@ -464,7 +486,8 @@ int pa_bp_fork_request(pa_block_pool* p, int64_t parent, int64_t child) {
     return fail(PA_ERR_INVALID_ARG, "no request %lld", (long long)parent);
   if (p->requests.count(child)) return fail(PA_ERR_INVALID_ARG, "request %lld exists", (long long)child);
   std::vector<int32_t> v = it->second;
-  for (int32_t b : v) ++p->ref[(size_t)b];
+  for (int32_t b : v)
+    if (b >= 0) ++p->ref[(size_t)b];
   p->requests[child] = std::move(v);
   return PA_OK;
 }
@@ -478,6 +501,7 @@ int pa_bp_prepare_write(pa_block_pool* p, int64_t rid, int32_t position, int64_t
   if (j >= (int32_t)it->second.size())
     return fail(PA_ERR_INVALID_ARG, "position %d beyond the request's blocks", position);
   const int32_t b = it->second[(size_t)j];
+  if (b < 0) return fail(PA_ERR_INVALID_ARG, "position %d lies in a released block", position);
   if (p->ref[(size_t)b] <= 1) return 0;
   if (p->nfree < 1) return fail(PA_ERR_NO_BLOCKS, "no free block for copy-on-write");
   int32_t nb;

@@ -92,6 +92,11 @@ __device__ __forceinline__ uint32_t e5m2_pair(uint32_t w0, uint32_t w1, int b) {
   return (((w0 >> (8 * b)) & 0xFFu) << 8) | (((w1 >> (8 * b)) & 0xFFu) << 24);
 }
 
+// First position the query of a length-len context sees (sliding window).
+__device__ __forceinline__ int win_start(int len, int window) {
+  return (window > 0 && len > window) ? len - window : 0;
+}
+
 // Byte bases, inside the pools, of a tile's two halves (equal when block_size >= 16).
 struct Ids {
   int64_t lo, hi;
@@ -250,7 +255,9 @@ struct Engine {
 
   // Fold tile j (tokens 16j..16j+15) into the running state; tokens >= t_end
   // are masked.
-  __device__ __forceinline__ void compute(int j, int t_end, const uint4* kr, const VT* vr_in) {
+  // Tokens t_begin .. t_end - 1 of tile j count; the others are masked.
+  __device__ __forceinline__ void compute(int j, int t_begin, int t_end, const uint4* kr,
+                                          const VT* vr_in) {
     // Loads issued before this point stay before it: otherwise the scheduler
     // hoists the waits for this tile above the next tile's loads.
     __builtin_amdgcn_sched_barrier(0);
@@ -280,11 +287,13 @@ struct Engine {
         sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kop, qop[cl * GPL + grp], sacc, 0, 0, 0);
       }
     }
-    const bool partial = j * 16 + 16 > t_end;   // wave-uniform
+    const bool partial = j * 16 + 16 > t_end || j * 16 < t_begin;   // wave-uniform
+    const uint32_t span = (uint32_t)(t_end - t_begin);
     const int tb = j * 16 + r;                  // token of score i: tb + 4 i
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * i < t_end) ? sacc[i] * sc : -INFINITY;
+    for (int i = 0; i < 4; ++i)
+      x[i] = ((uint32_t)(tb + 4 * i - t_begin) < span) ? sacc[i] * sc : -INFINITY;
     float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     tmax = xor_max(tmax, 16);
     tmax = xor_max(tmax, 32);
@@ -314,7 +323,7 @@ struct Engine {
     if (partial) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const bool ok = tb + 4 * k < t_end;
+        const bool ok = (uint32_t)(tb + 4 * k - t_begin) < span;
 #pragma unroll
         for (int wi = 0; wi < VB / 4; ++wi) vw[k][wi] = ok ? vw[k][wi] : 0u;
       }
@@ -430,13 +439,16 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
   const int64_t head_off = (int64_t)kh * D * Engine<D, BS, KV, NT>::E;
   const PairRef row{tables + (int64_t)s * a.max_blocks, a.max_blocks, 0, head_off};
   const int len = clamp_len(lens[s], a.len_cap);
-  int t_begin = 0, t_end = len;
+  const int w0 = win_start(len, a.window);    // first position the query sees
+  int t_begin = w0, t_end = len;
   if constexpr (SPLIT) {
     t_begin = part * a.part_tokens;
     if (t_begin >= len) return;               // partition past the end: nothing to do
     t_end = min(len, t_begin + a.part_tokens);
+    if (t_end <= w0) return;                  // partition before the window: not read
+    t_begin = max(t_begin, w0);               // (the reduce skips such partitions)
   }
-  const int j_begin = t_begin >> 4;           // partition sizes are multiples of 16
+  const int j_begin = t_begin >> 4;
   const int j_end = (t_end + 15) >> 4;
 
   __shared__ __attribute__((aligned(16))) char kstage[NW][En::KST];
@@ -447,7 +459,11 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
   en.load_q(a.q + ((int64_t)s * a.num_q_heads + (int64_t)kh * g) * D);
   en.reset();
   const PairRef pr{tables + (int64_t)s * a.max_blocks, (len + BS - 1) / BS, len, head_off};
-  const Ids ids0 = en.tile_ids(row, j0), ids1 = en.tile_ids(row, j0 + NW);
+  Ids ids0 = en.tile_ids(row, j0), ids1 = en.tile_ids(row, j0 + NW);
+  if (j_begin + wid != j0) {                  // window start: the speculation missed
+    ids0 = en.tile_ids(row, j_begin + wid);
+    ids1 = en.tile_ids(row, j_begin + wid + NW);
+  }
 
   // The loads of tile j+NW and the block ids of tile j+2NW are in flight while
   // tile j is computed; two register sets alternate.  Past the end of the
@@ -463,12 +479,12 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
     for (;;) {
       en.issue(ids_b, kB, vB);
       const Ids ids_a = en.tile_ids(pr, min(j + 2 * NW, j_last));
-      en.compute(j, t_end, kA, vA);
+      en.compute(j, t_begin, t_end, kA, vA);
       j += NW;
       if (j >= j_end) break;
       en.issue(ids_a, kA, vA);
       ids_b = en.tile_ids(pr, min(j + 2 * NW, j_last));
-      en.compute(j, t_end, kB, vB);
+      en.compute(j, t_begin, t_end, kB, vB);
       j += NW;
       if (j >= j_end) break;
     }
@@ -528,8 +544,10 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeArgs a) {
   const int row_id = blockIdx.x;
   const int s = row_id / a.num_q_heads;
   const int len = clamp_len(a.seq_lens[s], a.len_cap);
-  const int np = (len + a.part_tokens - 1) / a.part_tokens;
-  const int64_t base = (int64_t)row_id * a.num_parts;
+  // partitions before the sliding window wrote nothing: start at the window's
+  const int p0 = win_start(len, a.window) / a.part_tokens;
+  const int np = (len + a.part_tokens - 1) / a.part_tokens - p0;
+  const int64_t base = (int64_t)row_id * a.num_parts + p0;
   const float2* ml = a.ws_ml + base;
 
   __shared__ float red[NT / 64];
@@ -626,7 +644,7 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   for (int i = threadIdx.x; i < S; i += NTH) {
     const int len = clamp_len(lens[i], a.len_cap);
     sm_len[i] = len;
-    sm_pre[i + 1] = (len + 15) >> 4;
+    sm_pre[i + 1] = ((len + 15) >> 4) - (win_start(len, a.window) >> 4);   // tiles it reads
   }
   __syncthreads();
   {
@@ -697,10 +715,11 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   if (a.k_hs) en.sc *= a.k_hs[kh];
   const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
   const int64_t head_off = (int64_t)kh * D * En::E;
+  // unit j of a sequence is its tile j + (window start >> 4)
   auto ids_of = [&](Cur c) -> Ids {
     const int len = uni(sm_len[c.s]);
     const PairRef p{tables + (int64_t)c.s * a.max_blocks, (len + BS - 1) / BS, len, head_off};
-    return en.tile_ids(p, c.j);
+    return en.tile_ids(p, c.j + (win_start(len, a.window) >> 4));
   };
   auto q_of = [&](int cs) { return qs + ((int64_t)cs * a.num_q_heads + (int64_t)kh * g) * D; };
   float* rec_base = slots + (int64_t)gw * 2 * g * (D + 2);
@@ -760,7 +779,10 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
       }
       en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST]);
       ids_next = ids_of(cur[ST]);
-      en.compute(cur[0].j, uni(sm_len[cur[0].s]), kb[st], vb[st]);
+      {
+        const int len = uni(sm_len[cur[0].s]), w0 = win_start(len, a.window);
+        en.compute(cur[0].j + (w0 >> 4), w0, len, kb[st], vb[st]);
+      }
       finish();
       if (++gt == g1) return;
 #pragma unroll

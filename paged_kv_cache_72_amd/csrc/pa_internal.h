@@ -24,6 +24,7 @@ struct PoolGeom {
   uint32_t flags;        // pa_kv_pool.flags
   const float* k_hs;     // per-KV-head fp8 scales (device) or null
   const float* v_hs;
+  int32_t window;        // sliding window in positions, 0: none
 };
 
 struct DecodeArgs {
@@ -45,6 +46,8 @@ struct DecodeArgs {
   float v_scale;
   const float* k_hs;          // per-KV-head scales (device) or null: score_scale
   const float* v_hs;          //   and v_scale then take the head's factor
+  int32_t window;             // sliding window: the query sees the last `window`
+                              //   positions of its context (0: all)
   int32_t part_tokens;        // split pass: tokens per partition
   int32_t num_parts;          // split pass: partitions per (sequence, KV head)
   float* ws_o;                // split pass: [S][Hq][num_parts][D] normalised partials
@@ -101,6 +104,7 @@ struct PrefillArgs {
   float v_scale;
   const float* k_hs;          // per-KV-head scales (device) or null
   const float* v_hs;
+  int32_t window;             // sliding window (0: none): position p sees p - window + 1 .. p
 };
 
 // Query rows (token, head pairs) one prefill workgroup covers.

@@ -140,7 +140,18 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
   if (q0 >= q_len) return;                       // uniform: whole workgroup
   const int ctx = len - q_len;
   const int t_hi = q_len < q0 + QT ? q_len : q0 + QT;
-  const int kv_end = ctx + t_hi;                  // positions 0 .. kv_end - 1 are read
+  const int kv_end = ctx + t_hi;                  // positions kstart .. kv_end - 1 are read
+  // sliding window: the workgroup's first row sees nothing before
+  // ctx + q0 - window + 1; tiles start at that position's tile
+  const int lo = a.window > 0 ? ctx + q0 - a.window + 1 : 0;
+  const int kstart = lo > 0 ? (lo / kPfKeys) * kPfKeys : 0;
+  const int kstart_pos = lo > 0 ? lo : 0;         // first position any row sees
+  const uint32_t wu = a.window > 0 ? (uint32_t)a.window : 0x7FFFFFFFu;
+  // tiles at kt need the mask when they reach past the first row (causal) or
+  // begin before the last row's window
+  auto needs_mask = [&](int kt) {
+    return kt + kPfKeys - 1 > ctx + q0 || (a.window > 0 && kt < ctx + t_hi - a.window);
+  };
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
 
   // ---- query rows: this lane's B-operand row in each group, and its position
@@ -174,12 +185,16 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
   // bits 0-1 (and bit 2 when VK == 1) pick the position, the rest the chunk.
   const int vkey = VK == 2 ? 8 * wid + 2 * (tid & 3) : 8 * wid + (tid & 7);
   const int vch = VK == 2 ? (lane >> 2) : (lane >> 3);
-  auto row_addr = [&](int pos, int pos0, int ch, bool& ok) -> int64_t {
+  // Positions below the window (their blocks may be released) or at or past
+  // kv_end are not loaded: they stay zero in LDS and are masked.  A wave's
+  // positions form one aligned group of G (4 or 8) inside one block.
+  // G: the wave's group size (4 or 8 positions for K, 8 for V)
+  auto row_addr = [&](int pos, int pos0, int G, int ch, bool& ok) -> int64_t {
     ok = false;
-    if (pos0 >= kv_end) return 0;
-    int blk = bt[pos0 / BS];
+    if (pos0 >= kv_end || pos0 + G - 1 < kstart_pos) return 0;
+    int blk = bt[(pos0 > kstart_pos ? pos0 : kstart_pos) / BS];
     blk = blk < 0 ? 0 : (blk > a.num_blocks_m1 ? a.num_blocks_m1 : blk);
-    ok = pos < kv_end;
+    ok = pos >= kstart_pos && pos < kv_end;
     return (int64_t)blk * a.block_stride + (int64_t)(pos % BS) * a.row_stride + head_off +
            ch * 8 * E;
   };
@@ -190,7 +205,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
       const int pos = kt + idx / CPR;
       const int pos0 = uni(kt + (kPfWaves * 64 * i + 64 * wid) / CPR);
       bool ok;
-      const int64_t off = row_addr(pos, pos0, idx % CPR, ok);
+      const int64_t off = row_addr(pos, pos0, 64 / CPR, idx % CPR, ok);
       kr[i] = ok ? *(const Raw*)(a.k + off) : Raw{};
     }
     const int vbase = kt + vkey;
@@ -198,7 +213,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
 #pragma unroll
     for (int u = 0; u < VK; ++u) {
       bool ok;
-      const int64_t off = row_addr(vbase + u, vpos0, vch, ok);
+      const int64_t off = row_addr(vbase + u, vpos0, 8, vch, ok);
       vr[u] = ok ? *(const Raw*)(a.v + off) : Raw{};
     }
   };
@@ -241,7 +256,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
   const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
 
   // One tile of math on LDS buffer (ks, vs) for positions kt .. kt + 31.
-  auto compute = [&](const lds_char* ks, const lds_char* vs, int kt, bool diag) {
+  auto compute = [&](const lds_char* ks, const lds_char* vs, int kt, bool mask) {
     // scores S^T for both row groups; block kb row r is position kpos(kb, r)
     float4_t sa[2][2];
 #pragma unroll
@@ -273,10 +288,11 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[4 * kb + i] = sa[c][kb][i];
-      if (diag) {            // uniform branch: only diagonal tiles pay for the mask
-        const int lim = qpos[c] - kt - 8 * h;
+      if (mask) {            // uniform branch: only edge tiles pay for the mask
+        // position kt + 8h + k counts when 0 <= qpos - position < window
+        const int base = qpos[c] - kt - 8 * h;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = k <= lim ? x[k] : -INFINITY;
+        for (int k = 0; k < 8; ++k) x[k] = (uint32_t)(base - k) < wu ? x[k] : -INFINITY;
       }
       // The running max only has to move when some score exceeds it by more
       // than 2^8, so each lane tests its own 8 scores and the wave votes; the
@@ -311,19 +327,17 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
     }
   };
 
-  load_tile(0);
+  load_tile(kstart);
   store_tile(lds0);
   __syncthreads();
   int buf = 0;
-  for (int kt = 0; kt < kv_end; kt += kPfKeys) {
+  for (int kt = kstart; kt < kv_end; kt += kPfKeys) {
     // One barrier per tile: the next tile goes to the other buffer, whose last
     // readers finished before the barrier that ended the previous iteration.
     const bool more = kt + kPfKeys < kv_end;
     if (more) load_tile(kt + kPfKeys);
     const lds_char* ks = lds0 + buf * T::BUF;
-    // positions kt .. kt + 31 precede every query row of the workgroup except
-    // on the diagonal tiles: only those need the causal mask
-    compute(ks, ks + T::TILE_K, kt, kt + kPfKeys - 1 > ctx + q0);
+    compute(ks, ks + T::TILE_K, kt, needs_mask(kt));
     if (more) store_tile(lds0 + (buf ^ 1) * T::BUF);
     __syncthreads();
     buf ^= 1;
@@ -448,6 +462,13 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
   const int t_hi = q_len < q0 + QT ? q_len : q0 + QT;
   const int kv_end = ctx + t_hi;
   const int ntiles = (kv_end + kPfKeys - 1) / kPfKeys;
+  const int lo = a.window > 0 ? ctx + q0 - a.window + 1 : 0;
+  const int t0 = lo > 0 ? lo / kPfKeys : 0;     // first tile the sliding window reaches
+  const int lo_c = lo > 0 ? lo : 0;             // first position any row sees
+  const uint32_t wu = a.window > 0 ? (uint32_t)a.window : 0x7FFFFFFFu;
+  auto needs_mask = [&](int kt) {
+    return kt + kPfKeys - 1 > ctx + q0 || (a.window > 0 && kt < ctx + t_hi - a.window);
+  };
   const int32_t* bt = tables + (int64_t)s * a.max_blocks;
 
   half8_t qop[2][NST];
@@ -470,7 +491,8 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
   // ---- loads of tile t into buffer t % 3: wave w fills rows (w NI + i) RPI ..
   // of K and of V; lane -> row r0 + lane / CPR, LDS chunk lane % CPR, which
   // holds the row's chunk (lane % CPR) ^ swizzle.  Positions at or past kv_end
-  // repeat position kv_end - 1 (finite data; masked out of every score).
+  // repeat position kv_end - 1, positions before the sliding window repeat its
+  // first position (finite data; masked out of every score).
   const char* const kbase = a.k + (int64_t)kh * D * 2;
   const char* const vbase = a.v + (int64_t)kh * D * 2;
   auto issue = [&](int t, int b) {
@@ -479,10 +501,14 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
     for (int i = 0; i < T::NI; ++i) {
       const int r0 = (wid * T::NI + i) * T::RPI;
       const int r = r0 + lane / CPR, pch = lane % CPR;
-      const int pu = uni((kt + r0 < kv_end ? kt + r0 : kv_end - 1));
+      // positions are clamped into [lo_c, kv_end - 1]: outside rows repeat an
+      // in-window row (finite data, masked), never a released block
+      const int pr0 = kt + r0 < lo_c ? lo_c : kt + r0;
+      const int pu = uni(pr0 < kv_end ? pr0 : kv_end - 1);
       int blk = bt[pu / BS];
       blk = blk < 0 ? 0 : (blk > a.num_blocks_m1 ? a.num_blocks_m1 : blk);
-      const int pos = kt + r < kv_end ? kt + r : kv_end - 1;
+      const int pr = kt + r < lo_c ? lo_c : kt + r;
+      const int pos = pr < kv_end ? pr : kv_end - 1;
       const int64_t row_off = (int64_t)blk * a.block_stride + (int64_t)(pos % BS) * a.row_stride;
       lds_char* kdst = lds0 + b * T::BUF + r0 * RB;
       lds_char* vdst = kdst + T::TILE;
@@ -523,7 +549,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
   const float sc = a.k_hs ? a.score_scale * a.k_hs[kh] : a.score_scale;
   const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
 
-  auto compute = [&](uint32_t bo, int kt, bool diag) {
+  auto compute = [&](uint32_t bo, int kt, bool mask) {
     half8_t kop[2][NST];
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
@@ -561,10 +587,10 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[4 * kb + i] = sa[c][kb][i];
-      if (diag) {
-        const int lim = qpos[c] - kt - 8 * h;
+      if (mask) {
+        const int base = qpos[c] - kt - 8 * h;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = k <= lim ? x[k] : -INFINITY;
+        for (int k = 0; k < 8; ++k) x[k] = (uint32_t)(base - k) < wu ? x[k] : -INFINITY;
       }
       float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))) * sc;
@@ -611,10 +637,10 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
   // compute tile t.
   constexpr int NB_ = T::NBUF;
 #pragma unroll
-  for (int t = 0; t < NB_ - 1; ++t)
-    if (t < ntiles) issue(t, t);
+  for (int u = 0; u < NB_ - 1; ++u)
+    if (t0 + u < ntiles) issue(t0 + u, u);
   int b = 0;
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t0; t < ntiles; ++t) {
     // tiles t + 1 .. t + NBUF - 2 may stay in flight
     const int later = ntiles - 1 - t;
     if (NB_ >= 4 && later >= 2) vm_wait<(NB_ >= 4 ? 2 : 1) * T::DPT>();
@@ -624,7 +650,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
     __builtin_amdgcn_s_barrier();
     if (t + NB_ - 1 < ntiles) issue(t + NB_ - 1, b == 0 ? NB_ - 1 : b - 1);
     const int kt = t * kPfKeys;
-    compute((uint32_t)(b * T::BUF), kt, kt + kPfKeys - 1 > ctx + q0);
+    compute((uint32_t)(b * T::BUF), kt, needs_mask(kt));
     b = b == NB_ - 1 ? 0 : b + 1;
   }
 

@@ -31,7 +31,7 @@ EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
            "pa_bp_free_blocks", "pa_bp_touch", "pa_bp_cache_block", "pa_bp_lookup",
            "pa_hash_block_tokens", "pa_bp_allocate_request", "pa_bp_cache_request",
            "pa_bp_append_slots", "pa_bp_free_request", "pa_bp_request_blocks",
-           "pa_bp_fork_request", "pa_bp_prepare_write")
+           "pa_bp_fork_request", "pa_bp_prepare_write", "pa_bp_remove_skipped_blocks")
 
 
 class PaError(RuntimeError):
@@ -46,7 +46,7 @@ class pa_kv_pool(C.Structure):
         ("num_blocks", C.c_int64), ("block_stride_bytes", C.c_int64),
         ("block_size", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
         ("dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
-        ("flags", C.c_uint32), ("reserved", C.c_uint32),
+        ("flags", C.c_uint32), ("sliding_window", C.c_int32),
         ("k_head_scales", C.c_void_p), ("v_head_scales", C.c_void_p),
     ]
 
@@ -117,7 +117,7 @@ class KVPool:
                  v_scale: float = 1.0, num_blocks: Optional[int] = None,
                  block_stride_bytes: int = 0, shared_blocks: bool = False,
                  k_head_scales: Optional[torch.Tensor] = None,
-                 v_head_scales: Optional[torch.Tensor] = None):
+                 v_head_scales: Optional[torch.Tensor] = None, sliding_window: int = 0):
         """k_head_scales / v_head_scales: optional device float32 [num_kv_heads]
         fp8 scales, one per KV head (replacing k_scale / v_scale)."""
         self.k, self.v = k, v
@@ -134,7 +134,8 @@ class KVPool:
         self.desc = pa_kv_pool(k.data_ptr(), v.data_ptr(), self.num_blocks,
                                self.block_stride_bytes, block_size, num_kv_heads, head_dim,
                                _DTYPES[kv_dtype], self.k_scale, self.v_scale,
-                               PA_POOL_SHARED_BLOCKS if shared_blocks else 0, 0, khp, vhp)
+                               PA_POOL_SHARED_BLOCKS if shared_blocks else 0,
+                               int(sliding_window), khp, vhp)
 
     @property
     def shared_blocks(self) -> bool:
@@ -150,7 +151,7 @@ class KVPool:
                  kv_dtype: str = "f16", k_scale: float = 1.0, v_scale: float = 1.0,
                  device="cuda", fill_bits: Optional[int] = None,
                  shared_blocks: bool = False, k_head_scales=None,
-                 v_head_scales=None) -> "KVPool":
+                 v_head_scales=None, sliding_window: int = 0) -> "KVPool":
         tdt = torch.int16 if kv_dtype == "f16" else torch.uint8
         shape = (num_blocks, block_size, num_kv_heads, head_dim)
         k = torch.empty(shape, dtype=tdt, device=device)
@@ -165,7 +166,8 @@ class KVPool:
             khs = torch.as_tensor(k_head_scales, dtype=torch.float32).to(device).contiguous()
             vhs = torch.as_tensor(v_head_scales, dtype=torch.float32).to(device).contiguous()
         return cls(k, v, block_size, num_kv_heads, head_dim, kv_dtype, k_scale, v_scale,
-                   shared_blocks=shared_blocks, k_head_scales=khs, v_head_scales=vhs)
+                   shared_blocks=shared_blocks, k_head_scales=khs, v_head_scales=vhs,
+                   sliding_window=sliding_window)
 
     @property
     def elem_bytes(self) -> int:
@@ -285,6 +287,7 @@ def _bind_block_pool(L) -> None:
         "pa_bp_request_blocks": (I32, [P, I64, IP, I32]),
         "pa_bp_fork_request": (C.c_int, [P, I64, I64]),
         "pa_bp_prepare_write": (C.c_int, [P, I64, I32, LP]),
+        "pa_bp_remove_skipped_blocks": (I32, [P, I64, I32, I32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -404,6 +407,12 @@ class BlockPool:
 
     def fork_request(self, parent: int, child: int) -> None:
         self._ok(self._L.pa_bp_fork_request(self._p, int(parent), int(child)))
+
+    def remove_skipped_blocks(self, rid: int, num_tokens: int, window: int) -> int:
+        """Release the request's blocks that lie wholly before the sliding
+        window of its next query; returns how many were released."""
+        return self._ok(self._L.pa_bp_remove_skipped_blocks(self._p, int(rid), int(num_tokens),
+                                                            int(window)))
 
     def prepare_write(self, rid: int, position: int) -> Optional[tuple]:
         """(src, dst) for pa_copy_blocks when the block is shared, else None."""

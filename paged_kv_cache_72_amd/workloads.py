@@ -337,6 +337,12 @@ def llama3_8b_b64(seed: int = 7202) -> Workload:
     return _independent("llama3_8b_b64", seed, lens.tolist(), 32, 8, 128, 16, 20000)
 
 
+def llama3_8b_b64_w1024(seed: int = 7202) -> Workload:
+    """The Llama-3-8B-shaped batch of 64 as a sliding-window layer with a
+    1,024-token window: each query reads only its last 1,024 positions."""
+    return dataclasses.replace(llama3_8b_b64(seed), name="llama3_8b_b64_w1024", window=1024)
+
+
 def qwen25_7b_8k(seed: int = 7203) -> Workload:
     """Qwen2.5-7B-shaped decode at full context: 13 sequences x 8192 tokens
     (512 blocks each); 28 query / 4 KV heads (GQA 7), head_dim 128, block_size
@@ -514,6 +520,7 @@ CONFIGS = {
     "prefix_share_bs8": lambda: prefix_share(8),
     "long_fp8": long_fp8,
     "long_e5m2": long_e5m2,
+    "llama3_8b_b64_w1024": llama3_8b_b64_w1024,
 }
 
 

@@ -178,7 +178,9 @@ def test_pool_flags_validated(so):
         L.PLAN_FLAT
     assert so.pa_decode_plan(C.byref(_pool(flags=2)), 4, 32, 100, 0) == L.PA_ERR_INVALID_ARG
     assert "flags" in L.pa_last_error()
-    assert so.pa_decode_plan(C.byref(_pool(reserved=1)), 4, 32, 100, 0) == L.PA_ERR_INVALID_ARG
+    assert so.pa_decode_plan(C.byref(_pool(sliding_window=-1)), 4, 32, 100, 0) == \
+        L.PA_ERR_INVALID_ARG
+    assert so.pa_decode_plan(C.byref(_pool(sliding_window=4096)), 4, 32, 100, 0) >= 0
 
 
 def test_plan_falls_back_past_flat_limit(so):

@@ -171,3 +171,31 @@ def test_errors_change_nothing():
         assert _state(pool) == before
     with pytest.raises(L.PaError):
         L.BlockPool(0, 16)
+
+
+def test_sliding_window_release_matches_the_model():
+    bs, win = 4, 9
+    nat, mod = L.BlockPool(16, bs), BlockPoolModel(16, bs)
+    toks = _tokens(10, 60)
+    for p in (nat, mod):
+        p.allocate_request(1, toks)
+    n = len(toks)
+    released = []
+    for step in range(12):
+        n += 1
+        mod.append_slot(1, n)
+        nat.append_slots(1, n)
+        a = mod.remove_skipped_blocks(1, n, win)
+        b = nat.remove_skipped_blocks(1, n, win)
+        assert a == b
+        released.append(a)
+        assert nat.request_blocks(1) == mod.requests[1]
+        assert _state(nat) == _model_state(mod)
+        # every block still listed covers a position the next query may see
+        first = n - win + 1
+        for j, blk in enumerate(mod.requests[1]):
+            assert (blk < 0) == ((j + 1) * bs <= first)
+    assert sum(released) > 0
+    nat.free_request(1)
+    mod.free_request(1)
+    assert _state(nat) == _model_state(mod) and nat.num_free() == 16

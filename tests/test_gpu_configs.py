@@ -28,6 +28,7 @@ CONFIGS = [
     ("prefix_share_bs8", lambda: W.prefix_share(8), 48, [0, -1, 256]),
     ("long_fp8", W.long_fp8, 6, [0, 512]),
     ("long_e5m2", W.long_e5m2, 6, [0, 512]),
+    ("llama3_8b_b64_w1024", W.llama3_8b_b64_w1024, 12, [0, -1, 256]),
 ]
 
 

@@ -167,3 +167,29 @@ def test_cache_policy_flag_changes_no_bits(name, part):
     b = dc.decode(part, out=torch.empty_like(a))
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def _with_window(w, win, poison_outside=False):
+    """Sliding-window copy of w; with poison_outside, every table entry wholly
+    before a sequence's window points at the NaN padding block (released)."""
+    w2 = dataclasses.replace(w, window=win, block_tables=w.block_tables.copy())
+    if poison_outside:
+        bs = w.block_size
+        for s in range(w.num_seqs):
+            n = int(w.seq_lens[s])
+            first = max(0, n - win)
+            w2.block_tables[s, :first // bs] = w.pad_block
+    return w2
+
+
+@pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "fp8_d128_bs32", "d64_bs128_g2",
+                                  "e5m2h_d64_bs32_g2"])
+@pytest.mark.parametrize("win", [1, 15, 16, 17, 100, 1000])
+@pytest.mark.parametrize("part", [-1, 0, 16, 512])
+def test_sliding_window_decode(name, win, part):
+    w0, _ = _case(name)
+    w = _with_window(w0, win, poison_outside=True)
+    say(f"window {win} {name} partition={part}")
+    y = DeviceCase(w, poison=True).decode(part).cpu().numpy()
+    r = O.decode(oracle_pool(w, poison=True), w.q, w.block_tables, w.seq_lens, w.scale)
+    check_close(w, y, r, f"window{win}/{name}/p{part}")

@@ -129,3 +129,22 @@ def test_prefill_full_size_sampled(name, make, nrows):
     idx = prefill_row_index(w, rows)
     st = check_close(w, y[idx], r[idx], name)
     say(f"  {st}")
+
+
+@pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "d64_bs16_g16",
+                                  "d128_bs16_g4_e4m3"])
+@pytest.mark.parametrize("win", [1, 31, 32, 33, 100])
+def test_sliding_window_prefill(name, win):
+    w0 = SHAPES[name]()
+    w = dataclasses.replace(w0, window=win, block_tables=w0.block_tables.copy())
+    # blocks wholly before the window of a sequence's first new token are
+    # never read: point them at the NaN padding block
+    bs = w.block_size
+    for s in range(w.num_seqs):
+        first = max(0, int(w.seq_lens[s]) - int(w.q_lens[s]) - win + 1)
+        w.block_tables[s, :first // bs] = w.pad_block
+    say(f"prefill window {win} {name}")
+    y = DeviceCase(w, poison=True).prefill().cpu().numpy()
+    r = O.prefill(oracle_pool(w, poison=True), w.q, w.q_start, w.block_tables, w.seq_lens,
+                  w.scale)
+    check_close(w, y, r, f"prefill window{win}/{name}")
