@@ -32,8 +32,8 @@ int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
   if (!p) return fail(PA_ERR_INVALID_ARG, "pool descriptor is NULL");
   if (!p->k_base || !p->v_base) return fail(PA_ERR_INVALID_ARG, "pool k_base/v_base is NULL");
-  if (p->head_dim != 64 && p->head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", p->head_dim);
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128, 256)", p->head_dim);
   if (p->block_size != 8 && p->block_size != 16 && p->block_size != 32 && p->block_size != 64 &&
       p->block_size != 128)
     return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (8, 16, 32, 64, 128)",
@@ -330,6 +330,9 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
   if (total_q < 0) return fail(PA_ERR_INVALID_ARG, "total_q %d < 0", total_q);
   if (max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "max_q_len %d < 0", max_q_len);
+  if (g.head_dim > 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill supports head_dim 64 and 128 (got %d)",
+                g.head_dim);
   if (num_q_heads < 1 || num_q_heads % g.num_kv_heads)
     return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
                 num_q_heads, g.num_kv_heads);

@@ -76,12 +76,17 @@ namespace {
 
 template <int BYTES> struct Vec;
 template <> struct Vec<16> { typedef uint4 T; };
+struct u32x8 { uint4 lo, hi; };               // a lane's 32-byte value row (head_dim 256)
+template <> struct Vec<32> { typedef u32x8 T; };
 template <> struct Vec<8> { typedef uint2 T; };
 template <> struct Vec<4> { typedef uint32_t T; };
 
 template <int BYTES>
 __device__ __forceinline__ void vec_words(const typename Vec<BYTES>::T& v, uint32_t* w) {
-  if constexpr (BYTES == 16) { w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; }
+  if constexpr (BYTES == 32) {
+    w[0] = v.lo.x; w[1] = v.lo.y; w[2] = v.lo.z; w[3] = v.lo.w;
+    w[4] = v.hi.x; w[5] = v.hi.y; w[6] = v.hi.z; w[7] = v.hi.w;
+  } else if constexpr (BYTES == 16) { w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; }
   else if constexpr (BYTES == 8) { w[0] = v.x; w[1] = v.y; }
   else { w[0] = v; }
 }
@@ -224,7 +229,10 @@ struct Engine {
   __device__ __forceinline__ VT ld_v(__amdgpu_buffer_rsrc_t R, int k) const {
     // value load k: rows 4k .. 4k+3 of the tile (lane: row 4k + r, chunk c)
     const int so = (BS >= 16 ? 4 * k : ((4 * k) & 7)) * rs;
-    if constexpr (VB == 16)
+    if constexpr (VB == 32)
+      return u32x8{__builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, voff, so, CPOL)),
+                   __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, voff, so + 16, CPOL))};
+    else if constexpr (VB == 16)
       return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, voff, so, CPOL));
     else if constexpr (VB == 8)
       return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R, voff, so, CPOL));
@@ -385,10 +393,16 @@ struct Engine {
         _Float16 o[DCH];
 #pragma unroll
         for (int e = 0; e < DCH; ++e) o[e] = (_Float16)(acc[e][i] * inv);
-        if constexpr (DCH == 8)
+        if constexpr (DCH == 16) {
+          uint4* d16 = (uint4*)(dst + (int64_t)h * D + c * DCH);
+          const u32x8 w = __builtin_bit_cast(u32x8, o);
+          d16[0] = w.lo;
+          d16[1] = w.hi;
+        } else if constexpr (DCH == 8) {
           *(uint4*)(dst + (int64_t)h * D + c * DCH) = __builtin_bit_cast(uint4, o);
-        else
+        } else {
           *(uint2*)(dst + (int64_t)h * D + c * DCH) = __builtin_bit_cast(uint2, o);
+        }
       }
     }
   }
@@ -415,7 +429,8 @@ struct Engine {
 // ---------------------------------------------------------------- single / split
 
 template <int D, int BS, int KV, int NW, bool SPLIT, bool NT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU, 8)))
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : PA_WAVES_PER_EU, 8)))
 void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
                    const int32_t* __restrict__ lens) {
   // The tables arrive as restrict arguments so that their uniform reads stay
@@ -617,7 +632,8 @@ __device__ __forceinline__ int range_of(int64_t t, int64_t T, int64_t NR) {
 // range (slot 0: the range's first sequence, slot 1: its last), merged by
 // flat_merge_kernel.
 template <int D, int BS, int KV, int NW, bool NT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_FLAT_WAVES_PER_EU, 8)))
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : PA_FLAT_WAVES_PER_EU, 8)))
 void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ tables,
                         const int32_t* __restrict__ lens, const _Float16* __restrict__ qs,
                         _Float16* __restrict__ outs, float* __restrict__ slots,
@@ -931,6 +947,8 @@ hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seq
     return launch_d<128>(a, f, num_seqs, block_size, kv, stream_kv, mode, stream);
   if (head_dim == 64)
     return launch_d<64>(a, f, num_seqs, block_size, kv, stream_kv, mode, stream);
+  if (head_dim == 256)
+    return launch_d<256>(a, f, num_seqs, block_size, kv, stream_kv, mode, stream);
   return hipErrorInvalidValue;
 }
 

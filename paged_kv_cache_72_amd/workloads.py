@@ -343,6 +343,18 @@ def llama3_8b_b64_w1024(seed: int = 7202) -> Workload:
     return dataclasses.replace(llama3_8b_b64(seed), name="llama3_8b_b64_w1024", window=1024)
 
 
+def hybrid_d256_b64(seed: int = 7208) -> Workload:
+    """A full-attention layer of a hybrid model with head_dim 256 and 4 KV
+    heads, the shape of the pages' hybrid example ("Paging saves no KV bytes",
+    section 5), at the batch of llama3_8b_b64: 64 sequences, lengths uniform in
+    [512, 4096]; 16 query heads (GQA 4: the pages give no query-head count),
+    block_size 16, fp16, 20,000-block pool.  4 KiB of K and V per token, as
+    for Llama-3-8B."""
+    ss = np.random.SeedSequence(seed).spawn(6)
+    lens = np.random.default_rng(ss[0]).integers(512, 4096, size=64, endpoint=True)
+    return _independent("hybrid_d256_b64", seed, lens.tolist(), 16, 4, 256, 16, 20000)
+
+
 def qwen25_7b_8k(seed: int = 7203) -> Workload:
     """Qwen2.5-7B-shaped decode at full context: 13 sequences x 8192 tokens
     (512 blocks each); 28 query / 4 KV heads (GQA 7), head_dim 128, block_size
@@ -521,6 +533,7 @@ CONFIGS = {
     "long_fp8": long_fp8,
     "long_e5m2": long_e5m2,
     "llama3_8b_b64_w1024": llama3_8b_b64_w1024,
+    "hybrid_d256_b64": hybrid_d256_b64,
 }
 
 

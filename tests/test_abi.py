@@ -159,7 +159,8 @@ def test_flat_wave_count_follows_tile_bytes(so):
     workspace holds two records per wave, so its size shows the wave count."""
     S, Hq, T = 64, 32, 4096
     for D, dt, waves in ((128, L.PA_KV_F16, 1024), (128, L.PA_KV_FP8_E4M3FN, 2048),
-                         (64, L.PA_KV_F16, 2048), (64, L.PA_KV_FP8_E4M3FN, 2048)):
+                         (64, L.PA_KV_F16, 2048), (64, L.PA_KV_FP8_E4M3FN, 2048),
+                         (256, L.PA_KV_F16, 1024), (256, L.PA_KV_FP8_E4M3FN, 1024)):
         p = _pool(head_dim=D, dtype=dt, k_scale=0.5, v_scale=0.5)
         ranges = min(waves // 8, S * (T // 16) // 8)
         pre = (S + 1) * 4
@@ -201,6 +202,8 @@ def _prefill(so, pool, T=10, S=2, Hq=32, maxq=8, **kw):
 def test_prefill_validation(so):
     assert _prefill(so, None) == L.PA_ERR_INVALID_ARG
     assert _prefill(so, _pool(head_dim=96)) == L.PA_ERR_UNSUPPORTED
+    assert _prefill(so, _pool(head_dim=256)) == L.PA_ERR_UNSUPPORTED      # decode only
+    assert "head_dim" in L.pa_last_error()
     assert _prefill(so, _pool(), Hq=30) == L.PA_ERR_INVALID_ARG          # 30 % 8 != 0
     assert _prefill(so, _pool(num_kv_heads=1), Hq=32) == L.PA_ERR_UNSUPPORTED
     assert _prefill(so, _pool(), S=-1) == L.PA_ERR_INVALID_ARG

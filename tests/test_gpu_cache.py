@@ -23,6 +23,9 @@ pytestmark = pytest.mark.gpu
                                         kv_dtype="fp8_e4m3fn", scale_grain="head")),
     ("d64_e5m2_head", lambda: W.custom("c", 48, [17, 40], 8, 4, 64, 16, kv_dtype="fp8_e5m2",
                                        scale_grain="head")),
+    ("d256_bs16", lambda: W.custom("c", 49, [5, 64, 300], 16, 4, 256, 16)),
+    ("d256_e4m3_head", lambda: W.custom("c", 50, [17, 200], 16, 4, 256, 32,
+                                        kv_dtype="fp8_e4m3fn", scale_grain="head")),
 ])
 @pytest.mark.parametrize("poison", [False, True])
 def test_scatter_bit_exact(name, make, poison):

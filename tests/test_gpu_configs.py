@@ -1,4 +1,4 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration
+"""GPU parity at the listed workloads' full sizes, in the launch configuration
 the benchmark uses (the library's own partition choice) and in the forced
 single and split passes.  The oracle evaluates a seeded sample of
 (sequence, KV head) units -- all their query heads -- plus the shortest and
@@ -29,6 +29,7 @@ CONFIGS = [
     ("long_fp8", W.long_fp8, 6, [0, 512]),
     ("long_e5m2", W.long_e5m2, 6, [0, 512]),
     ("llama3_8b_b64_w1024", W.llama3_8b_b64_w1024, 12, [0, -1, 256]),
+    ("hybrid_d256_b64", W.hybrid_d256_b64, 12, [0, -1, 256]),
 ]
 
 

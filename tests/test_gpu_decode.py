@@ -44,6 +44,13 @@ SHAPES = {
                                           kv_dtype="fp8_e4m3fn", scale_grain="head"),
     "e5m2h_d64_bs32_g2": lambda: W.custom("s", 69, EDGE_LENS, 8, 4, 64, 32, kv_dtype="fp8_e5m2",
                                           scale_grain="head"),
+    # head_dim 256 with 4 KV heads, the full-attention layers of the pages' hybrid
+    # model example ("Paging saves no KV bytes", section 5)
+    "d256_bs16_g4": lambda: W.custom("s", 70, EDGE_LENS, 16, 4, 256, 16),
+    "fp8_d256_bs32_g2": lambda: W.custom("s", 71, EDGE_LENS, 8, 4, 256, 32,
+                                         kv_dtype="fp8_e4m3fn"),
+    "e5m2h_d256_bs8_g8": lambda: W.custom("s", 72, EDGE_LENS, 16, 2, 256, 8, kv_dtype="fp8_e5m2",
+                                          scale_grain="head"),
 }
 
 _cache = {}
@@ -74,7 +81,7 @@ def test_decode_matches_oracle(name, part):
 
 
 @pytest.mark.parametrize("name", ["tiny", "d128_bs8_g7", "fp8_d128_bs32", "d64_bs32_g16",
-                                  "e5m2_d128_bs16_g4", "fp8h_d128_bs16_g4"])
+                                  "e5m2_d128_bs16_g4", "fp8h_d128_bs16_g4", "d256_bs16_g4"])
 @pytest.mark.parametrize("variant", ["v_offset", "needles"])
 @pytest.mark.parametrize("part", [-1, 1, 64])
 def test_structured_variants(name, variant, part):
@@ -100,7 +107,7 @@ def _relabel(w, seed):
 
 
 @pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "fp8_d128_bs32",
-                                  "e5m2_d64_bs8_g4"])
+                                  "e5m2_d64_bs8_g4", "fp8_d256_bs32_g2"])
 @pytest.mark.parametrize("part", [-1, 1, 64])
 def test_physical_relabelling_is_bitwise_invariant(name, part):
     w, _ = _case(name)
@@ -183,7 +190,7 @@ def _with_window(w, win, poison_outside=False):
 
 
 @pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "fp8_d128_bs32", "d64_bs128_g2",
-                                  "e5m2h_d64_bs32_g2"])
+                                  "e5m2h_d64_bs32_g2", "d256_bs16_g4"])
 @pytest.mark.parametrize("win", [1, 15, 16, 17, 100, 1000])
 @pytest.mark.parametrize("part", [-1, 0, 16, 512])
 def test_sliding_window_decode(name, win, part):
