@@ -15,6 +15,14 @@ namespace {
 
 thread_local std::string g_last_error;
 
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+namespace pa {
+
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -25,11 +33,7 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
+int check_pool(const pa_kv_pool* p, PoolGeom* g) {
   if (!p) return fail(PA_ERR_INVALID_ARG, "pool descriptor is NULL");
   if (!p->k_base || !p->v_base) return fail(PA_ERR_INVALID_ARG, "pool k_base/v_base is NULL");
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
@@ -90,6 +94,13 @@ int check_pool(const pa_kv_pool* p, pa::PoolGeom* g) {
   if (g->k_hs) g->k_scale = g->v_scale = 1.f;
   return PA_OK;
 }
+
+}  // namespace pa
+
+using pa::check_pool;
+using pa::fail;
+
+namespace {
 
 // Planning.  The flat schedule balances any mix of context lengths, so it is
 // the default unless the batch is many short contexts; it keeps per-sequence

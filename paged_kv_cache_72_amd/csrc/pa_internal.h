@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
 
 // Resolved geometry of one pool, computed on the host from pa_kv_pool.
@@ -106,6 +108,11 @@ struct PrefillArgs {
   const float* v_hs;
   int32_t window;             // sliding window (0: none): position p sees p - window + 1 .. p
 };
+
+// Sets the calling thread's pa_last_error() message and returns code.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Validates a pool descriptor and resolves its geometry (PA_OK or a status).
+int check_pool(const pa_kv_pool* p, PoolGeom* g);
 
 // Query rows (token, head pairs) one prefill workgroup covers.
 int prefill_rows_per_workgroup();

@@ -3,6 +3,11 @@
 Argument marshalling only -- every step of the path runs in the library's HIP
 kernels.  PyTorch provides device memory and the stream.  Loading fails
 loudly if libpa.so has not been built; there is no fallback.
+
+With PA_CHECK_INPUTS=1 in the environment (or CHECK_INPUTS set to True), the
+compute calls first run the matching device-argument check of
+include/pa_check.h and raise PaError instead of launching on bad tables,
+lengths, slots or pairs.  Each check waits for the stream: a debugging aid.
 """
 from __future__ import annotations
 
@@ -31,7 +36,12 @@ EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
            "pa_bp_free_blocks", "pa_bp_touch", "pa_bp_cache_block", "pa_bp_lookup",
            "pa_hash_block_tokens", "pa_bp_allocate_request", "pa_bp_cache_request",
            "pa_bp_append_slots", "pa_bp_free_request", "pa_bp_request_blocks",
-           "pa_bp_fork_request", "pa_bp_prepare_write", "pa_bp_remove_skipped_blocks")
+           "pa_bp_fork_request", "pa_bp_prepare_write", "pa_bp_remove_skipped_blocks",
+           # device-argument checks (include/pa_check.h)
+           "pa_check_scratch_bytes", "pa_check_decode_inputs", "pa_check_prefill_inputs",
+           "pa_check_slot_mapping", "pa_check_block_mapping")
+
+CHECK_INPUTS = os.environ.get("PA_CHECK_INPUTS", "") not in ("", "0")
 
 
 class PaError(RuntimeError):
@@ -78,6 +88,17 @@ def load() -> C.CDLL:
         L.pa_prefill.argtypes = [PP, P, P, I32, P, I32, I32, P, I32, P, I32, C.c_float, P]
         L.pa_last_error.restype = C.c_char_p
         L.pa_last_error.argtypes = []
+        SZ = C.c_size_t
+        L.pa_check_scratch_bytes.restype = SZ
+        L.pa_check_scratch_bytes.argtypes = [PP]
+        L.pa_check_decode_inputs.restype = C.c_int
+        L.pa_check_decode_inputs.argtypes = [PP, I32, P, I32, P, I32, P, SZ, P]
+        L.pa_check_prefill_inputs.restype = C.c_int
+        L.pa_check_prefill_inputs.argtypes = [PP, I32, P, I32, P, I32, P, I32, P, SZ, P]
+        L.pa_check_slot_mapping.restype = C.c_int
+        L.pa_check_slot_mapping.argtypes = [PP, P, I64, P, SZ, P]
+        L.pa_check_block_mapping.restype = C.c_int
+        L.pa_check_block_mapping.argtypes = [PP, P, I64, P, SZ, P]
         _bind_block_pool(L)
         _lib = L
     return _lib
@@ -179,6 +200,8 @@ def pa_reshape_and_cache(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
     T = int(slot_mapping.numel())
     if k_new.shape != (T, pool.num_kv_heads, pool.head_dim) or v_new.shape != k_new.shape:
         raise ValueError("k_new/v_new must be [num_tokens, num_kv_heads, head_dim]")
+    if CHECK_INPUTS:
+        pa_check_slot_mapping(pool, slot_mapping, stream)
     _check(load().pa_reshape_and_cache(
         C.byref(pool.desc), _dev(k_new, torch.float16, "k_new"),
         _dev(v_new, torch.float16, "v_new"), _dev(slot_mapping, torch.int64, "slot_mapping"),
@@ -188,6 +211,8 @@ def pa_reshape_and_cache(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
 def pa_copy_blocks(pool: KVPool, block_mapping: torch.Tensor, stream=None) -> None:
     if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [num_pairs, 2]")
+    if CHECK_INPUTS:
+        pa_check_block_mapping(pool, block_mapping, stream)
     _check(load().pa_copy_blocks(C.byref(pool.desc),
                                  _dev(block_mapping, torch.int64, "block_mapping"),
                                  int(block_mapping.shape[0]), _stream(stream)))
@@ -227,6 +252,8 @@ def pa_decode(pool: KVPool, out: torch.Tensor, q: torch.Tensor, block_tables: to
     if workspace is not None:
         ws_ptr, ws_bytes = _dev(workspace, workspace.dtype, "workspace"), workspace.numel() * \
             workspace.element_size()
+    if CHECK_INPUTS:
+        pa_check_decode_inputs(pool, block_tables, seq_lens, max_seq_len, stream)
     _check(load().pa_decode(
         C.byref(pool.desc), _dev(out, torch.float16, "out"), _dev(q, torch.float16, "q"), S, Hq,
         _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
@@ -246,12 +273,66 @@ def pa_prefill(pool: KVPool, out: torch.Tensor, q: torch.Tensor, q_start: torch.
         raise ValueError("out must have q's shape [total_q, num_q_heads, head_dim]")
     if q_start.shape != (S + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != S:
         raise ValueError("q_start must be [num_seqs + 1], block_tables [num_seqs, max_blocks]")
+    if CHECK_INPUTS:
+        pa_check_prefill_inputs(pool, q_start, block_tables, seq_lens, T, max_q_len, stream)
     _check(load().pa_prefill(
         C.byref(pool.desc), _dev(out, torch.float16, "out"), _dev(q, torch.float16, "q"), T,
         _dev(q_start, torch.int32, "q_start"), S, Hq,
         _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
         _dev(seq_lens, torch.int32, "seq_lens"), int(max_q_len), C.c_float(scale),
         _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# device-argument checks (include/pa_check.h)
+
+def pa_check_scratch_bytes(pool: KVPool) -> int:
+    return int(load().pa_check_scratch_bytes(C.byref(pool.desc)))
+
+
+def _scratch(pool: KVPool):
+    """The pool's check scratch (allocated on first use, kept with the pool)."""
+    n = pa_check_scratch_bytes(pool)
+    t = getattr(pool, "_check_scratch", None)
+    if t is None or t.numel() < n:
+        t = torch.empty(max(n, 256), dtype=torch.uint8, device=pool.k.device)
+        pool._check_scratch = t
+    return t.data_ptr(), t.numel()
+
+
+def pa_check_decode_inputs(pool: KVPool, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                           max_seq_len: int, stream=None) -> None:
+    S = int(seq_lens.shape[0])
+    sp, sn = _scratch(pool)
+    _check(load().pa_check_decode_inputs(
+        C.byref(pool.desc), S, _dev(block_tables, torch.int32, "block_tables"),
+        int(block_tables.shape[1]), _dev(seq_lens, torch.int32, "seq_lens"), int(max_seq_len),
+        sp, sn, _stream(stream)))
+
+
+def pa_check_prefill_inputs(pool: KVPool, q_start: torch.Tensor, block_tables: torch.Tensor,
+                            seq_lens: torch.Tensor, total_q: int, max_q_len: int,
+                            stream=None) -> None:
+    S = int(seq_lens.shape[0])
+    sp, sn = _scratch(pool)
+    _check(load().pa_check_prefill_inputs(
+        C.byref(pool.desc), int(total_q), _dev(q_start, torch.int32, "q_start"), S,
+        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+        _dev(seq_lens, torch.int32, "seq_lens"), int(max_q_len), sp, sn, _stream(stream)))
+
+
+def pa_check_slot_mapping(pool: KVPool, slot_mapping: torch.Tensor, stream=None) -> None:
+    sp, sn = _scratch(pool)
+    _check(load().pa_check_slot_mapping(
+        C.byref(pool.desc), _dev(slot_mapping, torch.int64, "slot_mapping"),
+        int(slot_mapping.numel()), sp, sn, _stream(stream)))
+
+
+def pa_check_block_mapping(pool: KVPool, block_mapping: torch.Tensor, stream=None) -> None:
+    sp, sn = _scratch(pool)
+    _check(load().pa_check_block_mapping(
+        C.byref(pool.desc), _dev(block_mapping, torch.int64, "block_mapping"),
+        int(block_mapping.shape[0]), sp, sn, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -237,3 +237,40 @@ def test_per_head_scale_fields_validated(so):
     # accepted for fp8 pools: the call then fails only on the missing workspace
     assert _decode(so, _pool(**fp8, k_head_scales=FAKE, v_head_scales=FAKE + 64), part=1,
                    max_len=4096) == L.PA_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------- device-argument checks
+
+def test_check_scratch_bytes(so):
+    # a 256-byte report plus one bit per pool slot (or two bits per block)
+    p = _pool(num_blocks=1000, block_size=16)
+    assert so.pa_check_scratch_bytes(C.byref(p)) == (256 + 4 * (16000 // 32) + 255) // 256 * 256
+    p = _pool(num_blocks=1, block_size=8)
+    assert so.pa_check_scratch_bytes(C.byref(p)) == 512
+    assert so.pa_check_scratch_bytes(None) == 0
+    assert so.pa_check_scratch_bytes(C.byref(_pool(head_dim=96))) == 0
+
+
+def test_check_calls_validate_on_the_host(so):
+    p = _pool()
+    need = so.pa_check_scratch_bytes(C.byref(p))
+    dec = lambda pool=C.byref(p), S=4, sc=FAKE, n=need, maxb=64: so.pa_check_decode_inputs(
+        pool, S, FAKE, maxb, FAKE, 100, sc, n, None)
+    assert dec(pool=None) == L.PA_ERR_INVALID_ARG
+    assert dec(sc=None) == L.PA_ERR_INVALID_ARG
+    assert dec(sc=FAKE + 4) == L.PA_ERR_ALIGNMENT
+    assert dec(n=need - 1) == L.PA_ERR_WORKSPACE and "scratch" in L.pa_last_error()
+    assert dec(S=-1) == L.PA_ERR_INVALID_ARG
+    assert dec(maxb=0) == L.PA_ERR_INVALID_ARG
+    assert dec(S=0) == L.PA_OK                       # nothing to check, nothing launched
+    assert so.pa_check_prefill_inputs(C.byref(p), 10, None, 2, FAKE, 64, FAKE, 8, FAKE, need,
+                                      None) == L.PA_ERR_INVALID_ARG
+    assert so.pa_check_prefill_inputs(C.byref(p), -1, FAKE, 2, FAKE, 64, FAKE, 8, FAKE, need,
+                                      None) == L.PA_ERR_INVALID_ARG
+    assert so.pa_check_slot_mapping(C.byref(p), None, 5, FAKE, need, None) == L.PA_ERR_INVALID_ARG
+    assert so.pa_check_slot_mapping(C.byref(p), FAKE, -1, FAKE, need, None) == \
+        L.PA_ERR_INVALID_ARG
+    assert so.pa_check_slot_mapping(C.byref(p), FAKE, 0, FAKE, need, None) == L.PA_OK
+    assert so.pa_check_block_mapping(C.byref(p), None, 3, FAKE, need, None) == \
+        L.PA_ERR_INVALID_ARG
+    assert so.pa_check_block_mapping(C.byref(p), FAKE, 0, FAKE, need, None) == L.PA_OK
