@@ -424,6 +424,17 @@ __device__ __forceinline__ void lgkm_wait_all_regs() {
   asm volatile("s_waitcnt lgkmcnt(%0)" : : "i"(N) : "memory");
 }
 
+// Maxima of scores without the quieting of signalling NaNs that fmaxf adds
+// to each MFMA result (one extra instruction per input); the scores here are
+// never NaN (masked entries are -inf, loaded rows are finite).
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   // vmcnt(N), expcnt and lgkmcnt unchanged (gfx9 encoding: vmcnt low bits
@@ -495,6 +506,17 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
   // first position (finite data; masked out of every score).
   const char* const kbase = a.k + (int64_t)kh * D * 2;
   const char* const vbase = a.v + (int64_t)kh * D * 2;
+  // Block ids of the NI load groups of the next tile to issue, read one tile
+  // ahead (and range-clamped only when used) so that the scalar loads'
+  // latency passes behind a tile's compute.  A group's RPI rows lie in one
+  // block (RPI divides block_size), also when its positions are clamped.
+  auto group_block = [&](int t, int i) {
+    const int r0 = (wid * T::NI + i) * T::RPI;
+    const int pr0 = t * kPfKeys + r0 < lo_c ? lo_c : t * kPfKeys + r0;
+    const int pu = uni(pr0 < kv_end ? pr0 : kv_end - 1);
+    return bt[(uint32_t)pu / BS];
+  };
+  int next_blk[T::NI];
   auto issue = [&](int t, int b) {
     const int kt = t * kPfKeys;
 #pragma unroll
@@ -503,20 +525,24 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
       const int r = r0 + lane / CPR, pch = lane % CPR;
       // positions are clamped into [lo_c, kv_end - 1]: outside rows repeat an
       // in-window row (finite data, masked), never a released block
-      const int pr0 = kt + r0 < lo_c ? lo_c : kt + r0;
-      const int pu = uni(pr0 < kv_end ? pr0 : kv_end - 1);
-      int blk = bt[pu / BS];
-      blk = blk < 0 ? 0 : (blk > a.num_blocks_m1 ? a.num_blocks_m1 : blk);
       const int pr = kt + r < lo_c ? lo_c : kt + r;
       const int pos = pr < kv_end ? pr : kv_end - 1;
-      const int64_t row_off = (int64_t)blk * a.block_stride + (int64_t)(pos % BS) * a.row_stride;
+      // block base (uniform) plus a 32-bit per-lane offset inside the block
+      const int raw = next_blk[i];
+      const int blk = raw < 0 ? 0 : (raw > a.num_blocks_m1 ? a.num_blocks_m1 : raw);
+      const int64_t blk_off = (int64_t)blk * a.block_stride;
+      const uint32_t in_blk = ((uint32_t)pos & (BS - 1)) * (uint32_t)a.row_stride;
       lds_char* kdst = lds0 + b * T::BUF + r0 * RB;
       lds_char* vdst = kdst + T::TILE;
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + row_off + ((pch ^ T::ksw(r)) << 4)),
-                                       (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + row_off + ((pch ^ T::vsw(r)) << 4)),
-                                       (__attribute__((address_space(3))) void*)vdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(kbase + blk_off + (in_blk + ((uint32_t)(pch ^ T::ksw(r)) << 4))),
+          (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(vbase + blk_off + (in_blk + ((uint32_t)(pch ^ T::vsw(r)) << 4))),
+          (__attribute__((address_space(3))) void*)vdst, 16, 0, 0);
     }
+#pragma unroll
+    for (int i = 0; i < T::NI; ++i) next_blk[i] = group_block(t + 1, i);
   };
 
   // ---- per-lane LDS read addresses (buffer 0; buffers differ by an immediate)
@@ -592,8 +618,8 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
 #pragma unroll
         for (int k = 0; k < 8; ++k) x[k] = (uint32_t)(base - k) < wu ? x[k] : -INFINITY;
       }
-      float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))) * sc;
+      float tmax = max3_raw(max3_raw(x[0], x[1], x[2]), max3_raw(x[3], x[4], x[5]),
+                            max3_raw(x[6], x[7], x[7])) * sc;
       if (__any(tmax > m_run[c] + kLazy)) {
         tmax = xor_max(tmax, 16);
         tmax = xor_max(tmax, 32);
@@ -611,10 +637,18 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sc, -m_run[c]));
-      l_run[c] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       const float4_t p0 = {p[0], p[1], p[2], p[3]}, p1 = {p[4], p[5], p[6], p[7]};
       const half4_t h0 = __builtin_convertvector(p0, half4_t);
       const half4_t h1 = __builtin_convertvector(p1, half4_t);
+      // row sums of the binary16 weights the P V product uses, by 2-term dots
+      // with ones (fp32 accumulation): four instructions for eight weights
+      {
+        const half2_t one2 = {(_Float16)1.f, (_Float16)1.f};
+        float ls = __builtin_amdgcn_fdot2(half2_t{h0[0], h0[1]}, one2, l_run[c], false);
+        ls = __builtin_amdgcn_fdot2(half2_t{h0[2], h0[3]}, one2, ls, false);
+        ls = __builtin_amdgcn_fdot2(half2_t{h1[0], h1[1]}, one2, ls, false);
+        l_run[c] = __builtin_amdgcn_fdot2(half2_t{h1[2], h1[3]}, one2, ls, false);
+      }
       const half8_t pop = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
       if (c == 0) {
 #pragma unroll
@@ -636,6 +670,8 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
   // is done with tile t - 1, whose buffer tile t + 2 reuses), issue tile t + 2,
   // compute tile t.
   constexpr int NB_ = T::NBUF;
+#pragma unroll
+  for (int i = 0; i < T::NI; ++i) next_blk[i] = group_block(t0, i);
 #pragma unroll
   for (int u = 0; u < NB_ - 1; ++u)
     if (t0 + u < ntiles) issue(t0 + u, u);
