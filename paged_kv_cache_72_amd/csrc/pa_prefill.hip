@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
   lds_char* const lds0 = (lds_char*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds0;
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
   const int h = lane >> 4, n = lane & 15;
   const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
   const int xcd = wg & 7, per = nwg >> 3, rem = nwg & 7;
@@ -517,29 +517,48 @@ __global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
     return bt[(uint32_t)pu / BS];
   };
   int next_blk[T::NI];
+  // In-block byte offsets of this lane's K and V chunks for a tile with no
+  // clamped position (tile start a multiple of 32, so the row in the block is
+  // r mod block_size, plus the tile's offset in the block when blocks hold
+  // more than one tile).
+  uint32_t koff[T::NI], voff[T::NI];
+#pragma unroll
+  for (int i = 0; i < T::NI; ++i) {
+    const int r = (wid * T::NI + i) * T::RPI + lane / CPR, pch = lane % CPR;
+    const uint32_t in_blk = ((uint32_t)r & (BS - 1)) * (uint32_t)a.row_stride;
+    koff[i] = in_blk + ((uint32_t)(pch ^ T::ksw(r)) << 4);
+    voff[i] = in_blk + ((uint32_t)(pch ^ T::vsw(r)) << 4);
+  }
   auto issue = [&](int t, int b) {
     const int kt = t * kPfKeys;
+    const bool whole = kt >= lo_c && kt + kPfKeys <= kv_end;      // uniform
+    const int64_t tile_in_blk = BS > kPfKeys ? (int64_t)(kt & (BS - 1)) * a.row_stride : 0;
 #pragma unroll
     for (int i = 0; i < T::NI; ++i) {
       const int r0 = (wid * T::NI + i) * T::RPI;
-      const int r = r0 + lane / CPR, pch = lane % CPR;
-      // positions are clamped into [lo_c, kv_end - 1]: outside rows repeat an
-      // in-window row (finite data, masked), never a released block
-      const int pr = kt + r < lo_c ? lo_c : kt + r;
-      const int pos = pr < kv_end ? pr : kv_end - 1;
-      // block base (uniform) plus a 32-bit per-lane offset inside the block
       const int raw = next_blk[i];
       const int blk = raw < 0 ? 0 : (raw > a.num_blocks_m1 ? a.num_blocks_m1 : raw);
+      // block base (uniform) plus a 32-bit per-lane offset inside the block
       const int64_t blk_off = (int64_t)blk * a.block_stride;
-      const uint32_t in_blk = ((uint32_t)pos & (BS - 1)) * (uint32_t)a.row_stride;
+      uint32_t ko = koff[i], vo = voff[i];
+      int64_t base = blk_off + tile_in_blk;
+      if (!whole) {
+        // positions are clamped into [lo_c, kv_end - 1]: outside rows repeat
+        // an in-window row (finite data, masked), never a released block
+        const int r = r0 + lane / CPR, pch = lane % CPR;
+        const int pr = kt + r < lo_c ? lo_c : kt + r;
+        const int pos = pr < kv_end ? pr : kv_end - 1;
+        const uint32_t in_blk = ((uint32_t)pos & (BS - 1)) * (uint32_t)a.row_stride;
+        ko = in_blk + ((uint32_t)(pch ^ T::ksw(r)) << 4);
+        vo = in_blk + ((uint32_t)(pch ^ T::vsw(r)) << 4);
+        base = blk_off;
+      }
       lds_char* kdst = lds0 + b * T::BUF + r0 * RB;
       lds_char* vdst = kdst + T::TILE;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(kbase + blk_off + (in_blk + ((uint32_t)(pch ^ T::ksw(r)) << 4))),
-          (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(vbase + blk_off + (in_blk + ((uint32_t)(pch ^ T::vsw(r)) << 4))),
-          (__attribute__((address_space(3))) void*)vdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + base + ko),
+                                       (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + base + vo),
+                                       (__attribute__((address_space(3))) void*)vdst, 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < T::NI; ++i) next_blk[i] = group_block(t + 1, i);
