@@ -235,7 +235,9 @@ def pa_decode_workspace_size(pool: KVPool, num_seqs: int, num_q_heads: int, max_
 
 def alloc_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_seq_len: int,
                     partition_size: int = 0, device="cuda") -> Optional[torch.Tensor]:
-    """Zero-filled, as the flat schedule's arrival counters require."""
+    """Workspace for pa_decode.  The kernels write every word of it they read
+    within the same call, so its contents between calls do not matter; it is
+    zero-filled only so that dumps of unused parts are tidy."""
     n = pa_decode_workspace_size(pool, num_seqs, num_q_heads, max_seq_len, partition_size)
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
