@@ -861,6 +861,49 @@ __global__ __launch_bounds__(NG * D) void flat_merge_kernel(DecodeArgs a, FlatAr
   }
 }
 
+// One wave per (sequence, query head) row, four rows per workgroup: for the
+// usual few records per sequence.  The wave's lanes cover head_dim (D / 64
+// dims each) and fold the row's records online, in range order.
+template <int D>
+__global__ __launch_bounds__(256) void flat_merge_rows_kernel(DecodeArgs a, FlatArgs f) {
+  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (row >= f.num_seqs * a.num_q_heads) return;
+  const int lane = threadIdx.x & 63;
+  const int s = row / a.num_q_heads, h = row - s * a.num_q_heads;
+  const int g = a.gqa, kh = h / g, hl = h - kh * g;
+  const int64_t T = f.prefix[f.num_seqs];
+  const int pre = f.prefix[s], end = f.prefix[s + 1];
+  if (end == pre) return;
+  const int64_t NR = f.num_ranges;
+  const int r_first = range_of(pre, T, NR), r_last = range_of(end - 1, T, NR);
+  if (r_first == r_last) return;               // written by the decode kernel
+  const bool first_is_last_slot = (int64_t)r_first * T / NR < pre;
+  const int rec = g * (D + 2);
+  constexpr int DPL = D / 64;
+  float M = kNegBig, L = 0.f, O[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) O[e] = 0.f;
+#pragma unroll 4
+  for (int r = r_first; r <= r_last; ++r) {
+    const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
+    const float* p = f.slots + ((int64_t)(r * a.num_kv_heads + kh) * 2 + slot) * rec;
+    const float2 ml = ((const float2*)(p + g * D))[hl];
+    float ov[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) ov[e] = p[hl * D + lane * DPL + e];
+    const float mn = fmaxf(M, ml.x);
+    const float sa = __builtin_amdgcn_exp2f(M - mn), sb = ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
+    L = L * sa + sb;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) O[e] = O[e] * sa + sb * ov[e];
+    M = mn;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e)
+    a.out[(int64_t)row * D + lane * DPL + e] = (_Float16)(O[e] * inv);
+}
+
 // ---------------------------------------------------------------- launchers
 
 constexpr int kWaves = PA_DECODE_WAVES;
@@ -882,8 +925,9 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs
     // records per sequence ~ ranges / sequences: about 8 per thread group
     const int64_t per_seq = num_seqs > 0 ? f->num_ranges / num_seqs : 0;
     const dim3 mgrid((uint32_t)num_seqs * (uint32_t)a.num_q_heads);
-    if (per_seq < 16)
-      hipLaunchKernelGGL((flat_merge_kernel<D, 1>), mgrid, dim3(D), 0, stream, a, *f);
+    if (per_seq < 16)       // one wave per row (measured 0.7-0.9 us faster than a group per row)
+      hipLaunchKernelGGL((flat_merge_rows_kernel<D>), dim3((mgrid.x + 3) / 4), dim3(256), 0, stream,
+                         a, *f);
     else if (per_seq < 32)
       hipLaunchKernelGGL((flat_merge_kernel<D, 2>), mgrid, dim3(2 * D), 0, stream, a, *f);
     else if (per_seq < 64)
