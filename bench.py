@@ -114,7 +114,8 @@ def traffic_entry(config: str):
     return e.get("bytes_per_launch")
 
 
-DECODE_KERNELS = ("decode_flat_kernel", "flat_merge_kernel", "decode_kernel", "lse_reduce_kernel")
+DECODE_KERNELS = ("decode_flat_kernel", "flat_merge_rows_kernel", "flat_merge_kernel", "decode_kernel",
+                  "lse_reduce_kernel")
 PREFILL_KERNELS = ("prefill_f16_kernel", "prefill_kernel")
 
 
