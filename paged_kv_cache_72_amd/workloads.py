@@ -343,6 +343,25 @@ def llama3_8b_b64_w1024(seed: int = 7202) -> Workload:
     return dataclasses.replace(llama3_8b_b64(seed), name="llama3_8b_b64_w1024", window=1024)
 
 
+def llama3_8b_b64_bs(block_size: int, seed: int = 7202) -> Workload:
+    """The Llama-3-8B-shaped batch of 64 (same lengths and heads as
+    llama3_8b_b64) in blocks of 64 or 128 tokens, the top of the pages' block
+    size range; the pool holds the same 320,000 token slots."""
+    ss = np.random.SeedSequence(seed).spawn(6)
+    lens = np.random.default_rng(ss[0]).integers(512, 4096, size=64, endpoint=True)
+    return _independent(f"llama3_8b_b64_bs{block_size}", seed, lens.tolist(), 32, 8, 128,
+                        block_size, 320000 // block_size)
+
+
+def b64_d64(seed: int = 7209) -> Workload:
+    """The batch shape of llama3_8b_b64 (64 sequences, lengths uniform in
+    [512, 4096], 32 query / 8 KV heads, block_size 16, fp16) at head_dim 64:
+    2 KiB of K and V per token, half of the head_dim 128 case."""
+    ss = np.random.SeedSequence(seed).spawn(6)
+    lens = np.random.default_rng(ss[0]).integers(512, 4096, size=64, endpoint=True)
+    return _independent("b64_d64", seed, lens.tolist(), 32, 8, 64, 16, 20000)
+
+
 def hybrid_d256_b64(seed: int = 7208) -> Workload:
     """A full-attention layer of a hybrid model with head_dim 256 and 4 KV
     heads, the shape of the pages' hybrid example ("Paging saves no KV bytes",
@@ -534,6 +553,9 @@ CONFIGS = {
     "long_e5m2": long_e5m2,
     "llama3_8b_b64_w1024": llama3_8b_b64_w1024,
     "hybrid_d256_b64": hybrid_d256_b64,
+    "llama3_8b_b64_bs64": lambda: llama3_8b_b64_bs(64),
+    "llama3_8b_b64_bs128": lambda: llama3_8b_b64_bs(128),
+    "b64_d64": b64_d64,
 }
 
 

@@ -30,6 +30,9 @@ CONFIGS = [
     ("long_e5m2", W.long_e5m2, 6, [0, 512]),
     ("llama3_8b_b64_w1024", W.llama3_8b_b64_w1024, 12, [0, -1, 256]),
     ("hybrid_d256_b64", W.hybrid_d256_b64, 12, [0, -1, 256]),
+    ("llama3_8b_b64_bs64", lambda: W.llama3_8b_b64_bs(64), 12, [0, -1, 256]),
+    ("llama3_8b_b64_bs128", lambda: W.llama3_8b_b64_bs(128), 12, [0, -1, 256]),
+    ("b64_d64", W.b64_d64, 12, [0, -1, 256]),
 ]
 
 
