@@ -109,6 +109,7 @@ FULL = [
     ("prefill_cold_2000", W.prefill_cold_2000, 24),
     ("prefill_chunked_8k", W.prefill_chunked_8k, 24),
     ("prefill_prefix_hit", W.prefill_prefix_hit, 24),
+    ("prefill_chunked_8k_fp8", W.prefill_chunked_8k_fp8, 24),
 ]
 
 
