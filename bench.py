@@ -27,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,11 +41,21 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments, trailing blanks or empty lines."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash() -> str:
+    """Hash of the library's sources, comments excluded: a stored counter
+    measurement stays valid across documentation edits but not across any
+    change of code."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "paged_kv_cache_72_amd", "csrc"))):
-        with open(os.path.join(ROOT, "paged_kv_cache_72_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_72_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode() + b"\0")
     return h.hexdigest()[:16]
 
 

@@ -14,30 +14,31 @@
 // Work decomposition and data flow:
 //   * A workgroup owns one (sequence, KV head, tile of QT = floor(128 / gqa)
 //     new tokens); the query tiles of one (sequence, KV head) are placed on
-//     one XCD so that they share its L2.  Its 128 query rows are (token, head) pairs, head fastest,
-//     so the gqa query heads of the KV head share every K/V tile it stages.
-//     4 waves x 2 groups x 16 rows.
+//     one XCD so that they share its L2.  Its 128 query rows are (token, head)
+//     pairs, head fastest, so the gqa query heads of the KV head share every
+//     K/V tile it stages.  4 waves x 2 groups x 16 rows.
 //   * K/V tiles of 32 positions are gathered through the block table into LDS
-//     by whole 16-byte row chunks (fp8 pools are widened exactly to binary16 on
-//     the way).  Rows are XOR-swizzled by chunk so that the column-wise reads
-//     below hit distinct banks.  The next tile's global loads are issued before
-//     the current tile is computed and land in the other of two LDS buffers, so
-//     each tile costs one workgroup barrier.
+//     by whole 16-byte row chunks, XOR-swizzled by chunk so that the reads
+//     below hit distinct banks.  fp16 pools (prefill_f16_kernel): straight from
+//     HBM into LDS with the global-to-LDS load, three buffers deep, V kept
+//     row-major and read with the LDS transpose read.  fp8 pools
+//     (prefill_kernel): loaded into registers one tile ahead and widened
+//     exactly to binary16 on the way into LDS (two buffers), V stored
+//     transposed.  Either way each tile costs one workgroup barrier.
 //   * Scores are computed transposed, S^T = K Q^T, with the 16x16x32 f16 MFMA:
 //     K rows are the A operand (from LDS), the group's 16 query rows the B
-//     operand (held in registers for the whole loop).  Lane (h, n) then holds
-//     the scores of query row n for key positions 4h + i and 16 + 4h + i,
-//     which is directly the A-operand layout of O = P V with the key order
-//     permuted; V's B operand is read from LDS at the same permuted positions
-//     (8 positions x 8 dims per lane) and transposed in registers.  P V block
-//     nb covers dims {8n + nb} (head_dim 128) so a lane's output dims are
-//     contiguous and each row is written with one 16-byte store.
+//     operand (held in registers for the whole loop).  The K rows of a score
+//     block are permuted so that lane (h, n) receives the scores of query row
+//     n for positions 8h .. 8h + 7, which is the A-operand layout of O = P V
+//     directly; V's B operand is read at the same positions.  Lane (h, n)
+//     accumulates dims 16 nb + n of rows 4h .. 4h + 3.
 //   * Online softmax per query row in log2 units; the running max moves only
 //     when a tile exceeds it by more than 2^8 (P <= 256 fits binary16), which
 //     a wave vote detects, so the cross-lane row max is formed only then.  The
 //     causal mask is a select on position <= query position, applied only on
 //     tiles that reach past the workgroup's first query position; positions
-//     past the context are never loaded (zeros in LDS) and are masked as well.
+//     past the context are masked as well (their rows are finite: zeros or a
+//     repeated in-context row).
 #include <type_traits>
 
 #include "pa_device.h"
