@@ -72,6 +72,12 @@ int32_t pa_bp_lookup(const pa_block_pool* pool, const pa_block_hash* hashes, int
 /* out = SHA-256(parent or 32 zero bytes | tokens as int32 LE | extra). */
 void pa_hash_block_tokens(const pa_block_hash* parent, const int32_t* tokens, int32_t n,
                           const void* extra, int32_t extra_len, pa_block_hash* out);
+/* The chained hashes of the full blocks of a token sequence ("vLLM intro
+ * part 2", section 6.1): out[i] hashes block i with out[i - 1] (32 zero bytes
+ * for block 0) as parent.  Writes min(full blocks, cap) hashes and returns the
+ * number of full blocks, or a negative status on bad arguments. */
+int32_t pa_hash_blocks(const int32_t* tokens, int32_t num_tokens, int32_t block_size,
+                       const void* extra, int32_t extra_len, pa_block_hash* out, int32_t cap);
 
 /* Request-level calls.  allocate: hash the full blocks of the prompt, take
  * the cached prefix (touch), allocate the rest; *num_cached_tokens = hits *
@@ -85,6 +91,13 @@ int pa_bp_cache_request(pa_block_pool* pool, int64_t request, const int32_t* tok
                         int32_t num_tokens, const void* extra, int32_t extra_len);
 int pa_bp_append_slots(pa_block_pool* pool, int64_t request, int32_t num_tokens_after);
 int pa_bp_free_request(pa_block_pool* pool, int64_t request);
+/* One scheduler step of growth: request requests[i] grows to
+ * num_tokens_after[i] tokens, for i < n (each request listed at most once).
+ * All or nothing: PA_ERR_NO_BLOCKS when the step needs more blocks than are
+ * free, PA_ERR_INVALID_ARG for an unknown or repeated request; either way the
+ * pool is unchanged.  Blocks are taken in list order. */
+int pa_bp_append_slots_batch(pa_block_pool* pool, const int64_t* requests,
+                             const int32_t* num_tokens_after, int32_t n);
 int32_t pa_bp_request_blocks(const pa_block_pool* pool, int64_t request, int32_t* out,
                              int32_t cap);
 

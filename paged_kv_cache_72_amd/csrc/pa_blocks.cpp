@@ -438,6 +438,55 @@ int pa_bp_append_slots(pa_block_pool* p, int64_t rid, int32_t num_tokens_after) 
   return PA_OK;
 }
 
+int pa_bp_append_slots_batch(pa_block_pool* p, const int64_t* requests,
+                             const int32_t* num_tokens_after, int32_t n) {
+  if (!p) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+  if (n < 0 || (n && (!requests || !num_tokens_after)))
+    return fail(PA_ERR_INVALID_ARG, "bad request arrays");
+  // validate everything and count the blocks first: a failed call changes nothing
+  std::vector<std::vector<int32_t>*> rows((size_t)n);
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->requests.find(requests[i]);
+    if (it == p->requests.end())
+      return fail(PA_ERR_INVALID_ARG, "no request %lld (entry %d)", (long long)requests[i], i);
+    if (num_tokens_after[i] < 0) return fail(PA_ERR_INVALID_ARG, "negative token count (entry %d)", i);
+    for (int32_t j = 0; j < i; ++j)
+      if (rows[(size_t)j] == &it->second)
+        return fail(PA_ERR_INVALID_ARG, "request %lld listed twice", (long long)requests[i]);
+    rows[(size_t)i] = &it->second;
+    const int32_t need =
+        (num_tokens_after[i] + p->block_size - 1) / p->block_size - (int32_t)it->second.size();
+    if (need > 0) total += need;
+  }
+  if (total > p->nfree)
+    return fail(PA_ERR_NO_BLOCKS, "%lld blocks needed, %d free", (long long)total, p->nfree);
+  for (int32_t i = 0; i < n; ++i) {
+    std::vector<int32_t>& v = *rows[(size_t)i];
+    const int32_t need = (num_tokens_after[i] + p->block_size - 1) / p->block_size - (int32_t)v.size();
+    if (need <= 0) continue;
+    const size_t old = v.size();
+    v.resize(old + (size_t)need);
+    p->take(need, v.data() + old);
+  }
+  return PA_OK;
+}
+
+int32_t pa_hash_blocks(const int32_t* tokens, int32_t num_tokens, int32_t block_size,
+                       const void* extra, int32_t extra_len, pa_block_hash* out, int32_t cap) {
+  if (num_tokens < 0 || (num_tokens && !tokens) || block_size < 1 || cap < 0 ||
+      (cap && !out) || extra_len < 0 || (extra_len && !extra))
+    return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  const int32_t full = num_tokens / block_size;
+  const pa_block_hash* parent = nullptr;
+  const int32_t m = full < cap ? full : cap;
+  for (int32_t i = 0; i < m; ++i) {
+    hash_block(parent, tokens + (int64_t)i * block_size, block_size, extra, extra_len, out + i);
+    parent = out + i;
+  }
+  return full;
+}
+
 int pa_bp_free_request(pa_block_pool* p, int64_t rid) {
   if (!p) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
   auto it = p->requests.find(rid);

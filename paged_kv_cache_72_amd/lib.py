@@ -15,6 +15,7 @@ import ctypes as C
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +38,7 @@ EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
            "pa_hash_block_tokens", "pa_bp_allocate_request", "pa_bp_cache_request",
            "pa_bp_append_slots", "pa_bp_free_request", "pa_bp_request_blocks",
            "pa_bp_fork_request", "pa_bp_prepare_write", "pa_bp_remove_skipped_blocks",
+           "pa_bp_append_slots_batch", "pa_hash_blocks",
            # device-argument checks (include/pa_check.h)
            "pa_check_scratch_bytes", "pa_check_decode_inputs", "pa_check_prefill_inputs",
            "pa_check_slot_mapping", "pa_check_block_mapping")
@@ -371,6 +373,8 @@ def _bind_block_pool(L) -> None:
         "pa_bp_fork_request": (C.c_int, [P, I64, I64]),
         "pa_bp_prepare_write": (C.c_int, [P, I64, I32, LP]),
         "pa_bp_remove_skipped_blocks": (I32, [P, I64, I32, I32]),
+        "pa_bp_append_slots_batch": (C.c_int, [P, LP, IP, I32]),
+        "pa_hash_blocks": (I32, [IP, I32, I32, P, I32, H, I32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -378,7 +382,11 @@ def _bind_block_pool(L) -> None:
         f.argtypes = args
 
 
-def _ints(xs) -> C.Array:
+def _ints(xs):
+    """int32 array argument: a contiguous int32 numpy array is passed in place,
+    anything else is copied into a new ctypes array."""
+    if isinstance(xs, np.ndarray) and xs.dtype == np.int32 and xs.flags.c_contiguous and xs.size:
+        return xs.ctypes.data_as(C.POINTER(C.c_int32))
     xs = [int(x) for x in xs]
     return (C.c_int32 * max(1, len(xs)))(*xs)
 
@@ -403,6 +411,19 @@ def hash_block_tokens(parent: Optional[bytes], tokens, extra: bytes = b"") -> by
     L.pa_hash_block_tokens(C.byref(par) if par is not None else None, toks, len(tokens),
                            ex if extra else None, len(extra), C.byref(out))
     return bytes(out.bytes)
+
+
+def hash_blocks(tokens, block_size: int, extra: bytes = b"") -> list:
+    """Chained hashes of the full blocks of a token sequence (one native call)."""
+    L = load()
+    n = len(tokens) // int(block_size)
+    out = (pa_block_hash * max(1, n))()
+    ex = C.create_string_buffer(bytes(extra), max(1, len(extra)))
+    r = L.pa_hash_blocks(_ints(tokens), len(tokens), int(block_size), ex if extra else None,
+                         len(extra), out, n)
+    if r < 0:
+        raise PaError(r, L.pa_bp_last_error().decode())
+    return [bytes(out[i].bytes) for i in range(n)]
 
 
 class BlockPool:
@@ -478,6 +499,13 @@ class BlockPool:
 
     def append_slots(self, rid: int, num_tokens_after: int) -> None:
         self._ok(self._L.pa_bp_append_slots(self._p, int(rid), int(num_tokens_after)))
+
+    def append_slots_batch(self, rids, num_tokens_after) -> None:
+        """One scheduler step: each listed request grows to its token count
+        (all or nothing)."""
+        n = len(rids)
+        ids = (C.c_int64 * max(1, n))(*[int(r) for r in rids])
+        self._ok(self._L.pa_bp_append_slots_batch(self._p, ids, _ints(num_tokens_after), n))
 
     def free_request(self, rid: int) -> None:
         self._ok(self._L.pa_bp_free_request(self._p, int(rid)))

@@ -199,3 +199,54 @@ def test_sliding_window_release_matches_the_model():
     nat.free_request(1)
     mod.free_request(1)
     assert _state(nat) == _model_state(mod) and nat.num_free() == 16
+
+
+@pytest.mark.parametrize("bs", [1, 4, 16])
+def test_hash_blocks_is_the_chain(bs):
+    rng = np.random.default_rng(bs)
+    for n in (0, bs - 1, bs, 5 * bs + 3, 130):
+        toks = [int(x) for x in rng.integers(-2**31, 2**31 - 1, size=n)]
+        for extra in (b"", b"tenant-7"):
+            assert L.hash_blocks(toks, bs, extra) == chain_hashes(toks, bs, extra)
+
+
+def test_append_slots_batch_matches_sequential_appends():
+    bs = 4
+    nat, mod = L.BlockPool(40, bs), BlockPoolModel(40, bs)
+    lens = {}
+    for rid, n in enumerate([3, 8, 13, 1]):
+        toks = _tokens(n, 70 + rid)
+        nat.allocate_request(rid, toks)
+        mod.allocate_request(rid, toks)
+        lens[rid] = n
+    rng = np.random.default_rng(5)
+    for step in range(12):
+        rids = [int(r) for r in rng.permutation(4)[:int(rng.integers(1, 5))]]
+        after = [lens[r] + int(rng.integers(0, 6)) for r in rids]
+        nat.append_slots_batch(rids, after)
+        for r, a in zip(rids, after):
+            mod.append_slot(r, a)
+            lens[r] = max(lens[r], a)
+        assert _state(nat) == _model_state(mod), step
+        for r in range(4):
+            assert nat.request_blocks(r) == mod.requests[r]
+
+
+def test_append_slots_batch_is_all_or_nothing():
+    bs = 4
+    pool = L.BlockPool(6, bs)
+    pool.allocate_request(1, _tokens(4, 80))           # 1 block
+    pool.allocate_request(2, _tokens(4, 81))           # 1 block
+    before = _state(pool)
+    for rids, after, code in [
+        ([1, 2], [13, 13], L.PA_ERR_NO_BLOCKS),          # 3 + 3 needed, 4 free
+        ([1, 9], [8, 8], L.PA_ERR_INVALID_ARG),          # unknown request
+        ([1, 1], [8, 8], L.PA_ERR_INVALID_ARG),          # listed twice
+        ([1], [-1], L.PA_ERR_INVALID_ARG),
+    ]:
+        with pytest.raises(L.PaError) as e:
+            pool.append_slots_batch(rids, after)
+        assert e.value.status == code
+        assert _state(pool) == before
+    pool.append_slots_batch([1, 2], [12, 12])           # 2 + 2 needed, 4 free: fits
+    assert pool.num_free() == 0
