@@ -50,11 +50,14 @@ def _code_only(text: str) -> str:
 
 
 def kernel_source_hash() -> str:
-    """Hash of the library's sources, comments excluded: a stored counter
+    """Hash of the library's device sources (.hip and .h; the host-only C++
+    of the block pool is left out), comments excluded: a stored counter
     measurement stays valid across documentation edits but not across any
-    change of code."""
+    change of kernel code."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "paged_kv_cache_72_amd", "csrc"))):
+        if not f.endswith((".hip", ".h")):
+            continue
         with open(os.path.join(ROOT, "paged_kv_cache_72_amd", "csrc", f), encoding="utf-8") as fh:
             h.update(f.encode() + b"\0" + _code_only(fh.read()).encode() + b"\0")
     return h.hexdigest()[:16]
