@@ -15,6 +15,8 @@
  *   * A full block's hash is SHA-256(parent hash | its token ids as
  *     little-endian int32 | extra-key bytes), the first block's parent being
  *     32 zero bytes.  Lookups walk the chain and stop at the first miss.
+ *     SHA-256 runs on the x86 SHA extensions when the CPU has them (setting
+ *     PA_SHA256_PORTABLE=1 in the environment selects the portable code).
  *   * A request's lookup never covers its last token: at most
  *     (num_tokens - 1) / block_size blocks hit.
  *

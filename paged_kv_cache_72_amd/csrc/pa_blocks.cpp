@@ -32,9 +32,13 @@
 //
 // SHA-256 follows FIPS 180-4; its constants are the fractional parts of the
 // square and cube roots of the first primes, computed here at start-up.
+#include <cpuid.h>
+#include <immintrin.h>
+
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <unordered_map>
@@ -76,82 +80,124 @@ const Sha256Consts& sha_consts() {
 
 inline uint32_t rotr(uint32_t x, int n) { return (x >> n) | (x << (32 - n)); }
 
-class Sha256 {
- public:
-  Sha256() {
-    std::memcpy(h_, sha_consts().h0, sizeof h_);
+// One compression of a 64-byte block into state h (FIPS 180-4, section 6.2.2).
+void compress_portable(uint32_t h[8], const uint8_t* m) {
+  const uint32_t* K = sha_consts().k;
+  uint32_t w[64];
+  for (int t = 0; t < 16; ++t)
+    w[t] = (uint32_t)m[4 * t] << 24 | (uint32_t)m[4 * t + 1] << 16 |
+           (uint32_t)m[4 * t + 2] << 8 | (uint32_t)m[4 * t + 3];
+  for (int t = 16; t < 64; ++t) {
+    const uint32_t s0 = rotr(w[t - 15], 7) ^ rotr(w[t - 15], 18) ^ (w[t - 15] >> 3);
+    const uint32_t s1 = rotr(w[t - 2], 17) ^ rotr(w[t - 2], 19) ^ (w[t - 2] >> 10);
+    w[t] = w[t - 16] + s0 + w[t - 7] + s1;
   }
-  void update(const void* data, size_t n) {
-    const uint8_t* p = (const uint8_t*)data;
-    total_ += n;
-    while (n) {
-      const size_t take = std::min(n, (size_t)64 - fill_);
-      std::memcpy(buf_ + fill_, p, take);
-      fill_ += take;
-      p += take;
-      n -= take;
-      if (fill_ == 64) {
-        block(buf_);
-        fill_ = 0;
-      }
-    }
+  uint32_t a = h[0], b = h[1], c = h[2], d = h[3], e = h[4], f = h[5], g = h[6], hh = h[7];
+  for (int t = 0; t < 64; ++t) {
+    const uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);
+    const uint32_t ch = (e & f) ^ (~e & g);
+    const uint32_t t1 = hh + S1 + ch + K[t] + w[t];
+    const uint32_t S0 = rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22);
+    const uint32_t mj = (a & b) ^ (a & c) ^ (b & c);
+    const uint32_t t2 = S0 + mj;
+    hh = g; g = f; f = e; e = d + t1; d = c; c = b; b = a; a = t1 + t2;
   }
-  void final(uint8_t out[32]) {
-    const uint64_t bits = (uint64_t)total_ * 8;
-    const uint8_t one = 0x80, zero = 0;
-    update(&one, 1);
-    while (fill_ != 56) update(&zero, 1);
-    uint8_t len[8];
-    for (int i = 0; i < 8; ++i) len[i] = (uint8_t)(bits >> (56 - 8 * i));
-    update(len, 8);
-    for (int i = 0; i < 8; ++i)
-      for (int j = 0; j < 4; ++j) out[4 * i + j] = (uint8_t)(h_[i] >> (24 - 8 * j));
-  }
+  h[0] += a; h[1] += b; h[2] += c; h[3] += d;
+  h[4] += e; h[5] += f; h[6] += g; h[7] += hh;
+}
 
- private:
-  void block(const uint8_t* m) {
-    const uint32_t* K = sha_consts().k;
-    uint32_t w[64];
-    for (int t = 0; t < 16; ++t)
-      w[t] = (uint32_t)m[4 * t] << 24 | (uint32_t)m[4 * t + 1] << 16 |
-             (uint32_t)m[4 * t + 2] << 8 | (uint32_t)m[4 * t + 3];
-    for (int t = 16; t < 64; ++t) {
-      const uint32_t s0 = rotr(w[t - 15], 7) ^ rotr(w[t - 15], 18) ^ (w[t - 15] >> 3);
-      const uint32_t s1 = rotr(w[t - 2], 17) ^ rotr(w[t - 2], 19) ^ (w[t - 2] >> 10);
-      w[t] = w[t - 16] + s0 + w[t - 7] + s1;
+// The same compression with the x86 SHA extensions (SHA256RNDS2 does two
+// rounds on the state split as (a, b, e, f) and (c, d, g, h); SHA256MSG1 and
+// SHA256MSG2 extend the message schedule four words at a time).
+__attribute__((target("sha,sse4.1,ssse3"))) void compress_x86(uint32_t h[8],
+                                                              const uint8_t* m) {
+  const uint32_t* K = sha_consts().k;
+  const __m128i bswap = _mm_set_epi64x(0x0c0d0e0f08090a0bULL, 0x0405060700010203ULL);
+  __m128i tmp = _mm_shuffle_epi32(_mm_loadu_si128((const __m128i*)&h[0]), 0xB1);   // c d a b
+  __m128i st1 = _mm_shuffle_epi32(_mm_loadu_si128((const __m128i*)&h[4]), 0x1B);   // h g f e
+  __m128i st0 = _mm_alignr_epi8(tmp, st1, 8);                                       // a b e f
+  st1 = _mm_blend_epi16(st1, tmp, 0xF0);                                            // c d g h
+  const __m128i save0 = st0, save1 = st1;
+  __m128i w[4];
+  for (int j = 0; j < 4; ++j)
+    w[j] = _mm_shuffle_epi8(_mm_loadu_si128((const __m128i*)(m + 16 * j)), bswap);
+  for (int j = 0; j < 16; ++j) {
+    __m128i& wj = w[j & 3];                   // words 4j .. 4j + 3
+    if (j >= 4) {
+      // W[t] = W[t-16] + s0(W[t-15]) + W[t-7] + s1(W[t-2]) for four t at once
+      const __m128i prev = w[(j + 3) & 3], prev2 = w[(j + 2) & 3];
+      wj = _mm_sha256msg2_epu32(
+          _mm_add_epi32(_mm_sha256msg1_epu32(wj, w[(j + 1) & 3]), _mm_alignr_epi8(prev, prev2, 4)),
+          prev);
     }
-    uint32_t a = h_[0], b = h_[1], c = h_[2], d = h_[3], e = h_[4], f = h_[5], g = h_[6],
-             h = h_[7];
-    for (int t = 0; t < 64; ++t) {
-      const uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);
-      const uint32_t ch = (e & f) ^ (~e & g);
-      const uint32_t t1 = h + S1 + ch + K[t] + w[t];
-      const uint32_t S0 = rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22);
-      const uint32_t mj = (a & b) ^ (a & c) ^ (b & c);
-      const uint32_t t2 = S0 + mj;
-      h = g; g = f; f = e; e = d + t1; d = c; c = b; b = a; a = t1 + t2;
-    }
-    h_[0] += a; h_[1] += b; h_[2] += c; h_[3] += d;
-    h_[4] += e; h_[5] += f; h_[6] += g; h_[7] += h;
+    __m128i msg = _mm_add_epi32(wj, _mm_loadu_si128((const __m128i*)&K[4 * j]));
+    st1 = _mm_sha256rnds2_epu32(st1, st0, msg);
+    msg = _mm_shuffle_epi32(msg, 0x0E);
+    st0 = _mm_sha256rnds2_epu32(st0, st1, msg);
   }
-  uint32_t h_[8];
-  uint8_t buf_[64];
-  size_t fill_ = 0;
-  uint64_t total_ = 0;
-};
+  st0 = _mm_add_epi32(st0, save0);
+  st1 = _mm_add_epi32(st1, save1);
+  tmp = _mm_shuffle_epi32(st0, 0x1B);                                               // f e b a
+  st1 = _mm_shuffle_epi32(st1, 0xB1);                                               // d c h g
+  _mm_storeu_si128((__m128i*)&h[0], _mm_blend_epi16(tmp, st1, 0xF0));               // a b c d
+  _mm_storeu_si128((__m128i*)&h[4], _mm_alignr_epi8(st1, tmp, 8));                  // e f g h
+}
 
+// The x86 path when the CPU has the SHA extensions, unless PA_SHA256_PORTABLE
+// is set in the environment (to exercise the portable path).
+bool use_x86_sha() {
+  static const bool on = [] {
+    const char* env = std::getenv("PA_SHA256_PORTABLE");
+    if (env && *env && *env != '0') return false;
+    unsigned a, b, c, d;
+    return __get_cpuid_count(7, 0, &a, &b, &c, &d) && ((b >> 29) & 1u);
+  }();
+  return on;
+}
+
+// SHA-256 of a message already assembled in memory (padding appended here).
+void sha256(const uint8_t* msg, size_t n, uint8_t out[32]) {
+  uint32_t h[8];
+  std::memcpy(h, sha_consts().h0, sizeof h);
+  void (*compress)(uint32_t*, const uint8_t*) = use_x86_sha() ? compress_x86 : compress_portable;
+  size_t full = n / 64;
+  for (size_t i = 0; i < full; ++i) compress(h, msg + 64 * i);
+  uint8_t tail[128] = {0};
+  const size_t rem = n - 64 * full;
+  std::memcpy(tail, msg + 64 * full, rem);
+  tail[rem] = 0x80;
+  const size_t tl = rem + 1 + 8 <= 64 ? 64 : 128;
+  const uint64_t bits = (uint64_t)n * 8;
+  for (int i = 0; i < 8; ++i) tail[tl - 1 - i] = (uint8_t)(bits >> (8 * i));
+  compress(h, tail);
+  if (tl == 128) compress(h, tail + 64);
+  for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < 4; ++j) out[4 * i + j] = (uint8_t)(h[i] >> (24 - 8 * j));
+}
+
+// h = SHA-256(parent or 32 zero bytes | tokens as int32 little-endian | extra)
 void hash_block(const pa_block_hash* parent, const int32_t* tokens, int32_t n,
                 const void* extra, int32_t extra_len, pa_block_hash* out) {
-  Sha256 s;
-  static const uint8_t none[32] = {0};
-  s.update(parent ? parent->bytes : none, 32);
+  const size_t len = 32 + 4 * (size_t)n + (extra && extra_len > 0 ? (size_t)extra_len : 0);
+  uint8_t small[512];
+  std::vector<uint8_t> big;
+  uint8_t* m = small;
+  if (len > sizeof small) {
+    big.resize(len);
+    m = big.data();
+  }
+  if (parent) std::memcpy(m, parent->bytes, 32);
+  else std::memset(m, 0, 32);
+  uint8_t* p = m + 32;
   for (int32_t i = 0; i < n; ++i) {
     const uint32_t v = (uint32_t)tokens[i];
-    const uint8_t le[4] = {(uint8_t)v, (uint8_t)(v >> 8), (uint8_t)(v >> 16), (uint8_t)(v >> 24)};
-    s.update(le, 4);
+    p[4 * i] = (uint8_t)v;
+    p[4 * i + 1] = (uint8_t)(v >> 8);
+    p[4 * i + 2] = (uint8_t)(v >> 16);
+    p[4 * i + 3] = (uint8_t)(v >> 24);
   }
-  if (extra && extra_len > 0) s.update(extra, (size_t)extra_len);
-  s.final(out->bytes);
+  if (extra && extra_len > 0) std::memcpy(p + 4 * (size_t)n, extra, (size_t)extra_len);
+  sha256(m, len, out->bytes);
 }
 
 struct HashKey {

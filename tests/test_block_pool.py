@@ -250,3 +250,34 @@ def test_append_slots_batch_is_all_or_nothing():
         assert _state(pool) == before
     pool.append_slots_batch([1, 2], [12, 12])           # 2 + 2 needed, 4 free: fits
     assert pool.num_free() == 0
+
+
+_SHA_CHECK = r"""
+import hashlib, struct, sys
+sys.path.insert(0, sys.argv[1])
+from paged_kv_cache_72_amd import lib as L
+for e in range(0, 200):
+    extra = bytes((7 * i + e) & 255 for i in range(e))
+    for n in (0, 1, 7, 16):
+        toks = list(range(-n, n, 2))[:n] if n else []
+        want = hashlib.sha256(bytes(32) + b"".join(struct.pack("<i", t) for t in toks)
+                              + extra).digest()
+        assert L.hash_block_tokens(None, toks, extra) == want, (e, n)
+print("ok")
+"""
+
+
+@pytest.mark.parametrize("portable", ["0", "1"])
+def test_sha256_every_padding_length_on_both_paths(portable):
+    """Message lengths 32 .. 295 bytes (every padding case, one and two final
+    blocks) against hashlib, with the x86 SHA-extension compression (when the
+    CPU has it) and with the portable one (PA_SHA256_PORTABLE=1)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PA_SHA256_PORTABLE=portable)
+    r = subprocess.run([sys.executable, "-c", _SHA_CHECK, root], env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip() == "ok"
