@@ -200,3 +200,24 @@ def test_sliding_window_decode(name, win, part):
     y = DeviceCase(w, poison=True).decode(part).cpu().numpy()
     r = O.decode(oracle_pool(w, poison=True), w.q, w.block_tables, w.seq_lens, w.scale)
     check_close(w, y, r, f"window{win}/{name}/p{part}")
+
+
+def test_batch_past_the_flat_limit():
+    """9,000 short sequences: more than the flat schedule takes, so the
+    library's choice is the single pass; the forced flat schedule is refused
+    on the host and the split pass agrees."""
+    lens = np.random.default_rng(96).integers(0, 65, size=9000)
+    w = W.custom("many", 95, lens.tolist(), 8, 2, 64, 16)
+    say("decode 9000 sequences")
+    dc = DeviceCase(w, poison=True)
+    assert L.pa_decode_plan(dc.pool, w.num_seqs, 8, w.max_seq_len, 0) == L.PLAN_SINGLE
+    y = dc.decode(0).cpu().numpy()
+    r = _ref(w, oracle_pool(w, poison=True))
+    check_close(w, y, r, "9000 seqs auto")
+    for s in np.nonzero(w.seq_lens == 0)[0]:
+        assert np.all(y[s] == 0)
+    with pytest.raises(L.PaError) as e:
+        dc.decode(1)
+    assert e.value.status == L.PA_ERR_UNSUPPORTED
+    ys = dc.decode(16).cpu().numpy()
+    check_close(w, ys, r, "9000 seqs split")
