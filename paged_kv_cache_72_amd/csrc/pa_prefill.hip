@@ -386,7 +386,8 @@ struct PfDma {
   static constexpr int TILE = kPfKeys * RB;
   static constexpr int BUF = 2 * TILE;                    // K tile then V tile
   static constexpr int DPT = 2 * NI;                      // loads per thread per tile
-  static constexpr int NBUF = PA_PF_NBUF;
+  // head_dim 256: two buffers of 32 KiB (one workgroup per CU)
+  static constexpr int NBUF = D > 128 ? 2 : PA_PF_NBUF;
   static constexpr int NST = D / 32;
   static constexpr int NB = D / 16;
   static_assert(NI >= 1 && NBUF >= 2 && NBUF <= 4 && NBUF * BUF <= 65536, "tile shape");
@@ -444,7 +445,7 @@ __device__ __forceinline__ void vm_wait() {
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(kPfWaves * 64, PA_PF_OCC) void prefill_f16_kernel(
+__global__ __launch_bounds__(kPfWaves * 64, D > 128 ? 1 : PA_PF_OCC) void prefill_f16_kernel(
     PrefillArgs a, const int32_t* __restrict__ tables) {
   typedef PfDma<D> T;
   constexpr int CPR = T::CPR, RB = T::RB, NST = T::NST, NB = T::NB;
@@ -733,15 +734,17 @@ template <int D, int BS>
 hipError_t launch_pf_bs(const PrefillArgs& a, int kv, hipStream_t stream) {
   const dim3 grid((uint32_t)a.num_seqs * (uint32_t)a.num_kv_heads * (uint32_t)a.num_qt);
   const dim3 block(kPfWaves * 64);
-  switch (kv) {
-    case 0:
-      hipLaunchKernelGGL((prefill_f16_kernel<D, BS>), grid, block, 0, stream, a, a.block_tables);
-      break;
-    case 1: hipLaunchKernelGGL((prefill_kernel<D, BS, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<D, BS, 2>), grid, block, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+  if (kv == 0) {
+    hipLaunchKernelGGL((prefill_f16_kernel<D, BS>), grid, block, 0, stream, a, a.block_tables);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  if constexpr (D <= 128) {             // fp8 pools: head_dim 64 and 128
+    if (kv == 1) hipLaunchKernelGGL((prefill_kernel<D, BS, 1>), grid, block, 0, stream, a);
+    else if (kv == 2) hipLaunchKernelGGL((prefill_kernel<D, BS, 2>), grid, block, 0, stream, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D>
@@ -764,6 +767,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t head_dim, int32_t block_
                           hipStream_t stream) {
   if (head_dim == 128) return launch_pf_d<128>(a, block_size, kv, stream);
   if (head_dim == 64) return launch_pf_d<64>(a, block_size, kv, stream);
+  if (head_dim == 256 && kv == 0) return launch_pf_d<256>(a, block_size, kv, stream);
   return hipErrorInvalidValue;
 }
 

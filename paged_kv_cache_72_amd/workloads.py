@@ -501,6 +501,16 @@ def prefill_chunked_8k_fp8(seed: int = 7213) -> Workload:
                                 8192, kv_dtype="fp8_e4m3fn")
 
 
+def prefill_chunked_8k_d256(seed: int = 7213) -> Workload:
+    """The chunked 8K batch of prefill_chunked_8k (same lengths and chunks) at
+    head_dim 256 with 16 query / 4 KV heads, the hybrid example's
+    full-attention shape; fp16, block_size 16."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(7)[6])
+    ctx = (rng.integers(0, 8, size=16) * 512).tolist()
+    return _prefill_independent("prefill_chunked_8k_d256", seed, ctx, [512] * 16, 16, 4, 256,
+                                16, 8192)
+
+
 def prefill_prefix_hit(seed: int = 7214) -> Workload:
     """The pages' prefix-cache hit: a 2,000-token system prompt (125 full
     blocks of 16) is cached once and shared by 32 requests; each prefills its
@@ -539,6 +549,7 @@ PREFILL_CONFIGS = {
     "prefill_chunked_8k": prefill_chunked_8k,
     "prefill_prefix_hit": prefill_prefix_hit,
     "prefill_chunked_8k_fp8": prefill_chunked_8k_fp8,
+    "prefill_chunked_8k_d256": prefill_chunked_8k_d256,
 }
 
 

@@ -42,6 +42,10 @@ SHAPES = {
     "d128_bs16_g4_e4m3_head": lambda: W.custom_prefill("pf", 91, [0, 40], [64, 25], 32, 8, 128,
                                                        16, kv_dtype="fp8_e4m3fn",
                                                        scale_grain="head"),
+    # head_dim 256 (binary16 pools): the hybrid example's full-attention shape
+    "d256_bs16_g4": lambda: W.custom_prefill("pf", 92, [0, 5, 33, 300], [70, 31, 32, 129],
+                                             16, 4, 256, 16),
+    "d256_bs64_g8": lambda: W.custom_prefill("pf", 93, [0, 100], [45, 96], 16, 2, 256, 64),
 }
 
 
@@ -110,6 +114,7 @@ FULL = [
     ("prefill_chunked_8k", W.prefill_chunked_8k, 24),
     ("prefill_prefix_hit", W.prefill_prefix_hit, 24),
     ("prefill_chunked_8k_fp8", W.prefill_chunked_8k_fp8, 24),
+    ("prefill_chunked_8k_d256", W.prefill_chunked_8k_d256, 24),
 ]
 
 
@@ -133,7 +138,7 @@ def test_prefill_full_size_sampled(name, make, nrows):
 
 
 @pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "d64_bs16_g16",
-                                  "d128_bs16_g4_e4m3"])
+                                  "d128_bs16_g4_e4m3", "d256_bs16_g4"])
 @pytest.mark.parametrize("win", [1, 31, 32, 33, 100])
 def test_sliding_window_prefill(name, win):
     w0 = SHAPES[name]()
