@@ -397,8 +397,12 @@ struct PfDma {
     return (((key >> 3) << 2) | (key & 3)) & (CPR - 1);
   }
   // V rows: the 4 rows one transpose read spans (positions differing in
-  // bits 0-1) start their 32-byte dim windows on different banks.
-  __device__ static __forceinline__ int vsw(int key) { return (2 * (key & 3)) & (CPR - 1); }
+  // bits 0-1) start their 32-byte dim windows on different banks, and rows
+  // 8 apart (lanes 16-31 against lanes 0-15 of the same read) use the other
+  // half of a 256-byte bank row.
+  __device__ static __forceinline__ int vsw(int key) {
+    return (2 * (key & 3) + 8 * ((key >> 3) & 1)) & (CPR - 1);
+  }
 };
 
 template <int OFF>
