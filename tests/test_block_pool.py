@@ -281,3 +281,37 @@ def test_sha256_every_padding_length_on_both_paths(portable):
                        text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.strip() == "ok"
+
+
+def test_copy_on_write_walkthrough_from_the_pages_native():
+    """The pages' copy-on-write walkthrough on the native pool
+    (tests/golden/block_math.json, cow_walkthrough): a 40-token prompt in
+    blocks 7, 3, 12, four holders after the fork, the first one's write of its
+    41st token copies block 12 into block 20."""
+    import json
+    import os
+    wt = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                     "block_math.json")))["cow_walkthrough"]
+    pool = L.BlockPool(64, 16)
+    # arrange the free queue to start 7, 3, 12, 20: unhashed blocks freed one
+    # after another are each put at the head
+    every = pool.get_new_blocks(64)
+    head = wt["free_order"]
+    rest = [b for b in every if b not in head]
+    pool.free_blocks(list(reversed(rest)) + list(reversed(head)))
+    assert pool.free_queue()[:4] == head
+    toks = _tokens(wt["prompt_tokens"], 90)
+    pool.allocate_request(0, toks)
+    assert pool.request_blocks(0) == wt["prompt_blocks"]
+    for child in (1, 2, 3):
+        pool.fork_request(0, child)
+    assert [pool.ref_count(b) for b in wt["prompt_blocks"]] == [4, 4, 4]
+    pair = pool.prepare_write(0, wt["prompt_tokens"])      # slot 8 of block 12
+    assert pair == (wt["prompt_blocks"][2], wt["new_block"])
+    assert wt["prompt_tokens"] % 16 == wt["write_offset"]
+    assert pool.request_blocks(0) == wt["table_after"]
+    assert pool.ref_count(wt["prompt_blocks"][2]) == wt["old_ref_after"]
+    assert pool.ref_count(wt["new_block"]) == 1
+    assert pool.ref_count(7) == 4 and pool.ref_count(3) == 4
+    for child in (1, 2, 3):
+        assert pool.request_blocks(child) == wt["prompt_blocks"]
