@@ -221,3 +221,52 @@ def test_batch_past_the_flat_limit():
     assert e.value.status == L.PA_ERR_UNSUPPORTED
     ys = dc.decode(16).cpu().numpy()
     check_close(w, ys, r, "9000 seqs split")
+
+
+def _every_byte_pool(dtype):
+    """Pool whose block 1, slot 0 holds all 256 byte values in V (K bytes 0):
+    a query over that one token gets weight 1 on it, so its output is the
+    widened V row itself."""
+    Hkv, D = 2, 128
+    pool = L.KVPool.allocate(4, 16, Hkv, D, dtype, 1.0, 1.0, fill_bits=0)
+    pool.v[1, 0] = torch.from_numpy(np.arange(256, dtype=np.uint8).reshape(Hkv, D)).cuda()
+    return pool
+
+
+def _assert_widened_exactly(dtype, y):
+    dec = O.e4m3fn_values if dtype == "fp8_e4m3fn" else O.e5m2_values
+    want = dec(np.arange(256, dtype=np.uint8))
+    y = y.reshape(-1).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(y), nan)
+    assert np.array_equal(y[~nan], want[~nan])
+
+
+@pytest.mark.parametrize("dtype", ["fp8_e4m3fn", "fp8_e5m2"])
+@pytest.mark.parametrize("part", [-1, 0, 32])
+def test_fp8_widening_exact_for_every_byte(dtype, part):
+    """Decode's fp8 widening equals the oracle's decoder bit for bit on all
+    256 byte values, NaN bytes giving NaN and infinities staying infinite."""
+    say(f"fp8 widening decode {dtype} partition={part}")
+    pool = _every_byte_pool(dtype)
+    q = torch.randn(1, 2, 128, device="cuda").half()
+    out = torch.empty_like(q)
+    bt = torch.tensor([[1]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([1], dtype=torch.int32, device="cuda")
+    ws = L.alloc_workspace(pool, 1, 2, 1, part)
+    L.pa_decode(pool, out, q, bt, lens, 1, 0.088, part, ws)
+    _assert_widened_exactly(dtype, out.cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", ["fp8_e4m3fn", "fp8_e5m2"])
+def test_fp8_widening_exact_for_every_byte_prefill(dtype):
+    """The same through pa_prefill: one new token whose context is itself."""
+    say(f"fp8 widening prefill {dtype}")
+    pool = _every_byte_pool(dtype)
+    q = torch.randn(1, 2, 128, device="cuda").half()
+    out = torch.empty_like(q)
+    qs = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    bt = torch.tensor([[1]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([1], dtype=torch.int32, device="cuda")
+    L.pa_prefill(pool, out, q, qs, bt, lens, 1, 0.088)
+    _assert_widened_exactly(dtype, out.cpu().numpy())
