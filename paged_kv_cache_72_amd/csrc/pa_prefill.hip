@@ -453,6 +453,7 @@ __global__ __launch_bounds__(kPfWaves * 64, D > 128 ? 1 : PA_PF_OCC) void prefil
     PrefillArgs a, const int32_t* __restrict__ tables) {
   typedef PfDma<D> T;
   constexpr int CPR = T::CPR, RB = T::RB, NST = T::NST, NB = T::NB;
+  constexpr bool kPrio = D <= 128;
   __shared__ __attribute__((aligned(1024))) char smem[T::NBUF * T::BUF];
   lds_char* const lds0 = (lds_char*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds0;
@@ -612,7 +613,13 @@ __global__ __launch_bounds__(kPfWaves * 64, D > 128 ? 1 : PA_PF_OCC) void prefil
       lgkm_wait<0>(kop[0][st]);
       lgkm_wait<0>(kop[1][st]);
     }
+    // Two waves share each SIMD at head_dim <= 128.  The wave issuing its
+    // score MFMAs takes issue priority over the other wave (usually in its
+    // softmax), so the matrix core is kept fed and the VALU work fills in
+    // behind it (measured 1.5-3.5% faster; at head_dim 256, one wave per
+    // SIMD, it only costs).
     float4_t sa[2][2];
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -622,6 +629,7 @@ __global__ __launch_bounds__(kPfWaves * 64, D > 128 ? 1 : PA_PF_OCC) void prefil
         for (int st = 0; st < NST; ++st)
           sa[c][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb][st], qop[c][st], sa[c][kb], 0, 0, 0);
       }
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
     // V reads go out after the score MFMAs (the K operands are dead by then)
     // and land while the first group's softmax runs
     half4_t vh[NB][2];
