@@ -277,14 +277,13 @@ def run_prefill(args, w) -> int:
         if ev is not None:
             ev[1].record(stream)
 
-    for i in range(args.warmup):
-        step(i)
+    warmup = warm_up(step, args.warmup)
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        step(warmup + i, events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -302,7 +301,7 @@ def run_prefill(args, w) -> int:
     nbytes = prefill_bytes(w)
     res = {
         "metric": PREFILL_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and free-list block ids)",
         "config": {"workload": f"{w.name}: {w.num_seqs} seqs, new tokens "
@@ -418,11 +417,35 @@ def run_block_pool(args) -> int:
     return 0
 
 
+def warm_up(step, requested) -> int:
+    """Run the untimed steps and return how many ran: exactly `requested` if
+    given, else at least 20 and as many more as take about 250 ms of wall time
+    (a GPU idle during set-up starts the timed steps at low clocks; a 0.5 ms
+    prefill step measured 5-18% slower after 5 warm-up steps than after 500)."""
+    import torch
+    if requested is not None:
+        for i in range(requested):
+            step(i)
+        return requested
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < 20 or time.perf_counter() - t0 < 0.25:
+        step(n)
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
+    return n
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: at least 20, and "
+                         "more until about 250 ms of steps have run, so that the GPU's "
+                         "clocks have ramped up; the count run is reported)")
     ap.add_argument("--config", default="llama3_8b_b64")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--partition", type=int, default=0)
@@ -504,14 +527,13 @@ def main() -> int:
         if ev is not None:
             ev[1].record(stream)
 
-    for i in range(args.warmup):
-        step(i)
+    warmup = warm_up(step, args.warmup)
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        step(warmup + i, events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -561,7 +583,7 @@ def main() -> int:
     achieved = b["decode"] / (dec_avg * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and free-list block ids)",
         "config": {"workload": f"{w.name}: {w.num_seqs} seqs, seq_lens "

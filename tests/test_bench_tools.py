@@ -59,3 +59,20 @@ def test_ingest_counters_scales_by_the_copy(tmp_path, monkeypatch):
     stored = json.load(open(tmp_path / "traffic.json"))
     assert stored["llama3_8b_b64"]["kernel_source_hash"] == bench.kernel_source_hash()
     assert stored["llama3_8b_b64"]["commands"] == ["cmd1", "cmd2"]
+
+
+def test_warm_up_runs_exactly_the_requested_steps():
+    seen = []
+    assert bench.warm_up(seen.append, 3) == 3
+    assert seen == [0, 1, 2]
+
+
+def test_default_warm_up_runs_at_least_twenty_steps_and_a_quarter_second(monkeypatch):
+    import torch
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda: None)
+    clock = iter(range(0, 10_000))                   # each reading 10 ms later
+    monkeypatch.setattr(bench.time, "perf_counter", lambda: next(clock) * 0.01)
+    seen = []
+    n = bench.warm_up(seen.append, None)
+    assert n == len(seen) and seen == list(range(n))
+    assert n >= 25                                   # 20 steps are not yet 250 ms
