@@ -14,7 +14,8 @@
 // Work decomposition and data flow:
 //   * A workgroup owns one (sequence, KV head, tile of QT = floor(128 / gqa)
 //     new tokens); the query tiles of one (sequence, KV head) are placed on
-//     one XCD so that they share its L2.  Its 128 query rows are (token, head)
+//     one XCD so that they share its L2, and the pairs are spread over the
+//     XCDs so that each gets an equal share of work (pf_item).  Its 128 query rows are (token, head)
 //     pairs, head fastest, so the gqa query heads of the KV head share every
 //     K/V tile it stages.  4 waves x 2 groups x 16 rows.
 //   * K/V tiles of 32 positions are gathered through the block table into LDS
@@ -110,6 +111,62 @@ __device__ __forceinline__ uint32_t pick_halves(uint32_t x, uint32_t y, int sel)
   return sel ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
 }
 
+// Workgroups are dealt to the 8 XCDs round-robin.  Work items are the
+// (sequence, KV head) pairs ordered by residue pair mod 8, each pair's query
+// tiles longest first, and XCD x takes the x-th of 8 near-equal contiguous
+// runs of that list.  An XCD thus holds whole pairs, whose query tiles share
+// its L2, drawn from all sequences: with 8 KV heads XCD x runs KV head x of
+// every sequence, so sequences of unequal context length load the XCDs
+// equally (runs of whole sequences per XCD left the busiest XCD with 1.6x the
+// mean work on a batch of chunks over mixed cached lengths).  Within a residue
+// class the pairs go by descending causal work q_len (2 len - q_len), ties by
+// index, so that each XCD starts its longest pairs first and ends on short
+// ones; classes of more than kPfSortMax pairs keep index order.  The ranking
+// is a strict total order, so any lengths give a permutation of the pairs.
+constexpr int kPfSortMax = 256;
+
+__device__ __forceinline__ void pf_item(const PrefillArgs& a, int* pair, int* qt) {
+  __shared__ long long sm_work[kPfSortMax];
+  __shared__ int sm_pick;
+  const int wg = (int)blockIdx.x, nwg = (int)gridDim.x, num_qt = a.num_qt;
+  const int num_pairs = a.num_seqs * a.num_kv_heads;
+  const int xcd = wg & 7, per = nwg >> 3, rem = nwg & 7;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + (wg >> 3);
+  const int rank = item / num_qt;                       // place of the pair in the list
+  *qt = num_qt - 1 - (item - rank * num_qt);
+  // the ceil((num_pairs - c) / 8) pairs of residue c follow those of residues < c
+  int c = 0, base = 0;
+  for (; c < 7; ++c) {
+    const int n = (num_pairs - c + 7) >> 3;
+    if (rank < base + n) break;
+    base += n;
+  }
+  const int n_c = (num_pairs - c + 7) >> 3;             // pairs of residue c
+  int j = rank - base;                                  // place within the class
+  if (n_c <= kPfSortMax) {                              // uniform
+    for (int t = threadIdx.x; t < n_c; t += blockDim.x) {
+      const int s = (c + 8 * t) / a.num_kv_heads;
+      const int len = a.seq_lens[s] > 0 ? a.seq_lens[s] : 0;
+      int ql = a.q_start[s + 1] - a.q_start[s];
+      ql = ql < 0 ? 0 : (ql < len ? ql : len);
+      sm_work[t] = (long long)ql * (2LL * len - ql);
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < n_c; t += blockDim.x) {
+      const long long wt = sm_work[t];
+      int r = 0;
+      for (int i = 0; i < n_c; ++i) {
+        const long long wi = sm_work[i];
+        r += (wi > wt) | ((wi == wt) & (i < t));
+      }
+      if (r == j) sm_pick = t;
+    }
+    __syncthreads();
+    j = sm_pick;
+  }
+  *pair = c + 8 * j;
+}
+
 template <int D, int BS, int KV>
 __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a) {
   typedef PfTile<D, BS, KV> T;
@@ -120,14 +177,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int h = lane >> 4, n = lane & 15;
-  // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that each
-  // XCD gets a contiguous run of (sequence, KV head, query tile) items and the
-  // query tiles of one (sequence, KV head) share that XCD's L2.
-  const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
-  const int xcd = wg & 7, per = nwg >> 3, rem = nwg & 7;
-  const int item = xcd * per + (xcd < rem ? xcd : rem) + (wg >> 3);
-  const int pair = item / a.num_qt;
-  const int qt = a.num_qt - 1 - (item - pair * a.num_qt);   // longest tiles first
+  int pair, qt;
+  pf_item(a, &pair, &qt);
   const int s = pair / a.num_kv_heads;
   const int kh = pair - s * a.num_kv_heads;
   const int g = a.gqa, QT = a.tile_tokens;
@@ -460,11 +511,8 @@ __global__ __launch_bounds__(kPfWaves * 64, D > 128 ? 1 : PA_PF_OCC) void prefil
 
   const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
   const int h = lane >> 4, n = lane & 15;
-  const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
-  const int xcd = wg & 7, per = nwg >> 3, rem = nwg & 7;
-  const int item = xcd * per + (xcd < rem ? xcd : rem) + (wg >> 3);
-  const int pair = item / a.num_qt;
-  const int qt = a.num_qt - 1 - (item - pair * a.num_qt);
+  int pair, qt;
+  pf_item(a, &pair, &qt);
   const int s = pair / a.num_kv_heads;
   const int kh = pair - s * a.num_kv_heads;
   const int g = a.gqa, QT = a.tile_tokens;
