@@ -23,6 +23,8 @@ from helpers import (DeviceCase, check_close, oracle_pool, prefill_row_index,
 
 pytestmark = pytest.mark.gpu
 
+_RS = np.random.RandomState(94)      # lengths of the many-pairs shape (drawn once, at import)
+
 SHAPES = {
     "tiny": W.prefill_tiny,
     "d128_bs16_g4": lambda: W.custom_prefill("pf", 81, [0, 5, 33, 300], [70, 31, 32, 129],
@@ -46,6 +48,10 @@ SHAPES = {
     "d256_bs16_g4": lambda: W.custom_prefill("pf", 92, [0, 5, 33, 300], [70, 31, 32, 129],
                                              16, 4, 256, 16),
     "d256_bs64_g8": lambda: W.custom_prefill("pf", 93, [0, 100], [45, 96], 16, 2, 256, 64),
+    # 2,600 (sequence, KV head) pairs: more than 256 per XCD, so the workgroups
+    # take the pairs in index order instead of ranking them by length
+    "many_pairs": lambda: W.custom_prefill("pf", 94, _RS.randint(0, 48, 325).tolist(),
+                                           _RS.randint(1, 12, 325).tolist(), 32, 8, 128, 16),
 }
 
 
