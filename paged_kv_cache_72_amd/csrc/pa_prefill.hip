@@ -15,9 +15,10 @@
 //   * A workgroup owns one (sequence, KV head, tile of QT = floor(128 / gqa)
 //     new tokens); the query tiles of one (sequence, KV head) are placed on
 //     one XCD so that they share its L2, and the pairs are spread over the
-//     XCDs so that each gets an equal share of work (pf_item).  Its 128 query rows are (token, head)
-//     pairs, head fastest, so the gqa query heads of the KV head share every
-//     K/V tile it stages.  4 waves x 2 groups x 16 rows.
+//     XCDs so that each gets an equal share of the work (pf_item).  Its 128
+//     query rows are (token, head) pairs, head fastest, so the gqa query
+//     heads of the KV head share every K/V tile it stages.  4 waves x 2
+//     groups x 16 rows.
 //   * K/V tiles of 32 positions are gathered through the block table into LDS
 //     by whole 16-byte row chunks, XOR-swizzled by chunk so that the reads
 //     below hit distinct banks.  fp16 pools (prefill_f16_kernel): straight from
