@@ -360,7 +360,7 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
     return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(PA_ERR_INVALID_ARG, "scale must be finite and positive");
-  const int32_t tile = pa::prefill_rows_per_workgroup() / gqa;
+  const int32_t tile = pa::prefill_rows_per_workgroup(g.head_dim) / gqa;
   const int64_t num_qt = cdiv64(max_q_len, tile);
   if ((int64_t)num_seqs * g.num_kv_heads * num_qt > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "num_seqs * num_kv_heads * cdiv(max_q_len, %d) too large",

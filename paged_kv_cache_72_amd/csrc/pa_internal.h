@@ -114,8 +114,8 @@ int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 // Validates a pool descriptor and resolves its geometry (PA_OK or a status).
 int check_pool(const pa_kv_pool* p, PoolGeom* g);
 
-// Query rows (token, head pairs) one prefill workgroup covers.
-int prefill_rows_per_workgroup();
+// Query rows (token, head pairs) one prefill workgroup covers at this head_dim.
+int prefill_rows_per_workgroup(int head_dim);
 
 // kv: 0 binary16, 1 e4m3fn, 2 e5m2.
 hipError_t launch_prefill(const PrefillArgs& a, int32_t head_dim, int32_t block_size, int kv,

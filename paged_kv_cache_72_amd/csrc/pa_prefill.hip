@@ -13,12 +13,13 @@
 //
 // Work decomposition and data flow:
 //   * A workgroup owns one (sequence, KV head, tile of QT = floor(128 / gqa)
-//     new tokens); the query tiles of one (sequence, KV head) are placed on
-//     one XCD so that they share its L2, and the pairs are spread over the
-//     XCDs so that each gets an equal share of the work (pf_item).  Its 128
-//     query rows are (token, head) pairs, head fastest, so the gqa query
-//     heads of the KV head share every K/V tile it stages.  4 waves x 2
-//     groups x 16 rows.
+//     new tokens; floor(64 / gqa) at head_dim 256); the query tiles of one
+//     (sequence, KV head) are placed on one XCD so that they share its L2,
+//     and the pairs are spread over the XCDs so that each gets an equal
+//     share of the work (pf_item).  Its 128 query rows are (token, head)
+//     pairs, head fastest, so the gqa query heads of the KV head share every
+//     K/V tile it stages.  4 waves x 2 groups x 16 rows (x 1 group at head_dim
+//     256, which keeps two workgroups per CU).
 //   * K/V tiles of 32 positions are gathered through the block table into LDS
 //     by whole 16-byte row chunks, XOR-swizzled by chunk so that the reads
 //     below hit distinct banks.  fp16 pools (prefill_f16_kernel): straight from
@@ -54,6 +55,9 @@ namespace {
 #endif
 #ifndef PA_PF_NBUF
 #define PA_PF_NBUF 3          // fp16 prefill: LDS tile buffers (tiles in flight + 1)
+#endif
+#ifndef PA_PF_G256
+#define PA_PF_G256 1          // fp16 prefill at head_dim 256: 16-row groups per wave
 #endif
 
 constexpr int kPfWaves = 4;
@@ -438,7 +442,13 @@ struct PfDma {
   static constexpr int TILE = kPfKeys * RB;
   static constexpr int BUF = 2 * TILE;                    // K tile then V tile
   static constexpr int DPT = 2 * NI;                      // loads per thread per tile
-  // head_dim 256: two buffers of 32 KiB (one workgroup per CU)
+  // 16-row query groups per wave and workgroups per CU: at head_dim 256 one
+  // group per wave keeps the accumulators and query operands at head_dim
+  // 128's register count, so two workgroups fit per CU (two groups need 452
+  // registers per lane: one workgroup)
+  static constexpr int G = D > 128 ? PA_PF_G256 : 2;
+  static constexpr int OCC = D > 128 && G > 1 ? 1 : PA_PF_OCC;
+  // head_dim 256: two buffers of 32 KiB
   static constexpr int NBUF = D > 128 ? 2 : PA_PF_NBUF;
   static constexpr int NST = D / 32;
   static constexpr int NB = D / 16;
@@ -501,11 +511,11 @@ __device__ __forceinline__ void vm_wait() {
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(kPfWaves * 64, D > 128 ? 1 : PA_PF_OCC) void prefill_f16_kernel(
+__global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kernel(
     PrefillArgs a, const int32_t* __restrict__ tables) {
   typedef PfDma<D> T;
-  constexpr int CPR = T::CPR, RB = T::RB, NST = T::NST, NB = T::NB;
-  constexpr bool kPrio = D <= 128;
+  constexpr int CPR = T::CPR, RB = T::RB, NST = T::NST, NB = T::NB, G = T::G;
+  constexpr bool kPrio = T::OCC >= 2;
   __shared__ __attribute__((aligned(1024))) char smem[T::NBUF * T::BUF];
   lds_char* const lds0 = (lds_char*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds0;
@@ -538,11 +548,11 @@ __global__ __launch_bounds__(kPfWaves * 64, D > 128 ? 1 : PA_PF_OCC) void prefil
   };
   const int32_t* bt = tables + (int64_t)s * a.max_blocks;
 
-  half8_t qop[2][NST];
-  int qpos[2];
+  half8_t qop[G][NST];
+  int qpos[G];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int r = 32 * wid + 16 * c + n;
+  for (int c = 0; c < G; ++c) {
+    const int r = 16 * G * wid + 16 * c + n;
     const int t = r / g, j = r - t * g;
     const int row = qs0 + q0 + t;
     const bool ok = t < QT && q0 + t < q_len && row >= 0 && row < a.total_q;
@@ -641,12 +651,17 @@ __global__ __launch_bounds__(kPfWaves * 64, D > 128 ? 1 : PA_PF_OCC) void prefil
                   8 * (m & 1);
   }
 
-  float4_t acc[2][NB];
+  float4_t acc[G][NB];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < G; ++c)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[c][nb] = {0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {kNegBig, kNegBig}, l_run[2] = {0.f, 0.f};
+  float m_run[G], l_run[G];
+#pragma unroll
+  for (int c = 0; c < G; ++c) {
+    m_run[c] = kNegBig;
+    l_run[c] = 0.f;
+  }
   const float sc = a.k_hs ? a.score_scale * a.k_hs[kh] : a.score_scale;
   const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
 
@@ -667,12 +682,12 @@ __global__ __launch_bounds__(kPfWaves * 64, D > 128 ? 1 : PA_PF_OCC) void prefil
     // softmax), so the matrix core is kept fed and the VALU work fills in
     // behind it (measured 1.5-3.5% faster; at head_dim 256, one wave per
     // SIMD, it only costs).
-    float4_t sa[2][2];
+    float4_t sa[G][2];
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < G; ++c) {
         sa[c][kb] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < NST; ++st)
@@ -689,7 +704,7 @@ __global__ __launch_bounds__(kPfWaves * 64, D > 128 ? 1 : PA_PF_OCC) void prefil
     }
     half8_t vop[NB];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < G; ++c) {
       float x[8];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -773,13 +788,13 @@ __global__ __launch_bounds__(kPfWaves * 64, D > 128 ? 1 : PA_PF_OCC) void prefil
   }
 
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < G; ++c) {
     float lt = xor_sum(l_run[c], 16);
     lt = xor_sum(lt, 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float li = __shfl(lt, 4 * h + i);
-      const int r = 32 * wid + 16 * c + 4 * h + i;
+      const int r = 16 * G * wid + 16 * c + 4 * h + i;
       const int t = r / g, j = r - t * g;
       const int row = qs0 + q0 + t;
       if (!(t < QT && q0 + t < q_len && row >= 0 && row < a.total_q)) continue;
@@ -822,7 +837,9 @@ hipError_t launch_pf_d(const PrefillArgs& a, int bs, int kv, hipStream_t stream)
 
 }  // namespace
 
-int prefill_rows_per_workgroup() { return kPfRows; }
+int prefill_rows_per_workgroup(int head_dim) {
+  return head_dim > 128 ? kPfWaves * 16 * PfDma<256>::G : kPfRows;
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, int32_t head_dim, int32_t block_size, int kv,
                           hipStream_t stream) {
