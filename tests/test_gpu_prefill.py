@@ -48,6 +48,10 @@ SHAPES = {
     "d256_bs16_g4": lambda: W.custom_prefill("pf", 92, [0, 5, 33, 300], [70, 31, 32, 129],
                                              16, 4, 256, 16),
     "d256_bs64_g8": lambda: W.custom_prefill("pf", 93, [0, 100], [45, 96], 16, 2, 256, 64),
+    # 64 query rows per workgroup at head_dim 256: groups that do not divide
+    # it (3: 21 tokens, 63 rows) and the largest group (16: 4 tokens)
+    "d256_bs32_g3": lambda: W.custom_prefill("pf", 95, [0, 50, 7], [70, 22, 43], 6, 2, 256, 32),
+    "d256_bs8_g16": lambda: W.custom_prefill("pf", 96, [3, 0], [9, 30], 16, 1, 256, 8),
     # 2,600 (sequence, KV head) pairs: more than 256 per XCD, so the workgroups
     # take the pairs in index order instead of ranking them by length
     "many_pairs": lambda: W.custom_prefill("pf", 94, _RS.randint(0, 48, 325).tolist(),
