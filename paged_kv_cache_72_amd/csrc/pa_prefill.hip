@@ -24,10 +24,13 @@
 //     by whole 16-byte row chunks, XOR-swizzled by chunk so that the reads
 //     below hit distinct banks.  fp16 pools (prefill_f16_kernel): straight from
 //     HBM into LDS with the global-to-LDS load, three buffers deep, V kept
-//     row-major and read with the LDS transpose read.  fp8 pools
-//     (prefill_kernel): loaded into registers one tile ahead and widened
-//     exactly to binary16 on the way into LDS (two buffers), V stored
-//     transposed.  Either way each tile costs one workgroup barrier.
+//     row-major and read with the LDS transpose read.  fp8 pools at head_dim
+//     128 (the same kernel): the stored bytes take the same global-to-LDS
+//     path into a three-slot staging ring, and each tile is widened exactly
+//     into the binary16 layout one tile ahead of its compute (two buffers).
+//     fp8 pools at head_dim 64 (prefill_kernel): loaded into registers one
+//     tile ahead and widened on the way into LDS (two buffers), V stored
+//     transposed.  Every kernel spends one workgroup barrier per tile.
 //   * Scores are computed transposed, S^T = K Q^T, with the 16x16x32 f16 MFMA:
 //     K rows are the A operand (from LDS), the group's 16 query rows the B
 //     operand (held in registers for the whole loop).  The K rows of a score
@@ -503,6 +506,12 @@ __device__ __forceinline__ float max3_raw(float a, float b, float c) {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
+template <int OFF>
+__device__ __forceinline__ void lds_w128(uint32_t addr, uint4 v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2"
+               : : "v"(addr), "v"(__builtin_bit_cast(u32x4_t, v)), "i"(OFF) : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   // vmcnt(N), expcnt and lgkmcnt unchanged (gfx9 encoding: vmcnt low bits
@@ -510,13 +519,29 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int D, int BS>
+// KV: pool format, 0 binary16; 1 e4m3fn or 2 e5m2 (head_dim 128).  fp8 tiles
+// go by the global-to-LDS load into a three-slot staging ring as stored
+// (row-major bytes), and each is widened exactly into the binary16 tile layout
+// below one tile ahead of its compute, two binary16 buffers deep; the math is
+// the same for every format.
+template <int D, int BS, int KV>
 __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kernel(
     PrefillArgs a, const int32_t* __restrict__ tables) {
   typedef PfDma<D> T;
-  constexpr int CPR = T::CPR, RB = T::RB, NST = T::NST, NB = T::NB, G = T::G;
+  constexpr int RB = T::RB, NST = T::NST, NB = T::NB, G = T::G;
   constexpr bool kPrio = T::OCC >= 2;
-  __shared__ __attribute__((aligned(1024))) char smem[T::NBUF * T::BUF];
+  static_assert(KV == 0 || D == 128, "fp8 tiles are staged for head_dim 128");
+  constexpr int NBUF = KV ? 2 : T::NBUF;        // binary16 tile buffers
+  constexpr int E = KV ? 1 : 2;                 // bytes per stored element
+  constexpr int SRB = D * E;                    // stored bytes per row
+  constexpr int SCPR = SRB / 16;                // 16-byte chunks per stored row
+  constexpr int SRPI = 1024 / SRB;              // rows per wave load
+  constexpr int NI = kPfKeys / SRPI / kPfWaves; // loads per wave per tile, each of K and V
+  constexpr int STILE = kPfKeys * SRB;          // fp8 staging: K tile then V tile per slot
+  constexpr int NRAW = KV ? 3 : 0;
+  static_assert(NI >= 1 && (KV == 0 || (NI == 1 && 2 * kPfKeys * SCPR == 2 * kPfWaves * 64)),
+                "load shape");
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * T::BUF + NRAW * 2 * STILE];
   lds_char* const lds0 = (lds_char*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds0;
 
@@ -570,38 +595,42 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
   // holds the row's chunk (lane % CPR) ^ swizzle.  Positions at or past kv_end
   // repeat position kv_end - 1, positions before the sliding window repeat its
   // first position (finite data; masked out of every score).
-  const char* const kbase = a.k + (int64_t)kh * D * 2;
-  const char* const vbase = a.v + (int64_t)kh * D * 2;
+  const char* const kbase = a.k + (int64_t)kh * D * E;
+  const char* const vbase = a.v + (int64_t)kh * D * E;
   // Block ids of the NI load groups of the next tile to issue, read one tile
   // ahead (and range-clamped only when used) so that the scalar loads'
   // latency passes behind a tile's compute.  A group's RPI rows lie in one
   // block (RPI divides block_size), also when its positions are clamped.
   auto group_block = [&](int t, int i) {
-    const int r0 = (wid * T::NI + i) * T::RPI;
+    const int r0 = (wid * NI + i) * SRPI;
     const int pr0 = t * kPfKeys + r0 < lo_c ? lo_c : t * kPfKeys + r0;
     const int pu = uni(pr0 < kv_end ? pr0 : kv_end - 1);
     return bt[(uint32_t)pu / BS];
   };
-  int next_blk[T::NI];
+  int next_blk[NI];
   // In-block byte offsets of this lane's K and V chunks for a tile with no
   // clamped position (tile start a multiple of 32, so the row in the block is
   // r mod block_size, plus the tile's offset in the block when blocks hold
   // more than one tile).
-  uint32_t koff[T::NI], voff[T::NI];
+  // (Staged fp8 rows are not swizzled: the widening places the chunks.)
+  auto chunk_of = [&](int r, int pch, bool v) {
+    return KV ? pch : (pch ^ (v ? T::vsw(r) : T::ksw(r)));
+  };
+  uint32_t koff[NI], voff[NI];
 #pragma unroll
-  for (int i = 0; i < T::NI; ++i) {
-    const int r = (wid * T::NI + i) * T::RPI + lane / CPR, pch = lane % CPR;
+  for (int i = 0; i < NI; ++i) {
+    const int r = (wid * NI + i) * SRPI + lane / SCPR, pch = lane % SCPR;
     const uint32_t in_blk = ((uint32_t)r & (BS - 1)) * (uint32_t)a.row_stride;
-    koff[i] = in_blk + ((uint32_t)(pch ^ T::ksw(r)) << 4);
-    voff[i] = in_blk + ((uint32_t)(pch ^ T::vsw(r)) << 4);
+    koff[i] = in_blk + ((uint32_t)chunk_of(r, pch, false) << 4);
+    voff[i] = in_blk + ((uint32_t)chunk_of(r, pch, true) << 4);
   }
   auto issue = [&](int t, int b) {
     const int kt = t * kPfKeys;
     const bool whole = kt >= lo_c && kt + kPfKeys <= kv_end;      // uniform
     const int64_t tile_in_blk = BS > kPfKeys ? (int64_t)(kt & (BS - 1)) * a.row_stride : 0;
 #pragma unroll
-    for (int i = 0; i < T::NI; ++i) {
-      const int r0 = (wid * T::NI + i) * T::RPI;
+    for (int i = 0; i < NI; ++i) {
+      const int r0 = (wid * NI + i) * SRPI;
       const int raw = next_blk[i];
       const int blk = raw < 0 ? 0 : (raw > a.num_blocks_m1 ? a.num_blocks_m1 : raw);
       // block base (uniform) plus a 32-bit per-lane offset inside the block
@@ -611,23 +640,49 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
       if (!whole) {
         // positions are clamped into [lo_c, kv_end - 1]: outside rows repeat
         // an in-window row (finite data, masked), never a released block
-        const int r = r0 + lane / CPR, pch = lane % CPR;
+        const int r = r0 + lane / SCPR, pch = lane % SCPR;
         const int pr = kt + r < lo_c ? lo_c : kt + r;
         const int pos = pr < kv_end ? pr : kv_end - 1;
         const uint32_t in_blk = ((uint32_t)pos & (BS - 1)) * (uint32_t)a.row_stride;
-        ko = in_blk + ((uint32_t)(pch ^ T::ksw(r)) << 4);
-        vo = in_blk + ((uint32_t)(pch ^ T::vsw(r)) << 4);
+        ko = in_blk + ((uint32_t)chunk_of(r, pch, false) << 4);
+        vo = in_blk + ((uint32_t)chunk_of(r, pch, true) << 4);
         base = blk_off;
       }
-      lds_char* kdst = lds0 + b * T::BUF + r0 * RB;
-      lds_char* vdst = kdst + T::TILE;
+      // binary16: tile buffer b; fp8: staging slot b
+      lds_char* kdst = KV ? lds0 + NBUF * T::BUF + b * 2 * STILE + r0 * SRB
+                          : lds0 + b * T::BUF + r0 * RB;
+      lds_char* vdst = kdst + (KV ? STILE : T::TILE);
       __builtin_amdgcn_global_load_lds((const void*)(kbase + base + ko),
                                        (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(vbase + base + vo),
                                        (__attribute__((address_space(3))) void*)vdst, 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < T::NI; ++i) next_blk[i] = group_block(t + 1, i);
+    for (int i = 0; i < NI; ++i) next_blk[i] = group_block(t + 1, i);
+  };
+
+  // fp8: widen staging slot `slot` into binary16 buffer `fb`.  Thread tid takes
+  // stored chunk tid of the K tile and of the V tile (row tid / SCPR, dims
+  // 16 (tid % SCPR) .. + 15, as the global-to-LDS load laid them out) and
+  // writes binary16 chunks 2c and 2c + 1 of that row at their swizzled slots.
+  auto widen_tile = [&](int slot, int fb) {
+    if constexpr (KV != 0) {
+      const uint32_t src = lds_base + NBUF * T::BUF + slot * 2 * STILE + tid * 16;
+      const int key = tid / SCPR, c = tid % SCPR;
+      half8_t rk = lds_b128<0>(src), rv = lds_b128<STILE>(src);
+      lgkm_wait<0>(rk);
+      lgkm_wait<0>(rv);
+      const uint4 rw[2] = {__builtin_bit_cast(uint4, rk), __builtin_bit_cast(uint4, rv)};
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 lo = widen8(make_uint2(rw[q].x, rw[q].y), KV);
+        const uint4 hi = widen8(make_uint2(rw[q].z, rw[q].w), KV);
+        const int sw = q ? T::vsw(key) : T::ksw(key);
+        const uint32_t row = lds_base + fb * T::BUF + q * T::TILE + key * RB;
+        lds_w128<0>(row + (((2 * c) ^ sw) << 4), lo);
+        lds_w128<0>(row + (((2 * c + 1) ^ sw) << 4), hi);
+      }
+    }
   };
 
   // ---- per-lane LDS read addresses (buffer 0; buffers differ by an immediate)
@@ -766,9 +821,40 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
   // flight), barrier (every wave's loads of tile t have landed and every wave
   // is done with tile t - 1, whose buffer tile t + 2 reuses), issue tile t + 2,
   // compute tile t.
-  constexpr int NB_ = T::NBUF;
 #pragma unroll
-  for (int i = 0; i < T::NI; ++i) next_blk[i] = group_block(t0, i);
+  for (int i = 0; i < NI; ++i) next_blk[i] = group_block(t0, i);
+  if constexpr (KV != 0) {
+    // fp8: staging slot of tile t is (t - t0) % 3, binary16 buffer (t - t0) % 2.
+    // At tile t: wait for tile t + 1's bytes (t + 2's may stay in flight),
+    // barrier (tile t is widened, every wave is done with tile t - 1's buffer
+    // and with tile t's staging slot), issue tile t + 3 into that slot, widen
+    // tile t + 1, compute tile t.
+    constexpr int DPT = 2 * NI;
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+      if (t0 + u < ntiles) issue(t0 + u, u);
+    if (ntiles - t0 >= 3) vm_wait<2 * DPT>();
+    else if (ntiles - t0 == 2) vm_wait<DPT>();
+    else vm_wait<0>();
+    __builtin_amdgcn_s_barrier();
+    widen_tile(0, 0);
+    int rs = 0, fb = 0;
+    for (int t = t0; t < ntiles; ++t) {
+      if (ntiles - 1 - t >= 2) vm_wait<DPT>();
+      else vm_wait<0>();
+      lgkm_wait_all_regs<0>();
+      __builtin_amdgcn_s_barrier();
+      if (t + 3 < ntiles) issue(t + 3, rs);
+      const int rn = rs == 2 ? 0 : rs + 1;
+      if (t + 1 < ntiles) widen_tile(rn, fb ^ 1);
+      const int kt = t * kPfKeys;
+      compute((uint32_t)(fb * T::BUF), kt, needs_mask(kt));
+      rs = rn;
+      fb ^= 1;
+    }
+  }
+  constexpr int NB_ = NBUF;
+  if constexpr (KV == 0) {
 #pragma unroll
   for (int u = 0; u < NB_ - 1; ++u)
     if (t0 + u < ntiles) issue(t0 + u, u);
@@ -785,6 +871,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
     const int kt = t * kPfKeys;
     compute((uint32_t)(b * T::BUF), kt, needs_mask(kt));
     b = b == NB_ - 1 ? 0 : b + 1;
+  }
   }
 
 #pragma unroll
@@ -811,10 +898,18 @@ hipError_t launch_pf_bs(const PrefillArgs& a, int kv, hipStream_t stream) {
   const dim3 grid((uint32_t)a.num_seqs * (uint32_t)a.num_kv_heads * (uint32_t)a.num_qt);
   const dim3 block(kPfWaves * 64);
   if (kv == 0) {
-    hipLaunchKernelGGL((prefill_f16_kernel<D, BS>), grid, block, 0, stream, a, a.block_tables);
+    hipLaunchKernelGGL((prefill_f16_kernel<D, BS, 0>), grid, block, 0, stream, a, a.block_tables);
     return hipGetLastError();
   }
-  if constexpr (D <= 128) {             // fp8 pools: head_dim 64 and 128
+  if constexpr (D == 128) {             // fp8 pools at head_dim 128: staged bytes, widened in LDS
+    if (kv == 1)
+      hipLaunchKernelGGL((prefill_f16_kernel<D, BS, 1>), grid, block, 0, stream, a, a.block_tables);
+    else if (kv == 2)
+      hipLaunchKernelGGL((prefill_f16_kernel<D, BS, 2>), grid, block, 0, stream, a, a.block_tables);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  if constexpr (D == 64) {              // fp8 pools at head_dim 64: register-staged kernel
     if (kv == 1) hipLaunchKernelGGL((prefill_kernel<D, BS, 1>), grid, block, 0, stream, a);
     else if (kv == 2) hipLaunchKernelGGL((prefill_kernel<D, BS, 2>), grid, block, 0, stream, a);
     else return hipErrorInvalidValue;

@@ -52,6 +52,15 @@ SHAPES = {
     # it (3: 21 tokens, 63 rows) and the largest group (16: 4 tokens)
     "d256_bs32_g3": lambda: W.custom_prefill("pf", 95, [0, 50, 7], [70, 22, 43], 6, 2, 256, 32),
     "d256_bs8_g16": lambda: W.custom_prefill("pf", 96, [3, 0], [9, 30], 16, 1, 256, 8),
+    # fp8 pools at head_dim 128 (staged as bytes, widened in LDS) at other
+    # block sizes, gqa and scale granularities
+    "d128_bs8_g4_e5m2": lambda: W.custom_prefill("pf", 97, [0, 30, 5], [40, 17, 70], 32, 8,
+                                                 128, 8, kv_dtype="fp8_e5m2"),
+    "d128_bs64_g7_e4m3": lambda: W.custom_prefill("pf", 98, [0, 100], [90, 33], 28, 4, 128,
+                                                  64, kv_dtype="fp8_e4m3fn"),
+    "d128_bs128_g2_e4m3_head": lambda: W.custom_prefill("pf", 99, [130, 0], [20, 50], 8, 4,
+                                                        128, 128, kv_dtype="fp8_e4m3fn",
+                                                        scale_grain="head"),
     # 2,600 (sequence, KV head) pairs: more than 256 per XCD, so the workgroups
     # take the pairs in index order instead of ranking them by length
     "many_pairs": lambda: W.custom_prefill("pf", 94, _RS.randint(0, 48, 325).tolist(),
@@ -90,7 +99,8 @@ def _relabel(w, seed):
                                tok_slot=slot.astype(np.int64), pad_block=int(perm[w.pad_block]))
 
 
-@pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "d64_bs8_g2_e5m2"])
+@pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "d64_bs8_g2_e5m2",
+                                  "d128_bs64_g7_e4m3"])
 def test_prefill_relabelling_and_reruns_are_bitwise_equal(name):
     w = SHAPES[name]()
     dc = DeviceCase(w, poison=True)
@@ -148,7 +158,7 @@ def test_prefill_full_size_sampled(name, make, nrows):
 
 
 @pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "d64_bs16_g16",
-                                  "d128_bs16_g4_e4m3", "d256_bs16_g4"])
+                                  "d128_bs16_g4_e4m3", "d128_bs8_g4_e5m2", "d256_bs16_g4"])
 @pytest.mark.parametrize("win", [1, 31, 32, 33, 100])
 def test_sliding_window_prefill(name, win):
     w0 = SHAPES[name]()
