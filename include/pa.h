@@ -208,7 +208,12 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
  * num_q_heads must be a multiple of num_kv_heads with a ratio of at most 16.
  * No workspace is needed.  total_q, num_seqs or max_q_len of 0 is a no-op.
  * Outputs are bitwise reproducible and do not depend on which physical ids
- * hold the blocks. */
+ * hold the blocks.  Non-finite pool data: the K and V rows of a 32-position
+ * tile are shared by all query rows of a workgroup, so an infinite V element
+ * at an in-context position that a query does not see (a later position of
+ * the same tile) reaches that query as 0 * inf = NaN; positions outside the
+ * context or the window never do.  Pools written by pa_reshape_and_cache hold
+ * no infinities (the fp8 encoders saturate). */
 int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q,
                const int32_t* q_start, int32_t num_seqs, int32_t num_q_heads,
                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,

@@ -661,22 +661,28 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
     for (int i = 0; i < NI; ++i) next_blk[i] = group_block(t + 1, i);
   };
 
-  // fp8: widen staging slot `slot` into binary16 buffer `fb`.  Thread tid takes
-  // stored chunk tid of the K tile and of the V tile (row tid / SCPR, dims
-  // 16 (tid % SCPR) .. + 15, as the global-to-LDS load laid them out) and
+  // fp8: widen staging slot `slot` (tile t) into binary16 buffer `fb`.  Thread
+  // tid takes stored chunk tid of the K tile and of the V tile (row tid / SCPR,
+  // dims 16 (tid % SCPR) .. + 15, as the global-to-LDS load laid them out) and
   // writes binary16 chunks 2c and 2c + 1 of that row at their swizzled slots.
-  auto widen_tile = [&](int slot, int fb) {
+  // Rows of positions outside [lo_c, kv_end) (loaded as repeats of an
+  // in-range row) are written as zeros, so that a repeated V row holding an
+  // infinity (e5m2 has them) meets its zero weight as 0 * 0, not 0 * inf.
+  auto widen_tile = [&](int slot, int fb, int t) {
     if constexpr (KV != 0) {
       const uint32_t src = lds_base + NBUF * T::BUF + slot * 2 * STILE + tid * 16;
       const int key = tid / SCPR, c = tid % SCPR;
+      const int pos = t * kPfKeys + key;
+      const bool in_range = pos >= lo_c && pos < kv_end;
       half8_t rk = lds_b128<0>(src), rv = lds_b128<STILE>(src);
       lgkm_wait<0>(rk);
       lgkm_wait<0>(rv);
       const uint4 rw[2] = {__builtin_bit_cast(uint4, rk), __builtin_bit_cast(uint4, rv)};
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const uint4 lo = widen8(make_uint2(rw[q].x, rw[q].y), KV);
-        const uint4 hi = widen8(make_uint2(rw[q].z, rw[q].w), KV);
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        const uint4 lo = in_range ? widen8(make_uint2(rw[q].x, rw[q].y), KV) : z;
+        const uint4 hi = in_range ? widen8(make_uint2(rw[q].z, rw[q].w), KV) : z;
         const int sw = q ? T::vsw(key) : T::ksw(key);
         const uint32_t row = lds_base + fb * T::BUF + q * T::TILE + key * RB;
         lds_w128<0>(row + (((2 * c) ^ sw) << 4), lo);
@@ -837,7 +843,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
     else if (ntiles - t0 == 2) vm_wait<DPT>();
     else vm_wait<0>();
     __builtin_amdgcn_s_barrier();
-    widen_tile(0, 0);
+    widen_tile(0, 0, t0);
     int rs = 0, fb = 0;
     for (int t = t0; t < ntiles; ++t) {
       if (ntiles - 1 - t >= 2) vm_wait<DPT>();
@@ -846,7 +852,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
       __builtin_amdgcn_s_barrier();
       if (t + 3 < ntiles) issue(t + 3, rs);
       const int rn = rs == 2 ? 0 : rs + 1;
-      if (t + 1 < ntiles) widen_tile(rn, fb ^ 1);
+      if (t + 1 < ntiles) widen_tile(rn, fb ^ 1, t + 1);
       const int kt = t * kPfKeys;
       compute((uint32_t)(fb * T::BUF), kt, needs_mask(kt));
       rs = rn;
