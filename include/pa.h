@@ -77,10 +77,9 @@ typedef enum {
  * block_size * num_kv_heads * head_dim * elem_bytes; a larger stride (a
  * multiple of 16) lets K and V blocks interleave in one allocation.
  * Supported: head_dim 64, 128 or 256 (256, the head size of one of the pages'
- * model examples, "Paging saves no KV bytes", section 5; pa_prefill at 256
- * needs a binary16 pool); block_size 8, 16, 32, 64 or 128 (the range
- * the pages give the block size, 16 being the default: "vLLM intro part 2",
- * section 3.3); k_base, v_base 16-byte
+ * model examples, "Paging saves no KV bytes", section 5); block_size 8, 16,
+ * 32, 64 or 128 (the range the pages give the block size, 16 being the
+ * default: "vLLM intro part 2", section 3.3); k_base, v_base 16-byte
  * aligned.  k_scale / v_scale are the per-pool fp8 scales (ignored for f16);
  * k_head_scales / v_head_scales optionally give one scale per KV head.
  * flags: PA_POOL_SHARED_BLOCKS when some blocks are read by several sequences

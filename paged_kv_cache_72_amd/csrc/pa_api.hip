@@ -341,10 +341,6 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
   if (total_q < 0) return fail(PA_ERR_INVALID_ARG, "total_q %d < 0", total_q);
   if (max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "max_q_len %d < 0", max_q_len);
-  if (g.head_dim > 128 && g.elem_bytes != 2)
-    return fail(PA_ERR_UNSUPPORTED,
-                "pa_prefill at head_dim %d needs a binary16 pool (fp8 pools: 64 and 128)",
-                g.head_dim);
   if (num_q_heads < 1 || num_q_heads % g.num_kv_heads)
     return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
                 num_q_heads, g.num_kv_heads);

@@ -519,7 +519,7 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// KV: pool format, 0 binary16; 1 e4m3fn or 2 e5m2 (head_dim 128).  fp8 tiles
+// KV: pool format, 0 binary16; 1 e4m3fn or 2 e5m2 (head_dim 128, 256).  fp8 tiles
 // go by the global-to-LDS load into a three-slot staging ring as stored
 // (row-major bytes), and each is widened exactly into the binary16 tile layout
 // below one tile ahead of its compute, two binary16 buffers deep; the math is
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
   typedef PfDma<D> T;
   constexpr int RB = T::RB, NST = T::NST, NB = T::NB, G = T::G;
   constexpr bool kPrio = T::OCC >= 2;
-  static_assert(KV == 0 || D == 128, "fp8 tiles are staged for head_dim 128");
+  static_assert(KV == 0 || D >= 128, "fp8 tiles are staged for head_dim 128 and 256");
   constexpr int NBUF = KV ? 2 : T::NBUF;        // binary16 tile buffers
   constexpr int E = KV ? 1 : 2;                 // bytes per stored element
   constexpr int SRB = D * E;                    // stored bytes per row
@@ -539,8 +539,9 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
   constexpr int NI = kPfKeys / SRPI / kPfWaves; // loads per wave per tile, each of K and V
   constexpr int STILE = kPfKeys * SRB;          // fp8 staging: K tile then V tile per slot
   constexpr int NRAW = KV ? 3 : 0;
-  static_assert(NI >= 1 && (KV == 0 || (NI == 1 && 2 * kPfKeys * SCPR == 2 * kPfWaves * 64)),
-                "load shape");
+  // stored 16-byte chunks of the K tile (and of the V tile) each thread widens
+  constexpr int WCH = KV ? kPfKeys * SCPR / (kPfWaves * 64) : 1;
+  static_assert(NI >= 1 && (KV == 0 || WCH * kPfWaves * 64 == kPfKeys * SCPR), "load shape");
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * T::BUF + NRAW * 2 * STILE];
   lds_char* const lds0 = (lds_char*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds0;
@@ -662,16 +663,20 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
   };
 
   // fp8: widen staging slot `slot` (tile t) into binary16 buffer `fb`.  Thread
-  // tid takes stored chunk tid of the K tile and of the V tile (row tid / SCPR,
-  // dims 16 (tid % SCPR) .. + 15, as the global-to-LDS load laid them out) and
-  // writes binary16 chunks 2c and 2c + 1 of that row at their swizzled slots.
+  // tid takes stored chunks ch = tid + 256 w of the K tile and of the V tile
+  // (row ch / SCPR, dims 16 (ch % SCPR) .. + 15, as the global-to-LDS load laid
+  // them out) and writes binary16 chunks 2c and 2c + 1 of that row at their
+  // swizzled slots.
   // Rows of positions outside [lo_c, kv_end) (loaded as repeats of an
   // in-range row) are written as zeros, so that a repeated V row holding an
   // infinity (e5m2 has them) meets its zero weight as 0 * 0, not 0 * inf.
   auto widen_tile = [&](int slot, int fb, int t) {
     if constexpr (KV != 0) {
-      const uint32_t src = lds_base + NBUF * T::BUF + slot * 2 * STILE + tid * 16;
-      const int key = tid / SCPR, c = tid % SCPR;
+#pragma unroll
+     for (int w = 0; w < WCH; ++w) {
+      const int ch = tid + kPfWaves * 64 * w;
+      const uint32_t src = lds_base + NBUF * T::BUF + slot * 2 * STILE + ch * 16;
+      const int key = ch / SCPR, c = ch % SCPR;
       const int pos = t * kPfKeys + key;
       const bool in_range = pos >= lo_c && pos < kv_end;
       half8_t rk = lds_b128<0>(src), rv = lds_b128<STILE>(src);
@@ -688,6 +693,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
         lds_w128<0>(row + (((2 * c) ^ sw) << 4), lo);
         lds_w128<0>(row + (((2 * c + 1) ^ sw) << 4), hi);
       }
+     }
     }
   };
 
@@ -907,7 +913,7 @@ hipError_t launch_pf_bs(const PrefillArgs& a, int kv, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_f16_kernel<D, BS, 0>), grid, block, 0, stream, a, a.block_tables);
     return hipGetLastError();
   }
-  if constexpr (D == 128) {             // fp8 pools at head_dim 128: staged bytes, widened in LDS
+  if constexpr (D >= 128) {             // fp8 pools at head_dim 128, 256: staged bytes, widened in LDS
     if (kv == 1)
       hipLaunchKernelGGL((prefill_f16_kernel<D, BS, 1>), grid, block, 0, stream, a, a.block_tables);
     else if (kv == 2)
@@ -946,7 +952,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t head_dim, int32_t block_
                           hipStream_t stream) {
   if (head_dim == 128) return launch_pf_d<128>(a, block_size, kv, stream);
   if (head_dim == 64) return launch_pf_d<64>(a, block_size, kv, stream);
-  if (head_dim == 256 && kv == 0) return launch_pf_d<256>(a, block_size, kv, stream);
+  if (head_dim == 256) return launch_pf_d<256>(a, block_size, kv, stream);
   return hipErrorInvalidValue;
 }
 

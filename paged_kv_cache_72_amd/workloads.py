@@ -511,6 +511,15 @@ def prefill_chunked_8k_d256(seed: int = 7213) -> Workload:
                                 16, 8192)
 
 
+def prefill_chunked_8k_d256_fp8(seed: int = 7213) -> Workload:
+    """prefill_chunked_8k_d256 with the KV cache stored as OCP fp8 e4m3fn,
+    one scale per tensor."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(7)[6])
+    ctx = (rng.integers(0, 8, size=16) * 512).tolist()
+    return _prefill_independent("prefill_chunked_8k_d256_fp8", seed, ctx, [512] * 16, 16, 4,
+                                256, 16, 8192, kv_dtype="fp8_e4m3fn")
+
+
 def prefill_prefix_hit(seed: int = 7214) -> Workload:
     """The pages' prefix-cache hit: a 2,000-token system prompt (125 full
     blocks of 16) is cached once and shared by 32 requests; each prefills its
@@ -550,6 +559,7 @@ PREFILL_CONFIGS = {
     "prefill_prefix_hit": prefill_prefix_hit,
     "prefill_chunked_8k_fp8": prefill_chunked_8k_fp8,
     "prefill_chunked_8k_d256": prefill_chunked_8k_d256,
+    "prefill_chunked_8k_d256_fp8": prefill_chunked_8k_d256_fp8,
 }
 
 

@@ -202,8 +202,6 @@ def _prefill(so, pool, T=10, S=2, Hq=32, maxq=8, **kw):
 def test_prefill_validation(so):
     assert _prefill(so, None) == L.PA_ERR_INVALID_ARG
     assert _prefill(so, _pool(head_dim=96)) == L.PA_ERR_UNSUPPORTED
-    assert _prefill(so, _pool(head_dim=256, dtype=L.PA_KV_FP8_E4M3FN, k_scale=0.5,
-                              v_scale=0.5)) == L.PA_ERR_UNSUPPORTED      # fp16 pools only
     assert "head_dim" in L.pa_last_error()
     assert _prefill(so, _pool(), Hq=30) == L.PA_ERR_INVALID_ARG          # 30 % 8 != 0
     assert _prefill(so, _pool(num_kv_heads=1), Hq=32) == L.PA_ERR_UNSUPPORTED

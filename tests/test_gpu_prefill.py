@@ -44,7 +44,7 @@ SHAPES = {
     "d128_bs16_g4_e4m3_head": lambda: W.custom_prefill("pf", 91, [0, 40], [64, 25], 32, 8, 128,
                                                        16, kv_dtype="fp8_e4m3fn",
                                                        scale_grain="head"),
-    # head_dim 256 (binary16 pools): the hybrid example's full-attention shape
+    # head_dim 256: the hybrid example's full-attention shape
     "d256_bs16_g4": lambda: W.custom_prefill("pf", 92, [0, 5, 33, 300], [70, 31, 32, 129],
                                              16, 4, 256, 16),
     "d256_bs64_g8": lambda: W.custom_prefill("pf", 93, [0, 100], [45, 96], 16, 2, 256, 64),
@@ -52,6 +52,11 @@ SHAPES = {
     # it (3: 21 tokens, 63 rows) and the largest group (16: 4 tokens)
     "d256_bs32_g3": lambda: W.custom_prefill("pf", 95, [0, 50, 7], [70, 22, 43], 6, 2, 256, 32),
     "d256_bs8_g16": lambda: W.custom_prefill("pf", 96, [3, 0], [9, 30], 16, 1, 256, 8),
+    "d256_bs16_g4_e4m3": lambda: W.custom_prefill("pf", 100, [0, 5, 33, 300], [70, 31, 32, 129],
+                                                  16, 4, 256, 16, kv_dtype="fp8_e4m3fn"),
+    "d256_bs32_g2_e5m2_head": lambda: W.custom_prefill("pf", 101, [0, 64], [45, 20], 8, 4, 256,
+                                                       32, kv_dtype="fp8_e5m2",
+                                                       scale_grain="head"),
     # fp8 pools at head_dim 128 (staged as bytes, widened in LDS) at other
     # block sizes, gqa and scale granularities
     "d128_bs8_g4_e5m2": lambda: W.custom_prefill("pf", 97, [0, 30, 5], [40, 17, 70], 32, 8,
@@ -135,6 +140,7 @@ FULL = [
     ("prefill_prefix_hit", W.prefill_prefix_hit, 24),
     ("prefill_chunked_8k_fp8", W.prefill_chunked_8k_fp8, 24),
     ("prefill_chunked_8k_d256", W.prefill_chunked_8k_d256, 24),
+    ("prefill_chunked_8k_d256_fp8", W.prefill_chunked_8k_d256_fp8, 24),
 ]
 
 
