@@ -27,7 +27,9 @@
 //     row-major and read with the LDS transpose read.  fp8 pools at head_dim
 //     128 (the same kernel): the stored bytes take the same global-to-LDS
 //     path into a three-slot staging ring, and each tile is widened exactly
-//     into the binary16 layout one tile ahead of its compute (two buffers).
+//     into the binary16 layout one tile ahead of its compute (two buffers;
+//     at head_dim 256 one buffer and two slots, widened between two barriers,
+//     so that two workgroups fit per CU).
 //     fp8 pools at head_dim 64 (prefill_kernel): loaded into registers one
 //     tile ahead and widened on the way into LDS (two buffers), V stored
 //     transposed.  Every kernel spends one workgroup barrier per tile.
@@ -531,14 +533,17 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
   constexpr int RB = T::RB, NST = T::NST, NB = T::NB, G = T::G;
   constexpr bool kPrio = T::OCC >= 2;
   static_assert(KV == 0 || D >= 128, "fp8 tiles are staged for head_dim 128 and 256");
-  constexpr int NBUF = KV ? 2 : T::NBUF;        // binary16 tile buffers
+  // fp8 at head_dim 256: one binary16 buffer and two staging slots (66 KB),
+  // so that two workgroups fit per CU
+  constexpr bool F8W = KV != 0 && D > 128;
+  constexpr int NBUF = KV ? (F8W ? 1 : 2) : T::NBUF;   // binary16 tile buffers
   constexpr int E = KV ? 1 : 2;                 // bytes per stored element
   constexpr int SRB = D * E;                    // stored bytes per row
   constexpr int SCPR = SRB / 16;                // 16-byte chunks per stored row
   constexpr int SRPI = 1024 / SRB;              // rows per wave load
   constexpr int NI = kPfKeys / SRPI / kPfWaves; // loads per wave per tile, each of K and V
   constexpr int STILE = kPfKeys * SRB;          // fp8 staging: K tile then V tile per slot
-  constexpr int NRAW = KV ? 3 : 0;
+  constexpr int NRAW = KV ? (F8W ? 2 : 3) : 0;
   // stored 16-byte chunks of the K tile (and of the V tile) each thread widens
   constexpr int WCH = KV ? kPfKeys * SCPR / (kPfWaves * 64) : 1;
   static_assert(NI >= 1 && (KV == 0 || WCH * kPfWaves * 64 == kPfKeys * SCPR), "load shape");
@@ -835,7 +840,31 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
   // compute tile t.
 #pragma unroll
   for (int i = 0; i < NI; ++i) next_blk[i] = group_block(t0, i);
-  if constexpr (KV != 0) {
+  if constexpr (F8W) {
+    // fp8, head_dim 256: staging slot of tile t is (t - t0) % 2, one binary16
+    // buffer.  At tile t: wait for its bytes (tile t + 1's may stay in
+    // flight), barrier (every wave is done computing tile t - 1), widen it,
+    // barrier (every wave is done widening: its slot is free), issue tile
+    // t + 2 into that slot, compute tile t.
+    constexpr int DPT = 2 * NI;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (t0 + u < ntiles) issue(t0 + u, u);
+    int rs = 0;
+    for (int t = t0; t < ntiles; ++t) {
+      if (ntiles - 1 - t >= 1) vm_wait<DPT>();
+      else vm_wait<0>();
+      lgkm_wait_all_regs<0>();
+      __builtin_amdgcn_s_barrier();
+      widen_tile(rs, 0, t);
+      lgkm_wait_all_regs<0>();
+      __builtin_amdgcn_s_barrier();
+      if (t + 2 < ntiles) issue(t + 2, rs);
+      const int kt = t * kPfKeys;
+      compute(0u, kt, needs_mask(kt));
+      rs ^= 1;
+    }
+  } else if constexpr (KV != 0) {
     // fp8: staging slot of tile t is (t - t0) % 3, binary16 buffer (t - t0) % 2.
     // At tile t: wait for tile t + 1's bytes (t + 2's may stay in flight),
     // barrier (tile t is widened, every wave is done with tile t - 1's buffer
