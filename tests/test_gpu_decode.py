@@ -223,11 +223,11 @@ def test_batch_past_the_flat_limit():
     check_close(w, ys, r, "9000 seqs split")
 
 
-def _every_byte_pool(dtype):
-    """Pool whose block 1, slot 0 holds all 256 byte values in V (K bytes 0):
-    a query over that one token gets weight 1 on it, so its output is the
-    widened V row itself."""
-    Hkv, D = 2, 128
+def _every_byte_pool(dtype, D=128):
+    """Pool whose block 1, slot 0 holds all 256 byte values in V (K bytes 0),
+    over 256 / D KV heads: a query over that one token gets weight 1 on it,
+    so its output is the widened V row itself."""
+    Hkv = 256 // D
     pool = L.KVPool.allocate(4, 16, Hkv, D, dtype, 1.0, 1.0, fill_bits=0)
     pool.v[1, 0] = torch.from_numpy(np.arange(256, dtype=np.uint8).reshape(Hkv, D)).cuda()
     return pool
@@ -244,26 +244,28 @@ def _assert_widened_exactly(dtype, y):
 
 @pytest.mark.parametrize("dtype", ["fp8_e4m3fn", "fp8_e5m2"])
 @pytest.mark.parametrize("part", [-1, 0, 32])
-def test_fp8_widening_exact_for_every_byte(dtype, part):
+@pytest.mark.parametrize("D", [128, 256])
+def test_fp8_widening_exact_for_every_byte(dtype, part, D):
     """Decode's fp8 widening equals the oracle's decoder bit for bit on all
     256 byte values, NaN bytes giving NaN and infinities staying infinite."""
-    say(f"fp8 widening decode {dtype} partition={part}")
-    pool = _every_byte_pool(dtype)
-    q = torch.randn(1, 2, 128, device="cuda").half()
+    say(f"fp8 widening decode {dtype} partition={part} head_dim={D}")
+    pool = _every_byte_pool(dtype, D)
+    q = torch.randn(1, 256 // D, D, device="cuda").half()
     out = torch.empty_like(q)
     bt = torch.tensor([[1]], dtype=torch.int32, device="cuda")
     lens = torch.tensor([1], dtype=torch.int32, device="cuda")
-    ws = L.alloc_workspace(pool, 1, 2, 1, part)
+    ws = L.alloc_workspace(pool, 1, 256 // D, 1, part)
     L.pa_decode(pool, out, q, bt, lens, 1, 0.088, part, ws)
     _assert_widened_exactly(dtype, out.cpu().numpy())
 
 
 @pytest.mark.parametrize("dtype", ["fp8_e4m3fn", "fp8_e5m2"])
-def test_fp8_widening_exact_for_every_byte_prefill(dtype):
+@pytest.mark.parametrize("D", [128, 256])
+def test_fp8_widening_exact_for_every_byte_prefill(dtype, D):
     """The same through pa_prefill: one new token whose context is itself."""
-    say(f"fp8 widening prefill {dtype}")
-    pool = _every_byte_pool(dtype)
-    q = torch.randn(1, 2, 128, device="cuda").half()
+    say(f"fp8 widening prefill {dtype} head_dim={D}")
+    pool = _every_byte_pool(dtype, D)
+    q = torch.randn(1, 256 // D, D, device="cuda").half()
     out = torch.empty_like(q)
     qs = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
     bt = torch.tensor([[1]], dtype=torch.int32, device="cuda")
