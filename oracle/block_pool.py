@@ -1,64 +1,68 @@
 """Plain model of the host block pool with prefix caching.
 
 TEST INFRASTRUCTURE ONLY: the tests compare the native pool in libpa.so with
-this model; nothing in the library imports it.  Lists and dicts, O(n)
-operations, written from the pages' rules so that a reader can check each step
-against them:
+this model; nothing in the library imports it.  Python lists and dicts, O(n)
+operations, built from the rules the pages state (not from any code they
+print), so that a reader can check each rule in isolation:
 
-  * every block whose reference count is 0 sits in ONE free queue, whether it
-    was never used or still carries the hash of a cached block; the head is
-    handed out first ("KV Cache memory core", section 2.3, BlockPool sketch
-    and the six-block walkthrough T0-T4);
-  * handing a block out that still carries a hash removes that hash from the
-    cache index -- that is the eviction (same passage; "vLLM intro part 2",
-    section 6.3 step 3);
-  * freeing drops the count; a block reaching 0 goes to the TAIL if it carries
-    a hash (kept for future hits as long as possible) and to the HEAD if not
-    (handed out first) ("KV Cache memory core", section 2.3 free_blocks notes
-    and walkthrough T2); a request frees its blocks from last to first
-    ("vLLM intro part 2", section 6.3 free steps);
-  * a prefix hit on a block with count 0 takes it out of the middle of the
-    queue and raises its count ("touch"; same passages, walkthrough T4);
-  * block hashes are chained: h_i = H(h_{i-1}, the block's tokens, extra keys),
-    with a fixed NONE_HASH before the first block; only full blocks get a
-    hash; lookup walks the chain from the first block and stops at the first
-    miss ("vLLM intro part 2", section 6.1; "KV Cache memory core", section
-    4.1 chained-hash diagram);
-  * H is SHA-256 ("vLLM intro part 2", section 6.1: the default since 0.11).
+  R1  one queue holds every block nobody holds (count 0), whether it was never
+      used or still keeps the digest of a cached block; blocks are handed out
+      from its front ("KV Cache memory core", section 2.3, and its six-block
+      walkthrough T0-T4);
+  R2  a block handed out loses the digest it kept, and the cache forgets it:
+      eviction happens only as a side effect of handing out (same section;
+      "vLLM intro part 2", section 6.3, step 3);
+  R3  a block whose count falls to 0 joins the back of the queue if it keeps
+      a digest (so it stays available for hits as long as possible) and the
+      front otherwise; a request gives its blocks back last to first (same
+      sections, walkthrough T2);
+  R4  a prefix hit on a block nobody holds takes it out of the queue wherever
+      it sits and counts it as held (walkthrough T4);
+  R5  digests are chained over full blocks: the digest of block i covers the
+      digest of block i - 1 (a fixed all-zero value before block 0), block i's
+      token ids and the extra keys; a lookup follows the chain from block 0
+      and stops at the first digest the cache does not know ("vLLM intro
+      part 2", section 6.1; "KV Cache memory core", section 4.1);
+  R6  the digest function is SHA-256 ("vLLM intro part 2", section 6.1).
 
-Readings where the pages leave a step open (each also listed in the design
-notes): NONE_HASH is 32 zero bytes; H hashes the parent's 32 bytes, then the
-block's token ids as little-endian int32, then the extra-key bytes; several
-unhashed blocks freed in one call are prepended one after another (so the
-last one freed ends at the head); a request's lookup never covers its last
-token (at least one token is computed), so at most (n - 1) // block_size
-blocks hit; when several blocks carry the same hash a lookup takes the one
-cached first.
+Readings where the pages leave a step open (also listed in the design notes):
+the all-zero value is 32 bytes; the digest input is the parent's 32 bytes,
+then the token ids as little-endian int32, then the extra-key bytes; blocks
+without a digest given back in one call go to the front one after another (the
+last one given back ends up first); a request's lookup never covers its last
+token, so at most (n - 1) // block_size blocks hit; when several blocks keep
+the same digest a lookup takes the one cached first.  A sliding-window
+release marks the request's released entries -1; such entries are skipped by
+every later request-level operation.
 """
 from __future__ import annotations
 
 import hashlib
-import struct
 from typing import Dict, List, Optional, Sequence
 
-NONE_HASH = bytes(32)
+import numpy as np
+
+NONE_HASH = bytes(32)        # the digest "before" block 0 (R5)
 
 
-def hash_block_tokens(parent: Optional[bytes], tokens: Sequence[int],
-                      extra: bytes = b"") -> bytes:
-    """h = SHA-256(parent hash | token ids as int32 LE | extra keys)."""
-    p = NONE_HASH if parent is None else parent
-    body = b"".join(struct.pack("<i", int(t)) for t in tokens)
-    return hashlib.sha256(p + body + extra).digest()
+def block_digest(parent: Optional[bytes], token_ids: Sequence[int],
+                 extra: bytes = b"") -> bytes:
+    """R5/R6: SHA-256 over parent digest (all-zero before block 0), the token
+    ids as little-endian int32, then the extra-key bytes."""
+    head = NONE_HASH if parent is None else bytes(parent)
+    ids = np.asarray(list(token_ids), dtype="<i4").tobytes()
+    return hashlib.sha256(head + ids + bytes(extra)).digest()
 
 
-def chain_hashes(tokens: Sequence[int], block_size: int, extra: bytes = b"") -> List[bytes]:
-    """Hashes of the full blocks of a token sequence, chained from NONE_HASH."""
-    out, parent = [], None
-    for i in range(len(tokens) // block_size):
-        parent = hash_block_tokens(parent, tokens[i * block_size:(i + 1) * block_size], extra)
-        out.append(parent)
-    return out
+def prompt_digests(token_ids: Sequence[int], block_size: int, extra: bytes = b"") -> List[bytes]:
+    """R5: digests of the full blocks of a token sequence, each chained on the
+    one before."""
+    toks = list(token_ids)
+    digests: List[bytes] = []
+    for start in range(0, len(toks) - block_size + 1, block_size):
+        prev = digests[-1] if digests else None
+        digests.append(block_digest(prev, toks[start:start + block_size], extra))
+    return digests
 
 
 class PoolError(Exception):
@@ -66,117 +70,128 @@ class PoolError(Exception):
 
 
 class BlockPoolModel:
+    """count[b]: holders of block b; kept[b]: the digest block b keeps (or
+    None); queue: ids nobody holds, front first; cached: digest -> ids that
+    keep it, in the order they were cached; requests: id -> block table row."""
+
     def __init__(self, num_blocks: int, block_size: int):
         self.block_size = block_size
-        self.ref = [0] * num_blocks
-        self.hash: List[Optional[bytes]] = [None] * num_blocks
-        self.free: List[int] = list(range(num_blocks))          # head = index 0
-        self.index: Dict[bytes, List[int]] = {}                   # hash -> ids, first cached first
+        self.count = [0] * num_blocks
+        self.kept: List[Optional[bytes]] = [None] * num_blocks
+        self.queue: List[int] = list(range(num_blocks))
+        self.cached: Dict[bytes, List[int]] = {}
         self.requests: Dict[int, List[int]] = {}
 
-    # ---------------------------------------------------------------- pool
+    # ------------------------------------------------------------ R1-R4
     def num_free(self) -> int:
-        return len(self.free)
+        return len(self.queue)
+
+    def _forget_digest(self, b: int) -> None:
+        """R2: drop block b's digest from the block and from the cache."""
+        d = self.kept[b]
+        if d is None:
+            return
+        self.kept[b] = None
+        owners = self.cached[d]
+        owners.remove(b)
+        if not owners:
+            del self.cached[d]
 
     def get_new_blocks(self, n: int) -> List[int]:
-        if n > len(self.free):
+        """R1 + R2: the first n queued blocks, each now held once."""
+        if n > len(self.queue):
             raise PoolError("not enough free blocks")
-        out = self.free[:n]
-        del self.free[:n]
-        for b in out:
-            h = self.hash[b]
-            if h is not None:                       # eviction
-                self.index[h].remove(b)
-                if not self.index[h]:
-                    del self.index[h]
-                self.hash[b] = None
-            self.ref[b] += 1
-        return out
+        given = [self.queue.pop(0) for _ in range(n)]
+        for b in given:
+            self._forget_digest(b)
+            self.count[b] = 1
+        return given
 
     def free_blocks(self, ordered: Sequence[int]) -> None:
+        """R3: one count less per listed id, in the order given."""
+        if any(self.count[b] < 1 for b in ordered):
+            raise PoolError("a listed block is not held")
         for b in ordered:
-            if self.ref[b] <= 0:
-                raise PoolError(f"block {b} is not held")
-        for b in ordered:
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                if self.hash[b] is not None:
-                    self.free.append(b)
-                else:
-                    self.free.insert(0, b)
+            self.count[b] -= 1
+            if self.count[b]:
+                continue
+            if self.kept[b] is None:
+                self.queue.insert(0, b)
+            else:
+                self.queue.append(b)
 
     def touch(self, blocks: Sequence[int]) -> None:
+        """R4: count a hit block as held, leaving the queue if nobody held it."""
         for b in blocks:
-            if self.ref[b] == 0:
-                self.free.remove(b)
-            self.ref[b] += 1
+            if self.count[b] == 0:
+                self.queue.remove(b)
+            self.count[b] += 1
 
-    def cache_full_block(self, b: int, h: bytes) -> None:
-        if self.hash[b] is not None:
-            return                                  # already cached under its hash
-        self.hash[b] = h
-        self.index.setdefault(h, []).append(b)
+    def cache_full_block(self, b: int, digest: bytes) -> None:
+        """Let block b keep this digest (a block keeps its first digest)."""
+        if self.kept[b] is None:
+            self.kept[b] = digest
+            self.cached.setdefault(digest, []).append(b)
 
-    def lookup(self, hashes: Sequence[bytes]) -> List[int]:
-        """Cached blocks for the leading run of hashes (no side effects)."""
-        out = []
-        for h in hashes:
-            ids = self.index.get(h)
-            if not ids:
+    def lookup(self, digests: Sequence[bytes]) -> List[int]:
+        """R5: blocks for the leading run of known digests (changes nothing)."""
+        hits: List[int] = []
+        for d in digests:
+            if d not in self.cached:
                 break
-            out.append(ids[0])
-        return out
+            hits.append(self.cached[d][0])
+        return hits
 
-    # ---------------------------------------------------------------- requests
+    # ------------------------------------------------------------ requests
     def allocate_request(self, rid: int, tokens: Sequence[int], extra: bytes = b"") -> int:
-        """Give request rid blocks for its tokens, reusing the cached prefix.
-        Returns the number of tokens whose K/V are already cached."""
-        bs = self.block_size
-        n = len(tokens)
-        hashes = chain_hashes(tokens, bs, extra)
-        usable = (n - 1) // bs if n > 0 else 0
-        hits = self.lookup(hashes[:usable])
-        need = -(-n // bs) - len(hits)
-        if need > len(self.free) - sum(1 for b in hits if self.ref[b] == 0):
+        """Blocks for a new request: the cached prefix (never its last token),
+        then fresh blocks.  Returns how many tokens are already cached."""
+        bs, n = self.block_size, len(tokens)
+        lookable = (n - 1) // bs if n else 0
+        hits = self.lookup(prompt_digests(tokens, bs, extra)[:lookable])
+        fresh = -(-n // bs) - len(hits)
+        queued_hits = sum(1 for b in hits if self.count[b] == 0)
+        if fresh > len(self.queue) - queued_hits:
             raise PoolError("not enough free blocks")
         self.touch(hits)
-        fresh = self.get_new_blocks(need)
-        self.requests[rid] = hits + fresh
+        self.requests[rid] = hits + self.get_new_blocks(fresh)
         return len(hits) * bs
 
     def cache_request(self, rid: int, tokens: Sequence[int], extra: bytes = b"") -> None:
-        """After the request's K/V are written: register its full blocks."""
-        hashes = chain_hashes(tokens, self.block_size, extra)
-        for b, h in zip(self.requests[rid], hashes):
-            self.cache_full_block(b, h)
+        """Once the request's K/V are written, its full blocks keep their
+        digests; entries released by a sliding window (-1) are skipped."""
+        row = self.requests[rid]
+        for j, d in enumerate(prompt_digests(tokens, self.block_size, extra)[:len(row)]):
+            if row[j] >= 0:
+                self.cache_full_block(row[j], d)
 
     def append_slot(self, rid: int, num_tokens_after: int) -> None:
         """Grow request rid to hold num_tokens_after tokens."""
-        need = -(-num_tokens_after // self.block_size) - len(self.requests[rid])
-        if need > 0:
-            self.requests[rid] += self.get_new_blocks(need)
+        row = self.requests[rid]
+        more = -(-num_tokens_after // self.block_size) - len(row)
+        if more > 0:
+            row.extend(self.get_new_blocks(more))
 
     def free_request(self, rid: int) -> None:
-        self.free_blocks([b for b in reversed(self.requests.pop(rid)) if b >= 0])
+        row = self.requests.pop(rid)
+        self.free_blocks([b for b in row[::-1] if b >= 0])
 
     def remove_skipped_blocks(self, rid: int, num_tokens: int, window: int) -> int:
-        """Sliding window: the next query (position num_tokens) sees positions
-        from num_tokens - window + 1; blocks wholly before that are released,
-        last to first, and their table entries become -1 ("Paging saves no KV
-        bytes", section 5)."""
-        first = num_tokens - window + 1
-        if first <= 0:
-            return 0
-        blocks = self.requests[rid]
-        n = min(first // self.block_size, len(blocks))
-        out = [b for b in reversed(blocks[:n]) if b >= 0]
-        self.free_blocks(out)
-        for j in range(n):
-            blocks[j] = -1
-        return len(out)
+        """Sliding window ("Paging saves no KV bytes", section 5): the request's
+        next query sits at position num_tokens and sees its last `window`
+        positions, num_tokens - window + 1 onward.  Give back, last to first,
+        every block all of whose positions lie before that, and mark its
+        entry -1.  Returns how many blocks were given back."""
+        first_seen = num_tokens - window + 1
+        row = self.requests[rid]
+        before = min(max(first_seen, 0) // self.block_size, len(row))
+        gone = [row[j] for j in range(before - 1, -1, -1) if row[j] >= 0]
+        self.free_blocks(gone)
+        row[:before] = [-1] * before
+        return len(gone)
 
-    # ---------------------------------------------------------------- state
+    # ------------------------------------------------------------ state
     def state(self) -> dict:
-        return {"free": list(self.free), "ref": list(self.ref),
-                "hashed": sorted(b for b, h in enumerate(self.hash) if h is not None),
-                "index": {h.hex(): list(v) for h, v in self.index.items()}}
+        return {"free": list(self.queue), "ref": list(self.count),
+                "hashed": sorted(b for b, d in enumerate(self.kept) if d is not None),
+                "index": {d.hex(): list(v) for d, v in self.cached.items()}}

@@ -95,6 +95,19 @@ int check_pool(const pa_kv_pool* p, PoolGeom* g) {
   return PA_OK;
 }
 
+hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
+                         int32_t head_dim, int32_t block_size, int kv, bool stream_kv, int mode,
+                         hipStream_t stream) {
+#define PA_DK(D, KV)                                                                        \
+  if (head_dim == D && kv == KV)                                                            \
+    return launch_decode_dk<D, KV>(a, f, num_seqs, block_size, stream_kv, mode, stream);
+  PA_DK(128, 0) PA_DK(128, 1) PA_DK(128, 2)
+  PA_DK(64, 0) PA_DK(64, 1) PA_DK(64, 2)
+  PA_DK(256, 0) PA_DK(256, 1) PA_DK(256, 2)
+#undef PA_DK
+  return hipErrorInvalidValue;
+}
+
 }  // namespace pa
 
 using pa::check_pool;

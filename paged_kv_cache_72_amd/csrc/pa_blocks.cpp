@@ -462,6 +462,7 @@ int pa_bp_cache_request(pa_block_pool* p, int64_t rid, const int32_t* tokens, in
   const std::vector<pa_block_hash> h = chain(tokens, n, p->block_size, extra, extra_len);
   const size_t m = std::min(h.size(), it->second.size());
   for (size_t i = 0; i < m; ++i) {
+    if (it->second[i] < 0) continue;           // released by the sliding window
     HashKey k;
     std::memcpy(k.b, h[i].bytes, 32);
     p->cache(it->second[i], k);

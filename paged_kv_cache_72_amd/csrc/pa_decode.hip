@@ -625,6 +625,14 @@ __device__ __forceinline__ int range_of(int64_t t, int64_t T, int64_t NR) {
   return (int)(((t + 1) * NR - 1) / T);
 }
 
+// True when range r owns no unit (more ranges than units this call: the host
+// sizes the ranges from max_seq_len, and windows shorten what is read).  Its
+// waves return at once, so the merge must not read its record slots, which
+// hold whatever an earlier call left there.
+__device__ __forceinline__ bool range_empty(int64_t r, int64_t T, int64_t NR) {
+  return r * T / NR == (r + 1) * T / NR;
+}
+
 // Units are (sequence, 16-token tile) pairs in sequence order.  Range r is
 // walked by the Hkv consecutive waves r*Hkv + kh, one per KV head, so the heads
 // of a block are read together.  A sequence that lies inside one range is
@@ -831,6 +839,7 @@ __global__ __launch_bounds__(NG * D) void flat_merge_kernel(DecodeArgs a, FlatAr
   float M = kNegBig, L = 0.f, O = 0.f;
 #pragma unroll 4
   for (int r = r_first + grp; r <= r_last; r += NG) {
+    if (range_empty(r, T, NR)) continue;       // owns no unit: wrote no record this call
     const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
     const float* p = f.slots + ((int64_t)(r * a.num_kv_heads + kh) * 2 + slot) * rec;
     const float2 ml = ((const float2*)(p + g * D))[hl];
@@ -885,6 +894,7 @@ __global__ __launch_bounds__(256) void flat_merge_rows_kernel(DecodeArgs a, Flat
   for (int e = 0; e < DPL; ++e) O[e] = 0.f;
 #pragma unroll 4
   for (int r = r_first; r <= r_last; ++r) {
+    if (range_empty(r, T, NR)) continue;       // owns no unit: wrote no record this call
     const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
     const float* p = f.slots + ((int64_t)(r * a.num_kv_heads + kh) * 2 + slot) * rec;
     const float2 ml = ((const float2*)(p + g * D))[hl];
@@ -956,44 +966,40 @@ hipError_t launch_nt(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, b
                    : launch_typed<D, BS, KV, false>(a, f, num_seqs, mode, stream);
 }
 
-template <int D, int BS>
-hipError_t launch_bs(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int kv,
-                     bool stream_kv, int mode, hipStream_t stream) {
-  switch (kv) {
-    case 0: return launch_nt<D, BS, 0>(a, f, num_seqs, stream_kv, mode, stream);
-    case 1: return launch_nt<D, BS, 1>(a, f, num_seqs, stream_kv, mode, stream);
-    case 2: return launch_nt<D, BS, 2>(a, f, num_seqs, stream_kv, mode, stream);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <int D>
-hipError_t launch_d(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int32_t bs, int kv,
-                    bool stream_kv, int mode, hipStream_t stream) {
-  switch (bs) {
-    case 8: return launch_bs<D, 8>(a, f, num_seqs, kv, stream_kv, mode, stream);
-    case 16: return launch_bs<D, 16>(a, f, num_seqs, kv, stream_kv, mode, stream);
-    case 32: return launch_bs<D, 32>(a, f, num_seqs, kv, stream_kv, mode, stream);
-    case 64: return launch_bs<D, 64>(a, f, num_seqs, kv, stream_kv, mode, stream);
-    case 128: return launch_bs<D, 128>(a, f, num_seqs, kv, stream_kv, mode, stream);
-  }
-  return hipErrorInvalidValue;
-}
-
 }  // namespace
 
-int decode_waves_per_workgroup() { return kWaves; }
-
-hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
-                         int32_t head_dim, int32_t block_size, int kv, bool stream_kv, int mode,
-                         hipStream_t stream) {
-  if (head_dim == 128)
-    return launch_d<128>(a, f, num_seqs, block_size, kv, stream_kv, mode, stream);
-  if (head_dim == 64)
-    return launch_d<64>(a, f, num_seqs, block_size, kv, stream_kv, mode, stream);
-  if (head_dim == 256)
-    return launch_d<256>(a, f, num_seqs, block_size, kv, stream_kv, mode, stream);
+// Launchers of one (head_dim, KV format) pair over every block size.  Each
+// pair is explicitly instantiated below; the build compiles this file once per
+// pair (PA_DECODE_SLICE_D / PA_DECODE_SLICE_KV) so the slices compile in
+// parallel, and a plain compile instantiates all of them.
+template <int D, int KV>
+hipError_t launch_decode_dk(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int32_t bs,
+                            bool stream_kv, int mode, hipStream_t stream) {
+  switch (bs) {
+    case 8: return launch_nt<D, 8, KV>(a, f, num_seqs, stream_kv, mode, stream);
+    case 16: return launch_nt<D, 16, KV>(a, f, num_seqs, stream_kv, mode, stream);
+    case 32: return launch_nt<D, 32, KV>(a, f, num_seqs, stream_kv, mode, stream);
+    case 64: return launch_nt<D, 64, KV>(a, f, num_seqs, stream_kv, mode, stream);
+    case 128: return launch_nt<D, 128, KV>(a, f, num_seqs, stream_kv, mode, stream);
+  }
   return hipErrorInvalidValue;
 }
+
+#define PA_DECODE_INSTANTIATE(D, KV)                                                        \
+  template hipError_t launch_decode_dk<D, KV>(const DecodeArgs&, const FlatArgs*, int32_t, \
+                                              int32_t, bool, int, hipStream_t);
+#if defined(PA_DECODE_SLICE_D) && defined(PA_DECODE_SLICE_KV)
+PA_DECODE_INSTANTIATE(PA_DECODE_SLICE_D, PA_DECODE_SLICE_KV)
+#else
+PA_DECODE_INSTANTIATE(64, 0)
+PA_DECODE_INSTANTIATE(64, 1)
+PA_DECODE_INSTANTIATE(64, 2)
+PA_DECODE_INSTANTIATE(128, 0)
+PA_DECODE_INSTANTIATE(128, 1)
+PA_DECODE_INSTANTIATE(128, 2)
+PA_DECODE_INSTANTIATE(256, 0)
+PA_DECODE_INSTANTIATE(256, 1)
+PA_DECODE_INSTANTIATE(256, 2)
+#endif
 
 }  // namespace pa

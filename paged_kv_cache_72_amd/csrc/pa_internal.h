@@ -72,13 +72,16 @@ hipError_t launch_reshape_and_cache(const PoolGeom& g, const _Float16* k_new,
                                     hipStream_t stream);
 hipError_t launch_copy_blocks(const PoolGeom& g, const int64_t* pairs, int64_t n,
                               hipStream_t stream);
-int decode_waves_per_workgroup();
 // stream_kv: read K/V tiles with the streaming cache policy (pools without
 // blocks shared between sequences of the batch).
 // kv: 0 binary16, 1 e4m3fn, 2 e5m2.
 hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
                          int32_t head_dim, int32_t block_size, int kv, bool stream_kv, int mode,
                          hipStream_t stream);
+// The decode launchers of one (head_dim, kv) pair (pa_decode.hip).
+template <int D, int KV>
+hipError_t launch_decode_dk(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
+                            int32_t block_size, bool stream_kv, int mode, hipStream_t stream);
 
 // Prefill over the paged cache: sequence s owns q rows [q_start[s], q_start[s+1]);
 // its new tokens are the last q_len of its seq_lens[s] positions.

@@ -237,9 +237,12 @@ def pa_decode_workspace_size(pool: KVPool, num_seqs: int, num_q_heads: int, max_
 
 def alloc_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_seq_len: int,
                     partition_size: int = 0, device="cuda") -> Optional[torch.Tensor]:
-    """Workspace for pa_decode.  The kernels write every word of it they read
-    within the same call, so its contents between calls do not matter; it is
-    zero-filled only so that dumps of unused parts are tidy."""
+    """Workspace for pa_decode.  Within one call the kernels read only words
+    that the same call wrote (the flat schedule's merge skips ranges that own
+    no unit; the split reduce reads only partitions inside the context and the
+    window), so its contents between calls do not matter and one workspace may
+    be reused by consecutive calls on a stream.  It is zero-filled only so
+    that dumps of unused parts are tidy."""
     n = pa_decode_workspace_size(pool, num_seqs, num_q_heads, max_seq_len, partition_size)
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 

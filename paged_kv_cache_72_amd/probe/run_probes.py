@@ -3,15 +3,9 @@
     python -m paged_kv_cache_72_amd.probe.run_probes
 
 Measurement only: loads libpa_probe.so (built by ``__graft_entry__.build()``)
-and prints one markdown table.  Rows:
-
-- wave-contiguous reads: each wave streams its own contiguous chunk, 16 B per
-  lane per load, ``unroll`` loads in flight (the best plain-read rate);
-- tile gather: the decode kernels' read pattern without their arithmetic --
-  per KV head, 16-token tiles of K and V from shuffled 32 KB blocks of two
-  [20000, 16, 8, 128] binary16 pools -- with the three lane layouts of
-  ``stream_read.hip`` (0: 64 x 16 B pieces per load instruction, 1: 16 x 64 B,
-  2: 4 whole 256-B rows).
+and prints one markdown table of wave-contiguous reads: each wave streams its
+own contiguous chunk, 16 B per lane per load, ``unroll`` loads in flight (the
+best plain-read rate, the ceiling the decode kernels are compared with).
 
 Times are medians of 30 launches bracketed by HIP events, rotating over three
 buffers so that no launch finds its data in the 256 MB Infinity Cache.
@@ -35,8 +29,6 @@ def _lib():
     L = C.CDLL(LIB)
     L.pa_probe_wave_chunk.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int32, C.c_void_p,
                                       C.c_void_p]
-    L.pa_probe_tile_gather.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32,
-                                       C.c_int64, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
     return L
 
 
@@ -74,21 +66,6 @@ def main() -> int:
             rows.append((f"wave-contiguous read, {waves} waves, {unroll} KiB in flight per wave",
                          nbytes, t))
     del bufs
-
-    nb, hkv, listed = 20000, 8, 9330
-    pools = [(torch.ones(nb * 16 * hkv * 128, dtype=torch.float16, device="cuda"),
-              torch.ones(nb * 16 * hkv * 128, dtype=torch.float16, device="cuda"))
-             for _ in range(3)]
-    ids = np.random.default_rng(1).permutation(nb)[:listed].astype(np.int32)
-    blocks = torch.from_numpy(ids).cuda()
-    nbytes = listed * 16 * hkv * 128 * 2 * 2
-    for lane_map in (0, 1, 2):
-        for ranges in (256, 384):
-            assert ranges * hkv * 64 <= sink.numel()
-            t = _median_us(lambda i: L.pa_probe_tile_gather(
-                pools[i % 3][0].data_ptr(), pools[i % 3][1].data_ptr(), blocks.data_ptr(), listed,
-                hkv, ranges, 1, lane_map, sink.data_ptr(), st))
-            rows.append((f"tile gather, lane layout {lane_map}, {ranges * hkv} waves", nbytes, t))
 
     print("| probe | bytes | median µs | GB/s | % of 8 TB/s |")
     print("|---|---|---|---|---|")

@@ -83,92 +83,3 @@ int pa_probe_wave_chunk(const void* src, int64_t waves, int64_t steps_per_wave, 
   return (int)hipGetLastError();
 }
 }
-
-// ---------------------------------------------------------------- tile gather
-// The decode kernels' read pattern without their arithmetic: wave w serves KV
-// head w % Hkv of range w / Hkv, a contiguous slice of `blocks` (physical ids
-// of 16-token blocks, [nlisted]); for every block it reads the head's 16 rows
-// of 256 bytes (head_dim 128, binary16) from the K pool and from the V pool
-// with four 16-byte loads per lane, UT blocks in flight.  Pools are
-// [*, 16, Hkv, 128] binary16.  Lane layouts of load u (0..3):
-//   MAP 0: token l & 15, bytes (l >> 4) * 64 + 16 u   (64 pieces of 16 B)
-//   MAP 1: token l & 15, bytes u * 64 + (l >> 4) * 16 (16 pieces of 64 B)
-//   MAP 2: token 4 u + (l >> 4), bytes (l & 15) * 16  (4 whole 256-B rows)
-namespace {
-template <int MAP>
-__device__ __forceinline__ int64_t lane_offset(int lane, int u, int64_t row) {
-  if constexpr (MAP == 0) return (lane & 15) * row + (lane >> 4) * 64 + 16 * u;
-  else if constexpr (MAP == 1) return (lane & 15) * row + u * 64 + (lane >> 4) * 16;
-  else return (4 * u + (lane >> 4)) * row + (lane & 15) * 16;
-}
-
-template <int UT, int MAP>
-__global__ __launch_bounds__(256) void tile_gather_kernel(const char* __restrict__ kp,
-                                                          const char* __restrict__ vp,
-                                                          const int32_t* __restrict__ blocks,
-                                                          int64_t nlisted, int32_t hkv,
-                                                          int64_t ranges,
-                                                          uint32_t* __restrict__ sink) {
-  const int lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t r = w / hkv, kh = w % hkv;
-  uint32_t acc = 0;
-  if (r < ranges) {
-    const int64_t b0 = r * nlisted / ranges, b1 = (r + 1) * nlisted / ranges;
-    const int64_t row = (int64_t)hkv * 256;                   // bytes per token row
-    for (int64_t b = b0; b < b1; b += UT) {
-      u32x4 kv[UT][4], vv[UT][4];
-#pragma unroll
-      for (int t = 0; t < UT; ++t) {
-        const int64_t bb = b + t < b1 ? b + t : b1 - 1;
-        const int64_t base = (int64_t)blocks[bb] * 16 * row + kh * 256;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t o = base + lane_offset<MAP>(lane, u, row);
-          kv[t][u] = __builtin_nontemporal_load((const u32x4*)(kp + o));
-          vv[t][u] = __builtin_nontemporal_load((const u32x4*)(vp + o));
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < UT; ++t)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc ^= kv[t][u].x ^ vv[t][u].w;
-    }
-  }
-  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
-}
-
-template <int MAP>
-int launch_gather(const char* k, const char* v, const int32_t* blocks, int64_t nlisted,
-                  int32_t hkv, int64_t ranges, int32_t ut, uint32_t* sink, hipStream_t stream) {
-  const int64_t waves = (ranges * hkv + 3) / 4 * 4;
-  const dim3 grid((uint32_t)(waves / 4)), block(256);
-  if (ut == 1)
-    hipLaunchKernelGGL((tile_gather_kernel<1, MAP>), grid, block, 0, stream, k, v, blocks, nlisted, hkv, ranges, sink);
-  else if (ut == 2)
-    hipLaunchKernelGGL((tile_gather_kernel<2, MAP>), grid, block, 0, stream, k, v, blocks, nlisted, hkv, ranges, sink);
-  else if (ut == 4)
-    hipLaunchKernelGGL((tile_gather_kernel<4, MAP>), grid, block, 0, stream, k, v, blocks, nlisted, hkv, ranges, sink);
-  else
-    return (int)hipErrorInvalidValue;
-  return (int)hipGetLastError();
-}
-}  // namespace
-
-extern "C" {
-// waves = ranges * hkv rounded up to a multiple of 4; sink holds waves * 64
-// words.  Every id in blocks[0 .. nlisted) must be a valid block of both pools.
-int pa_probe_tile_gather(const void* k_pool, const void* v_pool, const int32_t* blocks,
-                         int64_t nlisted, int32_t hkv, int64_t ranges, int32_t tiles_in_flight,
-                         int32_t lane_map, uint32_t* sink, hipStream_t stream) {
-  if (nlisted <= 0 || hkv <= 0 || ranges <= 0 || ranges > nlisted) return (int)hipErrorInvalidValue;
-  const char* k = (const char*)k_pool;
-  const char* v = (const char*)v_pool;
-  switch (lane_map) {
-    case 0: return launch_gather<0>(k, v, blocks, nlisted, hkv, ranges, tiles_in_flight, sink, stream);
-    case 1: return launch_gather<1>(k, v, blocks, nlisted, hkv, ranges, tiles_in_flight, sink, stream);
-    case 2: return launch_gather<2>(k, v, blocks, nlisted, hkv, ranges, tiles_in_flight, sink, stream);
-    default: return (int)hipErrorInvalidValue;
-  }
-}
-}

@@ -58,13 +58,23 @@ class DeviceCase:
     def write_step(self):
         L.pa_reshape_and_cache(self.pool, self.k_new, self.v_new, self.slot_new)
 
-    def decode(self, partition_size: int = 0, out=None) -> torch.Tensor:
+    def decode(self, partition_size: int = 0, out=None, max_seq_len=None,
+               dirty_workspace: bool = False) -> torch.Tensor:
+        """pa_decode of the step.  max_seq_len: the host bound passed (default
+        the true maximum; a looser bound changes the plan, not the result).
+        dirty_workspace: run in the shared workspace of dirty_workspace(),
+        which holds NaN and whatever earlier calls left, instead of a fresh
+        zeroed one."""
         w = self.w
         out = self.out if out is None else out
-        ws = L.alloc_workspace(self.pool, w.num_seqs, w.num_q_heads, w.max_seq_len,
-                               partition_size)
-        L.pa_decode(self.pool, out, self.q, self.bt, self.lens, w.max_seq_len, w.scale,
-                    partition_size, ws)
+        msl = w.max_seq_len if max_seq_len is None else int(max_seq_len)
+        if dirty_workspace:
+            n = L.pa_decode_workspace_size(self.pool, w.num_seqs, w.num_q_heads, msl,
+                                           partition_size)
+            ws = dirty_workspace_of(n)
+        else:
+            ws = L.alloc_workspace(self.pool, w.num_seqs, w.num_q_heads, msl, partition_size)
+        L.pa_decode(self.pool, out, self.q, self.bt, self.lens, msl, w.scale, partition_size, ws)
         return out
 
     def prefill(self, out=None) -> torch.Tensor:
@@ -82,6 +92,21 @@ class DeviceCase:
             k, v = k.index_select(0, b), v.index_select(0, b)
         dt = np.uint16 if self.w.kv_dtype == "f16" else np.uint8
         return k.cpu().numpy().view(dt), v.cpu().numpy().view(dt)
+
+
+_DIRTY = []
+
+
+def dirty_workspace_of(nbytes: int):
+    """One workspace shared by every caller, filled with 0xFF bytes (float32
+    NaN) when it is first made or grown and never cleared afterwards, so each
+    call sees NaN or the records of the calls before it.  None for 0 bytes."""
+    if nbytes == 0:
+        return None
+    if not _DIRTY or _DIRTY[0].numel() < nbytes:
+        size = max(nbytes, 2 * _DIRTY[0].numel() if _DIRTY else 1 << 20)
+        _DIRTY[:] = [torch.full((size,), 0xFF, dtype=torch.uint8, device="cuda")]
+    return _DIRTY[0][:nbytes]
 
 
 def oracle_pool(w: W.Workload, poison: bool = False, token_idx=None) -> O.HostPool:

@@ -1,4 +1,4 @@
-"""Host block arithmetic, refcount/COW bookkeeping and the workload generator,
+"""Host block arithmetic, copy-on-write on the native pool and the workload generator,
 pinned to numbers and walkthroughs the pages print (CPU only).
 
 Fixtures with their citations live in tests/golden/block_math.json.
@@ -11,15 +11,15 @@ import pytest
 
 from paged_kv_cache_72_amd import sizing
 from paged_kv_cache_72_amd import workloads as W
-from paged_kv_cache_72_amd.block_manager import BlockManager, cdiv
+from paged_kv_cache_72_amd import lib as L
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "block_math.json")))
 
 
 @pytest.mark.parametrize("case", GOLD["cdiv"], ids=lambda c: f"{c['tokens']}@{c['block_size']}")
 def test_block_count_examples(case):
-    assert cdiv(case["tokens"], case["block_size"]) == case["blocks"]
     assert W.cdiv(case["tokens"], case["block_size"]) == case["blocks"]
+    assert sizing.cdiv(case["tokens"], case["block_size"]) == case["blocks"]
     if "slots" in case:
         assert sizing.slots_allocated(case["tokens"], case["block_size"]) == case["slots"]
 
@@ -58,66 +58,23 @@ def test_page_and_capacity_arithmetic():
     assert sizing.page_bytes(16, 4, 128, 1) * 2 == page
 
 
-def test_cow_walkthrough_from_the_pages():
-    """Prompt of 40 tokens in blocks 7, 3, 12; fork n=4; seq0 writes the 9th slot
-    of block 12 -> new block 20, table [7, 3, 20], block 12 keeps 3 refs."""
-    wt = GOLD["cow_walkthrough"]
-    bm = BlockManager(64, 16, free_order=wt["free_order"])
-    assert bm.allocate("prompt", wt["prompt_tokens"]) == wt["prompt_blocks"]
-    assert [bm.ref_cnt[b] for b in wt["prompt_blocks"]] == [1, 1, 1]
-    kids = ["seq0", "seq1", "seq2", "seq3"]
-    bm.fork("prompt", kids)
-    assert [bm.ref_cnt[b] for b in wt["prompt_blocks"]] == [4, 4, 4]
-    for k in kids:
-        assert bm.table(k) == wt["prompt_blocks"]
-    slot, copies = bm.append_slot("seq0")
-    assert copies == [(wt["prompt_blocks"][2], wt["new_block"])]
-    assert bm.table("seq0") == wt["table_after"]
-    assert slot == wt["new_block"] * 16 + wt["write_offset"]
-    assert bm.ref_cnt[wt["prompt_blocks"][2]] == wt["old_ref_after"]
-    assert bm.ref_cnt[wt["new_block"]] == 1
-    assert bm.ref_cnt[7] == 4 and bm.ref_cnt[3] == 4          # full blocks stay shared
-    for k in kids[1:]:
-        assert bm.table(k) == wt["prompt_blocks"]
-
-
 def test_cow_checks_the_blocks_own_count():
-    bm = BlockManager(8, 4)
-    bm.allocate("a", 3)                 # one block, 3/4 full, ref 1
-    slot, copies = bm.append_slot("a")  # unique owner: write in place
-    assert copies == [] and slot == bm.table("a")[0] * 4 + 3
-    bm.fork("a", ["b", "c"])            # now shared, ref 2
-    slot, copies = bm.append_slot("b")  # block full: a new block, no copy
-    assert copies == [] and len(bm.table("b")) == 2
-
-
-def test_exhaustion_raises_without_partial_state():
-    bm = BlockManager(4, 16)
-    bm.allocate("a", 40)                # 3 blocks
-    before = (bm.num_free, list(bm.ref_cnt))
-    with pytest.raises(ValueError):
-        bm.allocate("b", 40)
-    assert (bm.num_free, list(bm.ref_cnt)) == before and "b" not in bm.tables
-
-
-def test_no_leak_after_freeing_all_forks():
-    bm = BlockManager(64, 16)
-    initial = bm.num_free
-    bm.allocate("p", 40)
-    bm.fork("p", ["s0", "s1", "s2", "s3"])
-    for k in ("s0", "s1", "s2", "s3"):
-        for _ in range(30):
-            bm.append_slot(k)
-    for k in ("s0", "s1", "s2", "s3"):
-        bm.free_seq(k)
-    assert bm.num_free == initial and all(c == 0 for c in bm.ref_cnt)
-
-
-def test_free_returns_tail_first():
-    bm = BlockManager(8, 16, free_order=[5, 6, 7])
-    bm.allocate("a", 40)
-    bm.free_seq("a")
-    assert list(bm.free)[-3:] == [7, 6, 5]
+    """Copy-on-write looks at the count of the block being written ("GPU
+    memory & KV cache", incident fix): a request's own block (count 1) is
+    written in place, a shared one is copied first, and a write past the
+    shared blocks needs a new block but no copy.  The native host pool."""
+    pool = L.BlockPool(8, 4)
+    pool.allocate_request(1, list(range(3)))          # one block, 3 of 4 slots, count 1
+    (b,) = pool.request_blocks(1)
+    assert pool.prepare_write(1, 3) is None            # own block: write in place
+    pool.fork_request(1, 2)                            # now count 2
+    pool.append_slots(2, 5)                            # position 4: a new block, no copy
+    assert pool.request_blocks(2)[0] == b and pool.prepare_write(2, 4) is None
+    assert pool.prepare_write(2, 3) == (b, pool.request_blocks(2)[0])   # shared: copy first
+    assert pool.ref_count(b) == 1 and pool.request_blocks(1) == [b]
+    for rid in (1, 2):
+        pool.free_request(rid)
+    assert pool.num_free() == 8                        # no leak
 
 
 # ------------------------------------------------------------- generator
@@ -137,7 +94,7 @@ def test_tiny_workload_shape():
     assert (w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.num_blocks) == \
         (8, 2, 64, 16, 64)
     assert w.scale == np.float32(0.125)
-    used = sum(cdiv(n, 16) for n in w.seq_lens)
+    used = sum(W.cdiv(n, 16) for n in w.seq_lens)
     assert used == 13 and len(w.used_blocks) == 13
 
 
@@ -154,7 +111,7 @@ def _check_slots(w):
                 else w.block_tables_before_cow
             assert slot // w.block_size == bt[s, t // w.block_size]
             assert slot % w.block_size == t % w.block_size
-        assert np.all(w.block_tables[s, cdiv(n, w.block_size):] == w.pad_block)
+        assert np.all(w.block_tables[s, W.cdiv(n, w.block_size):] == w.pad_block)
 
 
 def test_prefix_share_structure():

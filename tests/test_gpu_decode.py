@@ -272,3 +272,41 @@ def test_fp8_widening_exact_for_every_byte_prefill(dtype, D):
     lens = torch.tensor([1], dtype=torch.int32, device="cuda")
     L.pa_prefill(pool, out, q, qs, bt, lens, 1, 0.088)
     _assert_widened_exactly(dtype, out.cpu().numpy())
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("part", [1, 16, 512])
+@pytest.mark.parametrize("loose", [1, 8])
+def test_dirty_workspace_reuse(name, part, loose):
+    """One workspace, NaN-filled once and then reused by every call (so each
+    call also finds the records earlier calls left), with the host bound
+    max_seq_len exact or 8x the longest context (more flat ranges than
+    16-token units: empty ranges).  Every word a call reads must be one it
+    wrote: outputs pass the oracle gate, and with the exact bound they equal
+    the fresh-workspace outputs bit for bit."""
+    w, hp = _case(name)
+    say(f"dirty workspace {name} partition={part} loose={loose}")
+    dc = DeviceCase(w, poison=True)
+    msl = max(1, w.max_seq_len) * loose
+    y = dc.decode(part, max_seq_len=msl, dirty_workspace=True).cpu().numpy()
+    check_close(w, y, _ref(w, hp), f"dirty/{name}/p{part}/x{loose}")
+    if loose == 1:
+        fresh = dc.decode(part, out=torch.empty_like(dc.out)).cpu().numpy()
+        assert np.array_equal(y.view(np.uint16), fresh.view(np.uint16))
+
+
+@pytest.mark.parametrize("name", ["d128_bs16_g4", "fp8_d128_bs32", "d64_bs128_g2",
+                                  "e5m2h_d64_bs32_g2", "d256_bs16_g4"])
+@pytest.mark.parametrize("win", [16, 100, 1000])
+@pytest.mark.parametrize("part", [0, 1, 16, 512])
+def test_dirty_workspace_reuse_with_window(name, win, part):
+    """Sliding windows read only the last positions of each context, so the
+    flat schedule has far fewer units than the host bound sizes ranges for;
+    the reused NaN-filled workspace must not leak into any output."""
+    w0, _ = _case(name)
+    w = _with_window(w0, win, poison_outside=True)
+    say(f"dirty workspace window {win} {name} partition={part}")
+    y = DeviceCase(w, poison=True).decode(part, max_seq_len=4 * max(1, w.max_seq_len),
+                                          dirty_workspace=True).cpu().numpy()
+    r = O.decode(oracle_pool(w, poison=True), w.q, w.block_tables, w.seq_lens, w.scale)
+    check_close(w, y, r, f"dirty window{win}/{name}/p{part}")

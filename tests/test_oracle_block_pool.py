@@ -19,8 +19,8 @@ import struct
 import numpy as np
 import pytest
 
-from oracle.block_pool import (NONE_HASH, BlockPoolModel, PoolError, chain_hashes,
-                               hash_block_tokens)
+from oracle.block_pool import (NONE_HASH, BlockPoolModel, PoolError, prompt_digests,
+                               block_digest)
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden", "block_pool_walkthrough.json")
 
@@ -44,13 +44,13 @@ def run_walkthrough(pool_factory):
             held[st["who"]] = pool.get_new_blocks(st["n"])
             seen.append({"got": held[st["who"]]})
         elif op == "finish":
-            hs = chain_hashes(a_tokens, bs)
+            hs = prompt_digests(a_tokens, bs)
             for b, h in zip(held["A"], hs):
                 pool.cache_full_block(b, h)
             pool.free_blocks(list(reversed(held.pop("A"))))
             seen.append({})
         elif op == "prefix_lookup":
-            hits = pool.lookup(chain_hashes(a_tokens, bs))
+            hits = pool.lookup(prompt_digests(a_tokens, bs))
             pool.touch(hits)
             seen.append({"hits": hits})
         else:
@@ -62,10 +62,10 @@ def run_walkthrough(pool_factory):
 
 class _Model(BlockPoolModel):
     def free_queue_list(self):
-        return list(self.free)
+        return list(self.queue)
 
     def hashed_list(self):
-        return sorted(b for b, h in enumerate(self.hash) if h is not None)
+        return sorted(b for b, h in enumerate(self.kept) if h is not None)
 
 
 def test_walkthrough_t0_to_t4():
@@ -77,7 +77,7 @@ def test_walkthrough_t0_to_t4():
             assert obs["got"] == st["got"], st["t"]
         if "hits" in st:
             assert obs["hits"] == st["hits"], st["t"]
-    assert pool.ref[0] == 1
+    assert pool.count[0] == 1
     with pytest.raises(PoolError):
         pool.get_new_blocks(1)               # B's second block: the queue is empty
 
@@ -86,10 +86,10 @@ def test_hash_byte_layout():
     toks = [1, -2, 70000, 5]
     expect = hashlib.sha256(bytes(32) + b"\x01\x00\x00\x00" + b"\xfe\xff\xff\xff" +
                             b"\x70\x11\x01\x00" + b"\x05\x00\x00\x00" + b"lora7").digest()
-    assert hash_block_tokens(None, toks, b"lora7") == expect
+    assert block_digest(None, toks, b"lora7") == expect
     assert NONE_HASH == bytes(32)
-    h0 = hash_block_tokens(None, toks)
-    assert hash_block_tokens(h0, toks) == hashlib.sha256(h0 + b"".join(
+    h0 = block_digest(None, toks)
+    assert block_digest(h0, toks) == hashlib.sha256(h0 + b"".join(
         struct.pack("<i", t) for t in toks)).digest()
 
 
@@ -98,12 +98,12 @@ def test_chain_divergence_and_first_token():
     sys_prompt = _tokens(2 * bs + 5, 2)
     r1 = sys_prompt + _tokens(20, 3)
     r2 = sys_prompt + _tokens(20, 4)
-    h1, h2 = chain_hashes(r1, bs), chain_hashes(r2, bs)
+    h1, h2 = prompt_digests(r1, bs), prompt_digests(r2, bs)
     assert h1[:2] == h2[:2] and h1[2] != h2[2]
     r3 = [r1[0] + 1] + r1[1:]
-    h3 = chain_hashes(r3, bs)
+    h3 = prompt_digests(r3, bs)
     assert all(a != b for a, b in zip(h1, h3))          # nothing shared after a changed head
-    assert chain_hashes(r1, bs, b"tenant-1")[0] != h1[0]  # extra keys separate tenants
+    assert prompt_digests(r1, bs, b"tenant-1")[0] != h1[0]  # extra keys separate tenants
 
 
 def test_prefix_hit_2000_token_prompt():
@@ -113,12 +113,12 @@ def test_prefix_hit_2000_token_prompt():
     a = sys_prompt + _tokens(2, 6)                       # "Hi"
     assert pool.allocate_request(1, a) == 0
     pool.cache_request(1, a)
-    assert len([h for h in pool.hash if h is not None]) == 125      # 125 full blocks
+    assert len([h for h in pool.kept if h is not None]) == 125      # 125 full blocks
     b = sys_prompt + _tokens(50, 7)
     assert pool.allocate_request(2, b) == 2000           # 125 blocks hit
     shared = pool.requests[1][:125]
     assert pool.requests[2][:125] == shared
-    assert all(pool.ref[x] == 2 for x in shared)
+    assert all(pool.count[x] == 2 for x in shared)
     assert len(pool.requests[2]) == -(-2050 // bs)       # 129 blocks, 4 of them new
     # self-test: 2,005 tokens -> 125 blocks hit, the last 5 tokens recomputed
     c = sys_prompt + _tokens(5, 8)
@@ -137,15 +137,15 @@ def test_free_keeps_hashes_and_prefix_blocks_leave_last():
     blocks = list(pool.requests[1])
     pool.free_request(1)
     # freed last to first: the prefix block ends nearest the tail (evicted last)
-    assert pool.free[-3:] == list(reversed(blocks))
-    assert all(pool.hash[b] is not None for b in blocks)
+    assert pool.queue[-3:] == list(reversed(blocks))
+    assert all(pool.kept[b] is not None for b in blocks)
     # shared block is released only when its last holder frees it
     pool.allocate_request(2, t)
     pool.allocate_request(3, t[:2 * bs] + [1, 2, 3, 4])
     first = pool.requests[2][0]
-    assert pool.ref[first] == 2
+    assert pool.count[first] == 2
     pool.free_request(2)
-    assert pool.ref[first] == 1 and first not in pool.free
+    assert pool.count[first] == 1 and first not in pool.queue
 
 
 def test_failed_allocation_changes_nothing():

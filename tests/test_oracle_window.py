@@ -66,3 +66,71 @@ def test_window_covering_everything_is_full_attention():
     ww = dataclasses.replace(w, window=200)
     win = O.decode(O.pool_for_workload(ww), w.q, w.block_tables, w.seq_lens, w.scale)
     assert np.array_equal(full, win)
+
+
+def _release_case(n, bs, win, seed, Hkv=2, D=64, g=2):
+    """A request holding n tokens (the model's blocks), grown by the slot of
+    its next token (position n), then the model's sliding-window release.
+    Returns the decode of that next query (length n + 1, window win) over the
+    unreleased row, over the released row with every -1 entry pointed at a
+    never-written NaN block, and over that row with one more entry (the first
+    kept one) pointed there too; plus the count the model reported."""
+    from oracle.block_pool import BlockPoolModel
+    nblk = -(-(n + 1) // bs)
+    m = BlockPoolModel(nblk + 2, bs)
+    m.allocate_request(0, list(range(n)))
+    m.append_slot(0, n + 1)
+    full = list(m.requests[0])
+    count = m.remove_skipped_blocks(0, n, win)
+    released = list(m.requests[0])
+    nan_block = nblk + 1                          # allocated to nobody, never written
+    rng = np.random.default_rng(seed)
+    pool = O.HostPool(nblk + 2, bs, Hkv, D, "f16", fill_bits=0x7E00, sliding_window=win)
+    k = rng.standard_normal((n + 1, Hkv, D), dtype=np.float32).astype(np.float16)
+    v = rng.standard_normal((n + 1, Hkv, D), dtype=np.float32).astype(np.float16)
+    t = np.arange(n + 1)
+    O.scatter(pool, k, v, np.asarray(full, np.int64)[t // bs] * bs + t % bs)
+    q = rng.standard_normal((1, Hkv * g, D), dtype=np.float32).astype(np.float16)
+    lens = np.array([n + 1], np.int32)
+
+    def dec(row):
+        bt = np.array([[nan_block if b < 0 else b for b in row]], np.int32)
+        return O.decode(pool, q, bt, lens, 1.0 / np.sqrt(D))
+
+    kept = sum(1 for b in released if b < 0)
+    one_more = released[:kept] + [-1] + released[kept + 1:] if kept < len(released) else None
+    return dec(full), dec(released), (dec(one_more) if one_more else None), count, released
+
+
+@pytest.mark.parametrize("bs,win", [(16, 1024), (16, 100), (8, 17), (32, 1), (16, 16),
+                                    (64, 200), (8, 8)])
+def test_window_release_drops_exactly_the_blocks_the_next_query_no_longer_reads(bs, win):
+    """Ties the host release rule of the block-pool model to the attention
+    window pinned above: for a sweep of token counts n, the next query's
+    decode over the row with the released entries pointing at NaN is bitwise
+    the decode over the unreleased row (nothing released is read), and
+    pointing the first kept entry at NaN too makes it non-finite (the first
+    kept block holds a position the query reads, so no further block could
+    have been released)."""
+    rng = np.random.default_rng(bs * 1000 + win)
+    ns = {0, 1, win - 2, win - 1, win, win + 1, win + bs - 1, win + bs, win + bs + 1,
+          win + 3 * bs - 1, 2 * win + 5 * bs + 3}
+    ns |= {int(x) for x in rng.integers(0, 3 * win + 8 * bs, size=6)}
+    for n in sorted(x for x in ns if x >= 0):
+        a, b, c, count, row = _release_case(n, bs, win, seed=n)
+        assert count == sum(1 for x in row if x < 0), n
+        assert np.array_equal(a, b), f"n={n}: a released block was still read"
+        assert np.all(np.isfinite(a)), n
+        if c is not None:
+            assert not np.all(np.isfinite(c)), f"n={n}: block {count} was releasable"
+
+
+def test_window_release_worked_example():
+    """bs 16, window 1,024, a request holding 4,096 tokens: its next query
+    (position 4,096) reads positions 3,073 .. 4,096, so blocks 0 .. 191
+    (positions 0 .. 3,071) go and block 192 (3,072 .. 3,087) stays: 192
+    blocks released, by hand."""
+    a, b, _, count, row = _release_case(4096, 16, 1024, seed=5)
+    assert count == 192
+    assert row[:192] == [-1] * 192 and min(row[192:]) >= 0 and len(row) == 257
+    assert np.array_equal(a, b)
