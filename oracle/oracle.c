@@ -199,7 +199,8 @@ void orc_scatter(const orc_pool* p, const uint16_t* k_new, const uint16_t* v_new
 #pragma omp parallel for schedule(static) num_threads(nthreads_or_default(nthreads))
   for (int64_t i = 0; i < T; ++i) {
     int64_t slot = slots[i];
-    if (slot < 0) continue;
+    /* padding (negative) and slots outside the pool write nothing */
+    if (slot < 0 || slot >= p->num_blocks * p->block_size) continue;
     int64_t blk = slot / p->block_size;
     int32_t off = (int32_t)(slot % p->block_size);
     for (int32_t kh = 0; kh < Hkv; ++kh) {
@@ -231,6 +232,7 @@ void orc_copy_blocks(const orc_pool* p, const int64_t* pairs, int64_t n) {
   const int64_t bytes = (int64_t)p->block_size * p->num_kv_heads * p->head_dim * p->elem_bytes;
   for (int64_t i = 0; i < n; ++i) {
     int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || src >= p->num_blocks || dst < 0 || dst >= p->num_blocks) continue;
     memmove((uint8_t*)p->k + dst * stride, (const uint8_t*)p->k + src * stride, (size_t)bytes);
     memmove((uint8_t*)p->v + dst * stride, (const uint8_t*)p->v + src * stride, (size_t)bytes);
   }

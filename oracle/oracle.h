@@ -88,13 +88,14 @@ void orc_e4m3fn_encode_n(const float* x, int64_t n, uint8_t* out);
 void orc_e5m2_values(const uint8_t* bytes, int64_t n, double* out);
 void orc_e5m2_encode_n(const float* x, int64_t n, uint8_t* out);
 
-/* Write T tokens: k_new/v_new are [T, Hkv, D] binary16 bit patterns; slot < 0
- * skips the token.  fp8 pools receive enc(float(x) / float(scale)) with the
+/* Write T tokens: k_new/v_new are [T, Hkv, D] binary16 bit patterns; a slot
+ * below 0 (padding) or at or beyond num_blocks * block_size skips the token.  fp8 pools receive enc(float(x) / float(scale)) with the
  * pool's fp8 encoder. */
 void orc_scatter(const orc_pool* p, const uint16_t* k_new, const uint16_t* v_new,
                  const int64_t* slots, int64_t T, int nthreads);
 
-/* Copy whole blocks: pairs is [n, 2] of (src, dst), applied in order. */
+/* Copy whole blocks: pairs is [n, 2] of (src, dst), applied in order; a pair
+ * naming a block outside [0, num_blocks) is skipped. */
 void orc_copy_blocks(const orc_pool* p, const int64_t* pairs, int64_t n);
 
 /* Gather KV head kh of a sequence into contiguous fp64 rows Kc/Vc [len, D]. */

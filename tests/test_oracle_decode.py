@@ -198,6 +198,19 @@ def test_scatter_and_copy_are_bit_copies():
     assert np.array_equal(pool.k[dst], pool.k[src]) and np.array_equal(pool.v[dst], pool.v[src])
 
 
+def test_out_of_pool_slots_and_pairs_write_nothing():
+    """Slots below 0 (padding) or past num_blocks * block_size, and copy
+    pairs naming a block outside the pool, leave every pool byte alone (the
+    boundary's contract for reshape_and_cache and copy_blocks)."""
+    pool = O.HostPool(4, 16, 2, 64, "f16", fill_bits=0x1234)
+    k = np.full((4, 2, 64), 2.0, np.float16)
+    O.scatter(pool, k, k, np.array([-1, 64, 65, 1 << 40], np.int64))
+    O.copy_blocks(pool, np.array([[0, 4], [4, 0], [-1, 2], [2, -3]], np.int64))
+    assert np.all(pool.k == 0x1234) and np.all(pool.v == 0x1234)
+    O.scatter(pool, k[:1], k[:1], np.array([63], np.int64))      # the last slot is in
+    assert np.all(pool.k[3, 15] == np.float16(2.0).view(np.uint16))
+
+
 @pytest.mark.parametrize("dt,tdt,top", [("fp8_e4m3fn", torch.float8_e4m3fn, 448.0),
                                          ("fp8_e5m2", torch.float8_e5m2, 57344.0)])
 def test_fp8_scatter_quantises_x_over_scale(dt, tdt, top):
