@@ -184,6 +184,28 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
               const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_size,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* pa_decode for callers that cannot allocate device memory (code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results as pa_decode, but the flat and
+ * split schedules use the library's own scratch instead of a workspace
+ * argument.  The scratch is one static device array of
+ * PA_DECODE_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load until
+ * the process ends; its address is looked up on the first call on each
+ * device.  Nothing is allocated and nothing is synchronised.
+ * Returns PA_ERR_WORKSPACE, launching nothing, when the planned schedule
+ * needs more workspace than that (pa_decode_workspace_size tells beforehand;
+ * the default flat schedule needs at most about 35 MB).  Every call on a
+ * GPU uses that GPU's one array: calls that may overlap on one GPU (on
+ * different streams, or from different threads) race on it and must be
+ * serialised by the caller, e.g. by issuing them on one stream.  The array
+ * keeps whatever the last call left; the kernels read only what the same
+ * call wrote, so nothing needs clearing. */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int pa_decode_noalloc(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs,
+                      int32_t num_q_heads, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                      float scale, int32_t partition_size, hipStream_t stream);
+
 /* Prefill and chunked-prefill attention over the paged cache.  A prompt's new
  * tokens are written first (pa_reshape_and_cache, on the same stream) and then
  * each attends to itself and every earlier position of its sequence ("vLLM

@@ -30,7 +30,8 @@ PA_POOL_SHARED_BLOCKS = 1
 _DTYPES = {"f16": PA_KV_F16, "fp8_e4m3fn": PA_KV_FP8_E4M3FN, "fp8_e5m2": PA_KV_FP8_E5M2}
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
-           "pa_decode_workspace_size", "pa_decode", "pa_prefill", "pa_last_error",
+           "pa_decode_workspace_size", "pa_decode", "pa_decode_noalloc", "pa_prefill",
+           "pa_last_error",
            # host block pool (include/pa_blocks.h)
            "pa_bp_create", "pa_bp_destroy", "pa_bp_last_error", "pa_bp_num_free",
            "pa_bp_ref_count", "pa_bp_block_hash", "pa_bp_free_queue", "pa_bp_get_new_blocks",
@@ -86,6 +87,8 @@ def load() -> C.CDLL:
         L.pa_decode.restype = C.c_int
         L.pa_decode.argtypes = [PP, P, P, I32, I32, P, I32, P, I32, C.c_float, I32, P, C.c_size_t,
                                 P]
+        L.pa_decode_noalloc.restype = C.c_int
+        L.pa_decode_noalloc.argtypes = [PP, P, P, I32, I32, P, I32, P, I32, C.c_float, I32, P]
         L.pa_prefill.restype = C.c_int
         L.pa_prefill.argtypes = [PP, P, P, I32, P, I32, I32, P, I32, P, I32, C.c_float, P]
         L.pa_last_error.restype = C.c_char_p
@@ -266,6 +269,30 @@ def pa_decode(pool: KVPool, out: torch.Tensor, q: torch.Tensor, block_tables: to
         _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
         _dev(seq_lens, torch.int32, "seq_lens"), int(max_seq_len), C.c_float(scale),
         int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+PA_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pa_decode_noalloc(pool: KVPool, out: torch.Tensor, q: torch.Tensor,
+                      block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                      scale: float, partition_size: int = 0, stream=None) -> None:
+    """pa_decode without a workspace argument: the library's per-device
+    scratch (PA_DECODE_NOALLOC_SCRATCH_BYTES) serves the flat and split
+    schedules.  For callers that cannot allocate; overlapping calls on one
+    GPU race on the scratch."""
+    S, Hq, D = q.shape
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape [num_seqs, num_q_heads, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], seq_lens [num_seqs]")
+    if CHECK_INPUTS:
+        pa_check_decode_inputs(pool, block_tables, seq_lens, max_seq_len, stream)
+    _check(load().pa_decode_noalloc(
+        C.byref(pool.desc), _dev(out, torch.float16, "out"), _dev(q, torch.float16, "q"), S, Hq,
+        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+        _dev(seq_lens, torch.int32, "seq_lens"), int(max_seq_len), C.c_float(scale),
+        int(partition_size), _stream(stream)))
 
 
 def pa_prefill(pool: KVPool, out: torch.Tensor, q: torch.Tensor, q_start: torch.Tensor,
