@@ -97,25 +97,103 @@ def alg_bytes(w) -> dict:
             "decode_logical": kv_logical + qo + tables, "write": write}
 
 
-def cpu_baseline(w, budget_s: float) -> dict:
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads() -> int:
+    """Every core this process may run on, but no more than OMP_NUM_THREADS
+    when that is set (the share of the host's cores a one-GPU job gets)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(env)) if env.isdigit() and int(env) > 0 else n
+
+
+def _time_oracle_decode(w, pool, nthreads: int, budget_s: float):
     import oracle as O
-    nthreads = min(16, len(os.sched_getaffinity(0)))
-    pool = O.pool_for_workload(w, nthreads=nthreads)
     reps, t0 = 0, time.perf_counter()
     while True:
         O.decode(pool, w.q, w.block_tables, w.seq_lens, w.scale, nthreads=nthreads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
-            break
-    per = el / reps
+            return el / reps, reps, el
+
+
+def cpu_baseline(w, budget_s: float, single_thread_configs=()) -> dict:
+    """The fp64 oracle, as it stands, on the host: the full decode of w on
+    every allowed core, then (single_thread_configs) one thread on each listed
+    workload for about a second each."""
+    import oracle as O
+    from paged_kv_cache_72_amd import workloads as W
+    nthreads = oracle_threads()
+    pool = O.pool_for_workload(w, nthreads=nthreads)
+    per, reps, el = _time_oracle_decode(w, pool, nthreads, budget_s)
+    del pool
     b = alg_bytes(w)
-    return {"value": round(b["decode"] / per / 1e9, 4), "unit": "GB/s", "cores": nthreads,
-            "kind": "oracle", "ms_per_step": round(per * 1e3, 2),
-            "kv_tokens_per_s": round(float(w.seq_lens.sum()) / per, 1),
-            "sample": f"full decode of the {w.name} step (all {w.num_seqs} sequences, "
-                      f"{w.num_q_heads} query heads), repeated {reps}x over {el:.1f} s; "
-                      "fp64 C oracle, OpenMP"}
+    res = {"value": round(b["decode"] / per / 1e9, 4), "unit": "GB/s", "cores": nthreads,
+           "kind": "oracle", "ms_per_step": round(per * 1e3, 2),
+           "kv_tokens_per_s": round(float(w.seq_lens.sum()) / per, 1),
+           "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
+           "sample": f"full decode of the {w.name} step (all {w.num_seqs} sequences, "
+                     f"{w.num_q_heads} query heads), repeated {reps}x over {el:.1f} s; "
+                     "fp64 C oracle, OpenMP"}
+    single = {}
+    for name in single_thread_configs:
+        ws = W.CONFIGS[name]()
+        p1 = O.pool_for_workload(ws, nthreads=nthreads)
+        per1, reps1, _ = _time_oracle_decode(ws, p1, 1, 1.0)
+        del p1
+        single[name] = {"ms_per_step": round(per1 * 1e3, 2),
+                        "GB_per_s": round(alg_bytes(ws)["decode"] / per1 / 1e9, 4), "reps": reps1}
+    if single:
+        res["single_thread"] = single
+    return res
+
+
+def probe_ceiling(nbytes: int) -> dict:
+    """The plain-read ceiling at the decode call's size: the wave-contiguous
+    read probe (libpa_probe.so) over nbytes, rotating three buffers so no read
+    finds its data in the Infinity Cache; median of 30 event-timed launches."""
+    import torch
+    lib_path = os.path.join(ROOT, "paged_kv_cache_72_amd", "libpa_probe.so")
+    if not os.path.exists(lib_path):
+        return {}
+    P = C.CDLL(lib_path)
+    P.pa_probe_wave_chunk.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int32, C.c_void_p,
+                                      C.c_void_p]
+    waves, unroll = 2048, 16
+    steps = max(unroll, (nbytes // (waves * 1024)) // unroll * unroll)
+    n = waves * steps * 1024
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    sink = torch.empty(waves * 64, dtype=torch.int32, device="cuda")
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i in range(5):
+        P.pa_probe_wave_chunk(bufs[i % 3].data_ptr(), waves, steps, unroll, sink.data_ptr(), st)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(30)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        P.pa_probe_wave_chunk(bufs[i % 3].data_ptr(), waves, steps, unroll, sink.data_ptr(), st)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    del bufs
+    return {"bytes": n, "median_ms": round(ms, 5), "GB_per_s": round(n / (ms * 1e-3) / 1e9, 1),
+            "probe": f"wave-contiguous 16-byte loads, {waves} waves, {unroll} KiB in flight per "
+                     "wave"}
+
+
+def percentiles_ms(ms) -> dict:
+    a = np.asarray(ms, np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 5), "p50": round(float(np.median(a)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "mean": round(float(a.mean()), 5)}
 
 
 def traffic_entry(config: str):
@@ -129,7 +207,9 @@ def traffic_entry(config: str):
     return e.get("bytes_per_launch")
 
 
-DECODE_KERNELS = ("decode_flat_kernel", "flat_merge_rows_kernel", "flat_merge_kernel", "decode_kernel",
+DECODE_KERNELS = ("decode_flat_group_kernel", "flat_group_merge_kernel", "decode_flat_kernel",
+                  "flat_merge_rows_kernel", "flat_merge_kernel", "decode_group_kernel",
+                  "decode_kernel",
                   "lse_reduce_kernel")
 PREFILL_KERNELS = ("prefill_f16_kernel", "prefill_kernel")
 
@@ -145,7 +225,8 @@ def ingest_counters(fetch_csv: str, write_csv: str, calib_gib: float, config: st
     from paged_kv_cache_72_amd import workloads as W
     kernels = PREFILL_KERNELS if config in W.PREFILL_CONFIGS else DECODE_KERNELS
     # the kernels that run once per call (the rest, merges and reduces, run after them)
-    primary = ("prefill_f16_kernel", "prefill_kernel", "decode_flat_kernel", "decode_kernel")
+    primary = ("prefill_f16_kernel", "prefill_kernel", "decode_flat_group_kernel",
+               "decode_flat_kernel", "decode_group_kernel", "decode_kernel")
 
     def load(path):
         rows = list(csv.DictReader(open(path)))
@@ -211,7 +292,7 @@ def prefill_bytes(w) -> int:
 def cpu_baseline_prefill(w, budget_s: float) -> dict:
     """The oracle's prefill on seeded query rows for about budget_s seconds."""
     import oracle as O
-    nthreads = min(16, len(os.sched_getaffinity(0)))
+    nthreads = oracle_threads()
     pool = O.pool_for_workload(w, nthreads=nthreads)
     rng = np.random.default_rng(0)
     qs = w.q_start
@@ -232,6 +313,7 @@ def cpu_baseline_prefill(w, budget_s: float) -> dict:
     rate = done_flops / el
     return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads,
             "kind": "oracle", "ms_per_step": round(prefill_flops(w) / rate * 1e3, 1),
+            "cpu_model": cpu_model(),
             "sample": f"{done_rows} seeded (sequence, KV head, new token) rows of the "
                       f"{w.name} step, each for its {w.gqa} query heads, over {el:.1f} s; "
                       "fp64 C oracle, OpenMP; ms_per_step extrapolates to the whole step"}
@@ -449,8 +531,18 @@ def main() -> int:
     ap.add_argument("--config", default="llama3_8b_b64")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--decode", choices=("auto", "plain", "grouped"), default="auto",
+                    help="auto: pa_decode_grouped when blocks are shared between sequences "
+                         "(planned on the host once), else pa_decode")
+    ap.add_argument("--grouped-schedule", type=int, default=0,
+                    help="pa_decode_grouped schedule: 0 library choice, 1 flat, 2 per group")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the plain-read ceiling probe (pct_of_probe)")
+    ap.add_argument("--cpu-single-thread", type=int, default=1,
+                    help="1: also time the oracle on one thread on the tiny, Llama, Qwen and "
+                         "prefix-sharing workloads (about a second each)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -516,14 +608,33 @@ def main() -> int:
                               v_head_scales=base.v_head_scales, sliding_window=w.window))
     part = L.pa_decode_plan(base, w.num_seqs, w.num_q_heads, w.max_seq_len, args.partition)
     ws = L.alloc_workspace(base, w.num_seqs, w.num_q_heads, w.max_seq_len, args.partition)
+    grouped = args.decode == "grouped" or (args.decode == "auto" and shared and not w.window)
+    groups, plan_us = None, None
+    if grouped:   # the host planner, as a scheduler would run it each step (timed on its own)
+        t_p = time.perf_counter()
+        for _ in range(20):
+            groups = L.pa_decode_group_plan(w.block_tables, w.seq_lens, w.block_size,
+                                            w.num_q_heads, w.num_kv_heads)
+        plan_us = (time.perf_counter() - t_p) / 20 * 1e6
+        gsched = L.pa_decode_grouped_plan(base, w.num_seqs, w.num_q_heads, w.max_seq_len,
+                                          groups.num_groups, args.grouped_schedule)
+        gws = L.alloc_grouped_workspace(base, w.num_seqs, w.num_q_heads, w.max_seq_len,
+                                        groups.num_groups, gsched)
     torch.cuda.synchronize()
+
+    def decode(p):
+        if grouped:
+            L.pa_decode_grouped(p, out, q, bt, lens, w.max_seq_len, w.scale, groups,
+                                schedule=gsched, workspace=gws, stream=stream)
+        else:
+            L.pa_decode(p, out, q, bt, lens, w.max_seq_len, w.scale, args.partition, ws, stream)
 
     def step(i, ev=None):
         p = pools[i % len(pools)]
         L.pa_reshape_and_cache(p, k_new, v_new, slot_new, stream)
         if ev is not None:
             ev[0].record(stream)
-        L.pa_decode(p, out, q, bt, lens, w.max_seq_len, w.scale, args.partition, ws, stream)
+        decode(p)
         if ev is not None:
             ev[1].record(stream)
 
@@ -554,6 +665,14 @@ def main() -> int:
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(c) for a, c in ev]))
 
+    # warm: back-to-back calls on one pool (K/V partly served from the
+    # Infinity Cache), labelled as such
+    warm_ms = event_avg_ms(lambda i: decode(pools[0]))
+    plain_ms = None
+    if grouped:   # the same step through pa_decode, for comparison
+        plain_ms = event_avg_ms(lambda i: L.pa_decode(pools[i % len(pools)], out, q, bt, lens,
+                                                      w.max_seq_len, w.scale, args.partition,
+                                                      ws, stream), reps=100)
     rc_ms = event_avg_ms(lambda i: L.pa_reshape_and_cache(pools[i % len(pools)], k_new, v_new,
                                                            slot_new, stream))
     pairs = w.cow_pairs
@@ -581,6 +700,24 @@ def main() -> int:
     step_bytes = b["decode"] + b["write"]
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = b["decode"] / (dec_avg * 1e-3) / 1e9
+    del pools
+    probe = probe_ceiling(b["decode"]) if not args.no_probe else {}
+    pct = percentiles_ms(dec_ms)
+    call = {"events_ms": pct,
+            "GB_per_s_at_p50": round(b["decode"] / (pct["p50"] * 1e-3) / 1e9, 1),
+            "pct_of_peak_at_p50": round(100 * b["decode"] / (pct["p50"] * 1e-3) / 1e9
+                                        / HBM_PEAK_GBS, 2),
+            "warm_back_to_back_ms": round(warm_ms, 5),
+            "warm_GB_per_s": round(b["decode"] / (warm_ms * 1e-3) / 1e9, 1)}
+    if grouped:
+        call["entry_point"] = "pa_decode_grouped"
+        call["grouped_schedule"] = {1: "flat ranges over the groups", 2: "workgroup per group"}[gsched]
+        call["groups"] = groups.num_groups
+        call["host_group_plan_us"] = round(plan_us, 1)
+        call["pa_decode_ms_same_step"] = round(plain_ms, 5)
+    if probe:
+        call["probe_ceiling"] = probe
+        call["pct_of_probe"] = round(100 * achieved / probe["GB_per_s"], 2)
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
@@ -593,7 +730,8 @@ def main() -> int:
                                f"{w.block_size}, {w.kv_dtype} KV, {w.num_blocks}-block pool; "
                                f"step = reshape_and_cache of {w.new_idx.size} tokens + decode",
                    "global_batch": w.num_seqs, "seq_len": w.max_seq_len, "parallelism": "none",
-                   "layers_rotated": args.layers, "partition_tokens": part,
+                   "layers_rotated": args.layers,
+                   "partition_tokens": "grouped" if grouped else part,
                    "shared_blocks": shared},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kv_tokens_per_s": round(float((np.minimum(w.seq_lens, w.window) if w.window
@@ -607,7 +745,9 @@ def main() -> int:
                         "alg_bytes": cb_bytes,
                         "GB_per_s": round(cb_bytes / (cb_ms * 1e-3) / 1e9, 1)},
         "logical_decode_bytes": b["decode_logical"],
-        "roofline": {"bound": "hbm", "kernel": "pa_decode", "achieved": round(achieved, 1),
+        "pa_decode_call": call,
+        "roofline": {"bound": "hbm", "kernel": "pa_decode_grouped" if grouped else "pa_decode",
+                     "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_entry(w.name), "avg_launch_ms": round(dec_avg, 5),
@@ -615,7 +755,9 @@ def main() -> int:
                      "kernel_source_hash": kernel_source_hash()},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        singles = ("tiny", "llama3_8b_b64", "qwen25_7b_8k", "prefix_share_bs16") \
+            if args.cpu_single_thread else ()
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, singles)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -6,7 +6,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <string>
+#include <unordered_map>
+#include <vector>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -95,12 +98,12 @@ int check_pool(const pa_kv_pool* p, PoolGeom* g) {
   return PA_OK;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
-                         int32_t head_dim, int32_t block_size, int kv, bool stream_kv, int mode,
-                         hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, const GroupArgs* gr,
+                         int32_t num_seqs, int32_t head_dim, int32_t block_size, int kv,
+                         bool stream_kv, int mode, hipStream_t stream) {
 #define PA_DK(D, KV)                                                                        \
   if (head_dim == D && kv == KV)                                                            \
-    return launch_decode_dk<D, KV>(a, f, num_seqs, block_size, stream_kv, mode, stream);
+    return launch_decode_dk<D, KV>(a, f, gr, num_seqs, block_size, stream_kv, mode, stream);
   PA_DK(128, 0) PA_DK(128, 1) PA_DK(128, 2)
   PA_DK(64, 0) PA_DK(64, 1) PA_DK(64, 2)
   PA_DK(256, 0) PA_DK(256, 1) PA_DK(256, 2)
@@ -223,6 +226,88 @@ size_t workspace_bytes_for(const Plan& pl, int64_t S, int64_t Hq, int64_t Hkv, i
   return 0;
 }
 
+// Grouped schedules: 1 flat ranges over the groups' units (per-group and
+// per-member tables in LDS, a workspace for the cut groups' records), 2 one
+// workgroup per (group, KV head) (no workspace, any batch size).
+constexpr int32_t kGroupFlat = 1, kGroupPerGroup = 2;
+constexpr int64_t kGroupFlatMaxLdsInts = 16384;   // 64 KiB of group and member tables
+
+struct GroupPlan {
+  int32_t mode;
+  int64_t ranges;
+  size_t workspace;
+};
+
+int group_plan(const pa_kv_pool* pool, int32_t S, int32_t Hq, int32_t max_seq_len, int32_t G,
+               int32_t schedule, pa::PoolGeom* g, GroupPlan* gp) {
+  Plan pl;
+  int st = plan(pool, S, Hq, max_seq_len, -1, g, &pl);
+  if (st) return st;
+  if (g->window > 0)
+    return fail(PA_ERR_UNSUPPORTED, "the grouped schedules do not take sliding-window pools");
+  if (G < 0 || G > S) return fail(PA_ERR_INVALID_ARG, "num_groups %d out of range [0, %d]", G, S);
+  if (schedule < 0 || schedule > kGroupPerGroup)
+    return fail(PA_ERR_INVALID_ARG, "grouped schedule %d invalid (0, 1 or 2)", schedule);
+  const int64_t lds_ints = 3 * (int64_t)G + 2 + 3 * (int64_t)S;
+  const bool flat_fits = lds_ints <= kGroupFlatMaxLdsInts;
+  if (schedule == kGroupFlat && !flat_fits)
+    return fail(PA_ERR_UNSUPPORTED, "the flat grouped schedule takes at most %lld groups + "
+                "sequences", (long long)(kGroupFlatMaxLdsInts / 3));
+  if ((int64_t)G * g->num_kv_heads > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "too many groups");
+  gp->mode = schedule ? schedule : (flat_fits ? kGroupFlat : kGroupPerGroup);
+  gp->ranges = 0;
+  gp->workspace = 0;
+  if (gp->mode == kGroupFlat) {
+    const int64_t per_head_ub = (int64_t)S * cdiv64(max_seq_len, 16);
+    int64_t ranges = flat_waves(*g) / g->num_kv_heads;
+    if (ranges > per_head_ub / kFlatMinTiles) ranges = per_head_ub / kFlatMinTiles;
+    if (ranges < 1) ranges = 1;
+    gp->ranges = ranges;
+    gp->workspace = align256((size_t)(G + 1) * 4) +
+                    (size_t)(ranges * g->num_kv_heads * 2 * 16 * (g->head_dim + 2) * 4);
+  }
+  return PA_OK;
+}
+
+// Host checks shared by every decode entry point, then the kernel arguments.
+int decode_args(const pa::PoolGeom& g, void* out, const void* q, int32_t num_seqs,
+                int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* seq_lens, int32_t max_seq_len, float scale, pa::DecodeArgs* ap) {
+  if (!out || !q || !block_tables || !seq_lens)
+    return fail(PA_ERR_INVALID_ARG, "out, q, block_tables and seq_lens must be non-NULL");
+  if (!aligned16(out) || !aligned16(q))
+    return fail(PA_ERR_ALIGNMENT, "q and out must be 16-byte aligned");
+  if (max_blocks_per_seq < 1)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  pa::DecodeArgs& a = *ap;
+  a = pa::DecodeArgs{};
+  a.k = g.k;
+  a.v = g.v;
+  a.block_stride = g.block_stride;
+  a.row_stride = g.row_stride;
+  a.num_kv_heads = g.num_kv_heads;
+  a.num_blocks_m1 = (int32_t)(g.num_blocks - 1);
+  a.num_q_heads = num_q_heads;
+  a.gqa = num_q_heads / g.num_kv_heads;
+  a.q = (const _Float16*)q;
+  a.out = (_Float16*)out;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  const int64_t table_cap = (int64_t)max_blocks_per_seq * g.block_size;
+  a.len_cap = (int32_t)(table_cap < max_seq_len ? table_cap : max_seq_len);
+  a.seq_lens = seq_lens;
+  a.score_scale = (float)((double)scale * 1.4426950408889634 * (double)g.k_scale);
+  a.v_scale = g.v_scale;
+  a.k_hs = g.k_hs;
+  a.v_hs = g.v_hs;
+  a.window = g.window;
+  (void)num_seqs;
+  return PA_OK;
+}
+
+int kv_code(const pa::PoolGeom& g) { return g.elem_bytes == 2 ? 0 : (g.fp8_e5m2 ? 2 : 1); }
+
 }  // namespace
 
 extern "C" {
@@ -278,6 +363,7 @@ size_t pa_decode_workspace_size(const pa_kv_pool* pool, int32_t num_seqs, int32_
   return workspace_bytes_for(pl, num_seqs, num_q_heads, g.num_kv_heads, g.head_dim);
 }
 
+
 int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs,
               int32_t num_q_heads, const int32_t* block_tables, int32_t max_blocks_per_seq,
               const int32_t* seq_lens, int32_t max_seq_len, float scale, int32_t partition_size,
@@ -287,13 +373,10 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
   int st = plan(pool, num_seqs, num_q_heads, max_seq_len, partition_size, &g, &pl);
   if (st) return st;
   if (num_seqs == 0) return PA_OK;
-  if (!out || !q || !block_tables || !seq_lens)
-    return fail(PA_ERR_INVALID_ARG, "out, q, block_tables and seq_lens must be non-NULL");
-  if (!aligned16(out) || !aligned16(q))
-    return fail(PA_ERR_ALIGNMENT, "q and out must be 16-byte aligned");
-  if (max_blocks_per_seq < 1)
-    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  pa::DecodeArgs a;
+  st = decode_args(g, out, q, num_seqs, num_q_heads, block_tables, max_blocks_per_seq, seq_lens,
+                   max_seq_len, scale, &a);
+  if (st) return st;
   const size_t need = workspace_bytes_for(pl, num_seqs, num_q_heads, g.num_kv_heads, g.head_dim);
   if (need) {
     if (!workspace || workspace_bytes < need)
@@ -302,27 +385,6 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
     if (!aligned16(workspace)) return fail(PA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   }
 
-  pa::DecodeArgs a{};
-  a.k = g.k;
-  a.v = g.v;
-  a.block_stride = g.block_stride;
-  a.row_stride = g.row_stride;
-  a.num_kv_heads = g.num_kv_heads;
-  a.num_blocks_m1 = (int32_t)(g.num_blocks - 1);
-  a.num_q_heads = num_q_heads;
-  a.gqa = num_q_heads / g.num_kv_heads;
-  a.q = (const _Float16*)q;
-  a.out = (_Float16*)out;
-  a.block_tables = block_tables;
-  a.max_blocks = max_blocks_per_seq;
-  const int64_t table_cap = (int64_t)max_blocks_per_seq * g.block_size;
-  a.len_cap = (int32_t)(table_cap < max_seq_len ? table_cap : max_seq_len);
-  a.seq_lens = seq_lens;
-  a.score_scale = (float)((double)scale * 1.4426950408889634 * (double)g.k_scale);
-  a.v_scale = g.v_scale;
-  a.k_hs = g.k_hs;
-  a.v_hs = g.v_hs;
-  a.window = g.window;
   pa::FlatArgs f{};
   if (pl.mode == pa::kModeSplit) {
     a.part_tokens = pl.part;
@@ -337,10 +399,147 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
     f.slots = (float*)((char*)workspace + align256((size_t)(num_seqs + 1) * 4));
   }
   const bool stream_kv = !(g.flags & PA_POOL_SHARED_BLOCKS);
-  if (hipError_t e = pa::launch_decode(a, &f, num_seqs, g.head_dim, g.block_size,
-                                       g.elem_bytes == 2 ? 0 : (g.fp8_e5m2 ? 2 : 1),
-                                       stream_kv, pl.mode, stream))
+  if (hipError_t e = pa::launch_decode(a, &f, nullptr, num_seqs, g.head_dim, g.block_size,
+                                       kv_code(g), stream_kv, pl.mode, stream))
     return fail(PA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int32_t pa_decode_group_plan(const int32_t* block_tables, int32_t num_seqs,
+                             int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                             int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t* members, int32_t* member_start, int32_t* shared_tokens) {
+  if (num_seqs < 0 || max_blocks_per_seq < 1 || block_size < 1 || num_kv_heads < 1 ||
+      num_q_heads < num_kv_heads || num_q_heads % num_kv_heads ||
+      num_q_heads / num_kv_heads > 16)
+    return fail(PA_ERR_INVALID_ARG, "bad sizes for the group plan");
+  if (num_seqs && (!block_tables || !seq_lens || !members || !member_start || !shared_tokens))
+    return fail(PA_ERR_INVALID_ARG, "group plan arrays must be non-NULL");
+  const int32_t cap = 16 / (num_q_heads / num_kv_heads);
+  auto len_of = [&](int32_t s) {
+    const int64_t n = seq_lens[s], m = (int64_t)max_blocks_per_seq * block_size;
+    return (int32_t)(n < 0 ? 0 : (n > m ? m : n));
+  };
+  // families: sequences whose first block is the same physical block, in order
+  // of their first member; short contexts (no whole 16-token tile) stay alone
+  std::vector<std::vector<int32_t>> fam;
+  std::unordered_map<int32_t, size_t> by_first;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (len_of(s) < 16 || cap < 2) {
+      fam.push_back({s});
+      continue;
+    }
+    auto it = by_first.find(block_tables[(int64_t)s * max_blocks_per_seq]);
+    if (it == by_first.end()) {
+      by_first.emplace(block_tables[(int64_t)s * max_blocks_per_seq], fam.size());
+      fam.push_back({s});
+    } else {
+      fam[it->second].push_back(s);
+    }
+  }
+  // groups: runs of up to `cap` members of a family; shared = the leading
+  // blocks all of them list, in whole 16-token tiles, within every context
+  struct G { int32_t first, n, shared; int64_t work; };
+  std::vector<G> groups;
+  std::vector<int32_t> order;
+  order.reserve((size_t)num_seqs);
+  for (const auto& f : fam) {
+    for (size_t i0 = 0; i0 < f.size(); i0 += (size_t)cap) {
+      const size_t i1 = std::min(f.size(), i0 + (size_t)cap);
+      int32_t min_len = INT32_MAX;
+      for (size_t i = i0; i < i1; ++i) min_len = std::min(min_len, len_of(f[i]));
+      int32_t lcp = (min_len + block_size - 1) / block_size;
+      const int32_t* r0 = block_tables + (int64_t)f[i0] * max_blocks_per_seq;
+      for (size_t i = i0 + 1; i < i1 && lcp > 0; ++i) {
+        const int32_t* ri = block_tables + (int64_t)f[i] * max_blocks_per_seq;
+        int32_t k = 0;
+        while (k < lcp && ri[k] == r0[k]) ++k;
+        lcp = k;
+      }
+      int32_t shared = i1 - i0 > 1 ? std::min((int64_t)lcp * block_size, (int64_t)min_len) : 0;
+      shared &= ~15;
+      if (shared == 0 && i1 - i0 > 1) {       // nothing to share: one group per sequence
+        for (size_t i = i0; i < i1; ++i) {
+          groups.push_back({(int32_t)order.size(), 1, 0, (len_of(f[i]) + 15) / 16});
+          order.push_back(f[i]);
+        }
+        continue;
+      }
+      int64_t work = shared / 16;
+      for (size_t i = i0; i < i1; ++i) work += (len_of(f[i]) + 15) / 16 - shared / 16;
+      groups.push_back({(int32_t)order.size(), (int32_t)(i1 - i0), shared, work});
+      for (size_t i = i0; i < i1; ++i) order.push_back(f[i]);
+    }
+  }
+  // the longest groups start first, so that the short ones fill in at the end
+  std::stable_sort(groups.begin(), groups.end(),
+                   [](const G& x, const G& y) { return x.work > y.work; });
+  int32_t pos = 0;
+  for (size_t i = 0; i < groups.size(); ++i) {
+    member_start[i] = pos;
+    shared_tokens[i] = groups[i].shared;
+    for (int32_t k = 0; k < groups[i].n; ++k) members[pos++] = order[(size_t)groups[i].first + k];
+  }
+  member_start[groups.size()] = pos;
+  return (int32_t)groups.size();
+}
+
+int32_t pa_decode_grouped_plan(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t max_seq_len, int32_t num_groups, int32_t schedule) {
+  pa::PoolGeom g;
+  GroupPlan gp;
+  int st = group_plan(pool, num_seqs, num_q_heads, max_seq_len, num_groups, schedule, &g, &gp);
+  return st ? st : gp.mode;
+}
+
+size_t pa_decode_grouped_workspace_size(const pa_kv_pool* pool, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t max_seq_len,
+                                        int32_t num_groups, int32_t schedule) {
+  pa::PoolGeom g;
+  GroupPlan gp;
+  if (group_plan(pool, num_seqs, num_q_heads, max_seq_len, num_groups, schedule, &g, &gp))
+    return 0;
+  return gp.workspace;
+}
+
+int pa_decode_grouped(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs,
+                      int32_t num_q_heads, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                      float scale, int32_t num_groups, const int32_t* members,
+                      const int32_t* member_start, const int32_t* shared_tokens,
+                      int32_t schedule, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  pa::PoolGeom g;
+  GroupPlan gpl;
+  int st = group_plan(pool, num_seqs, num_q_heads, max_seq_len, num_groups, schedule, &g, &gpl);
+  if (st) return st;
+  if (num_seqs == 0 || num_groups == 0) return PA_OK;
+  if (!members || !member_start || !shared_tokens)
+    return fail(PA_ERR_INVALID_ARG, "members, member_start and shared_tokens must be non-NULL");
+  pa::DecodeArgs a;
+  st = decode_args(g, out, q, num_seqs, num_q_heads, block_tables, max_blocks_per_seq, seq_lens,
+                   max_seq_len, scale, &a);
+  if (st) return st;
+  if (gpl.workspace) {
+    if (!workspace || workspace_bytes < gpl.workspace)
+      return fail(PA_ERR_WORKSPACE, "this schedule needs %zu workspace bytes, got %zu",
+                  gpl.workspace, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(PA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  }
+  pa::GroupArgs gr{num_groups, num_seqs, num_seqs, members, member_start, shared_tokens};
+  pa::FlatArgs f{};
+  if (gpl.mode == kGroupFlat) {
+    f.num_seqs = num_seqs;
+    f.num_ranges = (int32_t)gpl.ranges;
+    f.prefix = (int32_t*)workspace;
+    f.slots = (float*)((char*)workspace + align256((size_t)(num_groups + 1) * 4));
+  }
+  // every tile is read by one wave: streaming loads whatever the pool flag says
+  if (hipError_t e = pa::launch_decode(a, &f, &gr, num_seqs, g.head_dim, g.block_size,
+                                       kv_code(g), true,
+                                       gpl.mode == kGroupFlat ? pa::kModeFlatGroup
+                                                              : pa::kModeGroup, stream))
+    return fail(PA_ERR_HIP, "grouped decode launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

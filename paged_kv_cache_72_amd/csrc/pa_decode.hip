@@ -70,6 +70,18 @@ namespace {
 #ifndef PA_FLAT_WAVES_PER_EU
 #define PA_FLAT_WAVES_PER_EU 2
 #endif
+#ifndef PA_GROUP_WAVES_PER_EU
+#define PA_GROUP_WAVES_PER_EU 2
+#endif
+#ifndef PA_GROUP_WAVES
+#define PA_GROUP_WAVES 4      // grouped schedule: waves per workgroup
+#endif
+#ifndef PA_GROUP_NT
+#define PA_GROUP_NT 1         // grouped schedule: streaming K/V loads whatever the pool flag
+#endif
+#ifndef PA_GROUP_EXTRA_LDS
+#define PA_GROUP_EXTRA_LDS 0  // bytes of dynamic LDS per workgroup (limits residency)
+#endif
 #ifndef PA_FLAT_STAGES
 #define PA_FLAT_STAGES 2      // flat schedule: tiles in flight per wave, plus one
 #endif
@@ -198,6 +210,19 @@ struct Engine {
     }
   }
   __device__ __forceinline__ void load_q(const _Float16* qrow0) { load_q_into(qop, qrow0); }
+  // Query operands when every column has its own row: lane (r, c) reads
+  // qrow, the row of column c (nullptr: a padding column, zeros), at the
+  // dims load_q_into gives it.
+  __device__ __forceinline__ void load_q_rows_into(half4_t* dst, const _Float16* qrow) const {
+#pragma unroll
+    for (int cl = 0; cl < NKL; ++cl) {
+#pragma unroll
+      for (int grp = 0; grp < GPL; ++grp)
+        dst[cl * GPL + grp] =
+            qrow ? *(const half4_t*)(qrow + cl * 4 * KCH + r * KCH + 4 * grp) : (half4_t){};
+    }
+  }
+  __device__ __forceinline__ void load_q_rows(const _Float16* qrow) { load_q_rows_into(qop, qrow); }
   __device__ __forceinline__ void take_q(const half4_t* src) {
 #pragma unroll
     for (int i = 0; i < NQ; ++i) qop[i] = src[i];
@@ -261,11 +286,14 @@ struct Engine {
     }
   }
 
-  // Fold tile j (tokens 16j..16j+15) into the running state; tokens >= t_end
-  // are masked.
-  // Tokens t_begin .. t_end - 1 of tile j count; the others are masked.
+  // Fold tile j (tokens 16j..16j+15) into the running state.  Tokens
+  // t_begin .. t_end - 1 of tile j count; the others are masked.  With
+  // COLS, only query columns col_lo .. col_hi - 1 take this tile (the other
+  // columns' scores are masked, so their state is untouched): the grouped
+  // schedule's columns belong to several sequences.
+  template <bool COLS = false>
   __device__ __forceinline__ void compute(int j, int t_begin, int t_end, const uint4* kr,
-                                          const VT* vr_in) {
+                                          const VT* vr_in, int col_lo = 0, int col_hi = 16) {
     // Loads issued before this point stay before it: otherwise the scheduler
     // hoists the waits for this tile above the next tile's loads.
     __builtin_amdgcn_sched_barrier(0);
@@ -299,13 +327,14 @@ struct Engine {
     const uint32_t span = (uint32_t)(t_end - t_begin);
     const int tb = j * 16 + r;                  // token of score i: tb + 4 i
     float x[4];
+    const bool col_ok = !COLS || (uint32_t)(c - col_lo) < (uint32_t)(col_hi - col_lo);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      x[i] = ((uint32_t)(tb + 4 * i - t_begin) < span) ? sacc[i] * sc : -INFINITY;
+      x[i] = (col_ok && (uint32_t)(tb + 4 * i - t_begin) < span) ? sacc[i] * sc : -INFINITY;
     float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     tmax = xor_max(tmax, 16);
     tmax = xor_max(tmax, 32);
-    const bool grow = (c < g) && (tmax > m_run + kLazy);
+    const bool grow = (COLS ? col_ok : (c < g)) && (tmax > m_run + kLazy);
     if (__any(grow)) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -405,6 +434,55 @@ struct Engine {
         }
       }
     }
+  }
+
+  // Write acc / l (times v_scale) for columns 0 .. ncols - 1, column h to the
+  // row dst(h) (a grouped segment: the columns belong to several sequences).
+  template <class RowOf>
+  __device__ __forceinline__ void store_out_cols(const RowOf& dst, int ncols, float lt,
+                                                 float v_scale) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * r + i;
+      const float lh = __shfl(lt, h);
+      if (h < ncols) {
+        const float inv = lh > 0.f ? v_scale / lh : 0.f;
+        _Float16 o[DCH];
+#pragma unroll
+        for (int e = 0; e < DCH; ++e) o[e] = (_Float16)(acc[e][i] * inv);
+        _Float16* row = dst(h) + c * DCH;
+        if constexpr (DCH == 16) {
+          const u32x8 w = __builtin_bit_cast(u32x8, o);
+          ((uint4*)row)[0] = w.lo;
+          ((uint4*)row)[1] = w.hi;
+        } else if constexpr (DCH == 8) {
+          *(uint4*)row = __builtin_bit_cast(uint4, o);
+        } else {
+          *(uint2*)row = __builtin_bit_cast(uint2, o);
+        }
+      }
+    }
+  }
+
+  // A 16-column partial record: o[h][d] (fp32, normalised, times v_scale) for
+  // h < 16, then (m, l) per column; columns >= ncols are written as empty.
+  __device__ __forceinline__ void store_partial16(float* rec, int ncols, float lt,
+                                                  float v_scale) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * r + i;
+      const float lh = __shfl(lt, h);
+      if (h < ncols) {
+        const float inv = lh > 0.f ? v_scale / lh : 0.f;
+        float4* d4 = (float4*)(rec + (int64_t)h * D + c * DCH);
+#pragma unroll
+        for (int q = 0; q < DCH / 4; ++q)
+          d4[q] = make_float4(acc[4 * q][i] * inv, acc[4 * q + 1][i] * inv,
+                              acc[4 * q + 2][i] * inv, acc[4 * q + 3][i] * inv);
+      }
+    }
+    if (r == 0)
+      ((float2*)(rec + 16 * D))[c] = c < ncols ? make_float2(m_run, lt) : make_float2(kNegBig, 0.f);
   }
 
   // Write a partial: o[h][d] = acc / l * v_scale (fp32) then (m, l) per head.
@@ -547,6 +625,171 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
     } else {
       a.out[row * D + d] = (_Float16)o;
     }
+  }
+}
+
+// ---------------------------------------------------------------- grouped
+
+// One workgroup per (group, KV head).  A group is up to 16 / gqa sequences
+// whose first `shared` positions sit in the same physical blocks (forked
+// sequences, prefix-cache hits: "PagedAttention & vLLM", memory sharing).
+// Query column c is (member c / gqa, head c % gqa), so one 16x16 MFMA scores a
+// K tile for every member at once and each shared K/V tile leaves HBM once
+// per group instead of once per member.  Units: the shared tiles (every
+// member's columns take them), then each member's own tiles from `shared` on
+// (only its columns take them; the others' scores are masked).  The waves
+// take units round-robin, one tile in flight ahead of the one computed, and
+// merge in LDS.
+template <int D, int BS, int KV, int NW, bool NT>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : PA_GROUP_WAVES_PER_EU, 8)))
+void decode_group_kernel(DecodeArgs a, GroupArgs gp, const int32_t* __restrict__ tables,
+                         const int32_t* __restrict__ lens) {
+  typedef Engine<D, BS, KV, NT> En;
+  typedef typename En::VT VT;
+  const int lane = threadIdx.x & 63;
+  const int wid = uni(threadIdx.x >> 6);
+  const int kh = blockIdx.x % a.num_kv_heads;
+  const int grp = blockIdx.x / a.num_kv_heads;
+  const int g = a.gqa;
+
+  // ---- members, clamped into the arrays (device contents are not validated),
+  // read by the lanes of wave 0 in parallel: one member per lane
+  __shared__ int sm_seq[16], sm_len[16], sm_pre[17], sm_meta[2];
+  if (wid == 0) {
+    int m0 = gp.member_start[grp], m1 = gp.member_start[grp + 1];
+    m0 = m0 < 0 ? 0 : (m0 > gp.num_members ? gp.num_members : m0);
+    m1 = m1 < m0 ? m0 : (m1 > gp.num_members ? gp.num_members : m1);
+    const int nm = m1 - m0 < 16 / g ? m1 - m0 : 16 / g;
+    int sq = 0, ln = INT32_MAX;
+    if (lane < nm) {
+      sq = gp.members[m0 + lane];
+      sq = sq < 0 ? 0 : (sq >= gp.num_seqs ? gp.num_seqs - 1 : sq);
+      ln = clamp_len(lens[sq], a.len_cap);
+    }
+    int mn = ln;                              // shortest member
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mn = min(mn, __shfl_xor(mn, o));
+    int sh = gp.shared_tokens[grp];
+    sh = nm == 0 ? 0 : (sh < 0 ? 0 : (sh > mn ? mn : sh) & ~15);   // whole 16-token tiles
+    int x = lane < nm ? ((ln + 15) >> 4) - (sh >> 4) : 0;          // member's own tiles
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {        // inclusive scan over lanes 0..15
+      const int y = __shfl_up(x, o);
+      if ((lane & 15) >= o) x += y;
+    }
+    if (lane < nm) {
+      sm_seq[lane] = sq;
+      sm_len[lane] = ln;
+    }
+    if (lane < 16) sm_pre[lane + 1] = x;
+    if (lane == 0) {
+      sm_pre[0] = 0;
+      sm_meta[0] = nm;
+      sm_meta[1] = sh;
+    }
+  }
+  __syncthreads();
+  const int nm = uni(sm_meta[0]), sh = uni(sm_meta[1]);
+  const int nsh = sh >> 4;                    // shared tiles
+  const int U = nsh + uni(sm_pre[nm]);        // units of the workgroup
+  const int ncols = nm * g;
+
+  __shared__ __attribute__((aligned(16))) char kstage[NW][En::KST];
+  En en;
+  en.init(a, lane, (lds_char*)kstage[wid]);
+  if (a.k_hs) en.sc *= a.k_hs[kh];
+  const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
+  const int64_t head_off = (int64_t)kh * D * En::E;
+  {
+    const int c = lane & 15;
+    const _Float16* qrow = nullptr;
+    if (c < ncols)
+      qrow = a.q + ((int64_t)sm_seq[c / g] * a.num_q_heads + (int64_t)kh * g + c % g) * D;
+    en.load_q_rows(qrow);
+  }
+  en.reset();
+
+  // unit u -> member (-1: shared tile) and the tile's block ids
+  auto member_of = [&](int u) -> int {
+    if (u < nsh) return -1;
+    const int v = u - nsh;
+    int i = 0;
+    while (i + 1 < nm && sm_pre[i + 1] <= v) ++i;
+    return uni(i);
+  };
+  auto ids_of = [&](int u) -> Ids {
+    const int i = member_of(u);
+    const int m = i < 0 ? 0 : i;
+    const int ln = uni(sm_len[m]);
+    const PairRef p{tables + (int64_t)uni(sm_seq[m]) * a.max_blocks,
+                    ln > 0 ? (ln + BS - 1) / BS : 1, ln, head_off};
+    return en.tile_ids(p, i < 0 ? u : nsh + (u - nsh - uni(sm_pre[i])));
+  };
+  auto run = [&](int u, const uint4* kr, const VT* vr) {
+    const int i = member_of(u);
+    if (i < 0)
+      en.template compute<true>(u, 0, sh, kr, vr, 0, ncols);
+    else
+      en.template compute<true>(nsh + (u - nsh - uni(sm_pre[i])), 0, uni(sm_len[i]), kr, vr,
+                                i * g, i * g + g);
+  };
+
+  uint4 kA[En::NKL], kB[En::NKL];
+  VT vA[4], vB[4];
+  int u = wid;
+  if (u < U) {
+    const int u_last = U - 1;
+    en.issue(ids_of(u), kA, vA);
+    Ids ids_b = ids_of(min(u + NW, u_last));  // past the end: repeat a loaded tile
+    for (;;) {
+      en.issue(ids_b, kB, vB);
+      const Ids ids_a = ids_of(min(u + 2 * NW, u_last));
+      run(u, kA, vA);
+      u += NW;
+      if (u >= U) break;
+      en.issue(ids_a, kA, vA);
+      ids_b = ids_of(min(u + 2 * NW, u_last));
+      run(u, kB, vB);
+      u += NW;
+      if (u >= U) break;
+    }
+  }
+  const float l_tot = en.l_total();
+
+  // ---- merge the waves of the workgroup in LDS, then write every column
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  __shared__ float sm_o[NW][16][D];
+  const int r = lane >> 4, c = lane & 15;
+  if (r == 0) {
+    sm_m[wid][c] = en.m_run;
+    sm_l[wid][c] = l_tot;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * r + i;
+    if (h < ncols) {
+#pragma unroll
+      for (int e = 0; e < En::DCH; ++e) sm_o[wid][h][c * En::DCH + e] = en.acc[e][i];
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ncols * D; idx += NW * 64) {
+    const int h = idx / D, d = idx - (idx / D) * D;
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = exp2f(sm_m[w][h] - M);
+      L += f * sm_l[w][h];
+      O += f * sm_o[w][h][d];
+    }
+    const float o = L > 0.f ? (O / L) * v_scale : 0.f;
+    const int64_t row = (int64_t)sm_seq[h / g] * a.num_q_heads + (int64_t)kh * g + h % g;
+    a.out[row * D + d] = (_Float16)o;
   }
 }
 
@@ -914,13 +1157,289 @@ __global__ __launch_bounds__(256) void flat_merge_rows_kernel(DecodeArgs a, Flat
     a.out[(int64_t)row * D + lane * DPL + e] = (_Float16)(O[e] * inv);
 }
 
+// ---------------------------------------------------------------- flat schedule over groups
+
+// The grouped schedule's work laid out as the flat schedule lays out
+// sequences: the units of each group (its shared tiles, then each member's own
+// tiles from the shared length on) are listed group after group and cut into
+// equal ranges, walked by one wave per KV head.  A group inside one range is
+// written directly; a group cut by range boundaries leaves one 16-column
+// partial record per range (slot 0: the range's first segment, slot 1: its
+// last), merged by flat_group_merge_kernel.  Query column c of a group is
+// (member c / gqa, head c % gqa), as in decode_group_kernel.
+template <int D, int BS, int KV, int NW, bool NT>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : PA_FLAT_WAVES_PER_EU, 8)))
+void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
+                              const int32_t* __restrict__ tables,
+                              const int32_t* __restrict__ lens, const _Float16* __restrict__ qs,
+                              _Float16* __restrict__ outs, float* __restrict__ slots,
+                              int32_t* __restrict__ prefix) {
+  typedef Engine<D, BS, KV, NT> En;
+  typedef typename En::VT VT;
+  const int G = gp.num_groups, M = gp.num_members, Hkv = a.num_kv_heads, g = a.gqa;
+  const int cap = 16 / g;
+  extern __shared__ int sm[];
+  int* sm_pre = sm;                            // [G + 1] units before group i
+  int* sm_ms = sm_pre + G + 1;                 // [G + 1] first member of group i
+  int* sm_nsh = sm_ms + G + 1;                 // [G] shared tiles of group i
+  int* sm_seq = sm_nsh + G;                    // [M] sequence of member p
+  int* sm_len = sm_seq + M;                    // [M] its context length
+  int* sm_mpre = sm_len + M;                   // [M] own units of the members before p
+  const int lane = threadIdx.x & 63;
+  const int wid = uni(threadIdx.x >> 6);
+  constexpr int NTH = NW * 64;
+
+  // ---- group and member tables in LDS, clamped into the arrays (device
+  // contents are not validated); per-group unit counts, then their scan
+  for (int i = threadIdx.x; i <= G; i += NTH) {
+    const int v = gp.member_start[i];
+    sm_ms[i] = v < 0 ? 0 : (v > M ? M : v);
+  }
+  for (int p = threadIdx.x; p < M; p += NTH) {
+    int sq = gp.members[p];
+    sq = sq < 0 ? 0 : (sq >= gp.num_seqs ? gp.num_seqs - 1 : sq);
+    sm_seq[p] = sq;
+    sm_len[p] = clamp_len(lens[sq], a.len_cap);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G; i += NTH) {
+    const int m0 = sm_ms[i], m1 = sm_ms[i + 1] > m0 ? sm_ms[i + 1] : m0;
+    const int nm = m1 - m0 < cap ? m1 - m0 : cap;
+    int mn = INT32_MAX;
+    for (int p = m0; p < m0 + nm; ++p) mn = sm_len[p] < mn ? sm_len[p] : mn;
+    int sh = gp.shared_tokens[i];
+    sh = nm == 0 ? 0 : (sh < 0 ? 0 : (sh > mn ? mn : sh) & ~15);
+    int own = 0;
+    for (int p = m0; p < m0 + nm; ++p) {
+      sm_mpre[p] = own;
+      own += ((sm_len[p] + 15) >> 4) - (sh >> 4);
+    }
+    sm_nsh[i] = sh >> 4;
+    sm_pre[i + 1] = (sh >> 4) + own;
+  }
+  __syncthreads();
+  __shared__ int sm_wsum[NW];
+  {
+    const int per = (G + NTH - 1) / NTH;
+    const int b0 = min(G, (int)threadIdx.x * per), b1 = min(G, b0 + per);
+    int sum = 0;
+    for (int i = b0; i < b1; ++i) sum += sm_pre[i + 1];
+    int x = sum;                               // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) sm_wsum[wid] = x;
+    __syncthreads();
+    int run = x - sum;
+    for (int w = 0; w < wid; ++w) run += sm_wsum[w];
+    for (int i = b0; i < b1; ++i) {
+      run += sm_pre[i + 1];
+      sm_pre[i + 1] = run;
+    }
+    if (threadIdx.x == 0) sm_pre[0] = 0;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= G; i += NTH) prefix[i] = sm_pre[i];
+  // groups without any unit (every member empty) get all-zero rows here
+  for (int i = blockIdx.x; i < G; i += gridDim.x) {
+    if (sm_pre[i + 1] != sm_pre[i]) continue;
+    const int m0 = sm_ms[i], m1 = sm_ms[i + 1] > m0 ? sm_ms[i + 1] : m0;
+    const int nm = m1 - m0 < cap ? m1 - m0 : cap;
+    for (int p = m0; p < m0 + nm; ++p) {
+      _Float16* o = outs + (int64_t)sm_seq[p] * a.num_q_heads * D;
+      for (int k = threadIdx.x; k < a.num_q_heads * D; k += NTH) o[k] = (_Float16)0.f;
+    }
+  }
+
+  const int64_t T = sm_pre[G];
+  const int64_t NR = f.num_ranges;
+  const int gw = blockIdx.x * NW + wid;
+  const int rg = gw / Hkv, kh = gw - (gw / Hkv) * Hkv;
+  if (rg >= NR) return;                        // no barrier follows
+  const int g0 = (int)((int64_t)rg * T / NR), g1 = (int)((int64_t)(rg + 1) * T / NR);
+  if (g0 >= g1) return;
+
+  auto ntiles = [&](int gi) { return uni(sm_pre[gi + 1] - sm_pre[gi]); };
+  auto members = [&](int gi) {                 // (first member, member count)
+    const int m0 = uni(sm_ms[gi]), m1 = uni(sm_ms[gi + 1]);
+    const int n = m1 > m0 ? m1 - m0 : 0;
+    return make_int2(m0, n < cap ? n : cap);
+  };
+  struct Cur { int s, j; };                    // s: group, j: unit within it
+  auto advance = [&](Cur c) -> Cur {
+    if (c.j + 1 < ntiles(c.s)) return {c.s, c.j + 1};
+    int ns = c.s;
+    do { ++ns; } while (ntiles(ns) == 0);
+    return {uni(ns), 0};
+  };
+  // unit -> (member p, tile j); p = -1 for a shared tile (member m0's table)
+  struct Unit { int p, j; };
+  auto unit_of = [&](Cur c) -> Unit {
+    const int nsh = uni(sm_nsh[c.s]);
+    const int2 mm = members(c.s);
+    if (c.j < nsh) return {-1, c.j};
+    const int v = c.j - nsh;
+    int p = mm.x;
+    while (p + 1 < mm.x + mm.y && sm_mpre[p + 1] <= v) ++p;
+    p = uni(p);
+    return {p, nsh + v - uni(sm_mpre[p])};
+  };
+  int lo = 0, hi = G;                          // group with pre[i] <= g0 < pre[i+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (sm_pre[mid] <= g0) lo = mid; else hi = mid;
+  }
+  constexpr int ST = PA_FLAT_STAGES;
+  Cur cur[ST + 1];
+  cur[0] = {uni(lo), uni(g0 - sm_pre[lo])};
+#pragma unroll
+  for (int k = 1; k <= ST; ++k) cur[k] = g0 + k < g1 ? advance(cur[k - 1]) : cur[k - 1];
+
+  __shared__ __attribute__((aligned(16))) char kstage[NW][En::KST];
+  En en;
+  en.init(a, lane, (lds_char*)kstage[wid]);
+  if (a.k_hs) en.sc *= a.k_hs[kh];
+  const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
+  const int64_t head_off = (int64_t)kh * D * En::E;
+  auto ids_of = [&](Cur c) -> Ids {
+    const Unit un = unit_of(c);
+    const int p = un.p < 0 ? uni(sm_ms[c.s]) : un.p;
+    const int len = uni(sm_len[p]);
+    const PairRef pr{tables + (int64_t)uni(sm_seq[p]) * a.max_blocks,
+                     len > 0 ? (len + BS - 1) / BS : 1, len, head_off};
+    return en.tile_ids(pr, un.j);
+  };
+  // this lane's query row in group gi (column c = lane & 15), or nullptr
+  auto qrow_of = [&](int gi) -> const _Float16* {
+    const int2 mm = members(gi);
+    const int c = lane & 15;
+    if (c >= mm.y * g) return nullptr;
+    return qs + ((int64_t)sm_seq[mm.x + c / g] * a.num_q_heads + (int64_t)kh * g + c % g) * D;
+  };
+  float* rec_base = slots + (int64_t)gw * 2 * 16 * (D + 2);
+
+  en.load_q_rows(qrow_of(cur[0].s));
+  en.reset();
+  half4_t qpre[En::NQ];
+  int q_grp = -1;
+  bool seg_from_start = cur[0].j == 0;
+  int seg_start = g0;
+  int gt = g0;
+
+  auto finish = [&]() {
+    const bool grp_end = cur[0].j + 1 == ntiles(cur[0].s);
+    if (!(grp_end || gt + 1 == g1)) return;
+    const float lt = en.l_total();
+    const int2 mm = members(cur[0].s);
+    if (seg_from_start && grp_end) {
+      en.store_out_cols(
+          [&](int h) {
+            return outs + ((int64_t)sm_seq[mm.x + h / g] * a.num_q_heads + (int64_t)kh * g +
+                           h % g) * D;
+          },
+          mm.y * g, lt, v_scale);
+    } else {
+      en.store_partial16(rec_base + (seg_start == g0 ? 0 : 1) * 16 * (D + 2), mm.y * g, lt,
+                         v_scale);
+    }
+    if (gt + 1 < g1) {
+      if (q_grp == cur[1].s) en.take_q(qpre); else en.load_q_rows(qrow_of(cur[1].s));
+      q_grp = -1;
+      en.reset();
+      seg_from_start = true;
+      seg_start = gt + 1;
+    }
+  };
+
+  uint4 kb[ST][En::NKL];
+  VT vb[ST][4];
+#pragma unroll
+  for (int k = 0; k < ST - 1; ++k) {
+    if (k > 0 && cur[k].j == 0 && g0 + k < g1 && q_grp < 0) {
+      en.load_q_rows_into(qpre, qrow_of(cur[k].s));
+      q_grp = cur[k].s;
+    }
+    en.issue(ids_of(cur[k]), kb[k], vb[k]);
+  }
+  Ids ids_next = ids_of(cur[ST - 1]);
+  for (;;) {
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      if (cur[ST - 1].j == 0 && gt + ST - 1 < g1 && q_grp < 0) {
+        en.load_q_rows_into(qpre, qrow_of(cur[ST - 1].s));
+        q_grp = cur[ST - 1].s;
+      }
+      en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST]);
+      ids_next = ids_of(cur[ST]);
+      {
+        const Unit un = unit_of(cur[0]);
+        const int2 mm = members(cur[0].s);
+        const int i = un.p - mm.x;             // the member whose columns take the tile
+        const int t_end = un.p < 0 ? uni(sm_nsh[cur[0].s]) * 16 : uni(sm_len[un.p]);
+        const int clo = un.p < 0 ? 0 : i * g, chi = un.p < 0 ? mm.y * g : i * g + g;
+        en.template compute<true>(un.j, 0, t_end, kb[st], vb[st], clo, chi);
+      }
+      finish();
+      if (++gt == g1) return;
+#pragma unroll
+      for (int k = 0; k < ST; ++k) cur[k] = cur[k + 1];
+      if (gt + ST < g1) cur[ST] = advance(cur[ST]);
+    }
+  }
+}
+
+// One workgroup per (group, KV head): if the group was cut by range
+// boundaries, merge its per-range 16-column records by log-sum-exp, in range
+// order (deterministic), and write every member's rows.
+template <int D>
+__global__ __launch_bounds__(256) void flat_group_merge_kernel(DecodeArgs a, FlatArgs f,
+                                                               GroupArgs gp) {
+  const int kh = blockIdx.x % a.num_kv_heads, gi = blockIdx.x / a.num_kv_heads;
+  const int g = a.gqa, cap = 16 / g, G = gp.num_groups;
+  const int64_t T = f.prefix[G];
+  const int pre = f.prefix[gi], end = f.prefix[gi + 1];
+  if (end == pre) return;
+  const int64_t NR = f.num_ranges;
+  const int r_first = range_of(pre, T, NR), r_last = range_of(end - 1, T, NR);
+  if (r_first == r_last) return;               // written by the decode kernel
+  const bool first_is_last_slot = (int64_t)r_first * T / NR < pre;
+  int m0 = gp.member_start[gi], m1 = gp.member_start[gi + 1];
+  m0 = m0 < 0 ? 0 : (m0 > gp.num_members ? gp.num_members : m0);
+  m1 = m1 < m0 ? m0 : (m1 > gp.num_members ? gp.num_members : m1);
+  const int ncols = (m1 - m0 < cap ? m1 - m0 : cap) * g;
+  for (int idx = threadIdx.x; idx < ncols * D; idx += 256) {
+    const int h = idx / D, d = idx - (idx / D) * D;
+    float M = kNegBig, L = 0.f, O = 0.f;
+    for (int r = r_first; r <= r_last; ++r) {
+      if (range_empty(r, T, NR)) continue;     // owns no unit: wrote no record this call
+      const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
+      const float* p = f.slots + ((int64_t)(r * a.num_kv_heads + kh) * 2 + slot) * 16 * (D + 2);
+      const float2 ml = ((const float2*)(p + 16 * D))[h];
+      const float ov = p[h * D + d];
+      const float mn = fmaxf(M, ml.x);
+      const float sa = __builtin_amdgcn_exp2f(M - mn), sb = ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
+      L = L * sa + sb;
+      O = O * sa + sb * ov;
+      M = mn;
+    }
+    int sq = gp.members[m0 + h / g];
+    sq = sq < 0 ? 0 : (sq >= gp.num_seqs ? gp.num_seqs - 1 : sq);
+    a.out[((int64_t)sq * a.num_q_heads + (int64_t)kh * g + h % g) * D + d] =
+        (_Float16)(L > 0.f ? O / L : 0.f);
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 constexpr int kWaves = PA_DECODE_WAVES;
 
 template <int D, int BS, int KV, bool NT>
-hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int mode,
-                        hipStream_t stream) {
+hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, const GroupArgs* gr,
+                        int32_t num_seqs, int mode, hipStream_t stream) {
   const uint32_t units = (uint32_t)num_seqs * (uint32_t)a.num_kv_heads;
   if (mode == kModeFlat) {
     const size_t lds = sizeof(int) * (2 * (size_t)num_seqs + 1);
@@ -944,6 +1463,26 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs
       hipLaunchKernelGGL((flat_merge_kernel<D, 4>), mgrid, dim3(4 * D), 0, stream, a, *f);
     else
       hipLaunchKernelGGL((flat_merge_kernel<D, 8>), mgrid, dim3(8 * D), 0, stream, a, *f);
+  } else if (mode == kModeFlatGroup) {
+    const size_t lds = sizeof(int) * (3 * (size_t)gr->num_groups + 2 + 3 * (size_t)gr->num_members);
+    const int64_t waves = (int64_t)f->num_ranges * a.num_kv_heads;
+    constexpr int FW = PA_FLAT_WAVES;
+    hipLaunchKernelGGL((decode_flat_group_kernel<D, BS, KV, FW, PA_GROUP_NT || NT>),
+                       dim3((uint32_t)((waves + FW - 1) / FW)), dim3(FW * 64), lds, stream, a,
+                       *f, *gr, a.block_tables, a.seq_lens, a.q, a.out, f->slots, f->prefix);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((flat_group_merge_kernel<D>),
+                       dim3((uint32_t)gr->num_groups * (uint32_t)a.num_kv_heads), dim3(256), 0,
+                       stream, a, *f, *gr);
+  } else if (mode == kModeGroup) {
+    // every tile is read by one wave of one group: streaming loads (a member's
+    // own tiles may sit in blocks other members also list past the shared
+    // length; those few re-reads go to HBM again)
+    hipLaunchKernelGGL((decode_group_kernel<D, BS, KV, PA_GROUP_WAVES, PA_GROUP_NT || NT>),
+                       dim3((uint32_t)gr->num_groups * (uint32_t)a.num_kv_heads),
+                       dim3(PA_GROUP_WAVES * 64), PA_GROUP_EXTRA_LDS, stream, a, *gr,
+                       a.block_tables, a.seq_lens);
   } else if (mode == kModeSplit) {
     hipLaunchKernelGGL((decode_kernel<D, BS, KV, kWaves, true, NT>),
                        dim3(units * (uint32_t)a.num_parts), dim3(kWaves * 64), 0, stream, a,
@@ -960,10 +1499,10 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs
 }
 
 template <int D, int BS, int KV>
-hipError_t launch_nt(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, bool stream_kv,
-                     int mode, hipStream_t stream) {
-  return stream_kv ? launch_typed<D, BS, KV, true>(a, f, num_seqs, mode, stream)
-                   : launch_typed<D, BS, KV, false>(a, f, num_seqs, mode, stream);
+hipError_t launch_nt(const DecodeArgs& a, const FlatArgs* f, const GroupArgs* gr,
+                     int32_t num_seqs, bool stream_kv, int mode, hipStream_t stream) {
+  return stream_kv ? launch_typed<D, BS, KV, true>(a, f, gr, num_seqs, mode, stream)
+                   : launch_typed<D, BS, KV, false>(a, f, gr, num_seqs, mode, stream);
 }
 
 }  // namespace
@@ -973,21 +1512,23 @@ hipError_t launch_nt(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, b
 // pair (PA_DECODE_SLICE_D / PA_DECODE_SLICE_KV) so the slices compile in
 // parallel, and a plain compile instantiates all of them.
 template <int D, int KV>
-hipError_t launch_decode_dk(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs, int32_t bs,
-                            bool stream_kv, int mode, hipStream_t stream) {
+hipError_t launch_decode_dk(const DecodeArgs& a, const FlatArgs* f, const GroupArgs* gr,
+                            int32_t num_seqs, int32_t bs, bool stream_kv, int mode,
+                            hipStream_t stream) {
   switch (bs) {
-    case 8: return launch_nt<D, 8, KV>(a, f, num_seqs, stream_kv, mode, stream);
-    case 16: return launch_nt<D, 16, KV>(a, f, num_seqs, stream_kv, mode, stream);
-    case 32: return launch_nt<D, 32, KV>(a, f, num_seqs, stream_kv, mode, stream);
-    case 64: return launch_nt<D, 64, KV>(a, f, num_seqs, stream_kv, mode, stream);
-    case 128: return launch_nt<D, 128, KV>(a, f, num_seqs, stream_kv, mode, stream);
+    case 8: return launch_nt<D, 8, KV>(a, f, gr, num_seqs, stream_kv, mode, stream);
+    case 16: return launch_nt<D, 16, KV>(a, f, gr, num_seqs, stream_kv, mode, stream);
+    case 32: return launch_nt<D, 32, KV>(a, f, gr, num_seqs, stream_kv, mode, stream);
+    case 64: return launch_nt<D, 64, KV>(a, f, gr, num_seqs, stream_kv, mode, stream);
+    case 128: return launch_nt<D, 128, KV>(a, f, gr, num_seqs, stream_kv, mode, stream);
   }
   return hipErrorInvalidValue;
 }
 
-#define PA_DECODE_INSTANTIATE(D, KV)                                                        \
-  template hipError_t launch_decode_dk<D, KV>(const DecodeArgs&, const FlatArgs*, int32_t, \
-                                              int32_t, bool, int, hipStream_t);
+#define PA_DECODE_INSTANTIATE(D, KV)                                                         \
+  template hipError_t launch_decode_dk<D, KV>(const DecodeArgs&, const FlatArgs*,            \
+                                              const GroupArgs*, int32_t, int32_t, bool, int, \
+                                              hipStream_t);
 #if defined(PA_DECODE_SLICE_D) && defined(PA_DECODE_SLICE_KV)
 PA_DECODE_INSTANTIATE(PA_DECODE_SLICE_D, PA_DECODE_SLICE_KV)
 #else

@@ -65,7 +65,19 @@ struct FlatArgs {
   float* slots;               // [num_ranges * Hkv][2][gqa][head_dim + 2] partial records
 };
 
-enum { kModeSingle = 0, kModeSplit = 1, kModeFlat = 2 };
+// Grouped schedule: group i is the sequences members[member_start[i] ..
+// member_start[i + 1]), whose first shared_tokens[i] positions sit in the same
+// physical blocks (device arrays).
+struct GroupArgs {
+  int32_t num_groups;
+  int32_t num_seqs;
+  int32_t num_members;        // length of members
+  const int32_t* members;
+  const int32_t* member_start;  // [num_groups + 1]
+  const int32_t* shared_tokens; // [num_groups]
+};
+
+enum { kModeSingle = 0, kModeSplit = 1, kModeFlat = 2, kModeGroup = 3, kModeFlatGroup = 4 };
 
 hipError_t launch_reshape_and_cache(const PoolGeom& g, const _Float16* k_new,
                                     const _Float16* v_new, const int64_t* slots, int64_t T,
@@ -75,13 +87,14 @@ hipError_t launch_copy_blocks(const PoolGeom& g, const int64_t* pairs, int64_t n
 // stream_kv: read K/V tiles with the streaming cache policy (pools without
 // blocks shared between sequences of the batch).
 // kv: 0 binary16, 1 e4m3fn, 2 e5m2.
-hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
-                         int32_t head_dim, int32_t block_size, int kv, bool stream_kv, int mode,
-                         hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, const GroupArgs* gr,
+                         int32_t num_seqs, int32_t head_dim, int32_t block_size, int kv,
+                         bool stream_kv, int mode, hipStream_t stream);
 // The decode launchers of one (head_dim, kv) pair (pa_decode.hip).
 template <int D, int KV>
-hipError_t launch_decode_dk(const DecodeArgs& a, const FlatArgs* f, int32_t num_seqs,
-                            int32_t block_size, bool stream_kv, int mode, hipStream_t stream);
+hipError_t launch_decode_dk(const DecodeArgs& a, const FlatArgs* f, const GroupArgs* gr,
+                            int32_t num_seqs, int32_t block_size, bool stream_kv, int mode,
+                            hipStream_t stream);
 
 // Prefill over the paged cache: sequence s owns q rows [q_start[s], q_start[s+1]);
 // its new tokens are the last q_len of its seq_lens[s] positions.

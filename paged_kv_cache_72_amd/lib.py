@@ -30,8 +30,9 @@ PA_POOL_SHARED_BLOCKS = 1
 _DTYPES = {"f16": PA_KV_F16, "fp8_e4m3fn": PA_KV_FP8_E4M3FN, "fp8_e5m2": PA_KV_FP8_E5M2}
 
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
-           "pa_decode_workspace_size", "pa_decode", "pa_decode_noalloc", "pa_prefill",
-           "pa_last_error",
+           "pa_decode_workspace_size", "pa_decode", "pa_decode_grouped", "pa_decode_grouped_plan",
+           "pa_decode_grouped_workspace_size", "pa_decode_group_plan",
+           "pa_decode_noalloc", "pa_prefill", "pa_last_error",
            # host block pool (include/pa_blocks.h)
            "pa_bp_create", "pa_bp_destroy", "pa_bp_last_error", "pa_bp_num_free",
            "pa_bp_ref_count", "pa_bp_block_hash", "pa_bp_free_queue", "pa_bp_get_new_blocks",
@@ -87,6 +88,15 @@ def load() -> C.CDLL:
         L.pa_decode.restype = C.c_int
         L.pa_decode.argtypes = [PP, P, P, I32, I32, P, I32, P, I32, C.c_float, I32, P, C.c_size_t,
                                 P]
+        L.pa_decode_grouped.restype = C.c_int
+        L.pa_decode_grouped.argtypes = [PP, P, P, I32, I32, P, I32, P, I32, C.c_float, I32, P, P,
+                                        P, I32, P, C.c_size_t, P]
+        L.pa_decode_grouped_plan.restype = I32
+        L.pa_decode_grouped_plan.argtypes = [PP, I32, I32, I32, I32, I32]
+        L.pa_decode_grouped_workspace_size.restype = C.c_size_t
+        L.pa_decode_grouped_workspace_size.argtypes = [PP, I32, I32, I32, I32, I32]
+        L.pa_decode_group_plan.restype = I32
+        L.pa_decode_group_plan.argtypes = [P, I32, I32, P, I32, I32, I32, P, P, P]
         L.pa_decode_noalloc.restype = C.c_int
         L.pa_decode_noalloc.argtypes = [PP, P, P, I32, I32, P, I32, P, I32, C.c_float, I32, P]
         L.pa_prefill.restype = C.c_int
@@ -269,6 +279,90 @@ def pa_decode(pool: KVPool, out: torch.Tensor, q: torch.Tensor, block_tables: to
         _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
         _dev(seq_lens, torch.int32, "seq_lens"), int(max_seq_len), C.c_float(scale),
         int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+class DecodeGroups:
+    """A grouping of a decode batch for pa_decode_grouped: host arrays from
+    pa_decode_group_plan and their device copies."""
+
+    def __init__(self, members: np.ndarray, member_start: np.ndarray,
+                 shared_tokens: np.ndarray, device="cuda"):
+        self.members, self.member_start, self.shared_tokens = members, member_start, shared_tokens
+        self.num_groups = int(shared_tokens.size)
+        self.d_members = torch.from_numpy(members).to(device)
+        self.d_member_start = torch.from_numpy(member_start).to(device)
+        self.d_shared_tokens = torch.from_numpy(shared_tokens).to(device)
+
+
+def pa_decode_group_plan(block_tables: np.ndarray, seq_lens: np.ndarray, block_size: int,
+                         num_q_heads: int, num_kv_heads: int, device="cuda") -> DecodeGroups:
+    """Group sequences that list the same leading physical blocks (host
+    arrays in, a DecodeGroups with device copies out)."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    S = int(lens.size)
+    members = np.zeros(max(1, S), np.int32)
+    start = np.zeros(S + 1, np.int32)
+    shared = np.zeros(max(1, S), np.int32)
+    p = lambda a: a.ctypes.data_as(C.c_void_p)
+    n = load().pa_decode_group_plan(p(bt), S, int(bt.shape[1]), p(lens), int(block_size),
+                                    int(num_q_heads), int(num_kv_heads), p(members), p(start),
+                                    p(shared))
+    if n < 0:
+        raise PaError(n, pa_last_error())
+    return DecodeGroups(members[:S].copy(), start[:n + 1].copy(), shared[:n].copy(), device)
+
+
+GROUPED_FLAT, GROUPED_PER_GROUP = 1, 2      # pa_decode_grouped schedules
+
+
+def pa_decode_grouped_plan(pool: KVPool, num_seqs: int, num_q_heads: int, max_seq_len: int,
+                           num_groups: int, schedule: int = 0) -> int:
+    r = load().pa_decode_grouped_plan(C.byref(pool.desc), num_seqs, num_q_heads, max_seq_len,
+                                      num_groups, schedule)
+    if r < 0:
+        raise PaError(r, pa_last_error())
+    return int(r)
+
+
+def alloc_grouped_workspace(pool: KVPool, num_seqs: int, num_q_heads: int, max_seq_len: int,
+                            num_groups: int, schedule: int = 0,
+                            device="cuda") -> Optional[torch.Tensor]:
+    n = int(load().pa_decode_grouped_workspace_size(C.byref(pool.desc), num_seqs, num_q_heads,
+                                                    max_seq_len, num_groups, schedule))
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def pa_decode_grouped(pool: KVPool, out: torch.Tensor, q: torch.Tensor,
+                      block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                      scale: float, groups: DecodeGroups, schedule: int = 0,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """pa_decode with the batch's shared prefixes read once per group; the
+    workspace (flat grouped schedule) is allocated here when not given."""
+    S, Hq, D = q.shape
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape [num_seqs, num_q_heads, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], seq_lens [num_seqs]")
+    if groups.members.size != S:
+        raise ValueError("the grouping must list every sequence once")
+    if CHECK_INPUTS:
+        pa_check_decode_inputs(pool, block_tables, seq_lens, max_seq_len, stream)
+    if workspace is None:
+        workspace = alloc_grouped_workspace(pool, S, Hq, max_seq_len, groups.num_groups,
+                                            schedule, device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, workspace.dtype, "workspace"), workspace.numel() * \
+            workspace.element_size()
+    _check(load().pa_decode_grouped(
+        C.byref(pool.desc), _dev(out, torch.float16, "out"), _dev(q, torch.float16, "q"), S, Hq,
+        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+        _dev(seq_lens, torch.int32, "seq_lens"), int(max_seq_len), C.c_float(scale),
+        groups.num_groups, _dev(groups.d_members, torch.int32, "members"),
+        _dev(groups.d_member_start, torch.int32, "member_start"),
+        _dev(groups.d_shared_tokens, torch.int32, "shared_tokens"), int(schedule), ws_ptr,
+        ws_bytes, _stream(stream)))
 
 
 PA_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20

@@ -462,6 +462,56 @@ def prefix_share(block_size: int = 16, seed: Optional[int] = None) -> Workload:
                    shared_start=shared_start)
 
 
+def shared_prefix_batch(name: str, seed: int, groups, Hq: int, Hkv: int, D: int, bs: int,
+                        num_blocks: Optional[int] = None, kv_dtype: str = "f16",
+                        scale_grain: str = "tensor") -> Workload:
+    """Sequences that reuse a cached prompt prefix, as prefix-cache hits do:
+    ``groups`` lists (prompt_tokens, [tail lengths]) pairs, one sequence per
+    tail; the members of a group list the same physical blocks for the
+    prompt's FULL blocks (written once: the blocks a prefix cache can hit),
+    while the rest of the prompt (a partial block) and each member's tail sit
+    in the member's own blocks.  The last token of every sequence is this
+    step's write."""
+    ss = np.random.SeedSequence(seed).spawn(6)
+    lens = [int(P) + int(t) for P, tails in groups for t in tails]
+    S = len(lens)
+    need = sum(int(P) // bs + sum(cdiv(int(P) + int(t), bs) - int(P) // bs for t in tails)
+               for P, tails in groups) + 1
+    if num_blocks is None:
+        num_blocks = max(need + 8, 2 * need)
+    free = _FreeList(num_blocks, np.random.default_rng(ss[1]))
+    max_blocks = max(1, max(cdiv(n, bs) for n in lens))
+    tables = np.zeros((S, max_blocks), np.int64)
+    slots, new_idx, pos, s = [], [], 0, 0
+    own_from = np.zeros(S, np.int64)
+    own_start = np.zeros(S, np.int64)
+    shared_start = np.full(S, -1, np.int64)
+    for P, tails in groups:
+        full = int(P) // bs
+        fb = free.take(full)
+        slots.append(_slots_for(fb, full * bs, bs))
+        g_start = pos
+        pos += full * bs
+        for t in tails:
+            n = int(P) + int(t)
+            tables[s, :full] = fb
+            tables[s, full:cdiv(n, bs)] = free.take(cdiv(n, bs) - full)
+            own_from[s], shared_start[s], own_start[s] = full * bs, g_start, pos
+            slots.append(_slots_for(tables[s], n - full * bs, bs, start=full * bs))
+            pos += n - full * bs
+            if n > full * bs:               # a member whose context is all shared writes nothing
+                new_idx.append(pos - 1)
+            s += 1
+    pad_block = int(free.take(1)[0])
+    for i in range(S):
+        tables[i, cdiv(lens[i], bs):] = pad_block
+    tok_slot = np.concatenate(slots) if slots else np.zeros(0, np.int64)
+    return _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, np.asarray(lens), tables,
+                   pad_block, tok_slot, np.asarray(new_idx, np.int64), ss,
+                   scale_grain=scale_grain, own_from=own_from, own_start=own_start,
+                   shared_start=shared_start)
+
+
 # --------------------------------------------------------------------------
 # prefill workloads (new tokens are written by reshape_and_cache, then attend
 # causally over the paged context)

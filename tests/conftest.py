@@ -19,3 +19,16 @@ def _oracle_built():
     if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
         oracle.build()
     yield
+
+
+@pytest.fixture
+def report(request):
+    """print() that reaches the terminal even while pytest captures output:
+    for figures a test is asked to report (error statistics, the fp8
+    quantisation effect)."""
+    capman = request.config.pluginmanager.getplugin("capturemanager")
+
+    def _report(msg: str) -> None:
+        with capman.global_and_fixture_disabled():
+            print(msg, flush=True)
+    return _report

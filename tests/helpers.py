@@ -7,6 +7,8 @@ is ever fed to the oracle.
 """
 from __future__ import annotations
 
+import ctypes as C
+
 import numpy as np
 import torch
 
@@ -75,6 +77,25 @@ class DeviceCase:
         else:
             ws = L.alloc_workspace(self.pool, w.num_seqs, w.num_q_heads, msl, partition_size)
         L.pa_decode(self.pool, out, self.q, self.bt, self.lens, msl, w.scale, partition_size, ws)
+        return out
+
+    def decode_grouped(self, groups=None, out=None, schedule: int = 0,
+                       dirty_workspace: bool = False) -> torch.Tensor:
+        """pa_decode_grouped of the step, with the host planner's grouping of
+        the workload's tables unless a grouping is given."""
+        w = self.w
+        out = self.out if out is None else out
+        if groups is None:
+            groups = L.pa_decode_group_plan(w.block_tables, w.seq_lens, w.block_size,
+                                            w.num_q_heads, w.num_kv_heads)
+        ws = None
+        if dirty_workspace:
+            n = int(L.load().pa_decode_grouped_workspace_size(
+                C.byref(self.pool.desc), w.num_seqs, w.num_q_heads, w.max_seq_len,
+                groups.num_groups, schedule))
+            ws = dirty_workspace_of(n)
+        L.pa_decode_grouped(self.pool, out, self.q, self.bt, self.lens, w.max_seq_len, w.scale,
+                            groups, schedule, ws)
         return out
 
     def prefill(self, out=None) -> torch.Tensor:

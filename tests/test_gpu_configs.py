@@ -52,7 +52,7 @@ def _quantisation_effect(w, r_stored):
 
 
 @pytest.mark.parametrize("name,make,parts", CONFIGS, ids=[c[0] for c in CONFIGS])
-def test_full_size_parity(name, make, parts):
+def test_full_size_parity(name, make, parts, report):
     say(f"config {name}: generating")
     w = make()
     say(f"config {name}: uploading + reshape_and_cache ({w.tok_slot.size} tokens)")
@@ -71,13 +71,16 @@ def test_full_size_parity(name, make, parts):
         say(f"config {name}: decode partition={part}")
         y = dc.decode(part).cpu().numpy()
         st = check_close(w, y, r, f"{name}/p{part}")
-        say(f"  every output: {st}")
+        report(f"\n  {name} p{part}, all {y.size} outputs: max_abs {st['max_abs']:.3g}, "
+               f"max_rel {st['max_rel']:.3g}, rms_ref {st['rms_ref']:.3g}")
     if w.kv_dtype != "f16":
         r16, qe = _quantisation_effect(w, r)
         y = dc.decode(parts[0]).cpu().numpy().astype(np.float64)
         qe["gpu_vs_binary16_max_abs"] = float(np.abs(y - r16).max())
-        say(f"  quantisation effect ({w.kv_dtype}): oracle on stored bytes vs oracle on the "
-            f"binary16 values {qe}")
+        report(f"\n  {name} quantisation effect ({w.kv_dtype}): oracle on the stored bytes vs "
+               f"oracle on the binary16 values before quantisation: max_abs {qe['max_abs']:.3g}, "
+               f"rms {qe['rms']:.3g} (rms of the output {qe['rms_ref']:.3g}); GPU vs the "
+               f"binary16 oracle: max_abs {qe['gpu_vs_binary16_max_abs']:.3g}")
 
 
 VARIANTS = [(name, make, parts[:1] + ([512] if name.startswith("long_") else []))
