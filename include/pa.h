@@ -193,27 +193,33 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
  *   (device int32 arrays, [num_seqs] and [num_groups + 1]); every sequence
  *   must be listed exactly once (a sequence left out gets no output row).  A
  *   group holds at most 16 / (num_q_heads / num_kv_heads) sequences (further
- *   members are ignored), whose first shared_tokens[i] positions (device
- *   int32 [num_groups], a multiple of 16, at most the shortest member's
- *   length; other values are rounded down and clamped) lie in the same
- *   physical blocks in every member's table.  The query heads of all members
- *   of a group form the columns of one matrix-core operand, so a shared tile
- *   is read once for the group; each member's own positions are read once
- *   for it.
- *   schedule: 0 library choice, 1 flat ranges over the groups' tiles (the
- *   default while 3 (num_groups + num_seqs) + 2 <= 16384; needs a workspace of
- *   pa_decode_grouped_workspace_size bytes), 2 one workgroup per (group, KV
- *   head) (no workspace).
+ *   members are ignored).  member_shared[p] (device int32 [num_seqs]) is the
+ *   number of leading positions the member at position p of members shares
+ *   with the member listed just before it in the same group: both tables
+ *   list the same physical blocks for those positions (whole 16-token tiles,
+ *   at most both lengths; other values are rounded down and clamped; the
+ *   entry of a group's first member is ignored).
+ *   The query heads of all members of a group form the columns of one
+ *   matrix-core operand; a tile that several consecutive members share is
+ *   read once and feeds all of their columns, so every distinct (position
+ *   range, physical block) of a group is read once.
+ *   schedule: 0 library choice, 1 flat ranges over the groups' tiles (needs
+ *   2 num_groups + 4 num_seqs + 2 <= 16384 and a workspace of
+ *   pa_decode_grouped_workspace_size bytes; chosen for fewer than 1024
+ *   (group, KV head) items), 2 one workgroup per (group, KV head) (no
+ *   workspace).
  * pa_decode_group_plan builds such a grouping on the host from host copies
  * of the tables.  Ids in members and member_start are clamped into their
  * arrays; nothing faults on bad contents, but outputs are then unspecified.
  * Pools with a sliding window are refused (PA_ERR_UNSUPPORTED).  Outputs are
- * bitwise reproducible for the same inputs, grouping and schedule. */
+ * bitwise reproducible for the same inputs, grouping and schedule, and for a
+ * given grouping they do not depend on which physical ids hold the blocks
+ * (the planner's member order does: it sorts by table rows). */
 int pa_decode_grouped(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs,
                       int32_t num_q_heads, const int32_t* block_tables,
                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
                       float scale, int32_t num_groups, const int32_t* members,
-                      const int32_t* member_start, const int32_t* shared_tokens,
+                      const int32_t* member_start, const int32_t* member_shared,
                       int32_t schedule, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
@@ -230,18 +236,20 @@ size_t pa_decode_grouped_workspace_size(const pa_kv_pool* pool, int32_t num_seqs
 
 /* Host planner for pa_decode_grouped.  block_tables [num_seqs,
  * max_blocks_per_seq] and seq_lens [num_seqs] are HOST int32 arrays; members
- * [num_seqs], member_start [num_seqs + 1] and shared_tokens [num_seqs] are
+ * [num_seqs], member_start [num_seqs + 1] and member_shared [num_seqs] are
  * host outputs.  Sequences whose first table entry names the same physical
- * block form a family; each family is cut, in order, into groups of at most
- * 16 / (num_q_heads / num_kv_heads) members whose shared length is the run
- * of leading table entries all members list, in whole 16-token tiles and
- * within every member's length (groups that would share nothing become one
- * group per sequence).  Groups are listed longest first.  Returns the number
- * of groups, or a negative pa_status. */
+ * block form a family; a family is sorted by its table rows, so that rows
+ * with long common prefixes are neighbours, and cut into groups: runs of at
+ * most 16 / (num_q_heads / num_kv_heads) consecutive members each of which
+ * shares at least one whole 16-token tile with the one before it.
+ * member_shared is that shared length (the common run of leading table
+ * entries, within both lengths, in whole tiles; 0 for a group's first
+ * member).  Groups are listed longest first.  Returns the number of groups,
+ * or a negative pa_status. */
 int32_t pa_decode_group_plan(const int32_t* block_tables, int32_t num_seqs,
                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
                              int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
-                             int32_t* members, int32_t* member_start, int32_t* shared_tokens);
+                             int32_t* members, int32_t* member_start, int32_t* member_shared);
 
 /* pa_decode for callers that cannot allocate device memory (code being
  * captured into a HIP graph, tight serving loops, harnesses that forbid

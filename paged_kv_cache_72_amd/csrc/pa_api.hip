@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -228,9 +229,12 @@ size_t workspace_bytes_for(const Plan& pl, int64_t S, int64_t Hq, int64_t Hkv, i
 
 // Grouped schedules: 1 flat ranges over the groups' units (per-group and
 // per-member tables in LDS, a workspace for the cut groups' records), 2 one
-// workgroup per (group, KV head) (no workspace, any batch size).
+// workgroup per (group, KV head) (no workspace, any batch size).  Measured on
+// the prefix-sharing batch (2,048 items): 124 us per group against 140 us
+// flat; on batches of few groups the flat ranges keep every CU busy.
 constexpr int32_t kGroupFlat = 1, kGroupPerGroup = 2;
 constexpr int64_t kGroupFlatMaxLdsInts = 16384;   // 64 KiB of group and member tables
+constexpr int64_t kGroupPerGroupMinItems = 1024;   // items from which one workgroup each pays
 
 struct GroupPlan {
   int32_t mode;
@@ -248,13 +252,16 @@ int group_plan(const pa_kv_pool* pool, int32_t S, int32_t Hq, int32_t max_seq_le
   if (G < 0 || G > S) return fail(PA_ERR_INVALID_ARG, "num_groups %d out of range [0, %d]", G, S);
   if (schedule < 0 || schedule > kGroupPerGroup)
     return fail(PA_ERR_INVALID_ARG, "grouped schedule %d invalid (0, 1 or 2)", schedule);
-  const int64_t lds_ints = 3 * (int64_t)G + 2 + 3 * (int64_t)S;
+  const int64_t lds_ints = 2 * (int64_t)G + 2 + 4 * (int64_t)S;
   const bool flat_fits = lds_ints <= kGroupFlatMaxLdsInts;
   if (schedule == kGroupFlat && !flat_fits)
-    return fail(PA_ERR_UNSUPPORTED, "the flat grouped schedule takes at most %lld groups + "
-                "sequences", (long long)(kGroupFlatMaxLdsInts / 3));
+    return fail(PA_ERR_UNSUPPORTED, "the flat grouped schedule needs 2 groups + 4 sequences + 2 "
+                "<= %lld", (long long)kGroupFlatMaxLdsInts);
   if ((int64_t)G * g->num_kv_heads > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "too many groups");
-  gp->mode = schedule ? schedule : (flat_fits ? kGroupFlat : kGroupPerGroup);
+  // enough (group, KV head) items to fill the GPU several times over: one
+  // workgroup each; fewer, larger groups: balanced flat ranges
+  const bool many_items = (int64_t)G * g->num_kv_heads >= kGroupPerGroupMinItems;
+  gp->mode = schedule ? schedule : (flat_fits && !many_items ? kGroupFlat : kGroupPerGroup);
   gp->ranges = 0;
   gp->workspace = 0;
   if (gp->mode == kGroupFlat) {
@@ -307,6 +314,7 @@ int decode_args(const pa::PoolGeom& g, void* out, const void* q, int32_t num_seq
 }
 
 int kv_code(const pa::PoolGeom& g) { return g.elem_bytes == 2 ? 0 : (g.fp8_e5m2 ? 2 : 1); }
+
 
 }  // namespace
 
@@ -408,20 +416,35 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
 int32_t pa_decode_group_plan(const int32_t* block_tables, int32_t num_seqs,
                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
                              int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
-                             int32_t* members, int32_t* member_start, int32_t* shared_tokens) {
+                             int32_t* members, int32_t* member_start, int32_t* member_shared) {
   if (num_seqs < 0 || max_blocks_per_seq < 1 || block_size < 1 || num_kv_heads < 1 ||
       num_q_heads < num_kv_heads || num_q_heads % num_kv_heads ||
       num_q_heads / num_kv_heads > 16)
     return fail(PA_ERR_INVALID_ARG, "bad sizes for the group plan");
-  if (num_seqs && (!block_tables || !seq_lens || !members || !member_start || !shared_tokens))
+  if (num_seqs && (!block_tables || !seq_lens || !members || !member_start || !member_shared))
     return fail(PA_ERR_INVALID_ARG, "group plan arrays must be non-NULL");
   const int32_t cap = 16 / (num_q_heads / num_kv_heads);
+  const int64_t mb = max_blocks_per_seq;
   auto len_of = [&](int32_t s) {
-    const int64_t n = seq_lens[s], m = (int64_t)max_blocks_per_seq * block_size;
+    const int64_t n = seq_lens[s], m = mb * block_size;
     return (int32_t)(n < 0 ? 0 : (n > m ? m : n));
   };
-  // families: sequences whose first block is the same physical block, in order
-  // of their first member; short contexts (no whole 16-token tile) stay alone
+  auto nblk = [&](int32_t s) { return (len_of(s) + block_size - 1) / block_size; };
+  auto row = [&](int32_t s) { return block_tables + (int64_t)s * mb; };
+  // positions shared by s and t: their common run of leading table entries,
+  // within both lengths, in whole 16-token tiles
+  auto shared = [&](int32_t s, int32_t t) {
+    const int32_t n = std::min(nblk(s), nblk(t));
+    const int32_t* a = row(s);
+    const int32_t* b = row(t);
+    int32_t k = 0;
+    while (k < n && a[k] == b[k]) ++k;
+    return (int32_t)(std::min((int64_t)k * block_size,
+                              (int64_t)std::min(len_of(s), len_of(t))) & ~15);
+  };
+  // families: sequences whose first block is the same physical block, in
+  // order of their first member; each family sorted by its table rows, so
+  // that rows with long common prefixes are neighbours
   std::vector<std::vector<int32_t>> fam;
   std::unordered_map<int32_t, size_t> by_first;
   for (int32_t s = 0; s < num_seqs; ++s) {
@@ -429,56 +452,52 @@ int32_t pa_decode_group_plan(const int32_t* block_tables, int32_t num_seqs,
       fam.push_back({s});
       continue;
     }
-    auto it = by_first.find(block_tables[(int64_t)s * max_blocks_per_seq]);
+    auto it = by_first.find(row(s)[0]);
     if (it == by_first.end()) {
-      by_first.emplace(block_tables[(int64_t)s * max_blocks_per_seq], fam.size());
+      by_first.emplace(row(s)[0], fam.size());
       fam.push_back({s});
     } else {
       fam[it->second].push_back(s);
     }
   }
-  // groups: runs of up to `cap` members of a family; shared = the leading
-  // blocks all of them list, in whole 16-token tiles, within every context
-  struct G { int32_t first, n, shared; int64_t work; };
+  struct G { int32_t first, n; int64_t work; };
   std::vector<G> groups;
-  std::vector<int32_t> order;
+  std::vector<int32_t> order, share;
   order.reserve((size_t)num_seqs);
-  for (const auto& f : fam) {
-    for (size_t i0 = 0; i0 < f.size(); i0 += (size_t)cap) {
-      const size_t i1 = std::min(f.size(), i0 + (size_t)cap);
-      int32_t min_len = INT32_MAX;
-      for (size_t i = i0; i < i1; ++i) min_len = std::min(min_len, len_of(f[i]));
-      int32_t lcp = (min_len + block_size - 1) / block_size;
-      const int32_t* r0 = block_tables + (int64_t)f[i0] * max_blocks_per_seq;
-      for (size_t i = i0 + 1; i < i1 && lcp > 0; ++i) {
-        const int32_t* ri = block_tables + (int64_t)f[i] * max_blocks_per_seq;
-        int32_t k = 0;
-        while (k < lcp && ri[k] == r0[k]) ++k;
-        lcp = k;
+  share.reserve((size_t)num_seqs);
+  for (auto& f : fam) {
+    std::stable_sort(f.begin(), f.end(), [&](int32_t s, int32_t t) {
+      return std::lexicographical_compare(row(s), row(s) + nblk(s), row(t), row(t) + nblk(t));
+    });
+    // chains of neighbours that share something, cut every `cap` members
+    for (size_t i = 0; i < f.size(); ++i) {
+      const int32_t sh = i ? shared(f[i - 1], f[i]) : 0;
+      if (sh == 0 || groups.empty() || groups.back().n == cap ||
+          order[(size_t)groups.back().first + groups.back().n - 1] != f[i - 1]) {
+        groups.push_back({(int32_t)order.size(), 0, 0});
+        share.push_back(0);
+      } else {
+        share.push_back(sh);
       }
-      int32_t shared = i1 - i0 > 1 ? std::min((int64_t)lcp * block_size, (int64_t)min_len) : 0;
-      shared &= ~15;
-      if (shared == 0 && i1 - i0 > 1) {       // nothing to share: one group per sequence
-        for (size_t i = i0; i < i1; ++i) {
-          groups.push_back({(int32_t)order.size(), 1, 0, (len_of(f[i]) + 15) / 16});
-          order.push_back(f[i]);
-        }
-        continue;
-      }
-      int64_t work = shared / 16;
-      for (size_t i = i0; i < i1; ++i) work += (len_of(f[i]) + 15) / 16 - shared / 16;
-      groups.push_back({(int32_t)order.size(), (int32_t)(i1 - i0), shared, work});
-      for (size_t i = i0; i < i1; ++i) order.push_back(f[i]);
+      G& gr = groups.back();
+      gr.work += (len_of(f[i]) + 15) / 16 - share.back() / 16;
+      ++gr.n;
+      order.push_back(f[i]);
     }
   }
   // the longest groups start first, so that the short ones fill in at the end
-  std::stable_sort(groups.begin(), groups.end(),
-                   [](const G& x, const G& y) { return x.work > y.work; });
+  std::vector<size_t> idx(groups.size());
+  for (size_t i = 0; i < idx.size(); ++i) idx[i] = i;
+  std::stable_sort(idx.begin(), idx.end(),
+                   [&](size_t x, size_t y) { return groups[x].work > groups[y].work; });
   int32_t pos = 0;
-  for (size_t i = 0; i < groups.size(); ++i) {
-    member_start[i] = pos;
-    shared_tokens[i] = groups[i].shared;
-    for (int32_t k = 0; k < groups[i].n; ++k) members[pos++] = order[(size_t)groups[i].first + k];
+  for (size_t k = 0; k < idx.size(); ++k) {
+    const G& gr = groups[idx[k]];
+    member_start[k] = pos;
+    for (int32_t m = 0; m < gr.n; ++m, ++pos) {
+      members[pos] = order[(size_t)gr.first + m];
+      member_shared[pos] = m ? share[(size_t)gr.first + m] : 0;
+    }
   }
   member_start[groups.size()] = pos;
   return (int32_t)groups.size();
@@ -506,7 +525,7 @@ int pa_decode_grouped(const pa_kv_pool* pool, void* out, const void* q, int32_t 
                       int32_t num_q_heads, const int32_t* block_tables,
                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
                       float scale, int32_t num_groups, const int32_t* members,
-                      const int32_t* member_start, const int32_t* shared_tokens,
+                      const int32_t* member_start, const int32_t* member_shared,
                       int32_t schedule, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
   pa::PoolGeom g;
@@ -514,8 +533,8 @@ int pa_decode_grouped(const pa_kv_pool* pool, void* out, const void* q, int32_t 
   int st = group_plan(pool, num_seqs, num_q_heads, max_seq_len, num_groups, schedule, &g, &gpl);
   if (st) return st;
   if (num_seqs == 0 || num_groups == 0) return PA_OK;
-  if (!members || !member_start || !shared_tokens)
-    return fail(PA_ERR_INVALID_ARG, "members, member_start and shared_tokens must be non-NULL");
+  if (!members || !member_start || !member_shared)
+    return fail(PA_ERR_INVALID_ARG, "members, member_start and member_shared must be non-NULL");
   pa::DecodeArgs a;
   st = decode_args(g, out, q, num_seqs, num_q_heads, block_tables, max_blocks_per_seq, seq_lens,
                    max_seq_len, scale, &a);
@@ -526,7 +545,7 @@ int pa_decode_grouped(const pa_kv_pool* pool, void* out, const void* q, int32_t 
                   gpl.workspace, workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(PA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   }
-  pa::GroupArgs gr{num_groups, num_seqs, num_seqs, members, member_start, shared_tokens};
+  pa::GroupArgs gr{num_groups, num_seqs, num_seqs, members, member_start, member_shared};
   pa::FlatArgs f{};
   if (gpl.mode == kGroupFlat) {
     f.num_seqs = num_seqs;

@@ -70,6 +70,9 @@ namespace {
 #ifndef PA_FLAT_WAVES_PER_EU
 #define PA_FLAT_WAVES_PER_EU 2
 #endif
+#ifndef PA_VMEM_TABLES
+#define PA_VMEM_TABLES 0      // block-table entries by vector loads (1) or scalar loads (0)
+#endif
 #ifndef PA_GROUP_WAVES_PER_EU
 #define PA_GROUP_WAVES_PER_EU 2
 #endif
@@ -115,8 +118,13 @@ __device__ __forceinline__ int win_start(int len, int window) {
 }
 
 // Byte bases, inside the pools, of a tile's two halves (equal when block_size >= 16).
+// live = 0 marks a tile past the end of what a wave computes: its loads are
+// still issued (the same instruction stream every iteration keeps the
+// compiler's wait counts tight) but through an empty buffer descriptor, so
+// they return zeros without touching memory.
 struct Ids {
   int64_t lo, hi;
+  int live;
 };
 
 // One (sequence, KV head) pair as the loads see it.
@@ -230,23 +238,31 @@ struct Engine {
 
   __device__ __forceinline__ int64_t phys(const PairRef& p, int lb) const {
     lb = lb < p.nblk - 1 ? lb : p.nblk - 1;      // never past the valid table entries
+#if PA_VMEM_TABLES
+    // a vector load (all lanes the same address): its wait counts with the
+    // K/V loads, so LDS accesses in between do not wait for it
+    const __amdgpu_buffer_rsrc_t R =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.bt, (short)0, p.nblk * 4, 0x00020000);
+    int id = uni((int)__builtin_amdgcn_raw_buffer_load_b32(R, lb * 4, 0, 0));
+#else
     int id = p.bt[lb];
+#endif
     id = id < 0 ? 0 : (id > nb_m1 ? nb_m1 : id);
     return (int64_t)id * block_stride + p.head_off;
   }
 
-  __device__ __forceinline__ Ids tile_ids(const PairRef& p, int j) const {
+  __device__ __forceinline__ Ids tile_ids(const PairRef& p, int j, bool live = true) const {
     if constexpr (BS >= 16) {
       const int t = j * 16;
       const int64_t b = phys(p, t / BS) + (int64_t)(t % BS) * rs;
-      return {b, b};
+      return {b, b, live};
     } else {
-      return {phys(p, 2 * j), phys(p, 2 * j + 1)};
+      return {phys(p, 2 * j), phys(p, 2 * j + 1), live};
     }
   }
 
-  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const char* p) const {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 16 * rs, 0x00020000);
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const char* p, int live) const {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, live ? 16 * rs : 0, 0x00020000);
   }
   __device__ __forceinline__ uint4 ld_k(__amdgpu_buffer_rsrc_t R, int soff) const {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R, koff, soff, CPOL));
@@ -266,7 +282,8 @@ struct Engine {
   }
 
   __device__ __forceinline__ void issue(const Ids& ids, uint4* kr, VT* vr) const {
-    const __amdgpu_buffer_rsrc_t klo = rsrc(kp + ids.lo), vlo = rsrc(vp + ids.lo);
+    const __amdgpu_buffer_rsrc_t klo = rsrc(kp + ids.lo, ids.live);
+    const __amdgpu_buffer_rsrc_t vlo = rsrc(vp + ids.lo, ids.live);
     // Key load u reads whole rows u*RPI .. u*RPI+RPI-1 of the tile (lane: row
     // t0, chunk ch), so each load instruction covers contiguous 256-B runs.
     if constexpr (BS >= 16) {
@@ -275,7 +292,8 @@ struct Engine {
 #pragma unroll
       for (int k = 0; k < 4; ++k) vr[k] = ld_v(vlo, k);
     } else {   // tokens 0-7 of the tile in block 2j, tokens 8-15 in block 2j+1
-      const __amdgpu_buffer_rsrc_t khi = rsrc(kp + ids.hi), vhi = rsrc(vp + ids.hi);
+      const __amdgpu_buffer_rsrc_t khi = rsrc(kp + ids.hi, ids.live);
+      const __amdgpu_buffer_rsrc_t vhi = rsrc(vp + ids.hi, ids.live);
 #pragma unroll
       for (int u = 0; u < NKL; ++u) {
         if constexpr (RPI <= 8) kr[u] = ld_k(u * RPI >= 8 ? khi : klo, ((u * RPI) & 7) * rs);
@@ -504,6 +522,89 @@ struct Engine {
   }
 };
 
+// ---------------------------------------------------------------- workgroup merge
+
+// The NW waves of a workgroup each hold softmax state (m, l, unnormalised
+// acc) for up to 16 rows; the workgroup's result per row is the log-sum-exp
+// merge of the waves' states.  The states go to LDS (acc as float4 rows);
+// one thread per row then forms the row's (M, L) and one weight per wave,
+// f_w = 2^(m_w - M) * v_scale / L, and every thread finishes four dims of a
+// row at a time as sum_w f_w * acc_w.  The per-row exponentials are formed
+// once per row instead of once per output element.
+template <int D, int NW>
+struct WgMergeLds {
+  float m[NW][16];
+  float l[NW][16];
+  float f[NW][16];
+  float2 ml[16];
+  float o[NW][16][D];
+};
+
+template <int D, int NW, int DCH>
+__device__ __forceinline__ void wg_merge_put(WgMergeLds<D, NW>& sm, int wid, int lane,
+                                             const float4_t* acc, float m_run, float l_tot,
+                                             int nrows) {
+  const int r = lane >> 4, c = lane & 15;
+  if (r == 0) {
+    sm.m[wid][c] = m_run;
+    sm.l[wid][c] = l_tot;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * r + i;
+    if (h < nrows) {
+#pragma unroll
+      for (int q = 0; q < DCH / 4; ++q)
+        *(float4*)&sm.o[wid][h][c * DCH + 4 * q] =
+            make_float4(acc[4 * q][i], acc[4 * q + 1][i], acc[4 * q + 2][i], acc[4 * q + 3][i]);
+    }
+  }
+}
+
+// After wg_merge_put by every wave and a barrier: calls put(h, d, o4, M, L)
+// for every row h < nrows and every fourth dim d, o4 = dims d .. d + 3 of the
+// merged, normalised row (times v_scale; zeros for an empty row).
+template <int D, int NW, class Put>
+__device__ __forceinline__ void wg_merge_finish(WgMergeLds<D, NW>& sm, int nrows, float v_scale,
+                                                const Put& put) {
+  if (threadIdx.x < 16) {
+    const int h = threadIdx.x;
+    float M = sm.m[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm.m[w][h]);
+    float e[NW], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      e[w] = exp2f(sm.m[w][h] - M);
+      L += e[w] * sm.l[w][h];
+    }
+    const float inv = L > 0.f ? v_scale / L : 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sm.f[w][h] = e[w] * inv;
+    sm.ml[h] = make_float2(M, L);
+  }
+  __syncthreads();
+  constexpr int Q = D / 4;
+  for (int idx = threadIdx.x; idx < nrows * Q; idx += NW * 64) {
+    const int h = idx / Q, d = (idx - (idx / Q) * Q) * 4;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = sm.f[w][h];
+      const float4 a = *(const float4*)&sm.o[w][h][d];
+      o.x += f * a.x;
+      o.y += f * a.y;
+      o.z += f * a.z;
+      o.w += f * a.w;
+    }
+    put(h, d, o, sm.ml[h].x, sm.ml[h].y);
+  }
+}
+
+__device__ __forceinline__ void store_half4(_Float16* dst, float4 o) {
+  *(half4_t*)dst = (half4_t){(_Float16)o.x, (_Float16)o.y, (_Float16)o.z, (_Float16)o.w};
+}
+
 // ---------------------------------------------------------------- single / split
 
 template <int D, int BS, int KV, int NW, bool SPLIT, bool NT>
@@ -559,24 +660,26 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
   }
 
   // The loads of tile j+NW and the block ids of tile j+2NW are in flight while
-  // tile j is computed; two register sets alternate.  Past the end of the
-  // range the next-tile loads repeat the range's last tile (cache-resident), so
-  // the wave always waits on exactly one tile of outstanding loads.
+  // tile j is computed; two register sets alternate.  Tiles past the wave's
+  // last one are dead (their loads fetch nothing).
   uint4 kA[En::NKL], kB[En::NKL];
   VT vA[4], vB[4];
   int j = j_begin + wid;
   if (j < j_end) {
     const int j_last = j_end - 1;
     en.issue(ids0, kA, vA);
-    Ids ids_b = j + NW <= j_last ? ids1 : ids0;  // past the end: repeat a loaded tile
+    Ids ids_b = ids1;
+    ids_b.live = j + NW <= j_last;
     for (;;) {
+      // the block ids two tiles ahead are read before the next tile's loads
+      // are issued, so waiting for them never waits for those loads
+      const Ids ids_a = en.tile_ids(pr, min(j + 2 * NW, j_last), j + 2 * NW <= j_last);
       en.issue(ids_b, kB, vB);
-      const Ids ids_a = en.tile_ids(pr, min(j + 2 * NW, j_last));
       en.compute(j, t_begin, t_end, kA, vA);
       j += NW;
       if (j >= j_end) break;
+      ids_b = en.tile_ids(pr, min(j + 2 * NW, j_last), j + 2 * NW <= j_last);
       en.issue(ids_a, kA, vA);
-      ids_b = en.tile_ids(pr, min(j + 2 * NW, j_last));
       en.compute(j, t_begin, t_end, kB, vB);
       j += NW;
       if (j >= j_end) break;
@@ -585,61 +688,35 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
   const float l_tot = en.l_total();
 
   // ---- merge the waves of the workgroup in LDS, then write
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
-  __shared__ float sm_o[NW][16][D];
-  const int r = lane >> 4, c = lane & 15;
-  if (r == 0) {
-    sm_m[wid][c] = en.m_run;
-    sm_l[wid][c] = l_tot;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * r + i;
-    if (h < g) {
-#pragma unroll
-      for (int e = 0; e < En::DCH; ++e) sm_o[wid][h][c * En::DCH + e] = en.acc[e][i];
-    }
-  }
+  __shared__ WgMergeLds<D, NW> sm;
+  wg_merge_put<D, NW, En::DCH>(sm, wid, lane, en.acc, en.m_run, l_tot, g);
   __syncthreads();
-
-  const int hq0 = kh * g;
-  for (int idx = threadIdx.x; idx < g * D; idx += NW * 64) {
-    const int h = idx / D, d = idx - (idx / D) * D;
-    float M = sm_m[0][h];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = exp2f(sm_m[w][h] - M);
-      L += f * sm_l[w][h];
-      O += f * sm_o[w][h][d];
-    }
-    const float o = L > 0.f ? (O / L) * v_scale : 0.f;
-    const int64_t row = (int64_t)s * a.num_q_heads + hq0 + h;
+  const int64_t row0 = (int64_t)s * a.num_q_heads + (int64_t)kh * g;
+  wg_merge_finish<D, NW>(sm, g, v_scale, [&](int h, int d, float4 o, float M, float L) {
     if constexpr (SPLIT) {
-      const int64_t prow = row * a.num_parts + part;
-      a.ws_o[prow * D + d] = o;
+      const int64_t prow = (row0 + h) * a.num_parts + part;
+      *(float4*)&a.ws_o[prow * D + d] = o;
       if (d == 0) a.ws_ml[prow] = make_float2(M, L);
     } else {
-      a.out[row * D + d] = (_Float16)o;
+      store_half4(a.out + (row0 + h) * D + d, o);
     }
-  }
+  });
 }
 
 // ---------------------------------------------------------------- grouped
 
 // One workgroup per (group, KV head).  A group is up to 16 / gqa sequences
-// whose first `shared` positions sit in the same physical blocks (forked
-// sequences, prefix-cache hits: "PagedAttention & vLLM", memory sharing).
-// Query column c is (member c / gqa, head c % gqa), so one 16x16 MFMA scores a
-// K tile for every member at once and each shared K/V tile leaves HBM once
-// per group instead of once per member.  Units: the shared tiles (every
-// member's columns take them), then each member's own tiles from `shared` on
-// (only its columns take them; the others' scores are masked).  The waves
-// take units round-robin, one tile in flight ahead of the one computed, and
-// merge in LDS.
+// listed in an order where each member shares its first positions with the
+// member before it: member i's table lists the same physical blocks as member
+// i - 1's for its first dep_i whole 16-token tiles (forks, prefix-cache hits:
+// "PagedAttention & vLLM", memory sharing).  Query column c is (member
+// c / gqa, head c % gqa), so one 16x16 MFMA scores a K tile for several
+// members at once.  Units: member i's tiles dep_i .. end_i - 1 (dep_0 = 0);
+// tile t of member i is also the tile t of members i + 1 .. j as long as
+// each of them shares more than t tiles with its predecessor, so the unit
+// feeds the columns of members i .. j and every distinct (tile, block) of
+// the group leaves HBM once.  The waves take units round-robin, one tile in
+// flight ahead of the one computed, and merge in LDS.
 template <int D, int BS, int KV, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : PA_GROUP_WAVES_PER_EU, 8)))
@@ -655,24 +732,23 @@ void decode_group_kernel(DecodeArgs a, GroupArgs gp, const int32_t* __restrict__
 
   // ---- members, clamped into the arrays (device contents are not validated),
   // read by the lanes of wave 0 in parallel: one member per lane
-  __shared__ int sm_seq[16], sm_len[16], sm_pre[17], sm_meta[2];
+  __shared__ int sm_seq[16], sm_len[16], sm_dep[16], sm_pre[17], sm_nm;
   if (wid == 0) {
     int m0 = gp.member_start[grp], m1 = gp.member_start[grp + 1];
     m0 = m0 < 0 ? 0 : (m0 > gp.num_members ? gp.num_members : m0);
     m1 = m1 < m0 ? m0 : (m1 > gp.num_members ? gp.num_members : m1);
     const int nm = m1 - m0 < 16 / g ? m1 - m0 : 16 / g;
-    int sq = 0, ln = INT32_MAX;
+    int sq = 0, ln = 0, sh = 0;
     if (lane < nm) {
       sq = gp.members[m0 + lane];
       sq = sq < 0 ? 0 : (sq >= gp.num_seqs ? gp.num_seqs - 1 : sq);
       ln = clamp_len(lens[sq], a.len_cap);
+      sh = gp.member_shared[m0 + lane];
     }
-    int mn = ln;                              // shortest member
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) mn = min(mn, __shfl_xor(mn, o));
-    int sh = gp.shared_tokens[grp];
-    sh = nm == 0 ? 0 : (sh < 0 ? 0 : (sh > mn ? mn : sh) & ~15);   // whole 16-token tiles
-    int x = lane < nm ? ((ln + 15) >> 4) - (sh >> 4) : 0;          // member's own tiles
+    const int prev = __shfl_up(ln, 1);        // the previous member's length
+    int dep = 0;                              // whole tiles shared with it
+    if (lane > 0 && lane < nm) dep = (sh < 0 ? 0 : min(sh, min(ln, prev))) >> 4;
+    int x = lane < nm ? ((ln + 15) >> 4) - dep : 0;   // the member's units
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) {        // inclusive scan over lanes 0..15
       const int y = __shfl_up(x, o);
@@ -681,18 +757,17 @@ void decode_group_kernel(DecodeArgs a, GroupArgs gp, const int32_t* __restrict__
     if (lane < nm) {
       sm_seq[lane] = sq;
       sm_len[lane] = ln;
+      sm_dep[lane] = dep;
     }
     if (lane < 16) sm_pre[lane + 1] = x;
     if (lane == 0) {
       sm_pre[0] = 0;
-      sm_meta[0] = nm;
-      sm_meta[1] = sh;
+      sm_nm = nm;
     }
   }
   __syncthreads();
-  const int nm = uni(sm_meta[0]), sh = uni(sm_meta[1]);
-  const int nsh = sh >> 4;                    // shared tiles
-  const int U = nsh + uni(sm_pre[nm]);        // units of the workgroup
+  const int nm = uni(sm_nm);
+  const int U = uni(sm_pre[nm]);              // units of the workgroup
   const int ncols = nm * g;
 
   __shared__ __attribute__((aligned(16))) char kstage[NW][En::KST];
@@ -710,29 +785,27 @@ void decode_group_kernel(DecodeArgs a, GroupArgs gp, const int32_t* __restrict__
   }
   en.reset();
 
-  // unit u -> member (-1: shared tile) and the tile's block ids
-  auto member_of = [&](int u) -> int {
-    if (u < nsh) return -1;
-    const int v = u - nsh;
+  // unit u -> (member i, tile t, last member j taking it)
+  struct Unit { int i, t, j; };
+  auto unit_of = [&](int u) -> Unit {
     int i = 0;
-    while (i + 1 < nm && sm_pre[i + 1] <= v) ++i;
-    return uni(i);
+    while (i + 1 < nm && sm_pre[i + 1] <= u) ++i;
+    i = uni(i);
+    const int t = uni(sm_dep[i]) + u - uni(sm_pre[i]);
+    int j = i;
+    while (j + 1 < nm && sm_dep[j + 1] > t) ++j;
+    return {i, t, uni(j)};
   };
   auto ids_of = [&](int u) -> Ids {
-    const int i = member_of(u);
-    const int m = i < 0 ? 0 : i;
-    const int ln = uni(sm_len[m]);
-    const PairRef p{tables + (int64_t)uni(sm_seq[m]) * a.max_blocks,
+    const Unit un = unit_of(u);
+    const int ln = uni(sm_len[un.i]);
+    const PairRef p{tables + (int64_t)uni(sm_seq[un.i]) * a.max_blocks,
                     ln > 0 ? (ln + BS - 1) / BS : 1, ln, head_off};
-    return en.tile_ids(p, i < 0 ? u : nsh + (u - nsh - uni(sm_pre[i])));
+    return en.tile_ids(p, un.t);
   };
   auto run = [&](int u, const uint4* kr, const VT* vr) {
-    const int i = member_of(u);
-    if (i < 0)
-      en.template compute<true>(u, 0, sh, kr, vr, 0, ncols);
-    else
-      en.template compute<true>(nsh + (u - nsh - uni(sm_pre[i])), 0, uni(sm_len[i]), kr, vr,
-                                i * g, i * g + g);
+    const Unit un = unit_of(u);
+    en.template compute<true>(un.t, 0, uni(sm_len[un.i]), kr, vr, un.i * g, (un.j + 1) * g);
   };
 
   uint4 kA[En::NKL], kB[En::NKL];
@@ -740,16 +813,21 @@ void decode_group_kernel(DecodeArgs a, GroupArgs gp, const int32_t* __restrict__
   int u = wid;
   if (u < U) {
     const int u_last = U - 1;
+    auto ids_ahead = [&](int v) {             // dead past the wave's last unit
+      Ids x = ids_of(min(v, u_last));
+      x.live = v <= u_last;
+      return x;
+    };
     en.issue(ids_of(u), kA, vA);
-    Ids ids_b = ids_of(min(u + NW, u_last));  // past the end: repeat a loaded tile
+    Ids ids_b = ids_ahead(u + NW);
     for (;;) {
+      const Ids ids_a = ids_ahead(u + 2 * NW);
       en.issue(ids_b, kB, vB);
-      const Ids ids_a = ids_of(min(u + 2 * NW, u_last));
       run(u, kA, vA);
       u += NW;
       if (u >= U) break;
+      ids_b = ids_ahead(u + 2 * NW);
       en.issue(ids_a, kA, vA);
-      ids_b = ids_of(min(u + 2 * NW, u_last));
       run(u, kB, vB);
       u += NW;
       if (u >= U) break;
@@ -758,39 +836,13 @@ void decode_group_kernel(DecodeArgs a, GroupArgs gp, const int32_t* __restrict__
   const float l_tot = en.l_total();
 
   // ---- merge the waves of the workgroup in LDS, then write every column
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
-  __shared__ float sm_o[NW][16][D];
-  const int r = lane >> 4, c = lane & 15;
-  if (r == 0) {
-    sm_m[wid][c] = en.m_run;
-    sm_l[wid][c] = l_tot;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * r + i;
-    if (h < ncols) {
-#pragma unroll
-      for (int e = 0; e < En::DCH; ++e) sm_o[wid][h][c * En::DCH + e] = en.acc[e][i];
-    }
-  }
+  __shared__ WgMergeLds<D, NW> sm;
+  wg_merge_put<D, NW, En::DCH>(sm, wid, lane, en.acc, en.m_run, l_tot, ncols);
   __syncthreads();
-  for (int idx = threadIdx.x; idx < ncols * D; idx += NW * 64) {
-    const int h = idx / D, d = idx - (idx / D) * D;
-    float M = sm_m[0][h];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = exp2f(sm_m[w][h] - M);
-      L += f * sm_l[w][h];
-      O += f * sm_o[w][h][d];
-    }
-    const float o = L > 0.f ? (O / L) * v_scale : 0.f;
+  wg_merge_finish<D, NW>(sm, ncols, v_scale, [&](int h, int d, float4 o, float, float) {
     const int64_t row = (int64_t)sm_seq[h / g] * a.num_q_heads + (int64_t)kh * g + h % g;
-    a.out[row * D + d] = (_Float16)o;
-  }
+    store_half4(a.out + row * D + d, o);
+  });
 }
 
 // One workgroup per (sequence, query head): merge the partitions by log-sum-exp.
@@ -954,8 +1006,8 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   if (g0 >= g1) return;
 
   // ---- cursors over (sequence, tile) units; all wave-uniform.  cur[0] is the
-  // unit being computed, cur[k] the k-th after it (clamped to the range's last
-  // unit, whose loads then repeat cache-resident data).
+  // unit being computed, cur[k] the k-th after it (clamped to the range's
+  // last unit; the loads of such a cursor are dead).
   auto ntiles = [&](int ss) { return uni(sm_pre[ss + 1] - sm_pre[ss]); };
   struct Cur { int s, j; };
   auto advance = [&](Cur c) -> Cur {           // the next unit (callers know one exists)
@@ -1025,7 +1077,7 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   };
 
   // ST register sets rotate: while unit gt is computed, units gt+1 .. gt+ST-1
-  // are in flight; the loads of a unit past the range repeat its last unit.
+  // are in flight.
   uint4 kb[ST][En::NKL];
   VT vb[ST][4];
 #pragma unroll
@@ -1034,9 +1086,12 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
       en.load_q_into(qpre, q_of(cur[k].s));
       q_seq = cur[k].s;
     }
-    en.issue(ids_of(cur[k]), kb[k], vb[k]);
+    Ids ik = ids_of(cur[k]);
+    ik.live = g0 + k < g1;
+    en.issue(ik, kb[k], vb[k]);
   }
   Ids ids_next = ids_of(cur[ST - 1]);
+  ids_next.live = g0 + ST - 1 < g1;
   for (;;) {
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
@@ -1044,8 +1099,15 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
         en.load_q_into(qpre, q_of(cur[ST - 1].s));
         q_seq = cur[ST - 1].s;
       }
-      en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST]);
-      ids_next = ids_of(cur[ST]);
+      {
+        // the block ids are read before the loads below are issued; the
+        // loads of a unit past the range are dead (a branch around the issue
+        // instead cost 8-13%: the waits after it then drain every load)
+        Ids ids_new = ids_of(cur[ST]);
+        ids_new.live = gt + ST < g1;
+        en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST]);
+        ids_next = ids_new;
+      }
       {
         const int len = uni(sm_len[cur[0].s]), w0 = win_start(len, a.window);
         en.compute(cur[0].j + (w0 >> 4), w0, len, kb[st], vb[st]);
@@ -1160,13 +1222,13 @@ __global__ __launch_bounds__(256) void flat_merge_rows_kernel(DecodeArgs a, Flat
 // ---------------------------------------------------------------- flat schedule over groups
 
 // The grouped schedule's work laid out as the flat schedule lays out
-// sequences: the units of each group (its shared tiles, then each member's own
-// tiles from the shared length on) are listed group after group and cut into
-// equal ranges, walked by one wave per KV head.  A group inside one range is
+// sequences: the units of each group (member i's tiles dep_i .. end_i - 1, as
+// in decode_group_kernel) are listed group after group and cut into equal
+// ranges, walked by one wave per KV head.  A group inside one range is
 // written directly; a group cut by range boundaries leaves one 16-column
 // partial record per range (slot 0: the range's first segment, slot 1: its
 // last), merged by flat_group_merge_kernel.  Query column c of a group is
-// (member c / gqa, head c % gqa), as in decode_group_kernel.
+// (member c / gqa, head c % gqa).
 template <int D, int BS, int KV, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : PA_FLAT_WAVES_PER_EU, 8)))
@@ -1182,10 +1244,10 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
   extern __shared__ int sm[];
   int* sm_pre = sm;                            // [G + 1] units before group i
   int* sm_ms = sm_pre + G + 1;                 // [G + 1] first member of group i
-  int* sm_nsh = sm_ms + G + 1;                 // [G] shared tiles of group i
-  int* sm_seq = sm_nsh + G;                    // [M] sequence of member p
+  int* sm_seq = sm_ms + G + 1;                 // [M] sequence of member p
   int* sm_len = sm_seq + M;                    // [M] its context length
-  int* sm_mpre = sm_len + M;                   // [M] own units of the members before p
+  int* sm_dep = sm_len + M;                    // [M] tiles it shares with member p - 1
+  int* sm_mpre = sm_dep + M;                   // [M] units of the members before p in its group
   const int lane = threadIdx.x & 63;
   const int wid = uni(threadIdx.x >> 6);
   constexpr int NTH = NW * 64;
@@ -1206,17 +1268,18 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
   for (int i = threadIdx.x; i < G; i += NTH) {
     const int m0 = sm_ms[i], m1 = sm_ms[i + 1] > m0 ? sm_ms[i + 1] : m0;
     const int nm = m1 - m0 < cap ? m1 - m0 : cap;
-    int mn = INT32_MAX;
-    for (int p = m0; p < m0 + nm; ++p) mn = sm_len[p] < mn ? sm_len[p] : mn;
-    int sh = gp.shared_tokens[i];
-    sh = nm == 0 ? 0 : (sh < 0 ? 0 : (sh > mn ? mn : sh) & ~15);
-    int own = 0;
+    int units = 0;
     for (int p = m0; p < m0 + nm; ++p) {
-      sm_mpre[p] = own;
-      own += ((sm_len[p] + 15) >> 4) - (sh >> 4);
+      int dep = 0;
+      if (p > m0) {
+        const int sh = gp.member_shared[p], lim = min(sm_len[p], sm_len[p - 1]);
+        dep = (sh < 0 ? 0 : min(sh, lim)) >> 4;
+      }
+      sm_dep[p] = dep;
+      sm_mpre[p] = units;
+      units += ((sm_len[p] + 15) >> 4) - dep;
     }
-    sm_nsh[i] = sh >> 4;
-    sm_pre[i + 1] = (sh >> 4) + own;
+    sm_pre[i + 1] = units;
   }
   __syncthreads();
   __shared__ int sm_wsum[NW];
@@ -1263,30 +1326,63 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
   const int g0 = (int)((int64_t)rg * T / NR), g1 = (int)((int64_t)(rg + 1) * T / NR);
   if (g0 >= g1) return;
 
+  // ---- cursors over (group, unit) pairs, all wave-uniform.  Besides the
+  // group s and the unit j, a cursor carries the member p whose tile t the
+  // unit is, that member's sequence and length, and the last member hi that
+  // takes the tile too, so stepping to the next unit reads LDS only for the
+  // sharing span and when the member or the group changes.
+  // nt caches the group's unit count and drop the tile from which the span
+  // hi shrinks (the smallest shared depth among members p + 1 .. hi), so the
+  // common step -- the member's next tile -- reads no LDS at all.
+  struct Cur { int s, j, p, t, seq, len, m0, nm, hi, drop, nt; };
   auto ntiles = [&](int gi) { return uni(sm_pre[gi + 1] - sm_pre[gi]); };
-  auto members = [&](int gi) {                 // (first member, member count)
-    const int m0 = uni(sm_ms[gi]), m1 = uni(sm_ms[gi + 1]);
-    const int n = m1 > m0 ? m1 - m0 : 0;
-    return make_int2(m0, n < cap ? n : cap);
+  auto set_span = [&](Cur& c) {               // drop: the smallest depth in the span
+    int q = c.p, mn = INT32_MAX;
+    while (q + 1 < c.m0 + c.nm && sm_dep[q + 1] > c.t) {
+      ++q;
+      mn = min(mn, (int)sm_dep[q]);
+    }
+    c.hi = uni(q);
+    c.drop = uni(mn);
   };
-  struct Cur { int s, j; };                    // s: group, j: unit within it
-  auto advance = [&](Cur c) -> Cur {
-    if (c.j + 1 < ntiles(c.s)) return {c.s, c.j + 1};
+  auto enter_member = [&](Cur c, int p) -> Cur {
+    c.p = p;
+    c.t = uni(sm_dep[p]);
+    c.seq = uni(sm_seq[p]);
+    c.len = uni(sm_len[p]);
+    set_span(c);
+    return c;
+  };
+  auto at_unit = [&](int gi, int j) -> Cur {   // unit j of group gi, from scratch
+    Cur c;
+    c.s = gi;
+    c.j = j;
+    c.nt = ntiles(gi);
+    c.m0 = uni(sm_ms[gi]);
+    const int m1 = uni(sm_ms[gi + 1]);
+    c.nm = m1 > c.m0 ? (m1 - c.m0 < cap ? m1 - c.m0 : cap) : 0;
+    int p = c.m0;
+    while (p + 1 < c.m0 + c.nm && sm_mpre[p + 1] <= j) ++p;
+    c = enter_member(c, uni(p));
+    c.t += j - uni(sm_mpre[c.p]);
+    set_span(c);
+    return c;
+  };
+  auto advance = [&](Cur c) -> Cur {           // the next unit (callers know one exists)
+    if (c.j + 1 < c.nt) {
+      ++c.j;
+      if (c.t + 1 < ((c.len + 15) >> 4)) {
+        ++c.t;
+        if (c.t >= c.drop) set_span(c);
+        return c;
+      }
+      int p = c.p + 1;                         // the next member with units of its own
+      while (((sm_len[p] + 15) >> 4) == sm_dep[p]) ++p;
+      return enter_member(c, uni(p));
+    }
     int ns = c.s;
     do { ++ns; } while (ntiles(ns) == 0);
-    return {uni(ns), 0};
-  };
-  // unit -> (member p, tile j); p = -1 for a shared tile (member m0's table)
-  struct Unit { int p, j; };
-  auto unit_of = [&](Cur c) -> Unit {
-    const int nsh = uni(sm_nsh[c.s]);
-    const int2 mm = members(c.s);
-    if (c.j < nsh) return {-1, c.j};
-    const int v = c.j - nsh;
-    int p = mm.x;
-    while (p + 1 < mm.x + mm.y && sm_mpre[p + 1] <= v) ++p;
-    p = uni(p);
-    return {p, nsh + v - uni(sm_mpre[p])};
+    return at_unit(uni(ns), 0);
   };
   int lo = 0, hi = G;                          // group with pre[i] <= g0 < pre[i+1]
   while (hi - lo > 1) {
@@ -1295,7 +1391,7 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
   }
   constexpr int ST = PA_FLAT_STAGES;
   Cur cur[ST + 1];
-  cur[0] = {uni(lo), uni(g0 - sm_pre[lo])};
+  cur[0] = at_unit(uni(lo), uni(g0 - sm_pre[lo]));
 #pragma unroll
   for (int k = 1; k <= ST; ++k) cur[k] = g0 + k < g1 ? advance(cur[k - 1]) : cur[k - 1];
 
@@ -1305,24 +1401,20 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
   if (a.k_hs) en.sc *= a.k_hs[kh];
   const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
   const int64_t head_off = (int64_t)kh * D * En::E;
-  auto ids_of = [&](Cur c) -> Ids {
-    const Unit un = unit_of(c);
-    const int p = un.p < 0 ? uni(sm_ms[c.s]) : un.p;
-    const int len = uni(sm_len[p]);
-    const PairRef pr{tables + (int64_t)uni(sm_seq[p]) * a.max_blocks,
-                     len > 0 ? (len + BS - 1) / BS : 1, len, head_off};
-    return en.tile_ids(pr, un.j);
+  auto ids_of = [&](const Cur& c) -> Ids {
+    const PairRef pr{tables + (int64_t)c.seq * a.max_blocks,
+                     c.len > 0 ? (c.len + BS - 1) / BS : 1, c.len, head_off};
+    return en.tile_ids(pr, c.t);
   };
-  // this lane's query row in group gi (column c = lane & 15), or nullptr
-  auto qrow_of = [&](int gi) -> const _Float16* {
-    const int2 mm = members(gi);
-    const int c = lane & 15;
-    if (c >= mm.y * g) return nullptr;
-    return qs + ((int64_t)sm_seq[mm.x + c / g] * a.num_q_heads + (int64_t)kh * g + c % g) * D;
+  // this lane's query row in a group (column lane & 15), or nullptr
+  auto qrow_of = [&](const Cur& c) -> const _Float16* {
+    const int col = lane & 15;
+    if (col >= c.nm * g) return nullptr;
+    return qs + ((int64_t)sm_seq[c.m0 + col / g] * a.num_q_heads + (int64_t)kh * g + col % g) * D;
   };
   float* rec_base = slots + (int64_t)gw * 2 * 16 * (D + 2);
 
-  en.load_q_rows(qrow_of(cur[0].s));
+  en.load_q_rows(qrow_of(cur[0]));
   en.reset();
   half4_t qpre[En::NQ];
   int q_grp = -1;
@@ -1331,23 +1423,23 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
   int gt = g0;
 
   auto finish = [&]() {
-    const bool grp_end = cur[0].j + 1 == ntiles(cur[0].s);
+    const bool grp_end = cur[0].j + 1 == cur[0].nt;
     if (!(grp_end || gt + 1 == g1)) return;
     const float lt = en.l_total();
-    const int2 mm = members(cur[0].s);
+    const int m0 = cur[0].m0, ncols = cur[0].nm * g;
     if (seg_from_start && grp_end) {
       en.store_out_cols(
           [&](int h) {
-            return outs + ((int64_t)sm_seq[mm.x + h / g] * a.num_q_heads + (int64_t)kh * g +
+            return outs + ((int64_t)sm_seq[m0 + h / g] * a.num_q_heads + (int64_t)kh * g +
                            h % g) * D;
           },
-          mm.y * g, lt, v_scale);
+          ncols, lt, v_scale);
     } else {
-      en.store_partial16(rec_base + (seg_start == g0 ? 0 : 1) * 16 * (D + 2), mm.y * g, lt,
+      en.store_partial16(rec_base + (seg_start == g0 ? 0 : 1) * 16 * (D + 2), ncols, lt,
                          v_scale);
     }
     if (gt + 1 < g1) {
-      if (q_grp == cur[1].s) en.take_q(qpre); else en.load_q_rows(qrow_of(cur[1].s));
+      if (q_grp == cur[1].s) en.take_q(qpre); else en.load_q_rows(qrow_of(cur[1]));
       q_grp = -1;
       en.reset();
       seg_from_start = true;
@@ -1360,28 +1452,35 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
 #pragma unroll
   for (int k = 0; k < ST - 1; ++k) {
     if (k > 0 && cur[k].j == 0 && g0 + k < g1 && q_grp < 0) {
-      en.load_q_rows_into(qpre, qrow_of(cur[k].s));
+      en.load_q_rows_into(qpre, qrow_of(cur[k]));
       q_grp = cur[k].s;
     }
-    en.issue(ids_of(cur[k]), kb[k], vb[k]);
+    Ids ik = ids_of(cur[k]);
+    ik.live = g0 + k < g1;
+    en.issue(ik, kb[k], vb[k]);
   }
   Ids ids_next = ids_of(cur[ST - 1]);
+  ids_next.live = g0 + ST - 1 < g1;
   for (;;) {
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
       if (cur[ST - 1].j == 0 && gt + ST - 1 < g1 && q_grp < 0) {
-        en.load_q_rows_into(qpre, qrow_of(cur[ST - 1].s));
+        en.load_q_rows_into(qpre, qrow_of(cur[ST - 1]));
         q_grp = cur[ST - 1].s;
       }
-      en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST]);
-      ids_next = ids_of(cur[ST]);
       {
-        const Unit un = unit_of(cur[0]);
-        const int2 mm = members(cur[0].s);
-        const int i = un.p - mm.x;             // the member whose columns take the tile
-        const int t_end = un.p < 0 ? uni(sm_nsh[cur[0].s]) * 16 : uni(sm_len[un.p]);
-        const int clo = un.p < 0 ? 0 : i * g, chi = un.p < 0 ? mm.y * g : i * g + g;
-        en.template compute<true>(un.j, 0, t_end, kb[st], vb[st], clo, chi);
+        // the block ids are read before the loads below are issued; the
+        // loads of a unit past the range are dead (a branch around the issue
+        // instead cost 8-13%: the waits after it then drain every load)
+        Ids ids_new = ids_of(cur[ST]);
+        ids_new.live = gt + ST < g1;
+        en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST]);
+        ids_next = ids_new;
+      }
+      {
+        const Cur& c = cur[0];                 // members p .. hi take the tile
+        en.template compute<true>(c.t, 0, c.len, kb[st], vb[st], (c.p - c.m0) * g,
+                                  (c.hi - c.m0 + 1) * g);
       }
       finish();
       if (++gt == g1) return;
@@ -1411,25 +1510,39 @@ __global__ __launch_bounds__(256) void flat_group_merge_kernel(DecodeArgs a, Fla
   m0 = m0 < 0 ? 0 : (m0 > gp.num_members ? gp.num_members : m0);
   m1 = m1 < m0 ? m0 : (m1 > gp.num_members ? gp.num_members : m1);
   const int ncols = (m1 - m0 < cap ? m1 - m0 : cap) * g;
-  for (int idx = threadIdx.x; idx < ncols * D; idx += 256) {
-    const int h = idx / D, d = idx - (idx / D) * D;
-    float M = kNegBig, L = 0.f, O = 0.f;
+  constexpr int Q = D / 4;
+  for (int idx = threadIdx.x; idx < ncols * Q; idx += 256) {
+    const int h = idx / Q, d = (idx - (idx / Q) * Q) * 4;
+    float M = kNegBig, L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    // records are loaded whether or not their range owns units (every slot
+    // lies inside the workspace); an empty range's record counts as empty,
+    // so the loads of several records can be in flight together
+#pragma unroll 4
     for (int r = r_first; r <= r_last; ++r) {
-      if (range_empty(r, T, NR)) continue;     // owns no unit: wrote no record this call
+      const bool empty = range_empty(r, T, NR);
       const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
       const float* p = f.slots + ((int64_t)(r * a.num_kv_heads + kh) * 2 + slot) * 16 * (D + 2);
-      const float2 ml = ((const float2*)(p + 16 * D))[h];
-      const float ov = p[h * D + d];
+      float2 ml = ((const float2*)(p + 16 * D))[h];
+      float4 ov = *(const float4*)(p + h * D + d);
+      if (empty) {
+        ml = make_float2(kNegBig, 0.f);
+        ov = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
       const float mn = fmaxf(M, ml.x);
       const float sa = __builtin_amdgcn_exp2f(M - mn), sb = ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
       L = L * sa + sb;
-      O = O * sa + sb * ov;
+      O.x = O.x * sa + sb * ov.x;
+      O.y = O.y * sa + sb * ov.y;
+      O.z = O.z * sa + sb * ov.z;
+      O.w = O.w * sa + sb * ov.w;
       M = mn;
     }
     int sq = gp.members[m0 + h / g];
     sq = sq < 0 ? 0 : (sq >= gp.num_seqs ? gp.num_seqs - 1 : sq);
-    a.out[((int64_t)sq * a.num_q_heads + (int64_t)kh * g + h % g) * D + d] =
-        (_Float16)(L > 0.f ? O / L : 0.f);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    store_half4(a.out + ((int64_t)sq * a.num_q_heads + (int64_t)kh * g + h % g) * D + d,
+                make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv));
   }
 }
 
@@ -1464,7 +1577,7 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, const GroupArgs*
     else
       hipLaunchKernelGGL((flat_merge_kernel<D, 8>), mgrid, dim3(8 * D), 0, stream, a, *f);
   } else if (mode == kModeFlatGroup) {
-    const size_t lds = sizeof(int) * (3 * (size_t)gr->num_groups + 2 + 3 * (size_t)gr->num_members);
+    const size_t lds = sizeof(int) * (2 * (size_t)gr->num_groups + 2 + 4 * (size_t)gr->num_members);
     const int64_t waves = (int64_t)f->num_ranges * a.num_kv_heads;
     constexpr int FW = PA_FLAT_WAVES;
     hipLaunchKernelGGL((decode_flat_group_kernel<D, BS, KV, FW, PA_GROUP_NT || NT>),

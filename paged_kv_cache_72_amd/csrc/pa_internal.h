@@ -65,16 +65,17 @@ struct FlatArgs {
   float* slots;               // [num_ranges * Hkv][2][gqa][head_dim + 2] partial records
 };
 
-// Grouped schedule: group i is the sequences members[member_start[i] ..
-// member_start[i + 1]), whose first shared_tokens[i] positions sit in the same
-// physical blocks (device arrays).
+// Grouped schedules: group i is the sequences members[member_start[i] ..
+// member_start[i + 1]); the member at position p shares its first
+// member_shared[p] positions (whole 16-token tiles) with the member before it
+// in its group (device arrays).
 struct GroupArgs {
   int32_t num_groups;
   int32_t num_seqs;
-  int32_t num_members;        // length of members
+  int32_t num_members;          // length of members and member_shared
   const int32_t* members;
   const int32_t* member_start;  // [num_groups + 1]
-  const int32_t* shared_tokens; // [num_groups]
+  const int32_t* member_shared; // [num_members]
 };
 
 enum { kModeSingle = 0, kModeSplit = 1, kModeFlat = 2, kModeGroup = 3, kModeFlatGroup = 4 };

@@ -286,12 +286,12 @@ class DecodeGroups:
     pa_decode_group_plan and their device copies."""
 
     def __init__(self, members: np.ndarray, member_start: np.ndarray,
-                 shared_tokens: np.ndarray, device="cuda"):
-        self.members, self.member_start, self.shared_tokens = members, member_start, shared_tokens
-        self.num_groups = int(shared_tokens.size)
+                 member_shared: np.ndarray, device="cuda"):
+        self.members, self.member_start, self.member_shared = members, member_start, member_shared
+        self.num_groups = int(member_start.size) - 1
         self.d_members = torch.from_numpy(members).to(device)
         self.d_member_start = torch.from_numpy(member_start).to(device)
-        self.d_shared_tokens = torch.from_numpy(shared_tokens).to(device)
+        self.d_member_shared = torch.from_numpy(member_shared).to(device)
 
 
 def pa_decode_group_plan(block_tables: np.ndarray, seq_lens: np.ndarray, block_size: int,
@@ -310,7 +310,7 @@ def pa_decode_group_plan(block_tables: np.ndarray, seq_lens: np.ndarray, block_s
                                     p(shared))
     if n < 0:
         raise PaError(n, pa_last_error())
-    return DecodeGroups(members[:S].copy(), start[:n + 1].copy(), shared[:n].copy(), device)
+    return DecodeGroups(members[:S].copy(), start[:n + 1].copy(), shared[:S].copy(), device)
 
 
 GROUPED_FLAT, GROUPED_PER_GROUP = 1, 2      # pa_decode_grouped schedules
@@ -361,7 +361,7 @@ def pa_decode_grouped(pool: KVPool, out: torch.Tensor, q: torch.Tensor,
         _dev(seq_lens, torch.int32, "seq_lens"), int(max_seq_len), C.c_float(scale),
         groups.num_groups, _dev(groups.d_members, torch.int32, "members"),
         _dev(groups.d_member_start, torch.int32, "member_start"),
-        _dev(groups.d_shared_tokens, torch.int32, "shared_tokens"), int(schedule), ws_ptr,
+        _dev(groups.d_member_shared, torch.int32, "member_shared"), int(schedule), ws_ptr,
         ws_bytes, _stream(stream)))
 
 

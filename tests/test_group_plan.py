@@ -17,8 +17,20 @@ def _plan(w):
                                   w.num_kv_heads, device="cpu")
 
 
+def _shared_brute(w, s, t):
+    """Positions s and t share: their common run of leading table entries,
+    within both lengths, in whole 16-token tiles."""
+    bs = w.block_size
+    ls, lt = int(w.seq_lens[s]), int(w.seq_lens[t])
+    n = min(-(-ls // bs), -(-lt // bs))
+    k = 0
+    while k < n and w.block_tables[s, k] == w.block_tables[t, k]:
+        k += 1
+    return min(k * bs, ls, lt) // 16 * 16
+
+
 def _check(w, gr):
-    S, bs = w.num_seqs, w.block_size
+    S = w.num_seqs
     cap = 16 // w.gqa
     assert sorted(gr.members.tolist()) == list(range(S))
     st = gr.member_start
@@ -26,20 +38,11 @@ def _check(w, gr):
     work = []
     for i in range(gr.num_groups):
         mem = gr.members[st[i]:st[i + 1]]
-        sh = int(gr.shared_tokens[i])
-        lens = w.seq_lens[mem].astype(np.int64)
-        assert sh % 16 == 0 and 0 <= sh <= lens.min()
-        if len(mem) > 1:
-            # brute force: leading entries common to every member, within every length
-            rows = w.block_tables[mem]
-            lcp = 0
-            nb_min = int(-(-lens.min() // bs))
-            while lcp < nb_min and np.all(rows[:, lcp] == rows[0, lcp]):
-                lcp += 1
-            assert sh == (min(lcp * bs, int(lens.min())) // 16) * 16 > 0
-        else:
-            assert sh == 0
-        work.append(sh // 16 + sum(int(-(-n // 16)) - sh // 16 for n in lens))
+        sh = gr.member_shared[st[i]:st[i + 1]]
+        assert sh[0] == 0
+        for k in range(1, len(mem)):
+            assert sh[k] == _shared_brute(w, mem[k - 1], mem[k]) > 0
+        work.append(sum(-(-int(w.seq_lens[m]) // 16) - int(x) // 16 for m, x in zip(mem, sh)))
     assert work == sorted(work, reverse=True)
     return work
 
@@ -58,19 +61,28 @@ def test_plan_on_the_prefix_sharing_workload(bs):
     w = W.prefix_share(bs)
     gr = _plan(w)
     _check(w, gr)
-    # 256 groups of 4; child 0 owns a copy of the last prompt block, so the
-    # four share the 240 tokens before it
+    # 256 groups of 4; child 0 owns a copy of the last prompt block: the
+    # other three share all 256 prompt tokens, child 0 the 240 before it, and
+    # sorting by table rows puts child 0 first or last
     assert gr.num_groups == 256 and np.all(np.diff(gr.member_start) == 4)
-    assert np.all(gr.shared_tokens == 240)
     for i in range(256):
-        assert sorted(gr.members[4 * i:4 * i + 4] // 4) == [gr.members[4 * i] // 4] * 4
+        mem = gr.members[4 * i:4 * i + 4]
+        assert sorted(mem // 4) == [mem[0] // 4] * 4
+        sh = gr.member_shared[4 * i:4 * i + 4].tolist()
+        assert sh in ([0, 240, 256, 256], [0, 256, 256, 240])
+        # every distinct (tile, block) of the group is read once
+        tiles = {(t, int(w.block_tables[m, t * 16 // bs])) for m in mem
+                 for t in range(-(-int(w.seq_lens[m]) // 16))}
+        if bs == 16:
+            assert sum(-(-int(w.seq_lens[m]) // 16) - x // 16 for m, x in zip(mem, sh)) == \
+                len(tiles)
 
 
 def test_plan_without_sharing_gives_singletons():
     w = W.llama3_8b_b64()
     gr = _plan(w)
     _check(w, gr)
-    assert gr.num_groups == w.num_seqs and np.all(gr.shared_tokens == 0)
+    assert gr.num_groups == w.num_seqs and np.all(gr.member_shared == 0)
 
 
 def test_plan_argument_checks():
@@ -80,7 +92,7 @@ def test_plan_argument_checks():
         with pytest.raises(L.PaError):
             L.pa_decode_group_plan(bt, lens, 16, hq, hkv, device="cpu")
     gr = L.pa_decode_group_plan(bt, lens, 16, 24, 8, device="cpu")
-    assert gr.num_groups == 2 and list(gr.shared_tokens) == [0, 0]
+    assert gr.num_groups == 2 and list(gr.member_shared) == [0, 0]
 
 
 def test_grouped_refuses_window_pools_on_the_host():
