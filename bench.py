@@ -208,8 +208,7 @@ def traffic_entry(config: str):
 
 
 DECODE_KERNELS = ("decode_flat_group_kernel", "flat_group_merge_kernel", "decode_flat_kernel",
-                  "flat_merge_rows_kernel", "flat_merge_kernel", "decode_group_kernel",
-                  "decode_kernel",
+                  "flat_merge_heads_kernel", "decode_group_kernel", "decode_kernel",
                   "lse_reduce_kernel")
 PREFILL_KERNELS = ("prefill_f16_kernel", "prefill_kernel")
 

@@ -48,8 +48,8 @@
 //                      the same per wave and the heads of a block are read
 //                      together.  Sequences inside one range are written
 //                      directly; a sequence cut by range boundaries leaves one
-//                      partial per range, merged by flat_merge_kernel in range
-//                      order (deterministic).
+//                      partial per range, merged by flat_merge_heads_kernel in
+//                      range order (deterministic).
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -933,7 +933,7 @@ __device__ __forceinline__ bool range_empty(int64_t r, int64_t T, int64_t NR) {
 // of a block are read together.  A sequence that lies inside one range is
 // written directly; one cut by range boundaries leaves a partial record per
 // range (slot 0: the range's first sequence, slot 1: its last), merged by
-// flat_merge_kernel.
+// flat_merge_heads_kernel.
 template <int D, int BS, int KV, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : PA_FLAT_WAVES_PER_EU, 8)))
@@ -1121,70 +1121,18 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   }
 }
 
-// One workgroup per (sequence, query head): if the sequence was cut by range
-// boundaries, merge its per-range records by log-sum-exp.  The NG thread
-// groups of the workgroup (head_dim threads each) take every NG-th record and
-// fold them online, loads of four records in flight; the groups' (M, L, O)
-// are then combined in LDS in group order, so the result is deterministic.
-// NG grows with the expected number of records per sequence.
-template <int D, int NG>
-__global__ __launch_bounds__(NG * D) void flat_merge_kernel(DecodeArgs a, FlatArgs f) {
-  const int row = blockIdx.x;
-  const int s = row / a.num_q_heads, h = row - s * a.num_q_heads;
-  const int g = a.gqa, kh = h / g, hl = h - kh * g;
-  const int64_t T = f.prefix[f.num_seqs];
-  const int pre = f.prefix[s], end = f.prefix[s + 1];
-  if (end == pre) return;
-  const int64_t NR = f.num_ranges;
-  const int r_first = range_of(pre, T, NR), r_last = range_of(end - 1, T, NR);
-  if (r_first == r_last) return;               // written by the decode kernel
-  const bool first_is_last_slot = (int64_t)r_first * T / NR < pre;
-  const int rec = g * (D + 2);
-  const int d = threadIdx.x % D, grp = threadIdx.x / D;
-  float M = kNegBig, L = 0.f, O = 0.f;
-#pragma unroll 4
-  for (int r = r_first + grp; r <= r_last; r += NG) {
-    if (range_empty(r, T, NR)) continue;       // owns no unit: wrote no record this call
-    const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
-    const float* p = f.slots + ((int64_t)(r * a.num_kv_heads + kh) * 2 + slot) * rec;
-    const float2 ml = ((const float2*)(p + g * D))[hl];
-    const float ov = p[hl * D + d];
-    const float mn = fmaxf(M, ml.x);
-    const float sa = __builtin_amdgcn_exp2f(M - mn), sb = ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
-    L = L * sa + sb;
-    O = O * sa + sb * ov;
-    M = mn;
-  }
-  __shared__ float sm_o[NG][D];
-  __shared__ float2 sm_ml[NG];
-  sm_o[grp][d] = O;
-  if (d == 0) sm_ml[grp] = make_float2(M, L);
-  __syncthreads();
-  if (grp == 0) {
-    float Mt = sm_ml[0].x;
-#pragma unroll
-    for (int q = 1; q < NG; ++q) Mt = fmaxf(Mt, sm_ml[q].x);
-    float Lt = 0.f, Ot = 0.f;
-#pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      const float w = __builtin_amdgcn_exp2f(sm_ml[q].x - Mt);
-      Lt += sm_ml[q].y * w;
-      Ot += sm_o[q][d] * w;
-    }
-    a.out[(int64_t)row * D + d] = (_Float16)(Lt > 0.f ? Ot / Lt : 0.f);
-  }
-}
-
-// One wave per (sequence, query head) row, four rows per workgroup: for the
-// usual few records per sequence.  The wave's lanes cover head_dim (D / 64
-// dims each) and fold the row's records online, in range order.
+// One workgroup per (sequence, KV head), for sequences cut by range
+// boundaries: the log-sum-exp merge of the sequence's records, all gqa rows at
+// once.  Thread t covers output float4 q = t mod F4 (F4 = gqa * D / 4) and
+// folds every K-th record from record t div F4 (K = the power of two that
+// fits the workgroup), so the records' loads are in flight together; the K
+// partial states of an output are then combined in LDS in a fixed order
+// (deterministic).  Records of ranges that own no unit hold an earlier call's
+// bytes and are replaced by an empty state by a select.
 template <int D>
-__global__ __launch_bounds__(256) void flat_merge_rows_kernel(DecodeArgs a, FlatArgs f) {
-  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-  if (row >= f.num_seqs * a.num_q_heads) return;
-  const int lane = threadIdx.x & 63;
-  const int s = row / a.num_q_heads, h = row - s * a.num_q_heads;
-  const int g = a.gqa, kh = h / g, hl = h - kh * g;
+__global__ __launch_bounds__(1024) void flat_merge_heads_kernel(DecodeArgs a, FlatArgs f) {
+  const int Hkv = a.num_kv_heads;
+  const int s = blockIdx.x / Hkv, kh = blockIdx.x - s * Hkv;
   const int64_t T = f.prefix[f.num_seqs];
   const int pre = f.prefix[s], end = f.prefix[s + 1];
   if (end == pre) return;
@@ -1192,31 +1140,56 @@ __global__ __launch_bounds__(256) void flat_merge_rows_kernel(DecodeArgs a, Flat
   const int r_first = range_of(pre, T, NR), r_last = range_of(end - 1, T, NR);
   if (r_first == r_last) return;               // written by the decode kernel
   const bool first_is_last_slot = (int64_t)r_first * T / NR < pre;
-  const int rec = g * (D + 2);
-  constexpr int DPL = D / 64;
-  float M = kNegBig, L = 0.f, O[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) O[e] = 0.f;
-#pragma unroll 4
-  for (int r = r_first; r <= r_last; ++r) {
-    if (range_empty(r, T, NR)) continue;       // owns no unit: wrote no record this call
-    const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
-    const float* p = f.slots + ((int64_t)(r * a.num_kv_heads + kh) * 2 + slot) * rec;
-    const float2 ml = ((const float2*)(p + g * D))[hl];
-    float ov[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) ov[e] = p[hl * D + lane * DPL + e];
-    const float mn = fmaxf(M, ml.x);
-    const float sa = __builtin_amdgcn_exp2f(M - mn), sb = ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
-    L = L * sa + sb;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) O[e] = O[e] * sa + sb * ov[e];
-    M = mn;
+  const int g = a.gqa, F4 = g * D / 4;
+  const int64_t rec = (int64_t)g * (D + 2);
+  int K = 1;
+  while (2 * K * F4 <= (int)blockDim.x) K *= 2;
+  const int t = threadIdx.x, k = t / F4, q = t - k * F4, h = 4 * q / D;
+  float M = kNegBig, L = 0.f;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (k < K) {
+#pragma unroll 8
+    for (int r = r_first + k; r <= r_last; r += K) {
+      const bool empty = range_empty(r, T, NR);
+      const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
+      const float* p = f.slots + ((int64_t)(r * Hkv + kh) * 2 + slot) * rec;
+      const float2 ml0 = ((const float2*)(p + g * D))[h];
+      const float4 ov0 = ((const float4*)p)[q];
+      const float2 ml = empty ? make_float2(kNegBig, 0.f) : ml0;
+      const float4 ov = empty ? make_float4(0.f, 0.f, 0.f, 0.f) : ov0;
+      const float mn = fmaxf(M, ml.x);
+      const float sa = __builtin_amdgcn_exp2f(M - mn), sb = ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
+      L = L * sa + sb;
+      O.x = O.x * sa + sb * ov.x;
+      O.y = O.y * sa + sb * ov.y;
+      O.z = O.z * sa + sb * ov.z;
+      O.w = O.w * sa + sb * ov.w;
+      M = mn;
+    }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e)
-    a.out[(int64_t)row * D + lane * DPL + e] = (_Float16)(O[e] * inv);
+  __shared__ float4 sm_o[1024];
+  __shared__ float2 sm_ml[1024];
+  sm_o[t] = O;
+  sm_ml[t] = make_float2(M, L);
+  __syncthreads();
+  if (k != 0) return;
+  float Mt = sm_ml[q].x;
+  for (int j = 1; j < K; ++j) Mt = fmaxf(Mt, sm_ml[j * F4 + q].x);
+  float Lt = 0.f;
+  float4 Ot = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < K; ++j) {
+    const float2 ml = sm_ml[j * F4 + q];
+    const float4 o = sm_o[j * F4 + q];
+    const float w = __builtin_amdgcn_exp2f(ml.x - Mt);
+    Lt += ml.y * w;
+    Ot.x += o.x * w;
+    Ot.y += o.y * w;
+    Ot.z += o.z * w;
+    Ot.w += o.w * w;
+  }
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  store_half4(a.out + ((int64_t)s * a.num_q_heads + (int64_t)kh * g) * D + 4 * q,
+              make_float4(Ot.x * inv, Ot.y * inv, Ot.z * inv, Ot.w * inv));
 }
 
 // ---------------------------------------------------------------- flat schedule over groups
@@ -1564,18 +1537,14 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, const GroupArgs*
                        f->prefix);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // records per sequence ~ ranges / sequences: about 8 per thread group
-    const int64_t per_seq = num_seqs > 0 ? f->num_ranges / num_seqs : 0;
-    const dim3 mgrid((uint32_t)num_seqs * (uint32_t)a.num_q_heads);
-    if (per_seq < 16)       // one wave per row (measured 0.7-0.9 us faster than a group per row)
-      hipLaunchKernelGGL((flat_merge_rows_kernel<D>), dim3((mgrid.x + 3) / 4), dim3(256), 0, stream,
-                         a, *f);
-    else if (per_seq < 32)
-      hipLaunchKernelGGL((flat_merge_kernel<D, 2>), mgrid, dim3(2 * D), 0, stream, a, *f);
-    else if (per_seq < 64)
-      hipLaunchKernelGGL((flat_merge_kernel<D, 4>), mgrid, dim3(4 * D), 0, stream, a, *f);
-    else
-      hipLaunchKernelGGL((flat_merge_kernel<D, 8>), mgrid, dim3(8 * D), 0, stream, a, *f);
+    // records per cut sequence ~ ranges / sequences + 1: a power of two of
+    // thread sets, each the gqa * D / 4 threads of one (sequence, KV head)
+    const int f4 = a.gqa * D / 4;
+    const int64_t per_seq = (num_seqs > 0 ? f->num_ranges / num_seqs : 0) + 2;
+    int sets = 1;
+    while (sets < per_seq && 2 * sets * f4 <= 1024) sets *= 2;
+    hipLaunchKernelGGL((flat_merge_heads_kernel<D>), dim3((uint32_t)num_seqs * a.num_kv_heads),
+                       dim3((sets * f4 + 63) / 64 * 64), 0, stream, a, *f);
   } else if (mode == kModeFlatGroup) {
     const size_t lds = sizeof(int) * (2 * (size_t)gr->num_groups + 2 + 4 * (size_t)gr->num_members);
     const int64_t waves = (int64_t)f->num_ranges * a.num_kv_heads;

@@ -40,7 +40,7 @@ def _write(path, counter, rows):
 def test_ingest_counters_scales_by_the_copy(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
     dec = "void pa::(anonymous namespace)::decode_flat_kernel<128, 16, 0, 4, true>(...)"
-    mer = "void pa::(anonymous namespace)::flat_merge_rows_kernel<128>(...)"
+    mer = "void pa::(anonymous namespace)::flat_merge_heads_kernel<128>(...)"
     copy = "__amd_rocclr_copyBuffer"
     # two calls of decode + merge; the 1 GiB copy reads half its bytes in
     # FETCH_SIZE and all of them in WRITE_SIZE
@@ -55,7 +55,7 @@ def test_ingest_counters_scales_by_the_copy(tmp_path, monkeypatch):
     assert e["write"]["bytes_per_call"] == int(52.0 * 1024)
     assert e["bytes_per_launch"] == e["fetch"]["bytes_per_call"] + e["write"]["bytes_per_call"]
     assert e["fetch"]["kib_raw_by_kernel"] == {"decode_flat_kernel": 1001.0,
-                                               "flat_merge_rows_kernel": 11.0}
+                                               "flat_merge_heads_kernel": 11.0}
     stored = json.load(open(tmp_path / "traffic.json"))
     assert stored["llama3_8b_b64"]["kernel_source_hash"] == bench.kernel_source_hash()
     assert stored["llama3_8b_b64"]["commands"] == ["cmd1", "cmd2"]
