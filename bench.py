@@ -223,14 +223,22 @@ def ingest_counters(fetch_csv: str, write_csv: str, calib_gib: float, config: st
     import csv
     from paged_kv_cache_72_amd import workloads as W
     kernels = PREFILL_KERNELS if config in W.PREFILL_CONFIGS else DECODE_KERNELS
-    # the kernels that run once per call (the rest, merges and reduces, run after them)
-    primary = ("prefill_f16_kernel", "prefill_kernel", "decode_flat_group_kernel",
-               "decode_flat_kernel", "decode_group_kernel", "decode_kernel")
+    # the kernel that runs once per call of the measured path, and the kernels
+    # that follow it within the call; the first listed one present is the
+    # path (a grouped workload's run also times the plain pa_decode, whose
+    # decode_kernel is then left out)
+    paths = (("prefill_f16_kernel", ()), ("prefill_kernel", ()),
+             ("decode_flat_group_kernel", ("flat_group_merge_kernel",)),
+             ("decode_flat_kernel", ("flat_merge_heads_kernel",)),
+             ("decode_group_kernel", ()), ("decode_kernel", ("lse_reduce_kernel",)))
 
     def load(path):
         rows = list(csv.DictReader(open(path)))
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         return rows
+
+    def kernel_of(r):
+        return next((k for k in kernels if k in r["Kernel_Name"]), None)
 
     out = {}
     for key, path in (("fetch", fetch_csv), ("write", write_csv)):
@@ -238,12 +246,13 @@ def ingest_counters(fetch_csv: str, write_csv: str, calib_gib: float, config: st
         copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]][-3:]
         kib_copy = sum(float(r["Counter_Value"]) for r in copies) / len(copies)
         factor = calib_gib * (1 << 30) / (kib_copy * 1024)
-        dec = [r for r in rows if any(k in r["Kernel_Name"] for k in kernels)]
-        calls = sum(1 for r in dec if any(p in r["Kernel_Name"] for p in primary))
+        present = {kernel_of(r) for r in rows}
+        primary, followers = next((p, f) for p, f in paths if p in present)
+        dec = [r for r in rows if kernel_of(r) in (primary,) + followers]
+        calls = sum(1 for r in dec if kernel_of(r) == primary)
         per_kernel = {}
         for r in dec:
-            name = next(k for k in kernels if k in r["Kernel_Name"])
-            per_kernel.setdefault(name, []).append(float(r["Counter_Value"]))
+            per_kernel.setdefault(kernel_of(r), []).append(float(r["Counter_Value"]))
         kib_per_call = sum(sum(v) for v in per_kernel.values()) / calls
         out[key] = {"counter": rows[0]["Counter_Name"], "kib_per_call_raw": round(kib_per_call, 2),
                     "copy_kib_raw": round(kib_copy, 2), "factor": round(factor, 5),

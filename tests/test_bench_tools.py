@@ -61,6 +61,24 @@ def test_ingest_counters_scales_by_the_copy(tmp_path, monkeypatch):
     assert stored["llama3_8b_b64"]["commands"] == ["cmd1", "cmd2"]
 
 
+def test_ingest_counters_takes_the_grouped_path_only(tmp_path, monkeypatch):
+    """A grouped workload's run also times the plain pa_decode on the same
+    step: its decode_kernel dispatches are not part of the grouped call."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    grp = "void pa::(anonymous namespace)::decode_group_kernel<128, 16, 0, 4, true>(...)"
+    plain = "void pa::(anonymous namespace)::decode_kernel<128, 16, 0, 4, false, false>(...)"
+    copy = "__amd_rocclr_copyBuffer"
+    _write(tmp_path / "f.csv", "FETCH_SIZE", [(grp, 300.0), (plain, 900.0), (grp, 302.0),
+                                              (plain, 900.0)] + [(copy, 524288.0)] * 3)
+    _write(tmp_path / "w.csv", "WRITE_SIZE", [(grp, 8.0), (plain, 8.0), (grp, 8.0),
+                                              (plain, 8.0)] + [(copy, 1048576.0)] * 3)
+    e = bench.ingest_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 1.0,
+                              "prefix_share_bs16", [])
+    assert e["fetch"]["kib_raw_by_kernel"] == {"decode_group_kernel": 301.0}
+    assert e["fetch"]["bytes_per_call"] == int(301.0 * 1024 * 2.0)
+    assert e["write"]["bytes_per_call"] == int(8.0 * 1024)
+
+
 def test_warm_up_runs_exactly_the_requested_steps():
     seen = []
     assert bench.warm_up(seen.append, 3) == 3
