@@ -37,6 +37,11 @@
  *   - Device contents are not validated.  Indices that would leave a buffer are
  *     made harmless instead (see each function), so a bad table cannot fault
  *     the GPU, but the affected outputs are then unspecified.
+ *   - With PA_LOG set (to anything but "0") in the environment when the
+ *     library is first used, pa_reshape_and_cache, pa_copy_blocks, pa_decode,
+ *     pa_decode_grouped and pa_prefill print one line each to stderr ("[pa] "
+ *     then the entry point, its shapes, the schedule chosen and the launch
+ *     size), including calls with nothing to do.
  */
 #ifndef PA_H
 #define PA_H

@@ -6,6 +6,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <algorithm>
 #include <mutex>
 #include <string>
@@ -18,6 +20,32 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Dispatch log: with PA_LOG set (and not "0") in the environment, read once,
+// every call that launches work prints one line to stderr naming its
+// schedule and launch shape.
+bool log_on() {
+  static const bool on = [] {
+    const char* e = std::getenv("PA_LOG");
+    return e && e[0] && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void log_line(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void log_line(const char* fmt, ...) {
+  if (!log_on()) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[pa] %s\n", buf);
+}
+
+const char* kv_name(int dtype) {
+  return dtype == PA_KV_F16 ? "f16" : (dtype == PA_KV_FP8_E4M3FN ? "fp8_e4m3fn" : "fp8_e5m2");
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -329,6 +357,9 @@ int pa_reshape_and_cache(const pa_kv_pool* pool, const void* k_new, const void* 
   if (st) return st;
   if (num_tokens < 0 || num_tokens > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "num_tokens %lld out of range", (long long)num_tokens);
+  log_line("pa_reshape_and_cache: %lld tokens, %s pool of %lld blocks x %d slots, %d kv heads, "
+           "head_dim %d", (long long)num_tokens, kv_name(pool->dtype), (long long)g.num_blocks,
+           g.block_size, g.num_kv_heads, g.head_dim);
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping)
     return fail(PA_ERR_INVALID_ARG, "k_new, v_new and slot_mapping must be non-NULL");
@@ -348,6 +379,8 @@ int pa_copy_blocks(const pa_kv_pool* pool, const int64_t* block_mapping, int64_t
   if (st) return st;
   if (num_pairs < 0 || num_pairs > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "num_pairs %lld out of range", (long long)num_pairs);
+  log_line("pa_copy_blocks: %lld pairs (K and V blocks of %lld bytes each)", (long long)num_pairs,
+           (long long)(g.row_stride * (int64_t)g.block_size));
   if (num_pairs == 0) return PA_OK;
   if (!block_mapping) return fail(PA_ERR_INVALID_ARG, "block_mapping is NULL");
   if (hipError_t e = pa::launch_copy_blocks(g, block_mapping, num_pairs, stream))
@@ -380,6 +413,24 @@ int pa_decode(const pa_kv_pool* pool, void* out, const void* q, int32_t num_seqs
   Plan pl;
   int st = plan(pool, num_seqs, num_q_heads, max_seq_len, partition_size, &g, &pl);
   if (st) return st;
+  if (log_on()) {
+    const int64_t units = (int64_t)num_seqs * g.num_kv_heads;
+    if (pl.mode == pa::kModeFlat)
+      log_line("pa_decode: %d seqs, %d/%d heads, head_dim %d, bs %d, %s, max_seq_len %d: flat, "
+               "%lld ranges x %d kv heads = %lld waves, then the merge of cut sequences",
+               num_seqs, num_q_heads, g.num_kv_heads, g.head_dim, g.block_size,
+               kv_name(pool->dtype), max_seq_len, (long long)pl.waves, g.num_kv_heads,
+               (long long)(pl.waves * g.num_kv_heads));
+    else if (pl.mode == pa::kModeSplit)
+      log_line("pa_decode: %d seqs, %d/%d heads, head_dim %d, bs %d, %s, max_seq_len %d: split, "
+               "%d-token partitions, %lld workgroups, then the log-sum-exp reduce", num_seqs,
+               num_q_heads, g.num_kv_heads, g.head_dim, g.block_size, kv_name(pool->dtype),
+               max_seq_len, pl.part, (long long)(units * pl.num_parts));
+    else
+      log_line("pa_decode: %d seqs, %d/%d heads, head_dim %d, bs %d, %s, max_seq_len %d: single "
+               "pass, %lld workgroups", num_seqs, num_q_heads, g.num_kv_heads, g.head_dim,
+               g.block_size, kv_name(pool->dtype), max_seq_len, (long long)units);
+  }
   if (num_seqs == 0) return PA_OK;
   pa::DecodeArgs a;
   st = decode_args(g, out, q, num_seqs, num_q_heads, block_tables, max_blocks_per_seq, seq_lens,
@@ -532,6 +583,16 @@ int pa_decode_grouped(const pa_kv_pool* pool, void* out, const void* q, int32_t 
   GroupPlan gpl;
   int st = group_plan(pool, num_seqs, num_q_heads, max_seq_len, num_groups, schedule, &g, &gpl);
   if (st) return st;
+  if (gpl.mode == kGroupFlat)
+    log_line("pa_decode_grouped: %d seqs in %d groups, %d/%d heads, head_dim %d, %s: flat over "
+             "groups, %lld ranges x %d kv heads, then the merge of cut groups", num_seqs,
+             num_groups, num_q_heads, g.num_kv_heads, g.head_dim, kv_name(pool->dtype),
+             (long long)gpl.ranges, g.num_kv_heads);
+  else
+    log_line("pa_decode_grouped: %d seqs in %d groups, %d/%d heads, head_dim %d, %s: one "
+             "workgroup per (group, kv head), %lld workgroups", num_seqs, num_groups,
+             num_q_heads, g.num_kv_heads, g.head_dim, kv_name(pool->dtype),
+             (long long)num_groups * g.num_kv_heads);
   if (num_seqs == 0 || num_groups == 0) return PA_OK;
   if (!members || !member_start || !member_shared)
     return fail(PA_ERR_INVALID_ARG, "members, member_start and member_shared must be non-NULL");
@@ -592,6 +653,10 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
   if ((int64_t)num_seqs * g.num_kv_heads * num_qt > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "num_seqs * num_kv_heads * cdiv(max_q_len, %d) too large",
                 tile);
+  log_line("pa_prefill: %d seqs, %d new tokens (at most %d per sequence), %d/%d heads, "
+           "head_dim %d, %s: %d new tokens per workgroup, %lld workgroups", num_seqs, total_q,
+           max_q_len, num_q_heads, g.num_kv_heads, g.head_dim, kv_name(pool->dtype), tile,
+           (long long)num_seqs * g.num_kv_heads * num_qt);
 
   pa::PrefillArgs a{};
   a.k = g.k;
