@@ -31,6 +31,7 @@ class OrcPool(C.Structure):
         ("k_scale", C.c_double), ("v_scale", C.c_double),
         ("k_head_scales", C.c_void_p), ("v_head_scales", C.c_void_p),
         ("sliding_window", C.c_int32),
+        ("k_block_scales", C.c_void_p), ("v_block_scales", C.c_void_p),
     ]
 
 
@@ -134,7 +135,7 @@ class HostPool:
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
                  kv_dtype: str = "f16", k_scale: float = 1.0, v_scale: float = 1.0,
                  fill_bits: int = 0, k_head_scales=None, v_head_scales=None,
-                 sliding_window: int = 0):
+                 sliding_window: int = 0, block_scales: bool = False):
         self.elem_bytes = 1 if kv_dtype in ("fp8_e4m3fn", "fp8_e5m2") else 2
         fp8_format = 1 if kv_dtype == "fp8_e5m2" else 0
         dt = np.uint8 if self.elem_bytes == 1 else np.uint16
@@ -152,18 +153,27 @@ class HostPool:
             self.k_head = np.ascontiguousarray(np.asarray(k_head_scales, np.float32), np.float64)
             self.v_head = np.ascontiguousarray(np.asarray(v_head_scales, np.float32), np.float64)
             assert self.k_head.shape == (num_kv_heads,) == self.v_head.shape
+        # per-(block, KV head) scales (fp8 only): float32 [num_blocks, Hkv], kept
+        # beside the pools and updated by scatter, zero before the first write
+        self.k_blk = self.v_blk = None
+        if block_scales:
+            assert self.elem_bytes == 1 and k_head_scales is None
+            self.k_blk = np.zeros((num_blocks, num_kv_heads), np.float32)
+            self.v_blk = np.zeros((num_blocks, num_kv_heads), np.float32)
         self.desc = OrcPool(self.k.ctypes.data, self.v.ctypes.data, num_blocks, 0, block_size,
                             num_kv_heads, head_dim, self.elem_bytes, fp8_format,
                             float(k_scale), float(v_scale),
                             None if self.k_head is None else self.k_head.ctypes.data,
                             None if self.v_head is None else self.v_head.ctypes.data,
-                            int(sliding_window))
+                            int(sliding_window),
+                            None if self.k_blk is None else self.k_blk.ctypes.data,
+                            None if self.v_blk is None else self.v_blk.ctypes.data)
 
     @classmethod
     def for_workload(cls, w, fill_bits: int = 0) -> "HostPool":
         return cls(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype,
                    w.k_scale, w.v_scale, fill_bits, w.k_head_scales, w.v_head_scales,
-                   w.window)
+                   w.window, w.block_scales)
 
 
 def scatter(pool: HostPool, k_new: np.ndarray, v_new: np.ndarray, slots: np.ndarray,
@@ -256,6 +266,17 @@ def pool_for_workload(w, fill_bits: int = 0, token_idx: Optional[np.ndarray] = N
     """Host pool holding the workload's context (or the given token subset)
     written by the oracle's own scatter; COW copies applied after the write."""
     p = HostPool.for_workload(w, fill_bits)
+    if w.block_scales:
+        # the scales depend on how the writes are grouped: the calls the
+        # device makes, in its order (the context, the fork's copies, the step)
+        assert token_idx is None, "per-block scales need every write"
+        old = np.ones(w.tok_slot.size, bool)
+        old[w.new_idx] = False
+        scatter(p, w.tok_k, w.tok_v, np.where(old, w.tok_slot, -1), nthreads)
+        if w.cow_pairs is not None:
+            copy_blocks(p, w.cow_pairs)
+        scatter(p, w.tok_k[w.new_idx], w.tok_v[w.new_idx], w.tok_slot[w.new_idx], nthreads)
+        return p
     if token_idx is None:
         scatter(p, w.tok_k, w.tok_v, w.tok_slot, nthreads)
     else:

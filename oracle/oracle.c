@@ -8,6 +8,7 @@
  */
 #include "oracle.h"
 
+#include <float.h>
 #include <math.h>
 #include <omp.h>
 #include <stdlib.h>
@@ -193,9 +194,78 @@ static double v_scale_of(const orc_pool* p, int32_t kh) {
 
 /* ---------------------------------------------------------------- writes */
 
+static int slot_ok(const orc_pool* p, int64_t slot) {
+  return slot >= 0 && slot < p->num_blocks * p->block_size;
+}
+
+/* Per-block scales: runs of consecutive tokens in one block, taken one after
+ * another (the rule is spelled out in oracle.h). */
+static void scatter_per_block(const orc_pool* p, const uint16_t* k_new, const uint16_t* v_new,
+                              const int64_t* slots, int64_t T) {
+  const int32_t Hkv = p->num_kv_heads, D = p->head_dim, bs = p->block_size;
+  const int e5m2 = p->fp8_format == ORC_FP8_E5M2;
+  const float fmax_fmt = e5m2 ? 57344.0f : 448.0f;
+  char* written = (char*)malloc((size_t)bs);
+  int64_t i = 0;
+  while (i < T) {
+    if (!slot_ok(p, slots[i])) {
+      ++i;
+      continue;
+    }
+    const int64_t blk = slots[i] / bs;
+    int64_t j = i + 1;
+    while (j < T && slot_ok(p, slots[j]) && slots[j] / bs == blk) ++j;
+    memset(written, 0, (size_t)bs);
+    for (int64_t t = i; t < j; ++t) written[slots[t] % bs] = 1;
+    const int fresh = written[0];
+    for (int which = 0; which < 2; ++which) {
+      uint8_t* pool = (uint8_t*)(which ? p->v : p->k);
+      const uint16_t* src = which ? v_new : k_new;
+      float* scales = which ? p->v_block_scales : p->k_block_scales;
+      for (int32_t kh = 0; kh < Hkv; ++kh) {
+        float amax = 0.0f;
+        for (int64_t t = i; t < j; ++t)
+          for (int32_t d = 0; d < D; ++d) {
+            const float x = (float)orc_f16_value(src[(t * Hkv + kh) * D + d]);
+            if (isfinite(x)) amax = fmaxf(amax, fabsf(x));
+          }
+        const float c = fmaxf(amax / fmax_fmt, FLT_MIN);
+        const float old = scales[blk * Hkv + kh];
+        const float nw = fresh ? c : fmaxf(old, c);
+        if (!fresh && nw > old) {
+          for (int32_t o = 0; o < bs; ++o) {
+            if (written[o]) continue;
+            for (int32_t d = 0; d < D; ++d) {
+              uint8_t* b = pool + elem_offset(p, blk, o, kh, d);
+              const float v = (float)(e5m2 ? orc_e5m2_value(*b) : orc_e4m3fn_value(*b));
+              const float y = (v * old) / nw;
+              *b = e5m2 ? orc_e5m2_encode(y) : orc_e4m3fn_encode(y);
+            }
+          }
+        }
+        for (int64_t t = i; t < j; ++t) {
+          const int32_t off = (int32_t)(slots[t] % bs);
+          for (int32_t d = 0; d < D; ++d) {
+            const float x = (float)orc_f16_value(src[(t * Hkv + kh) * D + d]);
+            pool[elem_offset(p, blk, off, kh, d)] =
+                e5m2 ? orc_e5m2_encode(x / nw) : orc_e4m3fn_encode(x / nw);
+          }
+        }
+        scales[blk * Hkv + kh] = nw;
+      }
+    }
+    i = j;
+  }
+  free(written);
+}
+
 void orc_scatter(const orc_pool* p, const uint16_t* k_new, const uint16_t* v_new,
                  const int64_t* slots, int64_t T, int nthreads) {
   const int32_t Hkv = p->num_kv_heads, D = p->head_dim;
+  if (p->elem_bytes == 1 && p->k_block_scales) {
+    scatter_per_block(p, k_new, v_new, slots, T);
+    return;
+  }
 #pragma omp parallel for schedule(static) num_threads(nthreads_or_default(nthreads))
   for (int64_t i = 0; i < T; ++i) {
     int64_t slot = slots[i];
@@ -235,6 +305,11 @@ void orc_copy_blocks(const orc_pool* p, const int64_t* pairs, int64_t n) {
     if (src < 0 || src >= p->num_blocks || dst < 0 || dst >= p->num_blocks) continue;
     memmove((uint8_t*)p->k + dst * stride, (const uint8_t*)p->k + src * stride, (size_t)bytes);
     memmove((uint8_t*)p->v + dst * stride, (const uint8_t*)p->v + src * stride, (size_t)bytes);
+    if (p->k_block_scales) {
+      const int32_t H = p->num_kv_heads;
+      memmove(p->k_block_scales + dst * H, p->k_block_scales + src * H, (size_t)H * sizeof(float));
+      memmove(p->v_block_scales + dst * H, p->v_block_scales + src * H, (size_t)H * sizeof(float));
+    }
   }
 }
 
@@ -246,10 +321,17 @@ void orc_gather_head(const orc_pool* p, const int32_t* bt_row, int32_t len, int3
   for (int32_t t = 0; t < len; ++t) {
     int64_t blk = bt_row[t / p->block_size];
     int32_t off = t % p->block_size;
+    /* the row's dequantisation scales: per block when the pool keeps them */
+    const double ks = p->k_block_scales && p->elem_bytes == 1
+                          ? (double)p->k_block_scales[blk * p->num_kv_heads + kh]
+                          : k_scale_of(p, kh);
+    const double vs = p->v_block_scales && p->elem_bytes == 1
+                          ? (double)p->v_block_scales[blk * p->num_kv_heads + kh]
+                          : v_scale_of(p, kh);
     for (int32_t d = 0; d < D; ++d) {
       int64_t o = elem_offset(p, blk, off, kh, d);
-      Kc[(int64_t)t * D + d] = read_elem(p, p->k, o, k_scale_of(p, kh));
-      Vc[(int64_t)t * D + d] = read_elem(p, p->v, o, v_scale_of(p, kh));
+      Kc[(int64_t)t * D + d] = read_elem(p, p->k, o, ks);
+      Vc[(int64_t)t * D + d] = read_elem(p, p->v, o, vs);
     }
   }
 }

@@ -23,8 +23,9 @@
  *     ("vLLM intro part 2", section 3.2 slot_mapping); fp8 pools store
  *     e4m3fn(x / scale) or e5m2(x / scale) (quantise on write, "KV Cache memory
  *     core", section 4.4; the two fp8 formats of "vLLM intro part 2", section 7).
- *     The scale is one per tensor, or one per KV head (the finer granularity
- *     the quantisation passage of "KV Cache memory core", section 4.4, names).
+ *     The scale is one per tensor, one per KV head, or one per (block, KV
+ *     head) kept beside the block (the finer granularities the quantisation
+ *     passage of "KV Cache memory core", section 4.4, names).
  *   - copy_blocks copies a whole block for copy-on-write ("GPU memory & KV
  *     cache", COW incident code; "vLLM intro part 2", section 5).
  *   - A sliding-window layer lets a query see only the last sliding_window
@@ -66,6 +67,12 @@ typedef struct {
   /* Sliding-window attention: > 0 limits a query at position p to positions
    * p - sliding_window + 1 .. p (0: every earlier position).                  */
   int32_t sliding_window;
+  /* Optional per-block grain (fp8 pools): [num_blocks][num_kv_heads] float32
+   * scales for K and for V, kept beside the pools; orc_scatter updates them
+   * and orc_copy_blocks copies them (see orc_scatter).  When non-NULL they
+   * replace the per-tensor and per-head scales.                               */
+  float*  k_block_scales;
+  float*  v_block_scales;
 } orc_pool;
 
 #define ORC_FP8_E4M3FN 0
@@ -90,12 +97,24 @@ void orc_e5m2_encode_n(const float* x, int64_t n, uint8_t* out);
 
 /* Write T tokens: k_new/v_new are [T, Hkv, D] binary16 bit patterns; a slot
  * below 0 (padding) or at or beyond num_blocks * block_size skips the token.  fp8 pools receive enc(float(x) / float(scale)) with the
- * pool's fp8 encoder. */
+ * pool's fp8 encoder.
+ * Per-block scales (quantise on write, with the scale kept beside the block,
+ * "KV Cache memory core", section 4.4): the tokens are taken in runs, a run
+ * being the consecutive entries of slots that lie in one block.  For each KV
+ * head, and for K and V separately, with a = the largest finite |x| of the
+ * run and m = the format's largest finite value (448, 57344), in fp32:
+ *   c   = max(a / m, smallest normal fp32)
+ *   new = c if the run writes the block's slot 0, else max(old, c)
+ * If the run does not write slot 0 and new > old, every slot of the block the
+ * run does not write is re-encoded: byte -> enc((value(byte) * old) / new).
+ * The run's values are stored as enc(x / new) and new becomes the block's
+ * scale.  Runs are taken in order, one after another. */
 void orc_scatter(const orc_pool* p, const uint16_t* k_new, const uint16_t* v_new,
                  const int64_t* slots, int64_t T, int nthreads);
 
 /* Copy whole blocks: pairs is [n, 2] of (src, dst), applied in order; a pair
- * naming a block outside [0, num_blocks) is skipped. */
+ * naming a block outside [0, num_blocks) is skipped.  Per-block scales are
+ * copied with their block. */
 void orc_copy_blocks(const orc_pool* p, const int64_t* pairs, int64_t n);
 
 /* Gather KV head kh of a sequence into contiguous fp64 rows Kc/Vc [len, D]. */

@@ -94,6 +94,9 @@ class Workload:
     v_head_scales: Optional[np.ndarray] = None
     # sliding-window layer: a query at position p sees positions p - window + 1 .. p
     window: int = 0
+    # fp8 pools with one scale per (block, KV head), kept beside the pools and
+    # written by reshape_and_cache (k_scale / v_scale are then unused)
+    block_scales: bool = False
 
     @property
     def is_prefill(self) -> bool:
@@ -245,7 +248,20 @@ def _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, lens, tables, p
         mult = (2.0 ** np.arange(Hkv) % 7 + 0.25).astype(np.float32)[None, :, None]
         tok_k = (tok_k.astype(np.float32) * mult).astype(np.float16)
         tok_v = (tok_v.astype(np.float32) * mult[:, ::-1]).astype(np.float16)
-    k_scale, v_scale, k_head, v_head = fp8_scales(kv_dtype, tok_k, tok_v, scale_grain)
+    if scale_grain == "block":
+        # blocks of different magnitude (2^-3 .. 2^3 by physical id), and this
+        # step's writes four times larger, so that appending to a block raises
+        # its scale and re-encodes the rows already there
+        e = ((tok_slot // bs) * 5 % 7 - 3).astype(np.float32)
+        mult = (2.0 ** e)[:, None, None].astype(np.float32)
+        mult[np.asarray(new_idx, np.int64)] *= 4.0
+        tok_k = (tok_k.astype(np.float32) * mult).astype(np.float16)
+        tok_v = (tok_v.astype(np.float32) * mult[:, :, ::-1]).astype(np.float16)
+        extra["block_scales"] = True
+        k_scale = v_scale = 1.0
+        k_head = v_head = None
+    else:
+        k_scale, v_scale, k_head, v_head = fp8_scales(kv_dtype, tok_k, tok_v, scale_grain)
     extra.setdefault("k_head_scales", k_head)
     extra.setdefault("v_head_scales", v_head)
     used = np.unique(tok_slot // bs).astype(np.int32)
