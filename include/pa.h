@@ -118,6 +118,20 @@ typedef struct {
    * aligned; when set, k_scale and v_scale are ignored. */
   const float* k_head_scales;
   const float* v_head_scales;
+  /* Optional per-block fp8 scale grain: device arrays of num_blocks *
+   * num_kv_heads float32 scales, [block][KV head], for K and for V, kept
+   * beside the pools ("KV Cache memory core", section 4.4: scale granularity
+   * finer than per tensor; quantised KV stays managed per block with its
+   * scale metadata).  The library reads AND writes them:
+   * pa_reshape_and_cache sets a block's scales as it writes the block (see
+   * there), pa_copy_blocks copies them with the block, and every decode and
+   * prefill call dequantises a row with its block's scale.  Both NULL or both
+   * set, fp8 pools only, not together with k_head_scales / v_head_scales,
+   * num_kv_heads <= 512, 4-byte aligned; when set, k_scale and v_scale are
+   * ignored.  A block's scales are defined once its slot 0 has been
+   * written. */
+  float* k_block_scales;
+  float* v_block_scales;
 } pa_kv_pool;
 
 /* Write num_tokens new tokens into their slots (the write side of slot_mapping,
@@ -131,7 +145,21 @@ typedef struct {
  * f16 pools receive the bits unchanged.  fp8 pools receive
  * enc(float(x) / scale), rounded to nearest even and saturated to the
  * format's largest finite value (448 for e4m3fn, 57344 for e5m2; infinities
- * saturate too), NaN stays NaN.  num_tokens == 0 is a no-op. */
+ * saturate too), NaN stays NaN.  num_tokens == 0 is a no-op.
+ * With per-block scales the tokens are taken in runs -- consecutive entries
+ * of slot_mapping that lie in one block -- and every block a call writes
+ * must be written by one run (a decode step appends one token per block; a
+ * prefill writes each block's new positions consecutively); blocks written
+ * by two runs of one call are a race.  For each run, KV head, and K and V
+ * separately, in fp32, with a = the largest finite |x| of the run and m = the
+ * format's largest finite value:
+ *   c = max(a / m, smallest normal fp32);
+ *   new = c when the run writes the block's slot 0 (a block starts over),
+ *   else max(old, c);
+ *   if the run does not write slot 0 and new > old, every slot of the block
+ *   the run does not write is re-encoded, byte -> enc((value(byte) * old) / new);
+ *   the run's values are stored as enc(x / new) and new becomes the scale.
+ * Values are never saturated by a scale that is too small. */
 int pa_reshape_and_cache(const pa_kv_pool* pool, const void* k_new, const void* v_new,
                          const int64_t* slot_mapping, int64_t num_tokens, hipStream_t stream);
 

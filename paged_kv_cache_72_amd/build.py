@@ -62,7 +62,7 @@ def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
         base = os.path.basename(src)
         # the decode kernels compile as one object per (head_dim, KV format) slice
         slices = ([(f"{base}.d{d}k{kv}", [f"-DPA_DECODE_SLICE_D={d}", f"-DPA_DECODE_SLICE_KV={kv}"])
-                   for d in (64, 128, 256) for kv in (0, 1, 2)]
+                   for d in (64, 128, 256) for kv in (0, 1, 2, 3, 4)]
                   if base == "pa_decode.hip" else [(base, [])])
         for name, defs in slices:
             obj = os.path.join(OBJ_DIR, f"{name}.{tag}.o")

@@ -107,6 +107,19 @@ int check_pool(const pa_kv_pool* p, PoolGeom* g) {
     if (((uintptr_t)p->k_head_scales & 3u) || ((uintptr_t)p->v_head_scales & 3u))
       return fail(PA_ERR_ALIGNMENT, "per-head scale arrays must be 4-byte aligned");
   }
+  if ((p->k_block_scales == nullptr) != (p->v_block_scales == nullptr))
+    return fail(PA_ERR_INVALID_ARG,
+                "k_block_scales and v_block_scales must be both set or both NULL");
+  if (p->k_block_scales) {
+    if (p->dtype == PA_KV_F16)
+      return fail(PA_ERR_INVALID_ARG, "per-block scales are for fp8 pools only");
+    if (p->k_head_scales)
+      return fail(PA_ERR_INVALID_ARG, "per-block and per-head scales cannot be combined");
+    if (p->num_kv_heads > 512)
+      return fail(PA_ERR_UNSUPPORTED, "per-block scales support at most 512 KV heads");
+    if (((uintptr_t)p->k_block_scales & 3u) || ((uintptr_t)p->v_block_scales & 3u))
+      return fail(PA_ERR_ALIGNMENT, "per-block scale arrays must be 4-byte aligned");
+  }
   g->k = (char*)p->k_base;
   g->v = (char*)p->v_base;
   g->num_blocks = p->num_blocks;
@@ -123,7 +136,9 @@ int check_pool(const pa_kv_pool* p, PoolGeom* g) {
   g->window = p->sliding_window;
   g->k_hs = p->k_head_scales;
   g->v_hs = p->v_head_scales;
-  if (g->k_hs) g->k_scale = g->v_scale = 1.f;
+  g->k_bs = p->k_block_scales;
+  g->v_bs = p->v_block_scales;
+  if (g->k_hs || g->k_bs) g->k_scale = g->v_scale = 1.f;
   return PA_OK;
 }
 
@@ -133,9 +148,9 @@ hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, const GroupArgs
 #define PA_DK(D, KV)                                                                        \
   if (head_dim == D && kv == KV)                                                            \
     return launch_decode_dk<D, KV>(a, f, gr, num_seqs, block_size, stream_kv, mode, stream);
-  PA_DK(128, 0) PA_DK(128, 1) PA_DK(128, 2)
-  PA_DK(64, 0) PA_DK(64, 1) PA_DK(64, 2)
-  PA_DK(256, 0) PA_DK(256, 1) PA_DK(256, 2)
+  PA_DK(128, 0) PA_DK(128, 1) PA_DK(128, 2) PA_DK(128, 3) PA_DK(128, 4)
+  PA_DK(64, 0) PA_DK(64, 1) PA_DK(64, 2) PA_DK(64, 3) PA_DK(64, 4)
+  PA_DK(256, 0) PA_DK(256, 1) PA_DK(256, 2) PA_DK(256, 3) PA_DK(256, 4)
 #undef PA_DK
   return hipErrorInvalidValue;
 }
@@ -337,11 +352,15 @@ int decode_args(const pa::PoolGeom& g, void* out, const void* q, int32_t num_seq
   a.k_hs = g.k_hs;
   a.v_hs = g.v_hs;
   a.window = g.window;
+  a.k_bs = g.k_bs;
+  a.v_bs = g.v_bs;
   (void)num_seqs;
   return PA_OK;
 }
 
-int kv_code(const pa::PoolGeom& g) { return g.elem_bytes == 2 ? 0 : (g.fp8_e5m2 ? 2 : 1); }
+int kv_code(const pa::PoolGeom& g) {
+  return g.elem_bytes == 2 ? 0 : (g.fp8_e5m2 ? 2 : 1) + (g.k_bs ? 2 : 0);
+}
 
 
 }  // namespace
@@ -638,6 +657,7 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
                 num_q_heads, g.num_kv_heads);
   const int32_t gqa = num_q_heads / g.num_kv_heads;
   if (gqa > 16) return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d > 16", gqa);
+  if (g.k_bs) return fail(PA_ERR_UNSUPPORTED, "pa_prefill does not read per-block scales");
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !q_start || !block_tables || !seq_lens)
     return fail(PA_ERR_INVALID_ARG,

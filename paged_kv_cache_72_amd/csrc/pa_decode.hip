@@ -125,6 +125,7 @@ __device__ __forceinline__ int win_start(int len, int window) {
 struct Ids {
   int64_t lo, hi;
   int live;
+  float ks0, ks1, vs0, vs1;   // per-block scales of the two halves (formats 3, 4)
 };
 
 // One (sequence, KV head) pair as the loads see it.
@@ -139,11 +140,16 @@ struct PairRef {
 // pools whose blocks each belong to one sequence; blocks shared by several
 // sequences of the batch are read with the default policy so that they stay
 // cached for the other readers.  KV: element format of the pools, 0 binary16,
-// 1 e4m3fn, 2 e5m2.
+// 1 e4m3fn, 2 e5m2; 3 and 4: e4m3fn and e5m2 with one scale per (block, KV
+// head), read with the block ids one tile ahead: the key scale multiplies the
+// tile's scores (per half tile at block_size 8) in fp32, and the values are
+// widened to fp32, scaled and rounded to binary16 for the P.V product.
 template <int D, int BS, int KV, bool NT>
 struct Engine {
+  static constexpr int FMT = KV >= 3 ? KV - 2 : KV;   // 0 binary16, 1 e4m3fn, 2 e5m2
+  static constexpr bool BSC = KV >= 3;         // scales per (block, KV head)
   static constexpr int CPOL = NT ? 2 : 0;      // cache-policy operand of the tile loads
-  static constexpr int E = KV ? 1 : 2;         // bytes per KV element
+  static constexpr int E = FMT ? 1 : 2;        // bytes per KV element
   static constexpr int KCH = 16 / E;           // elements in a 16-B key chunk
   static constexpr int NKL = D * E / 64;       // 16-B key loads per lane per tile
   static constexpr int GPL = KCH / 4;          // MFMA operand groups per key chunk
@@ -165,6 +171,9 @@ struct Engine {
   const char* vp;
   lds_char* kst;                               // this wave's key tile in LDS
   float sc;
+  const float* kbs;                            // per-block scales of this wave's KV head
+  const float* vbs;                            //   (stride hkv), formats 3 and 4
+  int hkv;
 
   half4_t qop[NQ];
   float m_run, l_run;
@@ -182,10 +191,21 @@ struct Engine {
     vp = a.v;
     kst = kstage;
     sc = a.score_scale;
+    kbs = vbs = nullptr;
+    hkv = a.num_kv_heads;
     t0 = lane / CPR;
     ch = lane % CPR;
     koff = (uint32_t)((BS >= 16 || RPI <= 8 ? t0 : (t0 & 7)) * rs + ch * 16);
     voff = (uint32_t)(r * rs + c * VB);
+  }
+
+  // The per-block scale arrays ([num_blocks][Hkv]; kernel arguments, so that
+  // their entries are read with scalar loads) at KV head kh.
+  __device__ __forceinline__ void set_block_scales(const float* k, const float* v, int kh) {
+    if constexpr (BSC) {
+      kbs = k + kh;
+      vbs = v + kh;
+    }
   }
 
   // LDS chunk slot of chunk `k` of token row t: XOR-swizzled so that both the
@@ -237,6 +257,10 @@ struct Engine {
   }
 
   __device__ __forceinline__ int64_t phys(const PairRef& p, int lb) const {
+    return (int64_t)id_of(p, lb) * block_stride + p.head_off;
+  }
+
+  __device__ __forceinline__ int id_of(const PairRef& p, int lb) const {
     lb = lb < p.nblk - 1 ? lb : p.nblk - 1;      // never past the valid table entries
 #if PA_VMEM_TABLES
     // a vector load (all lanes the same address): its wait counts with the
@@ -247,17 +271,31 @@ struct Engine {
 #else
     int id = p.bt[lb];
 #endif
-    id = id < 0 ? 0 : (id > nb_m1 ? nb_m1 : id);
-    return (int64_t)id * block_stride + p.head_off;
+    return id < 0 ? 0 : (id > nb_m1 ? nb_m1 : id);
   }
 
   __device__ __forceinline__ Ids tile_ids(const PairRef& p, int j, bool live = true) const {
     if constexpr (BS >= 16) {
       const int t = j * 16;
-      const int64_t b = phys(p, t / BS) + (int64_t)(t % BS) * rs;
-      return {b, b, live};
+      const int id = id_of(p, t / BS);
+      const int64_t b = (int64_t)id * block_stride + p.head_off + (int64_t)(t % BS) * rs;
+      Ids r{b, b, live, 1.f, 1.f, 1.f, 1.f};
+      if constexpr (BSC) {
+        r.ks0 = r.ks1 = kbs[(int64_t)id * hkv];
+        r.vs0 = r.vs1 = vbs[(int64_t)id * hkv];
+      }
+      return r;
     } else {
-      return {phys(p, 2 * j), phys(p, 2 * j + 1), live};
+      const int i0 = id_of(p, 2 * j), i1 = id_of(p, 2 * j + 1);
+      Ids r{(int64_t)i0 * block_stride + p.head_off, (int64_t)i1 * block_stride + p.head_off,
+            live, 1.f, 1.f, 1.f, 1.f};
+      if constexpr (BSC) {
+        r.ks0 = kbs[(int64_t)i0 * hkv];
+        r.ks1 = kbs[(int64_t)i1 * hkv];
+        r.vs0 = vbs[(int64_t)i0 * hkv];
+        r.vs1 = vbs[(int64_t)i1 * hkv];
+      }
+      return r;
     }
   }
 
@@ -281,7 +319,13 @@ struct Engine {
       return __builtin_amdgcn_raw_buffer_load_b32(R, voff, so, CPOL);
   }
 
-  __device__ __forceinline__ void issue(const Ids& ids, uint4* kr, VT* vr) const {
+  // ts: where the tile's per-block scales (keys of its two halves, values of
+  // its two halves) go, for compute (formats 3 and 4).
+  __device__ __forceinline__ void issue(const Ids& ids, uint4* kr, VT* vr,
+                                        float4* ts = nullptr) const {
+    if constexpr (BSC) {
+      if (ts) *ts = make_float4(ids.ks0, ids.ks1, ids.vs0, ids.vs1);
+    }
     const __amdgpu_buffer_rsrc_t klo = rsrc(kp + ids.lo, ids.live);
     const __amdgpu_buffer_rsrc_t vlo = rsrc(vp + ids.lo, ids.live);
     // Key load u reads whole rows u*RPI .. u*RPI+RPI-1 of the tile (lane: row
@@ -311,7 +355,8 @@ struct Engine {
   // schedule's columns belong to several sequences.
   template <bool COLS = false>
   __device__ __forceinline__ void compute(int j, int t_begin, int t_end, const uint4* kr,
-                                          const VT* vr_in, int col_lo = 0, int col_hi = 16) {
+                                          const VT* vr_in, int col_lo = 0, int col_hi = 16,
+                                          float4 ts = float4{1.f, 1.f, 1.f, 1.f}) {
     // Loads issued before this point stay before it: otherwise the scheduler
     // hoists the waits for this tile above the next tile's loads.
     __builtin_amdgcn_sched_barrier(0);
@@ -335,8 +380,8 @@ struct Engine {
 #pragma unroll
       for (int grp = 0; grp < GPL; ++grp) {
         half4_t kop;
-        if constexpr (KV == 1) kop = e4m3x4_to_half4(w[grp]);
-        else if constexpr (KV == 2) kop = e5m2x4_to_half4(w[grp]);
+        if constexpr (FMT == 1) kop = e4m3x4_to_half4(w[grp]);
+        else if constexpr (FMT == 2) kop = e5m2x4_to_half4(w[grp]);
         else kop = halves_of(w[2 * grp], w[2 * grp + 1]);
         sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kop, qop[cl * GPL + grp], sacc, 0, 0, 0);
       }
@@ -346,9 +391,13 @@ struct Engine {
     const int tb = j * 16 + r;                  // token of score i: tb + 4 i
     float x[4];
     const bool col_ok = !COLS || (uint32_t)(c - col_lo) < (uint32_t)(col_hi - col_lo);
+    // the key scale of each score's block: scores 0, 1 are tokens r, r + 4 (the
+    // first half tile), 2, 3 tokens r + 8, r + 12
+    const float sc_lo = BSC ? sc * ts.x : sc, sc_hi = BSC ? sc * (BS >= 16 ? ts.x : ts.y) : sc;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      x[i] = (col_ok && (uint32_t)(tb + 4 * i - t_begin) < span) ? sacc[i] * sc : -INFINITY;
+      x[i] = (col_ok && (uint32_t)(tb + 4 * i - t_begin) < span)
+                 ? sacc[i] * (i < 2 ? sc_lo : sc_hi) : -INFINITY;
     float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     tmax = xor_max(tmax, 16);
     tmax = xor_max(tmax, 32);
@@ -383,7 +432,7 @@ struct Engine {
         for (int wi = 0; wi < VB / 4; ++wi) vw[k][wi] = ok ? vw[k][wi] : 0u;
       }
     }
-    if constexpr (KV == 0) {
+    if constexpr (FMT == 0) {
 #pragma unroll
       for (int e = 0; e < DCH; ++e) {
         const int wi = e >> 1, sh = (e & 1) * 16;
@@ -392,7 +441,7 @@ struct Engine {
         const half4_t bop = halves_of(h0 | (h1 << 16), h2 | (h3 << 16));
         acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(pop, bop, acc[e], 0, 0, 0);
       }
-    } else if constexpr (KV == 2) {
+    } else if constexpr (FMT == 2 && !BSC) {
 #pragma unroll
       for (int e = 0; e < DCH; ++e) {
         const int wi = e >> 2, b = e & 3;
@@ -401,17 +450,32 @@ struct Engine {
         acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(pop, bop, acc[e], 0, 0, 0);
       }
     } else {
+      // e4m3fn (and e5m2 with per-block scales): fp32 values, times the
+      // block's value scale (value load k holds rows 4k .. 4k + 3: the first
+      // half tile for k < 2)
       float vf[4][DCH];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
 #pragma unroll
         for (int wi = 0; wi < VB / 4; ++wi) {
-          const float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k][wi], false);
-          const float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k][wi], true);
-          vf[k][4 * wi + 0] = lo.x;
-          vf[k][4 * wi + 1] = lo.y;
-          vf[k][4 * wi + 2] = hi.x;
-          vf[k][4 * wi + 3] = hi.y;
+          if constexpr (FMT == 1) {
+            const float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k][wi], false);
+            const float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k][wi], true);
+            vf[k][4 * wi + 0] = lo.x;
+            vf[k][4 * wi + 1] = lo.y;
+            vf[k][4 * wi + 2] = hi.x;
+            vf[k][4 * wi + 3] = hi.y;
+          } else {                             // e5m2 byte b is binary16 bits b << 8
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              vf[k][4 * wi + q] = (float)__builtin_bit_cast(
+                  _Float16, (uint16_t)(((vw[k][wi] >> (8 * q)) & 0xFFu) << 8));
+          }
+        }
+        if constexpr (BSC) {
+          const float vsk = (BS >= 16 || k < 2) ? ts.z : ts.w;
+#pragma unroll
+          for (int e = 0; e < DCH; ++e) vf[k][e] *= vsk;
         }
       }
 #pragma unroll
@@ -611,7 +675,8 @@ template <int D, int BS, int KV, int NW, bool SPLIT, bool NT>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : PA_WAVES_PER_EU, 8)))
 void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
-                   const int32_t* __restrict__ lens) {
+                   const int32_t* __restrict__ lens, const float* __restrict__ kbs,
+                   const float* __restrict__ vbs) {
   // The tables arrive as restrict arguments so that their uniform reads stay
   // scalar loads (as in decode_flat_kernel).
   typedef Engine<D, BS, KV, NT> En;
@@ -649,6 +714,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
   En en;
   en.init(a, lane, (lds_char*)kstage[wid]);
   if (a.k_hs) en.sc *= a.k_hs[kh];
+  en.set_block_scales(kbs, vbs, kh);
   const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
   en.load_q(a.q + ((int64_t)s * a.num_q_heads + (int64_t)kh * g) * D);
   en.reset();
@@ -664,23 +730,24 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ tables,
   // last one are dead (their loads fetch nothing).
   uint4 kA[En::NKL], kB[En::NKL];
   VT vA[4], vB[4];
+  float4 tsA = float4{1.f, 1.f, 1.f, 1.f}, tsB = tsA;
   int j = j_begin + wid;
   if (j < j_end) {
     const int j_last = j_end - 1;
-    en.issue(ids0, kA, vA);
+    en.issue(ids0, kA, vA, &tsA);
     Ids ids_b = ids1;
     ids_b.live = j + NW <= j_last;
     for (;;) {
       // the block ids two tiles ahead are read before the next tile's loads
       // are issued, so waiting for them never waits for those loads
       const Ids ids_a = en.tile_ids(pr, min(j + 2 * NW, j_last), j + 2 * NW <= j_last);
-      en.issue(ids_b, kB, vB);
-      en.compute(j, t_begin, t_end, kA, vA);
+      en.issue(ids_b, kB, vB, &tsB);
+      en.compute(j, t_begin, t_end, kA, vA, 0, 16, tsA);
       j += NW;
       if (j >= j_end) break;
       ids_b = en.tile_ids(pr, min(j + 2 * NW, j_last), j + 2 * NW <= j_last);
-      en.issue(ids_a, kA, vA);
-      en.compute(j, t_begin, t_end, kB, vB);
+      en.issue(ids_a, kA, vA, &tsA);
+      en.compute(j, t_begin, t_end, kB, vB, 0, 16, tsB);
       j += NW;
       if (j >= j_end) break;
     }
@@ -721,7 +788,8 @@ template <int D, int BS, int KV, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : PA_GROUP_WAVES_PER_EU, 8)))
 void decode_group_kernel(DecodeArgs a, GroupArgs gp, const int32_t* __restrict__ tables,
-                         const int32_t* __restrict__ lens) {
+                         const int32_t* __restrict__ lens, const float* __restrict__ kbs,
+                         const float* __restrict__ vbs) {
   typedef Engine<D, BS, KV, NT> En;
   typedef typename En::VT VT;
   const int lane = threadIdx.x & 63;
@@ -774,6 +842,7 @@ void decode_group_kernel(DecodeArgs a, GroupArgs gp, const int32_t* __restrict__
   En en;
   en.init(a, lane, (lds_char*)kstage[wid]);
   if (a.k_hs) en.sc *= a.k_hs[kh];
+  en.set_block_scales(kbs, vbs, kh);
   const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
   const int64_t head_off = (int64_t)kh * D * En::E;
   {
@@ -803,13 +872,14 @@ void decode_group_kernel(DecodeArgs a, GroupArgs gp, const int32_t* __restrict__
                     ln > 0 ? (ln + BS - 1) / BS : 1, ln, head_off};
     return en.tile_ids(p, un.t);
   };
-  auto run = [&](int u, const uint4* kr, const VT* vr) {
+  auto run = [&](int u, const uint4* kr, const VT* vr, float4 ts) {
     const Unit un = unit_of(u);
-    en.template compute<true>(un.t, 0, uni(sm_len[un.i]), kr, vr, un.i * g, (un.j + 1) * g);
+    en.template compute<true>(un.t, 0, uni(sm_len[un.i]), kr, vr, un.i * g, (un.j + 1) * g, ts);
   };
 
   uint4 kA[En::NKL], kB[En::NKL];
   VT vA[4], vB[4];
+  float4 tsA = float4{1.f, 1.f, 1.f, 1.f}, tsB = tsA;
   int u = wid;
   if (u < U) {
     const int u_last = U - 1;
@@ -818,17 +888,17 @@ void decode_group_kernel(DecodeArgs a, GroupArgs gp, const int32_t* __restrict__
       x.live = v <= u_last;
       return x;
     };
-    en.issue(ids_of(u), kA, vA);
+    en.issue(ids_of(u), kA, vA, &tsA);
     Ids ids_b = ids_ahead(u + NW);
     for (;;) {
       const Ids ids_a = ids_ahead(u + 2 * NW);
-      en.issue(ids_b, kB, vB);
-      run(u, kA, vA);
+      en.issue(ids_b, kB, vB, &tsB);
+      run(u, kA, vA, tsA);
       u += NW;
       if (u >= U) break;
       ids_b = ids_ahead(u + 2 * NW);
-      en.issue(ids_a, kA, vA);
-      run(u, kB, vB);
+      en.issue(ids_a, kA, vA, &tsA);
+      run(u, kB, vB, tsB);
       u += NW;
       if (u >= U) break;
     }
@@ -940,7 +1010,8 @@ __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : PA_FLAT_WAVES_PER_EU, 8)))
 void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ tables,
                         const int32_t* __restrict__ lens, const _Float16* __restrict__ qs,
                         _Float16* __restrict__ outs, float* __restrict__ slots,
-                        int32_t* __restrict__ prefix) {
+                        int32_t* __restrict__ prefix, const float* __restrict__ kbs,
+                        const float* __restrict__ vbs) {
   // The read-only arrays arrive as separate restrict arguments: stores to the
   // outputs inside the loop then provably leave the block table alone, so its
   // entries can be read with scalar loads.
@@ -1032,6 +1103,7 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   En en;
   en.init(a, lane, (lds_char*)kstage[wid]);
   if (a.k_hs) en.sc *= a.k_hs[kh];
+  en.set_block_scales(kbs, vbs, kh);
   const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
   const int64_t head_off = (int64_t)kh * D * En::E;
   // unit j of a sequence is its tile j + (window start >> 4)
@@ -1080,6 +1152,7 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
   // are in flight.
   uint4 kb[ST][En::NKL];
   VT vb[ST][4];
+  float4 tsc[ST];
 #pragma unroll
   for (int k = 0; k < ST - 1; ++k) {
     if (k > 0 && cur[k].j == 0 && g0 + k < g1 && q_seq < 0) {   // a sequence starts early
@@ -1088,7 +1161,7 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
     }
     Ids ik = ids_of(cur[k]);
     ik.live = g0 + k < g1;
-    en.issue(ik, kb[k], vb[k]);
+    en.issue(ik, kb[k], vb[k], &tsc[k]);
   }
   Ids ids_next = ids_of(cur[ST - 1]);
   ids_next.live = g0 + ST - 1 < g1;
@@ -1105,12 +1178,12 @@ void decode_flat_kernel(DecodeArgs a, FlatArgs f, const int32_t* __restrict__ ta
         // instead cost 8-13%: the waits after it then drain every load)
         Ids ids_new = ids_of(cur[ST]);
         ids_new.live = gt + ST < g1;
-        en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST]);
+        en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST], &tsc[(st + ST - 1) % ST]);
         ids_next = ids_new;
       }
       {
         const int len = uni(sm_len[cur[0].s]), w0 = win_start(len, a.window);
-        en.compute(cur[0].j + (w0 >> 4), w0, len, kb[st], vb[st]);
+        en.compute(cur[0].j + (w0 >> 4), w0, len, kb[st], vb[st], 0, 16, tsc[st]);
       }
       finish();
       if (++gt == g1) return;
@@ -1209,7 +1282,8 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
                               const int32_t* __restrict__ tables,
                               const int32_t* __restrict__ lens, const _Float16* __restrict__ qs,
                               _Float16* __restrict__ outs, float* __restrict__ slots,
-                              int32_t* __restrict__ prefix) {
+                              int32_t* __restrict__ prefix, const float* __restrict__ kbs,
+                              const float* __restrict__ vbs) {
   typedef Engine<D, BS, KV, NT> En;
   typedef typename En::VT VT;
   const int G = gp.num_groups, M = gp.num_members, Hkv = a.num_kv_heads, g = a.gqa;
@@ -1372,6 +1446,7 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
   En en;
   en.init(a, lane, (lds_char*)kstage[wid]);
   if (a.k_hs) en.sc *= a.k_hs[kh];
+  en.set_block_scales(kbs, vbs, kh);
   const float v_scale = a.v_hs ? a.v_hs[kh] : a.v_scale;
   const int64_t head_off = (int64_t)kh * D * En::E;
   auto ids_of = [&](const Cur& c) -> Ids {
@@ -1422,6 +1497,7 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
 
   uint4 kb[ST][En::NKL];
   VT vb[ST][4];
+  float4 tsc[ST];
 #pragma unroll
   for (int k = 0; k < ST - 1; ++k) {
     if (k > 0 && cur[k].j == 0 && g0 + k < g1 && q_grp < 0) {
@@ -1430,7 +1506,7 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
     }
     Ids ik = ids_of(cur[k]);
     ik.live = g0 + k < g1;
-    en.issue(ik, kb[k], vb[k]);
+    en.issue(ik, kb[k], vb[k], &tsc[k]);
   }
   Ids ids_next = ids_of(cur[ST - 1]);
   ids_next.live = g0 + ST - 1 < g1;
@@ -1447,13 +1523,13 @@ void decode_flat_group_kernel(DecodeArgs a, FlatArgs f, GroupArgs gp,
         // instead cost 8-13%: the waits after it then drain every load)
         Ids ids_new = ids_of(cur[ST]);
         ids_new.live = gt + ST < g1;
-        en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST]);
+        en.issue(ids_next, kb[(st + ST - 1) % ST], vb[(st + ST - 1) % ST], &tsc[(st + ST - 1) % ST]);
         ids_next = ids_new;
       }
       {
         const Cur& c = cur[0];                 // members p .. hi take the tile
         en.template compute<true>(c.t, 0, c.len, kb[st], vb[st], (c.p - c.m0) * g,
-                                  (c.hi - c.m0 + 1) * g);
+                                  (c.hi - c.m0 + 1) * g, tsc[st]);
       }
       finish();
       if (++gt == g1) return;
@@ -1534,7 +1610,7 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, const GroupArgs*
     hipLaunchKernelGGL((decode_flat_kernel<D, BS, KV, FW, NT>),
                        dim3((uint32_t)((waves + FW - 1) / FW)), dim3(FW * 64), lds,
                        stream, a, *f, a.block_tables, a.seq_lens, a.q, a.out, f->slots,
-                       f->prefix);
+                       f->prefix, a.k_bs, a.v_bs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // records per cut sequence ~ ranges / sequences + 1: a power of two of
@@ -1551,7 +1627,8 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, const GroupArgs*
     constexpr int FW = PA_FLAT_WAVES;
     hipLaunchKernelGGL((decode_flat_group_kernel<D, BS, KV, FW, PA_GROUP_NT || NT>),
                        dim3((uint32_t)((waves + FW - 1) / FW)), dim3(FW * 64), lds, stream, a,
-                       *f, *gr, a.block_tables, a.seq_lens, a.q, a.out, f->slots, f->prefix);
+                       *f, *gr, a.block_tables, a.seq_lens, a.q, a.out, f->slots, f->prefix,
+                       a.k_bs, a.v_bs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((flat_group_merge_kernel<D>),
@@ -1564,18 +1641,19 @@ hipError_t launch_typed(const DecodeArgs& a, const FlatArgs* f, const GroupArgs*
     hipLaunchKernelGGL((decode_group_kernel<D, BS, KV, PA_GROUP_WAVES, PA_GROUP_NT || NT>),
                        dim3((uint32_t)gr->num_groups * (uint32_t)a.num_kv_heads),
                        dim3(PA_GROUP_WAVES * 64), PA_GROUP_EXTRA_LDS, stream, a, *gr,
-                       a.block_tables, a.seq_lens);
+                       a.block_tables, a.seq_lens, a.k_bs, a.v_bs);
   } else if (mode == kModeSplit) {
     hipLaunchKernelGGL((decode_kernel<D, BS, KV, kWaves, true, NT>),
                        dim3(units * (uint32_t)a.num_parts), dim3(kWaves * 64), 0, stream, a,
-                       a.block_tables, a.seq_lens);
+                       a.block_tables, a.seq_lens, a.k_bs, a.v_bs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((lse_reduce_kernel<D>), dim3((uint32_t)num_seqs * (uint32_t)a.num_q_heads),
                        dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((decode_kernel<D, BS, KV, kWaves, false, NT>), dim3(units),
-                       dim3(kWaves * 64), 0, stream, a, a.block_tables, a.seq_lens);
+                       dim3(kWaves * 64), 0, stream, a, a.block_tables, a.seq_lens, a.k_bs,
+                       a.v_bs);
   }
   return hipGetLastError();
 }

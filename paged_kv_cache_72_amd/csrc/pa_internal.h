@@ -27,6 +27,8 @@ struct PoolGeom {
   const float* k_hs;     // per-KV-head fp8 scales (device) or null
   const float* v_hs;
   int32_t window;        // sliding window in positions, 0: none
+  float* k_bs;           // per-(block, KV head) fp8 scales (device) or null
+  float* v_bs;
 };
 
 struct DecodeArgs {
@@ -50,6 +52,8 @@ struct DecodeArgs {
   const float* v_hs;          //   and v_scale then take the head's factor
   int32_t window;             // sliding window: the query sees the last `window`
                               //   positions of its context (0: all)
+  const float* k_bs;          // per-(block, KV head) scales [num_blocks][Hkv] (kv
+  const float* v_bs;          //   formats 3 and 4) or null
   int32_t part_tokens;        // split pass: tokens per partition
   int32_t num_parts;          // split pass: partitions per (sequence, KV head)
   float* ws_o;                // split pass: [S][Hq][num_parts][D] normalised partials
@@ -87,7 +91,7 @@ hipError_t launch_copy_blocks(const PoolGeom& g, const int64_t* pairs, int64_t n
                               hipStream_t stream);
 // stream_kv: read K/V tiles with the streaming cache policy (pools without
 // blocks shared between sequences of the batch).
-// kv: 0 binary16, 1 e4m3fn, 2 e5m2.
+// kv: 0 binary16, 1 e4m3fn, 2 e5m2, 3 e4m3fn and 4 e5m2 with per-block scales.
 hipError_t launch_decode(const DecodeArgs& a, const FlatArgs* f, const GroupArgs* gr,
                          int32_t num_seqs, int32_t head_dim, int32_t block_size, int kv,
                          bool stream_kv, int mode, hipStream_t stream);

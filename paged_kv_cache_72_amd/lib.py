@@ -62,6 +62,7 @@ class pa_kv_pool(C.Structure):
         ("dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
         ("flags", C.c_uint32), ("sliding_window", C.c_int32),
         ("k_head_scales", C.c_void_p), ("v_head_scales", C.c_void_p),
+        ("k_block_scales", C.c_void_p), ("v_block_scales", C.c_void_p),
     ]
 
 
@@ -153,15 +154,25 @@ class KVPool:
                  v_scale: float = 1.0, num_blocks: Optional[int] = None,
                  block_stride_bytes: int = 0, shared_blocks: bool = False,
                  k_head_scales: Optional[torch.Tensor] = None,
-                 v_head_scales: Optional[torch.Tensor] = None, sliding_window: int = 0):
+                 v_head_scales: Optional[torch.Tensor] = None, sliding_window: int = 0,
+                 k_block_scales: Optional[torch.Tensor] = None,
+                 v_block_scales: Optional[torch.Tensor] = None):
         """k_head_scales / v_head_scales: optional device float32 [num_kv_heads]
-        fp8 scales, one per KV head (replacing k_scale / v_scale)."""
+        fp8 scales, one per KV head (replacing k_scale / v_scale).
+        k_block_scales / v_block_scales: optional device float32 [num_blocks,
+        num_kv_heads] fp8 scales per (block, KV head), which the library
+        writes as it writes the blocks."""
         self.k, self.v = k, v
         self.k_head_scales, self.v_head_scales = k_head_scales, v_head_scales
+        self.k_block_scales, self.v_block_scales = k_block_scales, v_block_scales
         khp = _dev(k_head_scales, torch.float32, "k_head_scales") if k_head_scales is not None \
             else None
         vhp = _dev(v_head_scales, torch.float32, "v_head_scales") if v_head_scales is not None \
             else None
+        kbp = _dev(k_block_scales, torch.float32, "k_block_scales") \
+            if k_block_scales is not None else None
+        vbp = _dev(v_block_scales, torch.float32, "v_block_scales") \
+            if v_block_scales is not None else None
         self.block_size, self.num_kv_heads, self.head_dim = block_size, num_kv_heads, head_dim
         self.kv_dtype = kv_dtype
         self.k_scale, self.v_scale = float(k_scale), float(v_scale)
@@ -171,7 +182,7 @@ class KVPool:
                                self.block_stride_bytes, block_size, num_kv_heads, head_dim,
                                _DTYPES[kv_dtype], self.k_scale, self.v_scale,
                                PA_POOL_SHARED_BLOCKS if shared_blocks else 0,
-                               int(sliding_window), khp, vhp)
+                               int(sliding_window), khp, vhp, kbp, vbp)
 
     @property
     def shared_blocks(self) -> bool:
@@ -187,7 +198,10 @@ class KVPool:
                  kv_dtype: str = "f16", k_scale: float = 1.0, v_scale: float = 1.0,
                  device="cuda", fill_bits: Optional[int] = None,
                  shared_blocks: bool = False, k_head_scales=None,
-                 v_head_scales=None, sliding_window: int = 0) -> "KVPool":
+                 v_head_scales=None, sliding_window: int = 0,
+                 block_scales: bool = False) -> "KVPool":
+        """block_scales: keep one fp8 scale per (block, KV head) beside the
+        pools (zero-filled device arrays the library then writes)."""
         tdt = torch.int16 if kv_dtype == "f16" else torch.uint8
         shape = (num_blocks, block_size, num_kv_heads, head_dim)
         k = torch.empty(shape, dtype=tdt, device=device)
@@ -201,9 +215,13 @@ class KVPool:
         if k_head_scales is not None:
             khs = torch.as_tensor(k_head_scales, dtype=torch.float32).to(device).contiguous()
             vhs = torch.as_tensor(v_head_scales, dtype=torch.float32).to(device).contiguous()
+        kbs = vbs = None
+        if block_scales:
+            kbs = torch.zeros((num_blocks, num_kv_heads), dtype=torch.float32, device=device)
+            vbs = torch.zeros((num_blocks, num_kv_heads), dtype=torch.float32, device=device)
         return cls(k, v, block_size, num_kv_heads, head_dim, kv_dtype, k_scale, v_scale,
                    shared_blocks=shared_blocks, k_head_scales=khs, v_head_scales=vhs,
-                   sliding_window=sliding_window)
+                   sliding_window=sliding_window, k_block_scales=kbs, v_block_scales=vbs)
 
     @property
     def elem_bytes(self) -> int:

@@ -249,12 +249,13 @@ def _finish(name, seed, S, Hq, Hkv, D, bs, num_blocks, kv_dtype, lens, tables, p
         tok_k = (tok_k.astype(np.float32) * mult).astype(np.float16)
         tok_v = (tok_v.astype(np.float32) * mult[:, ::-1]).astype(np.float16)
     if scale_grain == "block":
-        # blocks of different magnitude (2^-3 .. 2^3 by physical id), and this
-        # step's writes four times larger, so that appending to a block raises
-        # its scale and re-encodes the rows already there
-        e = ((tok_slot // bs) * 5 % 7 - 3).astype(np.float32)
+        # blocks of different magnitude (2^-3 .. 2^0 by physical id: values of
+        # the size the fp8 gate is derived for), and this step's writes twice
+        # as large, so that appending to a block raises its scale and
+        # re-encodes the rows already there
+        e = ((tok_slot // bs) * 5 % 4 - 3).astype(np.float32)
         mult = (2.0 ** e)[:, None, None].astype(np.float32)
-        mult[np.asarray(new_idx, np.int64)] *= 4.0
+        mult[np.asarray(new_idx, np.int64)] *= 2.0
         tok_k = (tok_k.astype(np.float32) * mult).astype(np.float16)
         tok_v = (tok_v.astype(np.float32) * mult[:, :, ::-1]).astype(np.float16)
         extra["block_scales"] = True

@@ -34,7 +34,8 @@ class DeviceCase:
                                       w.kv_dtype, w.k_scale, w.v_scale, device, fill_bits=fill,
                                       shared_blocks=w.has_shared_blocks,
                                       k_head_scales=w.k_head_scales,
-                                      v_head_scales=w.v_head_scales, sliding_window=w.window)
+                                      v_head_scales=w.v_head_scales, sliding_window=w.window,
+                                      block_scales=w.block_scales)
         self.fill = fill
         self.q = torch.from_numpy(w.q).to(device)
         self.bt = torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(device)

@@ -312,3 +312,25 @@ def test_dispatch_log_follows_the_environment(so, value, expect):
     assert "flat" in lines[0]
     assert lines[1].startswith("[pa] pa_reshape_and_cache: 0 tokens, f16 pool of 1024 blocks")
     assert lines[2] == "[pa] pa_copy_blocks: 0 pairs (K and V blocks of 32768 bytes each)"
+
+
+def test_block_scale_pool_checks(so):
+    """Per-block scales: both arrays or neither, fp8 only, not with per-head
+    scales, at most 512 KV heads, 4-byte aligned; pa_prefill does not take
+    them."""
+    e4 = dict(dtype=L.PA_KV_FP8_E4M3FN, k_scale=0.5, v_scale=0.5)
+    assert _decode(so, _pool(k_block_scales=FAKE, **e4)) == L.PA_ERR_INVALID_ARG
+    assert "both" in L.pa_last_error()
+    assert _decode(so, _pool(k_block_scales=FAKE, v_block_scales=FAKE)) == L.PA_ERR_INVALID_ARG
+    assert "fp8" in L.pa_last_error()
+    assert _decode(so, _pool(k_block_scales=FAKE, v_block_scales=FAKE, k_head_scales=FAKE,
+                             v_head_scales=FAKE, **e4)) == L.PA_ERR_INVALID_ARG
+    assert _decode(so, _pool(num_kv_heads=1024, k_block_scales=FAKE, v_block_scales=FAKE, **e4),
+                   Hq=1024) == L.PA_ERR_UNSUPPORTED
+    assert _decode(so, _pool(k_block_scales=FAKE + 2, v_block_scales=FAKE, **e4)) == \
+        L.PA_ERR_ALIGNMENT
+    ok = _pool(k_block_scales=FAKE, v_block_scales=FAKE, **e4)
+    assert _decode(so, ok, S=0) == L.PA_OK
+    assert so.pa_prefill(C.byref(ok), FAKE, FAKE, 4, FAKE, 1, 32, FAKE, 64, FAKE, 4,
+                         C.c_float(0.1), None) == L.PA_ERR_UNSUPPORTED
+    assert "per-block" in L.pa_last_error()

@@ -51,6 +51,18 @@ SHAPES = {
                                          kv_dtype="fp8_e4m3fn"),
     "e5m2h_d256_bs8_g8": lambda: W.custom("s", 72, EDGE_LENS, 16, 2, 256, 8, kv_dtype="fp8_e5m2",
                                           scale_grain="head"),
+    # one fp8 scale per (block, KV head), written by reshape_and_cache (blocks
+    # of different magnitude; the step's rows raise some blocks' scales)
+    "fp8b_d128_bs16_g4": lambda: W.custom("s", 73, EDGE_LENS, 32, 8, 128, 16,
+                                          kv_dtype="fp8_e4m3fn", scale_grain="block"),
+    "e5m2b_d128_bs8_g7": lambda: W.custom("s", 74, EDGE_LENS, 28, 4, 128, 8, kv_dtype="fp8_e5m2",
+                                          scale_grain="block"),
+    "fp8b_d64_bs32_g2": lambda: W.custom("s", 75, EDGE_LENS, 8, 4, 64, 32,
+                                         kv_dtype="fp8_e4m3fn", scale_grain="block"),
+    "e5m2b_d256_bs16_g4": lambda: W.custom("s", 76, EDGE_LENS, 16, 4, 256, 16,
+                                           kv_dtype="fp8_e5m2", scale_grain="block"),
+    "fp8b_d128_bs128_g8": lambda: W.custom("s", 77, EDGE_LENS, 16, 2, 128, 128,
+                                           kv_dtype="fp8_e4m3fn", scale_grain="block"),
 }
 
 _cache = {}

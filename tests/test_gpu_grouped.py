@@ -35,6 +35,13 @@ SHAPES = {
                                                            kv_dtype="fp8_e5m2",
                                                            scale_grain="head"),
     "sp_d256_bs8_g8": lambda: W.shared_prefix_batch("sp", 308, GROUPS, 16, 2, 256, 8),
+    # one fp8 scale per (block, KV head), written by reshape_and_cache
+    "sp_fp8b_d128_bs16_g4": lambda: W.shared_prefix_batch("sp", 309, GROUPS, 32, 8, 128, 16,
+                                                          kv_dtype="fp8_e4m3fn",
+                                                          scale_grain="block"),
+    "sp_e5m2b_d128_bs8_g4": lambda: W.shared_prefix_batch("sp", 310, GROUPS, 16, 4, 128, 8,
+                                                          kv_dtype="fp8_e5m2",
+                                                          scale_grain="block"),
 }
 
 _cache = {}

@@ -184,7 +184,7 @@ def _deq_from_pool(w, hp, which):
 def test_decode_with_block_scales_matches_sdpa(kv):
     w = W.custom("b", 55, [1, 17, 100, 40], 8, 4, 64, 16, kv_dtype=kv, scale_grain="block")
     hp = O.pool_for_workload(w)
-    # the step's rows (four times larger) raised the scale of some blocks
+    # the step's rows (twice as large) raised the scale of some blocks
     h0 = O.HostPool.for_workload(w)
     keep = np.ones(w.tok_slot.size, bool)
     keep[w.new_idx] = False
