@@ -657,7 +657,8 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
                 num_q_heads, g.num_kv_heads);
   const int32_t gqa = num_q_heads / g.num_kv_heads;
   if (gqa > 16) return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d > 16", gqa);
-  if (g.k_bs) return fail(PA_ERR_UNSUPPORTED, "pa_prefill does not read per-block scales");
+  if (g.k_bs && g.head_dim < 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill reads per-block scales at head_dim 128 and 256");
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !q_start || !block_tables || !seq_lens)
     return fail(PA_ERR_INVALID_ARG,
@@ -703,8 +704,9 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
   a.k_hs = g.k_hs;
   a.v_hs = g.v_hs;
   a.window = g.window;
-  if (hipError_t e = pa::launch_prefill(a, g.head_dim, g.block_size,
-                                        g.elem_bytes == 2 ? 0 : (g.fp8_e5m2 ? 2 : 1), stream))
+  a.k_bs = g.k_bs;
+  a.v_bs = g.v_bs;
+  if (hipError_t e = pa::launch_prefill(a, g.head_dim, g.block_size, kv_code(g), stream))
     return fail(PA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return PA_OK;
 }

@@ -128,6 +128,8 @@ struct PrefillArgs {
   const float* k_hs;          // per-KV-head scales (device) or null
   const float* v_hs;
   int32_t window;             // sliding window (0: none): position p sees p - window + 1 .. p
+  const float* k_bs;          // per-(block, KV head) scales [num_blocks][Hkv] (kv codes 3, 4)
+  const float* v_bs;          //   or null
 };
 
 // Sets the calling thread's pa_last_error() message and returns code.

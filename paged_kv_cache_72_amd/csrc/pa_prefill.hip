@@ -112,6 +112,34 @@ __device__ __forceinline__ uint4 widen8(uint2 w, int kv) {
   return make_uint4(ua.x, ua.y, ub.x, ub.y);
 }
 
+// 8 fp8 bytes -> 8 binary16 values of (byte value * scale), each product
+// formed in fp32 and rounded to nearest even once (fp8 pools with per-block
+// scales).
+__device__ __forceinline__ uint4 widen8_scaled(uint2 w, int kv, float scale) {
+  float f[8];
+  const uint32_t ws[2] = {w.x, w.y};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (kv == 1) {
+      const float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[q], false);
+      const float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[q], true);
+      f[4 * q] = lo.x;
+      f[4 * q + 1] = lo.y;
+      f[4 * q + 2] = hi.x;
+      f[4 * q + 3] = hi.y;
+    } else {                                   // e5m2 byte b is binary16 bits b << 8
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        f[4 * q + i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(((ws[q] >> (8 * i)) & 0xFFu) << 8));
+    }
+  }
+  const float4_t a = {f[0] * scale, f[1] * scale, f[2] * scale, f[3] * scale};
+  const float4_t b = {f[4] * scale, f[5] * scale, f[6] * scale, f[7] * scale};
+  const uint2 ua = __builtin_bit_cast(uint2, __builtin_convertvector(a, half4_t));
+  const uint2 ub = __builtin_bit_cast(uint2, __builtin_convertvector(b, half4_t));
+  return make_uint4(ua.x, ua.y, ub.x, ub.y);
+}
+
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
@@ -521,14 +549,20 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// KV: pool format, 0 binary16; 1 e4m3fn or 2 e5m2 (head_dim 128, 256).  fp8 tiles
+// KVC: pool format, 0 binary16; 1 e4m3fn or 2 e5m2 (head_dim 128, 256); 3, 4:
+// e4m3fn, e5m2 with one scale per (block, KV head), applied as the tile is
+// widened (the scales of the tile's blocks are read with scalar loads one
+// tile ahead).  fp8 tiles
 // go by the global-to-LDS load into a three-slot staging ring as stored
 // (row-major bytes), and each is widened exactly into the binary16 tile layout
 // below one tile ahead of its compute, two binary16 buffers deep; the math is
 // the same for every format.
-template <int D, int BS, int KV>
+template <int D, int BS, int KVC>
 __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kernel(
-    PrefillArgs a, const int32_t* __restrict__ tables) {
+    PrefillArgs a, const int32_t* __restrict__ tables, const float* __restrict__ kbs,
+    const float* __restrict__ vbs) {
+  constexpr int KV = KVC >= 3 ? KVC - 2 : KVC;  // element format
+  constexpr bool BSC = KVC >= 3;                // per-block scales
   typedef PfDma<D> T;
   constexpr int RB = T::RB, NST = T::NST, NB = T::NB, G = T::G;
   constexpr bool kPrio = T::OCC >= 2;
@@ -675,7 +709,27 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
   // Rows of positions outside [lo_c, kv_end) (loaded as repeats of an
   // in-range row) are written as zeros, so that a repeated V row holding an
   // infinity (e5m2 has them) meets its zero weight as 0 * 0, not 0 * inf.
-  auto widen_tile = [&](int slot, int fb, int t) {
+  // per-block scales of tile t's blocks (at most 4: block_size >= 8), for K
+  // and V; positions outside the rows in use read an in-use block's entry
+  constexpr int NBT = BS >= kPfKeys ? 1 : kPfKeys / BS;
+  struct TSc { float k[NBT], v[NBT]; };
+  auto tile_scales = [&](int t) {
+    TSc r;
+    if constexpr (BSC) {
+      const int lb_lo = lo_c / BS, lb_hi = (kv_end - 1) / BS;
+#pragma unroll
+      for (int i = 0; i < NBT; ++i) {
+        int lb = (t * kPfKeys) / BS + i;
+        lb = lb < lb_lo ? lb_lo : (lb > lb_hi ? lb_hi : lb);
+        int id = bt[lb];
+        id = id < 0 ? 0 : (id > a.num_blocks_m1 ? a.num_blocks_m1 : id);
+        r.k[i] = kbs[(int64_t)id * a.num_kv_heads + kh];
+        r.v[i] = vbs[(int64_t)id * a.num_kv_heads + kh];
+      }
+    }
+    return r;
+  };
+  auto widen_tile = [&](int slot, int fb, int t, const TSc& ts) {
     if constexpr (KV != 0) {
 #pragma unroll
      for (int w = 0; w < WCH; ++w) {
@@ -691,8 +745,17 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const uint4 z = make_uint4(0, 0, 0, 0);
-        const uint4 lo = in_range ? widen8(make_uint2(rw[q].x, rw[q].y), KV) : z;
-        const uint4 hi = in_range ? widen8(make_uint2(rw[q].z, rw[q].w), KV) : z;
+        uint4 lo, hi;
+        if constexpr (BSC) {
+          float sc = q ? ts.v[0] : ts.k[0];
+#pragma unroll
+          for (int i = 1; i < NBT; ++i) sc = key >= i * BS ? (q ? ts.v[i] : ts.k[i]) : sc;
+          lo = in_range ? widen8_scaled(make_uint2(rw[q].x, rw[q].y), KV, sc) : z;
+          hi = in_range ? widen8_scaled(make_uint2(rw[q].z, rw[q].w), KV, sc) : z;
+        } else {
+          lo = in_range ? widen8(make_uint2(rw[q].x, rw[q].y), KV) : z;
+          hi = in_range ? widen8(make_uint2(rw[q].z, rw[q].w), KV) : z;
+        }
         const int sw = q ? T::vsw(key) : T::ksw(key);
         const uint32_t row = lds_base + fb * T::BUF + q * T::TILE + key * RB;
         lds_w128<0>(row + (((2 * c) ^ sw) << 4), lo);
@@ -851,12 +914,15 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
     for (int u = 0; u < 2; ++u)
       if (t0 + u < ntiles) issue(t0 + u, u);
     int rs = 0;
+    TSc ts_next = tile_scales(t0);
     for (int t = t0; t < ntiles; ++t) {
+      const TSc ts = ts_next;
+      if (BSC && t + 1 < ntiles) ts_next = tile_scales(t + 1);
       if (ntiles - 1 - t >= 1) vm_wait<DPT>();
       else vm_wait<0>();
       lgkm_wait_all_regs<0>();
       __builtin_amdgcn_s_barrier();
-      widen_tile(rs, 0, t);
+      widen_tile(rs, 0, t, ts);
       lgkm_wait_all_regs<0>();
       __builtin_amdgcn_s_barrier();
       if (t + 2 < ntiles) issue(t + 2, rs);
@@ -878,16 +944,19 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
     else if (ntiles - t0 == 2) vm_wait<DPT>();
     else vm_wait<0>();
     __builtin_amdgcn_s_barrier();
-    widen_tile(0, 0, t0);
+    widen_tile(0, 0, t0, tile_scales(t0));
+    TSc ts_next = tile_scales(t0 + 1 < ntiles ? t0 + 1 : t0);
     int rs = 0, fb = 0;
     for (int t = t0; t < ntiles; ++t) {
+      const TSc ts = ts_next;
+      if (BSC && t + 2 < ntiles) ts_next = tile_scales(t + 2);
       if (ntiles - 1 - t >= 2) vm_wait<DPT>();
       else vm_wait<0>();
       lgkm_wait_all_regs<0>();
       __builtin_amdgcn_s_barrier();
       if (t + 3 < ntiles) issue(t + 3, rs);
       const int rn = rs == 2 ? 0 : rs + 1;
-      if (t + 1 < ntiles) widen_tile(rn, fb ^ 1, t + 1);
+      if (t + 1 < ntiles) widen_tile(rn, fb ^ 1, t + 1, ts);
       const int kt = t * kPfKeys;
       compute((uint32_t)(fb * T::BUF), kt, needs_mask(kt));
       rs = rn;
@@ -939,15 +1008,17 @@ hipError_t launch_pf_bs(const PrefillArgs& a, int kv, hipStream_t stream) {
   const dim3 grid((uint32_t)a.num_seqs * (uint32_t)a.num_kv_heads * (uint32_t)a.num_qt);
   const dim3 block(kPfWaves * 64);
   if (kv == 0) {
-    hipLaunchKernelGGL((prefill_f16_kernel<D, BS, 0>), grid, block, 0, stream, a, a.block_tables);
+    hipLaunchKernelGGL((prefill_f16_kernel<D, BS, 0>), grid, block, 0, stream, a, a.block_tables,
+                       a.k_bs, a.v_bs);
     return hipGetLastError();
   }
   if constexpr (D >= 128) {             // fp8 pools at head_dim 128, 256: staged bytes, widened in LDS
-    if (kv == 1)
-      hipLaunchKernelGGL((prefill_f16_kernel<D, BS, 1>), grid, block, 0, stream, a, a.block_tables);
-    else if (kv == 2)
-      hipLaunchKernelGGL((prefill_f16_kernel<D, BS, 2>), grid, block, 0, stream, a, a.block_tables);
-    else return hipErrorInvalidValue;
+#define PA_PF_KV(C)                                                                            \
+  if (kv == C)                                                                                 \
+    hipLaunchKernelGGL((prefill_f16_kernel<D, BS, C>), grid, block, 0, stream, a,             \
+                       a.block_tables, a.k_bs, a.v_bs);
+    PA_PF_KV(1) else PA_PF_KV(2) else PA_PF_KV(3) else PA_PF_KV(4) else return hipErrorInvalidValue;
+#undef PA_PF_KV
     return hipGetLastError();
   }
   if constexpr (D == 64) {              // fp8 pools at head_dim 64: register-staged kernel

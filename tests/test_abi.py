@@ -316,8 +316,8 @@ def test_dispatch_log_follows_the_environment(so, value, expect):
 
 def test_block_scale_pool_checks(so):
     """Per-block scales: both arrays or neither, fp8 only, not with per-head
-    scales, at most 512 KV heads, 4-byte aligned; pa_prefill does not take
-    them."""
+    scales, at most 512 KV heads, 4-byte aligned; pa_prefill takes them at
+    head_dim 128 and 256 only."""
     e4 = dict(dtype=L.PA_KV_FP8_E4M3FN, k_scale=0.5, v_scale=0.5)
     assert _decode(so, _pool(k_block_scales=FAKE, **e4)) == L.PA_ERR_INVALID_ARG
     assert "both" in L.pa_last_error()
@@ -331,6 +331,7 @@ def test_block_scale_pool_checks(so):
         L.PA_ERR_ALIGNMENT
     ok = _pool(k_block_scales=FAKE, v_block_scales=FAKE, **e4)
     assert _decode(so, ok, S=0) == L.PA_OK
-    assert so.pa_prefill(C.byref(ok), FAKE, FAKE, 4, FAKE, 1, 32, FAKE, 64, FAKE, 4,
+    d64 = _pool(head_dim=64, k_block_scales=FAKE, v_block_scales=FAKE, **e4)
+    assert so.pa_prefill(C.byref(d64), FAKE, FAKE, 4, FAKE, 1, 32, FAKE, 64, FAKE, 4,
                          C.c_float(0.1), None) == L.PA_ERR_UNSUPPORTED
     assert "per-block" in L.pa_last_error()

@@ -66,6 +66,22 @@ SHAPES = {
     "d128_bs128_g2_e4m3_head": lambda: W.custom_prefill("pf", 99, [130, 0], [20, 50], 8, 4,
                                                         128, 128, kv_dtype="fp8_e4m3fn",
                                                         scale_grain="head"),
+    # one fp8 scale per (block, KV head), written by reshape_and_cache
+    "d128_bs16_g4_e4m3_block": lambda: W.custom_prefill("pf", 102, [0, 40, 7], [64, 25, 90], 32,
+                                                        8, 128, 16, kv_dtype="fp8_e4m3fn",
+                                                        scale_grain="block"),
+    "d128_bs8_g7_e5m2_block": lambda: W.custom_prefill("pf", 103, [0, 17, 64], [19, 37, 100],
+                                                       28, 4, 128, 8, kv_dtype="fp8_e5m2",
+                                                       scale_grain="block"),
+    "d256_bs16_g4_e5m2_block": lambda: W.custom_prefill("pf", 104, [0, 5, 33, 300],
+                                                        [70, 31, 32, 129], 16, 4, 256, 16,
+                                                        kv_dtype="fp8_e5m2", scale_grain="block"),
+    "d256_bs128_g2_e4m3_block": lambda: W.custom_prefill("pf", 105, [130, 0], [20, 50], 8, 4,
+                                                         256, 128, kv_dtype="fp8_e4m3fn",
+                                                         scale_grain="block"),
+    "d128_bs64_g4_e4m3_block": lambda: W.custom_prefill("pf", 106, [0, 100], [90, 33], 32, 8,
+                                                        128, 64, kv_dtype="fp8_e4m3fn",
+                                                        scale_grain="block"),
     # 2,600 (sequence, KV head) pairs: more than 256 per XCD, so the workgroups
     # take the pairs in index order instead of ranking them by length
     "many_pairs": lambda: W.custom_prefill("pf", 94, _RS.randint(0, 48, 325).tolist(),
@@ -164,7 +180,8 @@ def test_prefill_full_size_sampled(name, make, nrows):
 
 
 @pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "d64_bs16_g16",
-                                  "d128_bs16_g4_e4m3", "d128_bs8_g4_e5m2", "d256_bs16_g4"])
+                                  "d128_bs16_g4_e4m3", "d128_bs8_g4_e5m2", "d256_bs16_g4",
+                                  "d128_bs8_g7_e5m2_block"])
 @pytest.mark.parametrize("win", [1, 31, 32, 33, 100])
 def test_sliding_window_prefill(name, win):
     w0 = SHAPES[name]()
