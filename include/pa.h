@@ -335,7 +335,9 @@ int pa_decode_noalloc(const pa_kv_pool* pool, void* out, const void* q, int32_t 
  * the same tile) reaches that query as 0 * inf = NaN; positions outside the
  * context or the window never do.  fp8 pools written by pa_reshape_and_cache
  * hold no infinities (the encoders saturate), but binary16 pools receive the
- * bits unchanged, so an infinite element written there does this. */
+ * bits unchanged, so an infinite element written there does this.  Pools
+ * with per-block scales are read at head_dim 128 and 256; at head_dim 64
+ * they are refused with PA_ERR_UNSUPPORTED. */
 int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q,
                const int32_t* q_start, int32_t num_seqs, int32_t num_q_heads,
                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
