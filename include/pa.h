@@ -329,10 +329,15 @@ int pa_decode_noalloc(const pa_kv_pool* pool, void* out, const void* q, int32_t 
  * num_q_heads must be a multiple of num_kv_heads with a ratio of at most 16.
  * No workspace is needed.  total_q, num_seqs or max_q_len of 0 is a no-op.
  * Outputs are bitwise reproducible and do not depend on which physical ids
- * hold the blocks.  Non-finite pool data: the K and V rows of a 32-position
- * tile are shared by all query rows of a workgroup, so an infinite V element
- * at an in-context position that a query does not see (a later position of
- * the same tile) reaches that query as 0 * inf = NaN; positions outside the
+ * hold the blocks.  At head_dim 128 a workgroup takes 128 or 192 query rows
+ * (32 or 48 new tokens at 4 query heads per KV head): 192 when the grid has
+ * at least four workgroups per CU and max_q_len pads no worse, else 128; the
+ * two differ only in rounding order.  PA_PREFILL_GROUPS=2 (128 rows) or 3
+ * (192 rows) in the environment, read at every call, fixes the choice.
+ * Non-finite pool data: the K and V rows of a 32-position tile are shared by
+ * the query rows of a wave (16 to 48 rows), so an infinite V element at an
+ * in-context position that a query does not see (a later position of the
+ * same tile) can reach that query as 0 * inf = NaN; positions outside the
  * context or the window never do.  fp8 pools written by pa_reshape_and_cache
  * hold no infinities (the encoders saturate), but binary16 pools receive the
  * bits unchanged, so an infinite element written there does this.  Pools
@@ -342,6 +347,16 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
                const int32_t* q_start, int32_t num_seqs, int32_t num_q_heads,
                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                int32_t max_q_len, float scale, hipStream_t stream);
+
+/* Query rows ((token, query head) pairs) per workgroup that pa_prefill will
+ * use for these arguments: a workgroup takes n new tokens of one sequence and
+ * all g = num_q_heads / num_kv_heads query heads of one KV head, n g rows,
+ * with n = floor(R / g) for R = 128 at head_dim 64 and 256 and R = 128 or
+ * 192 at head_dim 128 (the library's choice described at pa_prefill, or the
+ * one PA_PREFILL_GROUPS fixes).  Returns n g, or a negative pa_status on
+ * arguments pa_prefill would refuse for the same reason. */
+int32_t pa_prefill_plan(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t max_q_len);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* pa_last_error(void);

@@ -43,6 +43,17 @@ void log_line(const char* fmt, ...) {
   std::fprintf(stderr, "[pa] %s\n", buf);
 }
 
+// PA_PREFILL_GROUPS=2 or 3 in the environment, read at every pa_prefill call,
+// fixes the 16-row query groups per wave of head_dim 128 prefill instead of
+// the library's choice (both give the same results up to rounding order).
+int prefill_groups_override() {
+  const char* e = std::getenv("PA_PREFILL_GROUPS");
+  if (!e) return 0;
+  if (std::strcmp(e, "2") == 0) return 2;
+  if (std::strcmp(e, "3") == 0) return 3;
+  return 0;
+}
+
 const char* kv_name(int dtype) {
   return dtype == PA_KV_F16 ? "f16" : (dtype == PA_KV_FP8_E4M3FN ? "fp8_e4m3fn" : "fp8_e5m2");
 }
@@ -642,23 +653,43 @@ int pa_decode_grouped(const pa_kv_pool* pool, void* out, const void* q, int32_t 
   return PA_OK;
 }
 
+// Checks shared by pa_prefill and pa_prefill_plan.
+int prefill_shape(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                  int32_t max_q_len, pa::PoolGeom* g) {
+  int st = check_pool(pool, g);
+  if (st) return st;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+  if (max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "max_q_len %d < 0", max_q_len);
+  if (num_q_heads < 1 || num_q_heads % g->num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, g->num_kv_heads);
+  if (num_q_heads / g->num_kv_heads > 16)
+    return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d > 16",
+                num_q_heads / g->num_kv_heads);
+  if (g->k_bs && g->head_dim < 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill reads per-block scales at head_dim 128 and 256");
+  return PA_OK;
+}
+
+int32_t pa_prefill_plan(const pa_kv_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t max_q_len) {
+  pa::PoolGeom g;
+  if (int st = prefill_shape(pool, num_seqs, num_q_heads, max_q_len, &g)) return st;
+  const int32_t gqa = num_q_heads / g.num_kv_heads;
+  const pa::PrefillPlan plan = pa::prefill_plan(g.head_dim, kv_code(g), gqa,
+                                                (int64_t)num_seqs * g.num_kv_heads, max_q_len,
+                                                prefill_groups_override());
+  return plan.tile_tokens * gqa;
+}
+
 int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q,
                const int32_t* q_start, int32_t num_seqs, int32_t num_q_heads,
                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                int32_t max_q_len, float scale, hipStream_t stream) {
   pa::PoolGeom g;
-  int st = check_pool(pool, &g);
-  if (st) return st;
-  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+  if (int st = prefill_shape(pool, num_seqs, num_q_heads, max_q_len, &g)) return st;
   if (total_q < 0) return fail(PA_ERR_INVALID_ARG, "total_q %d < 0", total_q);
-  if (max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "max_q_len %d < 0", max_q_len);
-  if (num_q_heads < 1 || num_q_heads % g.num_kv_heads)
-    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
-                num_q_heads, g.num_kv_heads);
   const int32_t gqa = num_q_heads / g.num_kv_heads;
-  if (gqa > 16) return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d > 16", gqa);
-  if (g.k_bs && g.head_dim < 128)
-    return fail(PA_ERR_UNSUPPORTED, "pa_prefill reads per-block scales at head_dim 128 and 256");
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !q_start || !block_tables || !seq_lens)
     return fail(PA_ERR_INVALID_ARG,
@@ -669,15 +700,18 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
     return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(PA_ERR_INVALID_ARG, "scale must be finite and positive");
-  const int32_t tile = pa::prefill_rows_per_workgroup(g.head_dim) / gqa;
+  const pa::PrefillPlan plan = pa::prefill_plan(g.head_dim, kv_code(g), gqa,
+                                                (int64_t)num_seqs * g.num_kv_heads, max_q_len,
+                                                prefill_groups_override());
+  const int32_t tile = plan.tile_tokens;
   const int64_t num_qt = cdiv64(max_q_len, tile);
   if ((int64_t)num_seqs * g.num_kv_heads * num_qt > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "num_seqs * num_kv_heads * cdiv(max_q_len, %d) too large",
                 tile);
   log_line("pa_prefill: %d seqs, %d new tokens (at most %d per sequence), %d/%d heads, "
-           "head_dim %d, %s: %d new tokens per workgroup, %lld workgroups", num_seqs, total_q,
-           max_q_len, num_q_heads, g.num_kv_heads, g.head_dim, kv_name(pool->dtype), tile,
-           (long long)num_seqs * g.num_kv_heads * num_qt);
+           "head_dim %d, %s: %d new tokens per workgroup (%d row groups per wave), %lld "
+           "workgroups", num_seqs, total_q, max_q_len, num_q_heads, g.num_kv_heads, g.head_dim,
+           kv_name(pool->dtype), tile, plan.groups, (long long)num_seqs * g.num_kv_heads * num_qt);
 
   pa::PrefillArgs a{};
   a.k = g.k;
@@ -697,6 +731,7 @@ int pa_prefill(const pa_kv_pool* pool, void* out, const void* q, int32_t total_q
   a.num_seqs = num_seqs;
   a.total_q = total_q;
   a.max_q_len = max_q_len;
+  a.groups = plan.groups;
   a.tile_tokens = tile;
   a.num_qt = (int32_t)num_qt;
   a.score_scale = (float)((double)scale * 1.4426950408889634 * (double)g.k_scale);

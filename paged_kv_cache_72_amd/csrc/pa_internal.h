@@ -121,6 +121,7 @@ struct PrefillArgs {
   int32_t num_seqs;
   int32_t total_q;
   int32_t max_q_len;
+  int32_t groups;             // 16-row query groups per wave (prefill_plan)
   int32_t tile_tokens;        // new tokens per workgroup: rows per workgroup / gqa
   int32_t num_qt;             // workgroups per (sequence, KV head): cdiv(max_q_len, tile)
   float score_scale;          // scale * log2(e) * k_scale
@@ -137,8 +138,17 @@ int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 // Validates a pool descriptor and resolves its geometry (PA_OK or a status).
 int check_pool(const pa_kv_pool* p, PoolGeom* g);
 
-// Query rows (token, head pairs) one prefill workgroup covers at this head_dim.
-int prefill_rows_per_workgroup(int head_dim);
+// The prefill launch shape for this head_dim, pool code (0 binary16, 1-4 fp8
+// formats with or without block scales), query heads per KV head, number of
+// (sequence, KV head) pairs and largest new-token count: 16-row query groups
+// per wave, and new tokens per workgroup (its query rows / gqa).  force: 2 or
+// 3 fixes the groups at head_dim 128; 0 lets the plan choose.
+struct PrefillPlan {
+  int groups;
+  int tile_tokens;
+};
+PrefillPlan prefill_plan(int head_dim, int kv_code, int gqa, int64_t pairs, int max_q_len,
+                         int force);
 
 // kv: 0 binary16, 1 e4m3fn, 2 e5m2.
 hipError_t launch_prefill(const PrefillArgs& a, int32_t head_dim, int32_t block_size, int kv,

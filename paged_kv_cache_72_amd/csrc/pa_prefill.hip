@@ -12,14 +12,18 @@
 // the decode formula of the same pages, one query position at a time.
 //
 // Work decomposition and data flow:
-//   * A workgroup owns one (sequence, KV head, tile of QT = floor(128 / gqa)
-//     new tokens; floor(64 / gqa) at head_dim 256); the query tiles of one
-//     (sequence, KV head) are placed on one XCD so that they share its L2,
-//     and the pairs are spread over the XCDs so that each gets an equal
-//     share of the work (pf_item).  Its 128 query rows are (token, head)
-//     pairs, head fastest, so the gqa query heads of the KV head share every
-//     K/V tile it stages.  4 waves x 2 groups x 16 rows (x 1 group at head_dim
-//     256, which keeps two workgroups per CU).
+//   * A workgroup owns one (sequence, KV head, tile of QT = floor(R / gqa)
+//     new tokens); the query tiles of one (sequence, KV head) are placed on
+//     one XCD so that they share its L2, and the pairs are spread over the
+//     XCDs so that each gets an equal share of the work (pf_item).  Its R
+//     query rows are (token, head) pairs, head fastest, so the gqa query
+//     heads of the KV head share every K/V tile it stages.  R = waves x
+//     groups x 16 rows: 4 x 2 x 16 = 128 at head_dim 64; at head_dim 128
+//     4 x 3 x 16 = 192 on grids of several workgroups per CU, else 4 x 2 x 16
+//     (prefill_plan); at head_dim 256 8 x 1 x 16 = 128, one workgroup per
+//     CU (two groups per wave would not fit the registers).  A wave skips the
+//     compute of every tile none of its rows can see (all positions after
+//     its last row, or before its first row's window, or no row in use).
 //   * K/V tiles of 32 positions are gathered through the block table into LDS
 //     by whole 16-byte row chunks, XOR-swizzled by chunk so that the reads
 //     below hit distinct banks.  fp16 pools (prefill_f16_kernel): straight from
@@ -29,7 +33,7 @@
 //     path into a three-slot staging ring, and each tile is widened exactly
 //     into the binary16 layout one tile ahead of its compute (two buffers;
 //     at head_dim 256 one buffer and two slots, widened between two barriers,
-//     so that two workgroups fit per CU).
+//     66 KB of LDS).
 //     fp8 pools at head_dim 64 (prefill_kernel): loaded into registers one
 //     tile ahead and widened on the way into LDS (two buffers), V stored
 //     transposed.  Every kernel spends one workgroup barrier per tile.
@@ -61,12 +65,20 @@ namespace {
 #ifndef PA_PF_NBUF
 #define PA_PF_NBUF 3          // fp16 prefill: LDS tile buffers (tiles in flight + 1)
 #endif
+#ifndef PA_PF_W16
+#define PA_PF_W16 4           // fp16 prefill at head_dim 128: waves per workgroup (4 or 8)
+#endif
+#ifndef PA_PF_W256
+#define PA_PF_W256 8          // prefill at head_dim 256: waves per workgroup (4 or 8)
+#endif
+#ifndef PA_PF_F8W
+#define PA_PF_F8W 1           // fp8 at head_dim 256: one binary16 buffer, two staging slots
+#endif
 #ifndef PA_PF_G256
 #define PA_PF_G256 1          // fp16 prefill at head_dim 256: 16-row groups per wave
 #endif
 
 constexpr int kPfWaves = 4;
-constexpr int kPfRows = 128;       // query rows per workgroup
 constexpr int kPfKeys = 32;        // key positions per tile
 
 template <int D, int BS, int KV>
@@ -466,21 +478,28 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
-template <int D>
+// waves per workgroup of prefill_f16_kernel at head_dim d for pool code kvc
+// (fp8 pools, and head_dim 64, load whole tiles with four waves)
+constexpr int pf_waves(int d, int kvc) {
+  return d > 128 ? PA_PF_W256 : (kvc == 0 && d == 128 ? PA_PF_W16 : kPfWaves);
+}
+
+template <int D, int W = kPfWaves, int GG = 2>
 struct PfDma {
   static constexpr int CPR = D / 8;                       // 16-byte chunks per row
   static constexpr int RB = 2 * D;                        // bytes per row
   static constexpr int RPI = 1024 / RB;                   // rows per wave load
-  static constexpr int NI = kPfKeys / RPI / kPfWaves;     // loads per wave per tile, each of K and V
+  static constexpr int NI = kPfKeys / RPI / W;            // loads per wave per tile, each of K and V
   static constexpr int TILE = kPfKeys * RB;
   static constexpr int BUF = 2 * TILE;                    // K tile then V tile
   static constexpr int DPT = 2 * NI;                      // loads per thread per tile
-  // 16-row query groups per wave and workgroups per CU: at head_dim 256 one
-  // group per wave keeps the accumulators and query operands at head_dim
-  // 128's register count, so two workgroups fit per CU (two groups need 452
-  // registers per lane: one workgroup)
-  static constexpr int G = D > 128 ? PA_PF_G256 : 2;
-  static constexpr int OCC = D > 128 && G > 1 ? 1 : PA_PF_OCC;
+  // 16-row query groups per wave and workgroups per CU: two waves per SIMD
+  // (registers for 2 or 3 groups at head_dim 128: 185 and 244 VGPRs; at head_dim
+  // 256 one group per wave keeps head_dim 128's count, two would need 452
+  // registers per lane and one wave per SIMD)
+  static constexpr int G = D > 128 ? PA_PF_G256 : GG;
+  static constexpr int OCC = (D > 128 && G > 1) || W >= 8 ? 1 : PA_PF_OCC;
+  static constexpr bool PRIO = W * OCC >= 8;              // two or more waves per SIMD
   // head_dim 256: two buffers of 32 KiB
   static constexpr int NBUF = D > 128 ? 2 : PA_PF_NBUF;
   static constexpr int NST = D / 32;
@@ -557,30 +576,31 @@ __device__ __forceinline__ void vm_wait() {
 // (row-major bytes), and each is widened exactly into the binary16 tile layout
 // below one tile ahead of its compute, two binary16 buffers deep; the math is
 // the same for every format.
-template <int D, int BS, int KVC>
-__global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kernel(
+template <int D, int BS, int KVC, int GG>
+__global__ __launch_bounds__(pf_waves(D, KVC) * 64, (PfDma<D, pf_waves(D, KVC), GG>::OCC)) void prefill_f16_kernel(
     PrefillArgs a, const int32_t* __restrict__ tables, const float* __restrict__ kbs,
     const float* __restrict__ vbs) {
   constexpr int KV = KVC >= 3 ? KVC - 2 : KVC;  // element format
   constexpr bool BSC = KVC >= 3;                // per-block scales
-  typedef PfDma<D> T;
+  constexpr int NW = pf_waves(D, KVC);
+  typedef PfDma<D, NW, GG> T;
   constexpr int RB = T::RB, NST = T::NST, NB = T::NB, G = T::G;
-  constexpr bool kPrio = T::OCC >= 2;
+  constexpr bool kPrio = T::PRIO;
   static_assert(KV == 0 || D >= 128, "fp8 tiles are staged for head_dim 128 and 256");
-  // fp8 at head_dim 256: one binary16 buffer and two staging slots (66 KB),
-  // so that two workgroups fit per CU
-  constexpr bool F8W = KV != 0 && D > 128;
+  // fp8 at head_dim 256: one binary16 buffer and two staging slots (66 KB;
+  // measured faster than two buffers and three slots)
+  constexpr bool F8W = KV != 0 && D > 128 && PA_PF_F8W;
   constexpr int NBUF = KV ? (F8W ? 1 : 2) : T::NBUF;   // binary16 tile buffers
   constexpr int E = KV ? 1 : 2;                 // bytes per stored element
   constexpr int SRB = D * E;                    // stored bytes per row
   constexpr int SCPR = SRB / 16;                // 16-byte chunks per stored row
   constexpr int SRPI = 1024 / SRB;              // rows per wave load
-  constexpr int NI = kPfKeys / SRPI / kPfWaves; // loads per wave per tile, each of K and V
+  constexpr int NI = kPfKeys / SRPI / NW;       // loads per wave per tile, each of K and V
   constexpr int STILE = kPfKeys * SRB;          // fp8 staging: K tile then V tile per slot
   constexpr int NRAW = KV ? (F8W ? 2 : 3) : 0;
   // stored 16-byte chunks of the K tile (and of the V tile) each thread widens
-  constexpr int WCH = KV ? kPfKeys * SCPR / (kPfWaves * 64) : 1;
-  static_assert(NI >= 1 && (KV == 0 || WCH * kPfWaves * 64 == kPfKeys * SCPR), "load shape");
+  constexpr int WCH = KV ? kPfKeys * SCPR / (NW * 64) : 1;
+  static_assert(NI >= 1 && (KV == 0 || WCH * NW * 64 == kPfKeys * SCPR), "load shape");
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * T::BUF + NRAW * 2 * STILE];
   lds_char* const lds0 = (lds_char*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds0;
@@ -612,6 +632,23 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
     return kt + kPfKeys - 1 > ctx + q0 || (a.window > 0 && kt < ctx + t_hi - a.window);
   };
   const int32_t* bt = tables + (int64_t)s * a.max_blocks;
+  // Positions of this wave's first and last query rows in use.  A tile whose
+  // positions all follow the last (causal mask) or all precede the first
+  // one's window is skipped by the wave: its weights would all be exact
+  // zeros.  A wave with no row in use (a partial last query tile) skips
+  // every tile; it still takes part in the loads and barriers.
+  int w_first, w_last;
+  {
+    const int tf = (16 * G * wid) / g;
+    int tl = (16 * G * (wid + 1) - 1) / g;
+    tl = tl < QT - 1 ? tl : QT - 1;
+    tl = tl < q_len - q0 - 1 ? tl : q_len - q0 - 1;
+    w_first = uni(ctx + q0 + tf);
+    w_last = uni(tf <= tl ? ctx + q0 + tl : -1);
+  }
+  auto wave_sees = [&](int kt) {
+    return kt <= w_last && (a.window <= 0 || kt + kPfKeys - 1 >= w_first - a.window + 1);
+  };
 
   half8_t qop[G][NST];
   int qpos[G];
@@ -733,7 +770,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
     if constexpr (KV != 0) {
 #pragma unroll
      for (int w = 0; w < WCH; ++w) {
-      const int ch = tid + kPfWaves * 64 * w;
+      const int ch = tid + NW * 64 * w;
       const uint32_t src = lds_base + NBUF * T::BUF + slot * 2 * STILE + ch * 16;
       const int key = ch / SCPR, c = ch % SCPR;
       const int pos = t * kPfKeys + key;
@@ -927,7 +964,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
       __builtin_amdgcn_s_barrier();
       if (t + 2 < ntiles) issue(t + 2, rs);
       const int kt = t * kPfKeys;
-      compute(0u, kt, needs_mask(kt));
+      if (wave_sees(kt)) compute(0u, kt, needs_mask(kt));
       rs ^= 1;
     }
   } else if constexpr (KV != 0) {
@@ -958,7 +995,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
       const int rn = rs == 2 ? 0 : rs + 1;
       if (t + 1 < ntiles) widen_tile(rn, fb ^ 1, t + 1, ts);
       const int kt = t * kPfKeys;
-      compute((uint32_t)(fb * T::BUF), kt, needs_mask(kt));
+      if (wave_sees(kt)) compute((uint32_t)(fb * T::BUF), kt, needs_mask(kt));
       rs = rn;
       fb ^= 1;
     }
@@ -979,7 +1016,7 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
     __builtin_amdgcn_s_barrier();
     if (t + NB_ - 1 < ntiles) issue(t + NB_ - 1, b == 0 ? NB_ - 1 : b - 1);
     const int kt = t * kPfKeys;
-    compute((uint32_t)(b * T::BUF), kt, needs_mask(kt));
+    if (wave_sees(kt)) compute((uint32_t)(b * T::BUF), kt, needs_mask(kt));
     b = b == NB_ - 1 ? 0 : b + 1;
   }
   }
@@ -1003,20 +1040,20 @@ __global__ __launch_bounds__(kPfWaves * 64, PfDma<D>::OCC) void prefill_f16_kern
   }
 }
 
-template <int D, int BS>
-hipError_t launch_pf_bs(const PrefillArgs& a, int kv, hipStream_t stream) {
+template <int D, int BS, int GG>
+hipError_t launch_pf_g(const PrefillArgs& a, int kv, hipStream_t stream) {
   const dim3 grid((uint32_t)a.num_seqs * (uint32_t)a.num_kv_heads * (uint32_t)a.num_qt);
   const dim3 block(kPfWaves * 64);
   if (kv == 0) {
-    hipLaunchKernelGGL((prefill_f16_kernel<D, BS, 0>), grid, block, 0, stream, a, a.block_tables,
-                       a.k_bs, a.v_bs);
+    hipLaunchKernelGGL((prefill_f16_kernel<D, BS, 0, GG>), grid, dim3(pf_waves(D, 0) * 64), 0,
+                       stream, a, a.block_tables, a.k_bs, a.v_bs);
     return hipGetLastError();
   }
   if constexpr (D >= 128) {             // fp8 pools at head_dim 128, 256: staged bytes, widened in LDS
 #define PA_PF_KV(C)                                                                            \
   if (kv == C)                                                                                 \
-    hipLaunchKernelGGL((prefill_f16_kernel<D, BS, C>), grid, block, 0, stream, a,             \
-                       a.block_tables, a.k_bs, a.v_bs);
+    hipLaunchKernelGGL((prefill_f16_kernel<D, BS, C, GG>), grid, dim3(pf_waves(D, C) * 64), 0, \
+                       stream, a, a.block_tables, a.k_bs, a.v_bs);
     PA_PF_KV(1) else PA_PF_KV(2) else PA_PF_KV(3) else PA_PF_KV(4) else return hipErrorInvalidValue;
 #undef PA_PF_KV
     return hipGetLastError();
@@ -1028,6 +1065,19 @@ hipError_t launch_pf_bs(const PrefillArgs& a, int kv, hipStream_t stream) {
     return hipGetLastError();
   }
   return hipErrorInvalidValue;
+}
+
+template <int D, int BS>
+hipError_t launch_pf_bs(const PrefillArgs& a, int kv, hipStream_t stream) {
+  if constexpr (D == 128) {
+    if (a.groups == 3) return launch_pf_g<D, BS, 3>(a, kv, stream);
+    if (a.groups == 2) return launch_pf_g<D, BS, 2>(a, kv, stream);
+    return hipErrorInvalidValue;
+  } else {
+    constexpr int G = D > 128 ? PfDma<256>::G : 2;
+    if (a.groups != G) return hipErrorInvalidValue;
+    return launch_pf_g<D, BS, G>(a, kv, stream);
+  }
 }
 
 template <int D>
@@ -1044,8 +1094,31 @@ hipError_t launch_pf_d(const PrefillArgs& a, int bs, int kv, hipStream_t stream)
 
 }  // namespace
 
-int prefill_rows_per_workgroup(int head_dim) {
-  return head_dim > 128 ? kPfWaves * 16 * PfDma<256>::G : kPfRows;
+// Three 16-row groups per wave at head_dim 128 (192 rows per workgroup) read
+// each staged K/V tile for 1.5x the rows of two, which measured 5% faster on
+// fp16 pools and 13% on fp8 ones when the grid holds several workgroups per
+// CU; a grid that fits the CUs about once (a batch of short chunks) ends with
+// the length of its longest workgroup, where two groups per wave are faster
+// (22% on 32 prompts of 50 new tokens over a 2,000-token cached prefix).  The
+// host sees only the largest new-token count, so the choice is: three groups
+// when that grid has at least four workgroups per CU and pads the largest
+// sequence's new tokens by at most 1/16 more than two groups would.
+PrefillPlan prefill_plan(int head_dim, int kv_code, int gqa, int64_t pairs, int max_q_len,
+                         int force) {
+  constexpr int64_t kWorkgroupsPerPass = 256 * 2;   // MI355X: 256 CUs, two workgroups each
+  const int w = pf_waves(head_dim, kv_code);
+  PrefillPlan p;
+  if (head_dim != 128) {
+    p.groups = head_dim > 128 ? PfDma<256>::G : 2;
+  } else {
+    const int64_t t2 = w * 32 / gqa, t3 = w * 48 / gqa;
+    const int64_t n3 = (max_q_len + t3 - 1) / t3, n2 = (max_q_len + t2 - 1) / t2;
+    const bool many = pairs * n3 >= 2 * kWorkgroupsPerPass;
+    p.groups = force == 2 || force == 3 ? force
+                                        : (many && 16 * n3 * t3 <= 17 * n2 * t2 ? 3 : 2);
+  }
+  p.tile_tokens = w * 16 * p.groups / gqa;
+  return p;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int32_t head_dim, int32_t block_size, int kv,

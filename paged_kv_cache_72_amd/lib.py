@@ -32,7 +32,7 @@ _DTYPES = {"f16": PA_KV_F16, "fp8_e4m3fn": PA_KV_FP8_E4M3FN, "fp8_e5m2": PA_KV_F
 EXPORTS = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_plan",
            "pa_decode_workspace_size", "pa_decode", "pa_decode_grouped", "pa_decode_grouped_plan",
            "pa_decode_grouped_workspace_size", "pa_decode_group_plan",
-           "pa_decode_noalloc", "pa_prefill", "pa_last_error",
+           "pa_decode_noalloc", "pa_prefill", "pa_prefill_plan", "pa_last_error",
            # host block pool (include/pa_blocks.h)
            "pa_bp_create", "pa_bp_destroy", "pa_bp_last_error", "pa_bp_num_free",
            "pa_bp_ref_count", "pa_bp_block_hash", "pa_bp_free_queue", "pa_bp_get_new_blocks",
@@ -102,6 +102,8 @@ def load() -> C.CDLL:
         L.pa_decode_noalloc.argtypes = [PP, P, P, I32, I32, P, I32, P, I32, C.c_float, I32, P]
         L.pa_prefill.restype = C.c_int
         L.pa_prefill.argtypes = [PP, P, P, I32, P, I32, I32, P, I32, P, I32, C.c_float, P]
+        L.pa_prefill_plan.restype = I32
+        L.pa_prefill_plan.argtypes = [PP, I32, I32, I32]
         L.pa_last_error.restype = C.c_char_p
         L.pa_last_error.argtypes = []
         SZ = C.c_size_t
@@ -405,6 +407,14 @@ def pa_decode_noalloc(pool: KVPool, out: torch.Tensor, q: torch.Tensor,
         _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
         _dev(seq_lens, torch.int32, "seq_lens"), int(max_seq_len), C.c_float(scale),
         int(partition_size), _stream(stream)))
+
+
+def pa_prefill_plan(pool: KVPool, num_seqs: int, num_q_heads: int, max_q_len: int) -> int:
+    """Query rows per workgroup pa_prefill will use (128 or 192)."""
+    r = load().pa_prefill_plan(C.byref(pool.desc), num_seqs, num_q_heads, max_q_len)
+    if r < 0:
+        raise PaError(r, pa_last_error())
+    return int(r)
 
 
 def pa_prefill(pool: KVPool, out: torch.Tensor, q: torch.Tensor, q_start: torch.Tensor,

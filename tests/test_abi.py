@@ -314,6 +314,41 @@ def test_dispatch_log_follows_the_environment(so, value, expect):
     assert lines[2] == "[pa] pa_copy_blocks: 0 pairs (K and V blocks of 32768 bytes each)"
 
 
+def _prefill_plan(so, pool, S, Hq, mq):
+    return so.pa_prefill_plan(C.byref(pool), S, Hq, mq)
+
+
+def test_prefill_plan_rows(so, monkeypatch):
+    """Query rows per prefill workgroup: 192 at head_dim 128 when the grid
+    holds at least four workgroups per CU and the largest new-token count
+    pads no worse (chunked 8K and cold 2,000-token batches, fp16 or fp8),
+    else 128 (the prefix-hit batch of 32 x 50 tokens, small batches); 128 at
+    head_dim 64 and 256; whole tokens of all the KV head's query heads;
+    PA_PREFILL_GROUPS fixes the head_dim-128 choice."""
+    monkeypatch.delenv("PA_PREFILL_GROUPS", raising=False)
+    f16, e4 = _pool(), _pool(dtype=L.PA_KV_FP8_E4M3FN)
+    assert _prefill_plan(so, f16, 16, 32, 512) == 192          # chunked 8K
+    assert _prefill_plan(so, e4, 16, 32, 512) == 192
+    assert _prefill_plan(so, f16, 8, 32, 2000) == 192          # cold 2,000-token prompts
+    assert _prefill_plan(so, f16, 32, 32, 50) == 128           # prefix hit: one pass of the CUs
+    assert _prefill_plan(so, f16, 2, 32, 100) == 128
+    assert _prefill_plan(so, f16, 64, 32, 49) == 128           # 2 x 48 tokens pad 49 too much
+    assert _prefill_plan(so, _pool(num_kv_heads=4), 64, 28, 2000) == 27 * 7   # gqa 7
+    assert _prefill_plan(so, _pool(num_kv_heads=4), 1, 28, 2000) == 18 * 7
+    assert _prefill_plan(so, _pool(head_dim=256, num_kv_heads=4), 16, 16, 512) == 128
+    assert _prefill_plan(so, _pool(head_dim=64), 16, 32, 512) == 128
+    assert _prefill_plan(so, f16, 16, 30, 512) == L.PA_ERR_INVALID_ARG
+    assert _prefill_plan(so, _pool(num_kv_heads=1), 16, 32, 512) == L.PA_ERR_UNSUPPORTED
+    assert _prefill_plan(so, f16, -1, 32, 512) == L.PA_ERR_INVALID_ARG
+    monkeypatch.setenv("PA_PREFILL_GROUPS", "2")
+    assert _prefill_plan(so, f16, 16, 32, 512) == 128
+    monkeypatch.setenv("PA_PREFILL_GROUPS", "3")
+    assert _prefill_plan(so, f16, 32, 32, 50) == 192
+    assert _prefill_plan(so, _pool(head_dim=256, num_kv_heads=4), 16, 16, 512) == 128
+    monkeypatch.setenv("PA_PREFILL_GROUPS", "5")                # not a choice: ignored
+    assert _prefill_plan(so, f16, 32, 32, 50) == 128
+
+
 def test_block_scale_pool_checks(so):
     """Per-block scales: both arrays or neither, fp8 only, not with per-head
     scales, at most 512 KV heads, 4-byte aligned; pa_prefill takes them at

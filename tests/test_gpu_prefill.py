@@ -4,10 +4,11 @@ Each case writes the context and this step's new tokens with
 pa_reshape_and_cache into a pool whose unused slots and padding block hold
 NaN, runs pa_prefill, and compares every output element with the oracle's
 causal attention: |y - r| <= 2e-3 + 1e-2 |r| for fp16 KV, |y - r| <= 3e-2 for
-fp8 KV.  Shapes cover head_dim 64/128, block sizes 8..128, GQA 1..16 (so
-tiles of 128 / gqa tokens with ragged tails), fp8 e4m3fn and e5m2 pools,
-one-token and cache-free prompts, empty sequences, and the three full-size
-prefill workloads on sampled rows."""
+fp8 KV.  Shapes cover head_dim 64/128/256, block sizes 8..128, GQA 1..16 (so
+tiles of 128 / gqa tokens with ragged tails, and at head_dim 128 also of 192 /
+gqa: PA_PREFILL_GROUPS=3), fp8 e4m3fn and e5m2 pools, one-token and
+cache-free prompts, empty sequences, and the full-size prefill workloads on
+sampled rows with the library's choice of row groups and the other one."""
 import dataclasses
 import zlib
 
@@ -48,8 +49,8 @@ SHAPES = {
     "d256_bs16_g4": lambda: W.custom_prefill("pf", 92, [0, 5, 33, 300], [70, 31, 32, 129],
                                              16, 4, 256, 16),
     "d256_bs64_g8": lambda: W.custom_prefill("pf", 93, [0, 100], [45, 96], 16, 2, 256, 64),
-    # 64 query rows per workgroup at head_dim 256: groups that do not divide
-    # it (3: 21 tokens, 63 rows) and the largest group (16: 4 tokens)
+    # 128 query rows per workgroup at head_dim 256: groups that do not divide
+    # it (3: 42 tokens, 126 rows) and the largest group (16: 8 tokens)
     "d256_bs32_g3": lambda: W.custom_prefill("pf", 95, [0, 50, 7], [70, 22, 43], 6, 2, 256, 32),
     "d256_bs8_g16": lambda: W.custom_prefill("pf", 96, [3, 0], [9, 30], 16, 1, 256, 8),
     "d256_bs16_g4_e4m3": lambda: W.custom_prefill("pf", 100, [0, 5, 33, 300], [70, 31, 32, 129],
@@ -89,10 +90,25 @@ SHAPES = {
 }
 
 
-@pytest.mark.parametrize("name", list(SHAPES))
-def test_prefill_matches_oracle(name):
+D128 = [n for n in SHAPES if n.startswith("d128") or n in ("decode_like", "empty_seq",
+                                                             "many_pairs")]
+CASES = [(n, "auto") for n in SHAPES] + [(n, g) for n in D128 for g in ("2", "3")]
+
+
+def set_groups(monkeypatch, groups):
+    """Fix the head_dim-128 row groups per wave ("2", "3") or leave the
+    library's choice ("auto")."""
+    if groups == "auto":
+        monkeypatch.delenv("PA_PREFILL_GROUPS", raising=False)
+    else:
+        monkeypatch.setenv("PA_PREFILL_GROUPS", groups)
+
+
+@pytest.mark.parametrize("name,groups", CASES, ids=[f"{n}-{g}" for n, g in CASES])
+def test_prefill_matches_oracle(name, groups, monkeypatch):
+    set_groups(monkeypatch, groups)
     w = SHAPES[name]()
-    say(f"prefill {name} q_lens={w.q_lens.tolist()} lens={w.seq_lens.tolist()}")
+    say(f"prefill {name} groups={groups} q_lens={w.q_lens.tolist()} lens={w.seq_lens.tolist()}")
     dc = DeviceCase(w, poison=True)
     y = dc.prefill().cpu().numpy()
     r = O.prefill(oracle_pool(w, poison=True), w.q, w.q_start, w.block_tables, w.seq_lens,
@@ -122,7 +138,9 @@ def _relabel(w, seed):
 
 @pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "d64_bs8_g2_e5m2",
                                   "d128_bs64_g7_e4m3"])
-def test_prefill_relabelling_and_reruns_are_bitwise_equal(name):
+@pytest.mark.parametrize("groups", ["2", "3"])
+def test_prefill_relabelling_and_reruns_are_bitwise_equal(name, groups, monkeypatch):
+    set_groups(monkeypatch, groups)
     w = SHAPES[name]()
     dc = DeviceCase(w, poison=True)
     a = dc.prefill().clone()
@@ -150,19 +168,26 @@ def test_prefill_rows_beyond_total_q_are_not_written():
     assert np.all(y[cut:] == 7.0)
 
 
+# (workload, generator, sampled rows, row groups): at head_dim 128 the
+# library takes 3 groups on the chunked and cold batches and 2 on the
+# prefix-hit one; the other choice of each is run as well
 FULL = [
-    ("prefill_cold_2000", W.prefill_cold_2000, 24),
-    ("prefill_chunked_8k", W.prefill_chunked_8k, 24),
-    ("prefill_prefix_hit", W.prefill_prefix_hit, 24),
-    ("prefill_chunked_8k_fp8", W.prefill_chunked_8k_fp8, 24),
-    ("prefill_chunked_8k_d256", W.prefill_chunked_8k_d256, 24),
-    ("prefill_chunked_8k_d256_fp8", W.prefill_chunked_8k_d256_fp8, 24),
+    ("prefill_cold_2000", W.prefill_cold_2000, 24, "auto"),
+    ("prefill_chunked_8k", W.prefill_chunked_8k, 24, "auto"),
+    ("prefill_chunked_8k", W.prefill_chunked_8k, 24, "2"),
+    ("prefill_prefix_hit", W.prefill_prefix_hit, 24, "auto"),
+    ("prefill_prefix_hit", W.prefill_prefix_hit, 24, "3"),
+    ("prefill_chunked_8k_fp8", W.prefill_chunked_8k_fp8, 24, "auto"),
+    ("prefill_chunked_8k_fp8", W.prefill_chunked_8k_fp8, 24, "2"),
+    ("prefill_chunked_8k_d256", W.prefill_chunked_8k_d256, 24, "auto"),
+    ("prefill_chunked_8k_d256_fp8", W.prefill_chunked_8k_d256_fp8, 24, "auto"),
 ]
 
 
-@pytest.mark.parametrize("name,make,nrows", FULL, ids=[c[0] for c in FULL])
-def test_prefill_full_size_sampled(name, make, nrows):
-    say(f"prefill config {name}: generating")
+@pytest.mark.parametrize("name,make,nrows,groups", FULL, ids=[f"{c[0]}-{c[3]}" for c in FULL])
+def test_prefill_full_size_sampled(name, make, nrows, groups, monkeypatch):
+    set_groups(monkeypatch, groups)
+    say(f"prefill config {name} groups={groups}: generating")
     w = make()
     rows = sample_prefill_rows(w, nrows, seed=zlib.crc32(name.encode()))
     say(f"prefill config {name}: device run")
@@ -183,7 +208,11 @@ def test_prefill_full_size_sampled(name, make, nrows):
                                   "d128_bs16_g4_e4m3", "d128_bs8_g4_e5m2", "d256_bs16_g4",
                                   "d128_bs8_g7_e5m2_block"])
 @pytest.mark.parametrize("win", [1, 31, 32, 33, 100])
-def test_sliding_window_prefill(name, win):
+@pytest.mark.parametrize("groups", ["2", "3"])
+def test_sliding_window_prefill(name, win, groups, monkeypatch):
+    if groups == "3" and not name.startswith("d128"):
+        pytest.skip("row groups are chosen at head_dim 128 only")
+    set_groups(monkeypatch, groups)
     w0 = SHAPES[name]()
     w = dataclasses.replace(w0, window=win, block_tables=w0.block_tables.copy())
     # blocks wholly before the window of a sequence's first new token are
