@@ -502,7 +502,7 @@ struct PfDma {
   // registers per lane and one wave per SIMD)
   static constexpr int G = D > 128 ? PA_PF_G256 : GG;
   static constexpr int OCC = (D > 128 && G > 1) || W >= 8 ? 1 : PA_PF_OCC;
-  static constexpr bool PRIO = W * OCC >= 8;              // two or more waves per SIMD
+  static constexpr bool SHARED_SIMD = W * OCC >= 8;       // two or more waves per SIMD
   // head_dim 256: two buffers of 32 KiB
   static constexpr int NBUF = D > 128 ? 2 : PA_PF_NBUF;
   static constexpr int NST = D / 32;
@@ -588,7 +588,10 @@ __global__ __launch_bounds__(pf_waves(D, KVC) * 64, (PfDma<D, pf_waves(D, KVC), 
   constexpr int NW = pf_waves(D, KVC);
   typedef PfDma<D, NW, GG> T;
   constexpr int RB = T::RB, NST = T::NST, NB = T::NB, G = T::G;
-  constexpr bool kPrio = T::PRIO;
+  // raised issue priority for the score MFMAs where two waves share a SIMD,
+  // except for binary16 pools at head_dim 256 (measured 2% slower with it;
+  // fp8 pools there 5% faster)
+  constexpr bool kPrio = T::SHARED_SIMD && (D <= 128 || KV != 0);
   static_assert(KV == 0 || D >= 128, "fp8 tiles are staged for head_dim 128 and 256");
   // fp8 at head_dim 256: one binary16 buffer and two staging slots (66 KB;
   // measured faster than two buffers and three slots)
@@ -859,11 +862,10 @@ __global__ __launch_bounds__(pf_waves(D, KVC) * 64, (PfDma<D, pf_waves(D, KVC), 
       lgkm_wait<0>(kop[0][st]);
       lgkm_wait<0>(kop[1][st]);
     }
-    // Two waves share each SIMD at head_dim <= 128.  The wave issuing its
-    // score MFMAs takes issue priority over the other wave (usually in its
-    // softmax), so the matrix core is kept fed and the VALU work fills in
-    // behind it (measured 1.5-3.5% faster; at head_dim 256, one wave per
-    // SIMD, it only costs).
+    // Two waves share each SIMD.  The wave issuing its score MFMAs takes
+    // issue priority over the other wave (usually in its softmax), so the
+    // matrix core is kept fed and the VALU work fills in behind it (measured
+    // 1.5-3.5% faster at head_dim 128; see kPrio for head_dim 256).
     float4_t sa[G][2];
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
