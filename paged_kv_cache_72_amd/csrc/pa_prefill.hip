@@ -71,9 +71,6 @@ namespace {
 #ifndef PA_PF_W256
 #define PA_PF_W256 8          // prefill at head_dim 256: waves per workgroup (4 or 8)
 #endif
-#ifndef PA_PF_LMFMA
-#define PA_PF_LMFMA 1         // prefill: row sums by an MFMA against ones (1) or by dots (0)
-#endif
 #ifndef PA_PF_F8W
 #define PA_PF_F8W 1           // fp8 at head_dim 256: one binary16 buffer, two staging slots
 #endif
@@ -834,17 +831,14 @@ __global__ __launch_bounds__(pf_waves(D, KVC) * 64, (PfDma<D, pf_waves(D, KVC), 
   for (int c = 0; c < G; ++c)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[c][nb] = {0.f, 0.f, 0.f, 0.f};
-  float m_run[G], l_run[G];
-  // Row sums: with PA_PF_LMFMA one more 16x16x32 MFMA per group and tile
-  // forms P times a column of ones, the binary16 weights the P V product
-  // uses, summed in fp32 and laid out like the accumulators (rows 4h .. 4h +
-  // 3 of lane (h, n)); else two-term dots of the weights with ones, per lane
-  // over its 8 positions, reduced across lanes at the end.
+  // Row sums: one more 16x16x32 MFMA per group and tile forms P times a
+  // column of ones, the binary16 weights the P V product uses, summed in fp32
+  // and laid out like the accumulators (rows 4h .. 4h + 3 of lane (h, n)).
+  float m_run[G];
   float4_t l_acc[G];
 #pragma unroll
   for (int c = 0; c < G; ++c) {
     m_run[c] = kNegBig;
-    l_run[c] = 0.f;
     l_acc[c] = {0.f, 0.f, 0.f, 0.f};
   }
   const float sc = a.k_hs ? a.score_scale * a.k_hs[kh] : a.score_scale;
@@ -906,13 +900,12 @@ __global__ __launch_bounds__(pf_waves(D, KVC) * 64, (PfDma<D, pf_waves(D, KVC), 
         tmax = xor_max(tmax, 32);
         const float m_new = fmaxf(m_run[c], tmax);
         const float alpha = __builtin_amdgcn_exp2f(m_run[c] - m_new);
-        if (!PA_PF_LMFMA) l_run[c] *= alpha;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float ai = __shfl(alpha, 4 * h + i);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) acc[c][nb][i] *= ai;
-          if (PA_PF_LMFMA) l_acc[c][i] *= ai;
+          l_acc[c][i] *= ai;
         }
         m_run[c] = m_new;
       }
@@ -922,15 +915,6 @@ __global__ __launch_bounds__(pf_waves(D, KVC) * 64, (PfDma<D, pf_waves(D, KVC), 
       const float4_t p0 = {p[0], p[1], p[2], p[3]}, p1 = {p[4], p[5], p[6], p[7]};
       const half4_t h0 = __builtin_convertvector(p0, half4_t);
       const half4_t h1 = __builtin_convertvector(p1, half4_t);
-      // (PA_PF_LMFMA 0) row sums of the binary16 weights the P V product uses,
-      // by 2-term dots with ones (fp32 accumulation)
-      if (!PA_PF_LMFMA) {
-        const half2_t one2 = {(_Float16)1.f, (_Float16)1.f};
-        float ls = __builtin_amdgcn_fdot2(half2_t{h0[0], h0[1]}, one2, l_run[c], false);
-        ls = __builtin_amdgcn_fdot2(half2_t{h0[2], h0[3]}, one2, ls, false);
-        ls = __builtin_amdgcn_fdot2(half2_t{h1[0], h1[1]}, one2, ls, false);
-        l_run[c] = __builtin_amdgcn_fdot2(half2_t{h1[2], h1[3]}, one2, ls, false);
-      }
       const half8_t pop = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
       if (c == 0) {
 #pragma unroll
@@ -944,7 +928,7 @@ __global__ __launch_bounds__(pf_waves(D, KVC) * 64, (PfDma<D, pf_waves(D, KVC), 
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         acc[c][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, vop[nb], acc[c][nb], 0, 0, 0);
-      if (PA_PF_LMFMA) {
+      {
         const _Float16 o = (_Float16)1.f;
         const half8_t ones = {o, o, o, o, o, o, o, o};
         l_acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, ones, l_acc[c], 0, 0, 0);
@@ -1041,14 +1025,9 @@ __global__ __launch_bounds__(pf_waves(D, KVC) * 64, (PfDma<D, pf_waves(D, KVC), 
 
 #pragma unroll
   for (int c = 0; c < G; ++c) {
-    float lt = 0.f;
-    if (!PA_PF_LMFMA) {
-      lt = xor_sum(l_run[c], 16);
-      lt = xor_sum(lt, 32);
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float li = PA_PF_LMFMA ? l_acc[c][i] : __shfl(lt, 4 * h + i);
+      const float li = l_acc[c][i];
       const int r = 16 * G * wid + 16 * c + 4 * h + i;
       const int t = r / g, j = r - t * g;
       const int row = qs0 + q0 + t;
