@@ -1213,6 +1213,7 @@ __global__ __launch_bounds__(1024) void flat_merge_heads_kernel(DecodeArgs a, Fl
   const int r_first = range_of(pre, T, NR), r_last = range_of(end - 1, T, NR);
   if (r_first == r_last) return;               // written by the decode kernel
   const bool first_is_last_slot = (int64_t)r_first * T / NR < pre;
+  const bool some_empty = T < NR;              // else every range owns a unit
   const int g = a.gqa, F4 = g * D / 4;
   const int64_t rec = (int64_t)g * (D + 2);
   int K = 1;
@@ -1220,25 +1221,48 @@ __global__ __launch_bounds__(1024) void flat_merge_heads_kernel(DecodeArgs a, Fl
   const int t = threadIdx.x, k = t / F4, q = t - k * F4, h = 4 * q / D;
   float M = kNegBig, L = 0.f;
   float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (k < K) {
-#pragma unroll 8
-    for (int r = r_first + k; r <= r_last; r += K) {
-      const bool empty = range_empty(r, T, NR);
-      const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
-      const float* p = f.slots + ((int64_t)(r * Hkv + kh) * 2 + slot) * rec;
-      const float2 ml0 = ((const float2*)(p + g * D))[h];
-      const float4 ov0 = ((const float4*)p)[q];
-      const float2 ml = empty ? make_float2(kNegBig, 0.f) : ml0;
-      const float4 ov = empty ? make_float4(0.f, 0.f, 0.f, 0.f) : ov0;
-      const float mn = fmaxf(M, ml.x);
-      const float sa = __builtin_amdgcn_exp2f(M - mn), sb = ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
-      L = L * sa + sb;
-      O.x = O.x * sa + sb * ov.x;
-      O.y = O.y * sa + sb * ov.y;
-      O.z = O.z * sa + sb * ov.z;
-      O.w = O.w * sa + sb * ov.w;
-      M = mn;
+  // Records r_first + k, + K, ... of this thread are loaded RB at a time
+  // before any is folded, so their loads are in flight together (RB: the
+  // power of two, at most 8, that covers the records per thread).  Places
+  // past the last record load the last one again and fold an empty state,
+  // which leaves M, L and O bit for bit unchanged.
+  auto fold = [&](auto rb) {
+    constexpr int RB = decltype(rb)::value;
+    for (int r0 = r_first + k; r0 <= r_last; r0 += RB * K) {
+      float2 ml[RB];
+      float4 ov[RB];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int r = r0 + i * K;
+        const int rr = r <= r_last ? r : r_last;
+        const bool empty = r > r_last || (some_empty && range_empty(rr, T, NR));
+        const int slot = (rr == r_first && first_is_last_slot) ? 1 : 0;
+        const float* p = f.slots + ((int64_t)(rr * Hkv + kh) * 2 + slot) * rec;
+        const float2 ml0 = ((const float2*)(p + g * D))[h];
+        const float4 ov0 = ((const float4*)p)[q];
+        ml[i] = empty ? make_float2(kNegBig, 0.f) : ml0;
+        ov[i] = empty ? make_float4(0.f, 0.f, 0.f, 0.f) : ov0;
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const float mn = fmaxf(M, ml[i].x);
+        const float sa = __builtin_amdgcn_exp2f(M - mn);
+        const float sb = ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - mn);
+        L = L * sa + sb;
+        O.x = O.x * sa + sb * ov[i].x;
+        O.y = O.y * sa + sb * ov[i].y;
+        O.z = O.z * sa + sb * ov[i].z;
+        O.w = O.w * sa + sb * ov[i].w;
+        M = mn;
+      }
     }
+  };
+  if (k < K) {
+    const int per = (r_last - r_first + K) / K;          // records per thread, at most
+    if (per <= 1) fold(std::integral_constant<int, 1>());
+    else if (per <= 2) fold(std::integral_constant<int, 2>());
+    else if (per <= 4) fold(std::integral_constant<int, 4>());
+    else fold(std::integral_constant<int, 8>());
   }
   __shared__ float4 sm_o[1024];
   __shared__ float2 sm_ml[1024];
