@@ -599,7 +599,8 @@ def main() -> int:
     base = L.KVPool.allocate(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
                              w.kv_dtype, w.k_scale, w.v_scale, dev, fill_bits=0,
                              shared_blocks=shared, k_head_scales=w.k_head_scales,
-                             v_head_scales=w.v_head_scales, sliding_window=w.window)
+                             v_head_scales=w.v_head_scales, sliding_window=w.window,
+                             block_scales=w.block_scales)
     L.pa_reshape_and_cache(base, k_all, v_all, slots)
     if w.cow_pairs is not None:
         L.pa_copy_blocks(base, torch.from_numpy(w.cow_pairs).to(dev))
@@ -610,10 +611,13 @@ def main() -> int:
     del k_all, v_all, slots
     pools = [base]
     for _ in range(args.layers - 1):
+        bs_copy = (lambda t: None if t is None else t.clone())
         pools.append(L.KVPool(base.k.clone(), base.v.clone(), w.block_size, w.num_kv_heads,
                               w.head_dim, w.kv_dtype, w.k_scale, w.v_scale,
                               shared_blocks=shared, k_head_scales=base.k_head_scales,
-                              v_head_scales=base.v_head_scales, sliding_window=w.window))
+                              v_head_scales=base.v_head_scales, sliding_window=w.window,
+                              k_block_scales=bs_copy(base.k_block_scales),
+                              v_block_scales=bs_copy(base.v_block_scales)))
     part = L.pa_decode_plan(base, w.num_seqs, w.num_q_heads, w.max_seq_len, args.partition)
     ws = L.alloc_workspace(base, w.num_seqs, w.num_q_heads, w.max_seq_len, args.partition)
     grouped = args.decode == "grouped" or (args.decode == "auto" and shared and not w.window)

@@ -1579,6 +1579,7 @@ __global__ __launch_bounds__(256) void flat_group_merge_kernel(DecodeArgs a, Fla
   const int r_first = range_of(pre, T, NR), r_last = range_of(end - 1, T, NR);
   if (r_first == r_last) return;               // written by the decode kernel
   const bool first_is_last_slot = (int64_t)r_first * T / NR < pre;
+  const bool some_empty = T < NR;              // else every range owns a unit
   int m0 = gp.member_start[gi], m1 = gp.member_start[gi + 1];
   m0 = m0 < 0 ? 0 : (m0 > gp.num_members ? gp.num_members : m0);
   m1 = m1 < m0 ? m0 : (m1 > gp.num_members ? gp.num_members : m1);
@@ -1593,7 +1594,7 @@ __global__ __launch_bounds__(256) void flat_group_merge_kernel(DecodeArgs a, Fla
     // so the loads of several records can be in flight together
 #pragma unroll 4
     for (int r = r_first; r <= r_last; ++r) {
-      const bool empty = range_empty(r, T, NR);
+      const bool empty = some_empty && range_empty(r, T, NR);
       const int slot = (r == r_first && first_is_last_slot) ? 1 : 0;
       const float* p = f.slots + ((int64_t)(r * a.num_kv_heads + kh) * 2 + slot) * 16 * (D + 2);
       float2 ml = ((const float2*)(p + 16 * D))[h];

@@ -407,6 +407,15 @@ def long_fp8(seed: int = 7206) -> Workload:
                         kv_dtype="fp8_e4m3fn", partition_size=512)
 
 
+def long_fp8_block(seed: int = 7206) -> Workload:
+    """The long-context batch of long_fp8 (same lengths, blocks and values)
+    with one e4m3fn scale per (block, KV head), written by reshape_and_cache
+    as the blocks fill (amax of the block's rows / 448, raised and re-encoded
+    as later rows exceed it)."""
+    return _independent("long_fp8_block", seed, [131072] * 8, 32, 8, 128, 32, 36864,
+                        kv_dtype="fp8_e4m3fn", partition_size=512, scale_grain="block")
+
+
 def long_e5m2(seed: int = 7207) -> Workload:
     """The long-context split-KV shape of long_fp8 (8 x 131,072 tokens, 32 / 8
     heads, head_dim 128, block_size 32, 512-token partitions) with the KV
@@ -649,6 +658,7 @@ CONFIGS = {
     "prefix_share_bs8": lambda: prefix_share(8),
     "long_fp8": long_fp8,
     "long_e5m2": long_e5m2,
+    "long_fp8_block": long_fp8_block,
     "llama3_8b_b64_w1024": llama3_8b_b64_w1024,
     "hybrid_d256_b64": hybrid_d256_b64,
     "llama3_8b_b64_bs64": lambda: llama3_8b_b64_bs(64),
