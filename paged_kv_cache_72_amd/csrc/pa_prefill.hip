@@ -478,8 +478,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_kernel(PrefillArgs a
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
-// waves per workgroup of prefill_f16_kernel at head_dim d for pool code kvc
-// (fp8 pools, and head_dim 64, load whole tiles with four waves)
+// waves per workgroup of prefill_f16_kernel at head_dim d for pool code kvc:
+// eight at head_dim 256 (every pool format), four at head_dim 64 and for fp8
+// pools at head_dim 128 (whose 4 KiB byte tiles fill four waves' loads)
 constexpr int pf_waves(int d, int kvc) {
   return d > 128 ? PA_PF_W256 : (kvc == 0 && d == 128 ? PA_PF_W16 : kPfWaves);
 }
