@@ -405,6 +405,7 @@ def run_prefill(args, w) -> int:
                    "layers_rotated": args.layers, "shared_blocks": shared},
         "pct_of_peak": round(100 * value / MFMA_F16_PEAK_TFLOPS, 2),
         "prefill_tokens_per_s": round(float(w.q_lens.sum()) / (ms_step * 1e-3), 1),
+        "rows_per_workgroup": L.pa_prefill_plan(base, w.num_seqs, w.num_q_heads, w.max_q_len),
         "alg_flops_per_launch": flops,
         "alg_bytes_per_launch": nbytes,
         "hbm_GB_per_s": round(nbytes / (pf_avg * 1e-3) / 1e9, 1),
