@@ -36,7 +36,8 @@
 //     66 KB of LDS).
 //     fp8 pools at head_dim 64 (prefill_kernel): loaded into registers one
 //     tile ahead and widened on the way into LDS (two buffers), V stored
-//     transposed.  Every kernel spends one workgroup barrier per tile.
+//     transposed.  One workgroup barrier per tile (two for fp8 pools at
+//     head_dim 256, around the widening).
 //   * Scores are computed transposed, S^T = K Q^T, with the 16x16x32 f16 MFMA:
 //     K rows are the A operand (from LDS), the group's 16 query rows the B
 //     operand (held in registers for the whole loop).  The K rows of a score
