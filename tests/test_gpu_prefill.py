@@ -204,14 +204,16 @@ def test_prefill_full_size_sampled(name, make, nrows, groups, monkeypatch):
     say(f"  {st}")
 
 
-@pytest.mark.parametrize("name", ["d128_bs16_g4", "d128_bs8_g7", "d64_bs16_g16",
-                                  "d128_bs16_g4_e4m3", "d128_bs8_g4_e5m2", "d256_bs16_g4",
-                                  "d128_bs8_g7_e5m2_block"])
+WINDOW_SHAPES = ["d128_bs16_g4", "d128_bs8_g7", "d64_bs16_g16", "d128_bs16_g4_e4m3",
+                 "d128_bs8_g4_e5m2", "d256_bs16_g4", "d128_bs8_g7_e5m2_block"]
+# row groups are chosen at head_dim 128 only: both there, the library's elsewhere
+WINDOW_CASES = [(n, g) for n in WINDOW_SHAPES
+                for g in (("2", "3") if n.startswith("d128") else ("auto",))]
+
+
+@pytest.mark.parametrize("name,groups", WINDOW_CASES, ids=[f"{n}-{g}" for n, g in WINDOW_CASES])
 @pytest.mark.parametrize("win", [1, 31, 32, 33, 100])
-@pytest.mark.parametrize("groups", ["2", "3"])
-def test_sliding_window_prefill(name, win, groups, monkeypatch):
-    if groups == "3" and not name.startswith("d128"):
-        pytest.skip("row groups are chosen at head_dim 128 only")
+def test_sliding_window_prefill(name, groups, win, monkeypatch):
     set_groups(monkeypatch, groups)
     w0 = SHAPES[name]()
     w = dataclasses.replace(w0, window=win, block_tables=w0.block_tables.copy())
