@@ -177,12 +177,27 @@ namespace {
 // the default unless the batch is many short contexts; it keeps per-sequence
 // prefix and lengths in LDS (2 S + 1 ints).
 constexpr int32_t kFlatMaxSeqs = 8000;
-// Waves of the flat schedule: enough that about 8 MiB of K/V tiles are in
-// flight (each wave keeps about one 16-token tile of K and V in flight), at
-// least one wave per SIMD and at most the two per SIMD the kernel's registers
-// allow.  Measured: for fp16 head_dim 128 (8 KiB tiles) 1024 waves beat 2048;
-// for 4 KiB tiles (fp8, or head_dim 64) 2048 waves are needed.
+// Waves of the flat schedule, measured per size of a 16-token K+V tile (each
+// wave keeps about one tile in flight).  4 KiB tiles (fp8 at head_dim 128,
+// head_dim 64): 2048 waves, two per SIMD (1536 were 5-8% slower, 1024 10-27%).
+// 8 KiB tiles (fp16 at head_dim 128): 768, three per CU (1024 were 3-4%
+// slower, 640 8-9%, 704 2-3%, 896 2%; 832 was 2% faster on one shape and
+// slower on another).  head_dim 256: 1024, one per SIMD (896 2% slower, 768
+// 10%, 1152-1280 30-40%).
 int64_t flat_waves(const pa::PoolGeom& g) {
+#ifdef PA_FLAT_MAX_WAVES
+  (void)g;
+  return PA_FLAT_MAX_WAVES;
+#else
+  const int64_t tile_bytes = 16 * (int64_t)g.head_dim * g.elem_bytes * 2;
+  if (g.head_dim > 128) return 1024;
+  return tile_bytes <= 4096 ? 2048 : 768;
+#endif
+}
+// The grouped flat schedule's waves: enough that about 8 MiB of tiles are in
+// flight, 1024..2048 (for 8 KiB tiles 1024 beat 768 and 832 by 2-3% on 256
+// fork groups of 4).
+int64_t group_flat_waves(const pa::PoolGeom& g) {
 #ifdef PA_FLAT_MAX_WAVES
   (void)g;
   return PA_FLAT_MAX_WAVES;
@@ -320,7 +335,7 @@ int group_plan(const pa_kv_pool* pool, int32_t S, int32_t Hq, int32_t max_seq_le
   gp->workspace = 0;
   if (gp->mode == kGroupFlat) {
     const int64_t per_head_ub = (int64_t)S * cdiv64(max_seq_len, 16);
-    int64_t ranges = flat_waves(*g) / g->num_kv_heads;
+    int64_t ranges = group_flat_waves(*g) / g->num_kv_heads;
     if (ranges > per_head_ub / kFlatMinTiles) ranges = per_head_ub / kFlatMinTiles;
     if (ranges < 1) ranges = 1;
     gp->ranges = ranges;

@@ -131,7 +131,7 @@ def test_workspace_size_formula(so):
     assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, P) == ml + rows * D * 4
     assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, -1) == 0
     # flat: prefix [S+1] int32, then 2 records of gqa*(D+2) floats per wave
-    ranges = min(1024 // 8, S * (T // 16) // 8)    # 1024 waves for 8 KiB fp16 tiles
+    ranges = min(768 // 8, S * (T // 16) // 8)     # 768 waves for 8 KiB fp16 tiles
     pre = ((S + 1) * 4 + 255) // 256 * 256
     assert so.pa_decode_workspace_size(C.byref(p), S, Hq, T, 1) == \
         pre + ranges * 8 * 2 * 4 * 130 * 4
@@ -155,10 +155,11 @@ def test_plan_choices(so, S, Hkv, Hq, bs, maxlen):
 
 
 def test_flat_wave_count_follows_tile_bytes(so):
-    """About 8 MiB of 16-token K/V tiles in flight, 1024..2048 waves: the flat
-    workspace holds two records per wave, so its size shows the wave count."""
+    """2048 waves for 4 KiB 16-token K+V tiles, 768 for 8 KiB, 1024 at head_dim
+    256: the flat workspace holds two records per wave, so its size shows the
+    wave count."""
     S, Hq, T = 64, 32, 4096
-    for D, dt, waves in ((128, L.PA_KV_F16, 1024), (128, L.PA_KV_FP8_E4M3FN, 2048),
+    for D, dt, waves in ((128, L.PA_KV_F16, 768), (128, L.PA_KV_FP8_E4M3FN, 2048),
                          (64, L.PA_KV_F16, 2048), (64, L.PA_KV_FP8_E4M3FN, 2048),
                          (256, L.PA_KV_F16, 1024), (256, L.PA_KV_FP8_E4M3FN, 1024)):
         p = _pool(head_dim=D, dtype=dt, k_scale=0.5, v_scale=0.5)
