@@ -16,10 +16,15 @@ as a model's consecutive attention calls do, so no step finds its KV in the
 
 Prints ONE JSON line.  `value` is achieved algorithmic GB/s of the whole step
 (K/V context, q, out, tables, lengths, and the new tokens' write), from wall
-time over exactly --steps steps.  `roofline` covers the dominant kernel
-(pa_decode), timed with HIP events on its stream inside the timed region.
-`cpu_baseline` times the fp64 CPU oracle on the host cores over the same
-workload.
+time over exactly --steps steps, with no timing event between them.
+`roofline` covers the dominant kernel (pa_decode): its average launch
+duration is the GPU time between two HIP events on its stream around the same
+number of calls, back to back over the same rotated pools, right after the
+timed steps.  (A timing event recorded between calls is not free: each record
+adds about 4 us of queue time, which per-call event pairs would add to a
+100 us call; the per-call distribution is reported separately, from calls
+each between its own pair of events.)  `cpu_baseline` times the fp64 CPU
+oracle on the host cores over the same workload.
 """
 from __future__ import annotations
 
@@ -160,7 +165,8 @@ def cpu_baseline(w, budget_s: float, single_thread_configs=()) -> dict:
 def probe_ceiling(nbytes: int) -> dict:
     """The plain-read ceiling at the decode call's size: the wave-contiguous
     read probe (libpa_probe.so) over nbytes, rotating three buffers so no read
-    finds its data in the Infinity Cache; median of 30 event-timed launches."""
+    finds its data in the Infinity Cache; 30 launches back to back between one
+    pair of events."""
     import torch
     lib_path = os.path.join(ROOT, "paged_kv_cache_72_amd", "libpa_probe.so")
     if not os.path.exists(lib_path):
@@ -176,16 +182,11 @@ def probe_ceiling(nbytes: int) -> dict:
     st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
     for i in range(5):
         P.pa_probe_wave_chunk(bufs[i % 3].data_ptr(), waves, steps, unroll, sink.data_ptr(), st)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(30)]
-    for i, (a, b) in enumerate(ev):
-        a.record()
-        P.pa_probe_wave_chunk(bufs[i % 3].data_ptr(), waves, steps, unroll, sink.data_ptr(), st)
-        b.record()
-    torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    ms = span_avg_ms(lambda i: P.pa_probe_wave_chunk(bufs[i % 3].data_ptr(), waves, steps,
+                                                     unroll, sink.data_ptr(), st),
+                     30, torch.cuda.current_stream())
     del bufs
-    return {"bytes": n, "median_ms": round(ms, 5), "GB_per_s": round(n / (ms * 1e-3) / 1e9, 1),
+    return {"bytes": n, "avg_ms": round(ms, 5), "GB_per_s": round(n / (ms * 1e-3) / 1e9, 1),
             "probe": f"wave-contiguous 16-byte loads, {waves} waves, {unroll} KiB in flight per "
                      "wave"}
 
@@ -194,6 +195,21 @@ def percentiles_ms(ms) -> dict:
     a = np.asarray(ms, np.float64)
     return {"p10": round(float(np.percentile(a, 10)), 5), "p50": round(float(np.median(a)), 5),
             "p90": round(float(np.percentile(a, 90)), 5), "mean": round(float(a.mean()), 5)}
+
+
+def span_avg_ms(fn, reps: int, stream) -> float:
+    """Average GPU time per call of fn(0) .. fn(reps - 1) run back to back:
+    one pair of HIP events on `stream` around all of them."""
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(reps):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
 
 
 def traffic_entry(config: str):
@@ -358,26 +374,25 @@ def run_prefill(args, w) -> int:
                               shared_blocks=shared))
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    def prefill(p):
+        L.pa_prefill(p, out, q, qs, bt, lens, w.max_q_len, w.scale, stream)
+
+    def step(i):
         p = pools[i % len(pools)]
         L.pa_reshape_and_cache(p, k_new, v_new, slot_new, stream)
-        if ev is not None:
-            ev[0].record(stream)
-        L.pa_prefill(p, out, q, qs, bt, lens, w.max_q_len, w.scale, stream)
-        if ev is not None:
-            ev[1].record(stream)
+        prefill(p)
 
     warmup = warm_up(step, args.warmup)
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(warmup + i, events[i])
+        step(warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    pf_avg = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    # the same calls over the same rotated pools, back to back between one
+    # pair of events
+    pf_avg = span_avg_ms(lambda i: prefill(pools[(warmup + i) % len(pools)]), args.steps, stream)
     if args.calib_copy_gib > 0:
         n = int(args.calib_copy_gib * (1 << 30))
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -652,42 +667,41 @@ def main() -> int:
             ev[1].record(stream)
 
     warmup = warm_up(step, args.warmup)
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(warmup + i, events[i])
+        step(warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    # the call's average duration: the same calls over the same rotated pools,
+    # back to back between one pair of events
+    dec_avg = span_avg_ms(lambda i: decode(pools[(warmup + i) % len(pools)]), args.steps, stream)
+    # the per-call distribution: as many steps again, each call between its
+    # own pair of events (whose records the figures include)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(warmup + args.steps + i, events[i])
+    torch.cuda.synchronize()
     dec_ms = [a.elapsed_time(b) for a, b in events]
-    dec_avg = float(np.mean(dec_ms))
 
     # ---- the two write paths, timed on their own (after the decode timing)
-    def event_avg_ms(fn, reps=50):
+    def back_to_back_ms(fn, reps=50):
         for i in range(5):
             fn(i)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
-        torch.cuda.synchronize()
-        for i in range(reps):
-            ev[i][0].record(stream)
-            fn(i)
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(c) for a, c in ev]))
+        return span_avg_ms(fn, reps, stream)
 
     # warm: back-to-back calls on one pool (K/V partly served from the
     # Infinity Cache), labelled as such
-    warm_ms = event_avg_ms(lambda i: decode(pools[0]))
+    warm_ms = back_to_back_ms(lambda i: decode(pools[0]))
     plain_ms = None
     if grouped:   # the same step through pa_decode, for comparison
-        plain_ms = event_avg_ms(lambda i: L.pa_decode(pools[i % len(pools)], out, q, bt, lens,
-                                                      w.max_seq_len, w.scale, args.partition,
-                                                      ws, stream), reps=100)
-    rc_ms = event_avg_ms(lambda i: L.pa_reshape_and_cache(pools[i % len(pools)], k_new, v_new,
-                                                           slot_new, stream))
+        plain_ms = back_to_back_ms(lambda i: L.pa_decode(pools[i % len(pools)], out, q, bt, lens,
+                                                         w.max_seq_len, w.scale, args.partition,
+                                                         ws, stream), reps=100)
+    rc_ms = back_to_back_ms(lambda i: L.pa_reshape_and_cache(pools[i % len(pools)], k_new, v_new,
+                                                              slot_new, stream))
     pairs = w.cow_pairs
     if pairs is None:   # copy 256 context blocks into blocks no table lists
         nb_used = (w.seq_lens.astype(np.int64) + w.block_size - 1) // w.block_size
@@ -697,7 +711,7 @@ def main() -> int:
         n_p = int(min(256, used.size, free.size))
         pairs = np.stack([used[:n_p], free[:n_p]], axis=1).astype(np.int64)
     pairs_d = torch.from_numpy(np.ascontiguousarray(pairs)).to(dev)
-    cb_ms = event_avg_ms(lambda i: L.pa_copy_blocks(pools[i % len(pools)], pairs_d, stream))
+    cb_ms = back_to_back_ms(lambda i: L.pa_copy_blocks(pools[i % len(pools)], pairs_d, stream))
     blk_bytes = w.block_size * w.num_kv_heads * w.head_dim * w.kv_elem_bytes
     cb_bytes = int(pairs.shape[0]) * 2 * blk_bytes * 2
 
@@ -716,7 +730,10 @@ def main() -> int:
     del pools
     probe = probe_ceiling(b["decode"]) if not args.no_probe else {}
     pct = percentiles_ms(dec_ms)
-    call = {"events_ms": pct,
+    call = {"back_to_back_ms": round(dec_avg, 5),
+            "events_ms": pct,
+            "events_note": "each call between its own pair of events, whose records add "
+                           "their queue time",
             "GB_per_s_at_p50": round(b["decode"] / (pct["p50"] * 1e-3) / 1e9, 1),
             "pct_of_peak_at_p50": round(100 * b["decode"] / (pct["p50"] * 1e-3) / 1e9
                                         / HBM_PEAK_GBS, 2),
